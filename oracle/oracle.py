@@ -1,0 +1,110 @@
+"""ctypes front-end of the fp64 oracle (test infrastructure).
+
+All arrays are numpy float64, C-contiguous; inputs stored on a device in bf16
+or fp32 are widened to float64 exactly before they get here.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def _f64(a, shape, name):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if tuple(a.shape) != tuple(shape):
+        raise ValueError(f"oracle: {name} has shape {a.shape}, expected {shape}")
+    return a
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_dp) if a is not None else None
+
+
+class Oracle:
+    """One loaded copy of the oracle library."""
+
+    def __init__(self, lib_path: str = DEFAULT_LIB):
+        if lib_path == DEFAULT_LIB and not os.path.exists(lib_path):
+            from . import build as _build
+            _build.build()
+        lib = ctypes.CDLL(lib_path)
+        lib.ssm_oracle_scan.argtypes = [_dp] * 7 + [_dp, _dp] + [_i64] * 4 + [ctypes.c_int]
+        lib.ssm_oracle_scan.restype = ctypes.c_int
+        lib.ssm_oracle_step.argtypes = [_dp] * 8 + [_i64] * 3
+        lib.ssm_oracle_step.restype = ctypes.c_int
+        lib.ssm_oracle_max_threads.argtypes = []
+        lib.ssm_oracle_max_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = lib_path
+
+    def max_threads(self) -> int:
+        return int(self.lib.ssm_oracle_max_threads())
+
+    def scan(self, x, delta, A, B, C, D, h0=None, threads: int = 0):
+        """Sequential fp64 scan.  Returns (y [Bsz,L,Dm], h_final [Bsz,Dm,N])."""
+        x = np.asarray(x)
+        Bsz, L, Dm = x.shape
+        N = np.asarray(A).shape[1]
+        x = _f64(x, (Bsz, L, Dm), "x")
+        delta = _f64(delta, (Bsz, L, Dm), "delta")
+        A = _f64(A, (Dm, N), "A")
+        B = _f64(B, (Bsz, L, N), "B")
+        C = _f64(C, (Bsz, L, N), "C")
+        D = _f64(D, (Dm,), "D")
+        if h0 is not None:
+            h0 = _f64(h0, (Bsz, Dm, N), "h0")
+        y = np.empty((Bsz, L, Dm), dtype=np.float64)
+        hf = np.empty((Bsz, Dm, N), dtype=np.float64)
+        rc = self.lib.ssm_oracle_scan(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(h0), _ptr(y), _ptr(hf),
+                                      Bsz, L, Dm, N, int(threads))
+        if rc != 0:
+            raise RuntimeError(f"ssm_oracle_scan failed with code {rc}")
+        return y, hf
+
+    def step(self, x, delta, A, B, C, D, h):
+        """One recurrent step.  Returns (y [Bsz,Dm], h_new [Bsz,Dm,N]); h is not modified."""
+        x = np.asarray(x)
+        Bsz, Dm = x.shape
+        N = np.asarray(A).shape[1]
+        x = _f64(x, (Bsz, Dm), "x")
+        delta = _f64(delta, (Bsz, Dm), "delta")
+        A = _f64(A, (Dm, N), "A")
+        B = _f64(B, (Bsz, N), "B")
+        C = _f64(C, (Bsz, N), "C")
+        D = _f64(D, (Dm,), "D")
+        hn = _f64(h, (Bsz, Dm, N), "h").copy()
+        y = np.empty((Bsz, Dm), dtype=np.float64)
+        rc = self.lib.ssm_oracle_step(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(hn), _ptr(y), Bsz, Dm, N)
+        if rc != 0:
+            raise RuntimeError(f"ssm_oracle_step failed with code {rc}")
+        return y, hn
+
+
+_default = None
+
+
+def load() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def max_threads() -> int:
+    return load().max_threads()
+
+
+def scan(x, delta, A, B, C, D, h0=None, threads: int = 0):
+    return load().scan(x, delta, A, B, C, D, h0=h0, threads=threads)
+
+
+def step(x, delta, A, B, C, D, h):
+    return load().step(x, delta, A, B, C, D, h)

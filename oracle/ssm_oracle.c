@@ -1,0 +1,141 @@
+/*
+ * Reference oracle for the selective state-space scan -- TEST INFRASTRUCTURE.
+ *
+ * This file is a plain, slow, sequential fp64 implementation of what the
+ * selective-scan hot path computes.  Only the test-suite, the smoke check and
+ * the CPU-baseline leg of the benchmark may load it.  It shares no code,
+ * header, constant or helper with the HIP library and must never be used as a
+ * fallback for it.
+ *
+ * What it follows (page = "Mamba SSM Nedir? Transformer Alternatifi Rehberi",
+ * yapayzekasozluk.tr):
+ *   - section "State Space Model Temelleri", continuous model with the D
+ *     feed-through term:  h'(t) = A h(t) + B x(t),  y(t) = C h(t) + D x(t).
+ *   - section "Ayrik Zamana Gecis", zero-order-hold discretisation:
+ *       Abar = exp(delta*A),  Bbar = (delta*A)^-1 (exp(delta*A) - I) delta*B,
+ *     and the recurrence  h_t = Abar h_{t-1} + Bbar x_t,  y_t = C h_t.
+ *   - section "Mamba'nin Yeniligi: Selective SSM": B_t, C_t and delta_t are
+ *     given per token (they are inputs here, produced upstream).
+ * The same recurrence is stated on "Mamba: Transformer'a Meydan Okuyan
+ * Uzun-Bagimli Model" (matematikkaravani.com), section "Eski fikrin geri
+ * donusu: durum uzayi".
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - A is diagonal and real, stored as A[d][n]; the matrix ZOH formula is
+ *     then elementwise:  Bbar[n] = delta * phi(delta*A[d][n]) * B[n] with
+ *     phi(z) = (exp(z)-1)/z and phi(0) = 1 (the limit, which also covers
+ *     A == 0 and delta == 0).
+ *   - B_t and C_t are shared by all channels d of a batch row; delta_t and x_t
+ *     are per channel.
+ *   - y_t uses the updated state h_t, plus D[d]*x_t[d].
+ *   - initial state h_{-1} = h0 if given, else 0.
+ *
+ * Layouts (row-major, contiguous):
+ *   scan:  x, delta, y : [Bsz][L][Dm]      B, C : [Bsz][L][N]
+ *          A : [Dm][N]     D : [Dm]         h0, h_final : [Bsz][Dm][N]
+ *   step:  x, delta, y : [Bsz][Dm]          B, C : [Bsz][N]
+ *          A : [Dm][N]     D : [Dm]         h : [Bsz][Dm][N] (in/out)
+ *
+ * All arithmetic is IEEE double with libm exp/expm1; build without
+ * -ffast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* phi(z) = (exp(z) - 1) / z, with its limit 1 at z = 0. */
+static double zoh_phi(double z)
+{
+    if (z == 0.0)
+        return 1.0;
+    return expm1(z) / z;
+}
+
+/* One recurrence step for a single channel: updates h[0..N) in place and
+ * returns y.  a: A[d][*], b/c: B_t[*], C_t[*]. */
+static double channel_step(double *h, double xt, double dt, const double *a,
+                           const double *b, const double *c, double dskip,
+                           int64_t N)
+{
+    double y = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        const double z = dt * a[n];
+        const double abar = exp(z);
+        const double bbar = dt * zoh_phi(z) * b[n];
+        h[n] = abar * h[n] + bbar * xt;
+        y += c[n] * h[n];
+    }
+    return y + dskip * xt;
+}
+
+int ssm_oracle_scan(const double *x, const double *delta, const double *A,
+                    const double *B, const double *C, const double *D,
+                    const double *h0, double *y, double *h_final,
+                    int64_t Bsz, int64_t L, int64_t Dm, int64_t N,
+                    int nthreads)
+{
+    if (Bsz < 0 || L < 0 || Dm < 0 || N <= 0)
+        return 1;
+    const int64_t nchan = Bsz * Dm;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int err = 0;
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)N * sizeof(double));
+        if (!h) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t ch = 0; ch < nchan; ++ch) {
+                const int64_t b = ch / Dm, d = ch % Dm;
+                for (int64_t n = 0; n < N; ++n)
+                    h[n] = h0 ? h0[(b * Dm + d) * N + n] : 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    const int64_t i = (b * L + t) * Dm + d;
+                    const int64_t r = (b * L + t) * N;
+                    y[i] = channel_step(h, x[i], delta[i], A + d * N, B + r,
+                                        C + r, D[d], N);
+                }
+                if (h_final)
+                    for (int64_t n = 0; n < N; ++n)
+                        h_final[(b * Dm + d) * N + n] = h[n];
+            }
+            free(h);
+        }
+    }
+    return err;
+}
+
+int ssm_oracle_step(const double *x, const double *delta, const double *A,
+                    const double *B, const double *C, const double *D,
+                    double *h, double *y, int64_t Bsz, int64_t Dm, int64_t N)
+{
+    if (Bsz < 0 || Dm < 0 || N <= 0)
+        return 1;
+    for (int64_t b = 0; b < Bsz; ++b)
+        for (int64_t d = 0; d < Dm; ++d) {
+            const int64_t i = b * Dm + d;
+            y[i] = channel_step(h + i * N, x[i], delta[i], A + d * N,
+                                B + b * N, C + b * N, D[d], N);
+        }
+    return 0;
+}
+
+int ssm_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,88 @@
+"""Named synthetic workloads for the selective scan and the decode step.
+
+Shapes and distributions follow the five workload descriptions this project is
+measured on; none of them needs trained weights or a dataset.  Notation:
+N(mu, sigma) has standard deviation sigma; U[a, b] is uniform.
+
+The sizes imitate the layer shapes of the Mamba checkpoints the pages name
+(mamba-130m, mamba-2.8b; "Mamba SSM Nedir?" page, section "Nasil Denerim?"),
+but every value is drawn at random.
+"""
+from dataclasses import dataclass, replace
+from typing import Optional
+
+
+@dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    Bsz: int
+    L: int
+    Dm: int
+    N: int
+    dtype: str              # storage dtype of x, delta, B, C, y: "fp32" | "bf16"
+    a_kind: str             # "s4d_real": A[d,n] = -(n+1);  "lognormal": A = -exp(N(0, 0.5))
+    delta_kind: str         # "per_token": softplus(0.5*N(0,1) + inv_softplus(u_d));
+                            # "per_channel": softplus(inv_softplus(u_d)) = u_d for every t
+    bc_scale: float         # B, C ~ N(0,1) * bc_scale
+    seed: int
+
+    def elems(self) -> int:
+        return self.Bsz * self.L * self.Dm * self.N
+
+    def with_shape(self, **kw) -> "ScanConfig":
+        return replace(self, **kw)
+
+
+@dataclass(frozen=True)
+class StepConfig:
+    name: str
+    Bsz: int
+    Dm: int
+    N: int
+    dtype: str              # dtype of x, delta, B, C, y
+    h0_std: float           # resident state h ~ N(0, h0_std), fp32
+    n_tokens: int
+    seed: int
+
+    def elems_per_step(self) -> int:
+        return self.Bsz * self.Dm * self.N
+
+    def with_shape(self, **kw) -> "StepConfig":
+        return replace(self, **kw)
+
+
+# Tiny fp32 scan (the case the oracle runs in full in well under a second).
+TINY_FP32 = ScanConfig("tiny_fp32_b1_l256_d64_n16", 1, 256, 64, 16, "fp32",
+                       "s4d_real", "per_token", 1.0, seed=0)
+
+# A Mamba-130M-shaped layer: random (non-structured) negative A.
+MAMBA130M_LAYER = ScanConfig("mamba130m_layer_b8_l2048_d1536_n16", 8, 2048, 1536, 16,
+                             "bf16", "lognormal", "per_token", 1.0, seed=1)
+
+# A Mamba-2.8B-shaped layer: the headline throughput workload.
+MAMBA2P8B_LAYER = ScanConfig("mamba2p8b_layer_b4_l16384_d5120_n16", 4, 16384, 5120, 16,
+                             "bf16", "s4d_real", "per_token", 0.25, seed=2)
+
+# Long context: one sequence of 2^20 tokens, slow-decay channels.
+LONG_CONTEXT_1M = ScanConfig("long_context_b1_l1048576_d1024_n16", 1, 1 << 20, 1024, 16,
+                             "bf16", "s4d_real", "per_channel", 1.0, seed=3)
+
+# Recurrent decode step on a resident state.
+DECODE_256x8192 = StepConfig("decode_b256_d8192_n16", 256, 8192, 16, "bf16",
+                             h0_std=0.1, n_tokens=1000, seed=4)
+
+SCAN_CONFIGS = {c.name: c for c in (TINY_FP32, MAMBA130M_LAYER, MAMBA2P8B_LAYER,
+                                    LONG_CONTEXT_1M)}
+STEP_CONFIGS = {DECODE_256x8192.name: DECODE_256x8192}
+
+
+def get(name: str):
+    if name in SCAN_CONFIGS:
+        return SCAN_CONFIGS[name]
+    if name in STEP_CONFIGS:
+        return STEP_CONFIGS[name]
+    raise KeyError(name)
+
+
+def maybe(cfg: Optional[object], **kw):
+    return cfg.with_shape(**kw) if kw else cfg

@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs, shared by the oracle side and the HIP side.
+
+This module only draws random tensors with the distributions of the named
+workloads; it contains none of the scan's arithmetic.  The transform applied to
+delta (softplus of a shifted normal) is how the selection mechanism produces
+delta upstream of the scan ("Mamba SSM Nedir?" page, section "Mamba'nin
+Yeniligi: Selective SSM"); the scan itself consumes delta after it.
+
+Draw order is fixed:  x, delta-noise (per-token recipe only), u_d, B, C, D,
+then A (lognormal recipe only).  Decode draws u_d, D, h0 first, then per token
+x, delta-noise, B, C.  Values are drawn in fp32 and then cast to the storage
+dtype (round to nearest even for bf16).
+"""
+from typing import Dict, List
+
+import torch
+
+from .configs import ScanConfig, StepConfig
+
+_DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+U_LO, U_HI = 1e-3, 1e-1
+
+
+def storage_dtype(name: str) -> torch.dtype:
+    return _DT[name]
+
+
+def softplus(z: torch.Tensor) -> torch.Tensor:
+    return torch.nn.functional.softplus(z)
+
+
+def inv_softplus(u: torch.Tensor) -> torch.Tensor:
+    # u + log(-expm1(-u)) = log(exp(u) - 1), computed without cancellation
+    return u + torch.log(-torch.expm1(-u))
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _normal(shape, g, device, std=1.0):
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t
+
+
+def s4d_real_A(Dm: int, N: int, device) -> torch.Tensor:
+    """A[d, n] = -(n + 1) for every channel (fp32)."""
+    a = -torch.arange(1, N + 1, device=device, dtype=torch.float32)
+    return a.unsqueeze(0).expand(Dm, N).contiguous()
+
+
+def scan_inputs(cfg: ScanConfig, device="cpu", seed=None) -> Dict[str, torch.Tensor]:
+    """x, delta, A, B, C, D for one scan call on ``device``."""
+    device = torch.device(device)
+    g = _gen(device, cfg.seed if seed is None else seed)
+    sd = _DT[cfg.dtype]
+    Bsz, L, Dm, N = cfg.Bsz, cfg.L, cfg.Dm, cfg.N
+
+    x = _normal((Bsz, L, Dm), g, device).to(sd)
+    noise = _normal((Bsz, L, Dm), g, device, 0.5) if cfg.delta_kind == "per_token" else None
+    u = torch.rand((Dm,), generator=g, device=device, dtype=torch.float32) * (U_HI - U_LO) + U_LO
+    if noise is not None:
+        delta = softplus(noise.add_(inv_softplus(u))).to(sd)
+        del noise
+    elif cfg.delta_kind == "per_channel":
+        delta = softplus(inv_softplus(u)).to(sd).view(1, 1, Dm).expand(Bsz, L, Dm).contiguous()
+    else:
+        raise ValueError(cfg.delta_kind)
+    B = _normal((Bsz, L, N), g, device, cfg.bc_scale).to(sd)
+    C = _normal((Bsz, L, N), g, device, cfg.bc_scale).to(sd)
+    D = _normal((Dm,), g, device)
+    if cfg.a_kind == "s4d_real":
+        A = s4d_real_A(Dm, N, device)
+    elif cfg.a_kind == "lognormal":
+        A = -torch.exp(_normal((Dm, N), g, device, 0.5))
+    else:
+        raise ValueError(cfg.a_kind)
+    return {"x": x, "delta": delta, "A": A, "B": B, "C": C, "D": D}
+
+
+def step_state(cfg: StepConfig, device="cpu", seed=None) -> Dict[str, torch.Tensor]:
+    """Per-layer constants and the resident state: u (for delta), A, D, h0."""
+    device = torch.device(device)
+    g = _gen(device, cfg.seed if seed is None else seed)
+    Dm, N = cfg.Dm, cfg.N
+    u = torch.rand((Dm,), generator=g, device=device, dtype=torch.float32) * (U_HI - U_LO) + U_LO
+    D = _normal((Dm,), g, device)
+    h = _normal((cfg.Bsz, Dm, N), g, device, cfg.h0_std)
+    A = s4d_real_A(Dm, N, device)
+    return {"A": A, "D": D, "h": h, "_u": u, "_gen": g}
+
+
+def step_tokens(cfg: StepConfig, state: Dict[str, torch.Tensor], n_tokens: int) -> List[Dict[str, torch.Tensor]]:
+    """``n_tokens`` consecutive decode inputs (x, delta [Bsz,Dm]; B, C [Bsz,N])."""
+    g = state["_gen"]
+    u = state["_u"]
+    device = u.device
+    sd = _DT[cfg.dtype]
+    shift = inv_softplus(u)
+    out = []
+    for _ in range(n_tokens):
+        x = _normal((cfg.Bsz, cfg.Dm), g, device).to(sd)
+        delta = softplus(_normal((cfg.Bsz, cfg.Dm), g, device, 0.5).add_(shift)).to(sd)
+        B = _normal((cfg.Bsz, cfg.N), g, device).to(sd)
+        C = _normal((cfg.Bsz, cfg.N), g, device).to(sd)
+        out.append({"x": x, "delta": delta, "B": B, "C": C})
+    return out
+
+
+def alg_bytes_scan(cfg: ScanConfig) -> int:
+    """Bytes the scan must move at minimum: inputs once, outputs once."""
+    s = 4 if cfg.dtype == "fp32" else 2
+    BLD = cfg.Bsz * cfg.L * cfg.Dm
+    BLN = cfg.Bsz * cfg.L * cfg.N
+    return (2 * BLD * s + 2 * BLN * s + 4 * cfg.Dm * cfg.N + 4 * cfg.Dm
+            + BLD * s + 4 * cfg.Bsz * cfg.Dm * cfg.N)
+
+
+def alg_bytes_step(cfg: StepConfig) -> int:
+    s = 4 if cfg.dtype == "fp32" else 2
+    BD, BN = cfg.Bsz * cfg.Dm, cfg.Bsz * cfg.N
+    return (8 * BD * cfg.N + 2 * s * BD + 2 * s * BN + s * BD
+            + 4 * cfg.Dm * cfg.N + 4 * cfg.Dm)
+

@@ -1,0 +1,313 @@
+"""Pins for the fp64 oracle: checks against what the pages and mathematics fix.
+
+Each ``check_*`` takes an object with the oracle's ``scan``/``step`` interface
+and raises AssertionError on a mismatch.  They are run against the real oracle
+(tests/test_oracle_pins.py) and against deliberately broken copies of it
+(tests/test_oracle_mutants.py) to show that a plausible slip in the oracle
+fails at least one of them.
+
+None of these checks re-types the oracle's recurrence: they use the
+matrix-exponential (Van Loan) form of the zero-order hold, the unrolled
+closed-form sum, the LTI convolution mode, a library IIR filter, exact limits
+and invariants, and hand-derived worked examples.
+"""
+import json
+import os
+
+import numpy as np
+from scipy.linalg import expm
+from scipy.signal import lfilter
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_forms.json")
+
+
+def rel_err(a, b, floor_frac=0.1):
+    """max |a-b| / max(|b|, floor_frac * rms(b)) -- elementwise, RMS-floored."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if b.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(b * b))) if b.size else 0.0
+    den = np.maximum(np.abs(b), floor_frac * rms + 1e-300)
+    return float(np.max(np.abs(a - b) / den))
+
+
+# ---------------------------------------------------------------------------
+# independent evaluations
+
+
+def vanloan_zoh(a, dt, b=1.0):
+    """(Abar, Bbar) for h' = a h + b u with u held over [0, dt].
+
+    exp(dt * [[a, b], [0, 0]]) = [[Abar, Bbar], [0, 1]] -- the augmented-matrix
+    identity for the zero-order hold; it does not use the (e^z - 1)/A formula.
+    """
+    M = np.array([[a * dt, b * dt], [0.0, 0.0]], dtype=np.float64)
+    E = expm(M)
+    return E[0, 0], E[0, 1]
+
+
+def brute_force_scan(x, delta, A, B, C, D, h0=None):
+    """Unrolled closed form, O(L^2 N) per channel:
+
+    y_t = sum_{s<=t} sum_n C_t[n] (prod_{s<r<=t} Abar_r[n]) Bbar_s[n] x_s
+          + sum_n C_t[n] (prod_{r<=t} Abar_r[n]) h0[n] + D x_t
+    """
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    Ab = np.empty((Bsz, L, Dm, N))
+    Bb = np.empty((Bsz, L, Dm, N))
+    for b in range(Bsz):
+        for t in range(L):
+            for d in range(Dm):
+                for n in range(N):
+                    Ab[b, t, d, n], Bb[b, t, d, n] = vanloan_zoh(A[d, n], delta[b, t, d], B[b, t, n])
+    y = np.zeros((Bsz, L, Dm))
+    hf = np.zeros((Bsz, Dm, N))
+    for b in range(Bsz):
+        for d in range(Dm):
+            for n in range(N):
+                for t in range(L):
+                    # state h_t as an explicit sum over the inputs s <= t
+                    h_t = 0.0
+                    for s in range(t + 1):
+                        h_t += np.prod(Ab[b, s + 1:t + 1, d, n]) * Bb[b, s, d, n] * x[b, s, d]
+                    if h0 is not None:
+                        h_t += np.prod(Ab[b, 0:t + 1, d, n]) * h0[b, d, n]
+                    y[b, t, d] += C[b, t, n] * h_t
+                    if t == L - 1:
+                        hf[b, d, n] = h_t
+            for t in range(L):
+                y[b, t, d] += D[d] * x[b, t, d]
+    return y, hf
+
+
+def random_case(rng, Bsz, L, Dm, N, a_lo=-3.0, a_hi=-0.05):
+    x = rng.standard_normal((Bsz, L, Dm))
+    delta = np.exp(rng.uniform(np.log(1e-3), np.log(0.5), (Bsz, L, Dm)))
+    A = rng.uniform(a_lo, a_hi, (Dm, N))
+    B = rng.standard_normal((Bsz, L, N))
+    C = rng.standard_normal((Bsz, L, N))
+    D = rng.standard_normal(Dm)
+    return x, delta, A, B, C, D
+
+
+# ---------------------------------------------------------------------------
+# checks
+
+
+def check_golden(orc):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        A = np.array(c["A"], dtype=np.float64)
+        N = A.shape[1]
+        L = len(c["x"])
+        x = np.array(c["x"], dtype=np.float64).reshape(1, L, 1)
+        dl = np.array(c["delta"], dtype=np.float64).reshape(1, L, 1)
+        B = np.tile(np.array(c["B"], dtype=np.float64).reshape(1, 1, N), (1, L, 1))
+        C = np.tile(np.array(c["C"], dtype=np.float64).reshape(1, 1, N), (1, L, 1))
+        D = np.array(c["D"], dtype=np.float64)
+        y, hf = orc.scan(x, dl, A, B, C, D)
+        ey = np.array(c["y"], dtype=np.float64)
+        eh = np.array(c["h_final"], dtype=np.float64)
+        assert np.allclose(y.reshape(-1), ey, rtol=1e-13, atol=1e-14), (c["name"], y.reshape(-1), ey)
+        assert np.allclose(hf.reshape(-1), eh, rtol=1e-13, atol=1e-14), (c["name"], hf.reshape(-1), eh)
+
+
+def check_brute_force(orc, seed=0, with_h0=False):
+    rng = np.random.default_rng(seed)
+    x, delta, A, B, C, D = random_case(rng, 2, 9, 3, 4)
+    h0 = rng.standard_normal((2, 3, 4)) if with_h0 else None
+    y, hf = orc.scan(x, delta, A, B, C, D, h0=h0)
+    yb, hb = brute_force_scan(x, delta, A, B, C, D, h0=h0)
+    assert rel_err(y, yb) < 1e-11, rel_err(y, yb)
+    assert rel_err(hf, hb) < 1e-11, rel_err(hf, hb)
+
+
+def check_vanloan_step(orc):
+    """One step from h=0 with x=1, B=1 gives Bbar; from h=1 with x=0 gives Abar."""
+    a_vals = np.array([-20.0, -3.0, -1.0, -0.25, -1e-3, -1e-9, 0.0, 0.5])
+    d_vals = np.array([0.0, 1e-6, 1e-3, 0.05, 0.3, 1.0, 2.5])
+    Dm, Bsz = len(a_vals), len(d_vals)
+    # channel d has A = a_vals[d] (one state); batch row b uses delta = d_vals[b]
+    A = a_vals.reshape(Dm, 1)
+    x1 = np.ones((Bsz, Dm))
+    dl = np.tile(d_vals.reshape(Bsz, 1), (1, Dm))
+    ones = np.ones((Bsz, 1))
+    zeros = np.zeros((Bsz, 1))
+    _, hB = orc.step(x1, dl, A, ones, zeros, np.zeros(Dm), np.zeros((Bsz, Dm, 1)))
+    _, hA = orc.step(np.zeros((Bsz, Dm)), dl, A, ones, zeros, np.zeros(Dm), np.ones((Bsz, Dm, 1)))
+    for b in range(Bsz):
+        for d in range(Dm):
+            ea, eb = vanloan_zoh(a_vals[d], d_vals[b], 1.0)
+            assert abs(hA[b, d, 0] - ea) <= 1e-14 * max(1.0, abs(ea)), (a_vals[d], d_vals[b], hA[b, d, 0], ea)
+            assert abs(hB[b, d, 0] - eb) <= 1e-13 * abs(eb), (a_vals[d], d_vals[b], hB[b, d, 0], eb)
+
+
+def check_lti_convolution(orc, seed=1):
+    """Time-invariant delta, B, C: y = (K * x) + D x with K_k = sum_n C_n Abar_n^k Bbar_n;
+    also per state h_n = lfilter([Bbar_n], [1, -Abar_n], x)."""
+    rng = np.random.default_rng(seed)
+    L, Dm, N = 40, 3, 5
+    x = rng.standard_normal((1, L, Dm))
+    dch = np.exp(rng.uniform(np.log(1e-2), np.log(0.7), Dm))
+    delta = np.tile(dch.reshape(1, 1, Dm), (1, L, 1))
+    A = -np.exp(rng.uniform(-2, 1.5, (Dm, N)))
+    bvec = rng.standard_normal(N)
+    cvec = rng.standard_normal(N)
+    B = np.tile(bvec.reshape(1, 1, N), (1, L, 1))
+    C = np.tile(cvec.reshape(1, 1, N), (1, L, 1))
+    D = rng.standard_normal(Dm)
+    y, hf = orc.scan(x, delta, A, B, C, D)
+    for d in range(Dm):
+        ab = np.exp(dch[d] * A[d])
+        bb = np.array([vanloan_zoh(A[d, n], dch[d], bvec[n])[1] for n in range(N)])
+        K = np.array([np.sum(cvec * ab ** k * bb) for k in range(L)])
+        yc = np.array([np.sum(K[:t + 1][::-1] * x[0, :t + 1, d]) for t in range(L)]) + D[d] * x[0, :, d]
+        assert rel_err(y[0, :, d], yc) < 1e-12, rel_err(y[0, :, d], yc)
+        hs = np.stack([lfilter([bb[n]], [1.0, -ab[n]], x[0, :, d]) for n in range(N)], axis=1)
+        yl = hs @ cvec + D[d] * x[0, :, d]
+        assert rel_err(y[0, :, d], yl) < 1e-12
+        assert rel_err(hf[0, d], hs[-1]) < 1e-12
+
+
+def check_a_to_zero_limit(orc):
+    """Bbar -> delta*B as A -> 0 (error O(delta^2 |A|)); A == 0 gives delta*B exactly."""
+    dt, bval = 0.1, 1.7
+    prev = None
+    for k in range(3, 13):
+        a = -10.0 ** (-k)
+        _, h = orc.step(np.ones((1, 1)), np.full((1, 1), dt), np.full((1, 1), a), np.full((1, 1), bval),
+                        np.zeros((1, 1)), np.zeros(1), np.zeros((1, 1, 1)))
+        err = abs(h[0, 0, 0] - dt * bval)
+        bound = 0.5 * dt * dt * abs(a) * bval * 1.01 + 4e-16 * dt * bval
+        assert err <= bound, (k, err, bound)
+        if prev is not None and k <= 9:
+            assert err < prev, (k, err, prev)
+        prev = err
+    _, h = orc.step(np.ones((1, 1)), np.full((1, 1), dt), np.zeros((1, 1)), np.full((1, 1), bval),
+                    np.zeros((1, 1)), np.zeros(1), np.zeros((1, 1, 1)))
+    assert h[0, 0, 0] == dt * bval
+    _, h = orc.step(np.zeros((1, 1)), np.full((1, 1), dt), np.zeros((1, 1)), np.full((1, 1), bval),
+                    np.zeros((1, 1)), np.zeros(1), np.full((1, 1, 1), 0.37))
+    assert h[0, 0, 0] == 0.37
+
+
+def check_delta_zero_persistence(orc, seed=2):
+    """delta = 0 from t0 on: the state is held exactly and y_t = C_t h + D x_t."""
+    rng = np.random.default_rng(seed)
+    x, delta, A, B, C, D = random_case(rng, 2, 16, 3, 4)
+    t0 = 6
+    delta[:, t0:, :] = 0.0
+    y, hf = orc.scan(x, delta, A, B, C, D)
+    _, hpre = orc.scan(x[:, :t0], delta[:, :t0], A, B[:, :t0], C[:, :t0], D)
+    assert np.array_equal(hf, hpre)
+    ye = np.einsum("btn,bdn->btd", C[:, t0:], hpre) + D[None, None, :] * x[:, t0:]
+    assert rel_err(y[:, t0:], ye) < 1e-13
+
+
+def check_pure_decay(orc, seed=3):
+    """x = 0: h_L = exp(A * sum_t delta_t) h0 per state."""
+    rng = np.random.default_rng(seed)
+    Bsz, L, Dm, N = 2, 25, 3, 4
+    _, delta, A, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    h0 = rng.standard_normal((Bsz, Dm, N))
+    y, hf = orc.scan(np.zeros((Bsz, L, Dm)), delta, A, B, C, D, h0=h0)
+    tot = delta.sum(axis=1)  # [Bsz, Dm]
+    he = np.exp(tot[:, :, None] * A[None, :, :]) * h0
+    assert rel_err(hf, he) < 1e-12, rel_err(hf, he)
+
+
+def check_zoh_exact_for_constant_input(orc, seed=4):
+    """Constant x, delta, B and h0 = 0: h after k steps equals the ODE solution
+    at time k*delta, B x (exp(A k delta) - 1) / A, for every k."""
+    rng = np.random.default_rng(seed)
+    L, Dm, N = 12, 4, 3
+    xv = rng.standard_normal(Dm)
+    dv = rng.uniform(0.01, 0.4, Dm)
+    bv = rng.standard_normal(N)
+    A = -np.exp(rng.uniform(-1.5, 1.0, (Dm, N)))
+    x = np.tile(xv.reshape(1, 1, Dm), (1, L, 1))
+    delta = np.tile(dv.reshape(1, 1, Dm), (1, L, 1))
+    B = np.tile(bv.reshape(1, 1, N), (1, L, 1))
+    for n in range(N):
+        C = np.zeros((1, L, N))
+        C[..., n] = 1.0
+        y, _ = orc.scan(x, delta, A, B, C, np.zeros(Dm))
+        for k in range(1, L + 1):
+            exact = bv[n] * xv * np.expm1(A[:, n] * k * dv) / A[:, n]
+            assert rel_err(y[0, k - 1], exact) < 1e-12
+
+
+def check_linearity_causality_permutation(orc, seed=5):
+    rng = np.random.default_rng(seed)
+    Bsz, L, Dm, N = 3, 14, 5, 4
+    x1, delta, A, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    x2 = rng.standard_normal(x1.shape)
+    y1, h1 = orc.scan(x1, delta, A, B, C, D)
+    y2, h2 = orc.scan(x2, delta, A, B, C, D)
+    y12, h12 = orc.scan(2.0 * x1 - 0.5 * x2, delta, A, B, C, D)
+    assert rel_err(y12, 2.0 * y1 - 0.5 * y2) < 1e-11
+    assert rel_err(h12, 2.0 * h1 - 0.5 * h2) < 1e-11
+    # causality: perturbing x at t' leaves y_{t<t'} bitwise unchanged, changes y_{t'}
+    tp = 7
+    x3 = x1.copy()
+    x3[:, tp] += 1.0
+    y3, _ = orc.scan(x3, delta, A, B, C, D)
+    assert np.array_equal(y3[:, :tp], y1[:, :tp])
+    assert not np.array_equal(y3[:, tp], y1[:, tp])
+    # channel and batch permutations permute the outputs (channels are independent)
+    pd = rng.permutation(Dm)
+    pb = rng.permutation(Bsz)
+    yp, hp = orc.scan(x1[pb][:, :, pd], delta[pb][:, :, pd], A[pd], B[pb], C[pb], D[pd])
+    assert np.array_equal(yp, y1[pb][:, :, pd])
+    assert np.array_equal(hp, h1[pb][:, pd])
+
+
+def check_step_chain_matches_scan(orc, seed=6):
+    """Applying the step L times from h0 reproduces the scan's y and h_final
+    (recurrent mode, 'Mamba SSM Nedir?' section 'Ayrik Zamana Gecis')."""
+    rng = np.random.default_rng(seed)
+    Bsz, L, Dm, N = 2, 10, 3, 4
+    x, delta, A, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    h0 = rng.standard_normal((Bsz, Dm, N))
+    y, hf = orc.scan(x, delta, A, B, C, D, h0=h0)
+    h = h0
+    for t in range(L):
+        yt, h = orc.step(x[:, t], delta[:, t], A, B[:, t], C[:, t], D, h)
+        assert rel_err(yt, y[:, t]) < 1e-13
+    assert rel_err(h, hf) < 1e-13
+
+
+def check_split_scan_operator(orc, seed=7):
+    """The affine-map composition (a1,b1) o (a2,b2) = (a1 a2, a2 b1 + b2) used to
+    carry the state between time chunks: evaluating the scan in arbitrary chunks
+    and combining the chunk summaries reproduces the sequential oracle."""
+    rng = np.random.default_rng(seed)
+    Bsz, L, Dm, N = 1, 37, 2, 3
+    x, delta, A, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    _, hf = orc.scan(x, delta, A, B, C, D)
+    cuts = [0, 5, 6, 19, 31, L]
+    carry = np.zeros((Bsz, Dm, N))
+    for s, e in zip(cuts[:-1], cuts[1:]):
+        _, h_loc = orc.scan(x[:, s:e], delta[:, s:e], A, B[:, s:e], C[:, s:e], D)
+        decay = np.exp(delta[:, s:e].sum(axis=1)[:, :, None] * A[None])
+        carry = decay * carry + h_loc
+    assert rel_err(carry, hf) < 1e-12
+
+
+ALL_CHECKS = [
+    check_golden,
+    check_brute_force,
+    lambda o: check_brute_force(o, seed=11, with_h0=True),
+    check_vanloan_step,
+    check_lti_convolution,
+    check_a_to_zero_limit,
+    check_delta_zero_persistence,
+    check_pure_decay,
+    check_zoh_exact_for_constant_input,
+    check_linearity_causality_permutation,
+    check_step_chain_matches_scan,
+    check_split_scan_operator,
+]
