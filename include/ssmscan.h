@@ -1,0 +1,182 @@
+/*
+ * libssmscan -- selective state-space scan and recurrent decode step for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (pages: "Mamba SSM Nedir? Transformer Alternatifi Rehberi",
+ * yapayzekasozluk.tr, sections "State Space Model Temelleri", "Ayrik Zamana
+ * Gecis" and "Mamba'nin Yeniligi: Selective SSM"; and "Mamba: Transformer'a
+ * Meydan Okuyan Uzun-Bagimli Model", matematikkaravani.com, section "Eski
+ * fikrin geri donusu: durum uzayi"):
+ *
+ *   for every batch row b, channel d and state n, with a diagonal real A:
+ *     Abar   = exp(delta_t[d] * A[d,n])                       (zero-order hold)
+ *     Bbar   = (Abar - 1) / A[d,n] * B_t[n]    (limit delta_t[d]*B_t[n] at A=0)
+ *     h_t    = Abar * h_{t-1} + Bbar * x_t[d]
+ *     y_t[d] = sum_n C_t[n] * h_t[d,n] + D[d] * x_t[d]
+ *
+ * B_t, C_t and delta_t are per-token inputs (the selection mechanism computes
+ * them upstream); B_t and C_t are shared by all channels of a batch row.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, contiguous; there are no strides.
+ *   - Device pointers.  The caller owns every buffer; the library keeps no
+ *     pointer after the call returns.
+ *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t
+ *     passed as void*, NULL = the default stream) and the call returns.  The
+ *     caller synchronises.  Buffers must stay valid until the work completes.
+ *   - `dtype` (ssm_dtype) selects the storage type of x, delta, B, C and y.
+ *     A, D and the state (h_final, h) are always fp32.  Arithmetic is fp32.
+ *   - Return value: SSM_OK (0) or a positive ssm_status.  On an argument error
+ *     nothing is enqueued and no device call is made; ssm_last_error() gives
+ *     a thread-local description of the most recent failure.
+ *   - Preconditions that are documented, not checked: delta >= 0 and A <= 0
+ *     (a real part of A that is not negative lets the state grow; "Mamba SSM
+ *     Nedir?", section "Sinirliliklar ve Acik Sorular").  Non-finite inputs
+ *     propagate.
+ *   - A pointer may be NULL only when its tensor has no elements.
+ *   - Every pointer must be aligned to its element size.
+ *   - Supported state sizes: N in {1, 2, 4, 8, 16}.
+ *   - Thread safety: calls may come from several host threads.  Two calls that
+ *     run concurrently on different streams of one device use separate
+ *     library scratch memory (kept per device and stream).
+ *   - Library scratch memory (time-chunk summaries, converted B/C rows) is
+ *     allocated on first use per (device, stream), grows on demand, and is
+ *     kept until ssm_release_workspaces() or process exit.  Allocation
+ *     failure returns SSM_ERR_NOMEM.
+ */
+#ifndef SSMSCAN_H
+#define SSMSCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSM_F32 = 0,  /* IEEE binary32 */
+    SSM_BF16 = 1  /* bfloat16 (upper 16 bits of binary32); y is rounded to nearest even */
+} ssm_dtype;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULLPTR = 1,        /* a non-empty tensor has a NULL pointer */
+    SSM_ERR_BAD_DIM = 2,        /* a negative size, or a size whose byte count overflows */
+    SSM_ERR_BAD_DTYPE = 3,      /* dtype is not an ssm_dtype */
+    SSM_ERR_UNSUPPORTED_N = 4,  /* N not in {1, 2, 4, 8, 16} */
+    SSM_ERR_ALIGN = 5,          /* a pointer is not aligned to its element size */
+    SSM_ERR_ALIAS = 6,          /* an output overlaps an input or another output */
+    SSM_ERR_NOMEM = 7,          /* library scratch memory could not be allocated */
+    SSM_ERR_HIP = 8,            /* the HIP runtime reported an error (see ssm_last_error) */
+    SSM_ERR_BAD_OPTION = 9      /* unknown option id or value in ssm_set_option */
+} ssm_status;
+
+/*
+ * Full-sequence selective scan, zero initial state.
+ *
+ *   x, delta : [Bsz][L][Dm]   dtype          input sequence and step sizes
+ *   A        : [Dm][N]        fp32           diagonal state matrix per channel
+ *   B, C     : [Bsz][L][N]    dtype          per-token input/output projections
+ *   D        : [Dm]           fp32           feed-through
+ *   y        : [Bsz][L][Dm]   dtype  (out)   y_t as defined above
+ *   h_final  : [Bsz][Dm][N]   fp32   (out)   state after the last token; may be
+ *                                            NULL (then not written).  With L == 0
+ *                                            it is the zero initial state.
+ *
+ * y must not overlap any input; h_final must not overlap any input or y.
+ * Sizes of 0 are valid and do nothing beyond writing h_final.
+ * The scan is the recurrence above evaluated in parallel: channels are
+ * independent, and time is cut into chunks whose summaries are combined
+ * with the composition of affine maps (a1,b1) o (a2,b2) = (a1*a2, a2*b1 + b2)
+ * ("Mamba SSM Nedir?", section "Paralel Tarama Algoritmasi").  The result
+ * equals the sequential recurrence up to fp32 rounding.
+ */
+int ssm_scan_fwd(const void *x, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D,
+                 void *y, float *h_final,
+                 int64_t Bsz, int64_t L, int64_t Dm, int64_t N,
+                 int dtype, void *stream);
+
+/*
+ * Scan with an initial state (resumable prefill): as ssm_scan_fwd, but the
+ * recurrence starts from h_init [Bsz][Dm][N] fp32 instead of zero.  h_init may
+ * be NULL (zero state).  h_init may be the same buffer as h_final (the final
+ * state then overwrites the initial one); otherwise it must not overlap any
+ * output.  scan(L1+L2) equals scan(L2, h_init = h_final of scan(L1)) up to
+ * fp32 rounding.
+ */
+int ssm_scan_fwd_ex(const void *x, const void *delta, const float *A,
+                    const void *B, const void *C, const float *D,
+                    const float *h_init, void *y, float *h_final,
+                    int64_t Bsz, int64_t L, int64_t Dm, int64_t N,
+                    int dtype, void *stream);
+
+/*
+ * One recurrent decode step on a resident state, updated in place
+ * ("Mamba SSM Nedir?", section "Karmasiklik Karsilastirmasi": inference
+ * updates a fixed-size state per token).  bf16 I/O:
+ *
+ *   x, delta : [Bsz][Dm]     bf16
+ *   A        : [Dm][N]       fp32
+ *   B, C     : [Bsz][N]      bf16
+ *   D        : [Dm]          fp32
+ *   h        : [Bsz][Dm][N]  fp32   (in/out)  h <- Abar*h + Bbar*x
+ *   y        : [Bsz][Dm]     bf16   (out)     y = sum_n C[n]*h_new[n] + D*x
+ *
+ * y must not overlap any input or h; h must not overlap any input.
+ */
+int ssm_step(const void *x, const void *delta, const float *A,
+             const void *B, const void *C, const float *D,
+             float *h, void *y,
+             int64_t Bsz, int64_t Dm, int64_t N, void *stream);
+
+/* ssm_step with an explicit storage dtype for x, delta, B, C, y. */
+int ssm_step_ex(const void *x, const void *delta, const float *A,
+                const void *B, const void *C, const float *D,
+                float *h, void *y,
+                int64_t Bsz, int64_t Dm, int64_t N, int dtype, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *ssm_strerror(int code);
+
+/* Description of the most recent failure on the calling thread ("" if none). */
+const char *ssm_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int ssm_version(void);
+
+/*
+ * Tuning/diagnostic options (process-wide; they change how the work is cut,
+ * never what is computed):
+ *   SSM_OPT_SEGMENT_LEN  : time-chunk length of the scan; 0 = automatic
+ *                          (default).  Values < 0 are rejected.
+ *   SSM_OPT_FORCE_GENERAL: 1 = always take the general-A path, even when
+ *                          A[d,n] == (n+1)*A[d,0] would allow the structured
+ *                          one; 0 = automatic (default).
+ */
+typedef enum {
+    SSM_OPT_SEGMENT_LEN = 1,
+    SSM_OPT_FORCE_GENERAL = 2
+} ssm_option;
+
+int ssm_set_option(int option, int64_t value);
+int64_t ssm_get_option(int option);
+
+/*
+ * How ssm_scan_fwd would cut a problem: number of time segments and their
+ * length, for a device with `compute_units` CUs (0 = ask the current device).
+ * Returns SSM_OK or an argument error; makes no device call unless
+ * compute_units == 0.
+ */
+int ssm_scan_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
+                  int compute_units, int64_t *segments, int64_t *segment_len);
+
+/* Free all library scratch memory (all devices and streams).  The caller must
+ * make sure no library work is still running. */
+int ssm_release_workspaces(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSMSCAN_H */

@@ -1,0 +1,78 @@
+"""Build libssmscan.so (HIP, gfx950) in-tree with hipcc.
+
+    python -m selective_state_space_18_amd.build [-v] [--isa DIR]
+
+Objects go to ``_build/`` next to this file; the shared library is written to
+``libssmscan.so`` in the package directory, where the binding loads it.
+``--isa DIR`` additionally keeps the device assembly (for inspection).
+"""
+import argparse
+import os
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libssmscan.so")
+
+ARCH = "gfx950"
+SOURCES = ["abi.cpp", "scan_kernels.hip", "step_kernel.hip"]
+
+# Packed-FP32 instructions are switched off for every device pass.
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", CSRC, "-I", INCLUDE]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libssmscan)")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False, isa_dir: str = None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = [cc, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmds.append(cmd)
+        if isa_dir and src.endswith(".hip"):
+            os.makedirs(isa_dir, exist_ok=True)
+            asm = os.path.join(isa_dir, os.path.splitext(src)[0] + f"-{ARCH}.s")
+            cmds.append([cc, *COMMON, "-x", "hip", "--cuda-device-only", "-S",
+                         os.path.join(CSRC, src), "-o", asm])
+    with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("--isa", default=None)
+    a = ap.parse_args()
+    print(build(verbose=a.v, isa_dir=a.isa))

@@ -1,0 +1,445 @@
+// libssmscan C ABI: argument validation, work planning, scratch memory and
+// kernel dispatch.  Every argument check runs before the first HIP call, so
+// argument errors enqueue nothing and need no device.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "ssm_launch.h"
+#include "ssmscan.h"
+
+namespace {
+
+constexpr int kVersion = 10000;   // 1.0.0
+constexpr int kWavesPerBlock = 4;  // scan blocks: 4 independent 64-channel waves
+constexpr int64_t kMinSegment = 64;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return SSM_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(SSM_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+std::atomic<int64_t> g_opt_segment_len{0};
+std::atomic<int64_t> g_opt_force_general{0};
+
+bool supported_n(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// A tensor argument: pointer, element count, element size, name.
+struct Arg {
+    const void *p;
+    int64_t count;
+    int64_t esize;
+    const char *name;
+    uintptr_t lo() const { return reinterpret_cast<uintptr_t>(p); }
+    uintptr_t hi() const { return lo() + (uintptr_t)(count * esize); }
+};
+
+int check_args(const Arg *args, int n) {
+    for (int i = 0; i < n; ++i) {
+        const Arg &a = args[i];
+        int64_t bytes;
+        if (!mul_ok(a.count, a.esize, &bytes) || bytes > (INT64_MAX >> 2))
+            return fail(SSM_ERR_BAD_DIM, "%s: size overflows", a.name);
+        if (a.count > 0 && a.p == nullptr)
+            return fail(SSM_ERR_NULLPTR, "%s is NULL but has %lld elements", a.name, (long long)a.count);
+        if (a.p != nullptr && (a.lo() % (uintptr_t)a.esize) != 0)
+            return fail(SSM_ERR_ALIGN, "%s (%p) is not aligned to its %lld-byte element", a.name, a.p,
+                        (long long)a.esize);
+    }
+    return SSM_OK;
+}
+
+bool overlaps(const Arg &a, const Arg &b) {
+    if (a.count == 0 || b.count == 0 || a.p == nullptr || b.p == nullptr) return false;
+    return a.lo() < b.hi() && b.lo() < a.hi();
+}
+
+int check_output(const Arg &out, const Arg *others, int n) {
+    for (int i = 0; i < n; ++i)
+        if (overlaps(out, others[i]))
+            return fail(SSM_ERR_ALIAS, "%s overlaps %s", out.name, others[i].name);
+    return SSM_OK;
+}
+
+int64_t dtype_size(int dtype) { return dtype == SSM_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// Planning
+
+struct Plan {
+    int S;
+    int64_t seg_len;
+    int tiles_per_b;
+    int n_tiles;
+};
+
+// Time segments: enough 4-wave blocks to give every CU an equal whole number
+// (>= 4) of them when that is possible, with segments of at least kMinSegment
+// steps.  Channels are never split; only time is.
+Plan make_plan(int64_t Bsz, int64_t L, int64_t Dm, int cus) {
+    Plan pl;
+    pl.tiles_per_b = (int)((Dm + 63) / 64);
+    pl.n_tiles = (int)(Bsz * pl.tiles_per_b);
+    const int64_t bps = (pl.n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    int64_t S = 1;
+    const int64_t forced = g_opt_segment_len.load();
+    if (L <= 0 || bps == 0) {
+        S = 1;
+    } else if (forced > 0) {
+        // keep the grid (segments x blocks per segment) within 2^30 blocks
+        const int64_t max_seg = ((int64_t)1 << 30) / (bps > 0 ? bps : 1);
+        int64_t sl = forced < L ? forced : L;
+        if ((L + sl - 1) / sl > max_seg) sl = (L + max_seg - 1) / max_seg;
+        pl.seg_len = sl;
+        pl.S = (int)((L + sl - 1) / sl);
+        return pl;
+    } else {
+        const int64_t cap = L / kMinSegment > 1 ? L / kMinSegment : 1;
+        const int64_t c = cus > 0 ? cus : 256;
+        S = (4 * c + bps - 1) / bps;  // fallback: at least 4 blocks per CU
+        for (int64_t m = 4; m <= 8; ++m) {
+            if ((m * c) % bps == 0) {
+                S = m * c / bps;
+                break;
+            }
+        }
+        if (S > cap) S = cap;
+        if (S < 1) S = 1;
+    }
+    pl.seg_len = L > 0 ? (L + S - 1) / S : 1;
+    pl.S = L > 0 ? (int)((L + pl.seg_len - 1) / pl.seg_len) : 1;
+    return pl;
+}
+
+std::mutex g_dev_mu;
+std::map<int, int> g_cus;
+
+int device_cus(int dev, int *cus) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    auto it = g_cus.find(dev);
+    if (it != g_cus.end()) {
+        *cus = it->second;
+        return SSM_OK;
+    }
+    int v = 0;
+    hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    g_cus[dev] = v;
+    *cus = v;
+    return SSM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch memory, one growable buffer per (device, stream).  The lock is held
+// for the whole enqueue so that a concurrent growth on the same stream cannot
+// free a buffer that is about to be handed to a kernel.
+
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+int workspace(int dev, hipStream_t s, size_t need, void **out) {
+    Workspace &w = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
+    if (w.bytes >= need) {
+        *out = w.ptr;
+        return SSM_OK;
+    }
+    if (w.ptr != nullptr) {
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize before growing scratch");
+        e = hipFree(w.ptr);
+        w.ptr = nullptr;
+        w.bytes = 0;
+        if (e != hipSuccess) return hip_fail(e, "hipFree(scratch)");
+    }
+    const size_t gran = (size_t)2 << 20;
+    const size_t bytes = (need + gran - 1) / gran * gran;
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return fail(SSM_ERR_NOMEM, "hipMalloc(%zu) for scratch failed: %s", bytes, hipGetErrorString(e));
+    }
+    w.ptr = p;
+    w.bytes = bytes;
+    *out = p;
+    return SSM_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+
+int scan_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
+              const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
+              int64_t Dm, int64_t N, int dtype, void *stream) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
+    if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
+    if (Bsz < 0 || L < 0 || Dm < 0)
+        return fail(SSM_ERR_BAD_DIM, "negative size (Bsz=%lld, L=%lld, Dm=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm);
+    int64_t BL, BLD, BLN, DN, BD, BDN;
+    if (!mul_ok(Bsz, L, &BL) || !mul_ok(BL, Dm, &BLD) || !mul_ok(BL, N, &BLN) || !mul_ok(Dm, N, &DN) ||
+        !mul_ok(Bsz, Dm, &BD) || !mul_ok(BD, N, &BDN) || BD > INT32_MAX / 2 || Bsz * ((Dm + 63) / 64) > INT32_MAX / 8)
+        return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm, (long long)N);
+    const int64_t es = dtype_size(dtype);
+    const Arg in[] = {{x, BLD, es, "x"}, {delta, BLD, es, "delta"}, {A, DN, 4, "A"}, {B, BLN, es, "B"},
+                      {C, BLN, es, "C"}, {D, Dm, 4, "D"}};
+    const Arg hi = {h_init, h_init ? BDN : 0, 4, "h_init"};
+    const Arg ya = {y, BLD, es, "y"};
+    const Arg hf = {h_final, h_final ? BDN : 0, 4, "h_final"};
+    int rc;
+    if ((rc = check_args(in, 6)) || (rc = check_args(&hi, 1)) || (rc = check_args(&ya, 1)) ||
+        (rc = check_args(&hf, 1)))
+        return rc;
+    if ((rc = check_output(ya, in, 6)) || (rc = check_output(ya, &hi, 1)) || (rc = check_output(hf, in, 6)) ||
+        (rc = check_output(hf, &ya, 1)))
+        return rc;
+    if (h_init != nullptr && h_final != nullptr && (const void *)h_init != (const void *)h_final &&
+        overlaps(hi, hf))
+        return fail(SSM_ERR_ALIAS, "h_init partially overlaps h_final");
+
+    if (BD == 0) return ok();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    ssm::ScanParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x = x;
+    p.delta = delta;
+    p.B = B;
+    p.C = C;
+    p.A = A;
+    p.D = D;
+    p.h_init = h_init;
+    p.y = y;
+    p.h_final = h_final;
+    p.Bsz = Bsz;
+    p.L = L;
+    p.Dm = Dm;
+    p.waves_per_block = kWavesPerBlock;
+    p.force_general = g_opt_force_general.load() ? 1 : 0;
+
+    hipError_t e;
+    if (L == 0) {
+        p.S = 1;
+        e = ssm::launch_state_init(p, (int)N, s);
+        return e == hipSuccess ? ok() : hip_fail(e, "state init launch");
+    }
+
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int cus = 0;
+    if ((rc = device_cus(dev, &cus))) return rc;
+    const Plan pl = make_plan(Bsz, L, Dm, cus);
+    p.S = pl.S;
+    p.seg_len = pl.seg_len;
+    p.tiles_per_b = pl.tiles_per_b;
+    p.n_tiles = pl.n_tiles;
+
+    const size_t acc = ssm::scan_acc_bytes(dtype);
+    const size_t bc_bytes = align256((size_t)BL * 2 * N * acc);
+    const size_t agg_bytes = pl.S > 1 ? align256((size_t)(pl.S - 1) * (N + 1) * BD * acc) : 0;
+    const size_t gin_bytes = pl.S > 1 ? align256((size_t)pl.S * N * BD * acc) : 0;
+
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    void *ws = nullptr;
+    if ((rc = workspace(dev, s, bc_bytes + agg_bytes + gin_bytes, &ws))) return rc;
+    char *base = static_cast<char *>(ws);
+    p.bc = base;
+    p.agg = agg_bytes ? base + bc_bytes : nullptr;
+    p.gin = gin_bytes ? base + bc_bytes + agg_bytes : nullptr;
+
+    if ((e = ssm::launch_bc_prep(p, (int)N, dtype, s)) != hipSuccess) return hip_fail(e, "B/C prep launch");
+    if (pl.S > 1) {
+        if ((e = ssm::launch_scan_aggregate(p, (int)N, dtype, s)) != hipSuccess)
+            return hip_fail(e, "segment aggregate launch");
+        if ((e = ssm::launch_scan_carry(p, (int)N, dtype, s)) != hipSuccess)
+            return hip_fail(e, "segment carry launch");
+    }
+    if ((e = ssm::launch_scan_output(p, (int)N, dtype, s)) != hipSuccess)
+        return hip_fail(e, "segment output launch");
+    return ok();
+}
+
+int step_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
+              const float *D, float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
+              void *stream) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
+    if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
+    if (Bsz < 0 || Dm < 0)
+        return fail(SSM_ERR_BAD_DIM, "negative size (Bsz=%lld, Dm=%lld)", (long long)Bsz, (long long)Dm);
+    int64_t BD, BN, DN, BDN;
+    if (!mul_ok(Bsz, Dm, &BD) || !mul_ok(Bsz, N, &BN) || !mul_ok(Dm, N, &DN) || !mul_ok(BD, N, &BDN) ||
+        BDN > INT64_MAX / 64)
+        return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, Dm=%lld, N=%lld)", (long long)Bsz, (long long)Dm,
+                    (long long)N);
+    const int64_t es = dtype_size(dtype);
+    const Arg in[] = {{x, BD, es, "x"}, {delta, BD, es, "delta"}, {A, DN, 4, "A"},
+                      {B, BN, es, "B"}, {C, BN, es, "C"}, {D, Dm, 4, "D"}};
+    const Arg ha = {h, BDN, 4, "h"};
+    const Arg ya = {y, BD, es, "y"};
+    int rc;
+    if ((rc = check_args(in, 6)) || (rc = check_args(&ha, 1)) || (rc = check_args(&ya, 1))) return rc;
+    if ((rc = check_output(ha, in, 6)) || (rc = check_output(ya, in, 6)) || (rc = check_output(ya, &ha, 1)))
+        return rc;
+    if (BD == 0) return ok();
+    ssm::StepParams p;
+    p.x = x;
+    p.delta = delta;
+    p.B = B;
+    p.C = C;
+    p.A = A;
+    p.D = D;
+    p.h = h;
+    p.y = y;
+    p.Bsz = Bsz;
+    p.Dm = Dm;
+    hipError_t e = ssm::launch_step(p, (int)N, dtype, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "decode step launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, void *y, float *h_final, int64_t Bsz, int64_t L, int64_t Dm, int64_t N,
+                 int dtype, void *stream) {
+    return scan_impl(x, delta, A, B, C, D, nullptr, y, h_final, Bsz, L, Dm, N, dtype, stream);
+}
+
+int ssm_scan_fwd_ex(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                    const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
+                    int64_t Dm, int64_t N, int dtype, void *stream) {
+    return scan_impl(x, delta, A, B, C, D, h_init, y, h_final, Bsz, L, Dm, N, dtype, stream);
+}
+
+int ssm_step(const void *x, const void *delta, const float *A, const void *B, const void *C,
+             const float *D, float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, void *stream) {
+    return step_impl(x, delta, A, B, C, D, h, y, Bsz, Dm, N, SSM_BF16, stream);
+}
+
+int ssm_step_ex(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                const float *D, float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
+                void *stream) {
+    return step_impl(x, delta, A, B, C, D, h, y, Bsz, Dm, N, dtype, stream);
+}
+
+const char *ssm_strerror(int code) {
+    switch (code) {
+        case SSM_OK: return "success";
+        case SSM_ERR_NULLPTR: return "a non-empty tensor has a NULL pointer";
+        case SSM_ERR_BAD_DIM: return "invalid or overflowing size";
+        case SSM_ERR_BAD_DTYPE: return "unsupported dtype";
+        case SSM_ERR_UNSUPPORTED_N: return "unsupported state size N";
+        case SSM_ERR_ALIGN: return "pointer not aligned to its element size";
+        case SSM_ERR_ALIAS: return "an output overlaps another argument";
+        case SSM_ERR_NOMEM: return "scratch allocation failed";
+        case SSM_ERR_HIP: return "HIP runtime error";
+        case SSM_ERR_BAD_OPTION: return "unknown option or invalid option value";
+        default: return "unknown status code";
+    }
+}
+
+const char *ssm_last_error(void) { return g_last_error.c_str(); }
+
+int ssm_version(void) { return kVersion; }
+
+int ssm_set_option(int option, int64_t value) {
+    switch (option) {
+        case SSM_OPT_SEGMENT_LEN:
+            if (value < 0) return fail(SSM_ERR_BAD_OPTION, "segment length %lld < 0", (long long)value);
+            g_opt_segment_len.store(value);
+            return ok();
+        case SSM_OPT_FORCE_GENERAL:
+            if (value != 0 && value != 1) return fail(SSM_ERR_BAD_OPTION, "force-general must be 0 or 1");
+            g_opt_force_general.store(value);
+            return ok();
+        default:
+            return fail(SSM_ERR_BAD_OPTION, "unknown option %d", option);
+    }
+}
+
+int64_t ssm_get_option(int option) {
+    switch (option) {
+        case SSM_OPT_SEGMENT_LEN: return g_opt_segment_len.load();
+        case SSM_OPT_FORCE_GENERAL: return g_opt_force_general.load();
+        default: return -1;
+    }
+}
+
+int ssm_scan_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, int compute_units,
+                  int64_t *segments, int64_t *segment_len) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d", dtype);
+    if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld", (long long)N);
+    if (Bsz < 0 || L < 0 || Dm < 0) return fail(SSM_ERR_BAD_DIM, "negative size");
+    if (segments == nullptr || segment_len == nullptr) return fail(SSM_ERR_NULLPTR, "output pointer is NULL");
+    int cus = compute_units;
+    if (cus <= 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        int rc = device_cus(dev, &cus);
+        if (rc) return rc;
+    }
+    const Plan pl = make_plan(Bsz, L, Dm, cus);
+    *segments = pl.S;
+    *segment_len = pl.seg_len;
+    return ok();
+}
+
+int ssm_release_workspaces(void) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int rc = SSM_OK;
+    for (auto &kv : g_ws) {
+        if (kv.second.ptr == nullptr) continue;
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first.first) == hipSuccess) {
+            hipError_t e = hipFree(kv.second.ptr);
+            if (e != hipSuccess) rc = hip_fail(e, "hipFree(scratch)");
+            (void)hipSetDevice(cur);
+        }
+        kv.second.ptr = nullptr;
+        kv.second.bytes = 0;
+    }
+    g_ws.clear();
+    return rc == SSM_OK ? ok() : rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,390 @@
+// Selective-scan kernels for gfx950 (CDNA4, wave64).
+//
+// What is computed ("Mamba SSM Nedir?" page, sections "Ayrik Zamana Gecis"
+// and "State Space Model Temelleri"): per batch row b, channel d, state n,
+//   Abar = exp(delta_t A),  Bbar = (Abar - 1)/A * B_t[n],
+//   h_t = Abar h_{t-1} + Bbar x_t,   y_t = sum_n C_t[n] h_t + D x_t.
+//
+// Layout of the work
+//   * One lane owns one (b, d) channel and keeps all N states in VGPRs for the
+//     whole time segment; the expanded [B, L, D, N] state never leaves the
+//     register file (the pages' kernel keeps it in on-chip memory too).
+//   * A wave covers 64 consecutive channels of one batch row, so B_t and C_t
+//     are wave-uniform: they are read with scalar loads into SGPRs and enter
+//     every FMA as the SGPR operand, costing no vector instructions.
+//   * x_t, delta_t are read per lane (64 lanes = 128 contiguous bytes in bf16)
+//     a few steps ahead, and y_t is written the same way.
+//   * Time is cut into S segments so that the chip has enough waves.  The
+//     segments are tied together with the composition of affine maps
+//     (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) -- the parallel prefix scan of
+//     section "Paralel Tarama Algoritmasi" -- in three passes:
+//       1. aggregate: every segment but the last runs from a zero state and
+//          stores its end state and the sum of its delta;
+//       2. carry: per (channel, state), a short sequential scan over segments
+//          gives the state entering each segment;
+//       3. output: every segment reruns from its true entering state and
+//          writes y (and h_final for the last one).
+//
+// State representation.  Lanes carry g_n = (n+1) h_n.  Then
+//   g_n <- g_n + E_n (g_n + B_t[n] x_t (n+1)/A_n),   E_n = exp(delta A_n) - 1,
+//   y_t  = sum_n (C_t[n]/(n+1)) g_n + D x_t,
+// which is the recurrence above rewritten (Abar h + (Abar-1)/A B x
+// = h + (Abar-1)(h + B x / A)).  When A[d, n] == (n+1) A[d, 0] for every n
+// (the S4D-real structure) the factor (n+1)/A_n is the per-channel constant
+// 1/A[d,0] and E_{n+1} = (1 + E_n)(1 + E_1) - 1: one transcendental per
+// (t, d) and four FMAs per state element.  Any other A takes the general path
+// with one exp per state element.
+//
+// Arithmetic: fp32 for bf16 storage; fp64 for fp32 storage (see AccOf).
+#include "ssm_device.h"
+#include "ssm_launch.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kPrefetch = 4;  // time steps of x/delta loaded ahead of use
+
+// ---------------------------------------------------------------------------
+// B/C rows -> arithmetic type, C pre-divided by (n+1) for the scaled state.
+
+template <typename T, int N>
+__global__ __launch_bounds__(kBlock) void bc_prep_kernel(const T *__restrict__ B,
+                                                         const T *__restrict__ C,
+                                                         typename AccOf<T>::type *__restrict__ bc,
+                                                         int64_t rows) {
+    typedef typename AccOf<T>::type Acc;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= rows * N) return;
+    const int64_t r = i / N;
+    const int n = (int)(i - r * N);
+    bc[r * (2 * N) + n] = (Acc)to_f32(B[i]);
+    bc[r * (2 * N) + N + n] = (Acc)to_f32(C[i]) / (Acc)(n + 1);
+}
+
+// ---------------------------------------------------------------------------
+// One time segment of one 64-channel tile.
+
+template <typename T>
+struct Stream {
+    const T *__restrict__ x;
+    const T *__restrict__ dl;
+    T *__restrict__ y;
+    int64_t stride;
+};
+
+// Per-channel constants of the two update paths.
+template <int N, bool kStruct, typename Acc>
+struct ChanConst {
+    Acc a0, inva;       // structured: A[d,0] and 1/A[d,0]
+    Acc Aeff[N], W[N];  // general: A (tiny stand-in for ~0) and (n+1)/A
+    __device__ __forceinline__ explicit ChanConst(const float (&Ar)[N]) {
+        a0 = (Acc)Ar[0];
+        inva = 0;
+        if constexpr (kStruct) {
+            inva = (Acc)1 / a0;
+        } else {
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                Aeff[n] = (__builtin_fabsf(Ar[n]) < -kTinyA) ? (Acc)kTinyA : (Acc)Ar[n];
+                W[n] = (Acc)(n + 1) / Aeff[n];
+            }
+        }
+    }
+};
+
+// One time step of one channel: updates the scaled state g and returns
+// sum_n (C_t[n]/(n+1)) g_n (kOut) -- D x is added by the caller.
+// row = {B_t[0..N), C_t[0..N)/(n+1)}, wave-uniform.
+template <int N, bool kStruct, bool kOut, typename Acc>
+__device__ __forceinline__ Acc scan_step(const ChanConst<N, kStruct, Acc> &cc, const Acc (&row)[2 * N],
+                                         Acc xv, Acc dv, Acc (&g)[N]) {
+    Acc yv = 0;
+    if constexpr (kStruct) {
+        Acc r;
+        const Acc E1 = expm1_and_exp(dv * cc.a0, r);
+        const Acc xa = xv * cc.inva;
+        Acc E = E1;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const Acc tt = fma_(row[n], xa, g[n]);
+            g[n] = fma_(E, tt, g[n]);
+            if constexpr (kOut) yv = fma_(row[N + n], g[n], yv);
+            // E_{n+1} = (1 + E_n)(1 + E_1) - 1.  fp32 uses the one-FMA form
+            // with r = exp(delta A[d,0]); fp64 keeps E_1 unrounded
+            // (E_n + E_1 + E_n E_1).
+            if (n + 1 < N) {
+                if constexpr (sizeof(Acc) == 8)
+                    E = fma_(E, E1, E + E1);
+                else
+                    E = fma_(E, r, E1);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            Acc e;
+            const Acc E = expm1_and_exp(dv * cc.Aeff[n], e);
+            const Acc tt = fma_(row[n], xv * cc.W[n], g[n]);
+            g[n] = fma_(E, tt, g[n]);
+            if constexpr (kOut) yv = fma_(row[N + n], g[n], yv);
+        }
+    }
+    return yv;
+}
+
+template <int N, typename Acc>
+__device__ __forceinline__ void load_row(Acc (&dst)[2 * N], const Acc *__restrict__ src) {
+#pragma unroll
+    for (int i = 0; i < 2 * N; ++i) dst[i] = src[i];
+}
+
+// Runs `nsteps` (>= 1) time steps of one segment.  x/delta are fetched
+// kPrefetch steps ahead with unconditional loads (indices clamped into the
+// segment, so no load is ever out of range) and widened only when used; the
+// B/C row of the next step is fetched while the current one is computed.
+// Idle lanes of a partial tile shadow a valid channel: they compute exactly
+// what that channel's lane computes and store the identical value.
+template <typename T, int N, bool kStruct, bool kOut, typename Acc>
+__device__ __forceinline__ void run_segment(const Stream<T> io, const Acc *__restrict__ bcp,
+                                            int64_t nsteps, const float (&Ar)[N], Acc Dd,
+                                            Acc (&g)[N], Acc &lam) {
+    const ChanConst<N, kStruct, Acc> cc(Ar);
+    const int64_t stride = io.stride;
+    const int64_t last = nsteps - 1;
+
+    T xr[kPrefetch], dr[kPrefetch];
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+        const int64_t i = (k < last ? k : last) * stride;
+        xr[k] = io.x[i];
+        dr[k] = io.dl[i];
+    }
+    Acc rowc[2 * N], rown[2 * N];
+    load_row<N>(rowc, bcp);
+
+    for (int64_t tb = 0; tb < nsteps; tb += kPrefetch) {
+        T xc[kPrefetch], dc[kPrefetch];
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) {
+            xc[k] = xr[k];
+            dc[k] = dr[k];
+            const int64_t t = tb + kPrefetch + k;
+            const int64_t i = (t < last ? t : last) * stride;
+            xr[k] = io.x[i];
+            dr[k] = io.dl[i];
+        }
+        const bool full = tb + kPrefetch <= nsteps;
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) {
+            if (full || tb + k < nsteps) {
+                const int64_t tn = tb + k + 1;
+                load_row<N>(rown, bcp + (tn < last ? tn : last) * (2 * N));
+                const Acc xv = (Acc)to_f32(xc[k]);
+                const Acc dv = (Acc)to_f32(dc[k]);
+                const Acc yv = scan_step<N, kStruct, kOut>(cc, rowc, xv, dv, g);
+                if constexpr (kOut) {
+                    io.y[(tb + k) * stride] = from_acc<T>(fma_(Dd, xv, yv));
+                } else {
+                    lam += dv;
+                }
+#pragma unroll
+                for (int i = 0; i < 2 * N; ++i) rowc[i] = rown[i];
+            }
+        }
+    }
+}
+
+// kOut = false: aggregate pass over segments 0..S-2.
+// kOut = true : output pass over segments 0..S-1.
+template <typename T, int N, bool kOut>
+__global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
+    typedef typename AccOf<T>::type Acc;
+    const int blocks_per_seg = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int s = lb / blocks_per_seg;
+    const int wave = uniform((int)threadIdx.x / kWave);
+    const int tile = (lb - s * blocks_per_seg) * p.waves_per_block + wave;
+    if (wave >= p.waves_per_block || tile >= p.n_tiles) return;
+    const int lane = threadIdx.x & (kWave - 1);
+
+    const int64_t b = tile / p.tiles_per_b;
+    const int64_t d0 = (int64_t)(tile - b * p.tiles_per_b) * kWave;
+    const bool active = d0 + lane < p.Dm;
+    const int64_t d = active ? d0 + lane : d0;  // idle lanes shadow a valid channel
+    const int64_t ch = b * p.Dm + d;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t t0 = (int64_t)s * p.seg_len;
+    const int64_t t1 = (t0 + p.seg_len < p.L) ? t0 + p.seg_len : p.L;
+
+    float Ar[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Ar[n] = p.A[d * N + n];
+    bool st = (Ar[0] != 0.f) && (p.force_general == 0);
+#pragma unroll
+    for (int n = 1; n < N; ++n) st = st && (Ar[n] == (float)(n + 1) * Ar[0]);
+    const bool wave_struct = __all(st);
+    const Acc Dd = (Acc)p.D[d];
+
+    // Entering state: from the carry pass when time is split (it also holds
+    // segment 0's, so h_init is never read here while the last segment may be
+    // writing h_final into the same buffer); else h_init read by this lane.
+    const Acc *gin = static_cast<const Acc *>(p.gin);
+    Acc g[N];
+    if (kOut && p.S > 1) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) g[n] = gin[((int64_t)s * N + n) * BD + ch];
+    } else if (kOut && p.h_init != nullptr) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) g[n] = (Acc)p.h_init[ch * N + n] * (Acc)(n + 1);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) g[n] = 0;
+    }
+
+    const int64_t off = (b * p.L + t0) * p.Dm + d;
+    Stream<T> io;
+    io.x = static_cast<const T *>(p.x) + off;
+    io.dl = static_cast<const T *>(p.delta) + off;
+    io.y = kOut ? static_cast<T *>(p.y) + off : nullptr;
+    io.stride = p.Dm;
+    const Acc *bcp = static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N);
+    Acc lam = 0;
+
+    if (wave_struct)
+        run_segment<T, N, true, kOut>(io, bcp, t1 - t0, Ar, Dd, g, lam);
+    else
+        run_segment<T, N, false, kOut>(io, bcp, t1 - t0, Ar, Dd, g, lam);
+
+    if (!active) return;
+    if constexpr (!kOut) {
+        Acc *a = static_cast<Acc *>(p.agg) + (int64_t)s * (N + 1) * BD + ch;
+#pragma unroll
+        for (int n = 0; n < N; ++n) a[(int64_t)n * BD] = g[n];
+        a[(int64_t)N * BD] = lam;
+    } else {
+        if (s == p.S - 1 && p.h_final != nullptr) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) p.h_final[ch * N + n] = (float)(g[n] / (Acc)(n + 1));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Carry between segments: one thread per (state n, channel).  Entering state
+// of segment s+1 = exp(A_n * sum(delta over s)) * entering state of s + local
+// end state of s; segment 0 enters with h_init (or zero).
+
+template <typename Acc, int N>
+__global__ __launch_bounds__(kBlock) void scan_carry_kernel(ScanParams p) {
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= BD * N) return;
+    const int n = (int)(i / BD);
+    const int64_t ch = i - (int64_t)n * BD;
+    const int64_t d = ch % p.Dm;
+    const Acc a = (Acc)p.A[d * N + n];
+    Acc carry = p.h_init ? (Acc)p.h_init[ch * N + n] * (Acc)(n + 1) : (Acc)0;
+    const Acc *agg = static_cast<const Acc *>(p.agg);
+    const Acc *lam = agg + (int64_t)N * BD + ch;
+    const Acc *gl = agg + (int64_t)n * BD + ch;
+    Acc *out = static_cast<Acc *>(p.gin) + (int64_t)n * BD + ch;
+    const int64_t sa = (int64_t)(N + 1) * BD, sg = (int64_t)N * BD;
+    out[0] = carry;
+#pragma unroll 4
+    for (int s = 0; s < p.S - 1; ++s) {
+        carry = fma_(exp_(a * lam[s * sa]), carry, gl[s * sa]);
+        out[(s + 1) * sg] = carry;
+    }
+}
+
+// h_final for an empty sequence: the initial state.
+__global__ __launch_bounds__(kBlock) void state_init_kernel(const float *__restrict__ h_init,
+                                                            float *__restrict__ h_final,
+                                                            int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < count) h_final[i] = h_init ? h_init[i] : 0.f;
+}
+
+template <typename T, int N>
+struct ByN {
+    typedef typename AccOf<T>::type Acc;
+    static hipError_t prep(const ScanParams &p, hipStream_t s) {
+        const int64_t rows = p.Bsz * p.L;
+        const int64_t work = rows * N;
+        if (work == 0) return hipSuccess;
+        const unsigned grid = (unsigned)((work + kBlock - 1) / kBlock);
+        hipLaunchKernelGGL((bc_prep_kernel<T, N>), dim3(grid), dim3(kBlock), 0, s,
+                           static_cast<const T *>(p.B), static_cast<const T *>(p.C),
+                           static_cast<Acc *>(p.bc), rows);
+        return hipGetLastError();
+    }
+    static hipError_t segments(const ScanParams &p, bool out, hipStream_t s) {
+        const int bps = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
+        const int nseg = out ? p.S : p.S - 1;
+        if (nseg <= 0 || bps == 0) return hipSuccess;
+        const unsigned grid = (unsigned)bps * (unsigned)nseg;
+        if (out)
+            hipLaunchKernelGGL((scan_segment_kernel<T, N, true>), dim3(grid), dim3(kBlock), 0, s, p);
+        else
+            hipLaunchKernelGGL((scan_segment_kernel<T, N, false>), dim3(grid), dim3(kBlock), 0, s, p);
+        return hipGetLastError();
+    }
+    static hipError_t carry(const ScanParams &p, hipStream_t s) {
+        const int64_t work = p.Bsz * p.Dm * N;
+        if (work == 0 || p.S <= 1) return hipSuccess;
+        const unsigned grid = (unsigned)((work + kBlock - 1) / kBlock);
+        hipLaunchKernelGGL((scan_carry_kernel<Acc, N>), dim3(grid), dim3(kBlock), 0, s, p);
+        return hipGetLastError();
+    }
+};
+
+template <typename T, typename F>
+hipError_t with_n(int N, F f) {
+    switch (N) {
+        case 1: return f(ByN<T, 1>());
+        case 2: return f(ByN<T, 2>());
+        case 4: return f(ByN<T, 4>());
+        case 8: return f(ByN<T, 8>());
+        case 16: return f(ByN<T, 16>());
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename F>
+hipError_t with_type(int N, int dtype, F f) {
+    if (dtype == 0) return with_n<float>(N, f);
+    if (dtype == 1) return with_n<bf16>(N, f);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t scan_acc_bytes(int dtype) { return dtype == 0 ? sizeof(double) : sizeof(float); }
+
+hipError_t launch_bc_prep(const ScanParams &p, int N, int dtype, hipStream_t s) {
+    return with_type(N, dtype, [&](auto k) { return decltype(k)::prep(p, s); });
+}
+
+hipError_t launch_scan_aggregate(const ScanParams &p, int N, int dtype, hipStream_t s) {
+    return with_type(N, dtype, [&](auto k) { return decltype(k)::segments(p, false, s); });
+}
+
+hipError_t launch_scan_carry(const ScanParams &p, int N, int dtype, hipStream_t s) {
+    return with_type(N, dtype, [&](auto k) { return decltype(k)::carry(p, s); });
+}
+
+hipError_t launch_scan_output(const ScanParams &p, int N, int dtype, hipStream_t s) {
+    return with_type(N, dtype, [&](auto k) { return decltype(k)::segments(p, true, s); });
+}
+
+hipError_t launch_state_init(const ScanParams &p, int N, hipStream_t s) {
+    const int64_t count = p.Bsz * p.Dm * N;
+    if (count == 0 || p.h_final == nullptr) return hipSuccess;
+    const unsigned grid = (unsigned)((count + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(state_init_kernel, dim3(grid), dim3(kBlock), 0, s, p.h_init, p.h_final, count);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the libssmscan kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Stand-in used for |A| < 1e-20 (A == 0 included) in the general-A path: the
+// ZOH input coefficient (exp(z)-1)/A then evaluates to its A -> 0 limit delta
+// (z = delta*A is tiny and expm1 is accurate there), and 1/A stays finite.
+constexpr float kTinyA = -1e-20f;
+
+typedef __bf16 bf16;
+
+// Arithmetic type per storage type.  bf16 storage: fp32 state and arithmetic.
+// fp32 storage: fp64 state and arithmetic (CDNA4 issues fp64 FMA at the
+// non-packed fp32 rate), rounded to fp32 only when written out.
+template <typename T>
+struct AccOf;
+template <>
+struct AccOf<bf16> {
+    typedef float type;
+};
+template <>
+struct AccOf<float> {
+    typedef double type;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+
+template <typename T>
+__device__ __forceinline__ T from_acc(float v);
+template <typename T>
+__device__ __forceinline__ T from_acc(double v);
+template <>
+__device__ __forceinline__ float from_acc<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float from_acc<float>(double v) { return static_cast<float>(v); }
+// v_cvt_pk_bf16_f32: round to nearest even
+template <>
+__device__ __forceinline__ bf16 from_acc<bf16>(float v) { return static_cast<bf16>(v); }
+template <>
+__device__ __forceinline__ bf16 from_acc<bf16>(double v) { return static_cast<bf16>(static_cast<float>(v)); }
+
+__device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_(double a, double b, double c) { return __builtin_fma(a, b, c); }
+__device__ __forceinline__ float abs_(float a) { return __builtin_fabsf(a); }
+__device__ __forceinline__ double abs_(double a) { return __builtin_fabs(a); }
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp(z) - 1, also returning exp(z) in `e`.
+//  fp64: ocml expm1 / exp.
+//  fp32: exp2 on the transcendental unit, and for |z| < 2^-6 the cubic Taylor
+//        polynomial z(1 + z/2 + z^2/6), whose truncation error there is below
+//        z^4/24 (relative 2e-7).  This keeps the ZOH input coefficient
+//        (exp(z)-1)/A accurate when delta*A is small, where exp(z)-1 alone
+//        would cancel.
+__device__ __forceinline__ double expm1_and_exp(double z, double& e) {
+    const double m = expm1(z);
+    e = m + 1.0;
+    return m;
+}
+__device__ __forceinline__ float expm1_and_exp(float z, float& e) {
+    e = fast_exp2(z * kLog2e);
+    const float poly = z * __builtin_fmaf(z, __builtin_fmaf(z, 1.0f / 6.0f, 0.5f), 1.0f);
+    return (__builtin_fabsf(z) < 0.015625f) ? poly : (e - 1.0f);
+}
+
+// Accurate fp32 variant (ocml expm1f), for the fp32-storage decode step.
+__device__ __forceinline__ float expm1_and_exp_precise(float z, float& e) {
+    const float m = expm1f(z);
+    e = m + 1.0f;
+    return m;
+}
+
+__device__ __forceinline__ double exp_(double z) { return exp(z); }
+__device__ __forceinline__ float exp_(float z) { return fast_exp2(z * kLog2e); }
+
+// Wave-uniform value (the compiler then keeps it in an SGPR).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// blockIdx -> logical block so that consecutive logical blocks run on the same
+// XCD (dispatch places block i on XCD i % 8).  Bijective for any grid size.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    constexpr int kXcd = 8;
+    const int q = nblocks / kXcd, r = nblocks % kXcd;
+    const int xcd = bid % kXcd, local = bid / kXcd;
+    return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+}  // namespace ssm

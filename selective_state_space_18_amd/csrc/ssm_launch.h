@@ -1,0 +1,50 @@
+// Kernel parameter blocks and launcher entry points (internal to libssmscan).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// One scan call, as cut by the host planner.  Scratch arrays hold the
+// arithmetic type Acc (fp32 for bf16 storage, fp64 for fp32 storage):
+//   bc  : [Bsz*L][2N] Acc -- B_t[n] in the first N slots, C_t[n]/(n+1) in the next N
+//   agg : [S-1][N+1][Bsz*Dm] Acc -- per segment: end state from a zero start
+//         (slots 0..N-1, scaled state g = (n+1) h) and the sum of delta (slot N)
+//   gin : [S][N][Bsz*Dm] Acc -- scaled state entering segment s (used when S > 1)
+struct ScanParams {
+    const void *x, *delta, *B, *C;
+    const float *A, *D, *h_init;
+    void *y;
+    float *h_final;
+    void *bc, *agg, *gin;
+    int64_t Bsz, L, Dm;
+    int64_t seg_len;   // time steps per segment (last one may be shorter)
+    int S;             // number of segments
+    int tiles_per_b;   // ceil(Dm / 64): 64-channel wave tiles per batch row
+    int n_tiles;       // Bsz * tiles_per_b
+    int waves_per_block;
+    int force_general; // 1: never take the structured-A path
+};
+
+struct StepParams {
+    const void *x, *delta, *B, *C;
+    const float *A, *D;
+    float *h;
+    void *y;
+    int64_t Bsz, Dm;
+};
+
+// Bytes per element of the scan's arithmetic type for a storage dtype.
+size_t scan_acc_bytes(int dtype);
+
+// dtype: 0 = fp32, 1 = bf16.  N in {1,2,4,8,16}.  All return hipSuccess or the
+// launch error.
+hipError_t launch_bc_prep(const ScanParams &p, int N, int dtype, hipStream_t s);
+hipError_t launch_scan_aggregate(const ScanParams &p, int N, int dtype, hipStream_t s);
+hipError_t launch_scan_carry(const ScanParams &p, int N, int dtype, hipStream_t s);
+hipError_t launch_scan_output(const ScanParams &p, int N, int dtype, hipStream_t s);
+hipError_t launch_state_init(const ScanParams &p, int N, hipStream_t s);
+hipError_t launch_step(const StepParams &p, int N, int dtype, hipStream_t s);
+
+}  // namespace ssm

@@ -1,0 +1,212 @@
+"""Python binding of libssmscan (ctypes).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, and their device pointers are passed to the C ABI together with
+the current HIP stream.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback.  If ``libssmscan.so`` has not been built
+the import fails with an explanation.
+
+Functions mirror the C entry points:
+
+    scan_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None)
+        -> (y, h_final)
+    step(x, delta, A, B, C, D, h, y=None) -> y       (h is updated in place)
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_OPT_SEGMENT_LEN, SSM_OPT_FORCE_GENERAL = 1, 2
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_BAD_DTYPE",
+          4: "SSM_ERR_UNSUPPORTED_N", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_NOMEM",
+          8: "SSM_ERR_HIP", 9: "SSM_ERR_BAD_OPTION"}
+
+# Every symbol include/ssmscan.h declares.
+EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_strerror",
+           "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
+           "ssm_scan_plan", "ssm_release_workspaces")
+
+
+class SSMError(RuntimeError):
+    def __init__(self, code, where, detail):
+        self.code = code
+        super().__init__(f"{where} failed: {STATUS.get(code, code)}: {detail}")
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib = None
+
+
+def lib():
+    """The loaded libssmscan (raises ImportError if it was never built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m selective_state_space_18_amd.build` (needs ROCm hipcc)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.ssm_scan_fwd.argtypes = [_vp] * 8 + [_i64] * 4 + [ctypes.c_int, _vp]
+    L.ssm_scan_fwd_ex.argtypes = [_vp] * 9 + [_i64] * 4 + [ctypes.c_int, _vp]
+    L.ssm_step.argtypes = [_vp] * 8 + [_i64] * 3 + [_vp]
+    L.ssm_step_ex.argtypes = [_vp] * 8 + [_i64] * 3 + [ctypes.c_int, _vp]
+    for f in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex"):
+        getattr(L, f).restype = ctypes.c_int
+    L.ssm_strerror.argtypes = [ctypes.c_int]
+    L.ssm_strerror.restype = ctypes.c_char_p
+    L.ssm_last_error.argtypes = []
+    L.ssm_last_error.restype = ctypes.c_char_p
+    L.ssm_version.argtypes = []
+    L.ssm_version.restype = ctypes.c_int
+    L.ssm_set_option.argtypes = [ctypes.c_int, _i64]
+    L.ssm_set_option.restype = ctypes.c_int
+    L.ssm_get_option.argtypes = [ctypes.c_int]
+    L.ssm_get_option.restype = _i64
+    L.ssm_scan_plan.argtypes = [_i64] * 4 + [ctypes.c_int, ctypes.c_int,
+                                             ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+    L.ssm_scan_plan.restype = ctypes.c_int
+    L.ssm_release_workspaces.argtypes = []
+    L.ssm_release_workspaces.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc, where):
+    if rc != 0:
+        detail = lib().ssm_last_error().decode(errors="replace")
+        raise SSMError(rc, where, detail)
+
+
+def last_error() -> str:
+    return lib().ssm_last_error().decode(errors="replace")
+
+
+def version() -> int:
+    return lib().ssm_version()
+
+
+def set_option(option: int, value: int) -> None:
+    _check(lib().ssm_set_option(int(option), int(value)), "ssm_set_option")
+
+
+def get_option(option: int) -> int:
+    return int(lib().ssm_get_option(int(option)))
+
+
+def plan(Bsz, L, Dm, N, dtype=SSM_BF16, compute_units=0):
+    """(segments, segment_len) the scan would use."""
+    s, sl = _i64(), _i64()
+    _check(lib().ssm_scan_plan(Bsz, L, Dm, N, dtype, compute_units, ctypes.byref(s), ctypes.byref(sl)),
+           "ssm_scan_plan")
+    return s.value, sl.value
+
+
+def release_workspaces() -> None:
+    _check(lib().ssm_release_workspaces(), "ssm_release_workspaces")
+
+
+_DT = {torch.float32: SSM_F32, torch.bfloat16: SSM_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _need(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def scan_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, want_state=True):
+    """Selective scan over [Bsz, L, Dm] with state size N = A.shape[1].
+
+    x, delta: [Bsz, L, Dm]; B, C: [Bsz, L, N] (all the same dtype, fp32 or bf16);
+    A: [Dm, N] fp32; D: [Dm] fp32; h_init: optional [Bsz, Dm, N] fp32.
+    Returns (y [Bsz, L, Dm] in x's dtype, h_final [Bsz, Dm, N] fp32 or None).
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (Bsz, L, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, L, Dm), dt, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(B, "B", (Bsz, L, N), dt, dev)
+    _need(C, "C", (Bsz, L, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    if h_init is not None:
+        _need(h_init, "h_init", (Bsz, Dm, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((Bsz, L, Dm), dtype=dt, device=dev)
+    _need(y, "y", (Bsz, L, Dm), dt, dev)
+    if h_final is None and want_state:
+        h_final = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev)
+    if h_final is not None:
+        _need(h_final, "h_final", (Bsz, Dm, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_fwd_ex(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   _ptr(h_init), _ptr(y), _ptr(h_final), Bsz, L, Dm, N, code,
+                                   _stream(dev))
+    _check(rc, "ssm_scan_fwd")
+    return y, h_final
+
+
+def step(x, delta, A, B, C, D, h, y=None):
+    """One decode step: h [Bsz, Dm, N] fp32 is updated in place; returns y [Bsz, Dm].
+
+    x, delta: [Bsz, Dm]; B, C: [Bsz, N] (same dtype: bf16, or fp32);
+    A: [Dm, N] fp32; D: [Dm] fp32.
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, Dm = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (Bsz, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, Dm), dt, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(B, "B", (Bsz, N), dt, dev)
+    _need(C, "C", (Bsz, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    _need(h, "h", (Bsz, Dm, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((Bsz, Dm), dtype=dt, device=dev)
+    _need(y, "y", (Bsz, Dm), dt, dev)
+    with torch.cuda.device(dev):
+        if code == SSM_BF16:
+            rc = lib().ssm_step(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h),
+                                _ptr(y), Bsz, Dm, N, _stream(dev))
+        else:
+            rc = lib().ssm_step_ex(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h),
+                                   _ptr(y), Bsz, Dm, N, code, _stream(dev))
+    _check(rc, "ssm_step")
+    return y

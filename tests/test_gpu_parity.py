@@ -1,0 +1,362 @@
+"""GPU parity: libssmscan (through its C ABI) against the fp64 oracle.
+
+Small cases compare every element; the full-size workloads run in the launch
+configuration the benchmark times and compare a sampled channel subset (exact,
+because channels are independent) or sampled sequences of the decode batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+from ssm_inputs import configs, generate
+import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ss():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_18_amd import ssmscan
+    ssmscan.lib()
+    yield ssmscan
+    ssmscan.set_option(ssmscan.SSM_OPT_SEGMENT_LEN, 0)
+    ssmscan.set_option(ssmscan.SSM_OPT_FORCE_GENERAL, 0)
+
+
+DEV = "cuda:0"
+
+
+def run_scan(ss, inp, h_init=None, seg=0, general=False):
+    ss.set_option(ss.SSM_OPT_SEGMENT_LEN, seg)
+    ss.set_option(ss.SSM_OPT_FORCE_GENERAL, 1 if general else 0)
+    try:
+        y, hf = ss.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], h_init=h_init)
+        torch.cuda.synchronize()
+    finally:
+        ss.set_option(ss.SSM_OPT_SEGMENT_LEN, 0)
+        ss.set_option(ss.SSM_OPT_FORCE_GENERAL, 0)
+    return y, hf
+
+
+def small_cfg(dtype, a_kind, Bsz, L, Dm, N, seed=7):
+    return configs.ScanConfig(f"small_{dtype}_{a_kind}_{Bsz}x{L}x{Dm}x{N}", Bsz, L, Dm, N, dtype,
+                              a_kind, "per_token", 1.0, seed)
+
+
+# ---------------------------------------------------------------------------
+# small problems, every element
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["auto_path", "general_path"])
+def test_tiny_fp32_workload(ss, general):
+    cfg = configs.TINY_FP32
+    P.say(f"case: {cfg.name} general={general}")
+    inp = generate.scan_inputs(cfg, DEV)
+    y, hf = run_scan(ss, inp, general=general)
+    yr, hr = P.oracle_scan(inp)
+    P.compare(y, yr, "fp32", "y")
+    P.compare(hf, hr, "fp32", "h_final")
+
+
+CASES = [
+    # dtype, A kind, Bsz, L, Dm, N, forced segment length (0 = planner)
+    ("fp32", "s4d_real", 1, 1, 1, 16, 0),
+    ("fp32", "s4d_real", 2, 7, 3, 16, 0),
+    ("fp32", "lognormal", 3, 130, 100, 16, 0),
+    ("fp32", "s4d_real", 2, 517, 130, 16, 64),
+    ("fp32", "lognormal", 1, 300, 64, 8, 5),
+    ("fp32", "s4d_real", 2, 259, 65, 4, 1),
+    ("fp32", "s4d_real", 1, 200, 70, 2, 33),
+    ("fp32", "lognormal", 2, 150, 33, 1, 7),
+    ("bf16", "s4d_real", 1, 1, 1, 16, 0),
+    ("bf16", "s4d_real", 4, 1030, 200, 16, 0),
+    ("bf16", "lognormal", 2, 700, 192, 16, 0),
+    ("bf16", "s4d_real", 2, 517, 130, 16, 64),
+    ("bf16", "lognormal", 3, 333, 77, 16, 3),
+    ("bf16", "s4d_real", 1, 640, 256, 8, 100),
+    ("bf16", "lognormal", 2, 99, 64, 4, 10),
+    ("bf16", "s4d_real", 2, 257, 40, 2, 0),
+    ("bf16", "lognormal", 1, 64, 129, 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
+def test_small_shapes(ss, case):
+    dtype, a_kind, Bsz, L, Dm, N, seg = case
+    cfg = small_cfg(dtype, a_kind, Bsz, L, Dm, N)
+    P.say(f"case: {case}")
+    inp = generate.scan_inputs(cfg, DEV)
+    y, hf = run_scan(ss, inp, seg=seg)
+    yr, hr = P.oracle_scan(inp)
+    P.compare(y, yr, dtype, "y")
+    P.compare(hf, hr, dtype, "h_final")
+    if a_kind == "s4d_real":
+        # the general-A path must agree on the same structured A
+        y2, h2 = run_scan(ss, inp, seg=seg, general=True)
+        P.compare(y2, yr, dtype, "y (general path)")
+        P.compare(h2, hr, dtype, "h_final (general path)")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_initial_state_and_resume(ss, dtype):
+    """scan with h_init matches the oracle; scan(L1+L2) == scan(L2, h_init=scan(L1).h_final)."""
+    cfg = small_cfg(dtype, "s4d_real", 2, 600, 96, 16, seed=11)
+    P.say(f"case: resume {dtype}")
+    inp = generate.scan_inputs(cfg, DEV)
+    h0 = torch.randn(2, 96, 16, device=DEV, generator=torch.Generator(DEV).manual_seed(5))
+    y, hf = run_scan(ss, inp, h_init=h0, seg=128)
+    yr, hr = P.oracle_scan(inp, h0=h0)
+    P.compare(y, yr, dtype, "y with h_init")
+    P.compare(hf, hr, dtype, "h_final with h_init")
+    L1 = 250
+    first = {k: (v[:, :L1].contiguous() if k in ("x", "delta", "B", "C") else v) for k, v in inp.items()}
+    second = {k: (v[:, L1:].contiguous() if k in ("x", "delta", "B", "C") else v) for k, v in inp.items()}
+    _, h1 = run_scan(ss, first, h_init=h0)
+    y2, h2 = run_scan(ss, second, h_init=h1)
+    P.compare(y2, yr[:, L1:], dtype, "y of the resumed half")
+    P.compare(h2, hr, dtype, "h_final after resume")
+    # h_init and h_final may be the same buffer (in-place state advance),
+    # with and without a time split
+    for seg in (0, 1000):
+        hbuf = h0.clone()
+        ss.set_option(ss.SSM_OPT_SEGMENT_LEN, seg)
+        try:
+            y3, _ = ss.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                h_init=hbuf, h_final=hbuf)
+            torch.cuda.synchronize()
+        finally:
+            ss.set_option(ss.SSM_OPT_SEGMENT_LEN, 0)
+        P.compare(y3, yr, dtype, f"y (h_init is h_final, seg={seg})")
+        P.compare(hbuf, hr, dtype, f"in-place h_final (seg={seg})")
+
+
+def test_empty_inputs(ss):
+    P.say("case: empty inputs")
+    for dt in (torch.float32, torch.bfloat16):
+        x = torch.empty(3, 0, 5, dtype=dt, device=DEV)
+        A = -torch.ones(5, 4, device=DEV)
+        D = torch.ones(5, device=DEV)
+        Bc = torch.empty(3, 0, 4, dtype=dt, device=DEV)
+        h0 = torch.randn(3, 5, 4, device=DEV)
+        y, hf = ss.scan_fwd(x, x, A, Bc, Bc, D, h_init=h0)
+        y0, hz = ss.scan_fwd(x, x, A, Bc, Bc, D)
+        torch.cuda.synchronize()
+        assert y.shape == (3, 0, 5)
+        assert torch.equal(hf, h0)
+        assert torch.count_nonzero(hz) == 0
+        # no channels at all
+        xe = torch.empty(0, 4, 5, dtype=dt, device=DEV)
+        ye, he = ss.scan_fwd(xe, xe, A, torch.empty(0, 4, 4, dtype=dt, device=DEV),
+                             torch.empty(0, 4, 4, dtype=dt, device=DEV), D)
+        assert ye.numel() == 0 and he.numel() == 0
+        ys = ss.step(torch.empty(0, 5, dtype=dt, device=DEV), torch.empty(0, 5, dtype=dt, device=DEV), A,
+                     torch.empty(0, 4, dtype=dt, device=DEV), torch.empty(0, 4, dtype=dt, device=DEV), D,
+                     torch.empty(0, 5, 4, device=DEV))
+        assert ys.numel() == 0
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_zero_and_tiny_A_and_zero_delta(ss, dtype):
+    """A == 0 (ZOH limit delta*B), |A| tiny, positive A, and delta == 0 spans."""
+    cfg = small_cfg(dtype, "lognormal", 2, 300, 64, 16, seed=3)
+    P.say(f"case: degenerate A/delta {dtype}")
+    inp = generate.scan_inputs(cfg, DEV)
+    A = inp["A"].clone()
+    A[0:8, :] = 0.0
+    A[8:16, :] = -1e-9
+    A[16:24, 3] = 0.0
+    A[24:32, :] = 0.05
+    A[32:40, :] = -torch.arange(1, 17, device=DEV, dtype=torch.float32) * 1e-8
+    inp["A"] = A
+    dl = inp["delta"].clone()
+    dl[:, 100:180, :] = 0
+    inp["delta"] = dl
+    for general in (False, True):
+        y, hf = run_scan(ss, inp, seg=64, general=general)
+        yr, hr = P.oracle_scan(inp)
+        P.compare(y, yr, dtype, f"y (general={general})")
+        P.compare(hf, hr, dtype, f"h_final (general={general})")
+
+
+def test_structured_A_with_other_scale(ss):
+    """A[d, n] = (n+1) * a_d with a per-channel a_d takes the structured path."""
+    cfg = small_cfg("bf16", "s4d_real", 2, 400, 128, 16, seed=9)
+    P.say("case: scaled S4D-real A")
+    inp = generate.scan_inputs(cfg, DEV)
+    a = -torch.exp(torch.randn(128, 1, device=DEV, generator=torch.Generator(DEV).manual_seed(2)))
+    inp["A"] = (a * torch.arange(1, 17, device=DEV, dtype=torch.float32)).contiguous()
+    y, hf = run_scan(ss, inp)
+    yr, hr = P.oracle_scan(inp)
+    P.compare(y, yr, "bf16", "y")
+    P.compare(hf, hr, "bf16", "h_final")
+
+
+def test_deterministic_and_segment_invariant(ss):
+    cfg = small_cfg("bf16", "s4d_real", 2, 2048, 256, 16, seed=13)
+    P.say("case: determinism / segment invariance")
+    inp = generate.scan_inputs(cfg, DEV)
+    y1, h1 = run_scan(ss, inp)
+    y2, h2 = run_scan(ss, inp)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    yr, hr = P.oracle_scan(inp)
+    for seg in (0, 64, 100, 333, 2048):
+        y, hf = run_scan(ss, inp, seg=seg)
+        P.compare(y, yr, "bf16", f"y seg={seg}")
+        P.compare(hf, hr, "bf16", f"h_final seg={seg}")
+
+
+def test_no_write_outside_outputs(ss):
+    """Guard bands around y and h_final stay untouched (ragged tiles, tails)."""
+    cfg = small_cfg("bf16", "s4d_real", 3, 203, 70, 16, seed=17)
+    P.say("case: canaries")
+    inp = generate.scan_inputs(cfg, DEV)
+    pad = 4096
+    ybuf = torch.full((pad + 3 * 203 * 70 + pad,), 7.0, dtype=torch.bfloat16, device=DEV)
+    hbuf = torch.full((pad + 3 * 70 * 16 + pad,), 7.0, dtype=torch.float32, device=DEV)
+    y = ybuf[pad:pad + 3 * 203 * 70].view(3, 203, 70)
+    hf = hbuf[pad:pad + 3 * 70 * 16].view(3, 70, 16)
+    ss.set_option(ss.SSM_OPT_SEGMENT_LEN, 50)
+    try:
+        ss.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], y=y, h_final=hf)
+        torch.cuda.synchronize()
+    finally:
+        ss.set_option(ss.SSM_OPT_SEGMENT_LEN, 0)
+    for buf, n in ((ybuf, 3 * 203 * 70), (hbuf, 3 * 70 * 16)):
+        assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + n:] == 7.0)
+    yr, hr = P.oracle_scan(inp)
+    P.compare(y, yr, "bf16", "y")
+    P.compare(hf, hr, "bf16", "h_final")
+
+
+# ---------------------------------------------------------------------------
+# decode step
+
+
+@pytest.mark.parametrize("dtype,N,Bsz,Dm", [("fp32", 16, 3, 70), ("bf16", 16, 5, 130), ("fp32", 4, 2, 33),
+                                            ("bf16", 8, 4, 64), ("bf16", 2, 3, 17), ("fp32", 1, 2, 9)])
+def test_step_matches_oracle(ss, dtype, N, Bsz, Dm):
+    cfg = configs.StepConfig("small_step", Bsz, Dm, N, dtype, 0.1, 4, seed=21)
+    P.say(f"case: step {dtype} N={N} {Bsz}x{Dm}")
+    st = generate.step_state(cfg, DEV)
+    A = -torch.exp(torch.randn(Dm, N, device=DEV, generator=torch.Generator(DEV).manual_seed(4)))
+    A[0, :] = 0.0
+    h = st["h"].clone()
+    href = P.f64(h)
+    for tok in generate.step_tokens(cfg, st, 4):
+        y = ss.step(tok["x"], tok["delta"], A, tok["B"], tok["C"], st["D"], h)
+        torch.cuda.synchronize()
+        yr, href = P.oracle_step(tok, A, st["D"], href)
+        P.compare(y, yr, dtype, "y")
+        P.compare(h, href, dtype, "h")
+
+
+def test_step_delta_zero_keeps_state_bitwise(ss):
+    P.say("case: step delta=0")
+    h = torch.randn(4, 64, 16, device=DEV)
+    h0 = h.clone()
+    A = -torch.arange(1, 17, device=DEV, dtype=torch.float32).expand(64, 16).contiguous()
+    z = torch.zeros(4, 64, dtype=torch.bfloat16, device=DEV)
+    Bc = torch.randn(4, 16, device=DEV).to(torch.bfloat16)
+    ss.step(torch.randn(4, 64, device=DEV).to(torch.bfloat16), z, A, Bc, Bc, torch.ones(64, device=DEV), h)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h0)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_step_chain_equals_scan(ss, dtype):
+    """Recurrent mode (step L times) equals the scan ('Ayrik Zamana Gecis')."""
+    cfg = small_cfg(dtype, "s4d_real", 2, 40, 64, 16, seed=23)
+    P.say(f"case: step chain vs scan {dtype}")
+    inp = generate.scan_inputs(cfg, DEV)
+    y, hf = run_scan(ss, inp, seg=8)
+    h = torch.zeros(2, 64, 16, device=DEV)
+    ys = []
+    for t in range(40):
+        ys.append(ss.step(inp["x"][:, t].contiguous(), inp["delta"][:, t].contiguous(), inp["A"],
+                          inp["B"][:, t].contiguous(), inp["C"][:, t].contiguous(), inp["D"], h))
+    torch.cuda.synchronize()
+    ystep = torch.stack(ys, 1)
+    yr, hr = P.oracle_scan(inp)
+    P.compare(ystep, yr, dtype, "y by steps")
+    P.compare(h, hr, dtype, "h by steps")
+    P.compare(y, P.f64(ystep) if dtype == "fp32" else yr, dtype, "scan vs steps")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled outputs
+
+
+def _sample_channels(Dm, every=64):
+    idx = list(range(0, Dm, every))
+    if Dm - 1 not in idx:
+        idx.append(Dm - 1)
+    return idx
+
+
+def test_mamba130m_layer_full(ss):
+    cfg = configs.MAMBA130M_LAYER
+    P.say(f"case: {cfg.name} (all outputs)")
+    inp = generate.scan_inputs(cfg, DEV)
+    y, hf = run_scan(ss, inp)
+    yr, hr = P.oracle_scan(inp)
+    P.compare(y, yr, "bf16", "y")
+    P.compare(hf, hr, "bf16", "h_final")
+
+
+@pytest.mark.slow
+def test_mamba2p8b_layer_sampled(ss):
+    cfg = configs.MAMBA2P8B_LAYER
+    P.say(f"case: {cfg.name} (every 64th channel)")
+    inp = generate.scan_inputs(cfg, DEV)
+    y, hf = run_scan(ss, inp)
+    idx = _sample_channels(cfg.Dm)
+    yr, hr = P.oracle_scan(inp, d_idx=idx)
+    ii = torch.tensor(idx, device=DEV)
+    P.compare(y.index_select(2, ii), yr, "bf16", "y (sampled channels)")
+    P.compare(hf.index_select(1, ii), hr, "bf16", "h_final (sampled channels)")
+
+
+@pytest.mark.slow
+def test_long_context_sampled(ss):
+    cfg = configs.LONG_CONTEXT_1M
+    P.say(f"case: {cfg.name} (every 64th channel)")
+    inp = generate.scan_inputs(cfg, DEV)
+    y, hf = run_scan(ss, inp)
+    idx = _sample_channels(cfg.Dm)
+    yr, hr = P.oracle_scan(inp, d_idx=idx)
+    ii = torch.tensor(idx, device=DEV)
+    P.compare(y.index_select(2, ii), yr, "bf16", "y (sampled channels)")
+    P.compare(hf.index_select(1, ii), hr, "bf16", "h_final (sampled channels)")
+
+
+@pytest.mark.slow
+def test_decode_full_batch(ss):
+    """Decode workload at full size: 16 steps checked on sampled sequences, then
+    1000 steps in total with the final state of two sequences checked."""
+    cfg = configs.DECODE_256x8192
+    P.say(f"case: {cfg.name}")
+    st = generate.step_state(cfg, DEV)
+    h = st["h"].clone()
+    bi = [0, 1, 127, 255]
+    href = P.f64(h[bi])
+    for k in range(16):
+        tok = generate.step_tokens(cfg, st, 1)[0]
+        y = ss.step(tok["x"], tok["delta"], st["A"], tok["B"], tok["C"], st["D"], h)
+        torch.cuda.synchronize()
+        yr, href = P.oracle_step(tok, st["A"], st["D"], href, b_idx=bi)
+        P.compare(y[bi], yr, "bf16", f"y step {k}")
+        P.compare(h[bi], href, "bf16", f"h step {k}")
+    bi2 = [3, 200]
+    href2 = P.f64(h[bi2])
+    for k in range(16, cfg.n_tokens):
+        tok = generate.step_tokens(cfg, st, 1)[0]
+        y = ss.step(tok["x"], tok["delta"], st["A"], tok["B"], tok["C"], st["D"], h)
+        yr, href2 = P.oracle_step(tok, st["A"], st["D"], href2, b_idx=bi2)
+        if k % 100 == 0 or k == cfg.n_tokens - 1:
+            torch.cuda.synchronize()
+            P.compare(y[bi2], yr, "bf16", f"y step {k}")
+    torch.cuda.synchronize()
+    P.compare(h[bi2], href2, "bf16", "h after 1000 steps")
+    assert np.isfinite(P.f64(h)).all()
