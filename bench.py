@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of libssmscan on one MI355X.
+
+A step is one selective-scan forward (B/C prep, segment aggregate, carry and
+output kernels) over the Mamba-2.8B-shaped layer: Bsz=4, L=16384, D=5120,
+N=16, bf16 storage, fp32 arithmetic, synthetic seeded inputs resident in HBM.
+The JSON line reports elements/s (B*L*D*N per second), the achieved
+algorithmic HBM bandwidth, the roofline of the dominant kernel, the fp64 CPU
+oracle timed on a bounded sample of the same workload, and -- under
+"secondary" -- the long-context scan and the decode step.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+                    [--no-cpu-baseline] [--no-secondary]
+    python bench.py --only decode      # one workload, for profiler runs
+    python bench.py --copy-calibration # plain copy of known size (for counters)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan elems/s (B·L·D·N) + achieved HBM GB/s vs MI355X peak"
+HBM_PEAK_GBPS = 8000.0
+# Non-packed fp32 FMA issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 2 flops.
+VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
+# Algorithmic fp32 flops per state element of the scan: z = delta*A, exp(z)-1,
+# divide by A, times B, times x, Abar*h + Bbar*x (FMA, 2), C*h + y (FMA, 2).
+SCAN_FLOPS_PER_ELEM = 9
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_18_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(name):
+    with open(os.path.join(KERNEL_SRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel, src_file):
+    """HBM bytes per launch measured with counters, if the kernel is unchanged."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_sha") != source_sha(src_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed_loop(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for i in range(steps):
+        fn(warmup + i)
+    b.record(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def bench_scan(torch, ss, generate, cfg, steps, warmup):
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name}")
+    inp = generate.scan_inputs(cfg, dev)
+    y = torch.empty_like(inp["x"])
+    hf = torch.empty(cfg.Bsz, cfg.Dm, cfg.N, device=dev, dtype=torch.float32)
+
+    def fn(_i):
+        ss.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], y=y, h_final=hf)
+
+    fn(0)
+    torch.cuda.synchronize()
+    ss.set_option(ss.SSM_OPT_PROFILE, 1)
+    ss.profile_read()
+    try:
+        log(f"[bench] timing {cfg.name}: {warmup} warmup + {steps} steps")
+        ms = timed_loop(torch, fn, steps, warmup)
+        prof = ss.profile_read()
+    finally:
+        ss.set_option(ss.SSM_OPT_PROFILE, 0)
+    S, seg = ss.plan(cfg.Bsz, cfg.L, cfg.Dm, cfg.N)
+    del inp, y, hf
+    torch.cuda.empty_cache()
+    kern = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / (steps + warmup)}
+            for k, v in prof.items() if v[1] > 0}
+    return ms, kern, S, seg
+
+
+def scan_record(cfg, ms, kern, S, seg, generate):
+    elems = cfg.elems()
+    alg = generate.alg_bytes_scan(cfg)
+    out_ms = kern["scan_output"]["avg_ms"]
+    achieved = elems * SCAN_FLOPS_PER_ELEM / (out_ms * 1e-3) / 1e12
+    roof = {
+        "kernel": "scan_segment_kernel (output pass)",
+        "bound": "alu",
+        "achieved": round(achieved, 3),
+        "peak": round(VALU_FP32_PEAK_TFLOPS, 2),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
+        "traffic": traffic_for("scan_output_" + cfg.name, "scan_kernels.hip"),
+        "avg_ms": round(out_ms, 5),
+        "algorithmic_flops_per_launch": elems * SCAN_FLOPS_PER_ELEM,
+        "hbm_frac_at_algorithmic_bytes": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+    hbm = {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg}
+    cfgd = {"workload": cfg.name, "Bsz": cfg.Bsz, "L": cfg.L, "Dm": cfg.Dm, "N": cfg.N,
+            "storage": cfg.dtype, "A": cfg.a_kind, "delta": cfg.delta_kind,
+            "segments": S, "segment_len": seg}
+    return roof, hbm, cfgd, {k: round(v["avg_ms"], 5) for k, v in kern.items()}
+
+
+def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
+    """n_tokens consecutive steps; the resident state cycles over `layers`
+    independent layer states so the working set (layers x 134 MB) exceeds the
+    256 MB last-level cache, as in a multi-layer model."""
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name} ({layers} layer states)")
+    states = [generate.step_state(cfg, dev, seed=cfg.seed + 17 * k) for k in range(layers)]
+    toks = generate.step_tokens(cfg, states[0], 16)
+    y = torch.empty(cfg.Bsz, cfg.Dm, dtype=toks[0]["x"].dtype, device=dev)
+
+    def fn(i):
+        st = states[i % layers]
+        t = toks[i % 16]
+        ss.step(t["x"], t["delta"], st["A"], t["B"], t["C"], st["D"], st["h"], y=y)
+
+    fn(0)
+    torch.cuda.synchronize()
+    ss.set_option(ss.SSM_OPT_PROFILE, 1)
+    ss.profile_read()
+    try:
+        log(f"[bench] timing {cfg.name}: {n_tokens} steps")
+        ms = timed_loop(torch, fn, n_tokens, 16)
+        prof = ss.profile_read()
+    finally:
+        ss.set_option(ss.SSM_OPT_PROFILE, 0)
+    k_ms = prof["step"][0] / prof["step"][1]
+    alg = generate.alg_bytes_step(cfg)
+    del states, toks, y
+    torch.cuda.empty_cache()
+    return {
+        "workload": cfg.name, "steps": n_tokens, "ms_per_step": round(ms, 5),
+        "value": cfg.elems_per_step() / (ms * 1e-3), "unit": "elems/s",
+        "hbm": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
+        "roofline": {"kernel": "step_kernel", "bound": "hbm",
+                     "achieved": round(alg / (k_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for("step_" + cfg.name, "step_kernel.hip"),
+                     "avg_ms": round(k_ms, 5)},
+        "state_layers_cycled": layers,
+    }
+
+
+def cpu_baseline(torch, generate, cfg, target_s=10.0):
+    """The fp64 oracle on a channel subset of the same workload (channels are
+    independent, so a subset is the same work per element)."""
+    import numpy as np
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    dev = "cuda:0"
+    inp = generate.scan_inputs(cfg, dev)
+
+    def run(nch):
+        stride = max(1, cfg.Dm // nch)
+        idx = torch.arange(0, cfg.Dm, stride, device=dev)[:nch]
+        f = lambda t: t.detach().to("cpu").to(torch.float64).numpy()
+        args = (f(inp["x"].index_select(2, idx)), f(inp["delta"].index_select(2, idx)),
+                f(inp["A"].index_select(0, idx)), f(inp["B"]), f(inp["C"]), f(inp["D"].index_select(0, idx)))
+        t0 = time.perf_counter()
+        oracle.scan(*args, threads=threads)
+        return time.perf_counter() - t0, len(idx)
+
+    probe_ch = min(cfg.Dm, 2 * threads)
+    dt, n = run(probe_ch)
+    rate = cfg.Bsz * cfg.L * n * cfg.N / dt
+    nch = int(min(cfg.Dm, max(probe_ch, target_s * rate / (cfg.Bsz * cfg.L * cfg.N))))
+    dt, n = run(nch)
+    elems = cfg.Bsz * cfg.L * n * cfg.N
+    del inp
+    torch.cuda.empty_cache()
+    _ = np
+    return {"value": elems / dt, "unit": "elems/s", "cores": threads, "kind": "oracle",
+            "sample": f"{cfg.name}: all {cfg.Bsz} rows x {cfg.L} steps, {n} of {cfg.Dm} channels "
+                      f"(every {max(1, cfg.Dm // nch)}th), fp64, {dt:.1f} s wall"}
+
+
+def copy_calibration(torch, nbytes=1 << 30):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {nbytes} bytes 3 times")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", choices=["scan", "long", "decode", "small"], default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the scan shards over (batch, channel) with no "
+              f"exchange, so there is no multi-GPU path to time (asked for --gpus {a.gpus}, "
+              f"WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_18_amd import ssmscan as ss
+    from ssm_inputs import configs, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ss.lib()
+    torch.cuda.set_device(0)
+
+    if a.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    if a.only == "decode":
+        rec = bench_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "long":
+        cfg = configs.LONG_CONTEXT_1M
+        ms, kern, S, seg = bench_scan(torch, ss, generate, cfg, a.steps, a.warmup)
+        roof, hbm, cfgd, kms = scan_record(cfg, ms, kern, S, seg, generate)
+        print(json.dumps({"workload": cfg.name, "ms_per_step": ms, "value": cfg.elems() / (ms * 1e-3),
+                          "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms}), flush=True)
+        return
+    if a.only == "small":
+        cfg = configs.MAMBA130M_LAYER
+        ms, kern, S, seg = bench_scan(torch, ss, generate, cfg, a.steps, a.warmup)
+        roof, hbm, cfgd, kms = scan_record(cfg, ms, kern, S, seg, generate)
+        print(json.dumps({"workload": cfg.name, "ms_per_step": ms, "value": cfg.elems() / (ms * 1e-3),
+                          "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms}), flush=True)
+        return
+
+    cfg = configs.MAMBA2P8B_LAYER
+    ms, kern, S, seg = bench_scan(torch, ss, generate, cfg, a.steps, a.warmup)
+    roof, hbm, cfgd, kms = scan_record(cfg, ms, kern, S, seg, generate)
+    out = {
+        "metric": METRIC,
+        "value": cfg.elems() / (ms * 1e-3),
+        "unit": "elems/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": cfgd,
+        "hbm": hbm,
+        "roofline": roof,
+        "kernels_avg_ms": kms,
+    }
+    if a.only is None and not a.no_secondary:
+        sec = {}
+        lc = configs.LONG_CONTEXT_1M
+        lms, lk, lS, lseg = bench_scan(torch, ss, generate, lc, max(3, a.steps // 5), 2)
+        lroof, lhbm, lcfg, lkms = scan_record(lc, lms, lk, lS, lseg, generate)
+        sec["long_context"] = {"workload": lc.name, "ms_per_step": round(lms, 5),
+                               "value": lc.elems() / (lms * 1e-3), "unit": "elems/s", "hbm": lhbm,
+                               "roofline": lroof, "config": lcfg, "kernels_avg_ms": lkms}
+        sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
+                                     configs.DECODE_256x8192.n_tokens)
+        out["secondary"] = sec
+    if a.only is None and not a.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(torch, generate, cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -153,14 +153,38 @@ int ssm_version(void);
  *   SSM_OPT_FORCE_GENERAL: 1 = always take the general-A path, even when
  *                          A[d,n] == (n+1)*A[d,0] would allow the structured
  *                          one; 0 = automatic (default).
+ *   SSM_OPT_PROFILE      : see ssm_profile_read below.
+ *   SSM_OPT_STEP_CHANNELS: work per thread of the decode step.
  */
 typedef enum {
     SSM_OPT_SEGMENT_LEN = 1,
-    SSM_OPT_FORCE_GENERAL = 2
+    SSM_OPT_FORCE_GENERAL = 2,
+    SSM_OPT_PROFILE = 3,      /* 1 = bracket every kernel launch with HIP events (see below) */
+    SSM_OPT_STEP_CHANNELS = 4 /* channels each decode-step thread updates: 1, 2 or 4 (default 4) */
 } ssm_option;
 
 int ssm_set_option(int option, int64_t value);
 int64_t ssm_get_option(int option);
+
+/*
+ * Kernel timing for diagnostics and benchmarks.  While SSM_OPT_PROFILE is 1,
+ * each kernel the library launches is bracketed by two HIP events recorded on
+ * the stream it is launched on.  ssm_profile_read() waits for the recorded
+ * events, writes per-kind totals -- total_ms[k] (milliseconds) and
+ * launches[k] for k < n, indexed by ssm_kernel_kind -- and clears them.
+ * Either output may be NULL.  Returns SSM_OK or SSM_ERR_HIP.
+ */
+typedef enum {
+    SSM_K_BC_PREP = 0,          /* B/C rows converted for the scan */
+    SSM_K_SCAN_AGGREGATE = 1,   /* per-segment end states from a zero start */
+    SSM_K_SCAN_CARRY = 2,       /* states entering each segment */
+    SSM_K_SCAN_OUTPUT = 3,      /* y (and h_final) from the entering states */
+    SSM_K_STEP = 4,             /* decode step */
+    SSM_K_STATE_INIT = 5,       /* h_final of an empty sequence */
+    SSM_K_COUNT = 6
+} ssm_kernel_kind;
+
+int ssm_profile_read(double *total_ms, int64_t *launches, int n);
 
 /*
  * How ssm_scan_fwd would cut a problem: number of time segments and their

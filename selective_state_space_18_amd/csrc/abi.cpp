@@ -11,6 +11,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "ssm_launch.h"
 #include "ssmscan.h"
@@ -20,6 +21,10 @@ namespace {
 constexpr int kVersion = 10000;   // 1.0.0
 constexpr int kWavesPerBlock = 4;  // scan blocks: 4 independent 64-channel waves
 constexpr int64_t kMinSegment = 64;
+// Scan blocks per CU the planner aims for.  The structured kernels hold about
+// ten 4-wave blocks per CU at once; more blocks than that keep every SIMD fed
+// while the last ones drain, at the price of a longer carry pass.
+constexpr int64_t kBlocksPerCu = 16;
 
 thread_local std::string g_last_error;
 
@@ -44,6 +49,39 @@ int hip_fail(hipError_t e, const char *what) {
 
 std::atomic<int64_t> g_opt_segment_len{0};
 std::atomic<int64_t> g_opt_force_general{0};
+std::atomic<int64_t> g_opt_profile{0};
+std::atomic<int64_t> g_opt_step_channels{4};
+
+// ---------------------------------------------------------------------------
+// Optional per-kernel event timing (SSM_OPT_PROFILE).
+
+struct ProfRec {
+    hipEvent_t a, b;
+    int kind;
+};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;
+
+template <typename F>
+hipError_t timed(int kind, hipStream_t s, F launch) {
+    if (!g_opt_profile.load()) return launch();
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e == hipSuccess) e = hipEventRecord(a, s);
+    if (e != hipSuccess) {
+        if (a) (void)hipEventDestroy(a);
+        if (b) (void)hipEventDestroy(b);
+        return e;
+    }
+    hipError_t le = launch();
+    e = hipEventRecord(b, s);
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        g_prof.push_back({a, b, kind});
+    }
+    return le != hipSuccess ? le : e;
+}
 
 bool supported_n(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
 
@@ -104,21 +142,25 @@ struct Plan {
 };
 
 // Time segments: enough 4-wave blocks to give every CU an equal whole number
-// (>= 4) of them when that is possible, with segments of at least kMinSegment
-// steps.  Channels are never split; only time is.
-Plan make_plan(int64_t Bsz, int64_t L, int64_t Dm, int cus) {
+// (>= kBlocksPerCu) of them when that is possible, with segments of at least kMinSegment
+// steps.  Channels are never split; only time is.  A segment never spans more
+// than 1 GiB of x (the kernels address it with 32-bit buffer offsets) and the
+// grid stays below 2^30 blocks.
+Plan make_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t esize, int cus) {
     Plan pl;
     pl.tiles_per_b = (int)((Dm + 63) / 64);
     pl.n_tiles = (int)(Bsz * pl.tiles_per_b);
     const int64_t bps = (pl.n_tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t row = (Dm > 0 ? Dm : 1) * esize;
+    const int64_t max_len = ((int64_t)1 << 30) / row > 1 ? ((int64_t)1 << 30) / row : 1;
     int64_t S = 1;
     const int64_t forced = g_opt_segment_len.load();
     if (L <= 0 || bps == 0) {
         S = 1;
     } else if (forced > 0) {
-        // keep the grid (segments x blocks per segment) within 2^30 blocks
         const int64_t max_seg = ((int64_t)1 << 30) / (bps > 0 ? bps : 1);
         int64_t sl = forced < L ? forced : L;
+        if (sl > max_len) sl = max_len;
         if ((L + sl - 1) / sl > max_seg) sl = (L + max_seg - 1) / max_seg;
         pl.seg_len = sl;
         pl.S = (int)((L + sl - 1) / sl);
@@ -126,8 +168,8 @@ Plan make_plan(int64_t Bsz, int64_t L, int64_t Dm, int cus) {
     } else {
         const int64_t cap = L / kMinSegment > 1 ? L / kMinSegment : 1;
         const int64_t c = cus > 0 ? cus : 256;
-        S = (4 * c + bps - 1) / bps;  // fallback: at least 4 blocks per CU
-        for (int64_t m = 4; m <= 8; ++m) {
+        S = (kBlocksPerCu * c + bps - 1) / bps;  // fallback: at least kBlocksPerCu per CU
+        for (int64_t m = kBlocksPerCu; m <= kBlocksPerCu + kBlocksPerCu / 2; ++m) {
             if ((m * c) % bps == 0) {
                 S = m * c / bps;
                 break;
@@ -135,6 +177,7 @@ Plan make_plan(int64_t Bsz, int64_t L, int64_t Dm, int cus) {
         }
         if (S > cap) S = cap;
         if (S < 1) S = 1;
+        if ((L + S - 1) / S > max_len) S = (L + max_len - 1) / max_len;
     }
     pl.seg_len = L > 0 ? (L + S - 1) / S : 1;
     pl.S = L > 0 ? (int)((L + pl.seg_len - 1) / pl.seg_len) : 1;
@@ -257,7 +300,8 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     hipError_t e;
     if (L == 0) {
         p.S = 1;
-        e = ssm::launch_state_init(p, (int)N, s);
+        if (h_final == nullptr) return ok();
+        e = timed(SSM_K_STATE_INIT, s, [&] { return ssm::launch_state_init(p, (int)N, s); });
         return e == hipSuccess ? ok() : hip_fail(e, "state init launch");
     }
 
@@ -266,7 +310,7 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     int cus = 0;
     if ((rc = device_cus(dev, &cus))) return rc;
-    const Plan pl = make_plan(Bsz, L, Dm, cus);
+    const Plan pl = make_plan(Bsz, L, Dm, es, cus);
     p.S = pl.S;
     p.seg_len = pl.seg_len;
     p.tiles_per_b = pl.tiles_per_b;
@@ -285,14 +329,17 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     p.agg = agg_bytes ? base + bc_bytes : nullptr;
     p.gin = gin_bytes ? base + bc_bytes + agg_bytes : nullptr;
 
-    if ((e = ssm::launch_bc_prep(p, (int)N, dtype, s)) != hipSuccess) return hip_fail(e, "B/C prep launch");
+    const int n = (int)N;
+    if ((e = timed(SSM_K_BC_PREP, s, [&] { return ssm::launch_bc_prep(p, n, dtype, s); })) != hipSuccess)
+        return hip_fail(e, "B/C prep launch");
     if (pl.S > 1) {
-        if ((e = ssm::launch_scan_aggregate(p, (int)N, dtype, s)) != hipSuccess)
+        if ((e = timed(SSM_K_SCAN_AGGREGATE, s, [&] { return ssm::launch_scan_aggregate(p, n, dtype, s); })) !=
+            hipSuccess)
             return hip_fail(e, "segment aggregate launch");
-        if ((e = ssm::launch_scan_carry(p, (int)N, dtype, s)) != hipSuccess)
+        if ((e = timed(SSM_K_SCAN_CARRY, s, [&] { return ssm::launch_scan_carry(p, n, dtype, s); })) != hipSuccess)
             return hip_fail(e, "segment carry launch");
     }
-    if ((e = ssm::launch_scan_output(p, (int)N, dtype, s)) != hipSuccess)
+    if ((e = timed(SSM_K_SCAN_OUTPUT, s, [&] { return ssm::launch_scan_output(p, n, dtype, s); })) != hipSuccess)
         return hip_fail(e, "segment output launch");
     return ok();
 }
@@ -330,7 +377,8 @@ int step_impl(const void *x, const void *delta, const float *A, const void *B, c
     p.y = y;
     p.Bsz = Bsz;
     p.Dm = Dm;
-    hipError_t e = ssm::launch_step(p, (int)N, dtype, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = timed(SSM_K_STEP, s, [&] { return ssm::launch_step(p, (int)N, dtype, s); });
     return e == hipSuccess ? ok() : hip_fail(e, "decode step launch");
 }
 
@@ -391,6 +439,16 @@ int ssm_set_option(int option, int64_t value) {
             if (value != 0 && value != 1) return fail(SSM_ERR_BAD_OPTION, "force-general must be 0 or 1");
             g_opt_force_general.store(value);
             return ok();
+        case SSM_OPT_PROFILE:
+            if (value != 0 && value != 1) return fail(SSM_ERR_BAD_OPTION, "profile must be 0 or 1");
+            g_opt_profile.store(value);
+            return ok();
+        case SSM_OPT_STEP_CHANNELS:
+            if (value != 1 && value != 2 && value != 4)
+                return fail(SSM_ERR_BAD_OPTION, "step channels per thread must be 1, 2 or 4");
+            g_opt_step_channels.store(value);
+            ssm::set_step_unroll((int)value);
+            return ok();
         default:
             return fail(SSM_ERR_BAD_OPTION, "unknown option %d", option);
     }
@@ -400,6 +458,8 @@ int64_t ssm_get_option(int option) {
     switch (option) {
         case SSM_OPT_SEGMENT_LEN: return g_opt_segment_len.load();
         case SSM_OPT_FORCE_GENERAL: return g_opt_force_general.load();
+        case SSM_OPT_PROFILE: return g_opt_profile.load();
+        case SSM_OPT_STEP_CHANNELS: return g_opt_step_channels.load();
         default: return -1;
     }
 }
@@ -418,10 +478,36 @@ int ssm_scan_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, int 
         int rc = device_cus(dev, &cus);
         if (rc) return rc;
     }
-    const Plan pl = make_plan(Bsz, L, Dm, cus);
+    const Plan pl = make_plan(Bsz, L, Dm, dtype_size(dtype), cus);
     *segments = pl.S;
     *segment_len = pl.seg_len;
     return ok();
+}
+
+int ssm_profile_read(double *total_ms, int64_t *launches, int n) {
+    std::vector<ProfRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        recs.swap(g_prof);
+    }
+    for (int k = 0; k < n; ++k) {
+        if (total_ms) total_ms[k] = 0.0;
+        if (launches) launches[k] = 0;
+    }
+    int rc = SSM_OK;
+    for (const ProfRec &r : recs) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && rc == SSM_OK) rc = hip_fail(e, "reading kernel timing events");
+        if (e == hipSuccess && r.kind >= 0 && r.kind < n) {
+            if (total_ms) total_ms[r.kind] += ms;
+            if (launches) launches[r.kind] += 1;
+        }
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    return rc == SSM_OK ? ok() : rc;
 }
 
 int ssm_release_workspaces(void) {

@@ -73,6 +73,43 @@ __device__ __forceinline__ float expm1_and_exp(float z, float& e) {
     return (__builtin_fabsf(z) < 0.015625f) ? poly : (e - 1.0f);
 }
 
+// The same for an argument already in base-2 units (z2 = z log2(e)), which
+// saves the scaling multiply: the cubic is z(1 + z/2 + z^2/6) with z = z2 ln2
+// folded into its coefficients, used for |z| < 2^-6.
+__device__ __forceinline__ float expm1_and_exp2(float z2, float& e) {
+    constexpr float c1 = 0.6931471805599453f;        // ln2
+    constexpr float c2 = 0.2402265069591007f;        // ln2^2 / 2
+    constexpr float c3 = 0.05550410866482158f;       // ln2^3 / 6
+    e = fast_exp2(z2);
+    const float poly = z2 * __builtin_fmaf(z2, __builtin_fmaf(z2, c3, c2), c1);
+    return (__builtin_fabsf(z2) < 0.015625f * kLog2e) ? poly : (e - 1.0f);
+}
+__device__ __forceinline__ double expm1_and_exp2(double z, double& e) { return expm1_and_exp(z, e); }
+
+// Raw buffer descriptor over [base, base + bytes): loads outside read 0 and
+// stores outside are dropped by the hardware range check.  Word 3 is the
+// gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff);
+template <>
+__device__ __forceinline__ bf16 buf_load<bf16>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+template <>
+__device__ __forceinline__ float buf_load<float>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store(bf16 v, __amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store(float v, __amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+
 // Accurate fp32 variant (ocml expm1f), for the fp32-storage decode step.
 __device__ __forceinline__ float expm1_and_exp_precise(float z, float& e) {
     const float m = expm1f(z);
@@ -80,8 +117,10 @@ __device__ __forceinline__ float expm1_and_exp_precise(float z, float& e) {
     return m;
 }
 
-__device__ __forceinline__ double exp_(double z) { return exp(z); }
-__device__ __forceinline__ float exp_(float z) { return fast_exp2(z * kLog2e); }
+// exp of an argument in the arithmetic type's exponent units: natural units
+// in fp64 (ocml exp), base-2 units in fp32 (z already multiplied by log2 e).
+__device__ __forceinline__ double exp_units(double z) { return exp(z); }
+__device__ __forceinline__ float exp_units(float z2) { return fast_exp2(z2); }
 
 // Wave-uniform value (the compiler then keeps it in an SGPR).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

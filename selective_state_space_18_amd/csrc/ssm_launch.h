@@ -46,5 +46,7 @@ hipError_t launch_scan_carry(const ScanParams &p, int N, int dtype, hipStream_t 
 hipError_t launch_scan_output(const ScanParams &p, int N, int dtype, hipStream_t s);
 hipError_t launch_state_init(const ScanParams &p, int N, hipStream_t s);
 hipError_t launch_step(const StepParams &p, int N, int dtype, hipStream_t s);
+// Channels per thread of the decode-step kernel (1, 2 or 4).
+void set_step_unroll(int u);
 
 }  // namespace ssm

@@ -19,6 +19,7 @@ namespace ssm {
 namespace {
 
 constexpr int kBlock = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int N>
 struct StepShape {
@@ -28,77 +29,108 @@ struct StepShape {
 
 // kVec: h and A rows are read/written as 16-byte vectors (needs 16-byte
 // aligned base pointers, checked on the host).
-template <typename T, int N, bool kPrecise, bool kVec>
-__global__ __launch_bounds__(kBlock) void step_kernel(StepParams p) {
+// kU: channels per thread.  A thread owns lane j of kU channels spaced one
+// grid-width apart, so every wave-wide access stays contiguous, and it issues
+// all kU state loads before using any of them: kU x 16 bytes in flight per
+// lane hides HBM latency at a modest occupancy.
+template <typename T, int N, bool kPrecise, bool kVec, int kU>
+__global__ __launch_bounds__(kBlock) void step_kernel(StepParams p, int64_t chan_stride) {
     constexpr int Q = StepShape<N>::Q;
     constexpr int SPL = StepShape<N>::SPL;
     const int64_t BD = p.Bsz * p.Dm;
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t ch = i / Q;
-    const int j = (int)(i - ch * Q);
+    const int64_t ch0 = i / Q;
+    const int j = (int)(i - ch0 * Q);
     // Q divides the wave size, so the Q lanes of a channel leave together.
-    if (ch >= BD) return;
-    const int64_t b = ch / p.Dm;
-    const int64_t d = ch - b * p.Dm;
+    if (ch0 >= BD) return;
 
-    const float xv = to_f32(static_cast<const T *>(p.x)[ch]);
-    const float dv = to_f32(static_cast<const T *>(p.delta)[ch]);
-    const T *Bp = static_cast<const T *>(p.B) + b * N + j * SPL;
-    const T *Cp = static_cast<const T *>(p.C) + b * N + j * SPL;
-    const float *Ap = p.A + d * N + j * SPL;
-    float *hp = p.h + ch * N + j * SPL;
+    float h[kU][SPL], a[kU][SPL], xv[kU], dv[kU];
+    int64_t chs[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int64_t ch = ch0 + u * chan_stride;
+        chs[u] = ch < BD ? ch : ch0;  // channels past the end redo ch0 and store nothing
+        const int64_t d = chs[u] % p.Dm;
+        float *hp = p.h + chs[u] * N + j * SPL;
+        const float *Ap = p.A + d * N + j * SPL;
+        if constexpr (kVec && SPL == 4) {
+            const f32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(hp));
+            h[u][0] = hv.x; h[u][1] = hv.y; h[u][2] = hv.z; h[u][3] = hv.w;
+            const float4 av = *reinterpret_cast<const float4 *>(Ap);
+            a[u][0] = av.x; a[u][1] = av.y; a[u][2] = av.z; a[u][3] = av.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < SPL; ++k) {
+                h[u][k] = hp[k];
+                a[u][k] = Ap[k];
+            }
+        }
+        xv[u] = to_f32(static_cast<const T *>(p.x)[chs[u]]);
+        dv[u] = to_f32(static_cast<const T *>(p.delta)[chs[u]]);
+    }
 
-    float h[SPL], a[SPL];
-    if constexpr (kVec && SPL == 4) {
-        const float4 hv = *reinterpret_cast<const float4 *>(hp);
-        h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
-        const float4 av = *reinterpret_cast<const float4 *>(Ap);
-        a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
-    } else {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int64_t ch = chs[u];
+        const int64_t b = ch / p.Dm;
+        const int64_t d = ch - b * p.Dm;
+        const T *Bp = static_cast<const T *>(p.B) + b * N + j * SPL;
+        const T *Cp = static_cast<const T *>(p.C) + b * N + j * SPL;
+        float yv = 0.f;
 #pragma unroll
         for (int k = 0; k < SPL; ++k) {
-            h[k] = hp[k];
-            a[k] = Ap[k];
+            float abar;
+            const float E = kPrecise ? expm1_and_exp_precise(dv[u] * a[u][k], abar)
+                                     : expm1_and_exp(dv[u] * a[u][k], abar);
+            float coef;
+            if constexpr (kPrecise)
+                coef = (a[u][k] != 0.f) ? E / a[u][k] : dv[u];
+            else
+                coef = (a[u][k] != 0.f) ? E * __builtin_amdgcn_rcpf(a[u][k]) : dv[u];
+            const float bx = to_f32(Bp[k]) * xv[u];
+            h[u][k] = __builtin_fmaf(abar, h[u][k], coef * bx);
+            yv = __builtin_fmaf(to_f32(Cp[k]), h[u][k], yv);
         }
+        const bool live = ch0 + u * chan_stride < BD;
+        float *hp = p.h + ch * N + j * SPL;
+        if (live) {
+            if constexpr (kVec && SPL == 4) {
+                const f32x4 hv = {h[u][0], h[u][1], h[u][2], h[u][3]};
+                __builtin_nontemporal_store(hv, reinterpret_cast<f32x4 *>(hp));
+            } else {
+#pragma unroll
+                for (int k = 0; k < SPL; ++k) hp[k] = h[u][k];
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < Q; off <<= 1) yv += __shfl_xor(yv, off, Q);
+        if (live && j == 0) static_cast<T *>(p.y)[ch] = from_acc<T>(__builtin_fmaf(p.D[d], xv[u], yv));
     }
+}
 
-    float yv = 0.f;
-#pragma unroll
-    for (int k = 0; k < SPL; ++k) {
-        float abar;
-        const float E = kPrecise ? expm1_and_exp_precise(dv * a[k], abar) : expm1_and_exp(dv * a[k], abar);
-        float coef;
-        if constexpr (kPrecise)
-            coef = (a[k] != 0.f) ? E / a[k] : dv;
-        else
-            coef = (a[k] != 0.f) ? E * __builtin_amdgcn_rcpf(a[k]) : dv;
-        const float bx = to_f32(Bp[k]) * xv;
-        h[k] = __builtin_fmaf(abar, h[k], coef * bx);
-        yv = __builtin_fmaf(to_f32(Cp[k]), h[k], yv);
-    }
+int g_step_unroll = 4;  // channels per thread (1, 2 or 4)
 
-    if constexpr (kVec && SPL == 4) {
-        *reinterpret_cast<float4 *>(hp) = make_float4(h[0], h[1], h[2], h[3]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < SPL; ++k) hp[k] = h[k];
-    }
-#pragma unroll
-    for (int off = 1; off < Q; off <<= 1) yv += __shfl_xor(yv, off, Q);
-    if (j == 0) static_cast<T *>(p.y)[ch] = from_acc<T>(__builtin_fmaf(p.D[d], xv, yv));
+template <typename T, bool kPrecise, int N, bool kVec, int kU>
+hipError_t launch_u(const StepParams &p, hipStream_t s) {
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t chan_stride = (BD + kU - 1) / kU;  // channels per "row" of the grid
+    const int64_t threads = chan_stride * StepShape<N>::Q;
+    const unsigned grid = (unsigned)((threads + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL((step_kernel<T, N, kPrecise, kVec, kU>), dim3(grid), dim3(kBlock), 0, s, p, chan_stride);
+    return hipGetLastError();
 }
 
 template <typename T, bool kPrecise, int N>
 hipError_t launch_n(const StepParams &p, hipStream_t s) {
-    const int64_t threads = p.Bsz * p.Dm * StepShape<N>::Q;
-    if (threads == 0) return hipSuccess;
-    const unsigned grid = (unsigned)((threads + kBlock - 1) / kBlock);
+    if (p.Bsz * p.Dm == 0) return hipSuccess;
     const bool vec = ((reinterpret_cast<uintptr_t>(p.h) | reinterpret_cast<uintptr_t>(p.A)) & 15) == 0;
-    if (vec)
-        hipLaunchKernelGGL((step_kernel<T, N, kPrecise, true>), dim3(grid), dim3(kBlock), 0, s, p);
-    else
-        hipLaunchKernelGGL((step_kernel<T, N, kPrecise, false>), dim3(grid), dim3(kBlock), 0, s, p);
-    return hipGetLastError();
+    const int u = g_step_unroll;
+    if (vec) {
+        if (u >= 4) return launch_u<T, kPrecise, N, true, 4>(p, s);
+        if (u == 2) return launch_u<T, kPrecise, N, true, 2>(p, s);
+        return launch_u<T, kPrecise, N, true, 1>(p, s);
+    }
+    return launch_u<T, kPrecise, N, false, 1>(p, s);
 }
 
 template <typename T, bool kPrecise>
@@ -114,6 +146,8 @@ hipError_t launch_t(const StepParams &p, int N, hipStream_t s) {
 }
 
 }  // namespace
+
+void set_step_unroll(int u) { g_step_unroll = u; }
 
 hipError_t launch_step(const StepParams &p, int N, int dtype, hipStream_t s) {
     if (dtype == 0) return launch_t<float, true>(p, N, s);

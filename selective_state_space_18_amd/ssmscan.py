@@ -21,7 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
-SSM_OPT_SEGMENT_LEN, SSM_OPT_FORCE_GENERAL = 1, 2
+SSM_OPT_SEGMENT_LEN, SSM_OPT_FORCE_GENERAL, SSM_OPT_PROFILE, SSM_OPT_STEP_CHANNELS = 1, 2, 3, 4
+KERNEL_KINDS = ("bc_prep", "scan_aggregate", "scan_carry", "scan_output", "step", "state_init")
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_BAD_DTYPE",
           4: "SSM_ERR_UNSUPPORTED_N", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_NOMEM",
           8: "SSM_ERR_HIP", 9: "SSM_ERR_BAD_OPTION"}
@@ -29,7 +30,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_B
 # Every symbol include/ssmscan.h declares.
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_strerror",
            "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
-           "ssm_scan_plan", "ssm_release_workspaces")
+           "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read")
 
 
 class SSMError(RuntimeError):
@@ -73,6 +74,8 @@ def lib():
     L.ssm_scan_plan.restype = ctypes.c_int
     L.ssm_release_workspaces.argtypes = []
     L.ssm_release_workspaces.restype = ctypes.c_int
+    L.ssm_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), ctypes.c_int]
+    L.ssm_profile_read.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -105,6 +108,15 @@ def plan(Bsz, L, Dm, N, dtype=SSM_BF16, compute_units=0):
     _check(lib().ssm_scan_plan(Bsz, L, Dm, N, dtype, compute_units, ctypes.byref(s), ctypes.byref(sl)),
            "ssm_scan_plan")
     return s.value, sl.value
+
+
+def profile_read():
+    """{kernel kind: (total ms, launches)} since the last read (SSM_OPT_PROFILE)."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (_i64 * n)()
+    _check(lib().ssm_profile_read(ms, cnt, n), "ssm_profile_read")
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}
 
 
 def release_workspaces() -> None:
@@ -171,9 +183,13 @@ def scan_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, want_state
     if h_final is not None:
         _need(h_final, "h_final", (Bsz, Dm, N), torch.float32, dev)
     with torch.cuda.device(dev):
-        rc = lib().ssm_scan_fwd_ex(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                   _ptr(h_init), _ptr(y), _ptr(h_final), Bsz, L, Dm, N, code,
-                                   _stream(dev))
+        if h_init is None:
+            rc = lib().ssm_scan_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(y), _ptr(h_final), Bsz, L, Dm, N, code, _stream(dev))
+        else:
+            rc = lib().ssm_scan_fwd_ex(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(h_init), _ptr(y), _ptr(h_final), Bsz, L, Dm, N, code,
+                                       _stream(dev))
     _check(rc, "ssm_scan_fwd")
     return y, h_final
 

@@ -109,7 +109,8 @@ def test_step_argument_errors(L):
 
 def test_options(L):
     from selective_state_space_18_amd import ssmscan
-    assert L.ssm_get_option(1) == 0 and L.ssm_get_option(2) == 0
+    assert L.ssm_get_option(1) == 0 and L.ssm_get_option(2) == 0 and L.ssm_get_option(4) == 4
+    assert L.ssm_set_option(4, 3) == 9
     assert L.ssm_set_option(1, -1) == 9
     assert L.ssm_set_option(2, 3) == 9
     assert L.ssm_set_option(99, 0) == 9
@@ -123,9 +124,9 @@ def test_options(L):
 
 @pytest.mark.parametrize("shape,expect", [
     # (Bsz, L, Dm) on 256 CUs -> (segments, segment length)
-    ((4, 16384, 5120), (16, 1024)),      # Mamba-2.8B-shaped layer: 5 blocks per CU
-    ((1, 1 << 20, 1024), (256, 4096)),   # long context: 4 blocks per CU
-    ((8, 2048, 1536), (32, 64)),         # Mamba-130M-shaped layer: 6 blocks per CU
+    ((4, 16384, 5120), (64, 256)),       # Mamba-2.8B-shaped layer: 20 blocks per CU
+    ((1, 1 << 20, 1024), (1024, 1024)),  # long context: 16 blocks per CU
+    ((8, 2048, 1536), (32, 64)),         # Mamba-130M-shaped layer: capped by the 64-step minimum
     ((1, 256, 64), (4, 64)),             # tiny: capped by the 64-step minimum
     ((1, 100, 64), (1, 100)),            # too short to split
     ((3, 1000, 100), (15, 67)),          # capped at 1000 // 64 = 15 segments
