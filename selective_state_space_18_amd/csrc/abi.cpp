@@ -50,7 +50,7 @@ int hip_fail(hipError_t e, const char *what) {
 std::atomic<int64_t> g_opt_segment_len{0};
 std::atomic<int64_t> g_opt_force_general{0};
 std::atomic<int64_t> g_opt_profile{0};
-std::atomic<int64_t> g_opt_step_channels{4};
+std::atomic<int64_t> g_opt_step_channels{1};
 
 // ---------------------------------------------------------------------------
 // Optional per-kernel event timing (SSM_OPT_PROFILE).

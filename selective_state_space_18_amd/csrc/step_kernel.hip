@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepParams p, int64_t chan
     }
 }
 
-int g_step_unroll = 4;  // channels per thread (1, 2 or 4)
+int g_step_unroll = 1;  // channels per thread (1, 2 or 4)
 
 template <typename T, bool kPrecise, int N, bool kVec, int kU>
 hipError_t launch_u(const StepParams &p, hipStream_t s) {

@@ -109,7 +109,7 @@ def test_step_argument_errors(L):
 
 def test_options(L):
     from selective_state_space_18_amd import ssmscan
-    assert L.ssm_get_option(1) == 0 and L.ssm_get_option(2) == 0 and L.ssm_get_option(4) == 4
+    assert L.ssm_get_option(1) == 0 and L.ssm_get_option(2) == 0 and L.ssm_get_option(4) == 1
     assert L.ssm_set_option(4, 3) == 9
     assert L.ssm_set_option(1, -1) == 9
     assert L.ssm_set_option(2, 3) == 9
