@@ -151,6 +151,33 @@ def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
         ss.set_option(ss.SSM_OPT_PROFILE, 0)
     k_ms = prof["step"][0] / prof["step"][1]
     alg = generate.alg_bytes_step(cfg)
+    # The same steps replayed from a captured HIP graph (a decode loop of a
+    # serving engine): removes the host launch gap between steps.
+    graph_ms = None
+    try:
+        per_graph = 16 * layers // 4
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            fn(0)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(per_graph):
+                fn(i)
+        reps = max(1, n_tokens // per_graph)
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b) / (reps * per_graph)
+        del g
+    except Exception as e:  # graph capture is an extra figure, never the value
+        log(f"[bench] decode graph timing skipped: {e}")
     del states, toks, y
     torch.cuda.empty_cache()
     return {
@@ -164,6 +191,8 @@ def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
                      "traffic": traffic_for("step_" + cfg.name, "step_kernel.hip"),
                      "avg_ms": round(k_ms, 5)},
         "state_layers_cycled": layers,
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "graph_value": None if graph_ms is None else cfg.elems_per_step() / (graph_ms * 1e-3),
     }
 
 

@@ -100,7 +100,10 @@ __device__ __forceinline__ Acc scan_step(const ChanConst<N, kStruct, Acc> &cc, c
     if constexpr (kStruct) {
         Acc r;
         const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
-        const Acc xa = xv * cc.inva;
+        // The aggregate pass (no y) carries j = A[d,0] g instead of g, which
+        // turns x/A[d,0] into x: j <- j + E_n (j + B_t[n] x).  The caller
+        // rescales j once at the end of the segment.
+        const Acc xa = kOut ? xv * cc.inva : xv;
         Acc E = E1;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
@@ -130,8 +133,14 @@ __device__ __forceinline__ Acc scan_step(const ChanConst<N, kStruct, Acc> &cc, c
     return yv;
 }
 
+// B/C rows are read through the constant address space: the kernel never
+// writes them, and telling the compiler so keeps them in scalar loads even
+// though y leaves through buffer stores it cannot see through.
+template <typename Acc>
+using const_row_ptr = const __attribute__((address_space(4))) Acc *;
+
 template <int N, typename Acc>
-__device__ __forceinline__ void load_row(Acc (&dst)[2 * N], const Acc *__restrict__ src) {
+__device__ __forceinline__ void load_row(Acc (&dst)[2 * N], const_row_ptr<Acc> src) {
 #pragma unroll
     for (int i = 0; i < 2 * N; ++i) dst[i] = src[i];
 }
@@ -141,20 +150,15 @@ __device__ __forceinline__ void load_row(Acc (&dst)[2 * N], const Acc *__restric
 // stride of one time step.  All offsets are 32-bit (the planner keeps a
 // segment's span below 1 GiB) and out-of-range accesses are dropped by the
 // descriptors' range check.
-// y is written through a plain restrict pointer (buffer-intrinsic stores
-// would hide from the compiler that the B/C rows are never written, and the
-// rows would then leave the scalar loads).
 template <typename T>
 struct SegIO {
-    __amdgpu_buffer_rsrc_t x, dl;
-    T *__restrict__ y;  // this lane's y at the segment start
-    int32_t voff;       // lane byte offset within a step (0 for idle lanes)
-    int32_t row;        // bytes per time step (Dm * sizeof(T))
-    int64_t ystride;    // elements per time step (Dm)
+    __amdgpu_buffer_rsrc_t x, dl, y;
+    int32_t voff;  // lane byte offset within a step (0 for idle lanes)
+    int32_t row;   // bytes per time step (Dm * sizeof(T))
 };
 
 template <typename T, int N, bool kStruct, bool kOut, typename Acc>
-__device__ __forceinline__ void run_group(const SegIO<T> &io, const Acc *__restrict__ bcp, int tb, int nsteps,
+__device__ __forceinline__ void run_group(const SegIO<T> &io, const_row_ptr<Acc> bcp, int tb, int nsteps,
                                           const T (&xs)[kPrefetch], const T (&ds)[kPrefetch],
                                           const ChanConst<N, kStruct, Acc> &cc, Acc Dd, Acc (&g)[N],
                                           Acc &lam, Acc (&rowc)[2 * N]) {
@@ -170,7 +174,7 @@ __device__ __forceinline__ void run_group(const SegIO<T> &io, const Acc *__restr
             const Acc dv = (Acc)to_f32(ds[k]);
             const Acc yv = scan_step<N, kStruct, kOut>(cc, rowc, xv, dv, g);
             if constexpr (kOut) {
-                io.y[(int64_t)(tb + k) * io.ystride] = from_acc<T>(fma_(Dd, xv, yv));
+                buf_store(from_acc<T>(fma_(Dd, xv, yv)), io.y, io.voff, (tb + k) * io.row);
             } else {
                 lam += dv;
             }
@@ -199,7 +203,7 @@ __device__ __forceinline__ void load_group(const SegIO<T> &io, int tb, int last,
 // channel: they compute exactly what that channel's lane computes and store
 // the identical value.
 template <typename T, int N, bool kStruct, bool kOut, typename Acc>
-__device__ __forceinline__ void run_segment(const SegIO<T> &io, const Acc *__restrict__ bcp, int nsteps,
+__device__ __forceinline__ void run_segment(const SegIO<T> &io, const_row_ptr<Acc> bcp, int nsteps,
                                             const float (&Ar)[N], Acc Dd, Acc (&g)[N], Acc &lam) {
     const ChanConst<N, kStruct, Acc> cc(Ar);
     const int last = nsteps - 1;
@@ -274,17 +278,21 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
     SegIO<T> io;
     io.x = make_rsrc(static_cast<const T *>(p.x) + off, span);
     io.dl = make_rsrc(static_cast<const T *>(p.delta) + off, span);
-    io.y = kOut ? static_cast<T *>(p.y) + off + (d - d0) : nullptr;
+    io.y = make_rsrc(kOut ? static_cast<const T *>(p.y) + off : static_cast<const T *>(p.x) + off, kOut ? span : 0);
     io.voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
     io.row = row;
-    io.ystride = p.Dm;
-    const Acc *bcp = static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N);
+    const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
     Acc lam = 0;
 
     run_segment<T, N, kStruct, kOut>(io, bcp, nsteps, Ar, Dd, g, lam);
 
     if (!active) return;
     if constexpr (!kOut) {
+        if constexpr (kStruct) {
+            const Acc inva = (Acc)1 / (Acc)Ar[0];
+#pragma unroll
+            for (int n = 0; n < N; ++n) g[n] *= inva;
+        }
         Acc *a = static_cast<Acc *>(p.agg) + (int64_t)s * (N + 1) * BD + ch;
 #pragma unroll
         for (int n = 0; n < N; ++n) a[(int64_t)n * BD] = g[n];
@@ -320,22 +328,36 @@ __global__ __launch_bounds__(kBlock) void scan_carry_kernel(ScanParams p) {
     const int64_t sa = (int64_t)(N + 1) * BD, sg = (int64_t)N * BD;
     out[0] = carry;
     const int nseg = p.S - 1;
-    // The decay factors do not depend on the carry, so a batch of them is
-    // computed up front; only the FMA chain is sequential.
+    if (nseg <= 0) return;
+    // The summaries of the next batch are in flight while the current batch's
+    // FMA chain runs; the decay factors do not depend on the carry.
+    Acc lc[kBatch], gc[kBatch], ln[kBatch], gn[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+        const int s = k < nseg ? k : nseg - 1;
+        lc[k] = lam[s * sa];
+        gc[k] = gl[s * sa];
+    }
     for (int s0 = 0; s0 < nseg; s0 += kBatch) {
-        Acc dec[kBatch], loc[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-            const int s = (s0 + k < nseg) ? s0 + k : nseg - 1;
-            dec[k] = exp_units(a * lam[s * sa]);
-            loc[k] = gl[s * sa];
+            const int s = (s0 + kBatch + k < nseg) ? s0 + kBatch + k : nseg - 1;
+            ln[k] = lam[s * sa];
+            gn[k] = gl[s * sa];
         }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) lc[k] = exp_units(a * lc[k]);
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             if (s0 + k < nseg) {
-                carry = fma_(dec[k], carry, loc[k]);
+                carry = fma_(lc[k], carry, gc[k]);
                 out[(int64_t)(s0 + k + 1) * sg] = carry;
             }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            lc[k] = ln[k];
+            gc[k] = gn[k];
         }
     }
 }
