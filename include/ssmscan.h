@@ -112,6 +112,32 @@ int ssm_scan_fwd_ex(const void *x, const void *delta, const float *A,
                     int dtype, void *stream);
 
 /*
+ * Packed variable-length scan (resumable prefill of several sequences at once,
+ * without padding).  nseq sequences are concatenated along time in one row:
+ * sequence k covers steps cu_seqlens[k] .. cu_seqlens[k+1]-1.
+ *
+ *   x, delta, y : [L][Dm]        dtype
+ *   B, C        : [L][N]         dtype
+ *   A           : [Dm][N] fp32;  D : [Dm] fp32
+ *   cu_seqlens  : [nseq+1] int64, device memory; cu_seqlens[0] = 0,
+ *                 non-decreasing, cu_seqlens[nseq] = L (empty sequences allowed)
+ *   h_init      : [nseq][Dm][N] fp32 or NULL -- state each sequence starts from
+ *   h_final     : [nseq][Dm][N] fp32 or NULL -- each sequence's last state (its
+ *                 h_init, or zero, if the sequence is empty)
+ *
+ * The state restarts at every sequence start, so y of each sequence equals
+ * ssm_scan_fwd_ex over that sequence alone.  cu_seqlens is read on the device
+ * and is not validated; values that break the rules above give unspecified
+ * results but every access stays inside the buffers.  h_init must not overlap
+ * h_final; no output may overlap an input.
+ */
+int ssm_scan_varlen_fwd(const void *x, const void *delta, const float *A,
+                        const void *B, const void *C, const float *D,
+                        const int64_t *cu_seqlens, int64_t nseq,
+                        const float *h_init, void *y, float *h_final,
+                        int64_t L, int64_t Dm, int64_t N, int dtype, void *stream);
+
+/*
  * One recurrent decode step on a resident state, updated in place
  * ("Mamba SSM Nedir?", section "Karmasiklik Karsilastirmasi": inference
  * updates a fixed-size state per token).  bf16 I/O:

@@ -249,7 +249,9 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int scan_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
               const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
-              int64_t Dm, int64_t N, int dtype, void *stream) {
+              int64_t Dm, int64_t N, int dtype, void *stream, const int64_t *cu = nullptr,
+              int64_t nseq = 0) {
+    const bool varlen = cu != nullptr;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
     if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
     if (Bsz < 0 || L < 0 || Dm < 0)
@@ -261,23 +263,27 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
         return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
                     (long long)L, (long long)Dm, (long long)N);
     const int64_t es = dtype_size(dtype);
+    int64_t SDN = BDN;  // elements of h_init / h_final
+    if (varlen && !mul_ok(nseq, DN, &SDN)) return fail(SSM_ERR_BAD_DIM, "nseq * Dm * N overflows");
     const Arg in[] = {{x, BLD, es, "x"}, {delta, BLD, es, "delta"}, {A, DN, 4, "A"}, {B, BLN, es, "B"},
-                      {C, BLN, es, "C"}, {D, Dm, 4, "D"}};
-    const Arg hi = {h_init, h_init ? BDN : 0, 4, "h_init"};
+                      {C, BLN, es, "C"}, {D, Dm, 4, "D"}, {cu, varlen ? nseq + 1 : 0, 8, "cu_seqlens"}};
+    const int nin = varlen ? 7 : 6;
+    const Arg hi = {h_init, h_init ? SDN : 0, 4, "h_init"};
     const Arg ya = {y, BLD, es, "y"};
-    const Arg hf = {h_final, h_final ? BDN : 0, 4, "h_final"};
+    const Arg hf = {h_final, h_final ? SDN : 0, 4, "h_final"};
     int rc;
-    if ((rc = check_args(in, 6)) || (rc = check_args(&hi, 1)) || (rc = check_args(&ya, 1)) ||
+    if ((rc = check_args(in, nin)) || (rc = check_args(&hi, 1)) || (rc = check_args(&ya, 1)) ||
         (rc = check_args(&hf, 1)))
         return rc;
-    if ((rc = check_output(ya, in, 6)) || (rc = check_output(ya, &hi, 1)) || (rc = check_output(hf, in, 6)) ||
+    if ((rc = check_output(ya, in, nin)) || (rc = check_output(ya, &hi, 1)) || (rc = check_output(hf, in, nin)) ||
         (rc = check_output(hf, &ya, 1)))
         return rc;
-    if (h_init != nullptr && h_final != nullptr && (const void *)h_init != (const void *)h_final &&
-        overlaps(hi, hf))
-        return fail(SSM_ERR_ALIAS, "h_init partially overlaps h_final");
+    if (h_init != nullptr && h_final != nullptr && overlaps(hi, hf) &&
+        (varlen || (const void *)h_init != (const void *)h_final))
+        return fail(SSM_ERR_ALIAS, varlen ? "h_init overlaps h_final (not allowed for packed sequences)"
+                                          : "h_init partially overlaps h_final");
 
-    if (BD == 0) return ok();
+    if (BD == 0 || (varlen && nseq == 0)) return ok();
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
     ssm::ScanParams p;
@@ -296,8 +302,16 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     p.Dm = Dm;
     p.waves_per_block = kWavesPerBlock;
     p.force_general = g_opt_force_general.load() ? 1 : 0;
+    p.cu = cu;
+    p.nseq = nseq;
 
     hipError_t e;
+    if (varlen) {
+        // empty sequences are never visited by the scan kernels
+        e = timed(SSM_K_STATE_INIT, s, [&] { return ssm::launch_varlen_empty(p, (int)N, s); });
+        if (e != hipSuccess) return hip_fail(e, "empty-sequence state launch");
+        if (L == 0) return ok();
+    }
     if (L == 0) {
         p.S = 1;
         if (h_final == nullptr) return ok();
@@ -320,14 +334,16 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     const size_t bc_bytes = align256((size_t)BL * 2 * N * acc);
     const size_t agg_bytes = pl.S > 1 ? align256((size_t)(pl.S - 1) * (N + 1) * BD * acc) : 0;
     const size_t gin_bytes = pl.S > 1 ? align256((size_t)pl.S * N * BD * acc) : 0;
+    const size_t flag_bytes = (varlen && pl.S > 1) ? align256((size_t)pl.S * sizeof(int)) : 0;
 
     std::lock_guard<std::mutex> lk(g_ws_mu);
     void *ws = nullptr;
-    if ((rc = workspace(dev, s, bc_bytes + agg_bytes + gin_bytes, &ws))) return rc;
+    if ((rc = workspace(dev, s, bc_bytes + agg_bytes + gin_bytes + flag_bytes, &ws))) return rc;
     char *base = static_cast<char *>(ws);
     p.bc = base;
     p.agg = agg_bytes ? base + bc_bytes : nullptr;
     p.gin = gin_bytes ? base + bc_bytes + agg_bytes : nullptr;
+    p.seg_reset = flag_bytes ? reinterpret_cast<int *>(base + bc_bytes + agg_bytes + gin_bytes) : nullptr;
 
     const int n = (int)N;
     if ((e = timed(SSM_K_BC_PREP, s, [&] { return ssm::launch_bc_prep(p, n, dtype, s); })) != hipSuccess)
@@ -396,6 +412,15 @@ int ssm_scan_fwd_ex(const void *x, const void *delta, const float *A, const void
                     const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
                     int64_t Dm, int64_t N, int dtype, void *stream) {
     return scan_impl(x, delta, A, B, C, D, h_init, y, h_final, Bsz, L, Dm, N, dtype, stream);
+}
+
+int ssm_scan_varlen_fwd(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                        const float *D, const int64_t *cu_seqlens, int64_t nseq, const float *h_init,
+                        void *y, float *h_final, int64_t L, int64_t Dm, int64_t N, int dtype, void *stream) {
+    if (nseq < 0) return fail(SSM_ERR_BAD_DIM, "nseq = %lld < 0", (long long)nseq);
+    if (nseq == 0 && L > 0) return fail(SSM_ERR_BAD_DIM, "nseq = 0 but L = %lld", (long long)L);
+    if (cu_seqlens == nullptr) return fail(SSM_ERR_NULLPTR, "cu_seqlens is NULL");
+    return scan_impl(x, delta, A, B, C, D, h_init, y, h_final, 1, L, Dm, N, dtype, stream, cu_seqlens, nseq);
 }
 
 int ssm_step(const void *x, const void *delta, const float *A, const void *B, const void *C,

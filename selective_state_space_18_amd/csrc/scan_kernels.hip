@@ -72,9 +72,11 @@ __global__ __launch_bounds__(kBlock) void bc_prep_kernel(const T *__restrict__ B
 template <int N, bool kStruct, typename Acc>
 struct ChanConst {
     Acc a0, inva;       // structured: A[d,0] (base-2 units in fp32) and 1/A[d,0]
+    Acc a0_nat;         // A[d,0] in natural units
     Acc Aeff[N], W[N];  // general: A (tiny stand-in for ~0, base-2 units in fp32) and (n+1)/A
     __device__ __forceinline__ explicit ChanConst(const float (&Ar)[N]) {
         constexpr Acc unit = sizeof(Acc) == 4 ? (Acc)kLog2e : (Acc)1;
+        a0_nat = (Acc)Ar[0];
         a0 = (Acc)Ar[0] * unit;
         inva = 0;
         if constexpr (kStruct) {
@@ -157,11 +159,77 @@ struct SegIO {
     int32_t row;   // bytes per time step (Dm * sizeof(T))
 };
 
-template <typename T, int N, bool kStruct, bool kOut, typename Acc>
+// Packed variable-length input: the wave-uniform position in the list of
+// sequences.  A sequence starts at cu[k] and ends at cu[k+1] - 1.
+struct SeqTrack {
+    const_row_ptr<int64_t> cu;  // constant address space: scalar loads
+    int64_t nseq;
+    int64_t next_start;  // absolute step at which the state restarts next
+    int64_t cur_end;     // absolute last step of the current sequence
+    int64_t cur;         // current sequence
+    const float *h_init;
+    float *h_final;
+    int64_t dn;          // Dm * N: stride of one sequence in h_init / h_final
+    int64_t ch_off;      // this lane's offset d * N inside a sequence
+    bool reset_seen;
+};
+
+// Largest k in [0, nseq) with cu[k] <= t (the sequence that holds step t,
+// skipping empty ones).  Always returns an index in range.
+__device__ __forceinline__ int64_t find_seq(const_row_ptr<int64_t> cu, int64_t nseq, int64_t t) {
+    int64_t lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void seq_begin(SeqTrack &sq, int64_t t0) {
+    sq.cur = find_seq(sq.cu, sq.nseq, t0);
+    const int64_t start = sq.cu[sq.cur];
+    if (start == t0) {  // a sequence starts exactly at the segment start
+        sq.next_start = t0;
+        sq.cur_end = -1;
+    } else {
+        sq.next_start = sq.cu[sq.cur + 1];
+        sq.cur_end = sq.next_start - 1;
+    }
+    sq.reset_seen = false;
+}
+
+// At step t == sq.next_start: move to the sequence starting at t (skipping
+// empty ones) and restart the state from its h_init (scaled to the state form
+// in use: g = (n+1) h, times `scale`).
+template <int N, typename Acc>
+__device__ __forceinline__ void seq_restart(SeqTrack &sq, int64_t t, Acc scale, Acc (&g)[N]) {
+    int64_t k = sq.cur;
+    if (sq.cu[k] != t) ++k;
+    while (k + 1 < sq.nseq && sq.cu[k + 1] <= t) ++k;
+    if (k >= sq.nseq) k = sq.nseq - 1;
+    sq.cur = k;
+    sq.next_start = sq.cu[k + 1];
+    sq.cur_end = sq.next_start - 1;
+    sq.reset_seen = true;
+    if (sq.h_init != nullptr) {
+        const float *hi = sq.h_init + k * sq.dn + sq.ch_off;
+#pragma unroll
+        for (int n = 0; n < N; ++n) g[n] = (Acc)hi[n] * (Acc)(n + 1) * scale;
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) g[n] = 0;
+    }
+}
+
+template <typename T, int N, bool kStruct, bool kOut, bool kVarlen, typename Acc>
 __device__ __forceinline__ void run_group(const SegIO<T> &io, const_row_ptr<Acc> bcp, int tb, int nsteps,
                                           const T (&xs)[kPrefetch], const T (&ds)[kPrefetch],
                                           const ChanConst<N, kStruct, Acc> &cc, Acc Dd, Acc (&g)[N],
-                                          Acc &lam, Acc (&rowc)[2 * N]) {
+                                          Acc &lam, Acc (&rowc)[2 * N], SeqTrack &sq, int64_t t0,
+                                          bool active) {
     const int last = nsteps - 1;
     const bool full = tb + kPrefetch <= nsteps;
 #pragma unroll
@@ -170,11 +238,23 @@ __device__ __forceinline__ void run_group(const SegIO<T> &io, const_row_ptr<Acc>
             Acc rown[2 * N];
             const int tn = tb + k + 1;
             load_row<N>(rown, bcp + (int64_t)(tn < last ? tn : last) * (2 * N));
+            if constexpr (kVarlen) {
+                // the aggregate pass of the structured path carries A[d,0] g
+                if (t0 + tb + k == sq.next_start)
+                    seq_restart<N>(sq, t0 + tb + k, (!kOut && kStruct) ? (Acc)cc.a0_nat : (Acc)1, g);
+            }
             const Acc xv = (Acc)to_f32(xs[k]);
             const Acc dv = (Acc)to_f32(ds[k]);
             const Acc yv = scan_step<N, kStruct, kOut>(cc, rowc, xv, dv, g);
             if constexpr (kOut) {
                 buf_store(from_acc<T>(fma_(Dd, xv, yv)), io.y, io.voff, (tb + k) * io.row);
+                if constexpr (kVarlen) {
+                    if (t0 + tb + k == sq.cur_end && sq.h_final != nullptr && active) {
+                        float *hf = sq.h_final + sq.cur * sq.dn + sq.ch_off;
+#pragma unroll
+                        for (int n = 0; n < N; ++n) hf[n] = (float)(g[n] / (Acc)(n + 1));
+                    }
+                }
             } else {
                 lam += dv;
             }
@@ -202,9 +282,10 @@ __device__ __forceinline__ void load_group(const SegIO<T> &io, int tb, int last,
 // the current one is computed.  Idle lanes of a partial tile shadow a valid
 // channel: they compute exactly what that channel's lane computes and store
 // the identical value.
-template <typename T, int N, bool kStruct, bool kOut, typename Acc>
+template <typename T, int N, bool kStruct, bool kOut, bool kVarlen, typename Acc>
 __device__ __forceinline__ void run_segment(const SegIO<T> &io, const_row_ptr<Acc> bcp, int nsteps,
-                                            const float (&Ar)[N], Acc Dd, Acc (&g)[N], Acc &lam) {
+                                            const float (&Ar)[N], Acc Dd, Acc (&g)[N], Acc &lam,
+                                            SeqTrack &sq, int64_t t0, bool active) {
     const ChanConst<N, kStruct, Acc> cc(Ar);
     const int last = nsteps - 1;
     T xa[kPrefetch], da[kPrefetch], xb[kPrefetch], db[kPrefetch];
@@ -213,10 +294,11 @@ __device__ __forceinline__ void run_segment(const SegIO<T> &io, const_row_ptr<Ac
     load_row<N>(rowc, bcp);
     for (int tb = 0; tb < nsteps; tb += 2 * kPrefetch) {
         load_group(io, tb + kPrefetch, last, xb, db);
-        run_group<T, N, kStruct, kOut>(io, bcp, tb, nsteps, xa, da, cc, Dd, g, lam, rowc);
+        run_group<T, N, kStruct, kOut, kVarlen>(io, bcp, tb, nsteps, xa, da, cc, Dd, g, lam, rowc, sq, t0, active);
         if (tb + kPrefetch >= nsteps) break;
         load_group(io, tb + 2 * kPrefetch, last, xa, da);
-        run_group<T, N, kStruct, kOut>(io, bcp, tb + kPrefetch, nsteps, xb, db, cc, Dd, g, lam, rowc);
+        run_group<T, N, kStruct, kOut, kVarlen>(io, bcp, tb + kPrefetch, nsteps, xb, db, cc, Dd, g, lam, rowc, sq,
+                                                t0, active);
     }
 }
 
@@ -227,7 +309,7 @@ __device__ __forceinline__ void run_segment(const SegIO<T> &io, const_row_ptr<Ac
 // by the kStruct = true launch, every other wave by the kStruct = false one.
 // Keeping the two paths in separate kernels keeps the structured kernel's
 // register count (and so its occupancy) free of the general path's.
-template <typename T, int N, bool kOut, bool kStruct>
+template <typename T, int N, bool kOut, bool kStruct, bool kVarlen>
 __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
     typedef typename AccOf<T>::type Acc;
     const int blocks_per_seg = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
@@ -261,7 +343,10 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
     // writing h_final into the same buffer); else h_init read by this lane.
     const Acc *gin = static_cast<const Acc *>(p.gin);
     Acc g[N];
-    if (kOut && p.S > 1) {
+    if (kVarlen && !(kOut && p.S > 1)) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) g[n] = 0;  // every sequence restarts from its own h_init
+    } else if (kOut && p.S > 1) {
 #pragma unroll
         for (int n = 0; n < N; ++n) g[n] = gin[((int64_t)s * N + n) * BD + ch];
     } else if (kOut && p.h_init != nullptr) {
@@ -284,8 +369,24 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
     const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
     Acc lam = 0;
 
-    run_segment<T, N, kStruct, kOut>(io, bcp, nsteps, Ar, Dd, g, lam);
+    SeqTrack sq;
+    if constexpr (kVarlen) {
+        sq.cu = (const_row_ptr<int64_t>)p.cu;
+        sq.nseq = p.nseq;
+        sq.h_init = p.h_init;
+        sq.h_final = p.h_final;
+        sq.dn = p.Dm * N;
+        sq.ch_off = d * N;
+        seq_begin(sq, t0);
+    }
 
+    run_segment<T, N, kStruct, kOut, kVarlen>(io, bcp, nsteps, Ar, Dd, g, lam, sq, t0, active);
+
+    if constexpr (kVarlen && !kOut) {
+        // one flag per segment for the carry pass: the incoming state does not
+        // survive a restart inside the segment
+        if (tile == 0 && lane == 0) p.seg_reset[s] = sq.reset_seen ? 1 : 0;
+    }
     if (!active) return;
     if constexpr (!kOut) {
         if constexpr (kStruct) {
@@ -297,7 +398,7 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
 #pragma unroll
         for (int n = 0; n < N; ++n) a[(int64_t)n * BD] = g[n];
         a[(int64_t)N * BD] = lam;
-    } else {
+    } else if constexpr (!kVarlen) {
         if (s == p.S - 1 && p.h_final != nullptr) {
 #pragma unroll
             for (int n = 0; n < N; ++n) p.h_final[ch * N + n] = (float)(g[n] / (Acc)(n + 1));
@@ -321,7 +422,7 @@ __global__ __launch_bounds__(kBlock) void scan_carry_kernel(ScanParams p) {
     const int64_t d = ch % p.Dm;
     constexpr Acc unit = sizeof(Acc) == 4 ? (Acc)kLog2e : (Acc)1;
     const Acc a = (Acc)p.A[d * N + n] * unit;
-    Acc carry = p.h_init ? (Acc)p.h_init[ch * N + n] * (Acc)(n + 1) : (Acc)0;
+    Acc carry = (p.h_init && p.cu == nullptr) ? (Acc)p.h_init[ch * N + n] * (Acc)(n + 1) : (Acc)0;
     const Acc *__restrict__ lam = static_cast<const Acc *>(p.agg) + (int64_t)N * BD + ch;
     const Acc *__restrict__ gl = static_cast<const Acc *>(p.agg) + (int64_t)n * BD + ch;
     Acc *__restrict__ out = static_cast<Acc *>(p.gin) + (int64_t)n * BD + ch;
@@ -345,12 +446,19 @@ __global__ __launch_bounds__(kBlock) void scan_carry_kernel(ScanParams p) {
             ln[k] = lam[s * sa];
             gn[k] = gl[s * sa];
         }
+        bool cut[kBatch];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) lc[k] = exp_units(a * lc[k]);
+        for (int k = 0; k < kBatch; ++k) {
+            lc[k] = exp_units(a * lc[k]);
+            // a sequence restart inside segment s cuts the incoming state off
+            // (selected rather than multiplied by 0, so an inf or NaN state of
+            // an earlier sequence cannot leak into the next one)
+            cut[k] = p.cu != nullptr && s0 + k < nseg && p.seg_reset[s0 + k] != 0;
+        }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             if (s0 + k < nseg) {
-                carry = fma_(lc[k], carry, gc[k]);
+                carry = cut[k] ? gc[k] : fma_(lc[k], carry, gc[k]);
                 out[(int64_t)(s0 + k + 1) * sg] = carry;
             }
         }
@@ -360,6 +468,18 @@ __global__ __launch_bounds__(kBlock) void scan_carry_kernel(ScanParams p) {
             gc[k] = gn[k];
         }
     }
+}
+
+// h_final of empty sequences in a packed variable-length call: their
+// initial state.  One thread per (sequence, d, n).
+__global__ __launch_bounds__(kBlock) void varlen_empty_kernel(const int64_t *__restrict__ cu, int64_t nseq,
+                                                              const float *__restrict__ h_init,
+                                                              float *__restrict__ h_final, int64_t dn) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= nseq * dn) return;
+    const int64_t k = i / dn;
+    if (cu[k] != cu[k + 1]) return;
+    h_final[i] = h_init ? h_init[i] : 0.f;
 }
 
 // h_final for an empty sequence: the initial state.
@@ -389,12 +509,20 @@ struct ByN {
         if (nseg <= 0 || bps == 0) return hipSuccess;
         const unsigned grid = (unsigned)bps * (unsigned)nseg;
         // Both paths are launched; each wave runs in exactly one of them.
-        if (out) {
-            hipLaunchKernelGGL((scan_segment_kernel<T, N, true, true>), dim3(grid), dim3(kBlock), 0, s, p);
-            hipLaunchKernelGGL((scan_segment_kernel<T, N, true, false>), dim3(grid), dim3(kBlock), 0, s, p);
+        if (p.cu != nullptr) {
+            if (out) {
+                hipLaunchKernelGGL((scan_segment_kernel<T, N, true, true, true>), dim3(grid), dim3(kBlock), 0, s, p);
+                hipLaunchKernelGGL((scan_segment_kernel<T, N, true, false, true>), dim3(grid), dim3(kBlock), 0, s, p);
+            } else {
+                hipLaunchKernelGGL((scan_segment_kernel<T, N, false, true, true>), dim3(grid), dim3(kBlock), 0, s, p);
+                hipLaunchKernelGGL((scan_segment_kernel<T, N, false, false, true>), dim3(grid), dim3(kBlock), 0, s, p);
+            }
+        } else if (out) {
+            hipLaunchKernelGGL((scan_segment_kernel<T, N, true, true, false>), dim3(grid), dim3(kBlock), 0, s, p);
+            hipLaunchKernelGGL((scan_segment_kernel<T, N, true, false, false>), dim3(grid), dim3(kBlock), 0, s, p);
         } else {
-            hipLaunchKernelGGL((scan_segment_kernel<T, N, false, true>), dim3(grid), dim3(kBlock), 0, s, p);
-            hipLaunchKernelGGL((scan_segment_kernel<T, N, false, false>), dim3(grid), dim3(kBlock), 0, s, p);
+            hipLaunchKernelGGL((scan_segment_kernel<T, N, false, true, false>), dim3(grid), dim3(kBlock), 0, s, p);
+            hipLaunchKernelGGL((scan_segment_kernel<T, N, false, false, false>), dim3(grid), dim3(kBlock), 0, s, p);
         }
         return hipGetLastError();
     }
@@ -444,6 +572,15 @@ hipError_t launch_scan_carry(const ScanParams &p, int N, int dtype, hipStream_t 
 
 hipError_t launch_scan_output(const ScanParams &p, int N, int dtype, hipStream_t s) {
     return with_type(N, dtype, [&](auto k) { return decltype(k)::segments(p, true, s); });
+}
+
+hipError_t launch_varlen_empty(const ScanParams &p, int N, hipStream_t s) {
+    const int64_t dn = p.Dm * N;
+    const int64_t count = p.nseq * dn;
+    if (count == 0 || p.h_final == nullptr || p.cu == nullptr) return hipSuccess;
+    const unsigned grid = (unsigned)((count + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(varlen_empty_kernel, dim3(grid), dim3(kBlock), 0, s, p.cu, p.nseq, p.h_init, p.h_final, dn);
+    return hipGetLastError();
 }
 
 hipError_t launch_state_init(const ScanParams &p, int N, hipStream_t s) {

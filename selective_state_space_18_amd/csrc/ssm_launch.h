@@ -25,6 +25,13 @@ struct ScanParams {
     int n_tiles;       // Bsz * tiles_per_b
     int waves_per_block;
     int force_general; // 1: never take the structured-A path
+    // Packed variable-length input (Bsz == 1): cu[0..nseq] are the sequence
+    // start offsets; the state restarts at each start from h_init[k] (or 0)
+    // and h_final[k] receives each sequence's last state.  nullptr: one
+    // sequence per batch row.
+    const int64_t *cu;
+    int64_t nseq;
+    int *seg_reset;    // [S]: 1 if a sequence starts inside segment s (varlen only)
 };
 
 struct StepParams {
@@ -45,6 +52,8 @@ hipError_t launch_scan_aggregate(const ScanParams &p, int N, int dtype, hipStrea
 hipError_t launch_scan_carry(const ScanParams &p, int N, int dtype, hipStream_t s);
 hipError_t launch_scan_output(const ScanParams &p, int N, int dtype, hipStream_t s);
 hipError_t launch_state_init(const ScanParams &p, int N, hipStream_t s);
+// h_final of the empty sequences of a packed variable-length call.
+hipError_t launch_varlen_empty(const ScanParams &p, int N, hipStream_t s);
 hipError_t launch_step(const StepParams &p, int N, int dtype, hipStream_t s);
 // Channels per thread of the decode-step kernel (1, 2 or 4).
 void set_step_unroll(int u);

@@ -30,7 +30,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_B
 # Every symbol include/ssmscan.h declares.
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_strerror",
            "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
-           "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read")
+           "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd")
 
 
 class SSMError(RuntimeError):
@@ -55,6 +55,8 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     L.ssm_scan_fwd.argtypes = [_vp] * 8 + [_i64] * 4 + [ctypes.c_int, _vp]
     L.ssm_scan_fwd_ex.argtypes = [_vp] * 9 + [_i64] * 4 + [ctypes.c_int, _vp]
+    L.ssm_scan_varlen_fwd.argtypes = [_vp] * 7 + [_i64] + [_vp] * 3 + [_i64] * 3 + [ctypes.c_int, _vp]
+    L.ssm_scan_varlen_fwd.restype = ctypes.c_int
     L.ssm_step.argtypes = [_vp] * 8 + [_i64] * 3 + [_vp]
     L.ssm_step_ex.argtypes = [_vp] * 8 + [_i64] * 3 + [ctypes.c_int, _vp]
     for f in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex"):
@@ -191,6 +193,46 @@ def scan_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, want_state
                                        _ptr(h_init), _ptr(y), _ptr(h_final), Bsz, L, Dm, N, code,
                                        _stream(dev))
     _check(rc, "ssm_scan_fwd")
+    return y, h_final
+
+
+def scan_varlen_fwd(x, delta, A, B, C, D, cu_seqlens, h_init=None, y=None, h_final=None, want_state=True):
+    """Packed variable-length scan: sequences concatenated along time.
+
+    x, delta: [L, Dm]; B, C: [L, N] (same dtype); A: [Dm, N] fp32; D: [Dm] fp32;
+    cu_seqlens: [nseq+1] int64 device tensor of sequence start offsets
+    (cu_seqlens[0] = 0, cu_seqlens[-1] = L); h_init: optional [nseq, Dm, N] fp32.
+    Returns (y [L, Dm], h_final [nseq, Dm, N] fp32 or None).
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    L, Dm = x.shape
+    N = A.shape[1]
+    nseq = cu_seqlens.shape[0] - 1
+    dt = x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (L, Dm), dt, dev)
+    _need(delta, "delta", (L, Dm), dt, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(B, "B", (L, N), dt, dev)
+    _need(C, "C", (L, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int64, dev)
+    if h_init is not None:
+        _need(h_init, "h_init", (nseq, Dm, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((L, Dm), dtype=dt, device=dev)
+    _need(y, "y", (L, Dm), dt, dev)
+    if h_final is None and want_state:
+        h_final = torch.empty((nseq, Dm, N), dtype=torch.float32, device=dev)
+    if h_final is not None:
+        _need(h_final, "h_final", (nseq, Dm, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_varlen_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(cu_seqlens), nseq, _ptr(h_init), _ptr(y), _ptr(h_final),
+                                       L, Dm, N, code, _stream(dev))
+    _check(rc, "ssm_scan_varlen_fwd")
     return y, h_final
 
 

@@ -13,6 +13,7 @@ dtype (round to nearest even for bf16).
 """
 from typing import Dict, List
 
+import numpy as np
 import torch
 
 from .configs import ScanConfig, StepConfig
@@ -112,6 +113,32 @@ def step_tokens(cfg: StepConfig, state: Dict[str, torch.Tensor], n_tokens: int) 
     return out
 
 
+def packed_lengths(nseq: int, mean_len: float, seed: int, p_empty: float = 0.0, sigma: float = 1.0,
+                   max_len: int = 0) -> List[int]:
+    """Lengths of ``nseq`` sequences for a packed (variable-length) call.
+
+    A log-normal length mix around ``mean_len`` steps (long tail, as in packed
+    prefill batches), each length at least 1, with a fraction ``p_empty`` of
+    empty sequences; optionally capped at ``max_len``.
+    """
+    rng = np.random.default_rng(int(seed))
+    mu = np.log(max(mean_len, 1.0)) - 0.5 * sigma * sigma
+    lens = np.maximum(1, np.rint(rng.lognormal(mu, sigma, size=nseq))).astype(np.int64)
+    if max_len > 0:
+        lens = np.minimum(lens, max_len)
+    if p_empty > 0:
+        lens[rng.random(nseq) < p_empty] = 0
+    return [int(v) for v in lens]
+
+
+def cu_seqlens(lengths: List[int], device="cpu") -> torch.Tensor:
+    """Start offsets [0, l0, l0+l1, ..., total] as int64."""
+    out = [0]
+    for v in lengths:
+        out.append(out[-1] + int(v))
+    return torch.tensor(out, dtype=torch.int64, device=device)
+
+
 def alg_bytes_scan(cfg: ScanConfig) -> int:
     """Bytes the scan must move at minimum: inputs once, outputs once."""
     s = 4 if cfg.dtype == "fp32" else 2
@@ -119,6 +146,14 @@ def alg_bytes_scan(cfg: ScanConfig) -> int:
     BLN = cfg.Bsz * cfg.L * cfg.N
     return (2 * BLD * s + 2 * BLN * s + 4 * cfg.Dm * cfg.N + 4 * cfg.Dm
             + BLD * s + 4 * cfg.Bsz * cfg.Dm * cfg.N)
+
+
+def alg_bytes_varlen(L: int, Dm: int, N: int, nseq: int, dtype: str, with_h_init: bool) -> int:
+    """Minimum bytes of a packed call: x, delta, B, C, A, D, offsets, h_init
+    (if given) read once; y and h_final written once."""
+    s = 4 if dtype == "fp32" else 2
+    return (3 * L * Dm * s + 2 * L * N * s + 4 * Dm * N + 4 * Dm + 8 * (nseq + 1)
+            + (2 if with_h_init else 1) * 4 * nseq * Dm * N)
 
 
 def alg_bytes_step(cfg: StepConfig) -> int:

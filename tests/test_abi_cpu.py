@@ -93,6 +93,32 @@ def test_scan_empty_is_valid_without_pointers(L):
     assert L.ssm_last_error() == b""
 
 
+def varlen(L, *, x=P[0], dl=P[1], A=P[2], B=P[3], C=P[4], D=P[5], cu=P[8], nseq=3, hi=None, y=P[6],
+           hf=P[7], Ls=8, Dm=64, N=16, dtype=1):
+    v = ctypes.c_void_p
+    return L.ssm_scan_varlen_fwd(v(x), v(dl), v(A), v(B), v(C), v(D), v(cu), nseq, v(hi), v(y), v(hf),
+                                 Ls, Dm, N, dtype, None)
+
+
+def test_varlen_argument_errors(L):
+    assert varlen(L, cu=0) == 1
+    assert b"cu_seqlens" in L.ssm_last_error()
+    assert varlen(L, nseq=-1) == 2
+    assert varlen(L, nseq=0) == 2              # L > 0 needs at least one sequence
+    assert varlen(L, cu=P[8] + 4) == 5         # int64 offsets need 8-byte alignment
+    assert varlen(L, dtype=5) == 3 and varlen(L, N=6) == 4
+    assert varlen(L, y=P[8]) == 6              # y overlaps cu_seqlens
+    assert varlen(L, hf=P[8] + 8) == 6         # h_final overlaps cu_seqlens
+    assert varlen(L, hi=P[7]) == 6             # in place is not allowed for packed sequences
+    assert b"packed" in L.ssm_last_error()
+    assert varlen(L, hi=P[9], x=0) == 1
+    assert varlen(L, nseq=1 << 60) == 2        # nseq * Dm * N overflows
+    # nothing to do: no device call
+    assert varlen(L, nseq=0, Ls=0, x=0, dl=0, B=0, C=0, y=0, hf=0) == 0
+    assert varlen(L, Dm=0, x=0, dl=0, A=0, D=0, y=0, hf=0) == 0
+    assert L.ssm_last_error() == b""
+
+
 def test_step_argument_errors(L):
     assert step(L, dtype=2) == 3
     assert step(L, N=5) == 4

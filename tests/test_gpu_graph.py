@@ -81,3 +81,36 @@ def test_step_replays_match_eager(ss):
         for i in range(3):
             assert torch.equal(ybuf[i], ye[i]), f"replay {k}, step {i}: y differs"
         assert torch.equal(hg, he), f"replay {k}: state differs"
+
+
+def test_packed_scan_replays_match_eager(ss):
+    print("case: packed scan graph replay", flush=True)
+    lengths = [100, 0, 333, 1, 250]
+    cfg = configs.ScanConfig("graph_packed", 1, sum(lengths), 192, 16, "bf16", "s4d_real", "per_token", 1.0, 41)
+    inp = generate.scan_inputs(cfg, DEV)
+    x, dl, B, C = (inp[k][0] for k in ("x", "delta", "B", "C"))
+    cu = generate.cu_seqlens(lengths, DEV)
+    h0 = torch.randn((len(lengths), 192, 16), device=DEV)
+    args = (x, dl, inp["A"], B, C, inp["D"], cu)
+    y_eager, h_eager = ss.scan_varlen_fwd(*args, h_init=h0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    y = torch.empty_like(y_eager)
+    hf = torch.empty_like(h_eager)
+    with torch.cuda.stream(s):
+        ss.scan_varlen_fwd(*args, h_init=h0, y=y, h_final=hf)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ss.scan_varlen_fwd(*args, h_init=h0, y=y, h_final=hf)
+    for k in range(3):
+        y.zero_()
+        hf.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {k}: y differs"
+        assert torch.equal(hf, h_eager), f"replay {k}: h_final differs"
+        y2, _ = ss.scan_varlen_fwd(*args, h_init=h0)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y_eager)
