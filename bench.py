@@ -7,11 +7,13 @@ N=16, bf16 storage, fp32 arithmetic, synthetic seeded inputs resident in HBM.
 The JSON line reports elements/s (B*L*D*N per second), the achieved
 algorithmic HBM bandwidth, the roofline of the dominant kernel, the fp64 CPU
 oracle timed on a bounded sample of the same workload, and -- under
-"secondary" -- the long-context scan and the decode step.
+"secondary" -- the long-context scan, a packed variable-length prefill and
+the decode step.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
                     [--no-cpu-baseline] [--no-secondary]
     python bench.py --only decode      # one workload, for profiler runs
+                                       # (scan, long, small, packed, decode)
     python bench.py --copy-calibration # plain copy of known size (for counters)
 """
 import argparse
@@ -81,22 +83,69 @@ def bench_scan(torch, ss, generate, cfg, steps, warmup):
     def fn(_i):
         ss.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], y=y, h_final=hf)
 
+    log(f"[bench] timing {cfg.name}: {warmup} warmup + {steps} steps")
+    ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    S, seg = ss.plan(cfg.Bsz, cfg.L, cfg.Dm, cfg.N)
+    del inp, y, hf
+    torch.cuda.empty_cache()
+    return ms, kern, S, seg
+
+
+def profiled_loop(torch, ss, fn, steps, warmup):
+    """timed_loop with the library's per-kernel event timers on: returns the
+    wall time per step and each kernel kind's average launch duration."""
     fn(0)
     torch.cuda.synchronize()
     ss.set_option(ss.SSM_OPT_PROFILE, 1)
     ss.profile_read()
     try:
-        log(f"[bench] timing {cfg.name}: {warmup} warmup + {steps} steps")
         ms = timed_loop(torch, fn, steps, warmup)
         prof = ss.profile_read()
     finally:
         ss.set_option(ss.SSM_OPT_PROFILE, 0)
-    S, seg = ss.plan(cfg.Bsz, cfg.L, cfg.Dm, cfg.N)
-    del inp, y, hf
-    torch.cuda.empty_cache()
     kern = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / (steps + warmup)}
             for k, v in prof.items() if v[1] > 0}
-    return ms, kern, S, seg
+    return ms, kern
+
+
+def bench_packed(torch, ss, generate, cfg, steps, warmup):
+    """Packed variable-length prefill: one row of cfg.L steps holding a few
+    dozen sequences, each restarting from its own initial state."""
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name}")
+    inp = generate.packed_inputs(cfg, dev)
+    nseq = inp["cu"].numel() - 1
+    y = torch.empty_like(inp["x"])
+    hf = torch.empty(nseq, cfg.Dm, cfg.N, device=dev, dtype=torch.float32)
+
+    def fn(_i):
+        ss.scan_varlen_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["cu"],
+                           h_init=inp["h_init"], y=y, h_final=hf)
+
+    log(f"[bench] timing {cfg.name}: {warmup} warmup + {steps} steps")
+    ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    S, seg = ss.plan(1, cfg.L, cfg.Dm, cfg.N)
+    lens = (inp["cu"][1:] - inp["cu"][:-1]).tolist()
+    del inp, y, hf
+    torch.cuda.empty_cache()
+    elems = cfg.elems()
+    alg = generate.alg_bytes_varlen(cfg.L, cfg.Dm, cfg.N, nseq, cfg.dtype, cfg.h0_std > 0)
+    out_ms = kern["scan_output"]["avg_ms"]
+    achieved = elems * SCAN_FLOPS_PER_ELEM / (out_ms * 1e-3) / 1e12
+    return {
+        "workload": cfg.name, "ms_per_step": round(ms, 5), "value": elems / (ms * 1e-3), "unit": "elems/s",
+        "config": {"workload": cfg.name, "L": cfg.L, "Dm": cfg.Dm, "N": cfg.N, "storage": cfg.dtype,
+                   "A": cfg.a_kind, "sequences": nseq, "empty_sequences": lens.count(0),
+                   "longest": max(lens), "segments": S, "segment_len": seg, "h_init": cfg.h0_std > 0},
+        "hbm": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
+        "roofline": {"kernel": "scan_segment_kernel (output pass, packed)", "bound": "alu",
+                     "achieved": round(achieved, 3), "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+                     "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
+                     "traffic": traffic_for("scan_output_" + cfg.name, "scan_kernels.hip"),
+                     "avg_ms": round(out_ms, 5)},
+        "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
+    }
 
 
 def scan_record(cfg, ms, kern, S, seg, generate):
@@ -248,7 +297,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["scan", "long", "decode", "small"], default=None)
+    ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
 
@@ -275,6 +324,10 @@ def main():
 
     if a.only == "decode":
         rec = bench_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "packed":
+        rec = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER, a.steps, a.warmup)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "long":
@@ -321,6 +374,8 @@ def main():
         sec["long_context"] = {"workload": lc.name, "ms_per_step": round(lms, 5),
                                "value": lc.elems() / (lms * 1e-3), "unit": "elems/s", "hbm": lhbm,
                                "roofline": lroof, "config": lcfg, "kernels_avg_ms": lkms}
+        sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER,
+                                             max(5, a.steps // 5), 2)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
                                      configs.DECODE_256x8192.n_tokens)
         out["secondary"] = sec

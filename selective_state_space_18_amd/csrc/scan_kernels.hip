@@ -72,11 +72,9 @@ __global__ __launch_bounds__(kBlock) void bc_prep_kernel(const T *__restrict__ B
 template <int N, bool kStruct, typename Acc>
 struct ChanConst {
     Acc a0, inva;       // structured: A[d,0] (base-2 units in fp32) and 1/A[d,0]
-    Acc a0_nat;         // A[d,0] in natural units
     Acc Aeff[N], W[N];  // general: A (tiny stand-in for ~0, base-2 units in fp32) and (n+1)/A
     __device__ __forceinline__ explicit ChanConst(const float (&Ar)[N]) {
         constexpr Acc unit = sizeof(Acc) == 4 ? (Acc)kLog2e : (Acc)1;
-        a0_nat = (Acc)Ar[0];
         a0 = (Acc)Ar[0] * unit;
         inva = 0;
         if constexpr (kStruct) {
@@ -165,13 +163,7 @@ struct SeqTrack {
     const_row_ptr<int64_t> cu;  // constant address space: scalar loads
     int64_t nseq;
     int64_t next_start;  // absolute step at which the state restarts next
-    int64_t cur_end;     // absolute last step of the current sequence
     int64_t cur;         // current sequence
-    const float *h_init;
-    float *h_final;
-    int64_t dn;          // Dm * N: stride of one sequence in h_init / h_final
-    int64_t ch_off;      // this lane's offset d * N inside a sequence
-    bool reset_seen;
 };
 
 // Largest k in [0, nseq) with cu[k] <= t (the sequence that holds step t,
@@ -188,48 +180,31 @@ __device__ __forceinline__ int64_t find_seq(const_row_ptr<int64_t> cu, int64_t n
     return lo;
 }
 
+// Position at the first step t0 of a segment.  If a sequence starts exactly at
+// t0, next_start = t0 so that the state restarts before the first step.
 __device__ __forceinline__ void seq_begin(SeqTrack &sq, int64_t t0) {
     sq.cur = find_seq(sq.cu, sq.nseq, t0);
     const int64_t start = sq.cu[sq.cur];
-    if (start == t0) {  // a sequence starts exactly at the segment start
-        sq.next_start = t0;
-        sq.cur_end = -1;
-    } else {
-        sq.next_start = sq.cu[sq.cur + 1];
-        sq.cur_end = sq.next_start - 1;
-    }
-    sq.reset_seen = false;
+    sq.next_start = start == t0 ? t0 : sq.cu[sq.cur + 1];
 }
 
 // At step t == sq.next_start: move to the sequence starting at t (skipping
-// empty ones) and restart the state from its h_init (scaled to the state form
-// in use: g = (n+1) h, times `scale`).
-template <int N, typename Acc>
-__device__ __forceinline__ void seq_restart(SeqTrack &sq, int64_t t, Acc scale, Acc (&g)[N]) {
+// empty ones) and return its index.
+__device__ __forceinline__ int64_t seq_advance(SeqTrack &sq, int64_t t) {
     int64_t k = sq.cur;
     if (sq.cu[k] != t) ++k;
     while (k + 1 < sq.nseq && sq.cu[k + 1] <= t) ++k;
     if (k >= sq.nseq) k = sq.nseq - 1;
     sq.cur = k;
     sq.next_start = sq.cu[k + 1];
-    sq.cur_end = sq.next_start - 1;
-    sq.reset_seen = true;
-    if (sq.h_init != nullptr) {
-        const float *hi = sq.h_init + k * sq.dn + sq.ch_off;
-#pragma unroll
-        for (int n = 0; n < N; ++n) g[n] = (Acc)hi[n] * (Acc)(n + 1) * scale;
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n) g[n] = 0;
-    }
+    return k;
 }
 
-template <typename T, int N, bool kStruct, bool kOut, bool kVarlen, typename Acc>
+template <typename T, int N, bool kStruct, bool kOut, typename Acc>
 __device__ __forceinline__ void run_group(const SegIO<T> &io, const_row_ptr<Acc> bcp, int tb, int nsteps,
                                           const T (&xs)[kPrefetch], const T (&ds)[kPrefetch],
                                           const ChanConst<N, kStruct, Acc> &cc, Acc Dd, Acc (&g)[N],
-                                          Acc &lam, Acc (&rowc)[2 * N], SeqTrack &sq, int64_t t0,
-                                          bool active) {
+                                          Acc &lam, Acc (&rowc)[2 * N]) {
     const int last = nsteps - 1;
     const bool full = tb + kPrefetch <= nsteps;
 #pragma unroll
@@ -238,23 +213,11 @@ __device__ __forceinline__ void run_group(const SegIO<T> &io, const_row_ptr<Acc>
             Acc rown[2 * N];
             const int tn = tb + k + 1;
             load_row<N>(rown, bcp + (int64_t)(tn < last ? tn : last) * (2 * N));
-            if constexpr (kVarlen) {
-                // the aggregate pass of the structured path carries A[d,0] g
-                if (t0 + tb + k == sq.next_start)
-                    seq_restart<N>(sq, t0 + tb + k, (!kOut && kStruct) ? (Acc)cc.a0_nat : (Acc)1, g);
-            }
             const Acc xv = (Acc)to_f32(xs[k]);
             const Acc dv = (Acc)to_f32(ds[k]);
             const Acc yv = scan_step<N, kStruct, kOut>(cc, rowc, xv, dv, g);
             if constexpr (kOut) {
                 buf_store(from_acc<T>(fma_(Dd, xv, yv)), io.y, io.voff, (tb + k) * io.row);
-                if constexpr (kVarlen) {
-                    if (t0 + tb + k == sq.cur_end && sq.h_final != nullptr && active) {
-                        float *hf = sq.h_final + sq.cur * sq.dn + sq.ch_off;
-#pragma unroll
-                        for (int n = 0; n < N; ++n) hf[n] = (float)(g[n] / (Acc)(n + 1));
-                    }
-                }
             } else {
                 lam += dv;
             }
@@ -282,10 +245,9 @@ __device__ __forceinline__ void load_group(const SegIO<T> &io, int tb, int last,
 // the current one is computed.  Idle lanes of a partial tile shadow a valid
 // channel: they compute exactly what that channel's lane computes and store
 // the identical value.
-template <typename T, int N, bool kStruct, bool kOut, bool kVarlen, typename Acc>
+template <typename T, int N, bool kStruct, bool kOut, typename Acc>
 __device__ __forceinline__ void run_segment(const SegIO<T> &io, const_row_ptr<Acc> bcp, int nsteps,
-                                            const float (&Ar)[N], Acc Dd, Acc (&g)[N], Acc &lam,
-                                            SeqTrack &sq, int64_t t0, bool active) {
+                                            const float (&Ar)[N], Acc Dd, Acc (&g)[N], Acc &lam) {
     const ChanConst<N, kStruct, Acc> cc(Ar);
     const int last = nsteps - 1;
     T xa[kPrefetch], da[kPrefetch], xb[kPrefetch], db[kPrefetch];
@@ -294,12 +256,29 @@ __device__ __forceinline__ void run_segment(const SegIO<T> &io, const_row_ptr<Ac
     load_row<N>(rowc, bcp);
     for (int tb = 0; tb < nsteps; tb += 2 * kPrefetch) {
         load_group(io, tb + kPrefetch, last, xb, db);
-        run_group<T, N, kStruct, kOut, kVarlen>(io, bcp, tb, nsteps, xa, da, cc, Dd, g, lam, rowc, sq, t0, active);
+        run_group<T, N, kStruct, kOut>(io, bcp, tb, nsteps, xa, da, cc, Dd, g, lam, rowc);
         if (tb + kPrefetch >= nsteps) break;
         load_group(io, tb + 2 * kPrefetch, last, xa, da);
-        run_group<T, N, kStruct, kOut, kVarlen>(io, bcp, tb + kPrefetch, nsteps, xb, db, cc, Dd, g, lam, rowc, sq,
-                                                t0, active);
+        run_group<T, N, kStruct, kOut>(io, bcp, tb + kPrefetch, nsteps, xb, db, cc, Dd, g, lam, rowc);
     }
+}
+
+// The x/delta/y streams and B/C rows of steps [t, t + n) of batch row b for
+// the 64-channel tile at d0 (lane channel d).
+template <typename T, typename Acc, int N, bool kOut>
+__device__ __forceinline__ SegIO<T> seg_io(const ScanParams &p, int64_t b, int64_t t, int n, int64_t d0,
+                                           int64_t d, const_row_ptr<Acc> &bcp) {
+    const int64_t off = (b * p.L + t) * p.Dm + d0;
+    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
+    const int32_t span = n * row;
+    SegIO<T> io;
+    io.x = make_rsrc(static_cast<const T *>(p.x) + off, span);
+    io.dl = make_rsrc(static_cast<const T *>(p.delta) + off, span);
+    io.y = make_rsrc(kOut ? static_cast<const T *>(p.y) + off : static_cast<const T *>(p.x) + off, kOut ? span : 0);
+    io.voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
+    io.row = row;
+    bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t) * (2 * N));
+    return io;
 }
 
 // kOut = false: aggregate pass over segments 0..S-2.
@@ -357,36 +336,60 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
         for (int n = 0; n < N; ++n) g[n] = 0;
     }
 
-    const int64_t off = (b * p.L + t0) * p.Dm + d0;
-    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
-    const int32_t span = nsteps * row;
-    SegIO<T> io;
-    io.x = make_rsrc(static_cast<const T *>(p.x) + off, span);
-    io.dl = make_rsrc(static_cast<const T *>(p.delta) + off, span);
-    io.y = make_rsrc(kOut ? static_cast<const T *>(p.y) + off : static_cast<const T *>(p.x) + off, kOut ? span : 0);
-    io.voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
-    io.row = row;
-    const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
     Acc lam = 0;
-
-    SeqTrack sq;
-    if constexpr (kVarlen) {
+    if constexpr (!kVarlen) {
+        const_row_ptr<Acc> bcp;
+        const SegIO<T> io = seg_io<T, Acc, N, kOut>(p, b, t0, nsteps, d0, d, bcp);
+        run_segment<T, N, kStruct, kOut>(io, bcp, nsteps, Ar, Dd, g, lam);
+    } else {
+        // Packed sequences: the segment is cut at every sequence start; each
+        // piece runs the plain loop, and between pieces the state restarts from
+        // the next sequence's h_init (or zero).
+        SeqTrack sq;
         sq.cu = (const_row_ptr<int64_t>)p.cu;
         sq.nseq = p.nseq;
-        sq.h_init = p.h_init;
-        sq.h_final = p.h_final;
-        sq.dn = p.Dm * N;
-        sq.ch_off = d * N;
         seq_begin(sq, t0);
+        const int64_t t_end = t0 + nsteps;
+        bool reset = false;
+        int64_t t = t0;
+        while (t < t_end) {
+            if (t == sq.next_start) {
+                const int64_t k = seq_advance(sq, t);
+                reset = true;
+                // the aggregate pass of the structured path carries A[d,0] g
+                const Acc scale = (!kOut && kStruct) ? (Acc)Ar[0] : (Acc)1;
+                if (p.h_init != nullptr) {
+                    const float *hi = p.h_init + (k * p.Dm + d) * N;
+#pragma unroll
+                    for (int n = 0; n < N; ++n) g[n] = (Acc)hi[n] * (Acc)(n + 1) * scale;
+                } else {
+#pragma unroll
+                    for (int n = 0; n < N; ++n) g[n] = 0;
+                }
+            }
+            int64_t piece_end = sq.next_start < t_end ? sq.next_start : t_end;
+            if (piece_end <= t) piece_end = t + 1;  // offsets that are not increasing: still progress
+            const int n = uniform((int)(piece_end - t));
+            const_row_ptr<Acc> bcp;
+            const SegIO<T> io = seg_io<T, Acc, N, kOut>(p, b, t, n, d0, d, bcp);
+            run_segment<T, N, kStruct, kOut>(io, bcp, n, Ar, Dd, g, lam);
+            if constexpr (kOut) {
+                // the current sequence ends with this piece
+                if (piece_end == sq.next_start && p.h_final != nullptr && active) {
+                    float *hf = p.h_final + (sq.cur * p.Dm + d) * N;
+#pragma unroll
+                    for (int n2 = 0; n2 < N; ++n2) hf[n2] = (float)(g[n2] / (Acc)(n2 + 1));
+                }
+            }
+            t = piece_end;
+        }
+        if constexpr (!kOut) {
+            // one flag per segment for the carry pass: the incoming state does
+            // not survive a restart inside the segment
+            if (tile == 0 && lane == 0) p.seg_reset[s] = reset ? 1 : 0;
+        }
     }
 
-    run_segment<T, N, kStruct, kOut, kVarlen>(io, bcp, nsteps, Ar, Dd, g, lam, sq, t0, active);
-
-    if constexpr (kVarlen && !kOut) {
-        // one flag per segment for the carry pass: the incoming state does not
-        // survive a restart inside the segment
-        if (tile == 0 && lane == 0) p.seg_reset[s] = sq.reset_seen ? 1 : 0;
-    }
     if (!active) return;
     if constexpr (!kOut) {
         if constexpr (kStruct) {

@@ -71,6 +71,44 @@ LONG_CONTEXT_1M = ScanConfig("long_context_b1_l1048576_d1024_n16", 1, 1 << 20, 1
 DECODE_256x8192 = StepConfig("decode_b256_d8192_n16", 256, 8192, 16, "bf16",
                              h0_std=0.1, n_tokens=1000, seed=4)
 
+@dataclass(frozen=True)
+class PackedConfig:
+    """Several sequences packed along time into one row (variable-length scan).
+
+    Lengths: log-normal around ``mean_len`` (capped at ``max_len``), a share
+    ``p_empty`` of empty sequences, drawn until the next one would overflow
+    ``L``; the rest of ``L`` is one last sequence.  Each sequence starts from
+    h_init ~ N(0, h0_std) when ``h0_std`` > 0.  x, delta, B, C follow the
+    ScanConfig recipe for a [1, L, Dm] row.
+    """
+    name: str
+    L: int
+    Dm: int
+    N: int
+    dtype: str
+    a_kind: str
+    delta_kind: str
+    bc_scale: float
+    mean_len: int
+    max_len: int
+    p_empty: float
+    h0_std: float
+    seed: int
+
+    def elems(self) -> int:
+        return self.L * self.Dm * self.N
+
+    def as_scan(self) -> ScanConfig:
+        return ScanConfig(self.name, 1, self.L, self.Dm, self.N, self.dtype, self.a_kind,
+                          self.delta_kind, self.bc_scale, self.seed)
+
+
+# Packed prefill of a Mamba-2.8B-shaped layer: the same 4 x 16384 steps as
+# MAMBA2P8B_LAYER, as a few dozen sequences of mixed length in one row.
+PACKED_2P8B_LAYER = PackedConfig("packed_prefill_l65536_d5120_n16", 65536, 5120, 16, "bf16",
+                                 "s4d_real", "per_token", 0.25, mean_len=2048, max_len=16384,
+                                 p_empty=0.05, h0_std=0.5, seed=5)
+
 SCAN_CONFIGS = {c.name: c for c in (TINY_FP32, MAMBA130M_LAYER, MAMBA2P8B_LAYER,
                                     LONG_CONTEXT_1M)}
 STEP_CONFIGS = {DECODE_256x8192.name: DECODE_256x8192}

@@ -16,7 +16,7 @@ from typing import Dict, List
 import numpy as np
 import torch
 
-from .configs import ScanConfig, StepConfig
+from .configs import PackedConfig, ScanConfig, StepConfig
 
 _DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
@@ -137,6 +137,33 @@ def cu_seqlens(lengths: List[int], device="cpu") -> torch.Tensor:
     for v in lengths:
         out.append(out[-1] + int(v))
     return torch.tensor(out, dtype=torch.int64, device=device)
+
+
+def packed_config_lengths(cfg: PackedConfig) -> List[int]:
+    """Sequence lengths of a PackedConfig (they sum to cfg.L)."""
+    draws = packed_lengths(max(1, 4 * cfg.L // max(cfg.mean_len, 1)), cfg.mean_len, cfg.seed,
+                           p_empty=cfg.p_empty, max_len=cfg.max_len)
+    out, total = [], 0
+    for v in draws:
+        if total + v > cfg.L:
+            break
+        out.append(v)
+        total += v
+    out.append(cfg.L - total)
+    return out
+
+
+def packed_inputs(cfg: PackedConfig, device="cpu") -> Dict[str, torch.Tensor]:
+    """x, delta [L, Dm]; B, C [L, N]; A, D; cu_seqlens; h_init [nseq, Dm, N] or None."""
+    inp = scan_inputs(cfg.as_scan(), device)
+    out = {k: (v[0] if k in ("x", "delta", "B", "C") else v) for k, v in inp.items()}
+    lengths = packed_config_lengths(cfg)
+    out["cu"] = cu_seqlens(lengths, device)
+    out["h_init"] = None
+    if cfg.h0_std > 0:
+        g = _gen(torch.device(device), cfg.seed + 1000)
+        out["h_init"] = _normal((len(lengths), cfg.Dm, cfg.N), g, torch.device(device), cfg.h0_std)
+    return out
 
 
 def alg_bytes_scan(cfg: ScanConfig) -> int:

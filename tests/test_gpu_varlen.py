@@ -187,19 +187,15 @@ def test_deterministic(ss):
 
 @pytest.mark.slow
 def test_packed_prefill_2p8b_layer_sampled(ss):
-    """A packed prefill batch of a Mamba-2.8B-shaped layer (Dm = 5120, N = 16):
-    65536 steps in a few dozen sequences of mixed length, planner launch configuration,
-    every 64th channel compared (channels are independent)."""
-    lengths = []
-    for v in generate.packed_lengths(64, 2048, seed=77, p_empty=0.05, max_len=16384):
-        if sum(lengths) + v > 65536:
-            break
-        lengths.append(v)
-    lengths.append(65536 - sum(lengths))
-    P.say(f"case: varlen packed 2.8B layer L={sum(lengths)} nseq={len(lengths)}")
-    inp = packed_inputs("bf16", "s4d_real", lengths, 5120, 16, seed=2, with_h_init=True)
+    """The packed prefill workload of a Mamba-2.8B-shaped layer (Dm = 5120,
+    N = 16, 65536 steps in a few dozen sequences of mixed length, each with its
+    own initial state), in the planner's launch configuration; every 64th
+    channel is compared (channels are independent)."""
+    cfg = configs.PACKED_2P8B_LAYER
+    inp = generate.packed_inputs(cfg, DEV)
+    P.say(f"case: {cfg.name} nseq={inp['cu'].numel() - 1}")
     y, hf = run(ss, inp)
-    idx = np.arange(0, 5120, 64) + 17
+    idx = np.arange(0, cfg.Dm, 64) + 17
     yr, hr = oracle_packed(inp, d_idx=idx)
     P.compare(y[:, idx], yr, "bf16", "y (sampled channels)")
     P.compare(hf[:, idx], hr, "bf16", "h_final (sampled channels)")

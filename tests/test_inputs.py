@@ -79,3 +79,26 @@ def test_algorithmic_bytes_match_published_table():
     assert abs(generate.alg_bytes_scan(configs.LONG_CONTEXT_1M) / 1e6 - 6509.7) < 0.5
     assert abs(generate.alg_bytes_scan(configs.MAMBA130M_LAYER) / 1e6 - 152.9) < 0.5
     assert abs(generate.alg_bytes_step(configs.DECODE_256x8192) / 1e6 - 281.6) < 0.5
+
+
+def test_packed_lengths_and_offsets():
+    lens = generate.packed_lengths(400, 50, seed=3, p_empty=0.1, max_len=200)
+    assert len(lens) == 400 and min(lens) == 0 and max(lens) <= 200
+    assert 20 <= lens.count(0) <= 70
+    assert generate.packed_lengths(400, 50, seed=3, p_empty=0.1, max_len=200) == lens
+    cu = generate.cu_seqlens([3, 0, 2])
+    assert cu.dtype == torch.int64 and cu.tolist() == [0, 3, 3, 5]
+
+
+def test_packed_config_sums_to_its_length():
+    from ssm_inputs import PACKED_2P8B_LAYER as cfg
+    lens = generate.packed_config_lengths(cfg)
+    assert sum(lens) == cfg.L and min(lens) >= 0 and len(lens) > 10
+    assert max(lens[:-1]) <= cfg.max_len
+    small = cfg.__class__(**{**cfg.__dict__, "L": 3000, "Dm": 8, "mean_len": 100, "max_len": 400})
+    inp = generate.packed_inputs(small)
+    nseq = inp["cu"].numel() - 1
+    assert inp["x"].shape == (3000, 8) and inp["B"].shape == (3000, 16)
+    assert inp["h_init"].shape == (nseq, 8, 16)
+    assert int(inp["cu"][0]) == 0 and int(inp["cu"][-1]) == 3000
+    assert bool(torch.all(inp["cu"][1:] >= inp["cu"][:-1]))
