@@ -22,6 +22,10 @@ def _f64(a, shape, name):
     return a
 
 
+def _flags(delta_softplus, euler_b):
+    return (1 if delta_softplus else 0) | (2 if euler_b else 0)
+
+
 def _ptr(a):
     return a.ctypes.data_as(_dp) if a is not None else None
 
@@ -34,9 +38,9 @@ class Oracle:
             from . import build as _build
             _build.build()
         lib = ctypes.CDLL(lib_path)
-        lib.ssm_oracle_scan.argtypes = [_dp] * 7 + [_dp, _dp] + [_i64] * 4 + [ctypes.c_int]
+        lib.ssm_oracle_scan.argtypes = [_dp] * 10 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int]
         lib.ssm_oracle_scan.restype = ctypes.c_int
-        lib.ssm_oracle_step.argtypes = [_dp] * 8 + [_i64] * 3
+        lib.ssm_oracle_step.argtypes = [_dp] * 9 + [_i64] * 3 + [ctypes.c_int]
         lib.ssm_oracle_step.restype = ctypes.c_int
         lib.ssm_oracle_max_threads.argtypes = []
         lib.ssm_oracle_max_threads.restype = ctypes.c_int
@@ -46,8 +50,12 @@ class Oracle:
     def max_threads(self) -> int:
         return int(self.lib.ssm_oracle_max_threads())
 
-    def scan(self, x, delta, A, B, C, D, h0=None, threads: int = 0):
-        """Sequential fp64 scan.  Returns (y [Bsz,L,Dm], h_final [Bsz,Dm,N])."""
+    def scan(self, x, delta, A, B, C, D, h0=None, threads: int = 0, delta_bias=None,
+             delta_softplus: bool = False, euler_b: bool = False):
+        """Sequential fp64 scan.  Returns (y [Bsz,L,Dm], h_final [Bsz,Dm,N]).
+
+        delta_bias [Dm] is added to delta; delta_softplus passes the sum through
+        softplus; euler_b uses Bbar = delta*B instead of the ZOH input term."""
         x = np.asarray(x)
         Bsz, L, Dm = x.shape
         N = np.asarray(A).shape[1]
@@ -59,17 +67,20 @@ class Oracle:
         D = _f64(D, (Dm,), "D")
         if h0 is not None:
             h0 = _f64(h0, (Bsz, Dm, N), "h0")
+        bias = None if delta_bias is None else _f64(delta_bias, (Dm,), "delta_bias")
         y = np.empty((Bsz, L, Dm), dtype=np.float64)
         hf = np.empty((Bsz, Dm, N), dtype=np.float64)
-        rc = self.lib.ssm_oracle_scan(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+        rc = self.lib.ssm_oracle_scan(_ptr(x), _ptr(delta), _ptr(bias), _ptr(A), _ptr(B), _ptr(C),
                                       _ptr(D), _ptr(h0), _ptr(y), _ptr(hf),
-                                      Bsz, L, Dm, N, int(threads))
+                                      Bsz, L, Dm, N, _flags(delta_softplus, euler_b), int(threads))
         if rc != 0:
             raise RuntimeError(f"ssm_oracle_scan failed with code {rc}")
         return y, hf
 
-    def step(self, x, delta, A, B, C, D, h):
-        """One recurrent step.  Returns (y [Bsz,Dm], h_new [Bsz,Dm,N]); h is not modified."""
+    def step(self, x, delta, A, B, C, D, h, delta_bias=None, delta_softplus: bool = False,
+             euler_b: bool = False):
+        """One recurrent step.  Returns (y [Bsz,Dm], h_new [Bsz,Dm,N]); h is not modified.
+        The options are those of scan()."""
         x = np.asarray(x)
         Bsz, Dm = x.shape
         N = np.asarray(A).shape[1]
@@ -80,9 +91,11 @@ class Oracle:
         C = _f64(C, (Bsz, N), "C")
         D = _f64(D, (Dm,), "D")
         hn = _f64(h, (Bsz, Dm, N), "h").copy()
+        bias = None if delta_bias is None else _f64(delta_bias, (Dm,), "delta_bias")
         y = np.empty((Bsz, Dm), dtype=np.float64)
-        rc = self.lib.ssm_oracle_step(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                      _ptr(D), _ptr(hn), _ptr(y), Bsz, Dm, N)
+        rc = self.lib.ssm_oracle_step(_ptr(x), _ptr(delta), _ptr(bias), _ptr(A), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(hn), _ptr(y), Bsz, Dm, N,
+                                      _flags(delta_softplus, euler_b))
         if rc != 0:
             raise RuntimeError(f"ssm_oracle_step failed with code {rc}")
         return y, hn
@@ -102,9 +115,9 @@ def max_threads() -> int:
     return load().max_threads()
 
 
-def scan(x, delta, A, B, C, D, h0=None, threads: int = 0):
-    return load().scan(x, delta, A, B, C, D, h0=h0, threads=threads)
+def scan(x, delta, A, B, C, D, h0=None, threads: int = 0, **opts):
+    return load().scan(x, delta, A, B, C, D, h0=h0, threads=threads, **opts)
 
 
-def step(x, delta, A, B, C, D, h):
-    return load().step(x, delta, A, B, C, D, h)
+def step(x, delta, A, B, C, D, h, **opts):
+    return load().step(x, delta, A, B, C, D, h, **opts)

@@ -30,11 +30,23 @@
  *   - y_t uses the updated state h_t, plus D[d]*x_t[d].
  *   - initial state h_{-1} = h0 if given, else 0.
  *
+ * Optional variants (flags of the entry points):
+ *   - ORACLE_DELTA_SOFTPLUS: the step size is produced from a raw value as
+ *     delta = softplus(raw + bias[d]), the activation the "Mamba SSM Nedir?"
+ *     page gives for delta in section "Mamba'nin Yeniligi: Selective SSM"
+ *     (softplus of a linear projection; bias[d] is that projection's bias).
+ *     Without the flag delta = raw + bias[d] (bias NULL means 0).
+ *   - ORACLE_EULER_B: the input term is discretised with the Euler rule,
+ *     Bbar = delta * B, while Abar stays exp(delta*A).  The bitig.info page
+ *     on Mamba-3 (section "Gelistirilmis Ayriklastirma Semasi") says Mamba-1
+ *     and -2 discretised with Euler's method; Bbar = delta*B is also the
+ *     A -> 0 limit of the ZOH input term.
+ *
  * Layouts (row-major, contiguous):
  *   scan:  x, delta, y : [Bsz][L][Dm]      B, C : [Bsz][L][N]
- *          A : [Dm][N]     D : [Dm]         h0, h_final : [Bsz][Dm][N]
+ *          A : [Dm][N]     D, bias : [Dm]   h0, h_final : [Bsz][Dm][N]
  *   step:  x, delta, y : [Bsz][Dm]          B, C : [Bsz][N]
- *          A : [Dm][N]     D : [Dm]         h : [Bsz][Dm][N] (in/out)
+ *          A : [Dm][N]     D, bias : [Dm]   h : [Bsz][Dm][N] (in/out)
  *
  * All arithmetic is IEEE double with libm exp/expm1; build without
  * -ffast-math.
@@ -46,6 +58,25 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+#define ORACLE_DELTA_SOFTPLUS 1
+#define ORACLE_EULER_B 2
+
+/* softplus(v) = log(1 + exp(v)), in a form that neither overflows for large v
+ * nor loses the tail exp(v) for very negative v. */
+static double softplus(double v)
+{
+    if (v > 0.0)
+        return v + log1p(exp(-v));
+    return log1p(exp(v));
+}
+
+/* The step size the recurrence uses. */
+static double step_size(double raw, double bias, int flags)
+{
+    const double v = raw + bias;
+    return (flags & ORACLE_DELTA_SOFTPLUS) ? softplus(v) : v;
+}
 
 /* phi(z) = (exp(z) - 1) / z, with its limit 1 at z = 0. */
 static double zoh_phi(double z)
@@ -59,27 +90,32 @@ static double zoh_phi(double z)
  * returns y.  a: A[d][*], b/c: B_t[*], C_t[*]. */
 static double channel_step(double *h, double xt, double dt, const double *a,
                            const double *b, const double *c, double dskip,
-                           int64_t N)
+                           int64_t N, int euler)
 {
     double y = 0.0;
     for (int64_t n = 0; n < N; ++n) {
         const double z = dt * a[n];
         const double abar = exp(z);
-        const double bbar = dt * zoh_phi(z) * b[n];
+        double bbar;
+        if (euler)
+            bbar = dt * b[n];
+        else
+            bbar = dt * zoh_phi(z) * b[n];
         h[n] = abar * h[n] + bbar * xt;
         y += c[n] * h[n];
     }
     return y + dskip * xt;
 }
 
-int ssm_oracle_scan(const double *x, const double *delta, const double *A,
-                    const double *B, const double *C, const double *D,
-                    const double *h0, double *y, double *h_final,
-                    int64_t Bsz, int64_t L, int64_t Dm, int64_t N,
-                    int nthreads)
+int ssm_oracle_scan(const double *x, const double *delta, const double *bias,
+                    const double *A, const double *B, const double *C,
+                    const double *D, const double *h0, double *y,
+                    double *h_final, int64_t Bsz, int64_t L, int64_t Dm,
+                    int64_t N, int flags, int nthreads)
 {
     if (Bsz < 0 || L < 0 || Dm < 0 || N <= 0)
         return 1;
+    const int euler = (flags & ORACLE_EULER_B) != 0;
     const int64_t nchan = Bsz * Dm;
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -98,13 +134,15 @@ int ssm_oracle_scan(const double *x, const double *delta, const double *A,
 #pragma omp for schedule(dynamic, 1)
             for (int64_t ch = 0; ch < nchan; ++ch) {
                 const int64_t b = ch / Dm, d = ch % Dm;
+                const double bias_d = bias ? bias[d] : 0.0;
                 for (int64_t n = 0; n < N; ++n)
                     h[n] = h0 ? h0[(b * Dm + d) * N + n] : 0.0;
                 for (int64_t t = 0; t < L; ++t) {
                     const int64_t i = (b * L + t) * Dm + d;
                     const int64_t r = (b * L + t) * N;
-                    y[i] = channel_step(h, x[i], delta[i], A + d * N, B + r,
-                                        C + r, D[d], N);
+                    const double dt = step_size(delta[i], bias_d, flags);
+                    y[i] = channel_step(h, x[i], dt, A + d * N, B + r,
+                                        C + r, D[d], N, euler);
                 }
                 if (h_final)
                     for (int64_t n = 0; n < N; ++n)
@@ -116,17 +154,20 @@ int ssm_oracle_scan(const double *x, const double *delta, const double *A,
     return err;
 }
 
-int ssm_oracle_step(const double *x, const double *delta, const double *A,
-                    const double *B, const double *C, const double *D,
-                    double *h, double *y, int64_t Bsz, int64_t Dm, int64_t N)
+int ssm_oracle_step(const double *x, const double *delta, const double *bias,
+                    const double *A, const double *B, const double *C,
+                    const double *D, double *h, double *y, int64_t Bsz,
+                    int64_t Dm, int64_t N, int flags)
 {
     if (Bsz < 0 || Dm < 0 || N <= 0)
         return 1;
+    const int euler = (flags & ORACLE_EULER_B) != 0;
     for (int64_t b = 0; b < Bsz; ++b)
         for (int64_t d = 0; d < Dm; ++d) {
             const int64_t i = b * Dm + d;
-            y[i] = channel_step(h + i * N, x[i], delta[i], A + d * N,
-                                B + b * N, C + b * N, D[d], N);
+            const double dt = step_size(delta[i], bias ? bias[d] : 0.0, flags);
+            y[i] = channel_step(h + i * N, x[i], dt, A + d * N,
+                                B + b * N, C + b * N, D[d], N, euler);
         }
     return 0;
 }

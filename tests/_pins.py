@@ -297,6 +297,127 @@ def check_split_scan_operator(orc, seed=7):
     assert rel_err(carry, hf) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# options: delta = softplus(raw + bias) and the Euler input term Bbar = delta*B
+
+
+def read_delta(orc, raw, bias=None, softplus=True):
+    """The step size the oracle derives from raw (+ bias), read off exactly:
+    with A = 0 the input coefficient is delta itself (ZOH limit), so one step
+    from h = 0 with x = 1 and B = 1 leaves h = delta."""
+    raw = np.asarray(raw, dtype=np.float64).reshape(1, -1)
+    Dm = raw.shape[1]
+    _, h = orc.step(np.ones((1, Dm)), raw, np.zeros((Dm, 1)), np.ones((1, 1)), np.zeros((1, 1)),
+                    np.zeros(Dm), np.zeros((1, Dm, 1)), delta_bias=bias, delta_softplus=softplus)
+    return h[0, :, 0]
+
+
+def check_softplus_closed_forms(orc):
+    """softplus(v) = log(1 + e^v): its value at 0, its inverse log(e^u - 1),
+    the identity softplus(v) - softplus(-v) = v, the tails e^v (v -> -inf)
+    and v (v -> +inf), and numpy's logaddexp(0, v) on a grid."""
+    assert abs(read_delta(orc, [0.0])[0] - np.log(2.0)) <= 2e-16
+    u = np.array([1e-6, 1e-3, 0.1, 1.0, 5.0, 30.0])
+    got = read_delta(orc, np.log(np.expm1(u)))
+    assert np.all(np.abs(got - u) <= 1e-14 * u), (got, u)
+    v = np.array([0.5, 3.0, 20.0, 40.0])
+    pos, neg = read_delta(orc, v), read_delta(orc, -v)
+    assert np.all(np.abs((pos - neg) - v) <= 1e-14 * v)
+    tail = np.array([-40.0, -100.0, -700.0])
+    assert np.all(np.abs(read_delta(orc, tail) - np.exp(tail)) <= 1e-14 * np.exp(tail))
+    assert np.array_equal(read_delta(orc, [800.0, 1e4]), np.array([800.0, 1e4]))
+    grid = np.linspace(-30.0, 30.0, 121)
+    ref = np.logaddexp(0.0, grid)
+    assert np.all(np.abs(read_delta(orc, grid) - ref) <= 4e-16 * np.maximum(ref, 1.0))
+    # the per-channel bias is added before softplus; without the flag delta = raw + bias
+    raw = np.array([0.3, -1.2, 2.0, -0.75])
+    bias = np.array([-0.3, 1.2, 0.5, 0.25])
+    got = read_delta(orc, raw, bias)
+    assert abs(got[0] - np.log(2.0)) <= 2e-16 and abs(got[1] - np.log(2.0)) <= 2e-16
+    assert np.allclose(got[2:], np.logaddexp(0.0, raw[2:] + bias[2:]), rtol=1e-15, atol=0)
+    assert np.array_equal(read_delta(orc, raw, bias, softplus=False), raw + bias)
+
+
+def check_fused_delta_matches_precomputed(orc, seed=8):
+    """The scan and the step with (raw, bias, softplus) equal the plain ones fed
+    delta = logaddexp(0, raw + bias) computed by numpy."""
+    rng = np.random.default_rng(seed)
+    Bsz, L, Dm, N = 2, 12, 5, 3
+    x, _, A, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    raw = rng.normal(0.0, 0.5, (Bsz, L, Dm))
+    bias = np.log(np.expm1(rng.uniform(1e-3, 0.1, Dm)))
+    h0 = rng.standard_normal((Bsz, Dm, N))
+    delta = np.logaddexp(0.0, raw + bias[None, None, :])
+    for euler in (False, True):
+        y1, h1 = orc.scan(x, raw, A, B, C, D, h0=h0, delta_bias=bias, delta_softplus=True, euler_b=euler)
+        y2, h2 = orc.scan(x, delta, A, B, C, D, h0=h0, euler_b=euler)
+        assert rel_err(y1, y2) < 1e-13 and rel_err(h1, h2) < 1e-13, (euler, rel_err(y1, y2))
+        ys, hs = orc.step(x[:, 0], raw[:, 0], A, B[:, 0], C[:, 0], D, h0, delta_bias=bias,
+                          delta_softplus=True, euler_b=euler)
+        yp, hp = orc.step(x[:, 0], delta[:, 0], A, B[:, 0], C[:, 0], D, h0, euler_b=euler)
+        assert rel_err(ys, yp) < 1e-13 and rel_err(hs, hp) < 1e-13
+
+
+def check_euler_b_closed_forms(orc, seed=9):
+    """Euler input term Bbar = delta*B with Abar = exp(delta*A):
+    constant inputs give the geometric sum h_k = delta B x (1 - Abar^k)/(1 - Abar);
+    time-varying x with constant delta is scipy's lfilter([delta B], [1, -Abar], x);
+    A = 0 coincides with the ZOH; with x = 0 (pure decay) it coincides with ZOH."""
+    rng = np.random.default_rng(seed)
+    L, Dm, N = 15, 4, 3
+    xv = rng.standard_normal(Dm)
+    dv = rng.uniform(0.01, 0.4, Dm)
+    bv = rng.standard_normal(N)
+    A = -np.exp(rng.uniform(-1.5, 1.0, (Dm, N)))
+    x = np.tile(xv.reshape(1, 1, Dm), (1, L, 1))
+    delta = np.tile(dv.reshape(1, 1, Dm), (1, L, 1))
+    B = np.tile(bv.reshape(1, 1, N), (1, L, 1))
+    for n in range(N):
+        C = np.zeros((1, L, N))
+        C[..., n] = 1.0
+        y, _ = orc.scan(x, delta, A, B, C, np.zeros(Dm), euler_b=True)
+        for k in range(1, L + 1):
+            z = dv * A[:, n]
+            exact = dv * bv[n] * xv * np.expm1(k * z) / np.expm1(z)
+            assert rel_err(y[0, k - 1], exact) < 1e-12
+    xs = rng.standard_normal((1, L, Dm))
+    Ct = np.tile(rng.standard_normal(N).reshape(1, 1, N), (1, L, 1))
+    y, hf = orc.scan(xs, delta, A, B, Ct, np.zeros(Dm), euler_b=True)
+    for d in range(Dm):
+        ab = np.exp(dv[d] * A[d])
+        hs = np.stack([lfilter([dv[d] * bv[n]], [1.0, -ab[n]], xs[0, :, d]) for n in range(N)], axis=1)
+        assert rel_err(y[0, :, d], hs @ Ct[0, 0]) < 1e-12
+        assert rel_err(hf[0, d], hs[-1]) < 1e-12
+    xr, dr, _, Br, Cr, Dr = random_case(rng, 2, 9, 3, 4)
+    A0 = np.zeros((3, 4))
+    ye, he = orc.scan(xr, dr, A0, Br, Cr, Dr, euler_b=True)
+    yz, hz = orc.scan(xr, dr, A0, Br, Cr, Dr)
+    assert np.array_equal(ye, yz) and np.array_equal(he, hz)
+    Ar = -np.exp(rng.uniform(-1.0, 1.0, (3, 4)))
+    h0 = rng.standard_normal((2, 3, 4))
+    xz = np.zeros_like(xr)
+    ye, he = orc.scan(xz, dr, Ar, Br, Cr, Dr, h0=h0, euler_b=True)
+    yz, hz = orc.scan(xz, dr, Ar, Br, Cr, Dr, h0=h0)
+    assert np.array_equal(ye, yz) and np.array_equal(he, hz)
+
+
+def check_options_step_chain_matches_scan(orc, seed=10):
+    """Recurrent mode with the options on: L steps equal the scan."""
+    rng = np.random.default_rng(seed)
+    Bsz, L, Dm, N = 2, 8, 3, 4
+    x, _, A, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    raw = rng.normal(-1.0, 1.0, (Bsz, L, Dm))
+    bias = rng.normal(0.0, 0.5, Dm)
+    h0 = rng.standard_normal((Bsz, Dm, N))
+    opts = dict(delta_bias=bias, delta_softplus=True, euler_b=True)
+    y, hf = orc.scan(x, raw, A, B, C, D, h0=h0, **opts)
+    h = h0
+    for t in range(L):
+        yt, h = orc.step(x[:, t], raw[:, t], A, B[:, t], C[:, t], D, h, **opts)
+        assert rel_err(yt, y[:, t]) < 1e-13
+    assert rel_err(h, hf) < 1e-13
+
+
 ALL_CHECKS = [
     check_golden,
     check_brute_force,
@@ -310,4 +431,8 @@ ALL_CHECKS = [
     check_linearity_causality_permutation,
     check_step_chain_matches_scan,
     check_split_scan_operator,
+    check_softplus_closed_forms,
+    check_fused_delta_matches_precomputed,
+    check_euler_b_closed_forms,
+    check_options_step_chain_matches_scan,
 ]

@@ -18,21 +18,37 @@ MUTANTS = [
      "h[n] = abar * h[n] + bbar * xt;\n        y += c[n] * h[n];",
      "y += c[n] * h[n];\n        h[n] = abar * h[n] + bbar * xt;"),
     ("wrong_sign_in_exp", "const double abar = exp(z);", "const double abar = exp(-z);"),
-    ("bbar_missing_delta", "const double bbar = dt * zoh_phi(z) * b[n];",
-     "const double bbar = zoh_phi(z) * b[n];"),
-    ("euler_instead_of_zoh", "const double bbar = dt * zoh_phi(z) * b[n];",
-     "const double bbar = dt * b[n];"),
+    ("bbar_missing_delta", "bbar = dt * zoh_phi(z) * b[n];", "bbar = zoh_phi(z) * b[n];"),
+    ("euler_instead_of_zoh", "bbar = dt * zoh_phi(z) * b[n];", "bbar = dt * b[n];"),
     ("phi_missing_division", "return expm1(z) / z;", "return expm1(z);"),
     ("B_and_C_swapped", "B + r,\n                                        C + r,",
      "C + r,\n                                        B + r,"),
     ("B_C_ignore_batch", "const int64_t r = (b * L + t) * N;", "const int64_t r = t * N;"),
-    ("delta_from_channel_0", "delta[i], A + d * N, B + r", "delta[(b * L + t) * Dm], A + d * N, B + r"),
-    ("A_row_of_channel_0_in_scan", "delta[i], A + d * N, B + r", "delta[i], A, B + r"),
-    ("D_of_channel_0", "C + r, D[d], N);", "C + r, D[0], N);"),
+    ("delta_from_channel_0", "step_size(delta[i], bias_d", "step_size(delta[(b * L + t) * Dm], bias_d"),
+    ("A_row_of_channel_0_in_scan", "dt, A + d * N, B + r", "dt, A, B + r"),
+    ("D_of_channel_0", "C + r, D[d], N, euler);", "C + r, D[0], N, euler);"),
     ("initial_state_ignored", "h[n] = h0 ? h0[(b * Dm + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     ("step_B_ignores_batch", "B + b * N, C + b * N", "B, C + b * N"),
-    ("step_A_row_of_channel_0", "delta[i], A + d * N,\n                                B + b * N",
-     "delta[i], A,\n                                B + b * N"),
+    ("step_A_row_of_channel_0", "dt, A + d * N,\n                                B + b * N",
+     "dt, A,\n                                B + b * N"),
+    # delta pre-processing and the Euler input term
+    ("softplus_flag_ignored", "return (flags & ORACLE_DELTA_SOFTPLUS) ? softplus(v) : v;", "return v;"),
+    ("softplus_always_on", "return (flags & ORACLE_DELTA_SOFTPLUS) ? softplus(v) : v;", "return softplus(v);"),
+    ("bias_ignored", "const double v = raw + bias;", "const double v = raw;"),
+    ("bias_subtracted", "const double v = raw + bias;", "const double v = raw - bias;"),
+    ("softplus_positive_branch_drops_v", "return v + log1p(exp(-v));", "return log1p(exp(-v));"),
+    ("softplus_naive_tail", "return log1p(exp(v));\n}", "return log(1.0 + exp(v));\n}"),
+    ("softplus_naive_overflow", "    if (v > 0.0)\n        return v + log1p(exp(-v));\n", ""),
+    ("scan_bias_of_channel_0", "const double bias_d = bias ? bias[d] : 0.0;",
+     "const double bias_d = bias ? bias[0] : 0.0;"),
+    ("step_bias_of_channel_0", "bias ? bias[d] : 0.0, flags);", "bias ? bias[0] : 0.0, flags);"),
+    ("euler_uses_zoh", "            bbar = dt * b[n];\n", "            bbar = dt * zoh_phi(z) * b[n];\n"),
+    ("euler_drops_delta", "            bbar = dt * b[n];\n", "            bbar = b[n];\n"),
+    ("euler_forward_abar", "const double abar = exp(z);", "const double abar = euler ? 1.0 + z : exp(z);"),
+    ("euler_ignored_in_step", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    for (int64_t b",
+     "const int euler = 0;\n    for (int64_t b"),
+    ("euler_ignored_in_scan", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    const int64_t nchan",
+     "const int euler = 0;\n    const int64_t nchan"),
     ("h_final_not_last_state",
      "h_final[(b * Dm + d) * N + n] = h[n];",
      "h_final[(b * Dm + d) * N + n] = h[n] * 0.5 + 0.5 * h[n] * (n == 0 ? 1.0 : 0.999);"),
