@@ -7,13 +7,14 @@ N=16, bf16 storage, fp32 arithmetic, synthetic seeded inputs resident in HBM.
 The JSON line reports elements/s (B*L*D*N per second), the achieved
 algorithmic HBM bandwidth, the roofline of the dominant kernel, the fp64 CPU
 oracle timed on a bounded sample of the same workload, and -- under
-"secondary" -- the long-context scan, a packed variable-length prefill and
-the decode step.
+"secondary" -- the long-context scan, the scan options (fused delta
+activation, Euler input term), a packed variable-length prefill and the
+decode step.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
                     [--no-cpu-baseline] [--no-secondary]
     python bench.py --only decode      # one workload, for profiler runs
-                                       # (scan, long, small, packed, decode)
+                                       # (scan, long, small, packed, options, decode)
     python bench.py --copy-calibration # plain copy of known size (for counters)
 """
 import argparse
@@ -73,22 +74,49 @@ def timed_loop(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
-def bench_scan(torch, ss, generate, cfg, steps, warmup):
+def bench_scan(torch, ss, generate, cfg, steps, warmup, **opts):
+    """opts: scan options (delta_bias is taken from the inputs when the
+    workload's delta is the raw projection output)."""
     dev = "cuda:0"
     log(f"[bench] generating {cfg.name}")
     inp = generate.scan_inputs(cfg, dev)
+    if "delta_bias" in inp:
+        opts = dict(opts, delta_bias=inp["delta_bias"], delta_softplus=True)
     y = torch.empty_like(inp["x"])
     hf = torch.empty(cfg.Bsz, cfg.Dm, cfg.N, device=dev, dtype=torch.float32)
 
     def fn(_i):
-        ss.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], y=y, h_final=hf)
+        ss.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], y=y, h_final=hf, **opts)
 
-    log(f"[bench] timing {cfg.name}: {warmup} warmup + {steps} steps")
+    log(f"[bench] timing {cfg.name} {sorted(k for k, v in opts.items() if v is not None and v is not False)}: "
+        f"{warmup} warmup + {steps} steps")
     ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
     S, seg = ss.plan(cfg.Bsz, cfg.L, cfg.Dm, cfg.N)
     del inp, y, hf
     torch.cuda.empty_cache()
     return ms, kern, S, seg
+
+
+def bench_unfused_softplus(torch, ss, generate, cfg, steps, warmup):
+    """For comparison only: the activation as a separate torch pass
+    (softplus(delta + bias) written back to HBM in the storage dtype), then the
+    plain scan.  Returns ms per step."""
+    dev = "cuda:0"
+    inp = generate.scan_inputs(cfg, dev)
+    y = torch.empty_like(inp["x"])
+    hf = torch.empty(cfg.Bsz, cfg.Dm, cfg.N, device=dev, dtype=torch.float32)
+    act = torch.empty_like(inp["delta"])
+    bias = inp["delta_bias"].to(inp["delta"].dtype)
+
+    def fn(_i):
+        torch.nn.functional.softplus(torch.add(inp["delta"], bias, out=act), out=act)
+        ss.scan_fwd(inp["x"], act, inp["A"], inp["B"], inp["C"], inp["D"], y=y, h_final=hf)
+
+    log(f"[bench] timing {cfg.name} with a separate softplus pass: {warmup} warmup + {steps} steps")
+    ms = timed_loop(torch, fn, steps, warmup)
+    del inp, y, hf, act
+    torch.cuda.empty_cache()
+    return ms
 
 
 def profiled_loop(torch, ss, fn, steps, warmup):
@@ -106,6 +134,29 @@ def profiled_loop(torch, ss, fn, steps, warmup):
     kern = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / (steps + warmup)}
             for k, v in prof.items() if v[1] > 0}
     return ms, kern
+
+
+def bench_options(torch, ss, generate, configs, steps):
+    """The Mamba-2.8B-shaped layer with the scan options: delta's activation
+    fused (softplus(delta + bias) inside the kernels), and the Euler input
+    term, against the separate-activation route."""
+    out = {}
+    fc = configs.FUSED_2P8B_LAYER
+    ms, kern, S, seg = bench_scan(torch, ss, generate, fc, steps, 2)
+    roof, hbm, cfgd, kms = scan_record(fc, ms, kern, S, seg, generate)
+    out["fused_softplus"] = {"workload": fc.name, "ms_per_step": round(ms, 5), "value": fc.elems() / (ms * 1e-3),
+                             "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
+                             "config": dict(cfgd, delta="softplus(raw + bias) in the kernels")}
+    ums = bench_unfused_softplus(torch, ss, generate, fc, steps, 2)
+    out["separate_softplus_pass"] = {"ms_per_step": round(ums, 5), "value": fc.elems() / (ums * 1e-3),
+                                     "note": "torch softplus pass over delta, then the plain scan"}
+    ec = configs.MAMBA2P8B_LAYER
+    ms, kern, S, seg = bench_scan(torch, ss, generate, ec, steps, 2, euler_b=True)
+    roof, hbm, cfgd, kms = scan_record(ec, ms, kern, S, seg, generate)
+    out["euler_b"] = {"workload": ec.name, "ms_per_step": round(ms, 5), "value": ec.elems() / (ms * 1e-3),
+                      "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
+                      "config": dict(cfgd, input_term="Euler: delta * B")}
+    return out
 
 
 def bench_packed(torch, ss, generate, cfg, steps, warmup):
@@ -142,7 +193,7 @@ def bench_packed(torch, ss, generate, cfg, steps, warmup):
         "roofline": {"kernel": "scan_segment_kernel (output pass, packed)", "bound": "alu",
                      "achieved": round(achieved, 3), "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
                      "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
-                     "traffic": traffic_for("scan_output_" + cfg.name, "scan_kernels.hip"),
+                     "traffic": traffic_for("scan_output_" + cfg.name, "scan_kernels.h"),
                      "avg_ms": round(out_ms, 5)},
         "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
     }
@@ -160,7 +211,7 @@ def scan_record(cfg, ms, kern, S, seg, generate):
         "peak": round(VALU_FP32_PEAK_TFLOPS, 2),
         "unit": "TFLOP/s",
         "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
-        "traffic": traffic_for("scan_output_" + cfg.name, "scan_kernels.hip"),
+        "traffic": traffic_for("scan_output_" + cfg.name, "scan_kernels.h"),
         "avg_ms": round(out_ms, 5),
         "algorithmic_flops_per_launch": elems * SCAN_FLOPS_PER_ELEM,
         "hbm_frac_at_algorithmic_bytes": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -297,7 +348,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed"], default=None)
+    ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
 
@@ -325,6 +376,9 @@ def main():
     if a.only == "decode":
         rec = bench_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
         print(json.dumps(rec), flush=True)
+        return
+    if a.only == "options":
+        print(json.dumps(bench_options(torch, ss, generate, configs, a.steps)), flush=True)
         return
     if a.only == "packed":
         rec = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER, a.steps, a.warmup)
@@ -374,6 +428,7 @@ def main():
         sec["long_context"] = {"workload": lc.name, "ms_per_step": round(lms, 5),
                                "value": lc.elems() / (lms * 1e-3), "unit": "elems/s", "hbm": lhbm,
                                "roofline": lroof, "config": lcfg, "kernels_avg_ms": lkms}
+        sec["fused_softplus"] = bench_options(torch, ss, generate, configs, max(5, a.steps // 5))
         sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER,
                                              max(5, a.steps // 5), 2)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,

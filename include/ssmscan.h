@@ -68,8 +68,26 @@ typedef enum {
     SSM_ERR_ALIAS = 6,          /* an output overlaps an input or another output */
     SSM_ERR_NOMEM = 7,          /* library scratch memory could not be allocated */
     SSM_ERR_HIP = 8,            /* the HIP runtime reported an error (see ssm_last_error) */
-    SSM_ERR_BAD_OPTION = 9      /* unknown option id or value in ssm_set_option */
+    SSM_ERR_BAD_OPTION = 9      /* unknown option id or value, or unknown flag bits */
 } ssm_status;
+
+/*
+ * Flags of ssm_scan_fused_fwd and ssm_step_fused (bitwise OR).
+ *
+ * SSM_DELTA_SOFTPLUS: the delta argument holds the raw projection output and
+ *   the recurrence uses delta = softplus(delta_in + delta_bias[d]), the
+ *   activation the "Mamba SSM Nedir?" page gives for delta (section
+ *   "Mamba'nin Yeniligi: Selective SSM").  Without it the recurrence uses
+ *   delta_in + delta_bias[d] (delta_bias NULL means 0).
+ * SSM_EULER_B: the input term uses the Euler rule, Bbar = delta * B, while
+ *   Abar stays exp(delta * A) -- the rule the bitig.info Mamba-3 page (section
+ *   "Gelistirilmis Ayriklastirma Semasi") attributes to Mamba-1 and -2.
+ *   Without it the input term is the zero-order hold (exp(delta A) - 1)/A * B.
+ */
+typedef enum {
+    SSM_DELTA_SOFTPLUS = 1,
+    SSM_EULER_B = 2
+} ssm_flags;
 
 /*
  * Full-sequence selective scan, zero initial state.
@@ -138,6 +156,27 @@ int ssm_scan_varlen_fwd(const void *x, const void *delta, const float *A,
                         int64_t L, int64_t Dm, int64_t N, int dtype, void *stream);
 
 /*
+ * The scan with every option: delta pre-processing and the input rule
+ * (ssm_flags), an initial state, and either a dense batch or packed sequences.
+ *
+ *   delta_bias : [Dm] fp32 or NULL -- added to delta before softplus
+ *   flags      : ssm_flags bits; other bits give SSM_ERR_BAD_OPTION
+ *   cu_seqlens : NULL -> dense batch, shapes as in ssm_scan_fwd_ex (h_init may
+ *                equal h_final);  non-NULL -> packed sequences as in
+ *                ssm_scan_varlen_fwd (Bsz must be 1, nseq sequences, h_init and
+ *                h_final [nseq][Dm][N] and not overlapping).  nseq is ignored
+ *                when cu_seqlens is NULL.
+ * Everything else as in ssm_scan_fwd_ex.  With flags = 0 and delta_bias NULL
+ * the result is bit-identical to ssm_scan_fwd_ex / ssm_scan_varlen_fwd.
+ */
+int ssm_scan_fused_fwd(const void *x, const void *delta, const float *delta_bias,
+                       const float *A, const void *B, const void *C, const float *D,
+                       const int64_t *cu_seqlens, int64_t nseq,
+                       const float *h_init, void *y, float *h_final,
+                       int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
+                       unsigned flags, void *stream);
+
+/*
  * One recurrent decode step on a resident state, updated in place
  * ("Mamba SSM Nedir?", section "Karmasiklik Karsilastirmasi": inference
  * updates a fixed-size state per token).  bf16 I/O:
@@ -161,6 +200,16 @@ int ssm_step_ex(const void *x, const void *delta, const float *A,
                 const void *B, const void *C, const float *D,
                 float *h, void *y,
                 int64_t Bsz, int64_t Dm, int64_t N, int dtype, void *stream);
+
+/*
+ * ssm_step_ex with the options of ssm_scan_fused_fwd: delta_bias [Dm] fp32 or
+ * NULL, flags = ssm_flags bits.  Stepping a state through L tokens with the
+ * same options reproduces the scan's y and final state.
+ */
+int ssm_step_fused(const void *x, const void *delta, const float *delta_bias,
+                   const float *A, const void *B, const void *C, const float *D,
+                   float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
+                   unsigned flags, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ssm_strerror(int code);

@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssmscan.so")
 
 ARCH = "gfx950"
-SOURCES = ["abi.cpp", "scan_kernels.hip", "step_kernel.hip"]
+SOURCES = ["abi.cpp", "scan_f32.hip", "scan_f32_packed.hip", "scan_bf16.hip", "scan_bf16_packed.hip",
+           "scan_launch.hip", "step_kernel.hip"]
 
 # Packed-FP32 instructions are switched off for every device pass.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
@@ -62,7 +63,7 @@ def build(verbose: bool = False, isa_dir: str = None) -> str:
             asm = os.path.join(isa_dir, os.path.splitext(src)[0] + f"-{ARCH}.s")
             cmds.append([cc, *COMMON, "-x", "hip", "--cuda-device-only", "-S",
                          os.path.join(CSRC, src), "-o", asm])
-    with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)

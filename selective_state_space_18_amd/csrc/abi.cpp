@@ -247,12 +247,15 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // ---------------------------------------------------------------------------
 
+constexpr unsigned kKnownFlags = SSM_DELTA_SOFTPLUS | SSM_EULER_B;
+
 int scan_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
               const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
               int64_t Dm, int64_t N, int dtype, void *stream, const int64_t *cu = nullptr,
-              int64_t nseq = 0) {
+              int64_t nseq = 0, const float *delta_bias = nullptr, unsigned flags = 0) {
     const bool varlen = cu != nullptr;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
+    if (flags & ~kKnownFlags) return fail(SSM_ERR_BAD_OPTION, "unknown flag bits 0x%x", flags & ~kKnownFlags);
     if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
     if (Bsz < 0 || L < 0 || Dm < 0)
         return fail(SSM_ERR_BAD_DIM, "negative size (Bsz=%lld, L=%lld, Dm=%lld)", (long long)Bsz,
@@ -266,8 +269,9 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     int64_t SDN = BDN;  // elements of h_init / h_final
     if (varlen && !mul_ok(nseq, DN, &SDN)) return fail(SSM_ERR_BAD_DIM, "nseq * Dm * N overflows");
     const Arg in[] = {{x, BLD, es, "x"}, {delta, BLD, es, "delta"}, {A, DN, 4, "A"}, {B, BLN, es, "B"},
-                      {C, BLN, es, "C"}, {D, Dm, 4, "D"}, {cu, varlen ? nseq + 1 : 0, 8, "cu_seqlens"}};
-    const int nin = varlen ? 7 : 6;
+                      {C, BLN, es, "C"}, {D, Dm, 4, "D"}, {delta_bias, delta_bias ? Dm : 0, 4, "delta_bias"},
+                      {cu, varlen ? nseq + 1 : 0, 8, "cu_seqlens"}};
+    const int nin = varlen ? 8 : 7;
     const Arg hi = {h_init, h_init ? SDN : 0, 4, "h_init"};
     const Arg ya = {y, BLD, es, "y"};
     const Arg hf = {h_final, h_final ? SDN : 0, 4, "h_final"};
@@ -304,6 +308,9 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     p.force_general = g_opt_force_general.load() ? 1 : 0;
     p.cu = cu;
     p.nseq = nseq;
+    p.delta_bias = delta_bias;
+    p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+    p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
 
     hipError_t e;
     if (varlen) {
@@ -362,8 +369,9 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
 
 int step_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
               const float *D, float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
-              void *stream) {
+              void *stream, const float *delta_bias = nullptr, unsigned flags = 0) {
     if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
+    if (flags & ~kKnownFlags) return fail(SSM_ERR_BAD_OPTION, "unknown flag bits 0x%x", flags & ~kKnownFlags);
     if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
     if (Bsz < 0 || Dm < 0)
         return fail(SSM_ERR_BAD_DIM, "negative size (Bsz=%lld, Dm=%lld)", (long long)Bsz, (long long)Dm);
@@ -374,15 +382,19 @@ int step_impl(const void *x, const void *delta, const float *A, const void *B, c
                     (long long)N);
     const int64_t es = dtype_size(dtype);
     const Arg in[] = {{x, BD, es, "x"}, {delta, BD, es, "delta"}, {A, DN, 4, "A"},
-                      {B, BN, es, "B"}, {C, BN, es, "C"}, {D, Dm, 4, "D"}};
+                      {B, BN, es, "B"}, {C, BN, es, "C"}, {D, Dm, 4, "D"},
+                      {delta_bias, delta_bias ? Dm : 0, 4, "delta_bias"}};
     const Arg ha = {h, BDN, 4, "h"};
     const Arg ya = {y, BD, es, "y"};
     int rc;
-    if ((rc = check_args(in, 6)) || (rc = check_args(&ha, 1)) || (rc = check_args(&ya, 1))) return rc;
-    if ((rc = check_output(ha, in, 6)) || (rc = check_output(ya, in, 6)) || (rc = check_output(ya, &ha, 1)))
+    if ((rc = check_args(in, 7)) || (rc = check_args(&ha, 1)) || (rc = check_args(&ya, 1))) return rc;
+    if ((rc = check_output(ha, in, 7)) || (rc = check_output(ya, in, 7)) || (rc = check_output(ya, &ha, 1)))
         return rc;
     if (BD == 0) return ok();
     ssm::StepParams p;
+    p.delta_bias = delta_bias;
+    p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+    p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
     p.x = x;
     p.delta = delta;
     p.B = B;
@@ -421,6 +433,25 @@ int ssm_scan_varlen_fwd(const void *x, const void *delta, const float *A, const 
     if (nseq == 0 && L > 0) return fail(SSM_ERR_BAD_DIM, "nseq = 0 but L = %lld", (long long)L);
     if (cu_seqlens == nullptr) return fail(SSM_ERR_NULLPTR, "cu_seqlens is NULL");
     return scan_impl(x, delta, A, B, C, D, h_init, y, h_final, 1, L, Dm, N, dtype, stream, cu_seqlens, nseq);
+}
+
+int ssm_scan_fused_fwd(const void *x, const void *delta, const float *delta_bias, const float *A,
+                       const void *B, const void *C, const float *D, const int64_t *cu_seqlens, int64_t nseq,
+                       const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L, int64_t Dm,
+                       int64_t N, int dtype, unsigned flags, void *stream) {
+    if (cu_seqlens != nullptr) {
+        if (Bsz != 1) return fail(SSM_ERR_BAD_DIM, "packed sequences need Bsz = 1 (got %lld)", (long long)Bsz);
+        if (nseq < 0) return fail(SSM_ERR_BAD_DIM, "nseq = %lld < 0", (long long)nseq);
+        if (nseq == 0 && L > 0) return fail(SSM_ERR_BAD_DIM, "nseq = 0 but L = %lld", (long long)L);
+    }
+    return scan_impl(x, delta, A, B, C, D, h_init, y, h_final, Bsz, L, Dm, N, dtype, stream, cu_seqlens,
+                     cu_seqlens ? nseq : 0, delta_bias, flags);
+}
+
+int ssm_step_fused(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+                   const void *C, const float *D, float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
+                   unsigned flags, void *stream) {
+    return step_impl(x, delta, A, B, C, D, h, y, Bsz, Dm, N, dtype, stream, delta_bias, flags);
 }
 
 int ssm_step(const void *x, const void *delta, const float *A, const void *B, const void *C,

@@ -1,9 +1,20 @@
-// Selective-scan kernels for gfx950 (CDNA4, wave64).
+// Selective-scan kernels for gfx950 (CDNA4, wave64): templates shared by the
+// per-(dtype, layout) translation units (scan_{bf16,f32}{,_packed}.hip).
 //
 // What is computed ("Mamba SSM Nedir?" page, sections "Ayrik Zamana Gecis"
 // and "State Space Model Temelleri"): per batch row b, channel d, state n,
 //   Abar = exp(delta_t A),  Bbar = (Abar - 1)/A * B_t[n],
 //   h_t = Abar h_{t-1} + Bbar x_t,   y_t = sum_n C_t[n] h_t + D x_t.
+// Options of the same recurrence:
+//   * Euler input term (kEuler): Bbar = delta_t B_t[n], Abar unchanged (the
+//     rule the bitig.info Mamba-3 page, section "Gelistirilmis Ayriklastirma
+//     Semasi", attributes to Mamba-1 and -2).
+//   * delta pre-processing (kPre): delta_t = softplus(raw_t + bias[d]) or
+//     raw_t + bias[d], the activation of delta's projection ("Mamba SSM
+//     Nedir?", section "Mamba'nin Yeniligi: Selective SSM"), applied as delta
+//     is read, so the activated delta never goes through HBM.
+//   * packed sequences (kVarlen, with ScanParams::cu): several sequences
+//     along time in one row, the state restarting at each start.
 //
 // Layout of the work
 //   * One lane owns one (b, d) channel and keeps all N states in VGPRs for the
@@ -25,7 +36,7 @@
 //       3. output: every segment reruns from its true entering state and
 //          writes y (and h_final for the last one).
 //
-// State representation.  Lanes carry g_n = (n+1) h_n.  Then
+// State representation.  Lanes carry g_n = (n+1) h_n.  Then (ZOH)
 //   g_n <- g_n + E_n (g_n + B_t[n] x_t (n+1)/A_n),   E_n = exp(delta A_n) - 1,
 //   y_t  = sum_n (C_t[n]/(n+1)) g_n + D x_t,
 // which is the recurrence above rewritten (Abar h + (Abar-1)/A B x
@@ -33,9 +44,13 @@
 // (the S4D-real structure) the factor (n+1)/A_n is the per-channel constant
 // 1/A[d,0] and E_{n+1} = (1 + E_n)(1 + E_1) - 1: one transcendental per
 // (t, d) and four FMAs per state element.  Any other A takes the general path
-// with one exp per state element.
+// with one exp per state element.  With the Euler input term the update is
+//   g_n <- g_n + E_n g_n + ((n+1) B_t[n]) (delta x_t),
+// also four FMAs per element.
 //
 // Arithmetic: fp32 for bf16 storage; fp64 for fp32 storage (see AccOf).
+#pragma once
+
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -47,44 +62,52 @@ constexpr int kBlock = 256;
 constexpr int kPrefetch = 4;  // time steps of x/delta loaded ahead of use
 
 // ---------------------------------------------------------------------------
-// B/C rows -> arithmetic type, C pre-divided by (n+1) for the scaled state.
+// B/C rows -> arithmetic type, C pre-divided by (n+1) for the scaled state;
+// with the Euler input term B is pre-multiplied by (n+1).
 
 template <typename T, int N>
 __global__ __launch_bounds__(kBlock) void bc_prep_kernel(const T *__restrict__ B,
                                                          const T *__restrict__ C,
                                                          typename AccOf<T>::type *__restrict__ bc,
-                                                         int64_t rows) {
+                                                         int64_t rows, int euler) {
     typedef typename AccOf<T>::type Acc;
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i >= rows * N) return;
     const int64_t r = i / N;
     const int n = (int)(i - r * N);
-    bc[r * (2 * N) + n] = (Acc)to_f32(B[i]);
+    const Acc bv = (Acc)to_f32(B[i]);
+    bc[r * (2 * N) + n] = euler ? bv * (Acc)(n + 1) : bv;
     bc[r * (2 * N) + N + n] = (Acc)to_f32(C[i]) / (Acc)(n + 1);
 }
 
 // ---------------------------------------------------------------------------
 // One time segment of one 64-channel tile.
 
-// Per-channel constants of the two update paths.  In fp32 the exponent
-// arguments are kept in base-2 units (a2 = A log2 e) so that exp2 needs no
-// scaling multiply; fp64 keeps natural units.
-template <int N, bool kStruct, typename Acc>
+// Per-channel constants of the update paths.  In fp32 the exponent arguments
+// are kept in base-2 units (a2 = A log2 e) so that exp2 needs no scaling
+// multiply; fp64 keeps natural units.
+template <int N, bool kStruct, bool kEuler, typename Acc>
 struct ChanConst {
-    Acc a0, inva;       // structured: A[d,0] (base-2 units in fp32) and 1/A[d,0]
-    Acc Aeff[N], W[N];  // general: A (tiny stand-in for ~0, base-2 units in fp32) and (n+1)/A
+    Acc a0, inva;       // structured: A[d,0] (base-2 units in fp32) and 1/A[d,0] (ZOH)
+    Acc Aeff[N], W[N];  // general: A (base-2 units in fp32) and, for ZOH, (n+1)/A
     __device__ __forceinline__ explicit ChanConst(const float (&Ar)[N]) {
         constexpr Acc unit = sizeof(Acc) == 4 ? (Acc)kLog2e : (Acc)1;
         a0 = (Acc)Ar[0] * unit;
         inva = 0;
         if constexpr (kStruct) {
-            inva = (Acc)1 / (Acc)Ar[0];
+            if constexpr (!kEuler) inva = (Acc)1 / (Acc)Ar[0];
         } else {
 #pragma unroll
             for (int n = 0; n < N; ++n) {
-                const Acc ae = (__builtin_fabsf(Ar[n]) < -kTinyA) ? (Acc)kTinyA : (Acc)Ar[n];
-                Aeff[n] = ae * unit;
-                W[n] = (Acc)(n + 1) / ae;
+                if constexpr (kEuler) {
+                    Aeff[n] = (Acc)Ar[n] * unit;  // no division by A: A = 0 is exact
+                    W[n] = 0;
+                } else {
+                    // tiny stand-in for A ~ 0 keeps (n+1)/A finite
+                    const Acc ae = (__builtin_fabsf(Ar[n]) < -kTinyA) ? (Acc)kTinyA : (Acc)Ar[n];
+                    Aeff[n] = ae * unit;
+                    W[n] = (Acc)(n + 1) / ae;
+                }
             }
         }
     }
@@ -92,23 +115,27 @@ struct ChanConst {
 
 // One time step of one channel: updates the scaled state g and returns
 // sum_n (C_t[n]/(n+1)) g_n (kOut) -- D x is added by the caller.
-// row = {B_t[0..N), C_t[0..N)/(n+1)}, wave-uniform.
-template <int N, bool kStruct, bool kOut, typename Acc>
-__device__ __forceinline__ Acc scan_step(const ChanConst<N, kStruct, Acc> &cc, const Acc (&row)[2 * N],
+// row = {B_t[n] (times n+1 for Euler), C_t[n]/(n+1)}, wave-uniform.
+template <int N, bool kStruct, bool kOut, bool kEuler, typename Acc>
+__device__ __forceinline__ Acc scan_step(const ChanConst<N, kStruct, kEuler, Acc> &cc, const Acc (&row)[2 * N],
                                          Acc xv, Acc dv, Acc (&g)[N]) {
     Acc yv = 0;
     if constexpr (kStruct) {
         Acc r;
         const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
-        // The aggregate pass (no y) carries j = A[d,0] g instead of g, which
-        // turns x/A[d,0] into x: j <- j + E_n (j + B_t[n] x).  The caller
+        // ZOH: the aggregate pass (no y) carries j = A[d,0] g instead of g,
+        // which turns x/A[d,0] into x: j <- j + E_n (j + B_t[n] x).  The caller
         // rescales j once at the end of the segment.
-        const Acc xa = kOut ? xv * cc.inva : xv;
+        const Acc xa = kEuler ? dv * xv : (kOut ? xv * cc.inva : xv);
         Acc E = E1;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const Acc tt = fma_(row[n], xa, g[n]);
-            g[n] = fma_(E, tt, g[n]);
+            if constexpr (kEuler) {
+                g[n] = fma_(row[n], xa, fma_(E, g[n], g[n]));
+            } else {
+                const Acc tt = fma_(row[n], xa, g[n]);
+                g[n] = fma_(E, tt, g[n]);
+            }
             if constexpr (kOut) yv = fma_(row[N + n], g[n], yv);
             // E_{n+1} = (1 + E_n)(1 + E_1) - 1.  fp32 uses the one-FMA form
             // with r = exp(delta A[d,0]); fp64 keeps E_1 unrounded
@@ -121,12 +148,17 @@ __device__ __forceinline__ Acc scan_step(const ChanConst<N, kStruct, Acc> &cc, c
             }
         }
     } else {
+        const Acc dx = dv * xv;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             Acc e;
             const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
-            const Acc tt = fma_(row[n], xv * cc.W[n], g[n]);
-            g[n] = fma_(E, tt, g[n]);
+            if constexpr (kEuler) {
+                g[n] = fma_(row[n], dx, fma_(E, g[n], g[n]));
+            } else {
+                const Acc tt = fma_(row[n], xv * cc.W[n], g[n]);
+                g[n] = fma_(E, tt, g[n]);
+            }
             if constexpr (kOut) yv = fma_(row[N + n], g[n], yv);
         }
     }
@@ -145,10 +177,10 @@ __device__ __forceinline__ void load_row(Acc (&dst)[2 * N], const_row_ptr<Acc> s
     for (int i = 0; i < 2 * N; ++i) dst[i] = src[i];
 }
 
-// The x/delta/y streams of one 64-channel tile over one segment: buffer
-// descriptors based at (b, t0, d0), a per-lane byte offset and the byte
-// stride of one time step.  All offsets are 32-bit (the planner keeps a
-// segment's span below 1 GiB) and out-of-range accesses are dropped by the
+// The x/delta/y streams of one 64-channel tile over a run of steps: buffer
+// descriptors based at (b, t, d0), a per-lane byte offset and the byte stride
+// of one time step.  All offsets are 32-bit (the planner keeps a segment's
+// span below 1 GiB) and out-of-range accesses are dropped by the
 // descriptors' range check.
 template <typename T>
 struct SegIO {
@@ -156,6 +188,108 @@ struct SegIO {
     int32_t voff;  // lane byte offset within a step (0 for idle lanes)
     int32_t row;   // bytes per time step (Dm * sizeof(T))
 };
+
+// delta as the recurrence uses it, from the stored value: + bias[d], then
+// softplus if asked (kPre); the stored value itself otherwise.
+template <typename Acc>
+struct DeltaPre {
+    Acc bias;
+    bool softplus;
+};
+
+template <typename T, int N, bool kStruct, bool kOut, bool kEuler, bool kPre, typename Acc>
+__device__ __forceinline__ void run_group(const SegIO<T> &io, const_row_ptr<Acc> bcp, int tb, int nsteps,
+                                          const T (&xs)[kPrefetch], const T (&ds)[kPrefetch],
+                                          const ChanConst<N, kStruct, kEuler, Acc> &cc, Acc Dd,
+                                          const DeltaPre<Acc> &dp, Acc (&g)[N], Acc &lam,
+                                          Acc (&rowc)[2 * N]) {
+    const int last = nsteps - 1;
+    const bool full = tb + kPrefetch <= nsteps;
+    Acc dpre[kPrefetch];
+    if constexpr (kPre) {
+        // the whole group at once: one uniform branch per kPrefetch steps
+        if (dp.softplus) {
+#pragma unroll
+            for (int k = 0; k < kPrefetch; ++k) dpre[k] = softplus_(to_f32(ds[k]) + dp.bias);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kPrefetch; ++k) dpre[k] = (Acc)to_f32(ds[k]) + dp.bias;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+        if (full || tb + k < nsteps) {
+            Acc rown[2 * N];
+            const int tn = tb + k + 1;
+            load_row<N>(rown, bcp + (int64_t)(tn < last ? tn : last) * (2 * N));
+            const Acc xv = (Acc)to_f32(xs[k]);
+            const Acc dv = kPre ? dpre[k] : (Acc)to_f32(ds[k]);
+            const Acc yv = scan_step<N, kStruct, kOut, kEuler>(cc, rowc, xv, dv, g);
+            if constexpr (kOut) {
+                buf_store(from_acc<T>(fma_(Dd, xv, yv)), io.y, io.voff, (tb + k) * io.row);
+            } else {
+                lam += dv;
+            }
+#pragma unroll
+            for (int i = 0; i < 2 * N; ++i) rowc[i] = rown[i];
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_group(const SegIO<T> &io, int tb, int last, T (&xs)[kPrefetch],
+                                           T (&ds)[kPrefetch]) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+        const int t = tb + k;
+        const int so = (t < last ? t : last) * io.row;
+        xs[k] = buf_load<T>(io.x, io.voff, so);
+        ds[k] = buf_load<T>(io.dl, io.voff, so);
+    }
+}
+
+// Runs `nsteps` (>= 1) time steps.  x/delta are fetched one group of
+// kPrefetch steps ahead into alternating register sets (indices clamped into
+// the run); the B/C row of the next step is fetched while the current one is
+// computed.  Idle lanes of a partial tile shadow a valid channel: they compute
+// exactly what that channel's lane computes and store the identical value.
+template <typename T, int N, bool kStruct, bool kOut, bool kEuler, bool kPre, typename Acc>
+__device__ __forceinline__ void run_segment(const SegIO<T> &io, const_row_ptr<Acc> bcp, int nsteps,
+                                            const float (&Ar)[N], Acc Dd, const DeltaPre<Acc> &dp,
+                                            Acc (&g)[N], Acc &lam) {
+    const ChanConst<N, kStruct, kEuler, Acc> cc(Ar);
+    const int last = nsteps - 1;
+    T xa[kPrefetch], da[kPrefetch], xb[kPrefetch], db[kPrefetch];
+    load_group(io, 0, last, xa, da);
+    Acc rowc[2 * N];
+    load_row<N>(rowc, bcp);
+    for (int tb = 0; tb < nsteps; tb += 2 * kPrefetch) {
+        load_group(io, tb + kPrefetch, last, xb, db);
+        run_group<T, N, kStruct, kOut, kEuler, kPre>(io, bcp, tb, nsteps, xa, da, cc, Dd, dp, g, lam, rowc);
+        if (tb + kPrefetch >= nsteps) break;
+        load_group(io, tb + 2 * kPrefetch, last, xa, da);
+        run_group<T, N, kStruct, kOut, kEuler, kPre>(io, bcp, tb + kPrefetch, nsteps, xb, db, cc, Dd, dp, g, lam,
+                                                     rowc);
+    }
+}
+
+// The x/delta/y streams and B/C rows of steps [t, t + n) of batch row b for
+// the 64-channel tile at d0 (lane channel d).
+template <typename T, typename Acc, int N, bool kOut>
+__device__ __forceinline__ SegIO<T> seg_io(const ScanParams &p, int64_t b, int64_t t, int n, int64_t d0,
+                                           int64_t d, const_row_ptr<Acc> &bcp) {
+    const int64_t off = (b * p.L + t) * p.Dm + d0;
+    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
+    const int32_t span = n * row;
+    SegIO<T> io;
+    io.x = make_rsrc(static_cast<const T *>(p.x) + off, span);
+    io.dl = make_rsrc(static_cast<const T *>(p.delta) + off, span);
+    io.y = make_rsrc(kOut ? static_cast<const T *>(p.y) + off : static_cast<const T *>(p.x) + off, kOut ? span : 0);
+    io.voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
+    io.row = row;
+    bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t) * (2 * N));
+    return io;
+}
 
 // Packed variable-length input: the wave-uniform position in the list of
 // sequences.  A sequence starts at cu[k] and ends at cu[k+1] - 1.
@@ -200,87 +334,6 @@ __device__ __forceinline__ int64_t seq_advance(SeqTrack &sq, int64_t t) {
     return k;
 }
 
-template <typename T, int N, bool kStruct, bool kOut, typename Acc>
-__device__ __forceinline__ void run_group(const SegIO<T> &io, const_row_ptr<Acc> bcp, int tb, int nsteps,
-                                          const T (&xs)[kPrefetch], const T (&ds)[kPrefetch],
-                                          const ChanConst<N, kStruct, Acc> &cc, Acc Dd, Acc (&g)[N],
-                                          Acc &lam, Acc (&rowc)[2 * N]) {
-    const int last = nsteps - 1;
-    const bool full = tb + kPrefetch <= nsteps;
-#pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) {
-        if (full || tb + k < nsteps) {
-            Acc rown[2 * N];
-            const int tn = tb + k + 1;
-            load_row<N>(rown, bcp + (int64_t)(tn < last ? tn : last) * (2 * N));
-            const Acc xv = (Acc)to_f32(xs[k]);
-            const Acc dv = (Acc)to_f32(ds[k]);
-            const Acc yv = scan_step<N, kStruct, kOut>(cc, rowc, xv, dv, g);
-            if constexpr (kOut) {
-                buf_store(from_acc<T>(fma_(Dd, xv, yv)), io.y, io.voff, (tb + k) * io.row);
-            } else {
-                lam += dv;
-            }
-#pragma unroll
-            for (int i = 0; i < 2 * N; ++i) rowc[i] = rown[i];
-        }
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void load_group(const SegIO<T> &io, int tb, int last, T (&xs)[kPrefetch],
-                                           T (&ds)[kPrefetch]) {
-#pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) {
-        const int t = tb + k;
-        const int so = (t < last ? t : last) * io.row;
-        xs[k] = buf_load<T>(io.x, io.voff, so);
-        ds[k] = buf_load<T>(io.dl, io.voff, so);
-    }
-}
-
-// Runs `nsteps` (>= 1) time steps of one segment.  x/delta are fetched one
-// group of kPrefetch steps ahead into alternating register sets (indices
-// clamped into the segment); the B/C row of the next step is fetched while
-// the current one is computed.  Idle lanes of a partial tile shadow a valid
-// channel: they compute exactly what that channel's lane computes and store
-// the identical value.
-template <typename T, int N, bool kStruct, bool kOut, typename Acc>
-__device__ __forceinline__ void run_segment(const SegIO<T> &io, const_row_ptr<Acc> bcp, int nsteps,
-                                            const float (&Ar)[N], Acc Dd, Acc (&g)[N], Acc &lam) {
-    const ChanConst<N, kStruct, Acc> cc(Ar);
-    const int last = nsteps - 1;
-    T xa[kPrefetch], da[kPrefetch], xb[kPrefetch], db[kPrefetch];
-    load_group(io, 0, last, xa, da);
-    Acc rowc[2 * N];
-    load_row<N>(rowc, bcp);
-    for (int tb = 0; tb < nsteps; tb += 2 * kPrefetch) {
-        load_group(io, tb + kPrefetch, last, xb, db);
-        run_group<T, N, kStruct, kOut>(io, bcp, tb, nsteps, xa, da, cc, Dd, g, lam, rowc);
-        if (tb + kPrefetch >= nsteps) break;
-        load_group(io, tb + 2 * kPrefetch, last, xa, da);
-        run_group<T, N, kStruct, kOut>(io, bcp, tb + kPrefetch, nsteps, xb, db, cc, Dd, g, lam, rowc);
-    }
-}
-
-// The x/delta/y streams and B/C rows of steps [t, t + n) of batch row b for
-// the 64-channel tile at d0 (lane channel d).
-template <typename T, typename Acc, int N, bool kOut>
-__device__ __forceinline__ SegIO<T> seg_io(const ScanParams &p, int64_t b, int64_t t, int n, int64_t d0,
-                                           int64_t d, const_row_ptr<Acc> &bcp) {
-    const int64_t off = (b * p.L + t) * p.Dm + d0;
-    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
-    const int32_t span = n * row;
-    SegIO<T> io;
-    io.x = make_rsrc(static_cast<const T *>(p.x) + off, span);
-    io.dl = make_rsrc(static_cast<const T *>(p.delta) + off, span);
-    io.y = make_rsrc(kOut ? static_cast<const T *>(p.y) + off : static_cast<const T *>(p.x) + off, kOut ? span : 0);
-    io.voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
-    io.row = row;
-    bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t) * (2 * N));
-    return io;
-}
-
 // kOut = false: aggregate pass over segments 0..S-2.
 // kOut = true : output pass over segments 0..S-1.
 // kStruct selects the waves this launch serves: a wave whose 64 channels all
@@ -288,7 +341,9 @@ __device__ __forceinline__ SegIO<T> seg_io(const ScanParams &p, int64_t b, int64
 // by the kStruct = true launch, every other wave by the kStruct = false one.
 // Keeping the two paths in separate kernels keeps the structured kernel's
 // register count (and so its occupancy) free of the general path's.
-template <typename T, int N, bool kOut, bool kStruct, bool kVarlen>
+// kVarlen: packed sequences (ScanParams::cu is set).  A template parameter
+// rather than a run-time test so the dense kernels carry none of its code.
+template <typename T, int N, bool kOut, bool kStruct, bool kEuler, bool kPre, bool kVarlen>
 __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
     typedef typename AccOf<T>::type Acc;
     const int blocks_per_seg = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
@@ -307,6 +362,7 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
     const int64_t BD = p.Bsz * p.Dm;
     const int64_t t0 = (int64_t)s * p.seg_len;
     const int nsteps = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
+    constexpr bool varlen = kVarlen;
 
     float Ar[N];
 #pragma unroll
@@ -316,19 +372,20 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
     for (int n = 1; n < N; ++n) st = st && (Ar[n] == (float)(n + 1) * Ar[0]);
     if ((bool)__all(st) != kStruct) return;
     const Acc Dd = (Acc)p.D[d];
+    DeltaPre<Acc> dp;
+    dp.bias = (kPre && p.delta_bias != nullptr) ? (Acc)p.delta_bias[d] : (Acc)0;
+    dp.softplus = p.delta_softplus != 0;
 
     // Entering state: from the carry pass when time is split (it also holds
     // segment 0's, so h_init is never read here while the last segment may be
-    // writing h_final into the same buffer); else h_init read by this lane.
+    // writing h_final into the same buffer); else h_init read by this lane
+    // (packed sequences restart from their own h_init below).
     const Acc *gin = static_cast<const Acc *>(p.gin);
     Acc g[N];
-    if (kVarlen && !(kOut && p.S > 1)) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) g[n] = 0;  // every sequence restarts from its own h_init
-    } else if (kOut && p.S > 1) {
+    if (kOut && p.S > 1) {
 #pragma unroll
         for (int n = 0; n < N; ++n) g[n] = gin[((int64_t)s * N + n) * BD + ch];
-    } else if (kOut && p.h_init != nullptr) {
+    } else if (kOut && p.h_init != nullptr && !varlen) {
 #pragma unroll
         for (int n = 0; n < N; ++n) g[n] = (Acc)p.h_init[ch * N + n] * (Acc)(n + 1);
     } else {
@@ -337,10 +394,10 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
     }
 
     Acc lam = 0;
-    if constexpr (!kVarlen) {
+    if constexpr (!varlen) {
         const_row_ptr<Acc> bcp;
         const SegIO<T> io = seg_io<T, Acc, N, kOut>(p, b, t0, nsteps, d0, d, bcp);
-        run_segment<T, N, kStruct, kOut>(io, bcp, nsteps, Ar, Dd, g, lam);
+        run_segment<T, N, kStruct, kOut, kEuler, kPre>(io, bcp, nsteps, Ar, Dd, dp, g, lam);
     } else {
         // Packed sequences: the segment is cut at every sequence start; each
         // piece runs the plain loop, and between pieces the state restarts from
@@ -356,8 +413,8 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
             if (t == sq.next_start) {
                 const int64_t k = seq_advance(sq, t);
                 reset = true;
-                // the aggregate pass of the structured path carries A[d,0] g
-                const Acc scale = (!kOut && kStruct) ? (Acc)Ar[0] : (Acc)1;
+                // the ZOH aggregate pass of the structured path carries A[d,0] g
+                const Acc scale = (!kOut && kStruct && !kEuler) ? (Acc)Ar[0] : (Acc)1;
                 if (p.h_init != nullptr) {
                     const float *hi = p.h_init + (k * p.Dm + d) * N;
 #pragma unroll
@@ -372,7 +429,7 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
             const int n = uniform((int)(piece_end - t));
             const_row_ptr<Acc> bcp;
             const SegIO<T> io = seg_io<T, Acc, N, kOut>(p, b, t, n, d0, d, bcp);
-            run_segment<T, N, kStruct, kOut>(io, bcp, n, Ar, Dd, g, lam);
+            run_segment<T, N, kStruct, kOut, kEuler, kPre>(io, bcp, n, Ar, Dd, dp, g, lam);
             if constexpr (kOut) {
                 // the current sequence ends with this piece
                 if (piece_end == sq.next_start && p.h_final != nullptr && active) {
@@ -392,7 +449,7 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
 
     if (!active) return;
     if constexpr (!kOut) {
-        if constexpr (kStruct) {
+        if constexpr (kStruct && !kEuler) {
             const Acc inva = (Acc)1 / (Acc)Ar[0];
 #pragma unroll
             for (int n = 0; n < N; ++n) g[n] *= inva;
@@ -401,8 +458,8 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
 #pragma unroll
         for (int n = 0; n < N; ++n) a[(int64_t)n * BD] = g[n];
         a[(int64_t)N * BD] = lam;
-    } else if constexpr (!kVarlen) {
-        if (s == p.S - 1 && p.h_final != nullptr) {
+    } else {
+        if (!kVarlen && s == p.S - 1 && p.h_final != nullptr) {
 #pragma unroll
             for (int n = 0; n < N; ++n) p.h_final[ch * N + n] = (float)(g[n] / (Acc)(n + 1));
         }
@@ -412,7 +469,8 @@ __global__ __launch_bounds__(kBlock) void scan_segment_kernel(ScanParams p) {
 // ---------------------------------------------------------------------------
 // Carry between segments: one thread per (state n, channel).  Entering state
 // of segment s+1 = exp(A_n * sum(delta over s)) * entering state of s + local
-// end state of s; segment 0 enters with h_init (or zero).
+// end state of s; segment 0 enters with h_init (or zero).  Abar is exp(delta
+// A) under both input rules, so the decay of a segment only needs its delta sum.
 
 template <typename Acc, int N>
 __global__ __launch_bounds__(kBlock) void scan_carry_kernel(ScanParams p) {
@@ -473,27 +531,32 @@ __global__ __launch_bounds__(kBlock) void scan_carry_kernel(ScanParams p) {
     }
 }
 
-// h_final of empty sequences in a packed variable-length call: their
-// initial state.  One thread per (sequence, d, n).
-__global__ __launch_bounds__(kBlock) void varlen_empty_kernel(const int64_t *__restrict__ cu, int64_t nseq,
-                                                              const float *__restrict__ h_init,
-                                                              float *__restrict__ h_final, int64_t dn) {
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= nseq * dn) return;
-    const int64_t k = i / dn;
-    if (cu[k] != cu[k + 1]) return;
-    h_final[i] = h_init ? h_init[i] : 0.f;
+template <typename T, int N, bool kOut, bool kEuler, bool kPre, bool kVarlen>
+void launch_both_paths(const ScanParams &p, unsigned grid, hipStream_t s) {
+    // Both A paths are launched; each wave runs in exactly one of them.
+    hipLaunchKernelGGL((scan_segment_kernel<T, N, kOut, true, kEuler, kPre, kVarlen>), dim3(grid), dim3(kBlock), 0,
+                       s, p);
+    hipLaunchKernelGGL((scan_segment_kernel<T, N, kOut, false, kEuler, kPre, kVarlen>), dim3(grid), dim3(kBlock), 0,
+                       s, p);
 }
 
-// h_final for an empty sequence: the initial state.
-__global__ __launch_bounds__(kBlock) void state_init_kernel(const float *__restrict__ h_init,
-                                                            float *__restrict__ h_final,
-                                                            int64_t count) {
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i < count) h_final[i] = h_init ? h_init[i] : 0.f;
+template <typename T, int N, bool kOut, bool kVarlen>
+void launch_variant(const ScanParams &p, unsigned grid, hipStream_t s) {
+    const bool pre = p.delta_bias != nullptr || p.delta_softplus != 0;
+    if (p.euler_b) {
+        if (pre)
+            launch_both_paths<T, N, kOut, true, true, kVarlen>(p, grid, s);
+        else
+            launch_both_paths<T, N, kOut, true, false, kVarlen>(p, grid, s);
+    } else {
+        if (pre)
+            launch_both_paths<T, N, kOut, false, true, kVarlen>(p, grid, s);
+        else
+            launch_both_paths<T, N, kOut, false, false, kVarlen>(p, grid, s);
+    }
 }
 
-template <typename T, int N>
+template <typename T, int N, bool kVarlen>
 struct ByN {
     typedef typename AccOf<T>::type Acc;
     static hipError_t prep(const ScanParams &p, hipStream_t s) {
@@ -501,9 +564,8 @@ struct ByN {
         const int64_t work = rows * N;
         if (work == 0) return hipSuccess;
         const unsigned grid = (unsigned)((work + kBlock - 1) / kBlock);
-        hipLaunchKernelGGL((bc_prep_kernel<T, N>), dim3(grid), dim3(kBlock), 0, s,
-                           static_cast<const T *>(p.B), static_cast<const T *>(p.C),
-                           static_cast<Acc *>(p.bc), rows);
+        hipLaunchKernelGGL((bc_prep_kernel<T, N>), dim3(grid), dim3(kBlock), 0, s, static_cast<const T *>(p.B),
+                           static_cast<const T *>(p.C), static_cast<Acc *>(p.bc), rows, p.euler_b);
         return hipGetLastError();
     }
     static hipError_t segments(const ScanParams &p, bool out, hipStream_t s) {
@@ -511,22 +573,10 @@ struct ByN {
         const int nseg = out ? p.S : p.S - 1;
         if (nseg <= 0 || bps == 0) return hipSuccess;
         const unsigned grid = (unsigned)bps * (unsigned)nseg;
-        // Both paths are launched; each wave runs in exactly one of them.
-        if (p.cu != nullptr) {
-            if (out) {
-                hipLaunchKernelGGL((scan_segment_kernel<T, N, true, true, true>), dim3(grid), dim3(kBlock), 0, s, p);
-                hipLaunchKernelGGL((scan_segment_kernel<T, N, true, false, true>), dim3(grid), dim3(kBlock), 0, s, p);
-            } else {
-                hipLaunchKernelGGL((scan_segment_kernel<T, N, false, true, true>), dim3(grid), dim3(kBlock), 0, s, p);
-                hipLaunchKernelGGL((scan_segment_kernel<T, N, false, false, true>), dim3(grid), dim3(kBlock), 0, s, p);
-            }
-        } else if (out) {
-            hipLaunchKernelGGL((scan_segment_kernel<T, N, true, true, false>), dim3(grid), dim3(kBlock), 0, s, p);
-            hipLaunchKernelGGL((scan_segment_kernel<T, N, true, false, false>), dim3(grid), dim3(kBlock), 0, s, p);
-        } else {
-            hipLaunchKernelGGL((scan_segment_kernel<T, N, false, true, false>), dim3(grid), dim3(kBlock), 0, s, p);
-            hipLaunchKernelGGL((scan_segment_kernel<T, N, false, false, false>), dim3(grid), dim3(kBlock), 0, s, p);
-        }
+        if (out)
+            launch_variant<T, N, true, kVarlen>(p, grid, s);
+        else
+            launch_variant<T, N, false, kVarlen>(p, grid, s);
         return hipGetLastError();
     }
     static hipError_t carry(const ScanParams &p, hipStream_t s) {
@@ -538,60 +588,29 @@ struct ByN {
     }
 };
 
-template <typename T, typename F>
-hipError_t with_n(int N, F f) {
+// Every pass of a scan for storage type T; kVarlen must match p.cu != nullptr.
+template <typename T, bool kVarlen>
+hipError_t scan_pass(ScanPass pass, const ScanParams &p, int N, hipStream_t s) {
+    auto run = [&](auto k) -> hipError_t {
+        typedef decltype(k) K;
+        switch (pass) {
+            case ScanPass::kPrep: return K::prep(p, s);
+            case ScanPass::kAggregate: return K::segments(p, false, s);
+            case ScanPass::kCarry: return K::carry(p, s);
+            case ScanPass::kOutput: return K::segments(p, true, s);
+        }
+        return hipErrorInvalidValue;
+    };
     switch (N) {
-        case 1: return f(ByN<T, 1>());
-        case 2: return f(ByN<T, 2>());
-        case 4: return f(ByN<T, 4>());
-        case 8: return f(ByN<T, 8>());
-        case 16: return f(ByN<T, 16>());
+        case 1: return run(ByN<T, 1, kVarlen>());
+        case 2: return run(ByN<T, 2, kVarlen>());
+        case 4: return run(ByN<T, 4, kVarlen>());
+        case 8: return run(ByN<T, 8, kVarlen>());
+        case 16: return run(ByN<T, 16, kVarlen>());
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename F>
-hipError_t with_type(int N, int dtype, F f) {
-    if (dtype == 0) return with_n<float>(N, f);
-    if (dtype == 1) return with_n<bf16>(N, f);
-    return hipErrorInvalidValue;
-}
-
 }  // namespace
-
-size_t scan_acc_bytes(int dtype) { return dtype == 0 ? sizeof(double) : sizeof(float); }
-
-hipError_t launch_bc_prep(const ScanParams &p, int N, int dtype, hipStream_t s) {
-    return with_type(N, dtype, [&](auto k) { return decltype(k)::prep(p, s); });
-}
-
-hipError_t launch_scan_aggregate(const ScanParams &p, int N, int dtype, hipStream_t s) {
-    return with_type(N, dtype, [&](auto k) { return decltype(k)::segments(p, false, s); });
-}
-
-hipError_t launch_scan_carry(const ScanParams &p, int N, int dtype, hipStream_t s) {
-    return with_type(N, dtype, [&](auto k) { return decltype(k)::carry(p, s); });
-}
-
-hipError_t launch_scan_output(const ScanParams &p, int N, int dtype, hipStream_t s) {
-    return with_type(N, dtype, [&](auto k) { return decltype(k)::segments(p, true, s); });
-}
-
-hipError_t launch_varlen_empty(const ScanParams &p, int N, hipStream_t s) {
-    const int64_t dn = p.Dm * N;
-    const int64_t count = p.nseq * dn;
-    if (count == 0 || p.h_final == nullptr || p.cu == nullptr) return hipSuccess;
-    const unsigned grid = (unsigned)((count + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL(varlen_empty_kernel, dim3(grid), dim3(kBlock), 0, s, p.cu, p.nseq, p.h_init, p.h_final, dn);
-    return hipGetLastError();
-}
-
-hipError_t launch_state_init(const ScanParams &p, int N, hipStream_t s) {
-    const int64_t count = p.Bsz * p.Dm * N;
-    if (count == 0 || p.h_final == nullptr) return hipSuccess;
-    const unsigned grid = (unsigned)((count + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL(state_init_kernel, dim3(grid), dim3(kBlock), 0, s, p.h_init, p.h_final, count);
-    return hipGetLastError();
-}
 
 }  // namespace ssm

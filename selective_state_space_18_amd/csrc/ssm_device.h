@@ -117,6 +117,32 @@ __device__ __forceinline__ float expm1_and_exp_precise(float z, float& e) {
     return m;
 }
 
+// softplus(v) = log(1 + exp(v)) = max(v, 0) + log1p(exp(-|v|)).
+//  fp64: ocml log1p / exp.
+//  fp32: u = exp(-|v|) on the transcendental unit; log1p(u) is the quartic
+//        series u - u^2/2 + u^3/3 - u^4/4 for u < 2^-5 (truncation below
+//        u^5/5, relative 2e-7), else log2(1 + u) ln 2 on the transcendental
+//        unit (1 + u rounds by at most 2^-24 against a result of at least
+//        0.03).  Large v gives u = 0 and returns v; NaN propagates.
+__device__ __forceinline__ double softplus_(double v) {
+    const double m = v < 0.0 ? 0.0 : v;
+    return m + log1p(exp(-__builtin_fabs(v)));
+}
+__device__ __forceinline__ float softplus_(float v) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    const float u = fast_exp2(-__builtin_fabsf(v) * kLog2e);
+    const float series = u * __builtin_fmaf(u, __builtin_fmaf(u, __builtin_fmaf(u, -0.25f, 1.0f / 3.0f), -0.5f), 1.0f);
+    const float lg = __builtin_amdgcn_logf(1.0f + u) * kLn2;
+    const float m = v < 0.f ? 0.f : v;
+    return m + (u < 0.03125f ? series : lg);
+}
+
+// Accurate fp32 softplus (ocml log1pf / expf), for the fp32-storage decode step.
+__device__ __forceinline__ float softplus_precise(float v) {
+    const float m = v < 0.f ? 0.f : v;
+    return m + log1pf(expf(-__builtin_fabsf(v)));
+}
+
 // exp of an argument in the arithmetic type's exponent units: natural units
 // in fp64 (ocml exp), base-2 units in fp32 (z already multiplied by log2 e).
 __device__ __forceinline__ double exp_units(double z) { return exp(z); }

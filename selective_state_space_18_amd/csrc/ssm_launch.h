@@ -32,6 +32,11 @@ struct ScanParams {
     const int64_t *cu;
     int64_t nseq;
     int *seg_reset;    // [S]: 1 if a sequence starts inside segment s (varlen only)
+    // delta as stored -> delta as used: + delta_bias[d] (if not null), then
+    // softplus (if delta_softplus).  Neither: delta is used as stored.
+    const float *delta_bias;
+    int delta_softplus;
+    int euler_b;       // 1: input term Bbar = delta B (else the ZOH term)
 };
 
 struct StepParams {
@@ -40,10 +45,24 @@ struct StepParams {
     float *h;
     void *y;
     int64_t Bsz, Dm;
+    const float *delta_bias;  // as in ScanParams
+    int delta_softplus;
+    int euler_b;
 };
+
+// The passes of one scan call, in launch order.
+enum class ScanPass { kPrep, kAggregate, kCarry, kOutput };
 
 // Bytes per element of the scan's arithmetic type for a storage dtype.
 size_t scan_acc_bytes(int dtype);
+
+// Per storage type and layout (dense batch / packed sequences), one
+// translation unit each: scan_f32.hip, scan_f32_packed.hip, scan_bf16.hip,
+// scan_bf16_packed.hip.
+hipError_t scan_pass_f32(ScanPass pass, const ScanParams &p, int N, hipStream_t s);
+hipError_t scan_pass_f32_packed(ScanPass pass, const ScanParams &p, int N, hipStream_t s);
+hipError_t scan_pass_bf16(ScanPass pass, const ScanParams &p, int N, hipStream_t s);
+hipError_t scan_pass_bf16_packed(ScanPass pass, const ScanParams &p, int N, hipStream_t s);
 
 // dtype: 0 = fp32, 1 = bf16.  N in {1,2,4,8,16}.  All return hipSuccess or the
 // launch error.

@@ -4,7 +4,9 @@
 // and "Karmasiklik Karsilastirmasi": inference updates a fixed-size state):
 //   h[n] <- exp(delta A[n]) h[n] + (exp(delta A[n]) - 1)/A[n] B[n] x
 //   y     = sum_n C[n] h[n] + D x
-// (the input coefficient takes its limit delta B[n] at A[n] = 0).
+// (the input coefficient takes its limit delta B[n] at A[n] = 0).  The
+// options of the scan apply here too: delta = softplus(delta_in + bias[d])
+// (or delta_in + bias[d]) and the Euler input term delta B[n] x.
 //
 // The step reads and writes the whole fp32 state once, so it is bound by HBM
 // bandwidth.  Q = N/4 lanes share one (b, d) channel and each owns 4
@@ -76,6 +78,10 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepParams p, int64_t chan
         const int64_t d = ch - b * p.Dm;
         const T *Bp = static_cast<const T *>(p.B) + b * N + j * SPL;
         const T *Cp = static_cast<const T *>(p.C) + b * N + j * SPL;
+        if (p.delta_bias != nullptr || p.delta_softplus) {  // uniform over the launch
+            const float v = dv[u] + (p.delta_bias != nullptr ? p.delta_bias[d] : 0.f);
+            dv[u] = p.delta_softplus ? (kPrecise ? softplus_precise(v) : softplus_(v)) : v;
+        }
         float yv = 0.f;
 #pragma unroll
         for (int k = 0; k < SPL; ++k) {
@@ -83,7 +89,9 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepParams p, int64_t chan
             const float E = kPrecise ? expm1_and_exp_precise(dv[u] * a[u][k], abar)
                                      : expm1_and_exp(dv[u] * a[u][k], abar);
             float coef;
-            if constexpr (kPrecise)
+            if (p.euler_b)
+                coef = dv[u];
+            else if constexpr (kPrecise)
                 coef = (a[u][k] != 0.f) ? E / a[u][k] : dv[u];
             else
                 coef = (a[u][k] != 0.f) ? E * __builtin_amdgcn_rcpf(a[u][k]) : dv[u];

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 SSM_OPT_SEGMENT_LEN, SSM_OPT_FORCE_GENERAL, SSM_OPT_PROFILE, SSM_OPT_STEP_CHANNELS = 1, 2, 3, 4
+SSM_DELTA_SOFTPLUS, SSM_EULER_B = 1, 2  # ssm_flags
 KERNEL_KINDS = ("bc_prep", "scan_aggregate", "scan_carry", "scan_output", "step", "state_init")
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_BAD_DTYPE",
           4: "SSM_ERR_UNSUPPORTED_N", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_NOMEM",
@@ -30,7 +31,8 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_B
 # Every symbol include/ssmscan.h declares.
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_strerror",
            "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
-           "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd")
+           "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
+           "ssm_scan_fused_fwd", "ssm_step_fused")
 
 
 class SSMError(RuntimeError):
@@ -57,6 +59,10 @@ def lib():
     L.ssm_scan_fwd_ex.argtypes = [_vp] * 9 + [_i64] * 4 + [ctypes.c_int, _vp]
     L.ssm_scan_varlen_fwd.argtypes = [_vp] * 7 + [_i64] + [_vp] * 3 + [_i64] * 3 + [ctypes.c_int, _vp]
     L.ssm_scan_varlen_fwd.restype = ctypes.c_int
+    L.ssm_scan_fused_fwd.argtypes = [_vp] * 8 + [_i64] + [_vp] * 3 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
+    L.ssm_scan_fused_fwd.restype = ctypes.c_int
+    L.ssm_step_fused.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint, _vp]
+    L.ssm_step_fused.restype = ctypes.c_int
     L.ssm_step.argtypes = [_vp] * 8 + [_i64] * 3 + [_vp]
     L.ssm_step_ex.argtypes = [_vp] * 8 + [_i64] * 3 + [ctypes.c_int, _vp]
     for f in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex"):
@@ -155,13 +161,30 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def scan_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, want_state=True):
+def _flags(delta_softplus, euler_b):
+    return (SSM_DELTA_SOFTPLUS if delta_softplus else 0) | (SSM_EULER_B if euler_b else 0)
+
+
+def _bias(delta_bias, Dm, dev):
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (Dm,), torch.float32, dev)
+    return delta_bias
+
+
+def scan_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, want_state=True,
+             delta_bias=None, delta_softplus=False, euler_b=False):
     """Selective scan over [Bsz, L, Dm] with state size N = A.shape[1].
 
     x, delta: [Bsz, L, Dm]; B, C: [Bsz, L, N] (all the same dtype, fp32 or bf16);
     A: [Dm, N] fp32; D: [Dm] fp32; h_init: optional [Bsz, Dm, N] fp32.
+    Options: delta_bias [Dm] fp32 is added to delta, delta_softplus applies
+    softplus to the sum, euler_b uses the input term delta*B.
     Returns (y [Bsz, L, Dm] in x's dtype, h_final [Bsz, Dm, N] fp32 or None).
     """
+    if delta_bias is not None or delta_softplus or euler_b:
+        return scan_fused_fwd(x, delta, A, B, C, D, h_init=h_init, y=y, h_final=h_final,
+                              want_state=want_state, delta_bias=delta_bias,
+                              delta_softplus=delta_softplus, euler_b=euler_b)
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
@@ -196,14 +219,20 @@ def scan_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, want_state
     return y, h_final
 
 
-def scan_varlen_fwd(x, delta, A, B, C, D, cu_seqlens, h_init=None, y=None, h_final=None, want_state=True):
+def scan_varlen_fwd(x, delta, A, B, C, D, cu_seqlens, h_init=None, y=None, h_final=None, want_state=True,
+                    delta_bias=None, delta_softplus=False, euler_b=False):
     """Packed variable-length scan: sequences concatenated along time.
 
     x, delta: [L, Dm]; B, C: [L, N] (same dtype); A: [Dm, N] fp32; D: [Dm] fp32;
     cu_seqlens: [nseq+1] int64 device tensor of sequence start offsets
     (cu_seqlens[0] = 0, cu_seqlens[-1] = L); h_init: optional [nseq, Dm, N] fp32.
+    Options as in scan_fwd.
     Returns (y [L, Dm], h_final [nseq, Dm, N] fp32 or None).
     """
+    if delta_bias is not None or delta_softplus or euler_b:
+        return scan_fused_fwd(x, delta, A, B, C, D, cu_seqlens=cu_seqlens, h_init=h_init, y=y,
+                              h_final=h_final, want_state=want_state, delta_bias=delta_bias,
+                              delta_softplus=delta_softplus, euler_b=euler_b)
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
@@ -236,12 +265,89 @@ def scan_varlen_fwd(x, delta, A, B, C, D, cu_seqlens, h_init=None, y=None, h_fin
     return y, h_final
 
 
-def step(x, delta, A, B, C, D, h, y=None):
+def scan_fused_fwd(x, delta, A, B, C, D, cu_seqlens=None, h_init=None, y=None, h_final=None,
+                   want_state=True, delta_bias=None, delta_softplus=False, euler_b=False):
+    """ssm_scan_fused_fwd: the scan with every option.
+
+    cu_seqlens None: dense batch, shapes as in scan_fwd.  Otherwise packed
+    sequences, shapes as in scan_varlen_fwd.  Returns (y, h_final).
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    if cu_seqlens is None:
+        Bsz, L, Dm = x.shape
+        nseq, rows, sdim = 0, (Bsz, L), Bsz
+    else:
+        L, Dm = x.shape
+        Bsz = 1
+        nseq = cu_seqlens.shape[0] - 1
+        rows, sdim = (L,), nseq
+        _need(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int64, dev)
+    _need(x, "x", (*rows, Dm), dt, dev)
+    _need(delta, "delta", (*rows, Dm), dt, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(B, "B", (*rows, N), dt, dev)
+    _need(C, "C", (*rows, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    _bias(delta_bias, Dm, dev)
+    if h_init is not None:
+        _need(h_init, "h_init", (sdim, Dm, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((*rows, Dm), dtype=dt, device=dev)
+    _need(y, "y", (*rows, Dm), dt, dev)
+    if h_final is None and want_state:
+        h_final = torch.empty((sdim, Dm, N), dtype=torch.float32, device=dev)
+    if h_final is not None:
+        _need(h_final, "h_final", (sdim, Dm, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_fused_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(cu_seqlens), nseq, _ptr(h_init), _ptr(y), _ptr(h_final),
+                                      Bsz, L, Dm, N, code, _flags(delta_softplus, euler_b), _stream(dev))
+    _check(rc, "ssm_scan_fused_fwd")
+    return y, h_final
+
+
+def step_fused(x, delta, A, B, C, D, h, y=None, delta_bias=None, delta_softplus=False, euler_b=False):
+    """ssm_step_fused: one decode step with the scan's options; h is updated in place."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, Dm = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (Bsz, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, Dm), dt, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(B, "B", (Bsz, N), dt, dev)
+    _need(C, "C", (Bsz, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    _need(h, "h", (Bsz, Dm, N), torch.float32, dev)
+    _bias(delta_bias, Dm, dev)
+    if y is None:
+        y = torch.empty((Bsz, Dm), dtype=dt, device=dev)
+    _need(y, "y", (Bsz, Dm), dt, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_step_fused(_ptr(x), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                  _ptr(h), _ptr(y), Bsz, Dm, N, code, _flags(delta_softplus, euler_b),
+                                  _stream(dev))
+    _check(rc, "ssm_step_fused")
+    return y
+
+
+def step(x, delta, A, B, C, D, h, y=None, delta_bias=None, delta_softplus=False, euler_b=False):
     """One decode step: h [Bsz, Dm, N] fp32 is updated in place; returns y [Bsz, Dm].
 
     x, delta: [Bsz, Dm]; B, C: [Bsz, N] (same dtype: bf16, or fp32);
-    A: [Dm, N] fp32; D: [Dm] fp32.
+    A: [Dm, N] fp32; D: [Dm] fp32.  Options as in scan_fwd.
     """
+    if delta_bias is not None or delta_softplus or euler_b:
+        return step_fused(x, delta, A, B, C, D, h, y=y, delta_bias=delta_bias,
+                          delta_softplus=delta_softplus, euler_b=euler_b)
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("libssmscan runs on the GPU: x must be a device tensor")

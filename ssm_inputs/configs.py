@@ -22,7 +22,9 @@ class ScanConfig:
     dtype: str              # storage dtype of x, delta, B, C, y: "fp32" | "bf16"
     a_kind: str             # "s4d_real": A[d,n] = -(n+1);  "lognormal": A = -exp(N(0, 0.5))
     delta_kind: str         # "per_token": softplus(0.5*N(0,1) + inv_softplus(u_d));
-                            # "per_channel": softplus(inv_softplus(u_d)) = u_d for every t
+                            # "per_channel": softplus(inv_softplus(u_d)) = u_d for every t;
+                            # "raw_softplus": delta stores 0.5*N(0,1) and delta_bias[d] =
+                            #   inv_softplus(u_d); the scan applies softplus(delta + bias)
     bc_scale: float         # B, C ~ N(0,1) * bc_scale
     seed: int
 
@@ -62,6 +64,12 @@ MAMBA130M_LAYER = ScanConfig("mamba130m_layer_b8_l2048_d1536_n16", 8, 2048, 1536
 # A Mamba-2.8B-shaped layer: the headline throughput workload.
 MAMBA2P8B_LAYER = ScanConfig("mamba2p8b_layer_b4_l16384_d5120_n16", 4, 16384, 5120, 16,
                              "bf16", "s4d_real", "per_token", 0.25, seed=2)
+
+# The same layer with delta's activation fused into the scan: delta holds the
+# projection output and delta_bias the projection bias; the draw order makes
+# softplus(delta + delta_bias) the layer's delta before storage rounding.
+FUSED_2P8B_LAYER = ScanConfig("fused_softplus_b4_l16384_d5120_n16", 4, 16384, 5120, 16,
+                              "bf16", "s4d_real", "raw_softplus", 0.25, seed=2)
 
 # Long context: one sequence of 2^20 tokens, slow-decay channels.
 LONG_CONTEXT_1M = ScanConfig("long_context_b1_l1048576_d1024_n16", 1, 1 << 20, 1024, 16,
@@ -110,7 +118,7 @@ PACKED_2P8B_LAYER = PackedConfig("packed_prefill_l65536_d5120_n16", 65536, 5120,
                                  p_empty=0.05, h0_std=0.5, seed=5)
 
 SCAN_CONFIGS = {c.name: c for c in (TINY_FP32, MAMBA130M_LAYER, MAMBA2P8B_LAYER,
-                                    LONG_CONTEXT_1M)}
+                                    FUSED_2P8B_LAYER, LONG_CONTEXT_1M)}
 STEP_CONFIGS = {DECODE_256x8192.name: DECODE_256x8192}
 
 

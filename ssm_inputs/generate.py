@@ -63,9 +63,16 @@ def scan_inputs(cfg: ScanConfig, device="cpu", seed=None) -> Dict[str, torch.Ten
     Bsz, L, Dm, N = cfg.Bsz, cfg.L, cfg.Dm, cfg.N
 
     x = _normal((Bsz, L, Dm), g, device).to(sd)
-    noise = _normal((Bsz, L, Dm), g, device, 0.5) if cfg.delta_kind == "per_token" else None
+    noise = _normal((Bsz, L, Dm), g, device, 0.5) if cfg.delta_kind in ("per_token", "raw_softplus") else None
     u = torch.rand((Dm,), generator=g, device=device, dtype=torch.float32) * (U_HI - U_LO) + U_LO
-    if noise is not None:
+    delta_bias = None
+    if cfg.delta_kind == "raw_softplus":
+        # the projection output before the activation, and the projection's
+        # bias: softplus(delta + delta_bias) has the per_token distribution
+        delta = noise.to(sd)
+        delta_bias = inv_softplus(u)
+        del noise
+    elif noise is not None:
         delta = softplus(noise.add_(inv_softplus(u))).to(sd)
         del noise
     elif cfg.delta_kind == "per_channel":
@@ -81,7 +88,10 @@ def scan_inputs(cfg: ScanConfig, device="cpu", seed=None) -> Dict[str, torch.Ten
         A = -torch.exp(_normal((Dm, N), g, device, 0.5))
     else:
         raise ValueError(cfg.a_kind)
-    return {"x": x, "delta": delta, "A": A, "B": B, "C": C, "D": D}
+    out = {"x": x, "delta": delta, "A": A, "B": B, "C": C, "D": D}
+    if delta_bias is not None:
+        out["delta_bias"] = delta_bias
+    return out
 
 
 def step_state(cfg: StepConfig, device="cpu", seed=None) -> Dict[str, torch.Tensor]:

@@ -119,6 +119,32 @@ def test_varlen_argument_errors(L):
     assert L.ssm_last_error() == b""
 
 
+def fused(L, *, x=P[0], dl=P[1], bias=None, A=P[2], B=P[3], C=P[4], D=P[5], cu=None, nseq=0, hi=None, y=P[6],
+          hf=P[7], Bsz=2, Ls=8, Dm=64, N=16, dtype=1, flags=1):
+    v = ctypes.c_void_p
+    return L.ssm_scan_fused_fwd(v(x), v(dl), v(bias), v(A), v(B), v(C), v(D), v(cu), nseq, v(hi), v(y), v(hf),
+                                Bsz, Ls, Dm, N, dtype, flags, None)
+
+
+def test_fused_argument_errors(L):
+    assert fused(L, flags=4) == 9 and fused(L, flags=0x80000000) == 9
+    assert b"flag" in L.ssm_last_error()
+    assert fused(L, bias=P[8] + 2) == 5        # fp32 bias needs 4-byte alignment
+    assert fused(L, y=P[8], bias=P[8]) == 6    # y overlaps delta_bias
+    assert fused(L, hf=P[8] + 64, bias=P[8]) == 6
+    assert fused(L, cu=P[9], nseq=3, Bsz=2) == 2   # packed sequences need Bsz = 1
+    assert fused(L, cu=P[9], nseq=-1, Bsz=1) == 2
+    assert fused(L, cu=P[9], nseq=3, Bsz=1, hi=P[7]) == 6  # packed: no in-place state
+    assert fused(L, Bsz=0, x=0, dl=0, B=0, C=0, y=0, hf=0, flags=3) == 0
+    v = ctypes.c_void_p
+    step_f = lambda **k: L.ssm_step_fused(v(P[0]), v(P[1]), v(k.get("bias")), v(P[2]), v(P[3]), v(P[4]),
+                                          v(P[5]), v(k.get("h", P[6])), v(P[7]), 2, 64, 16, 1,
+                                          k.get("flags", 1), None)
+    assert step_f(flags=8) == 9
+    assert step_f(bias=P[8] + 1) == 5
+    assert step_f(bias=P[6]) == 6              # h overlaps delta_bias
+
+
 def test_step_argument_errors(L):
     assert step(L, dtype=2) == 3
     assert step(L, N=5) == 4
