@@ -42,19 +42,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha(name):
-    with open(os.path.join(KERNEL_SRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# Sources each measured kernel is built from: a counter figure is reported
+# only while all of them are unchanged.
+KERNEL_SOURCES = {
+    "scan": ("scan_kernels.h", "ssm_device.h", "ssm_launch.h"),
+    "step": ("step_kernel.hip", "ssm_device.h", "ssm_launch.h"),
+}
 
 
-def traffic_for(kernel, src_file):
+def source_sha(kind):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(KERNEL_SRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, kind):
     """HBM bytes per launch measured with counters, if the kernel is unchanged."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f).get(kernel)
-    if not rec or rec.get("source_sha") != source_sha(src_file):
+    if not rec or rec.get("source_sha") != source_sha(kind):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -193,7 +204,7 @@ def bench_packed(torch, ss, generate, cfg, steps, warmup):
         "roofline": {"kernel": "scan_segment_kernel (output pass, packed)", "bound": "alu",
                      "achieved": round(achieved, 3), "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
                      "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
-                     "traffic": traffic_for("scan_output_" + cfg.name, "scan_kernels.h"),
+                     "traffic": traffic_for("scan_output_" + cfg.name, "scan"),
                      "avg_ms": round(out_ms, 5)},
         "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
     }
@@ -211,7 +222,7 @@ def scan_record(cfg, ms, kern, S, seg, generate):
         "peak": round(VALU_FP32_PEAK_TFLOPS, 2),
         "unit": "TFLOP/s",
         "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
-        "traffic": traffic_for("scan_output_" + cfg.name, "scan_kernels.h"),
+        "traffic": traffic_for("scan_output_" + cfg.name, "scan"),
         "avg_ms": round(out_ms, 5),
         "algorithmic_flops_per_launch": elems * SCAN_FLOPS_PER_ELEM,
         "hbm_frac_at_algorithmic_bytes": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -288,7 +299,7 @@ def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
         "roofline": {"kernel": "step_kernel", "bound": "hbm",
                      "achieved": round(alg / (k_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_for("step_" + cfg.name, "step_kernel.hip"),
+                     "traffic": traffic_for("step_" + cfg.name, "step"),
                      "avg_ms": round(k_ms, 5)},
         "state_layers_cycled": layers,
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
