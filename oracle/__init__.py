@@ -6,6 +6,7 @@ no fallback to it.  See ``ssm_oracle.c`` for the passages it follows.
 
 Every function here has a pin in ``tests/test_oracle_pins.py`` (closed forms,
 the matrix-exponential ZOH identity, the LTI convolution mode, limits and
-invariants); no function is "parity unpinned".
+invariants; for the backward, finite differences of the forward and exact
+adjoint dot-product identities); no function is "parity unpinned".
 """
-from .oracle import Oracle, scan, step, max_threads, load  # noqa: F401
+from .oracle import Oracle, scan, scan_bwd, step, max_threads, load  # noqa: F401

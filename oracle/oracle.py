@@ -33,7 +33,9 @@ def _ptr(a):
 class Oracle:
     """One loaded copy of the oracle library."""
 
-    def __init__(self, lib_path: str = DEFAULT_LIB):
+    def __init__(self, lib_path: str = DEFAULT_LIB, threads: int = 0):
+        """threads: default thread count of every call (0: OpenMP's default)."""
+        self.threads = int(threads)
         if lib_path == DEFAULT_LIB and not os.path.exists(lib_path):
             from . import build as _build
             _build.build()
@@ -42,6 +44,8 @@ class Oracle:
         lib.ssm_oracle_scan.restype = ctypes.c_int
         lib.ssm_oracle_step.argtypes = [_dp] * 9 + [_i64] * 3 + [ctypes.c_int]
         lib.ssm_oracle_step.restype = ctypes.c_int
+        lib.ssm_oracle_scan_bwd.argtypes = [_dp] * 18 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int]
+        lib.ssm_oracle_scan_bwd.restype = ctypes.c_int
         lib.ssm_oracle_max_threads.argtypes = []
         lib.ssm_oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -72,10 +76,44 @@ class Oracle:
         hf = np.empty((Bsz, Dm, N), dtype=np.float64)
         rc = self.lib.ssm_oracle_scan(_ptr(x), _ptr(delta), _ptr(bias), _ptr(A), _ptr(B), _ptr(C),
                                       _ptr(D), _ptr(h0), _ptr(y), _ptr(hf),
-                                      Bsz, L, Dm, N, _flags(delta_softplus, euler_b), int(threads))
+                                      Bsz, L, Dm, N, _flags(delta_softplus, euler_b), int(threads or self.threads))
         if rc != 0:
             raise RuntimeError(f"ssm_oracle_scan failed with code {rc}")
         return y, hf
+
+    def scan_bwd(self, x, delta, A, B, C, D, dy, h0=None, dh_final=None, delta_bias=None,
+                 delta_softplus: bool = False, euler_b: bool = False, want_dBC: bool = True,
+                 threads: int = 0):
+        """Gradients of the scan for output gradients dy [Bsz,L,Dm] (and dh_final
+        [Bsz,Dm,N] if given).  Returns a dict with dx, ddelta (for the delta
+        input as passed, i.e. the raw value when delta_softplus), dA, dD, dh0,
+        dbias (if delta_bias is given) and dB, dC (if want_dBC)."""
+        x = np.asarray(x)
+        Bsz, L, Dm = x.shape
+        N = np.asarray(A).shape[1]
+        x = _f64(x, (Bsz, L, Dm), "x")
+        delta = _f64(delta, (Bsz, L, Dm), "delta")
+        A = _f64(A, (Dm, N), "A")
+        B = _f64(B, (Bsz, L, N), "B")
+        C = _f64(C, (Bsz, L, N), "C")
+        D = _f64(D, (Dm,), "D")
+        dy = _f64(dy, (Bsz, L, Dm), "dy")
+        h0 = None if h0 is None else _f64(h0, (Bsz, Dm, N), "h0")
+        dhf = None if dh_final is None else _f64(dh_final, (Bsz, Dm, N), "dh_final")
+        bias = None if delta_bias is None else _f64(delta_bias, (Dm,), "delta_bias")
+        out = {"dx": np.empty((Bsz, L, Dm)), "ddelta": np.empty((Bsz, L, Dm)), "dA": np.empty((Dm, N)),
+               "dD": np.empty(Dm), "dh0": np.empty((Bsz, Dm, N))}
+        out["dbias"] = np.empty(Dm) if bias is not None else None
+        out["dB"] = np.empty((Bsz, L, N)) if want_dBC else None
+        out["dC"] = np.empty((Bsz, L, N)) if want_dBC else None
+        rc = self.lib.ssm_oracle_scan_bwd(
+            _ptr(x), _ptr(delta), _ptr(bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy), _ptr(dhf),
+            _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dbias"]), _ptr(out["dA"]), _ptr(out["dB"]),
+            _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]), Bsz, L, Dm, N,
+            _flags(delta_softplus, euler_b), int(threads or self.threads))
+        if rc != 0:
+            raise RuntimeError(f"ssm_oracle_scan_bwd failed with code {rc}")
+        return out
 
     def step(self, x, delta, A, B, C, D, h, delta_bias=None, delta_softplus: bool = False,
              euler_b: bool = False):
@@ -121,3 +159,7 @@ def scan(x, delta, A, B, C, D, h0=None, threads: int = 0, **opts):
 
 def step(x, delta, A, B, C, D, h, **opts):
     return load().step(x, delta, A, B, C, D, h, **opts)
+
+
+def scan_bwd(x, delta, A, B, C, D, dy, **opts):
+    return load().scan_bwd(x, delta, A, B, C, D, dy, **opts)

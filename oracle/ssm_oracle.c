@@ -172,6 +172,181 @@ int ssm_oracle_step(const double *x, const double *delta, const double *bias,
     return 0;
 }
 
+/* ------------------------------------------------------------------------
+ * Backward (reverse-mode derivative) of the scan.
+ *
+ * With lambda_t = dL/dh_t (all of h_t's later uses), the recurrence
+ * h_t = Abar_t h_{t-1} + k_t B_t x_t  (k_t = delta phi(delta A), or delta for
+ * the Euler term) and y_t = sum_n C_t h_t + D x_t give, going back in time:
+ *   lambda_t  = C_t dy_t + Abar_{t+1} lambda_{t+1}  (lambda_{L-1} includes dL/dh_final)
+ *   dx_t      = D dy_t + sum_n lambda_t k_t B_t
+ *   dB_t[n]   = sum_d lambda_t k_t x_t           dC_t[n] = sum_d dy_t h_t
+ *   ddelta_t  = sum_n lambda_t (A Abar_t h_{t-1} + dk/ddelta B_t x_t)
+ *   dA[d][n]  = sum_{b,t} lambda_t (delta Abar_t h_{t-1} + dk/dA B_t x_t)
+ *   dD[d]     = sum_{b,t} dy_t x_t               dh0 = Abar_0 lambda_0
+ * with dk/ddelta = Abar (ZOH) or 1 (Euler) and dk/dA = delta^2 phi'(delta A)
+ * (ZOH) or 0 (Euler).  With the softplus flag, ddelta is taken back through
+ * softplus to the raw input (times sigmoid(raw + bias)); dbias[d] sums it.
+ * This is the chain rule applied to the recurrence the forward follows; it is
+ * pinned against finite differences of the forward oracle.
+ * ---------------------------------------------------------------------- */
+
+/* phi'(z) = (z e^z - e^z + 1) / z^2: a power series near 0 (where the
+ * closed form cancels), the closed form elsewhere.  phi'(0) = 1/2. */
+static double zoh_dphi(double z)
+{
+    if (fabs(z) < 1.0) {
+        /* sum_{m>=1} m z^(m-1) / (m+1)! */
+        double term = 0.5, sum = 0.0; /* m = 1: 1 / 2! */
+        for (int m = 1; m < 40; ++m) {
+            sum += term;
+            term *= z * (double)(m + 1) / ((double)m * (double)(m + 2));
+        }
+        return sum;
+    }
+    return (z * exp(z) - expm1(z)) / (z * z);
+}
+
+static double sigmoid(double v)
+{
+    return v >= 0.0 ? 1.0 / (1.0 + exp(-v)) : exp(v) / (1.0 + exp(v));
+}
+
+int ssm_oracle_scan_bwd(const double *x, const double *delta, const double *bias,
+                        const double *A, const double *B, const double *C,
+                        const double *D, const double *h0, const double *dy,
+                        const double *dh_final, double *dx, double *ddelta,
+                        double *dbias, double *dA, double *dB, double *dC,
+                        double *dD, double *dh0, int64_t Bsz, int64_t L,
+                        int64_t Dm, int64_t N, int flags, int nthreads)
+{
+    if (Bsz < 0 || L < 0 || Dm < 0 || N <= 0)
+        return 1;
+    const int euler = (flags & ORACLE_EULER_B) != 0;
+    const int soft = (flags & ORACLE_DELTA_SOFTPLUS) != 0;
+    const int64_t BLN = Bsz * L * N;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    const int nth = omp_get_max_threads();
+#else
+    (void)nthreads;
+    const int nth = 1;
+#endif
+    /* dB, dC sum over channels: one private copy per thread, added in thread
+     * order at the end (static schedule, so the result is reproducible). */
+    double *priv = NULL;
+    if (dB || dC) {
+        priv = (double *)calloc((size_t)nth * 2 * (size_t)BLN + 1, sizeof(double));
+        if (!priv)
+            return 2;
+    }
+    int err = 0;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+        const int tid = omp_get_thread_num();
+#else
+        const int tid = 0;
+#endif
+        double *hs = (double *)malloc((size_t)(L + 1) * (size_t)N * sizeof(double));
+        double *lam = (double *)malloc((size_t)N * sizeof(double));
+        double *myB = priv ? priv + (size_t)tid * 2 * (size_t)BLN : NULL;
+        double *myC = priv ? myB + BLN : NULL;
+        if (!hs || !lam) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t d = 0; d < Dm; ++d) {
+                const double *a = A + d * N;
+                const double bias_d = bias ? bias[d] : 0.0;
+                double dA_d[64];
+                double *dAd = N <= 64 ? dA_d : (double *)calloc((size_t)N, sizeof(double));
+                for (int64_t n = 0; n < N; ++n)
+                    dAd[n] = 0.0;
+                double dD_d = 0.0, dbias_d = 0.0;
+                for (int64_t b = 0; b < Bsz; ++b) {
+                    /* forward, keeping every state: hs[t+1] = h_t, hs[0] = h0 */
+                    for (int64_t n = 0; n < N; ++n)
+                        hs[n] = h0 ? h0[(b * Dm + d) * N + n] : 0.0;
+                    for (int64_t t = 0; t < L; ++t) {
+                        const int64_t i = (b * L + t) * Dm + d;
+                        const int64_t r = (b * L + t) * N;
+                        const double dt = step_size(delta[i], bias_d, flags);
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double z = dt * a[n];
+                            const double k = euler ? dt : dt * zoh_phi(z);
+                            hs[(t + 1) * N + n] = exp(z) * hs[t * N + n] + k * B[r + n] * x[i];
+                        }
+                    }
+                    /* backward */
+                    for (int64_t n = 0; n < N; ++n)
+                        lam[n] = dh_final ? dh_final[(b * Dm + d) * N + n] : 0.0;
+                    for (int64_t t = L - 1; t >= 0; --t) {
+                        const int64_t i = (b * L + t) * Dm + d;
+                        const int64_t r = (b * L + t) * N;
+                        const double dt = step_size(delta[i], bias_d, flags);
+                        const double g = dy[i];
+                        double gx = D[d] * g, gdt = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            lam[n] += C[r + n] * g;
+                            const double z = dt * a[n];
+                            const double abar = exp(z);
+                            const double k = euler ? dt : dt * zoh_phi(z);
+                            const double dk_ddt = euler ? 1.0 : abar;
+                            const double dk_da = euler ? 0.0 : dt * dt * zoh_dphi(z);
+                            const double u = B[r + n] * x[i];
+                            const double hprev = hs[t * N + n];
+                            gx += lam[n] * k * B[r + n];
+                            gdt += lam[n] * (a[n] * abar * hprev + dk_ddt * u);
+                            dAd[n] += lam[n] * (dt * abar * hprev + dk_da * u);
+                            if (myB)
+                                myB[r + n] += lam[n] * k * x[i];
+                            if (myC)
+                                myC[r + n] += g * hs[(t + 1) * N + n];
+                            lam[n] *= abar;
+                        }
+                        dD_d += g * x[i];
+                        dx[i] = gx;
+                        if (soft)
+                            gdt *= sigmoid(delta[i] + bias_d);
+                        ddelta[i] = gdt;
+                        dbias_d += gdt;
+                    }
+                    if (dh0)
+                        for (int64_t n = 0; n < N; ++n)
+                            dh0[(b * Dm + d) * N + n] = lam[n];
+                }
+                for (int64_t n = 0; n < N; ++n)
+                    dA[d * N + n] = dAd[n];
+                dD[d] = dD_d;
+                if (dbias)
+                    dbias[d] = dbias_d;
+                if (dAd != dA_d)
+                    free(dAd);
+            }
+        }
+        free(hs);
+        free(lam);
+    }
+    if (priv) {
+        for (int64_t j = 0; j < BLN; ++j) {
+            double sb = 0.0, sc = 0.0;
+            for (int th = 0; th < nth; ++th) {
+                sb += priv[(size_t)th * 2 * (size_t)BLN + (size_t)j];
+                sc += priv[(size_t)th * 2 * (size_t)BLN + (size_t)BLN + (size_t)j];
+            }
+            if (dB)
+                dB[j] = sb;
+            if (dC)
+                dC[j] = sc;
+        }
+        free(priv);
+    }
+    return err;
+}
+
 int ssm_oracle_max_threads(void)
 {
 #ifdef _OPENMP

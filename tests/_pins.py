@@ -418,6 +418,89 @@ def check_options_step_chain_matches_scan(orc, seed=10):
     assert rel_err(h, hf) < 1e-13
 
 
+# ---------------------------------------------------------------------------
+# backward: finite differences of the forward oracle, adjoint identities
+
+
+def _bwd_case(rng, opts, Bsz=2, L=7, Dm=3, N=4):
+    x, delta, A, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    A[0, 1] = 0.0      # exact A = 0 (limit of the ZOH input term and of its derivative)
+    A[1, 2] = -1e-7    # tiny A
+    h0 = rng.standard_normal((Bsz, Dm, N))
+    dy = rng.standard_normal((Bsz, L, Dm))
+    dhf = rng.standard_normal((Bsz, Dm, N))
+    bias = None
+    if opts.get("delta_softplus"):
+        delta = rng.normal(-2.0, 1.0, delta.shape)   # raw projection output
+        bias = rng.normal(0.0, 0.5, Dm)
+    return dict(x=x, delta=delta, A=A, B=B, C=C, D=D, h0=h0), dy, dhf, bias
+
+
+def _loss(orc, p, dy, dhf, bias, opts):
+    y, hf = orc.scan(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], h0=p["h0"], delta_bias=bias, **opts)
+    return float(np.sum(dy * y) + np.sum(dhf * hf))
+
+
+def check_bwd_finite_differences(orc, seed=12):
+    """Every gradient against central differences of L = <dy, y> + <dhf, h_final>
+    computed with the forward oracle, for ZOH, softplus(delta + bias), and the
+    Euler input term."""
+    for k, opts in enumerate(({}, {"delta_softplus": True}, {"delta_softplus": True, "euler_b": True},
+                              {"euler_b": True})):
+        rng = np.random.default_rng(seed + k)
+        p, dy, dhf, bias = _bwd_case(rng, opts)
+        g = orc.scan_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], dy, h0=p["h0"], dh_final=dhf,
+                         delta_bias=bias, **opts)
+        names = {"x": "dx", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "h0": "dh0"}
+        params = dict(p)
+        if bias is not None:
+            params["bias"] = bias
+            names["bias"] = "dbias"
+        scale = max(1.0, max(float(np.max(np.abs(g[v]))) for v in names.values()))
+        for name, gname in names.items():
+            arr = params[name]
+            got = g[gname]
+            for idx in np.ndindex(arr.shape):
+                old = arr[idx]
+                eps = 1e-6 * max(1.0, abs(old))
+                arr[idx] = old + eps
+                lp = _loss(orc, p, dy, dhf, params.get("bias"), opts)
+                arr[idx] = old - eps
+                lm = _loss(orc, p, dy, dhf, params.get("bias"), opts)
+                arr[idx] = old
+                fd = (lp - lm) / (2 * eps)
+                assert abs(fd - got[idx]) <= 2e-7 * scale + 1e-6 * abs(fd), (opts, name, idx, fd, got[idx])
+
+
+def check_bwd_adjoint_identities(orc, seed=16):
+    """Exact identities (no differencing): with delta, A fixed the outputs are
+    linear in (x, h0), in B when h0 = 0, and y - D x is linear in C, so
+    <dy, y(v)> + <dhf, h_final(v)> = <gradient, v> for each of them."""
+    rng = np.random.default_rng(seed)
+    for opts in ({}, {"euler_b": True}):
+        p, dy, dhf, _ = _bwd_case(rng, opts, Bsz=2, L=11, Dm=4, N=5)
+        x, delta, A, B, C, D, h0 = (p[k] for k in ("x", "delta", "A", "B", "C", "D", "h0"))
+        g = orc.scan_bwd(x, delta, A, B, C, D, dy, h0=h0, dh_final=dhf, **opts)
+        y, hf = orc.scan(x, delta, A, B, C, D, h0=h0, **opts)
+        lhs = np.sum(dy * y) + np.sum(dhf * hf)
+        rhs = np.sum(g["dx"] * x) + np.sum(g["dh0"] * h0)
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), (opts, lhs, rhs)
+        # B: with h0 = 0 the outputs are linear in B
+        g0 = orc.scan_bwd(x, delta, A, B, C, D, dy, dh_final=dhf, **opts)
+        y0, hf0 = orc.scan(x, delta, A, B, C, D, **opts)
+        lhs = np.sum(dy * (y0 - D * x)) + np.sum(dhf * hf0)
+        assert abs(lhs - np.sum(g0["dB"] * B)) <= 1e-12 * max(1.0, abs(lhs))
+        # C: y - D x is linear in C (h_final does not depend on C)
+        lhs = np.sum(dy * (y - D * x))
+        assert abs(lhs - np.sum(g["dC"] * C)) <= 1e-12 * max(1.0, abs(lhs))
+        # D: dD = sum over (b, t) of dy x
+        assert np.allclose(g["dD"], np.sum(dy * x, axis=(0, 1)), rtol=1e-13, atol=1e-13)
+        # dC from states computed by the forward on prefixes
+        for t in (0, 5, 10):
+            _, ht = orc.scan(x[:, :t + 1], delta[:, :t + 1], A, B[:, :t + 1], C[:, :t + 1], D, h0=h0, **opts)
+            assert np.allclose(g["dC"][:, t], np.einsum("bd,bdn->bn", dy[:, t], ht), rtol=1e-12, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_golden,
     check_brute_force,
@@ -435,4 +518,6 @@ ALL_CHECKS = [
     check_fused_delta_matches_precomputed,
     check_euler_b_closed_forms,
     check_options_step_chain_matches_scan,
+    check_bwd_finite_differences,
+    check_bwd_adjoint_identities,
 ]

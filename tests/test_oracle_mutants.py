@@ -17,14 +17,17 @@ MUTANTS = [
     ("y_uses_old_state",
      "h[n] = abar * h[n] + bbar * xt;\n        y += c[n] * h[n];",
      "y += c[n] * h[n];\n        h[n] = abar * h[n] + bbar * xt;"),
-    ("wrong_sign_in_exp", "const double abar = exp(z);", "const double abar = exp(-z);"),
+    ("wrong_sign_in_exp", "const double abar = exp(z);\n        double bbar;",
+     "const double abar = exp(-z);\n        double bbar;"),
     ("bbar_missing_delta", "bbar = dt * zoh_phi(z) * b[n];", "bbar = zoh_phi(z) * b[n];"),
     ("euler_instead_of_zoh", "bbar = dt * zoh_phi(z) * b[n];", "bbar = dt * b[n];"),
     ("phi_missing_division", "return expm1(z) / z;", "return expm1(z);"),
     ("B_and_C_swapped", "B + r,\n                                        C + r,",
      "C + r,\n                                        B + r,"),
-    ("B_C_ignore_batch", "const int64_t r = (b * L + t) * N;", "const int64_t r = t * N;"),
-    ("delta_from_channel_0", "step_size(delta[i], bias_d", "step_size(delta[(b * L + t) * Dm], bias_d"),
+    ("B_C_ignore_batch", "const int64_t r = (b * L + t) * N;\n                    const double dt = step_size(delta[i], bias_d, flags);\n                    y[i]",
+     "const int64_t r = t * N;\n                    const double dt = step_size(delta[i], bias_d, flags);\n                    y[i]"),
+    ("delta_from_channel_0", "step_size(delta[i], bias_d, flags);\n                    y[i]",
+     "step_size(delta[(b * L + t) * Dm], bias_d, flags);\n                    y[i]"),
     ("A_row_of_channel_0_in_scan", "dt, A + d * N, B + r", "dt, A, B + r"),
     ("D_of_channel_0", "C + r, D[d], N, euler);", "C + r, D[0], N, euler);"),
     ("initial_state_ignored", "h[n] = h0 ? h0[(b * Dm + d) * N + n] : 0.0;", "h[n] = 0.0;"),
@@ -39,16 +42,40 @@ MUTANTS = [
     ("softplus_positive_branch_drops_v", "return v + log1p(exp(-v));", "return log1p(exp(-v));"),
     ("softplus_naive_tail", "return log1p(exp(v));\n}", "return log(1.0 + exp(v));\n}"),
     ("softplus_naive_overflow", "    if (v > 0.0)\n        return v + log1p(exp(-v));\n", ""),
-    ("scan_bias_of_channel_0", "const double bias_d = bias ? bias[d] : 0.0;",
-     "const double bias_d = bias ? bias[0] : 0.0;"),
+    ("scan_bias_of_channel_0", "const double bias_d = bias ? bias[d] : 0.0;\n                for (int64_t n = 0; n < N; ++n)\n                    h[n]",
+     "const double bias_d = bias ? bias[0] : 0.0;\n                for (int64_t n = 0; n < N; ++n)\n                    h[n]"),
     ("step_bias_of_channel_0", "bias ? bias[d] : 0.0, flags);", "bias ? bias[0] : 0.0, flags);"),
     ("euler_uses_zoh", "            bbar = dt * b[n];\n", "            bbar = dt * zoh_phi(z) * b[n];\n"),
     ("euler_drops_delta", "            bbar = dt * b[n];\n", "            bbar = b[n];\n"),
-    ("euler_forward_abar", "const double abar = exp(z);", "const double abar = euler ? 1.0 + z : exp(z);"),
+    ("euler_forward_abar", "const double abar = exp(z);\n        double bbar;",
+     "const double abar = euler ? 1.0 + z : exp(z);\n        double bbar;"),
     ("euler_ignored_in_step", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    for (int64_t b",
      "const int euler = 0;\n    for (int64_t b"),
     ("euler_ignored_in_scan", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    const int64_t nchan",
      "const int euler = 0;\n    const int64_t nchan"),
+    # backward
+    ("bwd_dx_drops_D", "double gx = D[d] * g, gdt = 0.0;", "double gx = 0.0, gdt = 0.0;"),
+    ("bwd_lambda_uses_C_of_state_0", "lam[n] += C[r + n] * g;", "lam[n] += C[r] * g;"),
+    ("bwd_zoh_dk_ddelta_missing_abar", "const double dk_ddt = euler ? 1.0 : abar;",
+     "const double dk_ddt = euler ? 1.0 : 1.0;"),
+    ("bwd_euler_dk_ddelta_is_abar", "const double dk_ddt = euler ? 1.0 : abar;",
+     "const double dk_ddt = euler ? abar : abar;"),
+    ("bwd_dk_dA_constant", "dt * dt * zoh_dphi(z);", "dt * dt * 0.5;"),
+    ("bwd_dphi_series_wrong", "term *= z * (double)(m + 1) / ((double)m * (double)(m + 2));",
+     "term *= z / (double)(m + 2);"),
+    ("bwd_uses_h_t_for_h_prev", "const double hprev = hs[t * N + n];", "const double hprev = hs[(t + 1) * N + n];"),
+    ("bwd_dC_uses_h_prev", "myC[r + n] += g * hs[(t + 1) * N + n];", "myC[r + n] += g * hs[t * N + n];"),
+    ("bwd_lambda_not_decayed", "                            lam[n] *= abar;\n", ""),
+    ("bwd_softplus_chain_missing", "                            gdt *= sigmoid(delta[i] + bias_d);\n",
+     "                            gdt *= 1.0;\n"),
+    ("bwd_sigmoid_without_bias", "gdt *= sigmoid(delta[i] + bias_d);", "gdt *= sigmoid(delta[i]);"),
+    ("bwd_dB_missing_x", "myB[r + n] += lam[n] * k * x[i];", "myB[r + n] += lam[n] * k;"),
+    ("bwd_dA_missing_abar", "dAd[n] += lam[n] * (dt * abar * hprev", "dAd[n] += lam[n] * (dt * hprev"),
+    ("bwd_ddelta_missing_A", "gdt += lam[n] * (a[n] * abar * hprev", "gdt += lam[n] * (abar * hprev"),
+    ("bwd_dh_final_ignored", "lam[n] = dh_final ? dh_final[(b * Dm + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
+    ("bwd_dbias_overwritten", "dbias_d += gdt;", "dbias_d = gdt;"),
+    ("bwd_forward_ignores_euler", "const double k = euler ? dt : dt * zoh_phi(z);\n                            hs[",
+     "const double k = dt * zoh_phi(z);\n                            hs["),
     ("h_final_not_last_state",
      "h_final[(b * Dm + d) * N + n] = h[n];",
      "h_final[(b * Dm + d) * N + n] = h[n] * 0.5 + 0.5 * h[n] * (n == 0 ? 1.0 : 0.999);"),
@@ -69,11 +96,11 @@ def _build_mutant(tmp_path, name, old, new):
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_planted_mistake(tmp_path, name, old, new):
     import oracle
-    mut = oracle.Oracle(_build_mutant(tmp_path, name, old, new))
-    failed = []
+    # one thread: the checks make many tiny calls, and test workers run side by side
+    mut = oracle.Oracle(_build_mutant(tmp_path, name, old, new), threads=1)
     for check in _pins.ALL_CHECKS:
         try:
             check(mut)
         except AssertionError:
-            failed.append(getattr(check, "__name__", "check"))
-    assert failed, f"no pin caught the planted mistake '{name}'"
+            return  # caught
+    pytest.fail(f"no pin caught the planted mistake '{name}'")
