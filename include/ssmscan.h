@@ -177,6 +177,40 @@ int ssm_scan_fused_fwd(const void *x, const void *delta, const float *delta_bias
                        unsigned flags, void *stream);
 
 /*
+ * Backward of the scan: every input gradient for given output gradients.
+ * The chain rule on the recurrence ("Mamba SSM Nedir?", section "Ayrik Zamana
+ * Gecis"), as training needs it (section "Paralel Tarama Algoritmasi": the
+ * same parallel scan serves training).  With lambda_t = dL/dh_t,
+ *   lambda_t = C_t dy_t + Abar_{t+1} lambda_{t+1}   (lambda_{L-1} adds dh_final)
+ * and every gradient is a sum over t of lambda_t, the states h_{t-1} and the
+ * inputs.
+ *
+ * Inputs: the forward's x, delta, delta_bias, A, B, C, D, h_init (shapes,
+ *   dtype and flags exactly as in ssm_scan_fused_fwd with cu_seqlens NULL;
+ *   delta_bias and h_init may be NULL) and
+ *   dy       : [Bsz][L][Dm] dtype   dL/dy
+ *   dh_final : [Bsz][Dm][N] fp32 or NULL (zero)   dL/dh_final
+ * Outputs (overwritten, never accumulated):
+ *   dx, ddelta  : [Bsz][L][Dm] dtype  (ddelta is for the delta argument as
+ *                 passed: the raw value when SSM_DELTA_SOFTPLUS is set)
+ *   ddelta_bias : [Dm] fp32 or NULL
+ *   dA          : [Dm][N] fp32       dD : [Dm] fp32
+ *   dB, dC      : [Bsz][L][N] fp32   (sums over channels)
+ *   dh_init     : [Bsz][Dm][N] fp32 or NULL
+ * No output may overlap an input or another output.  The forward states are
+ * recomputed (nothing is saved from the forward call).  Library scratch:
+ * about 4 state-sized arrays per 64 steps (for fp32 storage: per 32 steps),
+ * plus dB/dC partial sums.
+ */
+int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias,
+                 const float *A, const void *B, const void *C, const float *D,
+                 const float *h_init, const void *dy, const float *dh_final,
+                 void *dx, void *ddelta, float *ddelta_bias, float *dA,
+                 float *dB, float *dC, float *dD, float *dh_init,
+                 int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
+                 unsigned flags, void *stream);
+
+/*
  * One recurrent decode step on a resident state, updated in place
  * ("Mamba SSM Nedir?", section "Karmasiklik Karsilastirmasi": inference
  * updates a fixed-size state per token).  bf16 I/O:
@@ -255,8 +289,12 @@ typedef enum {
     SSM_K_SCAN_CARRY = 2,       /* states entering each segment */
     SSM_K_SCAN_OUTPUT = 3,      /* y (and h_final) from the entering states */
     SSM_K_STEP = 4,             /* decode step */
-    SSM_K_STATE_INIT = 5,       /* h_final of an empty sequence */
-    SSM_K_COUNT = 6
+    SSM_K_STATE_INIT = 5,       /* h_final of an empty sequence; zero fills */
+    SSM_K_BWD_AGGREGATE = 6,    /* backward: per-segment adjoint summaries */
+    SSM_K_BWD_CARRY = 7,        /* backward: adjoint entering each segment */
+    SSM_K_BWD_MAIN = 8,         /* backward: gradients per segment */
+    SSM_K_BWD_REDUCE = 9,       /* backward: dB, dC, dA, dD sums */
+    SSM_K_COUNT = 10
 } ssm_kernel_kind;
 
 int ssm_profile_read(double *total_ms, int64_t *launches, int n);

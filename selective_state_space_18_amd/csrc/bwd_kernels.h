@@ -1,0 +1,685 @@
+// Backward of the selective scan for gfx950: templates shared by the per-dtype
+// translation units (bwd_bf16.hip, bwd_f32.hip).
+//
+// Reverse-mode derivative of the recurrence the forward computes ("Mamba SSM
+// Nedir?" page, section "Ayrik Zamana Gecis"; training runs the same scan,
+// section "Paralel Tarama Algoritmasi").  With lambda_t = dL/dh_t:
+//   lambda_t = C_t dy_t + Abar_{t+1} lambda_{t+1}            (a reverse scan)
+//   dx_t     = D dy_t + sum_n lambda_t k_t B_t[n]            k_t = (Abar-1)/A or delta
+//   ddelta_t = sum_n lambda_t (A Abar h_{t-1} + dk/ddelta B_t x_t)
+//   dA_n     = sum_t lambda_t (delta Abar h_{t-1} + dk/dA B_t x_t)
+//   dB_t[n]  = sum_d lambda_t k_t x_t,  dC_t[n] = sum_d dy_t h_t,  dD = sum dy x
+//
+// Work layout (one lane per channel, as in the forward):
+//   1. forward aggregate + carry (the forward kernels) give the scaled state
+//      entering every segment;
+//   2. bwd_aggregate_kernel: each segment but the first runs the adjoint back
+//      from zero and stores what reaches its start, with its delta sum;
+//      bwd_carry_kernel joins them from the right (the same affine-map
+//      composition as the forward carry, in reverse);
+//   3. bwd_main_kernel: each wave takes one 64-channel tile over a group of
+//      segments.  Per segment it stores the state every kK steps in LDS, then
+//      walks back in sub-chunks of kC steps: recompute the sub-chunk's states
+//      into registers from the nearest checkpoint, then run the adjoint back
+//      over them and form every gradient.  dB and dC sum over channels: a
+//      reduce-scatter across the wave's lanes, an LDS sum over the block's
+//      waves, and block partials summed by bwd_reduce_bc_kernel.
+//
+// Units: the state is the forward's scaled g_n = (n+1) h_n and the adjoint is
+// mu_n = dL/dg_n = lambda_n / (n+1).  The B/C rows are the forward's
+// ({B or (n+1)B for Euler, C/(n+1)}).
+#pragma once
+
+#include "scan_kernels.h"
+
+namespace ssm {
+
+namespace {
+
+template <typename Acc>
+struct BwdShape;
+template <>
+struct BwdShape<float> {
+    static constexpr int kC = 8;   // sub-chunk kept in registers
+    static constexpr int kK = 16;  // checkpoint interval
+    static constexpr int kT = 64;  // segment length
+};
+template <>
+struct BwdShape<double> {
+    static constexpr int kC = 4;
+    static constexpr int kK = 16;
+    static constexpr int kT = 32;
+};
+
+// 1 - sigmoid-free form: d softplus(v)/dv = sigmoid(v) = 1 - exp(-softplus(v)).
+__device__ __forceinline__ float softplus_grad_from_value(float sp) {
+    float e;
+    return -expm1_and_exp(-sp, e);
+}
+__device__ __forceinline__ double softplus_grad_from_value(double sp) { return -expm1(-sp); }
+
+// phi'(z) = (z e^z - (e^z - 1)) / z^2 with E = e^z - 1; a Taylor polynomial
+// for |z| < 1/8 (truncation below z^5/840, relative 1e-7), where the closed
+// form cancels.
+template <typename Acc>
+__device__ __forceinline__ Acc zoh_dphi(Acc z, Acc E) {
+    const Acc poly =
+        fma_(z, fma_(z, fma_(z, fma_(z, (Acc)(1.0 / 144.0), (Acc)(1.0 / 30.0)), (Acc)(1.0 / 8.0)), (Acc)(1.0 / 3.0)),
+             (Acc)0.5);
+    const Acc closed = fma_(z, (Acc)1 + E, -E) / (z * z);
+    return abs_(z) < (Acc)0.125 ? poly : closed;
+}
+
+// ---------------------------------------------------------------------------
+// Reverse aggregate: segments 1..S-1, adjoint from zero at the segment end.
+
+template <typename T, int N, bool kStruct, bool kEuler, bool kPre>
+__global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
+    typedef typename AccOf<T>::type Acc;
+    const ScanParams &p = q.f;
+    const int blocks_per_seg = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int s = lb / blocks_per_seg + 1;
+    const int wave = uniform((int)threadIdx.x / kWave);
+    const int tile = (lb - (s - 1) * blocks_per_seg) * p.waves_per_block + wave;
+    if (wave >= p.waves_per_block || tile >= p.n_tiles) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t b = tile / p.tiles_per_b;
+    const int64_t d0 = (int64_t)(tile - b * p.tiles_per_b) * kWave;
+    const bool active = d0 + lane < p.Dm;
+    const int64_t d = active ? d0 + lane : d0;
+    const int64_t ch = b * p.Dm + d;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t t0 = (int64_t)s * p.seg_len;
+    const int nsteps = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
+
+    float Ar[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Ar[n] = p.A[d * N + n];
+    bool st = (Ar[0] != 0.f) && (p.force_general == 0);
+#pragma unroll
+    for (int n = 1; n < N; ++n) st = st && (Ar[n] == (float)(n + 1) * Ar[0]);
+    if ((bool)__all(st) != kStruct) return;
+    const ChanConst<N, kStruct, kEuler, Acc> cc(Ar);
+    const Acc bias = (kPre && p.delta_bias != nullptr) ? (Acc)p.delta_bias[d] : (Acc)0;
+    const bool soft = p.delta_softplus != 0;
+
+    const int64_t off = (b * p.L + t0) * p.Dm + d0;
+    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rdl = make_rsrc(static_cast<const T *>(p.delta) + off, nsteps * row);
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const T *>(q.dy) + off, nsteps * row);
+    const int32_t voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
+    const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
+
+    Acc nu[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) nu[n] = 0;
+    Acc lam = 0;
+    constexpr int G = kPrefetch;
+    T dl_c[G], dy_c[G], dl_n[G], dy_n[G];
+    auto load = [&](int tb, T(&dl)[G], T(&dyv)[G]) {
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int t = tb - k;
+            const int so = (t > 0 ? t : 0) * row;
+            dl[k] = buf_load<T>(rdl, voff, so);
+            dyv[k] = buf_load<T>(rdy, voff, so);
+        }
+    };
+    load(nsteps - 1, dl_c, dy_c);
+    for (int tb = nsteps - 1; tb >= 0; tb -= G) {
+        load(tb - G, dl_n, dy_n);
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int t = tb - k;
+            if (t >= 0) {
+                Acc crow[N];
+#pragma unroll
+                for (int n = 0; n < N; ++n) crow[n] = bcp[(int64_t)t * (2 * N) + N + n];
+                Acc dv = (Acc)to_f32(dl_c[k]);
+                if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
+                const Acc g = (Acc)to_f32(dy_c[k]);
+                lam += dv;
+                if constexpr (kStruct) {
+                    Acc r;
+                    const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
+                    Acc E = E1;
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        const Acc mu = fma_(crow[n], g, nu[n]);
+                        nu[n] = fma_(E, mu, mu);
+                        if (n + 1 < N) {
+                            if constexpr (sizeof(Acc) == 8)
+                                E = fma_(E, E1, E + E1);
+                            else
+                                E = fma_(E, r, E1);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        Acc e;
+                        const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
+                        const Acc mu = fma_(crow[n], g, nu[n]);
+                        nu[n] = fma_(E, mu, mu);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            dl_c[k] = dl_n[k];
+            dy_c[k] = dy_n[k];
+        }
+    }
+    if (!active) return;
+    Acc *a = static_cast<Acc *>(q.ragg) + (int64_t)s * (N + 1) * BD + ch;
+#pragma unroll
+    for (int n = 0; n < N; ++n) a[(int64_t)n * BD] = nu[n];
+    a[(int64_t)N * BD] = lam;
+}
+
+// Reverse carry: one thread per (state n, channel).  The adjoint entering the
+// last segment from the right is dL/dh_final (scaled units); segment s-1
+// receives exp(A_n * sum(delta over s)) times what enters s, plus s's summary.
+template <typename Acc, int N>
+__global__ __launch_bounds__(kBlock) void bwd_carry_kernel(BwdParams q) {
+    const ScanParams &p = q.f;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= BD * N) return;
+    const int n = (int)(i / BD);
+    const int64_t ch = i - (int64_t)n * BD;
+    const int64_t d = ch % p.Dm;
+    constexpr Acc unit = sizeof(Acc) == 4 ? (Acc)kLog2e : (Acc)1;
+    const Acc a = (Acc)p.A[d * N + n] * unit;
+    Acc nu = q.dh_final ? (Acc)q.dh_final[ch * N + n] / (Acc)(n + 1) : (Acc)0;
+    const Acc *__restrict__ ragg = static_cast<const Acc *>(q.ragg);
+    Acc *__restrict__ out = static_cast<Acc *>(q.gout) + (int64_t)n * BD + ch;
+    const int64_t sa = (int64_t)(N + 1) * BD, sg = (int64_t)N * BD;
+    out[(int64_t)(p.S - 1) * sg] = nu;
+    constexpr int kBatch = 16;
+    for (int s1 = p.S - 1; s1 >= 1; s1 -= kBatch) {
+        Acc lc[kBatch], gc[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int s = s1 - k >= 1 ? s1 - k : 1;
+            lc[k] = ragg[(int64_t)s * sa + (int64_t)N * BD + ch];
+            gc[k] = ragg[(int64_t)s * sa + (int64_t)n * BD + ch];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) lc[k] = exp_units(a * lc[k]);
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int s = s1 - k;
+            if (s >= 1) {
+                nu = fma_(lc[k], nu, gc[k]);
+                out[(int64_t)(s - 1) * sg] = nu;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Main backward pass.
+
+// Reduce-scatter of v[0..N) over the 64 lanes: afterwards lane l holds in
+// v[0] the wave sum of element idx(l); every lane with (l & (64/N - 1)) == 0
+// holds a distinct one.  Returns idx(l).
+template <int N, typename Acc>
+__device__ __forceinline__ int wave_reduce_scatter(Acc (&v)[N], int lane) {
+    int idx = 0;
+    int k = N;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        if (k > 1) {
+            const int half = k / 2;
+            const bool hi = (lane & m) != 0;
+#pragma unroll
+            for (int j = 0; j < N / 2; ++j) {
+                if (j < half) {
+                    const Acc keep = hi ? v[half + j] : v[j];
+                    const Acc send = hi ? v[j] : v[half + j];
+                    v[j] = keep + __shfl_xor(send, m);
+                }
+            }
+            idx = idx * 2 + (hi ? 1 : 0);
+            k = half;
+        } else {
+            v[0] += __shfl_xor(v[0], m);
+        }
+    }
+    return idx;
+}
+
+template <typename T, int N, bool kStruct, bool kEuler, bool kPre>
+__global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
+    typedef typename AccOf<T>::type Acc;
+    constexpr int kC = BwdShape<Acc>::kC;
+    constexpr int kK = BwdShape<Acc>::kK;
+    constexpr int kNck = BwdShape<Acc>::kT / kK;
+    constexpr int kWaves = kBlock / kWave;
+    __shared__ Acc ck[kWaves][kNck][N][kWave];  // state checkpoints, per wave
+    __shared__ Acc bacc[kWaves][kC][2][N];      // per-wave dB, dC sums of one sub-chunk
+    const ScanParams &p = q.f;
+
+    const int wave = uniform((int)threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_grp = (int)p.Bsz * q.blocks_per_row;
+    const int grp = lb / per_grp;
+    const int rem = lb - grp * per_grp;
+    const int64_t b = rem / q.blocks_per_row;
+    const int br = rem - (int)b * q.blocks_per_row;
+    const int tir = br * kWaves + wave;
+    const bool tile_ok = tir < p.tiles_per_b;
+    const int64_t d0 = (int64_t)(tile_ok ? tir : p.tiles_per_b - 1) * kWave;
+    const bool in_range = d0 + lane < p.Dm;
+    const int64_t d = in_range ? d0 + lane : d0;  // idle lanes shadow a valid channel
+    const int64_t ch = b * p.Dm + d;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t BLN = p.Bsz * p.L * N;
+
+    float Ar[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Ar[n] = p.A[d * N + n];
+    bool st = (Ar[0] != 0.f) && (p.force_general == 0);
+#pragma unroll
+    for (int n = 1; n < N; ++n) st = st && (Ar[n] == (float)(n + 1) * Ar[0]);
+    // Waves of the other A class (or past the row) compute on a shadow
+    // channel and write nothing; they still take part in every barrier.
+    const bool wave_on = tile_ok && ((bool)__all(st) == kStruct);
+    const bool live = wave_on && in_range;
+    const ChanConst<N, kStruct, kEuler, Acc> cc(Ar);
+    const Acc a0n = (Acc)Ar[0];
+    const Acc inva = kStruct ? (Acc)1 / (Acc)Ar[0] : (Acc)0;
+    const Acc Dd = (Acc)p.D[d];
+    DeltaPre<Acc> dp;
+    dp.bias = (kPre && p.delta_bias != nullptr) ? (Acc)p.delta_bias[d] : (Acc)0;
+    dp.softplus = p.delta_softplus != 0;
+    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
+    const int32_t voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
+
+    // state from step t_from over `count` steps (the forward's aggregate loop)
+    auto advance = [&](Acc(&g)[N], int64_t t_from, int count) {
+        if (count <= 0) return;
+        if constexpr (kStruct && !kEuler) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) g[n] *= a0n;
+        }
+        const_row_ptr<Acc> bcp;
+        const SegIO<T> io = seg_io<T, Acc, N, false>(p, b, t_from, count, d0, d, bcp);
+        Acc lam_unused = 0;
+        run_segment<T, N, kStruct, false, kEuler, kPre>(io, bcp, count, Ar, Dd, dp, g, lam_unused);
+        if constexpr (kStruct && !kEuler) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) g[n] *= inva;
+        }
+    };
+
+    Acc dA1[N], dA2[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) dA1[n] = dA2[n] = 0;
+    Acc dDacc = 0, dbacc = 0;
+    const int path = kStruct ? 0 : 1;
+
+    for (int si = 0; si < q.seg_per_group; ++si) {
+        const int s = grp * q.seg_per_group + si;
+        if (s >= p.S) break;
+        const int64_t t0 = (int64_t)s * p.seg_len;
+        const int nseg = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
+        const int nck = (nseg + kK - 1) / kK;
+
+        // checkpoints: the state before steps t0, t0 + kK, ...
+        Acc g[N];
+        if (s == 0) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) g[n] = p.h_init ? (Acc)p.h_init[ch * N + n] * (Acc)(n + 1) : (Acc)0;
+        } else {
+            const Acc *gin = static_cast<const Acc *>(p.gin);
+#pragma unroll
+            for (int n = 0; n < N; ++n) g[n] = gin[((int64_t)s * N + n) * BD + ch];
+        }
+        for (int j = 0; j < nck; ++j) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) ck[wave][j][n][lane] = g[n];
+            if (j + 1 < nck) advance(g, t0 + (int64_t)j * kK, kK);
+        }
+        __builtin_amdgcn_wave_barrier();
+
+        Acc nu[N];
+        {
+            const Acc *gout = static_cast<const Acc *>(q.gout);
+#pragma unroll
+            for (int n = 0; n < N; ++n) nu[n] = gout[((int64_t)s * N + n) * BD + ch];
+        }
+
+        for (int j = nck - 1; j >= 0; --j) {
+            const int64_t tb = t0 + (int64_t)j * kK;
+            const int nb = (int)((t0 + nseg) - tb) < kK ? (int)((t0 + nseg) - tb) : kK;
+            const int nsub = (nb + kC - 1) / kC;
+            for (int qq = nsub - 1; qq >= 0; --qq) {
+                const int64_t ta = tb + (int64_t)qq * kC;
+                const int nc = uniform(nb - qq * kC < kC ? nb - qq * kC : kC);
+                // state entering the sub-chunk
+                Acc gp[N];
+#pragma unroll
+                for (int n = 0; n < N; ++n) gp[n] = ck[wave][j][n][lane];
+                advance(gp, tb, qq * kC);
+
+                // inputs of the sub-chunk, then its states
+                const int64_t off = (b * p.L + ta) * p.Dm + d0;
+                const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const T *>(p.x) + off, nc * row);
+                const __amdgpu_buffer_rsrc_t rdl = make_rsrc(static_cast<const T *>(p.delta) + off, nc * row);
+                const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const T *>(q.dy) + off, nc * row);
+                const __amdgpu_buffer_rsrc_t rdx = make_rsrc(static_cast<const T *>(q.dx) + off, nc * row);
+                const __amdgpu_buffer_rsrc_t rdd = make_rsrc(static_cast<const T *>(q.ddelta) + off, nc * row);
+                const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + ta) * (2 * N));
+                Acc xs[kC], ds[kC], gys[kC];
+#pragma unroll
+                for (int i = 0; i < kC; ++i) {
+                    const int so = (i < nc ? i : nc - 1) * row;
+                    xs[i] = (Acc)to_f32(buf_load<T>(rx, voff, so));
+                    ds[i] = (Acc)to_f32(buf_load<T>(rdl, voff, so));
+                    gys[i] = (Acc)to_f32(buf_load<T>(rdy, voff, so));
+                }
+                if constexpr (kPre) {
+#pragma unroll
+                    for (int i = 0; i < kC; ++i) ds[i] = dp.softplus ? softplus_(ds[i] + dp.bias) : ds[i] + dp.bias;
+                }
+                Acc gs[kC][N];
+                {
+                    Acc gc[N];
+#pragma unroll
+                    for (int n = 0; n < N; ++n) gc[n] = gp[n];
+#pragma unroll
+                    for (int i = 0; i < kC; ++i) {
+                        if (i < nc) {
+                            Acc rw[2 * N];
+                            load_row<N>(rw, bcp + (int64_t)i * (2 * N));
+                            (void)scan_step<N, kStruct, true, kEuler>(cc, rw, xs[i], ds[i], gc);
+                        }
+#pragma unroll
+                        for (int n = 0; n < N; ++n) gs[i][n] = gc[n];
+                    }
+                }
+
+                // back over the sub-chunk
+#pragma unroll
+                for (int i = kC - 1; i >= 0; --i) {
+                    if (i < nc) {
+                        Acc rw[2 * N];
+                        load_row<N>(rw, bcp + (int64_t)i * (2 * N));
+                        const Acc xv = xs[i], dv = ds[i], gy = gys[i];
+                        Acc vB[N], vC[N];
+                        Acc acc_x = 0, acc_d = 0;
+                        if constexpr (kStruct) {
+                            Acc r;
+                            const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
+                            Acc E = E1;
+                            const Acc xi = xv * inva, dxv = dv * xv;
+#pragma unroll
+                            for (int n = 0; n < N; ++n) {
+                                const Acc gprev = i > 0 ? gs[i > 0 ? i - 1 : 0][n] : gp[n];
+                                const Acc mu = fma_(rw[N + n], gy, nu[n]);
+                                const Acc pp = E * mu;
+                                const Acc nup = mu + pp;
+                                vC[n] = gy * gs[i][n];
+                                if constexpr (!kEuler) {
+                                    acc_x = fma_(pp, rw[n], acc_x);
+                                    vB[n] = pp * xi;
+                                    const Acc w = fma_(a0n, gprev, rw[n] * xv);
+                                    const Acc qv = nup * w;
+                                    acc_d = fma_(qv, (Acc)(n + 1), acc_d);
+                                    dA1[n] = fma_(dv, qv, dA1[n]);
+                                    dA2[n] = fma_(vB[n], rw[n], dA2[n]);
+                                } else {
+                                    acc_x = fma_(mu, rw[n], acc_x);
+                                    vB[n] = mu * dxv;
+                                    const Acc ng = nup * gprev;
+                                    acc_d = fma_(ng, (Acc)(n + 1), acc_d);
+                                    dA1[n] = fma_(dv, ng, dA1[n]);
+                                }
+                                nu[n] = nup;
+                                if (n + 1 < N) {
+                                    if constexpr (sizeof(Acc) == 8)
+                                        E = fma_(E, E1, E + E1);
+                                    else
+                                        E = fma_(E, r, E1);
+                                }
+                            }
+                        } else {
+                            const Acc dxv = dv * xv;
+#pragma unroll
+                            for (int n = 0; n < N; ++n) {
+                                const Acc gprev = i > 0 ? gs[i > 0 ? i - 1 : 0][n] : gp[n];
+                                Acc e;
+                                const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
+                                const Acc mu = fma_(rw[N + n], gy, nu[n]);
+                                const Acc pp = E * mu;
+                                const Acc nup = mu + pp;
+                                vC[n] = gy * gs[i][n];
+                                if constexpr (!kEuler) {
+                                    const Acc pw = pp * cc.W[n];
+                                    acc_x = fma_(pw, rw[n], acc_x);
+                                    vB[n] = pw * xv;
+                                    const Acc bx = rw[n] * xv;
+                                    const Acc w = fma_(bx, (Acc)(n + 1), (Acc)Ar[n] * gprev);
+                                    acc_d = fma_(nup, w, acc_d);
+                                    const Acc z = dv * (Acc)Ar[n];
+                                    dA1[n] = fma_(dv, nup * gprev, dA1[n]);
+                                    dA2[n] = fma_(dv * dv * zoh_dphi(z, E), mu * bx, dA2[n]);
+                                } else {
+                                    acc_x = fma_(mu, rw[n], acc_x);
+                                    vB[n] = mu * dxv;
+                                    const Acc ng = nup * gprev;
+                                    acc_d = fma_((Acc)Ar[n], ng, acc_d);
+                                    dA1[n] = fma_(dv, ng, dA1[n]);
+                                }
+                                nu[n] = nup;
+                            }
+                        }
+                        Acc gx, gdl;
+                        if constexpr (!kEuler) {
+                            gx = fma_(Dd, gy, kStruct ? inva * acc_x : acc_x);
+                            gdl = acc_d;
+                        } else {
+                            gx = fma_(Dd, gy, dv * acc_x);
+                            gdl = fma_(xv, acc_x, kStruct ? a0n * acc_d : acc_d);
+                        }
+                        if constexpr (kPre) {
+                            if (dp.softplus) gdl *= softplus_grad_from_value(dv);
+                        }
+                        dDacc = fma_(gy, xv, dDacc);
+                        dbacc += gdl;
+                        if (wave_on) {
+                            buf_store(from_acc<T>(gx), rdx, voff, i * row);
+                            buf_store(from_acc<T>(gdl), rdd, voff, i * row);
+                        }
+                        // dB, dC: sum over the wave's channels, then over the block's waves
+#pragma unroll
+                        for (int n = 0; n < N; ++n) {
+                            vB[n] = live ? vB[n] : (Acc)0;
+                            vC[n] = live ? vC[n] : (Acc)0;
+                        }
+                        const int idx = wave_reduce_scatter<N>(vB, lane);
+                        (void)wave_reduce_scatter<N>(vC, lane);
+                        // every wave fills its slot (zeros when it is not on)
+                        if ((lane & (kWave / N - 1)) == 0) {
+                            bacc[wave][i][0][idx] = vB[0];
+                            bacc[wave][i][1][idx] = vC[0];
+                        }
+                    }
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    // the block's sum, in wave order (deterministic)
+                    Acc *dst = static_cast<Acc *>(q.part_bc) +
+                               ((int64_t)(path * q.blocks_per_row + br) * 2) * BLN + (b * p.L + ta) * N;
+                    for (int e = lane; e < kC * 2 * N; e += kWave) {
+                        const int i = e / (2 * N);
+                        const int v = (e / N) & 1;
+                        const int n = e % N;
+                        Acc sum = 0;
+#pragma unroll
+                        for (int w = 0; w < kWaves; ++w) sum += bacc[w][i][v][n];
+                        if (i < nc) dst[(int64_t)v * BLN + (int64_t)i * N + n] = sum;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if (s == 0 && live && q.dh_init != nullptr) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) q.dh_init[ch * N + n] = (float)(nu[n] * (Acc)(n + 1));
+        }
+    }
+
+    if (!live) return;
+    Acc *pa = static_cast<Acc *>(q.part_a) + ((int64_t)grp * BD + ch) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        Acc v;
+        if constexpr (kEuler)
+            v = dA1[n];
+        else if constexpr (kStruct)
+            v = ((Acc)(n + 1) * dA1[n] - dA2[n]) / ((Acc)(n + 1) * a0n);
+        else
+            v = dA1[n] + (Acc)(n + 1) * dA2[n];
+        pa[n] = v;
+    }
+    Acc *pd = static_cast<Acc *>(q.part_d) + ((int64_t)grp * BD + ch) * 2;
+    pd[0] = dDacc;
+    pd[1] = dbacc;
+}
+
+// dB, dC: sum of the block partials of both A paths, scaled to true units
+// (dC carries the scaled state: 1/(n+1); the Euler dB lane value lacks n+1).
+template <typename Acc, int N>
+__global__ __launch_bounds__(kBlock) void bwd_reduce_bc_kernel(BwdParams q) {
+    const ScanParams &p = q.f;
+    const int64_t BLN = p.Bsz * p.L * N;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= BLN) return;
+    const int n = (int)(i % N);
+    const Acc *src = static_cast<const Acc *>(q.part_bc);
+    const int parts = 2 * q.blocks_per_row;
+    Acc sb = 0, sc = 0;
+    for (int k = 0; k < parts; ++k) {
+        sb += src[((int64_t)k * 2) * BLN + i];
+        sc += src[((int64_t)k * 2 + 1) * BLN + i];
+    }
+    q.dB[i] = (float)(p.euler_b ? sb * (Acc)(n + 1) : sb);
+    q.dC[i] = (float)(sc / (Acc)(n + 1));
+}
+
+// dA, dD, d(delta_bias): sums over batch rows and segment groups.
+template <typename Acc, int N>
+__global__ __launch_bounds__(kBlock) void bwd_reduce_ad_kernel(BwdParams q) {
+    const ScanParams &p = q.f;
+    const int64_t DN = p.Dm * N;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= DN + 2 * p.Dm) return;
+    const int64_t BD = p.Bsz * p.Dm;
+    if (i < DN) {
+        const int64_t d = i / N;
+        const int n = (int)(i % N);
+        const Acc *src = static_cast<const Acc *>(q.part_a);
+        Acc sacc = 0;
+        for (int g = 0; g < q.n_groups; ++g)
+            for (int64_t b = 0; b < p.Bsz; ++b) sacc += src[((int64_t)g * BD + b * p.Dm + d) * N + n];
+        q.dA[i] = (float)sacc;
+        return;
+    }
+    const int64_t j = i - DN;
+    const int64_t d = j % p.Dm;
+    const int which = (int)(j / p.Dm);  // 0: dD, 1: d(delta_bias)
+    float *dst = which == 0 ? q.dD : q.ddelta_bias;
+    if (dst == nullptr) return;
+    const Acc *src = static_cast<const Acc *>(q.part_d);
+    Acc sacc = 0;
+    for (int g = 0; g < q.n_groups; ++g)
+        for (int64_t b = 0; b < p.Bsz; ++b) sacc += src[((int64_t)g * BD + b * p.Dm + d) * 2 + which];
+    dst[d] = (float)sacc;
+}
+
+template <typename T, int N, bool kStruct, bool kEuler, bool kPre>
+void bwd_launch_variant(BwdPass pass, const BwdParams &q, hipStream_t s) {
+    const ScanParams &p = q.f;
+    if (pass == BwdPass::kAggregate) {
+        const int bps = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
+        if (p.S <= 1 || bps == 0) return;
+        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, kStruct, kEuler, kPre>), dim3((unsigned)bps * (p.S - 1)),
+                           dim3(kBlock), 0, s, q);
+    } else {
+        const unsigned grid = (unsigned)(q.n_groups * p.Bsz * q.blocks_per_row);
+        if (grid == 0) return;
+        hipLaunchKernelGGL((bwd_main_kernel<T, N, kStruct, kEuler, kPre>), dim3(grid), dim3(kBlock), 0, s, q);
+    }
+}
+
+template <typename T, int N, bool kStruct>
+void bwd_launch_path(BwdPass pass, const BwdParams &q, hipStream_t s) {
+    const ScanParams &p = q.f;
+    const bool pre = p.delta_bias != nullptr || p.delta_softplus != 0;
+    if (p.euler_b) {
+        if (pre)
+            bwd_launch_variant<T, N, kStruct, true, true>(pass, q, s);
+        else
+            bwd_launch_variant<T, N, kStruct, true, false>(pass, q, s);
+    } else {
+        if (pre)
+            bwd_launch_variant<T, N, kStruct, false, true>(pass, q, s);
+        else
+            bwd_launch_variant<T, N, kStruct, false, false>(pass, q, s);
+    }
+}
+
+template <typename T, int N>
+hipError_t bwd_pass_n(BwdPass pass, const BwdParams &q, hipStream_t s) {
+    typedef typename AccOf<T>::type Acc;
+    const ScanParams &p = q.f;
+    switch (pass) {
+        case BwdPass::kAggregate:
+        case BwdPass::kMain:
+            // both A paths; each wave works in exactly one of them
+            bwd_launch_path<T, N, true>(pass, q, s);
+            bwd_launch_path<T, N, false>(pass, q, s);
+            break;
+        case BwdPass::kCarry: {
+            const int64_t work = p.Bsz * p.Dm * N;
+            if (work == 0) return hipSuccess;
+            hipLaunchKernelGGL((bwd_carry_kernel<Acc, N>), dim3((unsigned)((work + kBlock - 1) / kBlock)),
+                               dim3(kBlock), 0, s, q);
+            break;
+        }
+        case BwdPass::kReduce: {
+            const int64_t bln = p.Bsz * p.L * N;
+            if (bln > 0)
+                hipLaunchKernelGGL((bwd_reduce_bc_kernel<Acc, N>), dim3((unsigned)((bln + kBlock - 1) / kBlock)),
+                                   dim3(kBlock), 0, s, q);
+            const int64_t ad = p.Dm * N + 2 * p.Dm;
+            if (ad > 0)
+                hipLaunchKernelGGL((bwd_reduce_ad_kernel<Acc, N>), dim3((unsigned)((ad + kBlock - 1) / kBlock)),
+                                   dim3(kBlock), 0, s, q);
+            break;
+        }
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t bwd_pass(BwdPass pass, const BwdParams &q, int N, hipStream_t s) {
+    switch (N) {
+        case 1: return bwd_pass_n<T, 1>(pass, q, s);
+        case 2: return bwd_pass_n<T, 2>(pass, q, s);
+        case 4: return bwd_pass_n<T, 4>(pass, q, s);
+        case 8: return bwd_pass_n<T, 8>(pass, q, s);
+        case 16: return bwd_pass_n<T, 16>(pass, q, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+}  // namespace ssm

@@ -35,9 +35,23 @@ __global__ __launch_bounds__(kBlock) void state_init_kernel(const float *__restr
     if (i < count) h_final[i] = h_init ? h_init[i] : 0.f;
 }
 
+__global__ __launch_bounds__(kBlock) void fill_kernel(float *__restrict__ dst, int64_t count, float v) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < count) dst[i] = v;
+}
+
 }  // namespace
 
+hipError_t launch_fill(float *dst, int64_t count, float v, hipStream_t s) {
+    if (count == 0 || dst == nullptr) return hipSuccess;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((count + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, dst, count, v);
+    return hipGetLastError();
+}
+
 size_t scan_acc_bytes(int dtype) { return dtype == 0 ? sizeof(double) : sizeof(float); }
+
+// Must match BwdShape<Acc>::kT in bwd_kernels.h.
+int bwd_segment_len(int dtype) { return dtype == 0 ? 32 : 64; }
 
 hipError_t launch_bc_prep(const ScanParams &p, int N, int dtype, hipStream_t s) {
     return by_dtype(ScanPass::kPrep, p, N, dtype, s);

@@ -53,6 +53,37 @@ struct StepParams {
 // The passes of one scan call, in launch order.
 enum class ScanPass { kPrep, kAggregate, kCarry, kOutput };
 
+// One backward call.  f holds the forward inputs, the segment plan and the
+// forward scratch (bc, agg, gin); the forward aggregate and carry passes run
+// on it unchanged.  Scratch of the backward (Acc = AccOf<T>):
+//   ragg  : [S][N+1][B*D] Acc -- per segment s >= 1: the adjoint a zero
+//           incoming adjoint leaves at the segment start (times Abar there,
+//           scaled-state units) and the sum of delta
+//   gout  : [S][N][B*D] Acc -- adjoint entering segment s from the right
+//           (scaled-state units: dL/dg = dL/dh / (n+1))
+//   part_bc : [2 paths][blocks per row][2 (dB, dC)][B*L*N] Acc -- per block
+//           sums over its channels
+//   part_a  : [groups][B*D][N] Acc -- dA per group of segments (final form)
+//   part_d  : [groups][B*D][2] Acc -- dD and d(delta_bias)
+struct BwdParams {
+    ScanParams f;
+    const void *dy;          // [B,L,D] storage dtype
+    const float *dh_final;   // [B,D,N] or null
+    void *dx, *ddelta;       // [B,L,D] storage dtype
+    float *dA, *dB, *dC, *dD, *ddelta_bias, *dh_init;
+    void *ragg, *gout, *part_bc, *part_a, *part_d;
+    int seg_per_group;       // segments one wave processes in turn
+    int n_groups;            // ceil(S / seg_per_group)
+    int blocks_per_row;      // ceil(tiles_per_b / 4)
+};
+
+enum class BwdPass { kAggregate, kCarry, kMain, kReduce };
+
+// Segment length the backward kernels are built for (the plan must use it).
+int bwd_segment_len(int dtype);
+hipError_t bwd_pass_f32(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
+hipError_t bwd_pass_bf16(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
+
 // Bytes per element of the scan's arithmetic type for a storage dtype.
 size_t scan_acc_bytes(int dtype);
 
@@ -74,6 +105,8 @@ hipError_t launch_state_init(const ScanParams &p, int N, hipStream_t s);
 // h_final of the empty sequences of a packed variable-length call.
 hipError_t launch_varlen_empty(const ScanParams &p, int N, hipStream_t s);
 hipError_t launch_step(const StepParams &p, int N, int dtype, hipStream_t s);
+// dst[0..count) = v.
+hipError_t launch_fill(float *dst, int64_t count, float v, hipStream_t s);
 // Channels per thread of the decode-step kernel (1, 2 or 4).
 void set_step_unroll(int u);
 

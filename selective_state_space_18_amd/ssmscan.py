@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 SSM_F32, SSM_BF16 = 0, 1
 SSM_OPT_SEGMENT_LEN, SSM_OPT_FORCE_GENERAL, SSM_OPT_PROFILE, SSM_OPT_STEP_CHANNELS = 1, 2, 3, 4
 SSM_DELTA_SOFTPLUS, SSM_EULER_B = 1, 2  # ssm_flags
-KERNEL_KINDS = ("bc_prep", "scan_aggregate", "scan_carry", "scan_output", "step", "state_init")
+KERNEL_KINDS = ("bc_prep", "scan_aggregate", "scan_carry", "scan_output", "step", "state_init",
+                "bwd_aggregate", "bwd_carry", "bwd_main", "bwd_reduce")
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_BAD_DTYPE",
           4: "SSM_ERR_UNSUPPORTED_N", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_NOMEM",
           8: "SSM_ERR_HIP", 9: "SSM_ERR_BAD_OPTION"}
@@ -32,7 +33,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_B
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_strerror",
            "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
            "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
-           "ssm_scan_fused_fwd", "ssm_step_fused")
+           "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd")
 
 
 class SSMError(RuntimeError):
@@ -61,6 +62,8 @@ def lib():
     L.ssm_scan_varlen_fwd.restype = ctypes.c_int
     L.ssm_scan_fused_fwd.argtypes = [_vp] * 8 + [_i64] + [_vp] * 3 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_scan_fused_fwd.restype = ctypes.c_int
+    L.ssm_scan_bwd.argtypes = [_vp] * 18 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
+    L.ssm_scan_bwd.restype = ctypes.c_int
     L.ssm_step_fused.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_step_fused.restype = ctypes.c_int
     L.ssm_step.argtypes = [_vp] * 8 + [_i64] * 3 + [_vp]
@@ -309,6 +312,54 @@ def scan_fused_fwd(x, delta, A, B, C, D, cu_seqlens=None, h_init=None, y=None, h
                                       Bsz, L, Dm, N, code, _flags(delta_softplus, euler_b), _stream(dev))
     _check(rc, "ssm_scan_fused_fwd")
     return y, h_final
+
+
+def scan_bwd(x, delta, A, B, C, D, dy, h_init=None, dh_final=None, delta_bias=None, delta_softplus=False,
+             euler_b=False, want_dh_init=True, out=None):
+    """ssm_scan_bwd: gradients of the scan (dense batch).
+
+    Forward inputs as in scan_fwd (with the same options), dy [Bsz, L, Dm] in
+    x's dtype and optional dh_final [Bsz, Dm, N] fp32.  Returns a dict with dx,
+    ddelta (x's dtype), dA [Dm, N], dB, dC [Bsz, L, N], dD [Dm] (fp32),
+    dh_init [Bsz, Dm, N] (if want_dh_init) and ddelta_bias [Dm] (if
+    delta_bias is given).  `out` may supply any of these tensors.
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    for t, name, shape, tdt in ((x, "x", (Bsz, L, Dm), dt), (delta, "delta", (Bsz, L, Dm), dt),
+                                (A, "A", (Dm, N), torch.float32), (B, "B", (Bsz, L, N), dt),
+                                (C, "C", (Bsz, L, N), dt), (D, "D", (Dm,), torch.float32),
+                                (dy, "dy", (Bsz, L, Dm), dt)):
+        _need(t, name, shape, tdt, dev)
+    _bias(delta_bias, Dm, dev)
+    if h_init is not None:
+        _need(h_init, "h_init", (Bsz, Dm, N), torch.float32, dev)
+    if dh_final is not None:
+        _need(dh_final, "dh_final", (Bsz, Dm, N), torch.float32, dev)
+    o = dict(out or {})
+    shapes = {"dx": ((Bsz, L, Dm), dt), "ddelta": ((Bsz, L, Dm), dt), "dA": ((Dm, N), torch.float32),
+              "dB": ((Bsz, L, N), torch.float32), "dC": ((Bsz, L, N), torch.float32), "dD": ((Dm,), torch.float32)}
+    if want_dh_init:
+        shapes["dh_init"] = ((Bsz, Dm, N), torch.float32)
+    if delta_bias is not None:
+        shapes["ddelta_bias"] = ((Dm,), torch.float32)
+    for k, (shape, tdt) in shapes.items():
+        if o.get(k) is None:
+            o[k] = torch.empty(shape, dtype=tdt, device=dev)
+        _need(o[k], k, shape, tdt, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_bwd(_ptr(x), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(h_init), _ptr(dy), _ptr(dh_final), _ptr(o["dx"]), _ptr(o["ddelta"]),
+                                _ptr(o.get("ddelta_bias")), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
+                                _ptr(o["dD"]), _ptr(o.get("dh_init")), Bsz, L, Dm, N, code,
+                                _flags(delta_softplus, euler_b), _stream(dev))
+    _check(rc, "ssm_scan_bwd")
+    return o
 
 
 def step_fused(x, delta, A, B, C, D, h, y=None, delta_bias=None, delta_softplus=False, euler_b=False):

@@ -145,6 +145,32 @@ def test_fused_argument_errors(L):
     assert step_f(bias=P[6]) == 6              # h overlaps delta_bias
 
 
+def test_bwd_argument_errors(L):
+    v = ctypes.c_void_p
+    Q = [0x10000000 * (i + 1) for i in range(20)]  # fake, aligned, far apart
+
+    def bwd(**k):
+        a = dict(x=Q[0], dl=Q[1], bias=None, A=Q[2], B=Q[3], C=Q[4], D=Q[5], hi=None, dy=Q[6], dhf=None,
+                 dx=Q[7], ddl=Q[8], dbias=None, dA=Q[9], dB=Q[10], dC=Q[11], dD=Q[12], dhi=None,
+                 Bsz=2, Ls=8, Dm=64, N=16, dtype=1, flags=0)
+        a.update(k)
+        return L.ssm_scan_bwd(v(a["x"]), v(a["dl"]), v(a["bias"]), v(a["A"]), v(a["B"]), v(a["C"]), v(a["D"]),
+                              v(a["hi"]), v(a["dy"]), v(a["dhf"]), v(a["dx"]), v(a["ddl"]), v(a["dbias"]),
+                              v(a["dA"]), v(a["dB"]), v(a["dC"]), v(a["dD"]), v(a["dhi"]), a["Bsz"], a["Ls"],
+                              a["Dm"], a["N"], a["dtype"], a["flags"], None)
+    assert bwd(dtype=3) == 3 and bwd(N=7) == 4 and bwd(flags=4) == 9 and bwd(Ls=-1) == 2
+    assert bwd(dy=0) == 1 and bwd(dA=0) == 1 and bwd(dB=0) == 1 and bwd(dx=0) == 1
+    assert b"dx is NULL" in L.ssm_last_error()
+    assert bwd(dB=Q[10] + 2) == 5              # fp32 gradients need 4-byte alignment
+    assert bwd(dx=Q[7] + 1) == 5
+    assert bwd(dx=Q[0]) == 6                   # dx overlaps x
+    assert bwd(dC=Q[10]) == 6                  # dC overlaps dB
+    assert bwd(dhi=Q[13], dhf=Q[13]) == 6      # dh_init overlaps dh_final
+    assert bwd(dD=Q[6]) == 6                   # dD overlaps dy
+    assert b"overlaps" in L.ssm_last_error()
+    assert bwd(Bsz=1 << 40, Ls=1 << 40) == 2
+
+
 def test_step_argument_errors(L):
     assert step(L, dtype=2) == 3
     assert step(L, N=5) == 4
