@@ -14,7 +14,7 @@ decode step.
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
                     [--no-cpu-baseline] [--no-secondary]
     python bench.py --only decode      # one workload, for profiler runs
-                                       # (scan, long, small, packed, options, decode)
+                                       # (scan, long, small, packed, options, backward, decode)
     python bench.py --copy-calibration # plain copy of known size (for counters)
 """
 import argparse
@@ -168,6 +168,34 @@ def bench_options(torch, ss, generate, configs, steps):
                       "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
                       "config": dict(cfgd, input_term="Euler: delta * B")}
     return out
+
+
+def bench_backward(torch, ss, generate, cfg, steps, warmup):
+    """Backward of the scan over the layer: every input gradient for a random
+    dy (and dh_final), forward states recomputed inside the call."""
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name} (backward)")
+    inp = generate.scan_inputs(cfg, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 1)
+    dy = torch.randn(inp["x"].shape, generator=g, device=dev).to(inp["x"].dtype)
+    dhf = torch.randn((cfg.Bsz, cfg.Dm, cfg.N), generator=g, device=dev)
+    out = {}
+
+    def fn(_i):
+        nonlocal out
+        out = ss.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], dy, dh_final=dhf,
+                          out=out or None)
+
+    log(f"[bench] timing {cfg.name} backward: {warmup} warmup + {steps} steps")
+    ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    del inp, dy, dhf, out
+    torch.cuda.empty_cache()
+    elems = cfg.elems()
+    main_ms = kern["bwd_main"]["avg_ms"]
+    return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": elems / (ms * 1e-3), "unit": "elems/s",
+            "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
+            "main_kernel_elems_per_s": elems / (main_ms * 1e-3)}
 
 
 def bench_packed(torch, ss, generate, cfg, steps, warmup):
@@ -359,7 +387,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options"], default=None)
+    ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward"],
+                    default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
 
@@ -386,6 +415,10 @@ def main():
 
     if a.only == "decode":
         rec = bench_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "backward":
+        rec = bench_backward(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps, a.warmup)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "options":
@@ -442,6 +475,7 @@ def main():
         sec["fused_softplus"] = bench_options(torch, ss, generate, configs, max(5, a.steps // 5))
         sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER,
                                              max(5, a.steps // 5), 2)
+        sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
                                      configs.DECODE_256x8192.n_tokens)
         out["secondary"] = sec

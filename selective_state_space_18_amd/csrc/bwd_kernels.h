@@ -40,15 +40,15 @@ template <typename Acc>
 struct BwdShape;
 template <>
 struct BwdShape<float> {
-    static constexpr int kC = 8;   // sub-chunk kept in registers
-    static constexpr int kK = 16;  // checkpoint interval
-    static constexpr int kT = 64;  // segment length
+    static constexpr int kC = 4;   // sub-chunk kept in registers
+    static constexpr int kK = 8;   // checkpoint interval
+    static constexpr int kT = 32;  // segment length
 };
 template <>
 struct BwdShape<double> {
     static constexpr int kC = 4;
-    static constexpr int kK = 16;
-    static constexpr int kT = 32;
+    static constexpr int kK = 8;
+    static constexpr int kT = 16;
 };
 
 // 1 - sigmoid-free form: d softplus(v)/dv = sigmoid(v) = 1 - exp(-softplus(v)).
@@ -225,9 +225,98 @@ __global__ __launch_bounds__(kBlock) void bwd_carry_kernel(BwdParams q) {
 
 // Reduce-scatter of v[0..N) over the 64 lanes: afterwards lane l holds in
 // v[0] the wave sum of element idx(l); every lane with (l & (64/N - 1)) == 0
-// holds a distinct one.  Returns idx(l).
-template <int N, typename Acc>
-__device__ __forceinline__ int wave_reduce_scatter(Acc (&v)[N], int lane) {
+// holds a distinct one.  Returns idx(l).  Each stage pairs lanes across one
+// lane bit (5 down to 0); while more than one value is left, a lane keeps half
+// of them (the upper half when its bit is set) summed with its partner's.
+//
+// fp32: lane bits 5 and 4 use permlane32/permlane16 swaps, which exchange the
+// upper/lower halves (rows) of two registers so that adding the two results
+// leaves each half with the sum of one register -- no selects; bits 3..0 use
+// DPP row_mirror, row_half_mirror and quad permutations.  fp64: shuffles.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_read(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void swap_halves32(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                    false, false);
+    a = __builtin_bit_cast(float, (unsigned)r[0]);
+    b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ void swap_rows16(float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                    false, false);
+    a = __builtin_bit_cast(float, (unsigned)r[0]);
+    b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// One in-row stage (lane bit kBit, partner given by the DPP control kCtrl).
+template <int kCtrl, int kBit, int N>
+__device__ __forceinline__ void dpp_stage(float (&v)[N], int &k, int &idx, int lane) {
+    if (k > 1) {
+        const int half = k / 2;
+        const bool hi = (lane & kBit) != 0;
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+            if (j < half) {
+                const float lo_v = v[j], hi_v = v[half + j];
+                const float keep = hi ? hi_v : lo_v;
+                const float give = hi ? lo_v : hi_v;  // what the partner keeps
+                v[j] = keep + dpp_read<kCtrl>(give);
+            }
+        }
+        idx = idx * 2 + (hi ? 1 : 0);
+        k = half;
+    } else {
+        v[0] += dpp_read<kCtrl>(v[0]);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ int wave_reduce_scatter(float (&v)[N], int lane) {
+    int idx = 0, k = N;
+    // lane bit 5
+    if (k > 1) {
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) {
+            float a = v[j], b = v[N / 2 + j];
+            swap_halves32(a, b);
+            v[j] = a + b;
+        }
+        idx = (lane >> 5) & 1;
+        k = N / 2;
+    } else {
+        float a = v[0], b = v[0];
+        swap_halves32(a, b);
+        v[0] = a + b;
+    }
+    // lane bit 4
+    if (k > 1) {
+        const int half = k / 2;
+#pragma unroll
+        for (int j = 0; j < N / 4; ++j) {
+            if (j < half) {
+                float a = v[j], b = v[half + j];
+                swap_rows16(a, b);
+                v[j] = a + b;
+            }
+        }
+        idx = idx * 2 + ((lane >> 4) & 1);
+        k = half;
+    } else {
+        float a = v[0], b = v[0];
+        swap_rows16(a, b);
+        v[0] = a + b;
+    }
+    dpp_stage<0x140, 8>(v, k, idx, lane);   // row_mirror: lane i <-> 15 - i
+    dpp_stage<0x141, 4>(v, k, idx, lane);   // row_half_mirror: i <-> 7 - i
+    dpp_stage<0x4E, 2>(v, k, idx, lane);    // quad_perm [2,3,0,1]
+    dpp_stage<0xB1, 1>(v, k, idx, lane);    // quad_perm [1,0,3,2]
+    return idx;
+}
+
+template <int N>
+__device__ __forceinline__ int wave_reduce_scatter(double (&v)[N], int lane) {
     int idx = 0;
     int k = N;
 #pragma unroll
@@ -238,8 +327,11 @@ __device__ __forceinline__ int wave_reduce_scatter(Acc (&v)[N], int lane) {
 #pragma unroll
             for (int j = 0; j < N / 2; ++j) {
                 if (j < half) {
-                    const Acc keep = hi ? v[half + j] : v[j];
-                    const Acc send = hi ? v[j] : v[half + j];
+                    // select values, not element addresses: a select of
+                    // addresses would keep v out of registers
+                    const double lo_v = v[j], hi_v = v[half + j];
+                    const double keep = hi ? hi_v : lo_v;
+                    const double send = hi ? lo_v : hi_v;
                     v[j] = keep + __shfl_xor(send, m);
                 }
             }
@@ -286,8 +378,8 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     bool st = (Ar[0] != 0.f) && (p.force_general == 0);
 #pragma unroll
     for (int n = 1; n < N; ++n) st = st && (Ar[n] == (float)(n + 1) * Ar[0]);
-    // Waves of the other A class (or past the row) compute on a shadow
-    // channel and write nothing; they still take part in every barrier.
+    // Waves of the other A class (or past the row) do no work but take part
+    // in every barrier.
     const bool wave_on = tile_ok && ((bool)__all(st) == kStruct);
     const bool live = wave_on && in_range;
     const ChanConst<N, kStruct, kEuler, Acc> cc(Ar);
@@ -323,6 +415,81 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     Acc dDacc = 0, dbacc = 0;
     const int path = kStruct ? 0 : 1;
 
+    // Which waves of the block serve this launch.  A block with none writes
+    // zero dB/dC partials for its rows and leaves; a wave that is not on only
+    // keeps the block's barriers (its LDS slots stay zero).
+    __shared__ int on_flags[kWaves];
+    if (lane == 0) on_flags[wave] = wave_on ? 1 : 0;
+    for (int e = lane; e < kC * 2 * N; e += kWave) (&bacc[wave][0][0][0])[e] = 0;
+    __syncthreads();
+    int any_on = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any_on |= on_flags[w];
+    if (!any_on) {
+        const int64_t s_begin = (int64_t)grp * q.seg_per_group;
+        const int64_t s_end = s_begin + q.seg_per_group < p.S ? s_begin + q.seg_per_group : p.S;
+        const int64_t t_lo = s_begin * p.seg_len;
+        const int64_t t_hi = s_end * p.seg_len < p.L ? s_end * p.seg_len : p.L;
+        Acc *dst = static_cast<Acc *>(q.part_bc) + ((int64_t)(path * q.blocks_per_row + br) * 2) * BLN;
+        const int64_t cnt = (t_hi - t_lo) * N;
+        for (int64_t e = threadIdx.x; e < 2 * cnt; e += kBlock) {
+            const int64_t v = e / cnt, k = e - v * cnt;
+            dst[v * BLN + (b * p.L + t_lo) * N + k] = 0;
+        }
+        return;
+    }
+
+    // inputs of one sub-chunk (steps clamped into it), loaded one sub-chunk ahead
+    struct SubIn {
+        T x[kC], dl[kC], dy[kC];
+    };
+    auto load_sub = [&](int64_t ta, int nc, SubIn &in) {
+        const int64_t off = (b * p.L + ta) * p.Dm + d0;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const T *>(p.x) + off, nc * row);
+        const __amdgpu_buffer_rsrc_t rdl = make_rsrc(static_cast<const T *>(p.delta) + off, nc * row);
+        const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const T *>(q.dy) + off, nc * row);
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            const int so = (i < nc ? i : nc - 1) * row;
+            in.x[i] = buf_load<T>(rx, voff, so);
+            in.dl[i] = buf_load<T>(rdl, voff, so);
+            in.dy[i] = buf_load<T>(rdy, voff, so);
+        }
+    };
+
+    // the block's dB/dC sums of one sub-chunk, in wave order (deterministic)
+    auto write_block_sums = [&](int64_t ta, int nc) {
+        Acc *dst = static_cast<Acc *>(q.part_bc) + ((int64_t)(path * q.blocks_per_row + br) * 2) * BLN +
+                   (b * p.L + ta) * N;
+        for (int e = lane; e < kC * 2 * N; e += kWave) {
+            const int i = e / (2 * N);
+            const int v = (e / N) & 1;
+            const int n = e % N;
+            Acc sum = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) sum += bacc[w][i][v][n];
+            if (i < nc) dst[(int64_t)v * BLN + (int64_t)i * N + n] = sum;
+        }
+    };
+
+    if (!wave_on) {
+        // same barriers as the working waves; wave 0 still writes the sums
+        for (int si = 0; si < q.seg_per_group; ++si) {
+            const int s = grp * q.seg_per_group + si;
+            if (s >= p.S) break;
+            const int64_t t0 = (int64_t)s * p.seg_len;
+            const int nseg = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
+            for (int u = (nseg + kC - 1) / kC - 1; u >= 0; --u) {
+                const int64_t ta = t0 + (int64_t)u * kC;
+                const int nc = nseg - u * kC < kC ? nseg - u * kC : kC;
+                __syncthreads();
+                if (wave == 0) write_block_sums(ta, nc);
+                __syncthreads();
+            }
+        }
+        return;
+    }
+
     for (int si = 0; si < q.seg_per_group; ++si) {
         const int s = grp * q.seg_per_group + si;
         if (s >= p.S) break;
@@ -354,180 +521,170 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
             for (int n = 0; n < N; ++n) nu[n] = gout[((int64_t)s * N + n) * BD + ch];
         }
 
-        for (int j = nck - 1; j >= 0; --j) {
-            const int64_t tb = t0 + (int64_t)j * kK;
-            const int nb = (int)((t0 + nseg) - tb) < kK ? (int)((t0 + nseg) - tb) : kK;
-            const int nsub = (nb + kC - 1) / kC;
-            for (int qq = nsub - 1; qq >= 0; --qq) {
-                const int64_t ta = tb + (int64_t)qq * kC;
-                const int nc = uniform(nb - qq * kC < kC ? nb - qq * kC : kC);
-                // state entering the sub-chunk
-                Acc gp[N];
+        // sub-chunks from the last to the first
+        const int nsub = (nseg + kC - 1) / kC;
+        SubIn cur, nxt;
+        {
+            const int u = nsub - 1;
+            load_sub(t0 + (int64_t)u * kC, nseg - u * kC < kC ? nseg - u * kC : kC, cur);
+        }
+        for (int u = nsub - 1; u >= 0; --u) {
+            const int64_t ta = t0 + (int64_t)u * kC;
+            const int nc = uniform(nseg - u * kC < kC ? nseg - u * kC : kC);
+            if (u > 0) load_sub(ta - kC, kC, nxt);
+            // state entering the sub-chunk: its checkpoint, advanced
+            const int j = (u * kC) / kK;
+            Acc gp[N];
 #pragma unroll
-                for (int n = 0; n < N; ++n) gp[n] = ck[wave][j][n][lane];
-                advance(gp, tb, qq * kC);
+            for (int n = 0; n < N; ++n) gp[n] = ck[wave][j][n][lane];
+            advance(gp, t0 + (int64_t)j * kK, u * kC - j * kK);
 
-                // inputs of the sub-chunk, then its states
-                const int64_t off = (b * p.L + ta) * p.Dm + d0;
-                const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const T *>(p.x) + off, nc * row);
-                const __amdgpu_buffer_rsrc_t rdl = make_rsrc(static_cast<const T *>(p.delta) + off, nc * row);
-                const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const T *>(q.dy) + off, nc * row);
-                const __amdgpu_buffer_rsrc_t rdx = make_rsrc(static_cast<const T *>(q.dx) + off, nc * row);
-                const __amdgpu_buffer_rsrc_t rdd = make_rsrc(static_cast<const T *>(q.ddelta) + off, nc * row);
-                const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + ta) * (2 * N));
-                Acc xs[kC], ds[kC], gys[kC];
+            const int64_t off = (b * p.L + ta) * p.Dm + d0;
+            const __amdgpu_buffer_rsrc_t rdx = make_rsrc(static_cast<const T *>(q.dx) + off, nc * row);
+            const __amdgpu_buffer_rsrc_t rdd = make_rsrc(static_cast<const T *>(q.ddelta) + off, nc * row);
+            const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + ta) * (2 * N));
+            Acc xs[kC], ds[kC], gys[kC];
+#pragma unroll
+            for (int i = 0; i < kC; ++i) {
+                xs[i] = (Acc)to_f32(cur.x[i]);
+                ds[i] = (Acc)to_f32(cur.dl[i]);
+                gys[i] = (Acc)to_f32(cur.dy[i]);
+            }
+            if constexpr (kPre) {
+#pragma unroll
+                for (int i = 0; i < kC; ++i) ds[i] = dp.softplus ? softplus_(ds[i] + dp.bias) : ds[i] + dp.bias;
+            }
+            // the sub-chunk's states
+            Acc gs[kC][N];
+            {
+                Acc gc[N];
+#pragma unroll
+                for (int n = 0; n < N; ++n) gc[n] = gp[n];
 #pragma unroll
                 for (int i = 0; i < kC; ++i) {
-                    const int so = (i < nc ? i : nc - 1) * row;
-                    xs[i] = (Acc)to_f32(buf_load<T>(rx, voff, so));
-                    ds[i] = (Acc)to_f32(buf_load<T>(rdl, voff, so));
-                    gys[i] = (Acc)to_f32(buf_load<T>(rdy, voff, so));
-                }
-                if constexpr (kPre) {
-#pragma unroll
-                    for (int i = 0; i < kC; ++i) ds[i] = dp.softplus ? softplus_(ds[i] + dp.bias) : ds[i] + dp.bias;
-                }
-                Acc gs[kC][N];
-                {
-                    Acc gc[N];
-#pragma unroll
-                    for (int n = 0; n < N; ++n) gc[n] = gp[n];
-#pragma unroll
-                    for (int i = 0; i < kC; ++i) {
-                        if (i < nc) {
-                            Acc rw[2 * N];
-                            load_row<N>(rw, bcp + (int64_t)i * (2 * N));
-                            (void)scan_step<N, kStruct, true, kEuler>(cc, rw, xs[i], ds[i], gc);
-                        }
-#pragma unroll
-                        for (int n = 0; n < N; ++n) gs[i][n] = gc[n];
-                    }
-                }
-
-                // back over the sub-chunk
-#pragma unroll
-                for (int i = kC - 1; i >= 0; --i) {
                     if (i < nc) {
                         Acc rw[2 * N];
                         load_row<N>(rw, bcp + (int64_t)i * (2 * N));
-                        const Acc xv = xs[i], dv = ds[i], gy = gys[i];
-                        Acc vB[N], vC[N];
-                        Acc acc_x = 0, acc_d = 0;
-                        if constexpr (kStruct) {
-                            Acc r;
-                            const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
-                            Acc E = E1;
-                            const Acc xi = xv * inva, dxv = dv * xv;
+                        (void)scan_step<N, kStruct, true, kEuler>(cc, rw, xs[i], ds[i], gc);
+                    }
 #pragma unroll
-                            for (int n = 0; n < N; ++n) {
-                                const Acc gprev = i > 0 ? gs[i > 0 ? i - 1 : 0][n] : gp[n];
-                                const Acc mu = fma_(rw[N + n], gy, nu[n]);
-                                const Acc pp = E * mu;
-                                const Acc nup = mu + pp;
-                                vC[n] = gy * gs[i][n];
-                                if constexpr (!kEuler) {
-                                    acc_x = fma_(pp, rw[n], acc_x);
-                                    vB[n] = pp * xi;
-                                    const Acc w = fma_(a0n, gprev, rw[n] * xv);
-                                    const Acc qv = nup * w;
-                                    acc_d = fma_(qv, (Acc)(n + 1), acc_d);
-                                    dA1[n] = fma_(dv, qv, dA1[n]);
-                                    dA2[n] = fma_(vB[n], rw[n], dA2[n]);
-                                } else {
-                                    acc_x = fma_(mu, rw[n], acc_x);
-                                    vB[n] = mu * dxv;
-                                    const Acc ng = nup * gprev;
-                                    acc_d = fma_(ng, (Acc)(n + 1), acc_d);
-                                    dA1[n] = fma_(dv, ng, dA1[n]);
-                                }
-                                nu[n] = nup;
-                                if (n + 1 < N) {
-                                    if constexpr (sizeof(Acc) == 8)
-                                        E = fma_(E, E1, E + E1);
-                                    else
-                                        E = fma_(E, r, E1);
-                                }
-                            }
-                        } else {
-                            const Acc dxv = dv * xv;
+                    for (int n = 0; n < N; ++n) gs[i][n] = gc[n];
+                }
+            }
+
+            // back over the sub-chunk
 #pragma unroll
-                            for (int n = 0; n < N; ++n) {
-                                const Acc gprev = i > 0 ? gs[i > 0 ? i - 1 : 0][n] : gp[n];
-                                Acc e;
-                                const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
-                                const Acc mu = fma_(rw[N + n], gy, nu[n]);
-                                const Acc pp = E * mu;
-                                const Acc nup = mu + pp;
-                                vC[n] = gy * gs[i][n];
-                                if constexpr (!kEuler) {
-                                    const Acc pw = pp * cc.W[n];
-                                    acc_x = fma_(pw, rw[n], acc_x);
-                                    vB[n] = pw * xv;
-                                    const Acc bx = rw[n] * xv;
-                                    const Acc w = fma_(bx, (Acc)(n + 1), (Acc)Ar[n] * gprev);
-                                    acc_d = fma_(nup, w, acc_d);
-                                    const Acc z = dv * (Acc)Ar[n];
-                                    dA1[n] = fma_(dv, nup * gprev, dA1[n]);
-                                    dA2[n] = fma_(dv * dv * zoh_dphi(z, E), mu * bx, dA2[n]);
-                                } else {
-                                    acc_x = fma_(mu, rw[n], acc_x);
-                                    vB[n] = mu * dxv;
-                                    const Acc ng = nup * gprev;
-                                    acc_d = fma_((Acc)Ar[n], ng, acc_d);
-                                    dA1[n] = fma_(dv, ng, dA1[n]);
-                                }
-                                nu[n] = nup;
-                            }
-                        }
-                        Acc gx, gdl;
-                        if constexpr (!kEuler) {
-                            gx = fma_(Dd, gy, kStruct ? inva * acc_x : acc_x);
-                            gdl = acc_d;
-                        } else {
-                            gx = fma_(Dd, gy, dv * acc_x);
-                            gdl = fma_(xv, acc_x, kStruct ? a0n * acc_d : acc_d);
-                        }
-                        if constexpr (kPre) {
-                            if (dp.softplus) gdl *= softplus_grad_from_value(dv);
-                        }
-                        dDacc = fma_(gy, xv, dDacc);
-                        dbacc += gdl;
-                        if (wave_on) {
-                            buf_store(from_acc<T>(gx), rdx, voff, i * row);
-                            buf_store(from_acc<T>(gdl), rdd, voff, i * row);
-                        }
-                        // dB, dC: sum over the wave's channels, then over the block's waves
+            for (int i = kC - 1; i >= 0; --i) {
+                if (i < nc) {
+                    Acc rw[2 * N];
+                    load_row<N>(rw, bcp + (int64_t)i * (2 * N));
+                    const Acc xv = xs[i], dv = ds[i], gy = gys[i];
+                    Acc vB[N], vC[N];
+                    Acc acc_x = 0, acc_d = 0;
+                    if constexpr (kStruct) {
+                        Acc r;
+                        const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
+                        Acc E = E1;
+                        const Acc xi = xv * inva, dxv = dv * xv;
 #pragma unroll
                         for (int n = 0; n < N; ++n) {
-                            vB[n] = live ? vB[n] : (Acc)0;
-                            vC[n] = live ? vC[n] : (Acc)0;
+                            Acc gprev = gp[n];
+                            if (i > 0) gprev = gs[i > 0 ? i - 1 : 0][n];
+                            const Acc mu = fma_(rw[N + n], gy, nu[n]);
+                            const Acc pp = E * mu;
+                            const Acc nup = mu + pp;
+                            vC[n] = gy * gs[i][n];
+                            if constexpr (!kEuler) {
+                                acc_x = fma_(pp, rw[n], acc_x);
+                                vB[n] = pp * xi;
+                                const Acc w = fma_(a0n, gprev, rw[n] * xv);
+                                const Acc qv = nup * w;
+                                acc_d = fma_(qv, (Acc)(n + 1), acc_d);
+                                dA1[n] = fma_(dv, qv, dA1[n]);
+                                dA2[n] = fma_(vB[n], rw[n], dA2[n]);
+                            } else {
+                                acc_x = fma_(mu, rw[n], acc_x);
+                                vB[n] = mu * dxv;
+                                const Acc ng = nup * gprev;
+                                acc_d = fma_(ng, (Acc)(n + 1), acc_d);
+                                dA1[n] = fma_(dv, ng, dA1[n]);
+                            }
+                            nu[n] = nup;
+                            if (n + 1 < N) {
+                                if constexpr (sizeof(Acc) == 8)
+                                    E = fma_(E, E1, E + E1);
+                                else
+                                    E = fma_(E, r, E1);
+                            }
                         }
-                        const int idx = wave_reduce_scatter<N>(vB, lane);
-                        (void)wave_reduce_scatter<N>(vC, lane);
-                        // every wave fills its slot (zeros when it is not on)
-                        if ((lane & (kWave / N - 1)) == 0) {
-                            bacc[wave][i][0][idx] = vB[0];
-                            bacc[wave][i][1][idx] = vC[0];
-                        }
-                    }
-                }
-                __syncthreads();
-                if (wave == 0) {
-                    // the block's sum, in wave order (deterministic)
-                    Acc *dst = static_cast<Acc *>(q.part_bc) +
-                               ((int64_t)(path * q.blocks_per_row + br) * 2) * BLN + (b * p.L + ta) * N;
-                    for (int e = lane; e < kC * 2 * N; e += kWave) {
-                        const int i = e / (2 * N);
-                        const int v = (e / N) & 1;
-                        const int n = e % N;
-                        Acc sum = 0;
+                    } else {
+                        const Acc dxv = dv * xv;
 #pragma unroll
-                        for (int w = 0; w < kWaves; ++w) sum += bacc[w][i][v][n];
-                        if (i < nc) dst[(int64_t)v * BLN + (int64_t)i * N + n] = sum;
+                        for (int n = 0; n < N; ++n) {
+                            Acc gprev = gp[n];
+                            if (i > 0) gprev = gs[i > 0 ? i - 1 : 0][n];
+                            Acc e;
+                            const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
+                            const Acc mu = fma_(rw[N + n], gy, nu[n]);
+                            const Acc pp = E * mu;
+                            const Acc nup = mu + pp;
+                            vC[n] = gy * gs[i][n];
+                            if constexpr (!kEuler) {
+                                const Acc pw = pp * cc.W[n];
+                                acc_x = fma_(pw, rw[n], acc_x);
+                                vB[n] = pw * xv;
+                                const Acc bx = rw[n] * xv;
+                                const Acc w = fma_(bx, (Acc)(n + 1), (Acc)Ar[n] * gprev);
+                                acc_d = fma_(nup, w, acc_d);
+                                const Acc z = dv * (Acc)Ar[n];
+                                dA1[n] = fma_(dv, nup * gprev, dA1[n]);
+                                dA2[n] = fma_(dv * dv * zoh_dphi(z, E), mu * bx, dA2[n]);
+                            } else {
+                                acc_x = fma_(mu, rw[n], acc_x);
+                                vB[n] = mu * dxv;
+                                const Acc ng = nup * gprev;
+                                acc_d = fma_((Acc)Ar[n], ng, acc_d);
+                                dA1[n] = fma_(dv, ng, dA1[n]);
+                            }
+                            nu[n] = nup;
+                        }
+                    }
+                    Acc gx, gdl;
+                    if constexpr (!kEuler) {
+                        gx = fma_(Dd, gy, kStruct ? inva * acc_x : acc_x);
+                        gdl = acc_d;
+                    } else {
+                        gx = fma_(Dd, gy, dv * acc_x);
+                        gdl = fma_(xv, acc_x, kStruct ? a0n * acc_d : acc_d);
+                    }
+                    if constexpr (kPre) {
+                        if (dp.softplus) gdl *= softplus_grad_from_value(dv);
+                    }
+                    dDacc = fma_(gy, xv, dDacc);
+                    dbacc += gdl;
+                    if (wave_on) {
+                        buf_store(from_acc<T>(gx), rdx, voff, i * row);
+                        buf_store(from_acc<T>(gdl), rdd, voff, i * row);
+                    }
+                    // dB, dC: sum over the wave's channels, then over the block's waves
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        vB[n] = live ? vB[n] : (Acc)0;
+                        vC[n] = live ? vC[n] : (Acc)0;
+                    }
+                    const int idx = wave_reduce_scatter<N>(vB, lane);
+                    (void)wave_reduce_scatter<N>(vC, lane);
+                    // every wave fills its slot (zeros when it is not on)
+                    if ((lane & (kWave / N - 1)) == 0) {
+                        bacc[wave][i][0][idx] = vB[0];
+                        bacc[wave][i][1][idx] = vC[0];
                     }
                 }
-                __syncthreads();
             }
+            __syncthreads();
+            if (wave == 0) write_block_sums(ta, nc);
+            __syncthreads();
+            if (u > 0) cur = nxt;
         }
         if (s == 0 && live && q.dh_init != nullptr) {
 #pragma unroll

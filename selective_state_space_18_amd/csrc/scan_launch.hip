@@ -51,7 +51,7 @@ hipError_t launch_fill(float *dst, int64_t count, float v, hipStream_t s) {
 size_t scan_acc_bytes(int dtype) { return dtype == 0 ? sizeof(double) : sizeof(float); }
 
 // Must match BwdShape<Acc>::kT in bwd_kernels.h.
-int bwd_segment_len(int dtype) { return dtype == 0 ? 32 : 64; }
+int bwd_segment_len(int dtype) { return dtype == 0 ? 16 : 32; }
 
 hipError_t launch_bc_prep(const ScanParams &p, int N, int dtype, hipStream_t s) {
     return by_dtype(ScanPass::kPrep, p, N, dtype, s);

@@ -166,3 +166,17 @@ def test_bwd_mamba130m_layer_full(ss):
     got = gpu_bwd(ss, inp, {})
     torch.cuda.synchronize()
     check(got, oracle_bwd(inp, {}), "bf16")
+
+
+@pytest.mark.parametrize("kind", ["plain", "euler_softplus_bias"])
+def test_bwd_blocks_with_both_A_paths(ss, kind):
+    """Channels 64..127 of each row take the general path, the rest the
+    structured one: blocks hold waves of both kinds, and the row's last block
+    has waves past the row."""
+    P.say(f"case: bwd mixed blocks {kind}")
+    inp = make("bf16", "s4d_real", 2, 150, 300, 16, kind, True, True, seed=8)
+    inp["A"][64:128] = -torch.exp(torch.randn((64, 16), device=DEV) * 0.5)
+    opts = opts_of(kind, inp)
+    got = gpu_bwd(ss, inp, opts)
+    torch.cuda.synchronize()
+    check(got, oracle_bwd(inp, opts), "bf16")
