@@ -22,6 +22,22 @@ def _f64(a, shape, name):
     return a
 
 
+def _as_complex(a):
+    a = np.asarray(a)
+    if np.iscomplexobj(a):
+        return a.astype(np.complex128)
+    if a.shape[-1] != 2:
+        raise ValueError("oracle: expected a complex array or a trailing (re, im) axis")
+    return a[..., 0].astype(np.float64) + 1j * a[..., 1].astype(np.float64)
+
+
+def _pairs(c, shape, name):
+    c = np.asarray(c)
+    if tuple(c.shape) != tuple(shape):
+        raise ValueError(f"oracle: {name} has shape {c.shape}, expected {shape}")
+    return np.ascontiguousarray(np.stack([c.real, c.imag], axis=-1).astype(np.float64))
+
+
 def _flags(delta_softplus, euler_b):
     return (1 if delta_softplus else 0) | (2 if euler_b else 0)
 
@@ -46,6 +62,10 @@ class Oracle:
         lib.ssm_oracle_step.restype = ctypes.c_int
         lib.ssm_oracle_scan_bwd.argtypes = [_dp] * 18 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int]
         lib.ssm_oracle_scan_bwd.restype = ctypes.c_int
+        lib.ssm_oracle_scan_complex.argtypes = [_dp] * 10 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int]
+        lib.ssm_oracle_scan_complex.restype = ctypes.c_int
+        lib.ssm_oracle_step_complex.argtypes = [_dp] * 9 + [_i64] * 3 + [ctypes.c_int]
+        lib.ssm_oracle_step_complex.restype = ctypes.c_int
         lib.ssm_oracle_max_threads.argtypes = []
         lib.ssm_oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -80,6 +100,56 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"ssm_oracle_scan failed with code {rc}")
         return y, hf
+
+    def scan_complex(self, x, delta, A, B, C, D, h0=None, threads: int = 0, delta_bias=None,
+                     delta_softplus: bool = False, euler_b: bool = False):
+        """Scan with complex diagonal A.  A: complex [Dm, N] (numpy complex or a
+        real [Dm, N, 2] array of (re, im)); h0 complex [Bsz, Dm, N] or None.
+        Returns (y [Bsz, L, Dm] real, h_final [Bsz, Dm, N] complex)."""
+        x = np.asarray(x)
+        Bsz, L, Dm = x.shape
+        Ac = _as_complex(A)
+        N = Ac.shape[1]
+        x = _f64(x, (Bsz, L, Dm), "x")
+        delta = _f64(delta, (Bsz, L, Dm), "delta")
+        A2 = _pairs(Ac, (Dm, N), "A")
+        B = _f64(B, (Bsz, L, N), "B")
+        C = _f64(C, (Bsz, L, N), "C")
+        D = _f64(D, (Dm,), "D")
+        h2 = None if h0 is None else _pairs(_as_complex(h0), (Bsz, Dm, N), "h0")
+        bias = None if delta_bias is None else _f64(delta_bias, (Dm,), "delta_bias")
+        y = np.empty((Bsz, L, Dm), dtype=np.float64)
+        hf = np.empty((Bsz, Dm, N, 2), dtype=np.float64)
+        rc = self.lib.ssm_oracle_scan_complex(_ptr(x), _ptr(delta), _ptr(bias), _ptr(A2), _ptr(B), _ptr(C),
+                                              _ptr(D), _ptr(h2), _ptr(y), _ptr(hf), Bsz, L, Dm, N,
+                                              _flags(delta_softplus, euler_b), int(threads or self.threads))
+        if rc != 0:
+            raise RuntimeError(f"ssm_oracle_scan_complex failed with code {rc}")
+        return y, hf[..., 0] + 1j * hf[..., 1]
+
+    def step_complex(self, x, delta, A, B, C, D, h, delta_bias=None, delta_softplus: bool = False,
+                     euler_b: bool = False):
+        """One step with complex A; h complex [Bsz, Dm, N] (not modified).
+        Returns (y [Bsz, Dm], h_new complex)."""
+        x = np.asarray(x)
+        Bsz, Dm = x.shape
+        Ac = _as_complex(A)
+        N = Ac.shape[1]
+        x = _f64(x, (Bsz, Dm), "x")
+        delta = _f64(delta, (Bsz, Dm), "delta")
+        A2 = _pairs(Ac, (Dm, N), "A")
+        B = _f64(B, (Bsz, N), "B")
+        C = _f64(C, (Bsz, N), "C")
+        D = _f64(D, (Dm,), "D")
+        h2 = _pairs(_as_complex(h), (Bsz, Dm, N), "h").copy()
+        bias = None if delta_bias is None else _f64(delta_bias, (Dm,), "delta_bias")
+        y = np.empty((Bsz, Dm), dtype=np.float64)
+        rc = self.lib.ssm_oracle_step_complex(_ptr(x), _ptr(delta), _ptr(bias), _ptr(A2), _ptr(B), _ptr(C),
+                                              _ptr(D), _ptr(h2), _ptr(y), Bsz, Dm, N,
+                                              _flags(delta_softplus, euler_b))
+        if rc != 0:
+            raise RuntimeError(f"ssm_oracle_step_complex failed with code {rc}")
+        return y, h2[..., 0] + 1j * h2[..., 1]
 
     def scan_bwd(self, x, delta, A, B, C, D, dy, h0=None, dh_final=None, delta_bias=None,
                  delta_softplus: bool = False, euler_b: bool = False, want_dBC: bool = True,
@@ -163,3 +233,11 @@ def step(x, delta, A, B, C, D, h, **opts):
 
 def scan_bwd(x, delta, A, B, C, D, dy, **opts):
     return load().scan_bwd(x, delta, A, B, C, D, dy, **opts)
+
+
+def scan_complex(x, delta, A, B, C, D, **opts):
+    return load().scan_complex(x, delta, A, B, C, D, **opts)
+
+
+def step_complex(x, delta, A, B, C, D, h, **opts):
+    return load().step_complex(x, delta, A, B, C, D, h, **opts)

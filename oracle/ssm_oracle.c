@@ -347,6 +347,123 @@ int ssm_oracle_scan_bwd(const double *x, const double *delta, const double *bias
     return err;
 }
 
+/* ------------------------------------------------------------------------
+ * Complex diagonal A: the state update with complex eigenvalues that the
+ * bitig.info page on Mamba-3 describes (section "Karmasik Degerli Durum
+ * Guncellemesi": complex numbers in the state update give rotation and
+ * oscillation).  Readings: A[d][n] = a + i w is complex, the state h is
+ * complex, delta, x, B_t, C_t, D and y are real, and
+ *   Abar = exp(delta A),  Bbar = delta phi(delta A) B  (complex phi as above),
+ *   h_t = Abar h_{t-1} + Bbar x_t,   y_t = sum_n C_t[n] Re(h_t[n]) + D x_t.
+ * Layouts: A [Dm][N][2] and h0, h_final [Bsz][Dm][N][2] as (re, im) pairs.
+ * ---------------------------------------------------------------------- */
+
+/* (exp(z) - 1) for z = zr + i zi, without cancellation near 0:
+ * Re = expm1(zr) cos(zi) - 2 sin^2(zi/2),  Im = exp(zr) sin(zi). */
+static void cexpm1(double zr, double zi, double *er, double *ei)
+{
+    const double s = sin(0.5 * zi);
+    *er = expm1(zr) * cos(zi) - 2.0 * s * s;
+    *ei = exp(zr) * sin(zi);
+}
+
+/* One complex-state step for one channel; h holds (re, im) pairs. */
+static double channel_step_complex(double *h, double xt, double dt, const double *a,
+                                   const double *b, const double *c, double dskip,
+                                   int64_t N, int euler)
+{
+    double y = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        const double zr = dt * a[2 * n], zi = dt * a[2 * n + 1];
+        const double mag = exp(zr);
+        const double abr = mag * cos(zi), abi = mag * sin(zi);
+        double kr, ki; /* input coefficient Bbar / B */
+        if (euler) {
+            kr = dt;
+            ki = 0.0;
+        } else if (zr == 0.0 && zi == 0.0) {
+            kr = dt; /* phi(0) = 1 */
+            ki = 0.0;
+        } else {
+            double er, ei;
+            cexpm1(zr, zi, &er, &ei);
+            const double den = zr * zr + zi * zi; /* (er + i ei) / (zr + i zi) */
+            kr = dt * (er * zr + ei * zi) / den;
+            ki = dt * (ei * zr - er * zi) / den;
+        }
+        const double u = b[n] * xt;
+        const double hr = h[2 * n], hi = h[2 * n + 1];
+        h[2 * n] = abr * hr - abi * hi + kr * u;
+        h[2 * n + 1] = abr * hi + abi * hr + ki * u;
+        y += c[n] * h[2 * n];
+    }
+    return y + dskip * xt;
+}
+
+int ssm_oracle_scan_complex(const double *x, const double *delta, const double *bias,
+                            const double *A, const double *B, const double *C,
+                            const double *D, const double *h0, double *y,
+                            double *h_final, int64_t Bsz, int64_t L, int64_t Dm,
+                            int64_t N, int flags, int nthreads)
+{
+    if (Bsz < 0 || L < 0 || Dm < 0 || N <= 0)
+        return 1;
+    const int euler = (flags & ORACLE_EULER_B) != 0;
+    const int64_t nchan = Bsz * Dm;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int err = 0;
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)(2 * N) * sizeof(double));
+        if (!h) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t ch = 0; ch < nchan; ++ch) {
+                const int64_t b = ch / Dm, d = ch % Dm;
+                const double bias_d = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < 2 * N; ++k)
+                    h[k] = h0 ? h0[(b * Dm + d) * 2 * N + k] : 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    const int64_t i = (b * L + t) * Dm + d;
+                    const int64_t r = (b * L + t) * N;
+                    const double dt = step_size(delta[i], bias_d, flags);
+                    y[i] = channel_step_complex(h, x[i], dt, A + d * 2 * N, B + r, C + r, D[d], N, euler);
+                }
+                if (h_final)
+                    for (int64_t k = 0; k < 2 * N; ++k)
+                        h_final[(b * Dm + d) * 2 * N + k] = h[k];
+            }
+            free(h);
+        }
+    }
+    return err;
+}
+
+int ssm_oracle_step_complex(const double *x, const double *delta, const double *bias,
+                            const double *A, const double *B, const double *C,
+                            const double *D, double *h, double *y, int64_t Bsz,
+                            int64_t Dm, int64_t N, int flags)
+{
+    if (Bsz < 0 || Dm < 0 || N <= 0)
+        return 1;
+    const int euler = (flags & ORACLE_EULER_B) != 0;
+    for (int64_t b = 0; b < Bsz; ++b)
+        for (int64_t d = 0; d < Dm; ++d) {
+            const int64_t i = b * Dm + d;
+            const double dt = step_size(delta[i], bias ? bias[d] : 0.0, flags);
+            y[i] = channel_step_complex(h + i * 2 * N, x[i], dt, A + d * 2 * N, B + b * N,
+                                        C + b * N, D[d], N, euler);
+        }
+    return 0;
+}
+
 int ssm_oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -501,6 +501,134 @@ def check_bwd_adjoint_identities(orc, seed=16):
             assert np.allclose(g["dC"][:, t], np.einsum("bd,bdn->bn", dy[:, t], ht), rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# complex diagonal A
+
+
+def vanloan_complex(a, w, dt, b):
+    """(Abar, Bbar) of h' = (a + i w) h + b u as the real 2-state system
+    [[a, -w], [w, a]] with input (b, 0): exp of the augmented matrix."""
+    M = np.array([[a, -w, b], [w, a, 0.0], [0.0, 0.0, 0.0]], dtype=np.float64) * dt
+    E = expm(M)
+    return E[0, 0] + 1j * E[1, 0], E[0, 2] + 1j * E[1, 2]
+
+
+def check_complex_vanloan_step(orc):
+    """One step from h = 0 (x = 1) gives Bbar; from h = 1 and h = i (x = 0)
+    gives Abar and i Abar, over a grid including a = 0, w = 0 and delta = 0."""
+    a_v = [-3.0, -0.5, -1e-6, 0.0]
+    w_v = [0.0, 0.3, 2.0, 10.0, -4.0]
+    d_v = [0.0, 1e-4, 0.05, 0.7]
+    bval = 1.3
+    A = np.array([[complex(a, w)] for a in a_v for w in w_v])  # [Dm, 1]
+    Dm = A.shape[0]
+    for dt in d_v:
+        x1, x0 = np.ones((1, Dm)), np.zeros((1, Dm))
+        dl = np.full((1, Dm), dt)
+        Bm, Cm = np.full((1, 1), bval), np.zeros((1, 1))
+        _, hB = orc.step_complex(x1, dl, A, Bm, Cm, np.zeros(Dm), np.zeros((1, Dm, 1), complex))
+        _, hA = orc.step_complex(x0, dl, A, Bm, Cm, np.zeros(Dm), np.ones((1, Dm, 1), complex))
+        _, hI = orc.step_complex(x0, dl, A, Bm, Cm, np.zeros(Dm), np.full((1, Dm, 1), 1j))
+        for k in range(Dm):
+            ea, eb = vanloan_complex(A[k, 0].real, A[k, 0].imag, dt, bval)
+            # expm's own error grows with the norm of delta * A
+            tol = 1e-14 * max(1.0, abs(dt * A[k, 0])) * 4
+            assert abs(hA[0, k, 0] - ea) <= tol * max(1.0, abs(ea)), (A[k, 0], dt, hA[0, k, 0], ea)
+            assert abs(hI[0, k, 0] - 1j * ea) <= tol * max(1.0, abs(ea))
+            assert abs(hB[0, k, 0] - eb) <= 10 * tol * max(abs(eb), 1e-300), (A[k, 0], dt, hB[0, k, 0], eb)
+
+
+def check_complex_reduces_to_real(orc, seed=20):
+    """w = 0: the complex scan is the real scan (imaginary parts stay 0)."""
+    rng = np.random.default_rng(seed)
+    x, delta, A, B, C, D = random_case(rng, 2, 13, 3, 4)
+    h0 = rng.standard_normal((2, 3, 4))
+    for opts in ({}, {"euler_b": True}):
+        yc, hc = orc.scan_complex(x, delta, A.astype(complex), B, C, D, h0=h0.astype(complex), **opts)
+        yr, hr = orc.scan(x, delta, A, B, C, D, h0=h0, **opts)
+        assert rel_err(yc, yr) < 1e-14 and rel_err(hc.real, hr) < 1e-14
+        assert np.all(hc.imag == 0.0)
+
+
+def check_complex_rotation(orc, seed=21):
+    """a = 0, x = 0: the state turns by w * sum(delta) at constant modulus."""
+    rng = np.random.default_rng(seed)
+    Bsz, L, Dm, N = 2, 17, 3, 4
+    _, delta, _, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    w = rng.uniform(-6, 6, (Dm, N))
+    h0 = rng.standard_normal((Bsz, Dm, N)) + 1j * rng.standard_normal((Bsz, Dm, N))
+    _, hf = orc.scan_complex(np.zeros((Bsz, L, Dm)), delta, 1j * w, B, C, D, h0=h0)
+    expect = h0 * np.exp(1j * w[None] * delta.sum(axis=1)[:, :, None])
+    assert np.max(np.abs(hf - expect)) < 1e-13
+    assert np.max(np.abs(np.abs(hf) - np.abs(h0))) < 1e-13
+
+
+def check_complex_exact_for_constant_input(orc, seed=22):
+    """Constant x, delta, B, h0 = 0: after k steps the ZOH state is the exact
+    ODE solution B x (exp(A k delta) - 1) / A; the Euler term gives the
+    geometric sum delta B x (1 - Abar^k) / (1 - Abar)."""
+    rng = np.random.default_rng(seed)
+    L, Dm, N = 9, 3, 2
+    xv, dv = rng.standard_normal(Dm), rng.uniform(0.02, 0.4, Dm)
+    bv = rng.standard_normal(N)
+    A = -np.exp(rng.uniform(-1, 1, (Dm, N))) + 1j * rng.uniform(-5, 5, (Dm, N))
+    x = np.tile(xv.reshape(1, 1, Dm), (1, L, 1))
+    dl = np.tile(dv.reshape(1, 1, Dm), (1, L, 1))
+    B = np.tile(bv.reshape(1, 1, N), (1, L, 1))
+    C = np.zeros((1, L, N))
+    for k in range(1, L + 1):
+        _, hz = orc.scan_complex(x[:, :k], dl[:, :k], A, B[:, :k], C[:, :k], np.zeros(Dm))
+        _, he = orc.scan_complex(x[:, :k], dl[:, :k], A, B[:, :k], C[:, :k], np.zeros(Dm), euler_b=True)
+        ex = bv[None, :] * xv[:, None] * np.expm1(A * k * dv[:, None]) / A
+        ab = np.exp(A * dv[:, None])
+        ee = dv[:, None] * bv[None, :] * xv[:, None] * np.expm1(k * A * dv[:, None]) / np.expm1(A * dv[:, None])
+        assert np.max(np.abs(hz[0] - ex)) <= 1e-12 * np.max(np.abs(ex)), k
+        assert np.max(np.abs(he[0] - ee)) <= 1e-12 * np.max(np.abs(ee)), k
+        _ = ab
+
+
+def check_complex_lfilter(orc, seed=23):
+    """Time-varying x with constant delta, B, C: per state the complex IIR
+    filter lfilter([Bbar], [1, -Abar], x) (Abar, Bbar from the real 2-state
+    matrix exponential), and y = sum_n C_n Re(h_n) + D x."""
+    rng = np.random.default_rng(seed)
+    L, Dm, N = 30, 2, 3
+    x = rng.standard_normal((1, L, Dm))
+    dv = rng.uniform(0.05, 0.5, Dm)
+    dl = np.tile(dv.reshape(1, 1, Dm), (1, L, 1))
+    A = -np.exp(rng.uniform(-1.5, 0.5, (Dm, N))) + 1j * rng.uniform(-8, 8, (Dm, N))
+    bv, cv = rng.standard_normal(N), rng.standard_normal(N)
+    B = np.tile(bv.reshape(1, 1, N), (1, L, 1))
+    C = np.tile(cv.reshape(1, 1, N), (1, L, 1))
+    D = rng.standard_normal(Dm)
+    y, hf = orc.scan_complex(x, dl, A, B, C, D)
+    for d in range(Dm):
+        hs = np.empty((L, N), complex)
+        for n in range(N):
+            ab, bb = vanloan_complex(A[d, n].real, A[d, n].imag, dv[d], bv[n])
+            hs[:, n] = lfilter([bb], [1.0, -ab], x[0, :, d].astype(complex))
+        ye = hs.real @ cv + D[d] * x[0, :, d]
+        assert rel_err(y[0, :, d], ye) < 1e-12
+        assert np.max(np.abs(hf[0, d] - hs[-1])) < 1e-12 * max(1.0, np.max(np.abs(hs[-1])))
+
+
+def check_complex_step_chain(orc, seed=24):
+    rng = np.random.default_rng(seed)
+    Bsz, L, Dm, N = 2, 9, 3, 4
+    x, _, _, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    raw = rng.normal(-1.0, 1.0, (Bsz, L, Dm))
+    bias = rng.normal(0.0, 0.5, Dm)
+    A = -np.exp(rng.uniform(-1, 1, (Dm, N))) + 1j * rng.uniform(-3, 3, (Dm, N))
+    h0 = rng.standard_normal((Bsz, Dm, N)) + 1j * rng.standard_normal((Bsz, Dm, N))
+    opts = dict(delta_bias=bias, delta_softplus=True)
+    y, hf = orc.scan_complex(x, raw, A, B, C, D, h0=h0, **opts)
+    h = h0
+    for t in range(L):
+        yt, h = orc.step_complex(x[:, t], raw[:, t], A, B[:, t], C[:, t], D, h, **opts)
+        assert rel_err(yt, y[:, t]) < 1e-13
+    assert np.max(np.abs(h - hf)) < 1e-13 * max(1.0, np.max(np.abs(hf)))
+
+
 ALL_CHECKS = [
     check_golden,
     check_brute_force,
@@ -520,4 +648,10 @@ ALL_CHECKS = [
     check_options_step_chain_matches_scan,
     check_bwd_finite_differences,
     check_bwd_adjoint_identities,
+    check_complex_vanloan_step,
+    check_complex_reduces_to_real,
+    check_complex_rotation,
+    check_complex_exact_for_constant_input,
+    check_complex_lfilter,
+    check_complex_step_chain,
 ]

@@ -13,7 +13,7 @@ SRC = os.path.join(ROOT, "oracle", "ssm_oracle.c")
 
 # (name, text to replace, replacement)
 MUTANTS = [
-    ("drop_D_term", "return y + dskip * xt;", "return y;"),
+    ("drop_D_term", "y += c[n] * h[n];\n    }\n    return y + dskip * xt;", "y += c[n] * h[n];\n    }\n    return y;"),
     ("y_uses_old_state",
      "h[n] = abar * h[n] + bbar * xt;\n        y += c[n] * h[n];",
      "y += c[n] * h[n];\n        h[n] = abar * h[n] + bbar * xt;"),
@@ -25,11 +25,11 @@ MUTANTS = [
     ("B_and_C_swapped", "B + r,\n                                        C + r,",
      "C + r,\n                                        B + r,"),
     ("B_C_ignore_batch", "const int64_t r = (b * L + t) * N;\n                    const double dt = step_size(delta[i], bias_d, flags);\n                    y[i]",
-     "const int64_t r = t * N;\n                    const double dt = step_size(delta[i], bias_d, flags);\n                    y[i]"),
+     "const int64_t r = t * N;\n                    const double dt = step_size(delta[i], bias_d, flags);\n                    y[i]", 0),
     ("delta_from_channel_0", "step_size(delta[i], bias_d, flags);\n                    y[i]",
-     "step_size(delta[(b * L + t) * Dm], bias_d, flags);\n                    y[i]"),
+     "step_size(delta[(b * L + t) * Dm], bias_d, flags);\n                    y[i]", 0),
     ("A_row_of_channel_0_in_scan", "dt, A + d * N, B + r", "dt, A, B + r"),
-    ("D_of_channel_0", "C + r, D[d], N, euler);", "C + r, D[0], N, euler);"),
+    ("D_of_channel_0", "C + r, D[d], N, euler);", "C + r, D[0], N, euler);", 0),
     ("initial_state_ignored", "h[n] = h0 ? h0[(b * Dm + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     ("step_B_ignores_batch", "B + b * N, C + b * N", "B, C + b * N"),
     ("step_A_row_of_channel_0", "dt, A + d * N,\n                                B + b * N",
@@ -44,15 +44,15 @@ MUTANTS = [
     ("softplus_naive_overflow", "    if (v > 0.0)\n        return v + log1p(exp(-v));\n", ""),
     ("scan_bias_of_channel_0", "const double bias_d = bias ? bias[d] : 0.0;\n                for (int64_t n = 0; n < N; ++n)\n                    h[n]",
      "const double bias_d = bias ? bias[0] : 0.0;\n                for (int64_t n = 0; n < N; ++n)\n                    h[n]"),
-    ("step_bias_of_channel_0", "bias ? bias[d] : 0.0, flags);", "bias ? bias[0] : 0.0, flags);"),
+    ("step_bias_of_channel_0", "bias ? bias[d] : 0.0, flags);", "bias ? bias[0] : 0.0, flags);", 0),
     ("euler_uses_zoh", "            bbar = dt * b[n];\n", "            bbar = dt * zoh_phi(z) * b[n];\n"),
     ("euler_drops_delta", "            bbar = dt * b[n];\n", "            bbar = b[n];\n"),
     ("euler_forward_abar", "const double abar = exp(z);\n        double bbar;",
      "const double abar = euler ? 1.0 + z : exp(z);\n        double bbar;"),
     ("euler_ignored_in_step", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    for (int64_t b",
-     "const int euler = 0;\n    for (int64_t b"),
+     "const int euler = 0;\n    for (int64_t b", 0),
     ("euler_ignored_in_scan", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    const int64_t nchan",
-     "const int euler = 0;\n    const int64_t nchan"),
+     "const int euler = 0;\n    const int64_t nchan", 0),
     # backward
     ("bwd_dx_drops_D", "double gx = D[d] * g, gdt = 0.0;", "double gx = 0.0, gdt = 0.0;"),
     ("bwd_lambda_uses_C_of_state_0", "lam[n] += C[r + n] * g;", "lam[n] += C[r] * g;"),
@@ -76,28 +76,53 @@ MUTANTS = [
     ("bwd_dbias_overwritten", "dbias_d += gdt;", "dbias_d = gdt;"),
     ("bwd_forward_ignores_euler", "const double k = euler ? dt : dt * zoh_phi(z);\n                            hs[",
      "const double k = dt * zoh_phi(z);\n                            hs["),
+    # complex A
+    ("cplx_rotation_sign", "h[2 * n] = abr * hr - abi * hi + kr * u;", "h[2 * n] = abr * hr + abi * hi + kr * u;"),
+    ("cplx_no_imag_coupling", "h[2 * n + 1] = abr * hi + abi * hr + ki * u;", "h[2 * n + 1] = abr * hi + ki * u;"),
+    ("cplx_y_uses_imag", "y += c[n] * h[2 * n];", "y += c[n] * h[2 * n + 1];"),
+    ("cplx_phi_conjugate", "ki = dt * (ei * zr - er * zi) / den;", "ki = dt * (er * zi - ei * zr) / den;"),
+    ("cplx_sin_for_cos", "const double abr = mag * cos(zi), abi = mag * sin(zi);",
+     "const double abr = mag * sin(zi), abi = mag * cos(zi);"),
+    ("cplx_expm1_missing_term", "*er = expm1(zr) * cos(zi) - 2.0 * s * s;", "*er = expm1(zr) * cos(zi);"),
+    ("cplx_imag_A_ignored", "zi = dt * a[2 * n + 1];", "zi = 0.0 * a[2 * n + 1];"),
+    ("cplx_euler_ignored", "        if (euler) {\n            kr = dt;", "        if (0) {\n            kr = dt;"),
+    ("cplx_h0_imag_dropped", "h[k] = h0 ? h0[(b * Dm + d) * 2 * N + k] : 0.0;",
+     "h[k] = h0 && (k % 2 == 0) ? h0[(b * Dm + d) * 2 * N + k] : 0.0;"),
+    ("cplx_D_of_channel_0", "C + r, D[d], N, euler);", "C + r, D[0], N, euler);", 1),
+    ("cplx_euler_ignored_in_scan", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    const int64_t nchan",
+     "const int euler = 0;\n    const int64_t nchan", 1),
     ("h_final_not_last_state",
      "h_final[(b * Dm + d) * N + n] = h[n];",
      "h_final[(b * Dm + d) * N + n] = h[n] * 0.5 + 0.5 * h[n] * (n == 0 ? 1.0 : 0.999);"),
 ]
 
 
-def _build_mutant(tmp_path, name, old, new):
+def _build_mutant(tmp_path, name, old, new, occurrence=None):
+    """Replace `old` by `new` in a copy of the oracle: `old` must occur exactly
+    once, or `occurrence` picks one of several (0 = first)."""
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutant {name}: pattern must occur exactly once"
+    if occurrence is None:
+        assert src.count(old) == 1, f"mutant {name}: pattern must occur exactly once"
+        start = src.index(old)
+    else:
+        start = -1
+        for _ in range(occurrence + 1):
+            start = src.index(old, start + 1)
     path = tmp_path / f"{name}.c"
-    path.write_text(src.replace(old, new))
+    path.write_text(src[:start] + new + src[start + len(old):])
     lib = tmp_path / f"lib{name}.so"
     subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", str(path),
                     "-o", str(lib), "-lm"], check=True)
     return str(lib)
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, mutant):
     import oracle
+    name, old, new = mutant[:3]
+    occurrence = mutant[3] if len(mutant) > 3 else None
     # one thread: the checks make many tiny calls, and test workers run side by side
-    mut = oracle.Oracle(_build_mutant(tmp_path, name, old, new), threads=1)
+    mut = oracle.Oracle(_build_mutant(tmp_path, name, old, new, occurrence), threads=1)
     for check in _pins.ALL_CHECKS:
         try:
             check(mut)
