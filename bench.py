@@ -14,7 +14,8 @@ decode step.
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
                     [--no-cpu-baseline] [--no-secondary]
     python bench.py --only decode      # one workload, for profiler runs
-                                       # (scan, long, small, packed, options, backward, decode)
+                                       # (scan, long, small, packed, options, backward,
+                                       #  complex, decode)
     python bench.py --copy-calibration # plain copy of known size (for counters)
 """
 import argparse
@@ -196,6 +197,27 @@ def bench_backward(torch, ss, generate, cfg, steps, warmup):
     return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": elems / (ms * 1e-3), "unit": "elems/s",
             "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
             "main_kernel_elems_per_s": elems / (main_ms * 1e-3)}
+
+
+def bench_complex(torch, ss, generate, cfg, steps, warmup):
+    """The layer with complex diagonal A (decaying oscillators): one exp and
+    one sin/cos pair per state element; no structured fast path."""
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name} (complex A)")
+    inp = generate.scan_inputs(cfg, dev)
+    A = generate.complex_A(cfg.Dm, cfg.N, cfg.seed + 100, dev)
+    y = torch.empty_like(inp["x"])
+    hf = torch.empty((cfg.Bsz, cfg.Dm, cfg.N), dtype=torch.complex64, device=dev)
+
+    def fn(_i):
+        ss.scan_complex_fwd(inp["x"], inp["delta"], A, inp["B"], inp["C"], inp["D"], y=y, h_final=hf)
+
+    log(f"[bench] timing {cfg.name} complex: {warmup} warmup + {steps} steps")
+    ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    del inp, A, y, hf
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name + "_complex_A", "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
+            "unit": "elems/s", "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()}}
 
 
 def bench_packed(torch, ss, generate, cfg, steps, warmup):
@@ -387,7 +409,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward"],
+    ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
+                                       "complex"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
@@ -415,6 +438,10 @@ def main():
 
     if a.only == "decode":
         rec = bench_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "complex":
+        rec = bench_complex(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps, a.warmup)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "backward":
@@ -475,6 +502,7 @@ def main():
         sec["fused_softplus"] = bench_options(torch, ss, generate, configs, max(5, a.steps // 5))
         sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER,
                                              max(5, a.steps // 5), 2)
+        sec["complex_A"] = bench_complex(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
         sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
                                      configs.DECODE_256x8192.n_tokens)

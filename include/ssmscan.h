@@ -177,6 +177,33 @@ int ssm_scan_fused_fwd(const void *x, const void *delta, const float *delta_bias
                        unsigned flags, void *stream);
 
 /*
+ * Scan with complex diagonal A: the state update with complex eigenvalues
+ * (rotation as well as decay) that the bitig.info page on Mamba-3 describes
+ * (section "Karmasik Degerli Durum Guncellemesi").  Per (b, d, n), with
+ * A[d][n] = a + i w and a complex state h:
+ *   Abar = exp(delta A),  Bbar = (Abar - 1)/A * B_t[n]  (delta B_t[n] with SSM_EULER_B)
+ *   h_t = Abar h_{t-1} + Bbar x_t,   y_t = sum_n C_t[n] Re(h_t[n]) + D x_t
+ * x, delta, B, C, D, y, delta_bias, dtype and flags are as in
+ * ssm_scan_fused_fwd (real); complex arrays are (re, im) fp32 pairs:
+ *   A       : [Dm][N][2]
+ *   h_init  : [Bsz][Dm][N][2] or NULL (zero); may equal h_final
+ *   h_final : [Bsz][Dm][N][2] or NULL
+ * Dense batch only.  Other rules as ssm_scan_fwd_ex.
+ */
+int ssm_scan_complex_fwd(const void *x, const void *delta, const float *delta_bias,
+                         const float *A, const void *B, const void *C, const float *D,
+                         const float *h_init, void *y, float *h_final,
+                         int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
+                         unsigned flags, void *stream);
+
+/* One decode step with complex A; h [Bsz][Dm][N][2] fp32 updated in place.
+ * Arguments otherwise as ssm_step_fused. */
+int ssm_step_complex(const void *x, const void *delta, const float *delta_bias,
+                     const float *A, const void *B, const void *C, const float *D,
+                     float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
+                     unsigned flags, void *stream);
+
+/*
  * Backward of the scan: every input gradient for given output gradients.
  * The chain rule on the recurrence ("Mamba SSM Nedir?", section "Ayrik Zamana
  * Gecis"), as training needs it (section "Paralel Tarama Algoritmasi": the

@@ -411,6 +411,151 @@ int step_impl(const void *x, const void *delta, const float *A, const void *B, c
 }
 
 // ---------------------------------------------------------------------------
+// Complex diagonal A.
+
+int cplx_impl(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+              const void *C, const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
+              int64_t Dm, int64_t N, int dtype, unsigned flags, void *stream) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
+    if (flags & ~kKnownFlags) return fail(SSM_ERR_BAD_OPTION, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
+    if (Bsz < 0 || L < 0 || Dm < 0)
+        return fail(SSM_ERR_BAD_DIM, "negative size (Bsz=%lld, L=%lld, Dm=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm);
+    int64_t BL, BLD, BLN, DN, BD, BDN;
+    if (!mul_ok(Bsz, L, &BL) || !mul_ok(BL, Dm, &BLD) || !mul_ok(BL, N, &BLN) || !mul_ok(Dm, N, &DN) ||
+        !mul_ok(Bsz, Dm, &BD) || !mul_ok(BD, N, &BDN) || BD > INT32_MAX / 2 || Bsz * ((Dm + 63) / 64) > INT32_MAX / 8 ||
+        DN > INT64_MAX / 4 || BDN > INT64_MAX / 4)
+        return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm, (long long)N);
+    const int64_t es = dtype_size(dtype);
+    const Arg in[] = {{x, BLD, es, "x"},        {delta, BLD, es, "delta"}, {A, 2 * DN, 4, "A"},
+                      {B, BLN, es, "B"},        {C, BLN, es, "C"},         {D, Dm, 4, "D"},
+                      {delta_bias, delta_bias ? Dm : 0, 4, "delta_bias"}};
+    const Arg hi = {h_init, h_init ? 2 * BDN : 0, 4, "h_init"};
+    const Arg ya = {y, BLD, es, "y"};
+    const Arg hf = {h_final, h_final ? 2 * BDN : 0, 4, "h_final"};
+    int rc;
+    if ((rc = check_args(in, 7)) || (rc = check_args(&hi, 1)) || (rc = check_args(&ya, 1)) || (rc = check_args(&hf, 1)))
+        return rc;
+    if ((rc = check_output(ya, in, 7)) || (rc = check_output(ya, &hi, 1)) || (rc = check_output(hf, in, 7)) ||
+        (rc = check_output(hf, &ya, 1)))
+        return rc;
+    if (h_init != nullptr && h_final != nullptr && (const void *)h_init != (const void *)h_final && overlaps(hi, hf))
+        return fail(SSM_ERR_ALIAS, "h_init partially overlaps h_final");
+    if (BD == 0) return ok();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    ssm::ScanParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x = x;
+    p.delta = delta;
+    p.B = B;
+    p.C = C;
+    p.A = A;
+    p.D = D;
+    p.h_init = h_init;
+    p.y = y;
+    p.h_final = h_final;
+    p.Bsz = Bsz;
+    p.L = L;
+    p.Dm = Dm;
+    p.waves_per_block = kWavesPerBlock;
+    p.delta_bias = delta_bias;
+    p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+    p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
+    hipError_t e;
+    if (L == 0) {
+        if (h_final == nullptr) return ok();
+        // h_final = h_init (or zero): 2N floats per channel
+        ssm::ScanParams z = p;
+        z.Dm = Dm * 2;
+        e = timed(SSM_K_STATE_INIT, s, [&] { return ssm::launch_state_init(z, (int)N, s); });
+        return e == hipSuccess ? ok() : hip_fail(e, "state init launch");
+    }
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int cus = 0;
+    if ((rc = device_cus(dev, &cus))) return rc;
+    const Plan pl = make_plan(Bsz, L, Dm, es, cus);
+    p.S = pl.S;
+    p.seg_len = pl.seg_len;
+    p.tiles_per_b = pl.tiles_per_b;
+    p.n_tiles = pl.n_tiles;
+    const size_t acc = ssm::scan_acc_bytes(dtype);
+    const size_t bc_bytes = align256((size_t)BL * 2 * N * acc);
+    const size_t agg_bytes = pl.S > 1 ? align256((size_t)(pl.S - 1) * (2 * N + 1) * BD * acc) : 0;
+    const size_t gin_bytes = pl.S > 1 ? align256((size_t)pl.S * 2 * N * BD * acc) : 0;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    void *ws = nullptr;
+    if ((rc = workspace(dev, s, bc_bytes + agg_bytes + gin_bytes, &ws))) return rc;
+    char *base = static_cast<char *>(ws);
+    p.bc = base;
+    p.agg = agg_bytes ? base + bc_bytes : nullptr;
+    p.gin = gin_bytes ? base + bc_bytes + agg_bytes : nullptr;
+    const int n = (int)N;
+    auto pass = [&](ssm::ScanPass ps) {
+        return dtype == SSM_F32 ? ssm::cplx_pass_f32(ps, p, n, s) : ssm::cplx_pass_bf16(ps, p, n, s);
+    };
+    if ((e = timed(SSM_K_BC_PREP, s, [&] { return pass(ssm::ScanPass::kPrep); })) != hipSuccess)
+        return hip_fail(e, "B/C conversion launch");
+    if (pl.S > 1) {
+        if ((e = timed(SSM_K_SCAN_AGGREGATE, s, [&] { return pass(ssm::ScanPass::kAggregate); })) != hipSuccess)
+            return hip_fail(e, "segment aggregate launch");
+        if ((e = timed(SSM_K_SCAN_CARRY, s, [&] { return pass(ssm::ScanPass::kCarry); })) != hipSuccess)
+            return hip_fail(e, "segment carry launch");
+    }
+    if ((e = timed(SSM_K_SCAN_OUTPUT, s, [&] { return pass(ssm::ScanPass::kOutput); })) != hipSuccess)
+        return hip_fail(e, "segment output launch");
+    return ok();
+}
+
+int cplx_step_impl(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+                   const void *C, const float *D, float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
+                   unsigned flags, void *stream) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
+    if (flags & ~kKnownFlags) return fail(SSM_ERR_BAD_OPTION, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
+    if (Bsz < 0 || Dm < 0)
+        return fail(SSM_ERR_BAD_DIM, "negative size (Bsz=%lld, Dm=%lld)", (long long)Bsz, (long long)Dm);
+    int64_t BD, BN, DN, BDN;
+    if (!mul_ok(Bsz, Dm, &BD) || !mul_ok(Bsz, N, &BN) || !mul_ok(Dm, N, &DN) || !mul_ok(BD, N, &BDN) ||
+        BDN > INT64_MAX / 64)
+        return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, Dm=%lld, N=%lld)", (long long)Bsz, (long long)Dm,
+                    (long long)N);
+    const int64_t es = dtype_size(dtype);
+    const Arg in[] = {{x, BD, es, "x"}, {delta, BD, es, "delta"}, {A, 2 * DN, 4, "A"},
+                      {B, BN, es, "B"}, {C, BN, es, "C"},         {D, Dm, 4, "D"},
+                      {delta_bias, delta_bias ? Dm : 0, 4, "delta_bias"}};
+    const Arg ha = {h, 2 * BDN, 4, "h"};
+    const Arg ya = {y, BD, es, "y"};
+    int rc;
+    if ((rc = check_args(in, 7)) || (rc = check_args(&ha, 1)) || (rc = check_args(&ya, 1))) return rc;
+    if ((rc = check_output(ha, in, 7)) || (rc = check_output(ya, in, 7)) || (rc = check_output(ya, &ha, 1)))
+        return rc;
+    if (BD == 0) return ok();
+    ssm::StepParams p;
+    p.x = x;
+    p.delta = delta;
+    p.B = B;
+    p.C = C;
+    p.A = A;
+    p.D = D;
+    p.h = h;
+    p.y = y;
+    p.Bsz = Bsz;
+    p.Dm = Dm;
+    p.delta_bias = delta_bias;
+    p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+    p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = timed(SSM_K_STEP, s, [&] {
+        return dtype == SSM_F32 ? ssm::cplx_step_f32(p, (int)N, s) : ssm::cplx_step_bf16(p, (int)N, s);
+    });
+    return e == hipSuccess ? ok() : hip_fail(e, "complex decode step launch");
+}
+
+// ---------------------------------------------------------------------------
 // Backward.
 
 int bwd_impl(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
@@ -636,6 +781,18 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, cons
                  void *stream) {
     return bwd_impl(x, delta, delta_bias, A, B, C, D, h_init, dy, dh_final, dx, ddelta, ddelta_bias, dA, dB, dC,
                     dD, dh_init, Bsz, L, Dm, N, dtype, flags, stream);
+}
+
+int ssm_scan_complex_fwd(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+                         const void *C, const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz,
+                         int64_t L, int64_t Dm, int64_t N, int dtype, unsigned flags, void *stream) {
+    return cplx_impl(x, delta, delta_bias, A, B, C, D, h_init, y, h_final, Bsz, L, Dm, N, dtype, flags, stream);
+}
+
+int ssm_step_complex(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+                     const void *C, const float *D, float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
+                     unsigned flags, void *stream) {
+    return cplx_step_impl(x, delta, delta_bias, A, B, C, D, h, y, Bsz, Dm, N, dtype, flags, stream);
 }
 
 int ssm_step(const void *x, const void *delta, const float *A, const void *B, const void *C,

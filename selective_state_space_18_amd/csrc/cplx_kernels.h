@@ -1,0 +1,417 @@
+// Selective scan with complex diagonal A for gfx950: templates shared by
+// cplx_bf16.hip and cplx_f32.hip.
+//
+// The bitig.info page on Mamba-3 (section "Karmasik Degerli Durum
+// Guncellemesi") describes a state update with complex eigenvalues, which
+// rotate as well as decay.  Per batch row b, channel d, state n, with
+// A[d,n] = a + i w, a complex state h and real x, delta, B_t, C_t, D, y:
+//   Abar = exp(delta A),  Bbar = (Abar - 1)/A * B_t[n]  (or delta B_t[n], Euler),
+//   h_t = Abar h_{t-1} + Bbar x_t,   y_t = sum_n C_t[n] Re(h_t[n]) + D x_t.
+//
+// The work is laid out as in the real scan (scan_kernels.h): one lane per
+// channel with the N complex states in registers, B_t/C_t rows as scalar
+// operands, time cut into segments joined by an aggregate pass, a carry pass
+// (the decay of a segment is exp(A * sum(delta))) and an output pass.  There
+// is no structured fast path: every element takes one exp and one sin/cos pair.
+#pragma once
+
+#include "scan_kernels.h"
+
+namespace ssm {
+
+namespace {
+
+// cos and sin of an angle, and exp of a real part.
+//  fp32: the angle is reduced to revolutions in [0, 1) and fed to v_sin/v_cos
+//        (which take revolutions); exp2 on the transcendental unit.
+//  fp64: ocml sin, cos, exp.
+__device__ __forceinline__ void cplx_exp(float zr, float zi, float &mag, float &c, float &s, float &em1) {
+    constexpr float kInv2Pi = 0.15915494309189535f;
+    const float rev = __builtin_amdgcn_fractf(zi * kInv2Pi);
+    c = __builtin_amdgcn_cosf(rev);
+    s = __builtin_amdgcn_sinf(rev);
+    em1 = expm1_and_exp(zr, mag);
+}
+__device__ __forceinline__ void cplx_exp(double zr, double zi, double &mag, double &c, double &s, double &em1) {
+    c = cos(zi);
+    s = sin(zi);
+    em1 = expm1(zr);
+    mag = em1 + 1.0;
+}
+
+// Abar - 1 = (e^a cos w - 1) + i e^a sin w, with the real part as
+// expm1(a) cos w + (cos w - 1); fp64 writes cos w - 1 as -2 sin^2(w/2).
+__device__ __forceinline__ float cplx_cos_m1(float zi, float c) {
+    (void)zi;
+    return c - 1.0f;
+}
+__device__ __forceinline__ double cplx_cos_m1(double zi, double c) {
+    (void)c;
+    const double h = sin(0.5 * zi);
+    return -2.0 * h * h;
+}
+
+template <int N, typename Acc>
+struct CplxConst {
+    Acc ar[N], ai[N];  // A (a tiny real stand-in for |A| ~ 0)
+    Acc wr[N], wi[N];  // 1 / A
+    __device__ __forceinline__ explicit CplxConst(const float *A2) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            Acc a = (Acc)A2[2 * n], w = (Acc)A2[2 * n + 1];
+            if (abs_(a) < (Acc)(-kTinyA) && abs_(w) < (Acc)(-kTinyA)) {
+                a = (Acc)kTinyA;
+                w = 0;
+            }
+            ar[n] = a;
+            ai[n] = w;
+            const Acc den = a * a + w * w;
+            wr[n] = a / den;
+            wi[n] = -w / den;
+        }
+    }
+};
+
+// One step of one channel; returns sum_n C_n Re(h_n) (kOut).
+template <int N, bool kOut, bool kEuler, typename Acc>
+__device__ __forceinline__ Acc cplx_step(const CplxConst<N, Acc> &cc, const Acc (&row)[2 * N], Acc xv, Acc dv,
+                                         Acc (&hr)[N], Acc (&hi)[N]) {
+    Acc yv = 0;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const Acc zr = dv * cc.ar[n], zi = dv * cc.ai[n];
+        Acc mag, c, s, em1;
+        cplx_exp(zr, zi, mag, c, s, em1);
+        const Acc abr = mag * c, abi = mag * s;
+        const Acc u = row[n] * xv;
+        Acc br, bi;
+        if constexpr (kEuler) {
+            br = dv * u;
+            bi = 0;
+        } else {
+            const Acc er = fma_(em1, c, cplx_cos_m1(zi, c));
+            const Acc ei = abi;
+            br = (er * cc.wr[n] - ei * cc.wi[n]) * u;
+            bi = (er * cc.wi[n] + ei * cc.wr[n]) * u;
+        }
+        const Acc r = hr[n], m = hi[n];
+        hr[n] = fma_(abr, r, fma_(-abi, m, br));
+        hi[n] = fma_(abr, m, fma_(abi, r, bi));
+        if constexpr (kOut) yv = fma_(row[N + n], hr[n], yv);
+    }
+    return yv;
+}
+
+// B/C rows in the arithmetic type (unscaled).
+template <typename T, int N>
+__global__ __launch_bounds__(kBlock) void cplx_bc_prep_kernel(const T *__restrict__ B, const T *__restrict__ C,
+                                                              typename AccOf<T>::type *__restrict__ bc, int64_t rows) {
+    typedef typename AccOf<T>::type Acc;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= rows * N) return;
+    const int64_t r = i / N;
+    const int n = (int)(i - r * N);
+    bc[r * (2 * N) + n] = (Acc)to_f32(B[i]);
+    bc[r * (2 * N) + N + n] = (Acc)to_f32(C[i]);
+}
+
+// kOut = false: aggregate over segments 0..S-2 (from zero; stores the end
+// state and the sum of delta).  kOut = true: output over all segments.
+// Scratch: agg [S-1][2N+1][B*D], gin [S][2N][B*D] (re of state n at 2n,
+// im at 2n+1, the delta sum at 2N).
+template <typename T, int N, bool kOut, bool kEuler, bool kPre>
+__global__ __launch_bounds__(kBlock) void cplx_segment_kernel(ScanParams p) {
+    typedef typename AccOf<T>::type Acc;
+    const int blocks_per_seg = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int s = lb / blocks_per_seg;
+    const int wave = uniform((int)threadIdx.x / kWave);
+    const int tile = (lb - s * blocks_per_seg) * p.waves_per_block + wave;
+    if (wave >= p.waves_per_block || tile >= p.n_tiles) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t b = tile / p.tiles_per_b;
+    const int64_t d0 = (int64_t)(tile - b * p.tiles_per_b) * kWave;
+    const bool active = d0 + lane < p.Dm;
+    const int64_t d = active ? d0 + lane : d0;
+    const int64_t ch = b * p.Dm + d;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t t0 = (int64_t)s * p.seg_len;
+    const int nsteps = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
+
+    const CplxConst<N, Acc> cc(p.A + d * 2 * N);
+    const Acc Dd = (Acc)p.D[d];
+    const Acc bias = (kPre && p.delta_bias != nullptr) ? (Acc)p.delta_bias[d] : (Acc)0;
+    const bool soft = p.delta_softplus != 0;
+
+    Acc hr[N], hi[N];
+    if (kOut && p.S > 1) {
+        const Acc *gin = static_cast<const Acc *>(p.gin);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            hr[n] = gin[((int64_t)s * 2 * N + 2 * n) * BD + ch];
+            hi[n] = gin[((int64_t)s * 2 * N + 2 * n + 1) * BD + ch];
+        }
+    } else if (kOut && p.h_init != nullptr) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            hr[n] = (Acc)p.h_init[(ch * N + n) * 2];
+            hi[n] = (Acc)p.h_init[(ch * N + n) * 2 + 1];
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) hr[n] = hi[n] = 0;
+    }
+
+    const int64_t off = (b * p.L + t0) * p.Dm + d0;
+    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
+    const int32_t span = nsteps * row;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const T *>(p.x) + off, span);
+    const __amdgpu_buffer_rsrc_t rdl = make_rsrc(static_cast<const T *>(p.delta) + off, span);
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(kOut ? static_cast<const T *>(p.y) + off : static_cast<const T *>(p.x) + off, kOut ? span : 0);
+    const int32_t voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
+    const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
+
+    constexpr int G = kPrefetch;
+    T xc[G], dc[G], xn[G], dn[G];
+    auto load = [&](int tb, T(&xs)[G], T(&ds)[G]) {
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int t = tb + k;
+            const int so = (t < nsteps - 1 ? t : nsteps - 1) * row;
+            xs[k] = buf_load<T>(rx, voff, so);
+            ds[k] = buf_load<T>(rdl, voff, so);
+        }
+    };
+    Acc lam = 0;
+    load(0, xc, dc);
+    for (int tb = 0; tb < nsteps; tb += G) {
+        load(tb + G, xn, dn);
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int t = tb + k;
+            if (t < nsteps) {
+                Acc rw[2 * N];
+                load_row<N>(rw, bcp + (int64_t)t * (2 * N));
+                const Acc xv = (Acc)to_f32(xc[k]);
+                Acc dv = (Acc)to_f32(dc[k]);
+                if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
+                const Acc yv = cplx_step<N, kOut, kEuler>(cc, rw, xv, dv, hr, hi);
+                if constexpr (kOut)
+                    buf_store(from_acc<T>(fma_(Dd, xv, yv)), ry, voff, t * row);
+                else
+                    lam += dv;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            xc[k] = xn[k];
+            dc[k] = dn[k];
+        }
+    }
+    if (!active) return;
+    if constexpr (!kOut) {
+        Acc *a = static_cast<Acc *>(p.agg) + (int64_t)s * (2 * N + 1) * BD + ch;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            a[(int64_t)(2 * n) * BD] = hr[n];
+            a[(int64_t)(2 * n + 1) * BD] = hi[n];
+        }
+        a[(int64_t)(2 * N) * BD] = lam;
+    } else if (s == p.S - 1 && p.h_final != nullptr) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            p.h_final[(ch * N + n) * 2] = (float)hr[n];
+            p.h_final[(ch * N + n) * 2 + 1] = (float)hi[n];
+        }
+    }
+}
+
+// Carry: one thread per (state n, channel): entering state of s+1 =
+// exp(A * sum(delta over s)) * entering state of s + end state of s.
+template <typename Acc, int N>
+__global__ __launch_bounds__(kBlock) void cplx_carry_kernel(ScanParams p) {
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= BD * N) return;
+    const int n = (int)(i / BD);
+    const int64_t ch = i - (int64_t)n * BD;
+    const int64_t d = ch % p.Dm;
+    const Acc a = (Acc)p.A[(d * N + n) * 2], w = (Acc)p.A[(d * N + n) * 2 + 1];
+    Acc cr = 0, ci = 0;
+    if (p.h_init) {
+        cr = (Acc)p.h_init[(ch * N + n) * 2];
+        ci = (Acc)p.h_init[(ch * N + n) * 2 + 1];
+    }
+    const Acc *agg = static_cast<const Acc *>(p.agg);
+    Acc *gin = static_cast<Acc *>(p.gin);
+    const int64_t sa = (int64_t)(2 * N + 1) * BD, sg = (int64_t)(2 * N) * BD;
+    gin[(int64_t)(2 * n) * BD + ch] = cr;
+    gin[(int64_t)(2 * n + 1) * BD + ch] = ci;
+    for (int s = 0; s + 1 < p.S; ++s) {
+        const Acc lam = agg[(int64_t)s * sa + (int64_t)(2 * N) * BD + ch];
+        const Acc gr = agg[(int64_t)s * sa + (int64_t)(2 * n) * BD + ch];
+        const Acc gi = agg[(int64_t)s * sa + (int64_t)(2 * n + 1) * BD + ch];
+        Acc mag, c, sn, em1;
+        cplx_exp(a * lam, w * lam, mag, c, sn, em1);
+        const Acc er = mag * c, ei = mag * sn;
+        const Acc nr = fma_(er, cr, fma_(-ei, ci, gr));
+        const Acc ni = fma_(er, ci, fma_(ei, cr, gi));
+        cr = nr;
+        ci = ni;
+        gin[(int64_t)(s + 1) * sg + (int64_t)(2 * n) * BD + ch] = cr;
+        gin[(int64_t)(s + 1) * sg + (int64_t)(2 * n + 1) * BD + ch] = ci;
+    }
+}
+
+// Decode step: Q lanes per channel, each owning 2 complex states (16 bytes)
+// of the state row, so a wave-wide access is 1 KiB contiguous; y is summed
+// across the Q lanes with shuffles.
+template <typename T, int N, bool kPrecise>
+__global__ __launch_bounds__(kBlock) void cplx_step_kernel(StepParams p) {
+    constexpr int SPL = N >= 2 ? 2 : 1;  // complex states per lane
+    constexpr int Q = N / SPL;
+    typedef float Acc;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t ch = i / Q;
+    const int j = (int)(i - ch * Q);
+    if (ch >= BD) return;
+    const int64_t b = ch / p.Dm, d = ch - b * p.Dm;
+    Acc dv = to_f32(static_cast<const T *>(p.delta)[ch]);
+    if (p.delta_bias != nullptr || p.delta_softplus) {
+        const float v = dv + (p.delta_bias != nullptr ? p.delta_bias[d] : 0.f);
+        dv = p.delta_softplus ? (kPrecise ? softplus_precise(v) : softplus_(v)) : v;
+    }
+    const Acc xv = to_f32(static_cast<const T *>(p.x)[ch]);
+    float *hp = p.h + (ch * N + j * SPL) * 2;
+    Acc yv = 0;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+        const int n = j * SPL + k;
+        float a = p.A[(d * N + n) * 2], w = p.A[(d * N + n) * 2 + 1];
+        if (__builtin_fabsf(a) < -kTinyA && __builtin_fabsf(w) < -kTinyA) {
+            a = kTinyA;
+            w = 0.f;
+        }
+        const float zr = dv * a, zi = dv * w;
+        float mag, c, s, em1;
+        if constexpr (kPrecise) {
+            c = cosf(zi);
+            s = sinf(zi);
+            em1 = expm1f(zr);
+            mag = em1 + 1.f;
+        } else {
+            cplx_exp(zr, zi, mag, c, s, em1);
+        }
+        const float abr = mag * c, abi = mag * s;
+        const float u = to_f32(static_cast<const T *>(p.B)[b * N + n]) * xv;
+        float br, bi;
+        if (p.euler_b) {
+            br = dv * u;
+            bi = 0.f;
+        } else {
+            const float hs = kPrecise ? sinf(0.5f * zi) : 0.f;
+            const float cm1 = kPrecise ? -2.f * hs * hs : c - 1.f;
+            const float er = __builtin_fmaf(em1, c, cm1), ei = abi;
+            const float den = a * a + w * w;
+            const float wr = a / den, wi = -w / den;
+            br = (er * wr - ei * wi) * u;
+            bi = (er * wi + ei * wr) * u;
+        }
+        const float r = hp[2 * k], m = hp[2 * k + 1];
+        const float nr = __builtin_fmaf(abr, r, __builtin_fmaf(-abi, m, br));
+        const float ni = __builtin_fmaf(abr, m, __builtin_fmaf(abi, r, bi));
+        hp[2 * k] = nr;
+        hp[2 * k + 1] = ni;
+        yv = __builtin_fmaf(to_f32(static_cast<const T *>(p.C)[b * N + n]), nr, yv);
+    }
+#pragma unroll
+    for (int off = 1; off < Q; off <<= 1) yv += __shfl_xor(yv, off, Q);
+    if (j == 0) static_cast<T *>(p.y)[ch] = from_acc<T>(__builtin_fmaf(p.D[d], xv, yv));
+}
+
+template <typename T, int N, bool kOut>
+void cplx_launch_segments(const ScanParams &p, unsigned grid, hipStream_t s) {
+    const bool pre = p.delta_bias != nullptr || p.delta_softplus != 0;
+    if (p.euler_b) {
+        if (pre)
+            hipLaunchKernelGGL((cplx_segment_kernel<T, N, kOut, true, true>), dim3(grid), dim3(kBlock), 0, s, p);
+        else
+            hipLaunchKernelGGL((cplx_segment_kernel<T, N, kOut, true, false>), dim3(grid), dim3(kBlock), 0, s, p);
+    } else {
+        if (pre)
+            hipLaunchKernelGGL((cplx_segment_kernel<T, N, kOut, false, true>), dim3(grid), dim3(kBlock), 0, s, p);
+        else
+            hipLaunchKernelGGL((cplx_segment_kernel<T, N, kOut, false, false>), dim3(grid), dim3(kBlock), 0, s, p);
+    }
+}
+
+template <typename T, int N>
+hipError_t cplx_pass_n(ScanPass pass, const ScanParams &p, hipStream_t s) {
+    typedef typename AccOf<T>::type Acc;
+    switch (pass) {
+        case ScanPass::kPrep: {
+            const int64_t work = p.Bsz * p.L * N;
+            if (work == 0) return hipSuccess;
+            hipLaunchKernelGGL((cplx_bc_prep_kernel<T, N>), dim3((unsigned)((work + kBlock - 1) / kBlock)),
+                               dim3(kBlock), 0, s, static_cast<const T *>(p.B), static_cast<const T *>(p.C),
+                               static_cast<Acc *>(p.bc), p.Bsz * p.L);
+            break;
+        }
+        case ScanPass::kAggregate:
+        case ScanPass::kOutput: {
+            const bool out = pass == ScanPass::kOutput;
+            const int bps = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
+            const int nseg = out ? p.S : p.S - 1;
+            if (nseg <= 0 || bps == 0) return hipSuccess;
+            const unsigned grid = (unsigned)bps * (unsigned)nseg;
+            if (out)
+                cplx_launch_segments<T, N, true>(p, grid, s);
+            else
+                cplx_launch_segments<T, N, false>(p, grid, s);
+            break;
+        }
+        case ScanPass::kCarry: {
+            const int64_t work = p.Bsz * p.Dm * N;
+            if (work == 0 || p.S <= 1) return hipSuccess;
+            hipLaunchKernelGGL((cplx_carry_kernel<Acc, N>), dim3((unsigned)((work + kBlock - 1) / kBlock)),
+                               dim3(kBlock), 0, s, p);
+            break;
+        }
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t cplx_pass(ScanPass pass, const ScanParams &p, int N, hipStream_t s) {
+    switch (N) {
+        case 1: return cplx_pass_n<T, 1>(pass, p, s);
+        case 2: return cplx_pass_n<T, 2>(pass, p, s);
+        case 4: return cplx_pass_n<T, 4>(pass, p, s);
+        case 8: return cplx_pass_n<T, 8>(pass, p, s);
+        case 16: return cplx_pass_n<T, 16>(pass, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, bool kPrecise>
+hipError_t cplx_step_launch(const StepParams &p, int N, hipStream_t s) {
+    const int64_t BD = p.Bsz * p.Dm;
+    if (BD == 0) return hipSuccess;
+    const int Q = N >= 2 ? N / 2 : 1;
+    const unsigned grid = (unsigned)((BD * Q + kBlock - 1) / kBlock);
+    switch (N) {
+        case 1: hipLaunchKernelGGL((cplx_step_kernel<T, 1, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((cplx_step_kernel<T, 2, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((cplx_step_kernel<T, 4, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
+        case 8: hipLaunchKernelGGL((cplx_step_kernel<T, 8, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
+        case 16: hipLaunchKernelGGL((cplx_step_kernel<T, 16, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+}  // namespace ssm

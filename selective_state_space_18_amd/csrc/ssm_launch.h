@@ -79,6 +79,15 @@ struct BwdParams {
 
 enum class BwdPass { kAggregate, kCarry, kMain, kReduce };
 
+// Complex diagonal A (cplx_kernels.h).  ScanParams as for the real scan, with
+// A [Dm][N][2], h_init/h_final [Bsz][Dm][N][2] as (re, im) pairs and scratch
+// bc [Bsz*L][2N], agg [S-1][2N+1][Bsz*Dm], gin [S][2N][Bsz*Dm] (Acc).
+// StepParams likewise (h [Bsz][Dm][N][2]).
+hipError_t cplx_pass_f32(ScanPass pass, const ScanParams &p, int N, hipStream_t s);
+hipError_t cplx_pass_bf16(ScanPass pass, const ScanParams &p, int N, hipStream_t s);
+hipError_t cplx_step_f32(const StepParams &p, int N, hipStream_t s);
+hipError_t cplx_step_bf16(const StepParams &p, int N, hipStream_t s);
+
 // Segment length the backward kernels are built for (the plan must use it).
 int bwd_segment_len(int dtype);
 hipError_t bwd_pass_f32(BwdPass pass, const BwdParams &q, int N, hipStream_t s);

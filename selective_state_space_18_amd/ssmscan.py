@@ -33,7 +33,8 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_B
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_strerror",
            "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
            "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
-           "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd")
+           "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd", "ssm_scan_complex_fwd",
+           "ssm_step_complex")
 
 
 class SSMError(RuntimeError):
@@ -62,6 +63,10 @@ def lib():
     L.ssm_scan_varlen_fwd.restype = ctypes.c_int
     L.ssm_scan_fused_fwd.argtypes = [_vp] * 8 + [_i64] + [_vp] * 3 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_scan_fused_fwd.restype = ctypes.c_int
+    L.ssm_scan_complex_fwd.argtypes = [_vp] * 10 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
+    L.ssm_scan_complex_fwd.restype = ctypes.c_int
+    L.ssm_step_complex.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint, _vp]
+    L.ssm_step_complex.restype = ctypes.c_int
     L.ssm_scan_bwd.argtypes = [_vp] * 18 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_scan_bwd.restype = ctypes.c_int
     L.ssm_step_fused.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint, _vp]
@@ -360,6 +365,82 @@ def scan_bwd(x, delta, A, B, C, D, dy, h_init=None, dh_final=None, delta_bias=No
                                 _flags(delta_softplus, euler_b), _stream(dev))
     _check(rc, "ssm_scan_bwd")
     return o
+
+
+def _pairs(t, name, shape, dev):
+    """A complex64 tensor, or a float32 tensor with a trailing (re, im) axis,
+    as the float32 (re, im) view the library takes."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype == torch.complex64:
+        t = torch.view_as_real(t)
+    _need(t, name, (*shape, 2), torch.float32, dev)
+    return t
+
+
+def scan_complex_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, want_state=True,
+                     delta_bias=None, delta_softplus=False, euler_b=False):
+    """ssm_scan_complex_fwd: scan with complex diagonal A.
+
+    A: complex64 [Dm, N] (or float32 [Dm, N, 2]); h_init: complex64 [Bsz, Dm, N]
+    or None; everything else as scan_fwd.  Returns (y [Bsz, L, Dm] real,
+    h_final complex64 [Bsz, Dm, N] or None)."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (Bsz, L, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, L, Dm), dt, dev)
+    A2 = _pairs(A, "A", (Dm, N), dev)
+    _need(B, "B", (Bsz, L, N), dt, dev)
+    _need(C, "C", (Bsz, L, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    _bias(delta_bias, Dm, dev)
+    hi2 = None if h_init is None else _pairs(h_init, "h_init", (Bsz, Dm, N), dev)
+    if y is None:
+        y = torch.empty((Bsz, L, Dm), dtype=dt, device=dev)
+    _need(y, "y", (Bsz, L, Dm), dt, dev)
+    if h_final is None and want_state:
+        h_final = torch.empty((Bsz, Dm, N), dtype=torch.complex64, device=dev)
+    hf2 = None if h_final is None else _pairs(h_final, "h_final", (Bsz, Dm, N), dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_complex_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), _ptr(A2), _ptr(B), _ptr(C),
+                                        _ptr(D), _ptr(hi2), _ptr(y), _ptr(hf2), Bsz, L, Dm, N, code,
+                                        _flags(delta_softplus, euler_b), _stream(dev))
+    _check(rc, "ssm_scan_complex_fwd")
+    return y, h_final
+
+
+def step_complex(x, delta, A, B, C, D, h, y=None, delta_bias=None, delta_softplus=False, euler_b=False):
+    """ssm_step_complex: one decode step with complex A; h complex64
+    [Bsz, Dm, N] (or float32 [..., 2]) is updated in place.  Returns y."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, Dm = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (Bsz, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, Dm), dt, dev)
+    A2 = _pairs(A, "A", (Dm, N), dev)
+    _need(B, "B", (Bsz, N), dt, dev)
+    _need(C, "C", (Bsz, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    _bias(delta_bias, Dm, dev)
+    h2 = _pairs(h, "h", (Bsz, Dm, N), dev)
+    if y is None:
+        y = torch.empty((Bsz, Dm), dtype=dt, device=dev)
+    _need(y, "y", (Bsz, Dm), dt, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_step_complex(_ptr(x), _ptr(delta), _ptr(delta_bias), _ptr(A2), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(h2), _ptr(y), Bsz, Dm, N, code, _flags(delta_softplus, euler_b),
+                                    _stream(dev))
+    _check(rc, "ssm_step_complex")
+    return y
 
 
 def step_fused(x, delta, A, B, C, D, h, y=None, delta_bias=None, delta_softplus=False, euler_b=False):

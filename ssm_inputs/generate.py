@@ -123,6 +123,17 @@ def step_tokens(cfg: StepConfig, state: Dict[str, torch.Tensor], n_tokens: int) 
     return out
 
 
+def complex_A(Dm: int, N: int, seed: int, device="cpu") -> torch.Tensor:
+    """Complex diagonal A [Dm, N] (complex64): real part -exp(N(0, 0.5)),
+    imaginary part pi * n * (1 + 0.1 N(0, 1)) -- decaying oscillators whose
+    frequencies grow with the state index (draw order: real, then imaginary)."""
+    g = _gen(torch.device(device), seed)
+    re = -torch.exp(_normal((Dm, N), g, torch.device(device), 0.5))
+    n = torch.arange(N, device=device, dtype=torch.float32).unsqueeze(0)
+    im = torch.pi * n * (1.0 + 0.1 * _normal((Dm, N), g, torch.device(device)))
+    return torch.complex(re, im)
+
+
 def packed_lengths(nseq: int, mean_len: float, seed: int, p_empty: float = 0.0, sigma: float = 1.0,
                    max_len: int = 0) -> List[int]:
     """Lengths of ``nseq`` sequences for a packed (variable-length) call.
