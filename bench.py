@@ -48,6 +48,7 @@ def log(*a):
 KERNEL_SOURCES = {
     "scan": ("scan_kernels.h", "ssm_device.h", "ssm_launch.h"),
     "step": ("step_kernel.hip", "ssm_device.h", "ssm_launch.h"),
+    "bwd": ("bwd_kernels.h", "scan_kernels.h", "ssm_device.h", "ssm_launch.h"),
 }
 
 
