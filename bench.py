@@ -8,14 +8,16 @@ The JSON line reports elements/s (B*L*D*N per second), the achieved
 algorithmic HBM bandwidth, the roofline of the dominant kernel, the fp64 CPU
 oracle timed on a bounded sample of the same workload, and -- under
 "secondary" -- the long-context scan, the scan options (fused delta
-activation, Euler input term), a packed variable-length prefill and the
-decode step.
+activation, Euler input term), a packed variable-length prefill, the scan
+with complex A, the backward, the general-A path forced on the same layer
+and the decode step.  A measured device-copy rate is reported beside the
+8 TB/s specification.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
                     [--no-cpu-baseline] [--no-secondary]
     python bench.py --only decode      # one workload, for profiler runs
                                        # (scan, long, small, packed, options, backward,
-                                       #  complex, decode)
+                                       #  complex, general, decode)
     python bench.py --copy-calibration # plain copy of known size (for counters)
 """
 import argparse
@@ -170,6 +172,22 @@ def bench_options(torch, ss, generate, configs, steps):
                       "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
                       "config": dict(cfgd, input_term="Euler: delta * B")}
     return out
+
+
+def bench_general_path(torch, ss, generate, cfg, steps):
+    """The same layer with the structured-A fast path switched off, so every
+    state element takes its own exponential (the path a layer with arbitrary
+    real A runs)."""
+    ss.set_option(ss.SSM_OPT_FORCE_GENERAL, 1)
+    try:
+        ms, kern, S, seg = bench_scan(torch, ss, generate, cfg, steps, 2)
+    finally:
+        ss.set_option(ss.SSM_OPT_FORCE_GENERAL, 0)
+    roof, hbm, cfgd, kms = scan_record(cfg, ms, kern, S, seg, generate)
+    roof["kernel"] = "scan_segment_kernel (output pass, general A)"
+    return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
+            "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
+            "config": dict(cfgd, A="general path forced (one exp per state element)")}
 
 
 def bench_backward(torch, ss, generate, cfg, steps, warmup):
@@ -368,14 +386,14 @@ def cpu_baseline(torch, generate, cfg, target_s=10.0):
     dev = "cuda:0"
     inp = generate.scan_inputs(cfg, dev)
 
-    def run(nch):
+    def run(nch, nthreads=threads):
         stride = max(1, cfg.Dm // nch)
         idx = torch.arange(0, cfg.Dm, stride, device=dev)[:nch]
         f = lambda t: t.detach().to("cpu").to(torch.float64).numpy()
         args = (f(inp["x"].index_select(2, idx)), f(inp["delta"].index_select(2, idx)),
                 f(inp["A"].index_select(0, idx)), f(inp["B"]), f(inp["C"]), f(inp["D"].index_select(0, idx)))
         t0 = time.perf_counter()
-        oracle.scan(*args, threads=threads)
+        oracle.scan(*args, threads=nthreads)
         return time.perf_counter() - t0, len(idx)
 
     probe_ch = min(cfg.Dm, 2 * threads)
@@ -384,12 +402,29 @@ def cpu_baseline(torch, generate, cfg, target_s=10.0):
     nch = int(min(cfg.Dm, max(probe_ch, target_s * rate / (cfg.Bsz * cfg.L * cfg.N))))
     dt, n = run(nch)
     elems = cfg.Bsz * cfg.L * n * cfg.N
+    # one thread on 64 channels (about a second), for the per-core rate
+    dt1, n1 = run(min(cfg.Dm, 64), nthreads=1)
     del inp
     torch.cuda.empty_cache()
     _ = np
     return {"value": elems / dt, "unit": "elems/s", "cores": threads, "kind": "oracle",
             "sample": f"{cfg.name}: all {cfg.Bsz} rows x {cfg.L} steps, {n} of {cfg.Dm} channels "
-                      f"(every {max(1, cfg.Dm // nch)}th), fp64, {dt:.1f} s wall"}
+                      f"(every {max(1, cfg.Dm // nch)}th), fp64, {dt:.1f} s wall",
+            "one_thread": {"value": cfg.Bsz * cfg.L * n1 * cfg.N / dt1, "unit": "elems/s",
+                           "sample": f"{n1} channels, all rows and steps, {dt1:.1f} s wall"}}
+
+
+def copy_peak(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate (bytes read + bytes written per second) of
+    a plain torch copy: the practical HBM ceiling on this GPU, reported beside
+    the 8 TB/s specification."""
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    y = torch.empty_like(x)
+    ms = timed_loop(torch, lambda _i: y.copy_(x), reps, 2)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"achieved": round(2 * nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "what": f"torch copy of {nbytes >> 20} MiB, read + write bytes"}
 
 
 def copy_calibration(torch, nbytes=1 << 30):
@@ -411,7 +446,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
-                                       "complex"],
+                                       "complex", "general"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
@@ -443,6 +478,10 @@ def main():
         return
     if a.only == "complex":
         rec = bench_complex(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps, a.warmup)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "general":
+        rec = bench_general_path(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "backward":
@@ -505,8 +544,14 @@ def main():
                                              max(5, a.steps // 5), 2)
         sec["complex_A"] = bench_complex(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
         sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
+        sec["general_A_path"] = bench_general_path(torch, ss, generate, cfg, max(5, a.steps // 5))
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
                                      configs.DECODE_256x8192.n_tokens)
+        cp = copy_peak(torch)
+        out["copy_peak"] = cp
+        out["hbm"]["frac_of_copy_peak"] = round(out["hbm"]["achieved"] / cp["achieved"], 4)
+        dec = sec["decode"]
+        dec["roofline"]["frac_of_copy_peak"] = round(dec["roofline"]["achieved"] / cp["achieved"], 4)
         out["secondary"] = sec
     if a.only is None and not a.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample")
