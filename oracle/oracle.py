@@ -101,6 +101,36 @@ class Oracle:
             raise RuntimeError(f"ssm_oracle_scan failed with code {rc}")
         return y, hf
 
+    def scan_ssd(self, x, delta, A, B, C, D, head_dim: int, h0=None, threads: int = 0, delta_bias=None,
+                 delta_softplus: bool = False, euler_b: bool = False):
+        """The scan with one scalar decay per head (the state-space-duality form).
+
+        The bitig.info page on Mamba-3 (section "Karmasik Degerli Durum
+        Guncellemesi") says Mamba-2 reduced the state transition to real
+        scalars; the "Mamba SSM Nedir?" page (section "Mamba-2 ve Guncel
+        Gelismeler") states that model's equivalence with a masked attention.
+        Reading: channels form heads of ``head_dim`` consecutive channels; head
+        h has one real A[h] for all N states, one delta[b, t, h] per step and
+        one bias[h].  That is the selective scan with A[d, n] = A[h(d)] and
+        delta[b, t, d] = delta[b, t, h(d)], h(d) = d // head_dim, which is how
+        it is evaluated here.  Shapes: x [Bsz,L,Dm], delta [Bsz,L,H], A [H],
+        B, C [Bsz,L,N], D [Dm], delta_bias [H], h0 [Bsz,Dm,N].
+        Returns (y [Bsz,L,Dm], h_final [Bsz,Dm,N])."""
+        x = np.asarray(x)
+        Bsz, L, Dm = x.shape
+        P = int(head_dim)
+        if P <= 0 or Dm % P:
+            raise ValueError(f"oracle: Dm={Dm} is not a multiple of head_dim={P}")
+        H = Dm // P
+        N = np.asarray(B).shape[2]
+        delta = _f64(delta, (Bsz, L, H), "delta")
+        A = _f64(A, (H,), "A")
+        A_full = np.repeat(A, P)[:, None] * np.ones((1, N))
+        delta_full = np.repeat(delta, P, axis=2)
+        bias = None if delta_bias is None else np.repeat(_f64(delta_bias, (H,), "delta_bias"), P)
+        return self.scan(x, delta_full, A_full, B, C, D, h0=h0, threads=threads, delta_bias=bias,
+                         delta_softplus=delta_softplus, euler_b=euler_b)
+
     def scan_complex(self, x, delta, A, B, C, D, h0=None, threads: int = 0, delta_bias=None,
                      delta_softplus: bool = False, euler_b: bool = False):
         """Scan with complex diagonal A.  A: complex [Dm, N] (numpy complex or a
@@ -241,3 +271,7 @@ def scan_complex(x, delta, A, B, C, D, **opts):
 
 def step_complex(x, delta, A, B, C, D, h, **opts):
     return load().step_complex(x, delta, A, B, C, D, h, **opts)
+
+
+def scan_ssd(x, delta, A, B, C, D, head_dim, **opts):
+    return load().scan_ssd(x, delta, A, B, C, D, head_dim, **opts)

@@ -117,6 +117,45 @@ PACKED_2P8B_LAYER = PackedConfig("packed_prefill_l65536_d5120_n16", 65536, 5120,
                                  "s4d_real", "per_token", 0.25, mean_len=2048, max_len=16384,
                                  p_empty=0.05, h0_std=0.5, seed=5)
 
+@dataclass(frozen=True)
+class SsdConfig:
+    """A layer with a scalar decay per head (the state-space-duality form).
+
+    Channels form heads of ``head_dim`` consecutive channels.  Head h has one
+    real A[h] for all N states and its own delta per step; B_t and C_t are
+    shared by every head of a batch row.  Recipe: x ~ N(0,1) [Bsz,L,Dm];
+    delta per (b, t, h) from the per-token recipe with u_h ~ U[1e-3, 1e-1]
+    per head (or the raw projection output and its bias, "raw_softplus");
+    B, C ~ N(0,1) * bc_scale; D ~ N(0,1) per channel; A[h] = -exp(N(0, 0.5));
+    h_init ~ N(0, h0_std) when h0_std > 0.
+    """
+    name: str
+    Bsz: int
+    L: int
+    Dm: int
+    N: int
+    head_dim: int
+    dtype: str
+    delta_kind: str
+    bc_scale: float
+    h0_std: float
+    seed: int
+
+    def heads(self) -> int:
+        return self.Dm // self.head_dim
+
+    def elems(self) -> int:
+        return self.Bsz * self.L * self.Dm * self.N
+
+    def with_shape(self, **kw) -> "SsdConfig":
+        return replace(self, **kw)
+
+
+# The 2.8B-shaped layer width (80 heads of 64 channels) with the larger state
+# a scalar-decay layer affords (N = 128); B, C ~ N(0,1)/sqrt(N).
+SSD_LAYER = SsdConfig("ssd_layer_b4_l16384_d5120_n128_p64", 4, 16384, 5120, 128, 64, "bf16",
+                      "per_token", 128 ** -0.5, h0_std=0.0, seed=6)
+
 SCAN_CONFIGS = {c.name: c for c in (TINY_FP32, MAMBA130M_LAYER, MAMBA2P8B_LAYER,
                                     FUSED_2P8B_LAYER, LONG_CONTEXT_1M)}
 STEP_CONFIGS = {DECODE_256x8192.name: DECODE_256x8192}

@@ -16,7 +16,7 @@ from typing import Dict, List
 import numpy as np
 import torch
 
-from .configs import PackedConfig, ScanConfig, StepConfig
+from .configs import PackedConfig, ScanConfig, SsdConfig, StepConfig
 
 _DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
@@ -185,6 +185,45 @@ def packed_inputs(cfg: PackedConfig, device="cpu") -> Dict[str, torch.Tensor]:
         g = _gen(torch.device(device), cfg.seed + 1000)
         out["h_init"] = _normal((len(lengths), cfg.Dm, cfg.N), g, torch.device(device), cfg.h0_std)
     return out
+
+
+def ssd_inputs(cfg: SsdConfig, device="cpu", seed=None) -> Dict[str, torch.Tensor]:
+    """x, delta [Bsz,L,H], A [H], B, C, D [Dm] (and delta_bias [H], h_init)
+    for a layer with a scalar decay per head.  Draw order: x, delta noise,
+    u_h, B, C, D, A, h_init."""
+    device = torch.device(device)
+    g = _gen(device, cfg.seed if seed is None else seed)
+    sd = _DT[cfg.dtype]
+    Bsz, L, Dm, N, H = cfg.Bsz, cfg.L, cfg.Dm, cfg.N, cfg.heads()
+    x = _normal((Bsz, L, Dm), g, device).to(sd)
+    noise = _normal((Bsz, L, H), g, device, 0.5)
+    u = torch.rand((H,), generator=g, device=device, dtype=torch.float32) * (U_HI - U_LO) + U_LO
+    out = {}
+    if cfg.delta_kind == "raw_softplus":
+        delta = noise.to(sd)
+        out["delta_bias"] = inv_softplus(u)
+    elif cfg.delta_kind == "per_token":
+        delta = softplus(noise.add_(inv_softplus(u))).to(sd)
+    else:
+        raise ValueError(cfg.delta_kind)
+    del noise
+    B = _normal((Bsz, L, N), g, device, cfg.bc_scale).to(sd)
+    C = _normal((Bsz, L, N), g, device, cfg.bc_scale).to(sd)
+    D = _normal((Dm,), g, device)
+    A = -torch.exp(_normal((H,), g, device, 0.5))
+    out.update({"x": x, "delta": delta, "A": A, "B": B, "C": C, "D": D})
+    if cfg.h0_std > 0:
+        out["h_init"] = _normal((Bsz, Dm, N), g, device, cfg.h0_std)
+    return out
+
+
+def alg_bytes_ssd(cfg: SsdConfig) -> int:
+    """Minimum bytes of a scalar-decay layer call: x, delta, B, C, A, D (and
+    h_init) read once, y and h_final written once."""
+    s = 4 if cfg.dtype == "fp32" else 2
+    BLD = cfg.Bsz * cfg.L * cfg.Dm
+    return (2 * BLD * s + cfg.Bsz * cfg.L * cfg.heads() * s + 2 * cfg.Bsz * cfg.L * cfg.N * s
+            + 4 * cfg.heads() + 4 * cfg.Dm + (2 if cfg.h0_std > 0 else 1) * 4 * cfg.Bsz * cfg.Dm * cfg.N)
 
 
 def alg_bytes_scan(cfg: ScanConfig) -> int:

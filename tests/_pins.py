@@ -629,6 +629,61 @@ def check_complex_step_chain(orc, seed=24):
     assert np.max(np.abs(h - hf)) < 1e-13 * max(1.0, np.max(np.abs(hf)))
 
 
+
+# ---------------------------------------------------------------------------
+# scalar decay per head (state-space duality form)
+
+
+def check_ssd_duality(orc, seed=30):
+    """The scalar-decay layer equals its masked-attention form ("Mamba SSM
+    Nedir?" page, section "Mamba-2 ve Guncel Gelismeler": the SSM is a form of
+    attention).  Per row b and head h, with cum[t] = A[h] * sum_{r<=t} delta_r
+    and k_s the one-step input factor (Van Loan's matrix exponential for the
+    ZOH rule, delta_s for the Euler rule):
+        y[:, d]  = (G o Lmask) x[:, d] + D[d] x[:, d] + exp(cum) * (C h0[d])
+        G[t, s]  = (C_t . B_s) k_s,  Lmask[t, s] = exp(cum[t] - cum[s]) for s <= t, else 0
+        hL[d]    = exp(cum[L-1]) h0[d] + sum_s exp(cum[L-1] - cum[s]) k_s x_s[d] B_s
+    built as dense L x L matrices with numpy.  Covers a head with A = 0,
+    heads of several channels, the softplus/bias and Euler options, and h0."""
+    rng = np.random.default_rng(seed)
+    Bsz, L, H, P, N = 2, 37, 3, 2, 4
+    Dm = H * P
+    A = np.array([-0.7, 0.0, -2.5])
+    x = rng.standard_normal((Bsz, L, Dm))
+    B = rng.standard_normal((Bsz, L, N))
+    C = rng.standard_normal((Bsz, L, N))
+    D = rng.standard_normal(Dm)
+    h0 = rng.standard_normal((Bsz, Dm, N))
+    cases = [
+        (rng.uniform(0.01, 0.5, (Bsz, L, H)), None, False, False, None),
+        (rng.uniform(0.01, 0.5, (Bsz, L, H)), None, False, False, h0),
+        (0.5 * rng.standard_normal((Bsz, L, H)), rng.uniform(-3.0, 0.0, H), True, True, h0),
+        (rng.uniform(0.0, 0.3, (Bsz, L, H)), rng.uniform(0.0, 0.1, H), False, False, h0),
+    ]
+    for raw, bias, sp, eul, h in cases:
+        y, hf = orc.scan_ssd(x, raw, A, B, C, D, P, h0=h, delta_bias=bias, delta_softplus=sp, euler_b=eul)
+        y_ref = np.empty_like(x)
+        h_ref = np.empty((Bsz, Dm, N))
+        causal = np.tril(np.ones((L, L), dtype=bool))
+        for b in range(Bsz):
+            for hh in range(H):
+                v = raw[b, :, hh] + (0.0 if bias is None else bias[hh])
+                dt = np.logaddexp(0.0, v) if sp else v
+                cum = A[hh] * np.cumsum(dt)
+                k = dt.copy() if eul else np.array([vanloan_zoh(A[hh], t)[1] for t in dt])
+                G = (C[b] @ B[b].T) * k[None, :]
+                Lm = np.where(causal, np.exp(np.where(causal, cum[:, None] - cum[None, :], 0.0)), 0.0)
+                M = G * Lm
+                for d in range(hh * P, (hh + 1) * P):
+                    y_ref[b, :, d] = M @ x[b, :, d] + D[d] * x[b, :, d]
+                    h_ref[b, d] = (np.exp(cum[-1] - cum) * k * x[b, :, d]) @ B[b]
+                    if h is not None:
+                        y_ref[b, :, d] += np.exp(cum) * (C[b] @ h[b, d])
+                        h_ref[b, d] += np.exp(cum[-1]) * h[b, d]
+        assert rel_err(y, y_ref) < 1e-11, ("ssd y", rel_err(y, y_ref), sp, eul, h is None)
+        assert rel_err(hf, h_ref) < 1e-11, ("ssd h_final", rel_err(hf, h_ref), sp, eul, h is None)
+
+
 ALL_CHECKS = [
     check_golden,
     check_brute_force,
@@ -654,4 +709,5 @@ ALL_CHECKS = [
     check_complex_exact_for_constant_input,
     check_complex_lfilter,
     check_complex_step_chain,
+    check_ssd_duality,
 ]

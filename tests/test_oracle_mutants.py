@@ -129,3 +129,44 @@ def test_pins_catch_planted_mistake(tmp_path, mutant):
         except AssertionError:
             return  # caught
     pytest.fail(f"no pin caught the planted mistake '{name}'")
+
+
+# Mistakes in the Python front-end of the scalar-decay layer (head mapping and
+# per-head parameters), planted in a subclass of the real oracle.
+def _ssd_mutant(kind):
+    import numpy as np
+    import oracle
+
+    class Broken(oracle.Oracle):
+        def scan_ssd(self, x, delta, A, B, C, D, head_dim, h0=None, threads=0, delta_bias=None,
+                     delta_softplus=False, euler_b=False):
+            x = np.asarray(x)
+            Bsz, L, Dm = x.shape
+            P = int(head_dim)
+            H = Dm // P
+            N = np.asarray(B).shape[2]
+            A = np.asarray(A, dtype=np.float64)
+            delta = np.asarray(delta, dtype=np.float64)
+            rep = (lambda a, axis=0: np.tile(a, P) if axis == 0 else np.tile(a, (1, 1, P))) \
+                if kind == "heads_interleaved" else (lambda a, axis=0: np.repeat(a, P, axis=axis))
+            A_full = rep(A)[:, None] * np.ones((1, N))
+            delta_full = rep(delta, 2)
+            if kind == "delta_of_head_0":
+                delta_full = np.repeat(delta[:, :, :1], Dm, axis=2)
+            bias = None
+            if delta_bias is not None:
+                bias = np.repeat(np.asarray(delta_bias, dtype=np.float64), P)
+                if kind == "bias_ignored":
+                    bias = None
+            if kind == "A_of_head_0":
+                A_full = np.full((Dm, N), A[0])
+            return self.scan(x, delta_full, A_full, B, C, D, h0=h0, threads=threads, delta_bias=bias,
+                             delta_softplus=delta_softplus, euler_b=euler_b)
+
+    return Broken(threads=1)
+
+
+@pytest.mark.parametrize("kind", ["heads_interleaved", "delta_of_head_0", "bias_ignored", "A_of_head_0"])
+def test_pins_catch_ssd_front_end_mistake(kind):
+    with pytest.raises(AssertionError):
+        _pins.check_ssd_duality(_ssd_mutant(kind))
