@@ -9,15 +9,15 @@ algorithmic HBM bandwidth, the roofline of the dominant kernel, the fp64 CPU
 oracle timed on a bounded sample of the same workload, and -- under
 "secondary" -- the long-context scan, the scan options (fused delta
 activation, Euler input term), a packed variable-length prefill, the scan
-with complex A, the backward, the general-A path forced on the same layer
-and the decode step.  A measured device-copy rate is reported beside the
+with complex A, the backward, the general-A path forced on the same layer,
+the scalar-decay (state-space duality) layer and the decode step.  A measured device-copy rate is reported beside the
 8 TB/s specification.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
                     [--no-cpu-baseline] [--no-secondary]
     python bench.py --only decode      # one workload, for profiler runs
                                        # (scan, long, small, packed, options, backward,
-                                       #  complex, general, decode)
+                                       #  complex, general, ssd, decode)
     python bench.py --copy-calibration # plain copy of known size (for counters)
 """
 import argparse
@@ -34,6 +34,8 @@ METRIC = "selective-scan elems/s (B·L·D·N) + achieved HBM GB/s vs MI355X peak
 HBM_PEAK_GBPS = 8000.0
 # Non-packed fp32 FMA issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 2 flops.
 VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
+# Dense bf16 matrix-core peak of MI355X (no sparsity).
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 # Algorithmic fp32 flops per state element of the scan: z = delta*A, exp(z)-1,
 # divide by A, times B, times x, Abar*h + Bbar*x (FMA, 2), C*h + y (FMA, 2).
 SCAN_FLOPS_PER_ELEM = 9
@@ -188,6 +190,47 @@ def bench_general_path(torch, ss, generate, cfg, steps):
     return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
             "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
             "config": dict(cfgd, A="general path forced (one exp per state element)")}
+
+
+def bench_ssd(torch, ss, generate, cfg, steps, warmup):
+    """The scalar-decay layer (heads of 64 channels sharing A and delta, N =
+    128) in its chunked matrix form.  Algorithmic flops of the output pass per
+    (b, t, d): 2N for C H, 2N for the state update B^T (w x), Q + 1 for the
+    causal intra-chunk product (Q = 64 steps; the lower triangle of a Q x Q
+    matrix times x), plus (Q + 1) N / Dm for the shared G = C B^T."""
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name}")
+    inp = generate.ssd_inputs(cfg, dev)
+    y = torch.empty_like(inp["x"])
+    hf = torch.empty((cfg.Bsz, cfg.Dm, cfg.N), dtype=torch.float32, device=dev)
+
+    def fn(_i):
+        ss.scan_ssd_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], cfg.head_dim, y=y, h_final=hf)
+
+    log(f"[bench] timing {cfg.name}: {warmup} warmup + {steps} steps")
+    ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    del inp, y, hf
+    torch.cuda.empty_cache()
+    Q = 64
+    BLD = cfg.Bsz * cfg.L * cfg.Dm
+    flops_out = BLD * (4 * cfg.N + (Q + 1) + (Q + 1) * cfg.N / cfg.Dm)
+    out_ms = kern["ssd_output"]["avg_ms"]
+    alg = generate.alg_bytes_ssd(cfg)
+    mfma = flops_out / (out_ms * 1e-3) / 1e12
+    return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
+            "unit": "elems/s",
+            "hbm": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
+            "roofline": {"kernel": "ssd_chunk_kernel (output pass)", "bound": "mfma",
+                         "achieved": round(mfma, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(mfma / BF16_MFMA_PEAK_TFLOPS, 4), "avg_ms": round(out_ms, 5),
+                         "algorithmic_flops_per_launch": flops_out,
+                         "hbm_frac_at_algorithmic_bytes": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
+            "config": {"workload": cfg.name, "Bsz": cfg.Bsz, "L": cfg.L, "Dm": cfg.Dm, "N": cfg.N,
+                       "head_dim": cfg.head_dim, "storage": cfg.dtype,
+                       "A": "one real scalar per head, -exp(N(0, 0.5))", "delta": "per head, " + cfg.delta_kind,
+                       "input_term": "ZOH"}}
 
 
 def bench_backward(torch, ss, generate, cfg, steps, warmup):
@@ -446,7 +489,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
-                                       "complex", "general"],
+                                       "complex", "general", "ssd"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
@@ -478,6 +521,10 @@ def main():
         return
     if a.only == "complex":
         rec = bench_complex(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps, a.warmup)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "ssd":
+        rec = bench_ssd(torch, ss, generate, configs.SSD_LAYER, a.steps, a.warmup)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "general":
@@ -545,6 +592,7 @@ def main():
         sec["complex_A"] = bench_complex(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
         sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
         sec["general_A_path"] = bench_general_path(torch, ss, generate, cfg, max(5, a.steps // 5))
+        sec["ssd_layer"] = bench_ssd(torch, ss, generate, configs.SSD_LAYER, max(5, a.steps // 5), 2)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
                                      configs.DECODE_256x8192.n_tokens)
         cp = copy_peak(torch)

@@ -35,7 +35,7 @@
  *     propagate.
  *   - A pointer may be NULL only when its tensor has no elements.
  *   - Every pointer must be aligned to its element size.
- *   - Supported state sizes: N in {1, 2, 4, 8, 16}.
+ *   - Supported state sizes: N in {1, 2, 4, 8, 16} (ssm_scan_ssd_fwd: 32, 64, 128).
  *   - Thread safety: calls may come from several host threads.  Two calls that
  *     run concurrently on different streams of one device use separate
  *     library scratch memory (kept per device and stream).
@@ -204,6 +204,44 @@ int ssm_step_complex(const void *x, const void *delta, const float *delta_bias,
                      unsigned flags, void *stream);
 
 /*
+ * Scan with one scalar decay per head: the state-space-duality layer.  The
+ * bitig.info page on Mamba-3 (section "Karmasik Degerli Durum Guncellemesi")
+ * says Mamba-2 reduced the state transition to real scalars; the "Mamba SSM
+ * Nedir?" page (section "Mamba-2 ve Guncel Gelismeler") states that such an
+ * SSM equals a masked attention.  Channels form heads of head_dim consecutive
+ * channels; head h = d / head_dim has one real A[h] for all N states and one
+ * delta per step.  Per (b, d, n):
+ *   dt     = delta[b,t,h] (+ delta_bias[h], softplus with SSM_DELTA_SOFTPLUS)
+ *   Abar   = exp(dt * A[h])
+ *   Bbar   = (Abar - 1) / A[h] * B_t[n]    (dt * B_t[n] at A = 0 or with SSM_EULER_B)
+ *   h_t    = Abar * h_{t-1} + Bbar * x_t[d],   y_t[d] = sum_n C_t[n] h_t[d,n] + D[d] x_t[d]
+ * which is ssm_scan_fused_fwd with A[d,n] = A[h] and delta[b,t,d] = delta[b,t,h].
+ * bf16 storage evaluates it in its chunked matrix form on the matrix cores,
+ * exact up to rounding: per 64-step chunk, (C B^T masked by the decays) x for
+ * the steps inside the chunk plus C h for the state entering it.
+ *   x, y       : [Bsz][L][Dm]  dtype
+ *   delta      : [Bsz][L][H]   dtype, H = Dm / head_dim
+ *   delta_bias : [H] fp32, or NULL (0)
+ *   A          : [H] fp32
+ *   B, C       : [Bsz][L][N]   dtype, shared by all heads of a row
+ *   D          : [Dm] fp32
+ *   h_init     : [Bsz][Dm][N] fp32 or NULL (zero); may equal h_final
+ *   h_final    : [Bsz][Dm][N] fp32 or NULL
+ *   head_dim   : 64 (the only value supported); Dm must be a multiple of it
+ *   N          : 32, 64 or 128
+ * x, y, B, C, h_init and h_final must be 16-byte aligned.  bf16 storage
+ * multiplies bf16 operands exactly and splits fp32 operands into two bf16
+ * terms (about 2^-17 relative per product), accumulating in fp32; fp32
+ * storage evaluates the recurrence in fp64.  Other rules as
+ * ssm_scan_fused_fwd (dense batch only).
+ */
+int ssm_scan_ssd_fwd(const void *x, const void *delta, const float *delta_bias,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const float *h_init, void *y, float *h_final,
+                     int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int64_t head_dim,
+                     int dtype, unsigned flags, void *stream);
+
+/*
  * Backward of the scan: every input gradient for given output gradients.
  * The chain rule on the recurrence ("Mamba SSM Nedir?", section "Ayrik Zamana
  * Gecis"), as training needs it (section "Paralel Tarama Algoritmasi": the
@@ -321,7 +359,10 @@ typedef enum {
     SSM_K_BWD_CARRY = 7,        /* backward: adjoint entering each segment */
     SSM_K_BWD_MAIN = 8,         /* backward: gradients per segment */
     SSM_K_BWD_REDUCE = 9,       /* backward: dB, dC, dA, dD sums */
-    SSM_K_COUNT = 10
+    SSM_K_SSD_AGGREGATE = 10,   /* scalar-decay layer: per-segment end states */
+    SSM_K_SSD_CARRY = 11,       /* scalar-decay layer: states entering each segment */
+    SSM_K_SSD_OUTPUT = 12,      /* scalar-decay layer: y (and h_final) per chunk */
+    SSM_K_COUNT = 13
 } ssm_kernel_kind;
 
 int ssm_profile_read(double *total_ms, int64_t *launches, int n);

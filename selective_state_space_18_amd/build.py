@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libssmscan.so")
 
 ARCH = "gfx950"
 SOURCES = ["abi.cpp", "scan_f32.hip", "scan_f32_packed.hip", "scan_bf16.hip", "scan_bf16_packed.hip",
-           "scan_launch.hip", "step_kernel.hip", "bwd_f32.hip", "bwd_bf16.hip", "cplx_f32.hip", "cplx_bf16.hip"]
+           "scan_launch.hip", "step_kernel.hip", "bwd_f32.hip", "bwd_bf16.hip", "cplx_f32.hip", "cplx_bf16.hip",
+           "ssd_f32.hip", "ssd_bf16.hip"]
 
 # Packed-FP32 instructions are switched off for every device pass.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

@@ -558,6 +558,150 @@ int cplx_step_impl(const void *x, const void *delta, const float *delta_bias, co
 // ---------------------------------------------------------------------------
 // Backward.
 
+// ---------------------------------------------------------------------------
+// Scalar decay per head (state-space duality form).
+
+constexpr int64_t kSsdHeadDim = 64;
+constexpr int64_t kSsdChunk = 64;
+constexpr int64_t kSsdHeadsPerBlock = 2;
+// Blocks per CU the planner aims for: two 4-wave blocks fit on a CU at once,
+// and a few rounds of them smooth out the last round.
+constexpr int64_t kSsdBlocksPerCu = 4;
+
+bool ssd_supported_n(int64_t N) { return N == 32 || N == 64 || N == 128; }
+
+// Segments of whole 64-step chunks; SSM_OPT_SEGMENT_LEN (rounded up to a
+// chunk) overrides the automatic choice.
+void ssd_plan(int64_t Bsz, int64_t L, int64_t H, int cus, int *S, int64_t *seg_len) {
+    const int64_t nchunks = (L + kSsdChunk - 1) / kSsdChunk;
+    const int64_t rows = Bsz * ((H + kSsdHeadsPerBlock - 1) / kSsdHeadsPerBlock);
+    int64_t cps;
+    const int64_t forced = g_opt_segment_len.load();
+    if (nchunks <= 0 || rows <= 0) {
+        cps = 1;
+    } else if (forced > 0) {
+        cps = (forced + kSsdChunk - 1) / kSsdChunk;
+    } else {
+        const int64_t want = (kSsdBlocksPerCu * (cus > 0 ? cus : 256) + rows - 1) / rows;
+        const int64_t segs = want < nchunks ? (want > 0 ? want : 1) : nchunks;
+        cps = (nchunks + segs - 1) / segs;
+    }
+    if (cps < 1) cps = 1;
+    *seg_len = cps * kSsdChunk;
+    *S = nchunks > 0 ? (int)((nchunks + cps - 1) / cps) : 1;
+}
+
+int ssd_impl(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B, const void *C,
+             const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L, int64_t Dm,
+             int64_t N, int64_t head_dim, int dtype, unsigned flags, void *stream) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
+    if (flags & ~kKnownFlags) return fail(SSM_ERR_BAD_OPTION, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    if (!ssd_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 32, 64, 128", (long long)N);
+    if (head_dim != kSsdHeadDim)
+        return fail(SSM_ERR_BAD_DIM, "head_dim = %lld; supported: 64", (long long)head_dim);
+    if (Bsz < 0 || L < 0 || Dm < 0)
+        return fail(SSM_ERR_BAD_DIM, "negative size (Bsz=%lld, L=%lld, Dm=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm);
+    if (Dm % kSsdHeadDim != 0)
+        return fail(SSM_ERR_BAD_DIM, "Dm = %lld is not a multiple of head_dim = 64", (long long)Dm);
+    const int64_t H = Dm / kSsdHeadDim;
+    int64_t BL, BLD, BLH, BLN, BD, BDN;
+    if (!mul_ok(Bsz, L, &BL) || !mul_ok(BL, Dm, &BLD) || !mul_ok(BL, H, &BLH) || !mul_ok(BL, N, &BLN) ||
+        !mul_ok(Bsz, Dm, &BD) || !mul_ok(BD, N, &BDN) || Dm > ((int64_t)1 << 22) || Bsz > INT32_MAX / 2 ||
+        BDN > INT64_MAX / 16)
+        return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm, (long long)N);
+    const int64_t es = dtype_size(dtype);
+    const Arg in[] = {{x, BLD, es, "x"},        {delta, BLH, es, "delta"}, {A, H, 4, "A"},
+                      {B, BLN, es, "B"},        {C, BLN, es, "C"},         {D, Dm, 4, "D"},
+                      {delta_bias, delta_bias ? H : 0, 4, "delta_bias"}};
+    const Arg hi = {h_init, h_init ? BDN : 0, 4, "h_init"};
+    const Arg ya = {y, BLD, es, "y"};
+    const Arg hf = {h_final, h_final ? BDN : 0, 4, "h_final"};
+    int rc;
+    if ((rc = check_args(in, 7)) || (rc = check_args(&hi, 1)) || (rc = check_args(&ya, 1)) || (rc = check_args(&hf, 1)))
+        return rc;
+    const Arg vec[] = {in[0], in[3], in[4], hi, ya, hf};
+    for (const Arg &a : vec)
+        if (a.p != nullptr && (a.lo() % 16) != 0)
+            return fail(SSM_ERR_ALIGN, "%s (%p) is not 16-byte aligned", a.name, a.p);
+    if ((rc = check_output(ya, in, 7)) || (rc = check_output(ya, &hi, 1)) || (rc = check_output(hf, in, 7)) ||
+        (rc = check_output(hf, &ya, 1)))
+        return rc;
+    if (h_init != nullptr && h_final != nullptr && (const void *)h_init != (const void *)h_final && overlaps(hi, hf))
+        return fail(SSM_ERR_ALIAS, "h_init partially overlaps h_final");
+    if (BD == 0) return ok();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (L == 0) {
+        if (h_final == nullptr) return ok();
+        ssm::ScanParams z;
+        std::memset(&z, 0, sizeof z);
+        z.h_init = h_init;
+        z.h_final = h_final;
+        z.Bsz = Bsz;
+        z.Dm = Dm;
+        e = timed(SSM_K_STATE_INIT, s, [&] { return ssm::launch_state_init(z, (int)N, s); });
+        return e == hipSuccess ? ok() : hip_fail(e, "state init launch");
+    }
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int cus = 0;
+    if ((rc = device_cus(dev, &cus))) return rc;
+    ssm::SsdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x = x;
+    p.delta = delta;
+    p.B = B;
+    p.C = C;
+    p.A = A;
+    p.D = D;
+    p.delta_bias = delta_bias;
+    p.h_init = h_init;
+    p.y = y;
+    p.h_final = h_final;
+    p.Bsz = Bsz;
+    p.L = L;
+    p.Dm = Dm;
+    p.H = H;
+    p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+    p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
+    ssd_plan(Bsz, L, H, cus, &p.S, &p.seg_len);
+    if (dtype == SSM_F32) {  // the fp64 recurrence runs over all of time at once
+        p.S = 1;
+        p.seg_len = L;
+    }
+    const int64_t blocks = Bsz * ((H + kSsdHeadsPerBlock - 1) / kSsdHeadsPerBlock) * p.S;
+    if (blocks > INT32_MAX / 2)
+        return fail(SSM_ERR_BAD_DIM, "too many blocks (%lld); use a longer segment", (long long)blocks);
+    const size_t agg_bytes = p.S > 1 ? align256((size_t)(p.S - 1) * BDN * 4) : 0;
+    const size_t dec_bytes = p.S > 1 ? align256((size_t)(p.S - 1) * Bsz * H * 4) : 0;
+    const size_t gin_bytes = p.S > 1 ? align256((size_t)p.S * BDN * 4) : 0;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if (p.S > 1) {
+        void *ws = nullptr;
+        if ((rc = workspace(dev, s, agg_bytes + dec_bytes + gin_bytes, &ws))) return rc;
+        char *base = static_cast<char *>(ws);
+        p.agg = reinterpret_cast<float *>(base);
+        p.dec = reinterpret_cast<float *>(base + agg_bytes);
+        p.gin = reinterpret_cast<float *>(base + agg_bytes + dec_bytes);
+    }
+    const int n = (int)N;
+    auto pass = [&](ssm::SsdPass ps) {
+        return dtype == SSM_F32 ? ssm::ssd_pass_f32(ps, p, n, s) : ssm::ssd_pass_bf16(ps, p, n, s);
+    };
+    if (p.S > 1) {
+        if ((e = timed(SSM_K_SSD_AGGREGATE, s, [&] { return pass(ssm::SsdPass::kAggregate); })) != hipSuccess)
+            return hip_fail(e, "scalar-decay aggregate launch");
+        if ((e = timed(SSM_K_SSD_CARRY, s, [&] { return pass(ssm::SsdPass::kCarry); })) != hipSuccess)
+            return hip_fail(e, "scalar-decay carry launch");
+    }
+    if ((e = timed(SSM_K_SSD_OUTPUT, s, [&] { return pass(ssm::SsdPass::kOutput); })) != hipSuccess)
+        return hip_fail(e, "scalar-decay output launch");
+    return ok();
+}
+
 int bwd_impl(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
              const void *C, const float *D, const float *h_init, const void *dy, const float *dh_final, void *dx,
              void *ddelta, float *ddelta_bias, float *dA, float *dB, float *dC, float *dD, float *dh_init,
@@ -787,6 +931,13 @@ int ssm_scan_complex_fwd(const void *x, const void *delta, const float *delta_bi
                          const void *C, const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz,
                          int64_t L, int64_t Dm, int64_t N, int dtype, unsigned flags, void *stream) {
     return cplx_impl(x, delta, delta_bias, A, B, C, D, h_init, y, h_final, Bsz, L, Dm, N, dtype, flags, stream);
+}
+
+int ssm_scan_ssd_fwd(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+                     const void *C, const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz,
+                     int64_t L, int64_t Dm, int64_t N, int64_t head_dim, int dtype, unsigned flags, void *stream) {
+    return ssd_impl(x, delta, delta_bias, A, B, C, D, h_init, y, h_final, Bsz, L, Dm, N, head_dim, dtype, flags,
+                    stream);
 }
 
 int ssm_step_complex(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,

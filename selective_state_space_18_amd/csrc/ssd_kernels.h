@@ -1,0 +1,470 @@
+// Scan with one scalar decay per head (the state-space-duality layer) in its
+// chunked matrix form on the gfx950 matrix cores.  Templates shared by
+// ssd_bf16.hip and ssd_f32.hip.
+//
+// The bitig.info page on Mamba-3 (section "Karmasik Degerli Durum
+// Guncellemesi") says Mamba-2 reduced the state transition to real scalars;
+// the "Mamba SSM Nedir?" page (section "Mamba-2 ve Guncel Gelismeler") states
+// that such an SSM equals a masked attention.  With heads of 64 channels, a
+// scalar a = A[h] and per-step dt_t of the head, inside a chunk of 64 steps
+// starting from the state H (N x 64, one column per channel):
+//   c_t    = a * (dt_0 + ... + dt_t)                (log of the decay so far)
+//   k_s    = (exp(a dt_s) - 1) / a                  (dt_s at a = 0, or Euler)
+//   y_t    = exp(c_t) C_t H + sum_{s<=t} (C_t . B_s) exp(c_t - c_s) k_s x_s + D x_t
+//   H_next = exp(c_63) H + sum_s B_s^T exp(c_63 - c_s) k_s x_s
+// Every exponent is <= 0 for a <= 0, so nothing overflows.  The four products
+// -- G = B C^T over N, (G o mask) x over the chunk, C H over N and B^T (w x)
+// over the chunk -- are 32x32 tiles of v_mfma_f32_32x32x16_bf16.  B, C and x
+// are exact bf16 operands; the fp32 operand of each product (the masked G,
+// the state H, the weighted x) is split into hi + lo bf16 halves, two
+// instructions, leaving about 2^-17 relative error per product.
+//
+// fp32 storage takes the recurrence itself in fp64 instead (one thread per
+// channel and 8 states): fp32 matrix instructions accumulate in fp32, whose
+// rounding does not keep the fp32 storage path's error bound.
+//
+// Layout of work: a block of 4 waves serves two heads of one batch row over a
+// segment of chunks; wave w takes head w/2 and channels 32 (w%2) .. +32 of
+// it.  Chunk inputs are staged in LDS (B and C by rows; B and x transposed,
+// so that every matrix operand is read as two 8- or 16-byte pieces per lane).
+// Time is cut into segments joined as in the diagonal scan: an aggregate pass
+// (end state of each segment from zero, and its total log decay), a carry
+// pass, and an output pass that reruns each segment from its entering state.
+#pragma once
+
+#include <type_traits>
+
+#include "ssm_device.h"
+#include "ssm_launch.h"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kSsdQ = 64;       // chunk length (steps)
+constexpr int kSsdP = 64;       // channels per head
+constexpr int kSsdHeads = 2;    // heads per block
+constexpr int kSsdBlock = 256;  // 4 waves
+constexpr int kSsdPad = 4;      // LDS row padding (elements)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// A matrix-operand fragment: 8 k-slots per lane.  For a K = 16 step starting
+// at k0, lane group g = lane / 32 holds k0 + 4g + (0..3) in slots 0..3 and
+// k0 + 8 + 4g + (0..3) in slots 4..7.  (The instruction pairs slot e of group
+// g with hardware k = 8g + e in bf16, or issues one K = 2 instruction per
+// slot in fp32; either way A and B fragments built with the same slot order
+// contract over k0 .. k0 + 15.)  This order matches the rows a 32x32
+// accumulator holds per lane, so accumulators become operands in place.
+template <typename T>
+struct Frag;
+template <>
+struct Frag<bf16> {
+    bf16x8_t v;
+};
+
+__device__ __forceinline__ void mma(f32x16_t &acc, const Frag<bf16> &a, const Frag<bf16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split(const float (&v)[8], Frag<bf16> &hi, Frag<bf16> &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16 h = static_cast<bf16>(v[e]);
+        hi.v[e] = h;
+        lo.v[e] = static_cast<bf16>(v[e] - static_cast<float>(h));
+    }
+}
+
+// acc += A B with A given as fp32 values (split in the bf16 path), B exact.
+__device__ __forceinline__ void mma_fa(f32x16_t &acc, const float (&a)[8], const Frag<bf16> &b) {
+    Frag<bf16> hi, lo;
+    split(a, hi, lo);
+    mma(acc, hi, b);
+    mma(acc, lo, b);
+}
+// acc += A B with A exact, B given as fp32 values.
+__device__ __forceinline__ void mma_fb(f32x16_t &acc, const Frag<bf16> &a, const float (&b)[8]) {
+    Frag<bf16> hi, lo;
+    split(b, hi, lo);
+    mma(acc, a, hi);
+    mma(acc, a, lo);
+}
+
+// The fragment of one LDS row (matrix row or column, k contiguous) for the
+// K = 16 step at k0.
+__device__ __forceinline__ Frag<bf16> lds_frag(const bf16 *row, int k0, int g) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(row + k0 + 4 * g);
+    const uint2 b = *reinterpret_cast<const uint2 *>(row + k0 + 8 + 4 * g);
+    const u32x4_t u = {a.x, a.y, b.x, b.y};
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8_t, u);
+    return f;
+}
+__device__ __forceinline__ float frag_elem(const Frag<bf16> &f, int e) { return static_cast<float>(f.v[e]); }
+
+// 8 slot values from an LDS array of floats indexed by k.
+__device__ __forceinline__ void lds_slots(const float *v, int k0, int g, float (&o)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(v + k0 + 4 * g);
+    const float4 b = *reinterpret_cast<const float4 *>(v + k0 + 8 + 4 * g);
+    o[0] = a.x, o[1] = a.y, o[2] = a.z, o[3] = a.w;
+    o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
+}
+
+// One 16-byte element group of a storage row and its 16/sizeof(T) values.
+template <typename T>
+struct Piece {
+    static constexpr int kElems = 16 / (int)sizeof(T);
+};
+__device__ __forceinline__ u32x4_t load_piece(__amdgpu_buffer_rsrc_t r, int32_t voff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+// A piece stored into an LDS row (rows are 8-byte aligned: two 8-byte writes).
+__device__ __forceinline__ void store_piece(bf16 *dst, const u32x4_t &v) {
+    reinterpret_cast<uint2 *>(dst)[0] = make_uint2(v[0], v[1]);
+    reinterpret_cast<uint2 *>(dst)[1] = make_uint2(v[2], v[3]);
+}
+// The elements of a piece written down one LDS column (row stride `ld`
+// elements), each component named explicitly.
+__device__ __forceinline__ void store_column(bf16 *dst, int ld, const u32x4_t &v) {
+    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+    unsigned short *d = reinterpret_cast<unsigned short *>(dst);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        d[(2 * k) * ld] = (unsigned short)(w[k] & 0xffffu);
+        d[(2 * k + 1) * ld] = (unsigned short)(w[k] >> 16);
+    }
+}
+
+// Per-head step scalars on the transcendental unit (relative error near 1e-7).
+__device__ __forceinline__ float ssd_exp(float z) { return fast_exp2(z * kLog2e); }
+__device__ __forceinline__ float ssd_expm1(float z) {
+    float e;
+    return expm1_and_exp(z, e);
+}
+
+// LDS of one block.  The aggregate pass needs only the transposed B and x.
+// Rows are padded by 4 elements against bank conflicts.
+template <typename T, int N>
+struct alignas(16) SsdSmemOut {
+    T c[kSsdQ][N + kSsdPad];               // C rows of the chunk
+    T b[kSsdQ][N + kSsdPad];               // B rows
+    T bt[N][kSsdQ + kSsdPad];              // B transposed
+    T xt[kSsdHeads][kSsdP][kSsdQ + kSsdPad];  // x transposed, per head
+    alignas(16) float sc[kSsdHeads][4][kSsdQ];  // per head: c_t, k_t, w_t, exp(c_t)
+};
+template <typename T, int N>
+struct alignas(16) SsdSmemAgg {
+    T bt[N][kSsdQ + kSsdPad];
+    T xt[kSsdHeads][kSsdP][kSsdQ + kSsdPad];
+    alignas(16) float sc[kSsdHeads][4][kSsdQ];
+};
+
+// The state tiles of one wave (N x 32, fp32) to or from [Bsz][Dm][N]
+// memory: lane (channel, g) holds n = 32 nt + 8 m + 4 g + (0..3) in
+// registers 4m .. 4m+3 of tile nt -- four 16-byte pieces per tile.
+template <int N>
+__device__ __forceinline__ void state_load(f32x16_t (&hs)[N / 32], const float *src, int g) {
+#pragma unroll
+    for (int nt = 0; nt < N / 32; ++nt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + 32 * nt + 8 * m + 4 * g);
+            hs[nt][4 * m] = v.x, hs[nt][4 * m + 1] = v.y, hs[nt][4 * m + 2] = v.z, hs[nt][4 * m + 3] = v.w;
+        }
+}
+template <int N>
+__device__ __forceinline__ void state_store(const f32x16_t (&hs)[N / 32], float *dst, int g) {
+#pragma unroll
+    for (int nt = 0; nt < N / 32; ++nt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            *reinterpret_cast<float4 *>(dst + 32 * nt + 8 * m + 4 * g) =
+                make_float4(hs[nt][4 * m], hs[nt][4 * m + 1], hs[nt][4 * m + 2], hs[nt][4 * m + 3]);
+}
+
+template <typename T, int N, bool kOut>
+__global__ __launch_bounds__(kSsdBlock) void ssd_chunk_kernel(SsdParams p) {
+    constexpr int kNT = N / 32;  // 32-row state tiles
+    constexpr int kNS = N / 16;  // K = 16 steps over the state
+    constexpr int kPE = Piece<T>::kElems;
+    typedef typename std::conditional<kOut, SsdSmemOut<T, N>, SsdSmemAgg<T, N>>::type Smem;
+    __shared__ Smem sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int hh = wave >> 1;   // head of the block
+    const int dh = wave & 1;    // channel half of the head
+    const int g = lane >> 5;
+    const int li = lane & 31;
+
+    const int nhp = (int)((p.H + kSsdHeads - 1) / kSsdHeads);
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int hp = lb % nhp;
+    const int rest = lb / nhp;
+    const int64_t b = rest % p.Bsz;
+    const int seg = (int)(rest / p.Bsz);
+    const int heads_here = (int)(p.H - (int64_t)hp * kSsdHeads < kSsdHeads ? p.H - (int64_t)hp * kSsdHeads : kSsdHeads);
+    const bool head_ok = hh < heads_here;
+    const int64_t h = (int64_t)hp * kSsdHeads + (head_ok ? hh : 0);
+    const int64_t col0 = (int64_t)hp * kSsdHeads * kSsdP;     // first channel of the block
+    const int64_t d = h * kSsdP + 32 * dh + li;                // this lane's channel
+    const int ncols = heads_here * kSsdP;
+    const int64_t BD = p.Bsz * p.Dm;
+
+    const float a = p.A[h];
+    const float bias = p.delta_bias ? p.delta_bias[h] : 0.f;
+    const float Dd = p.D[d];
+
+    f32x16_t hs[kNT];
+    if (kOut && (p.S > 1 || p.h_init != nullptr)) {
+        const float *src = p.S > 1 ? p.gin + ((int64_t)seg * BD + b * p.Dm + d) * N : p.h_init + (b * p.Dm + d) * N;
+        state_load<N>(hs, src, g);
+    } else {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) hs[nt][r] = 0.f;
+    }
+
+    const int64_t nchunks = (p.L + kSsdQ - 1) / kSsdQ;
+    const int64_t cps = p.seg_len / kSsdQ;
+    const int64_t ch_begin = (int64_t)seg * cps;
+    const int64_t ch_end = ch_begin + cps < nchunks ? ch_begin + cps : nchunks;
+    float dec_total = 0.f;
+
+    for (int64_t ch = ch_begin; ch < ch_end; ++ch) {
+        const int64_t t0 = ch * kSsdQ;
+        const int nc = (int)(p.L - t0 < kSsdQ ? p.L - t0 : kSsdQ);
+        __syncthreads();  // the previous chunk is done with LDS
+
+        // ---- stage the chunk: B (rows and transposed), C rows, x transposed
+        {
+            const T *Bp = static_cast<const T *>(p.B) + (b * p.L + t0) * N;
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp, nc * N * (int)sizeof(T));
+            constexpr int kBPieces = kSsdQ * N / kPE;
+#pragma unroll
+            for (int i = 0; i < kBPieces / kSsdBlock; ++i) {
+                const int pid = tid + kSsdBlock * i;
+                const int s = pid % kSsdQ, n0 = kPE * (pid / kSsdQ);
+                const u32x4_t v = load_piece(rb, (s * N + n0) * (int)sizeof(T));
+                if constexpr (kOut) store_piece(&sm.b[s][n0], v);
+                store_column(&sm.bt[n0][s], kSsdQ + kSsdPad, v);
+            }
+            if constexpr (kOut) {
+                const T *Cp = static_cast<const T *>(p.C) + (b * p.L + t0) * N;
+                const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cp, nc * N * (int)sizeof(T));
+                constexpr int kRowPieces = N / kPE;
+#pragma unroll
+                for (int i = 0; i < kBPieces / kSsdBlock; ++i) {
+                    const int pid = tid + kSsdBlock * i;
+                    const int s = pid / kRowPieces, n0 = kPE * (pid % kRowPieces);
+                    store_piece(&sm.c[s][n0], load_piece(rc, (s * N + n0) * (int)sizeof(T)));
+                }
+            }
+            const T *Xp = static_cast<const T *>(p.x) + (b * p.L + t0) * p.Dm + col0;
+            const int32_t xbytes = (int32_t)(((int64_t)(nc - 1) * p.Dm + ncols) * (int64_t)sizeof(T));
+            const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xp, xbytes);
+            constexpr int kXPieces = kSsdQ * kSsdHeads * kSsdP / kPE;
+#pragma unroll
+            for (int i = 0; i < kXPieces / kSsdBlock; ++i) {
+                const int pid = tid + kSsdBlock * i;
+                const int s = pid % kSsdQ, c0 = kPE * (pid / kSsdQ);
+                const int hx = c0 / kSsdP, dl = c0 % kSsdP;
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (hx < heads_here) v = load_piece(rx, (int32_t)(((int64_t)s * p.Dm + c0) * (int64_t)sizeof(T)));
+                store_column(&sm.xt[hx][dl][s], kSsdQ + kSsdPad, v);
+            }
+        }
+
+        // ---- step scalars of this wave's head (lane = step)
+        float cum, cend;
+        {
+            float dt = 0.f;
+            if (lane < nc) {
+                const T *dp = static_cast<const T *>(p.delta) + (b * p.L + t0 + lane) * p.H + h;
+                float v = to_f32(*dp) + bias;
+                if (p.delta_softplus) v = softplus_(v);
+                dt = v;
+            }
+            const float la = dt * a;
+            cum = la;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const float o = __shfl_up(cum, off);
+                if (lane >= off) cum += o;
+            }
+            cend = __shfl(cum, kWave - 1);
+            // |a| below 1e-20 (zero included) takes the exact a -> 0 limit dt
+            const float k = (p.euler_b || __builtin_fabsf(a) < 1e-20f) ? dt : ssd_expm1(la) / a;
+            if (dh == 0) {
+                sm.sc[hh][0][lane] = cum;
+                sm.sc[hh][1][lane] = k;
+                sm.sc[hh][2][lane] = ssd_exp(cend - cum) * k;
+                sm.sc[hh][3][lane] = ssd_exp(cum);
+            }
+        }
+        dec_total += cend;
+        __syncthreads();
+        if (!head_ok) continue;
+
+        // x of this wave's channels, as the B operand over the chunk's steps
+        Frag<T> xf[kSsdQ / 16];
+#pragma unroll
+        for (int j = 0; j < kSsdQ / 16; ++j) xf[j] = lds_frag(&sm.xt[hh][32 * dh + li][0], 16 * j, g);
+
+        if constexpr (kOut) {
+            // ---- y = exp(c_t) C H + (G o mask) x + D x, two 32-step row tiles
+            f32x16_t yacc[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) yacc[tt][r] = 0.f;
+#pragma unroll
+            for (int j = 0; j < kNS; ++j) {
+                float hv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hv[e] = hs[j / 2][8 * (j % 2) + e];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) mma_fb(yacc[tt], lds_frag(&sm.c[32 * tt + li][0], 16 * j, g), hv);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float4 e4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][3][32 * tt + 8 * m + 4 * g]);
+                    yacc[tt][4 * m] *= e4.x, yacc[tt][4 * m + 1] *= e4.y;
+                    yacc[tt][4 * m + 2] *= e4.z, yacc[tt][4 * m + 3] *= e4.w;
+                }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int t = 32 * tt + li;  // this lane's step in G^T tiles
+                const float ct = sm.sc[hh][0][t];
+#pragma unroll
+                for (int st = 0; st <= tt; ++st) {
+                    // G^T tile: rows s = 32 st + .., columns t
+                    f32x16_t gacc;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) gacc[r] = 0.f;
+#pragma unroll
+                    for (int j = 0; j < kNS; ++j)
+                        mma(gacc, lds_frag(&sm.b[32 * st + li][0], 16 * j, g), lds_frag(&sm.c[t][0], 16 * j, g));
+                    float mv[16];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int s0 = 32 * st + 8 * m + 4 * g;
+                        const float4 c4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][0][s0]);
+                        const float4 k4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][1][s0]);
+                        const float cs[4] = {c4.x, c4.y, c4.z, c4.w};
+                        const float ks[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float w = ssd_exp(ct - cs[q]) * ks[q];
+                            mv[4 * m + q] = (s0 + q <= t) ? gacc[4 * m + q] * w : 0.f;
+                        }
+                    }
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        float av[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) av[e] = mv[8 * hf + e];
+                        mma_fa(yacc[tt], av, xf[2 * st + hf]);
+                    }
+                }
+            }
+            // + D x, then y rows t < nc
+            T *Yp = static_cast<T *>(p.y) + (b * p.L + t0) * p.Dm;
+            const __amdgpu_buffer_rsrc_t ry = make_rsrc(Yp, (int32_t)((int64_t)nc * p.Dm * (int64_t)sizeof(T)));
+            const T *xrow = &sm.xt[hh][32 * dh + li][0];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = 32 * tt + 8 * (r / 4) + 4 * g + (r % 4);
+                    const float v = fma_(Dd, to_f32(xrow[t]), yacc[tt][r]);
+                    buf_store(from_acc<T>(v), ry, (int32_t)(((int64_t)t * p.Dm + d) * (int64_t)sizeof(T)), 0);
+                }
+        }
+
+        // ---- H = exp(c_end) H + B^T (w x)
+        const float decay = ssd_exp(cend);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) hs[nt][r] *= decay;
+#pragma unroll
+        for (int j = 0; j < kSsdQ / 16; ++j) {
+            float wv[8];
+            lds_slots(&sm.sc[hh][2][0], 16 * j, g, wv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wv[e] *= frag_elem(xf[j], e);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) mma_fb(hs[nt], lds_frag(&sm.bt[32 * nt + li][0], 16 * j, g), wv);
+        }
+    }
+
+    if (!head_ok) return;
+    if constexpr (kOut) {
+        if (seg == p.S - 1 && p.h_final != nullptr) state_store<N>(hs, p.h_final + (b * p.Dm + d) * N, g);
+    } else {
+        state_store<N>(hs, p.agg + ((int64_t)seg * BD + b * p.Dm + d) * N, g);
+        if (dh == 0 && lane == 0) p.dec[(int64_t)seg * p.Bsz * p.H + b * p.H + h] = dec_total;
+    }
+}
+
+// States entering each segment: gin[0] = h_init (or 0); gin[s] =
+// exp(dec[s-1]) gin[s-1] + agg[s-1].  One thread per (b, d, n).
+__global__ __launch_bounds__(256) void ssd_carry_kernel(SsdParams p, int N) {
+    const int64_t BDN = p.Bsz * p.Dm * N;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= BDN) return;
+    const int64_t bd = i / N;
+    const int64_t b = bd / p.Dm, d = bd - b * p.Dm;
+    const int64_t h = d / kSsdP;
+    float s = p.h_init ? p.h_init[i] : 0.f;
+    p.gin[i] = s;
+    for (int k = 1; k < p.S; ++k) {
+        s = fma_(expf(p.dec[(int64_t)(k - 1) * p.Bsz * p.H + b * p.H + h]), s, p.agg[(int64_t)(k - 1) * BDN + i]);
+        p.gin[(int64_t)k * BDN + i] = s;
+    }
+}
+
+template <typename T, int N>
+hipError_t ssd_pass_n(SsdPass pass, const SsdParams &p, hipStream_t s) {
+    const unsigned nhp = (unsigned)((p.H + kSsdHeads - 1) / kSsdHeads);
+    switch (pass) {
+        case SsdPass::kAggregate:
+            if (p.S <= 1) return hipSuccess;
+            hipLaunchKernelGGL((ssd_chunk_kernel<T, N, false>), dim3(nhp * (unsigned)p.Bsz * (unsigned)(p.S - 1)),
+                               dim3(kSsdBlock), 0, s, p);
+            break;
+        case SsdPass::kCarry: {
+            if (p.S <= 1) return hipSuccess;
+            const int64_t n = p.Bsz * p.Dm * N;
+            hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, N);
+            break;
+        }
+        case SsdPass::kOutput:
+            hipLaunchKernelGGL((ssd_chunk_kernel<T, N, true>), dim3(nhp * (unsigned)p.Bsz * (unsigned)p.S),
+                               dim3(kSsdBlock), 0, s, p);
+            break;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t ssd_pass(SsdPass pass, const SsdParams &p, int N, hipStream_t s) {
+    switch (N) {
+        case 32: return ssd_pass_n<T, 32>(pass, p, s);
+        case 64: return ssd_pass_n<T, 64>(pass, p, s);
+        case 128: return ssd_pass_n<T, 128>(pass, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+}  // namespace ssm

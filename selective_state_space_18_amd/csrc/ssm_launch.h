@@ -88,6 +88,27 @@ hipError_t cplx_pass_bf16(ScanPass pass, const ScanParams &p, int N, hipStream_t
 hipError_t cplx_step_f32(const StepParams &p, int N, hipStream_t s);
 hipError_t cplx_step_bf16(const StepParams &p, int N, hipStream_t s);
 
+// Scalar decay per head, chunked matrix form (ssd_kernels.h).  x, y
+// [Bsz][L][Dm]; delta [Bsz][L][H]; A, delta_bias [H]; D [Dm]; B, C
+// [Bsz][L][N]; h_init, h_final [Bsz][Dm][N]; heads of 64 channels.  Scratch
+// (fp32): agg [S-1][Bsz*Dm][N] end state of each segment from zero, dec
+// [S-1][Bsz][H] its total log decay, gin [S][Bsz*Dm][N] the state entering it.
+struct SsdParams {
+    const void *x, *delta, *B, *C;
+    const float *A, *D, *delta_bias, *h_init;
+    void *y;
+    float *h_final;
+    float *agg, *dec, *gin;
+    int64_t Bsz, L, Dm, H;
+    int64_t seg_len;   // a multiple of the 64-step chunk
+    int S;
+    int delta_softplus;
+    int euler_b;
+};
+enum class SsdPass { kAggregate, kCarry, kOutput };
+hipError_t ssd_pass_f32(SsdPass pass, const SsdParams &p, int N, hipStream_t s);
+hipError_t ssd_pass_bf16(SsdPass pass, const SsdParams &p, int N, hipStream_t s);
+
 // Segment length the backward kernels are built for (the plan must use it).
 int bwd_segment_len(int dtype);
 hipError_t bwd_pass_f32(BwdPass pass, const BwdParams &q, int N, hipStream_t s);

@@ -24,7 +24,8 @@ SSM_F32, SSM_BF16 = 0, 1
 SSM_OPT_SEGMENT_LEN, SSM_OPT_FORCE_GENERAL, SSM_OPT_PROFILE, SSM_OPT_STEP_CHANNELS = 1, 2, 3, 4
 SSM_DELTA_SOFTPLUS, SSM_EULER_B = 1, 2  # ssm_flags
 KERNEL_KINDS = ("bc_prep", "scan_aggregate", "scan_carry", "scan_output", "step", "state_init",
-                "bwd_aggregate", "bwd_carry", "bwd_main", "bwd_reduce")
+                "bwd_aggregate", "bwd_carry", "bwd_main", "bwd_reduce", "ssd_aggregate", "ssd_carry",
+                "ssd_output")
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_BAD_DTYPE",
           4: "SSM_ERR_UNSUPPORTED_N", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_NOMEM",
           8: "SSM_ERR_HIP", 9: "SSM_ERR_BAD_OPTION"}
@@ -34,7 +35,7 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_st
            "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
            "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
            "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd", "ssm_scan_complex_fwd",
-           "ssm_step_complex")
+           "ssm_step_complex", "ssm_scan_ssd_fwd")
 
 
 class SSMError(RuntimeError):
@@ -65,6 +66,8 @@ def lib():
     L.ssm_scan_fused_fwd.restype = ctypes.c_int
     L.ssm_scan_complex_fwd.argtypes = [_vp] * 10 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_scan_complex_fwd.restype = ctypes.c_int
+    L.ssm_scan_ssd_fwd.argtypes = [_vp] * 10 + [_i64] * 5 + [ctypes.c_int, ctypes.c_uint, _vp]
+    L.ssm_scan_ssd_fwd.restype = ctypes.c_int
     L.ssm_step_complex.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_step_complex.restype = ctypes.c_int
     L.ssm_scan_bwd.argtypes = [_vp] * 18 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
@@ -411,6 +414,50 @@ def scan_complex_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, wa
                                         _ptr(D), _ptr(hi2), _ptr(y), _ptr(hf2), Bsz, L, Dm, N, code,
                                         _flags(delta_softplus, euler_b), _stream(dev))
     _check(rc, "ssm_scan_complex_fwd")
+    return y, h_final
+
+
+def scan_ssd_fwd(x, delta, A, B, C, D, head_dim=64, h_init=None, y=None, h_final=None, want_state=True,
+                 delta_bias=None, delta_softplus=False, euler_b=False):
+    """ssm_scan_ssd_fwd: scan with one scalar decay per head of head_dim channels.
+
+    x: [Bsz, L, Dm]; delta: [Bsz, L, H] (H = Dm / head_dim); B, C: [Bsz, L, N]
+    (all the same dtype); A: [H] fp32; D: [Dm] fp32; delta_bias: [H] fp32 or
+    None; h_init: optional [Bsz, Dm, N] fp32.  Returns (y [Bsz, L, Dm],
+    h_final [Bsz, Dm, N] fp32 or None)."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, L, Dm = x.shape
+    N = B.shape[2]
+    P = int(head_dim)
+    if P <= 0 or Dm % P:
+        raise ValueError(f"Dm = {Dm} is not a multiple of head_dim = {P}")
+    H = Dm // P
+    dt = x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (Bsz, L, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, L, H), dt, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (Bsz, L, N), dt, dev)
+    _need(C, "C", (Bsz, L, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (H,), torch.float32, dev)
+    if h_init is not None:
+        _need(h_init, "h_init", (Bsz, Dm, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((Bsz, L, Dm), dtype=dt, device=dev)
+    _need(y, "y", (Bsz, L, Dm), dt, dev)
+    if h_final is None and want_state:
+        h_final = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev)
+    if h_final is not None:
+        _need(h_final, "h_final", (Bsz, Dm, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_ssd_fwd(_ptr(x), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(h_init), _ptr(y), _ptr(h_final), Bsz, L, Dm, N, P, code,
+                                    _flags(delta_softplus, euler_b), _stream(dev))
+    _check(rc, "ssm_scan_ssd_fwd")
     return y, h_final
 
 

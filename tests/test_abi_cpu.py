@@ -171,6 +171,35 @@ def test_bwd_argument_errors(L):
     assert bwd(Bsz=1 << 40, Ls=1 << 40) == 2
 
 
+def test_ssd_argument_errors(L):
+    v = ctypes.c_void_p
+    Q = [0x10000000 * (i + 1) for i in range(12)]  # fake, 16-byte aligned, far apart
+
+    def ssd(**k):
+        a = dict(x=Q[0], dl=Q[1], bias=None, A=Q[2], B=Q[3], C=Q[4], D=Q[5], hi=None, y=Q[6], hf=Q[7],
+                 Bsz=2, Ls=100, Dm=128, N=64, P=64, dtype=1, flags=0)
+        a.update(k)
+        return L.ssm_scan_ssd_fwd(v(a["x"]), v(a["dl"]), v(a["bias"]), v(a["A"]), v(a["B"]), v(a["C"]),
+                                  v(a["D"]), v(a["hi"]), v(a["y"]), v(a["hf"]), a["Bsz"], a["Ls"], a["Dm"],
+                                  a["N"], a["P"], a["dtype"], a["flags"], None)
+    assert ssd(dtype=2) == 3
+    assert ssd(N=16) == 4 and ssd(N=256) == 4
+    assert b"32, 64, 128" in L.ssm_last_error()
+    assert ssd(P=32) == 2 and b"head_dim" in L.ssm_last_error()
+    assert ssd(Dm=96) == 2 and b"multiple" in L.ssm_last_error()
+    assert ssd(flags=4) == 9
+    assert ssd(Ls=-1) == 2
+    assert ssd(x=0) == 1 and ssd(A=0) == 1 and ssd(y=0) == 1
+    assert ssd(x=Q[0] + 8) == 5 and b"16-byte" in L.ssm_last_error()   # bf16 x needs 16 bytes here
+    assert ssd(B=Q[3] + 4) == 5 and ssd(hf=Q[7] + 4) == 5 and ssd(hi=Q[8] + 4) == 5
+    assert ssd(bias=Q[8] + 2) == 5
+    assert ssd(y=Q[0]) == 6 and ssd(hf=Q[3]) == 6 and ssd(hf=Q[6]) == 6
+    assert ssd(hi=Q[7], hf=Q[7] + 16) == 6      # partial overlap of the states
+    assert ssd(Bsz=1 << 40, Ls=1 << 40) == 2
+    assert ssd(Dm=(1 << 23)) == 2
+    assert ssd(Bsz=0, x=0, dl=0, B=0, C=0, y=0, hf=0) == 0
+
+
 def test_step_argument_errors(L):
     assert step(L, dtype=2) == 3
     assert step(L, N=5) == 4
