@@ -25,8 +25,10 @@
 //
 // Layout of work: a block of 4 waves serves two heads of one batch row over a
 // segment of chunks; wave w takes head w/2 and channels 32 (w%2) .. +32 of
-// it.  Chunk inputs are staged in LDS (B and C by rows; B and x transposed,
-// so that every matrix operand is read as two 8- or 16-byte pieces per lane).
+// it.  Chunk inputs are staged in LDS as stored (one row per step); operands
+// whose contraction runs over the steps (x, and B for the state update) are
+// read from those rows with gfx950's transposing LDS load, the others as two
+// 8-byte pieces per lane.
 // Time is cut into segments joined as in the diagonal scan: an aggregate pass
 // (end state of each segment from zero, and its total log decay), a carry
 // pass, and an output pass that reruns each segment from its entering state.
@@ -45,11 +47,29 @@ constexpr int kSsdQ = 64;       // chunk length (steps)
 constexpr int kSsdP = 64;       // channels per head
 constexpr int kSsdHeads = 2;    // heads per block
 constexpr int kSsdBlock = 256;  // 4 waves
-constexpr int kSsdPad = 4;      // LDS row padding (elements)
+
+// LDS row pitch (bf16 elements) for rows of w elements: the pitch in dwords,
+// modulo the 64 banks, lies in {10, 14, 18, 26, 38, 46, 50, 54}.  Then 32
+// consecutive rows read at one column (row fragments) hit 32 distinct bank
+// pairs, and 4 consecutive rows read as 32-byte runs (transposing reads) hit
+// 4 disjoint 8-bank ranges.
+constexpr bool ssd_pitch_ok(int dw) {
+    const int r = dw % 64;
+    return r == 10 || r == 14 || r == 18 || r == 26 || r == 38 || r == 46 || r == 50 || r == 54;
+}
+constexpr int ssd_pitch(int w) {
+    int dw = w / 2;
+    while (!ssd_pitch_ok(dw)) ++dw;
+    return 2 * dw;
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 // A matrix-operand fragment: 8 k-slots per lane.  For a K = 16 step starting
 // at k0, lane group g = lane / 32 holds k0 + 4g + (0..3) in slots 0..3 and
@@ -69,13 +89,22 @@ __device__ __forceinline__ void mma(f32x16_t &acc, const Frag<bf16> &a, const Fr
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
 }
 
+// v = hi + lo + r with hi, lo bf16 and |r| <= 2^-18 |v|: pairs are rounded
+// to nearest even by one packed conversion, and hi is read back as fp32 from
+// the packed word (a shift and a mask) for the remainder.
 __device__ __forceinline__ void split(const float (&v)[8], Frag<bf16> &hi, Frag<bf16> &lo) {
+    u32x4_t h, l;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const bf16 h = static_cast<bf16>(v[e]);
-        hi.v[e] = h;
-        lo.v[e] = static_cast<bf16>(v[e] - static_cast<float>(h));
+    for (int k = 0; k < 4; ++k) {
+        const f32x2_t ab = {v[2 * k], v[2 * k + 1]};
+        const unsigned hp = __builtin_bit_cast(unsigned, __builtin_convertvector(ab, bf16x2_t));
+        const f32x2_t r = {v[2 * k] - __builtin_bit_cast(float, hp << 16),
+                           v[2 * k + 1] - __builtin_bit_cast(float, hp & 0xffff0000u)};
+        h[k] = hp;
+        l[k] = __builtin_bit_cast(unsigned, __builtin_convertvector(r, bf16x2_t));
     }
+    hi.v = __builtin_bit_cast(bf16x8_t, h);
+    lo.v = __builtin_bit_cast(bf16x8_t, l);
 }
 
 // acc += A B with A given as fp32 values (split in the bf16 path), B exact.
@@ -98,6 +127,24 @@ __device__ __forceinline__ void mma_fb(f32x16_t &acc, const Frag<bf16> &a, const
 __device__ __forceinline__ Frag<bf16> lds_frag(const bf16 *row, int k0, int g) {
     const uint2 a = *reinterpret_cast<const uint2 *>(row + k0 + 4 * g);
     const uint2 b = *reinterpret_cast<const uint2 *>(row + k0 + 8 + 4 * g);
+    const u32x4_t u = {a.x, a.y, b.x, b.y};
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8_t, u);
+    return f;
+}
+// The fragment of the K = 16 step at row k0 of a row-major LDS matrix (rows
+// = k, pitch in elements) for the 32 columns col0 .. col0 + 31, one column
+// per lane (lane % 32), read with the transposing LDS load: within each 16-lane
+// group, lane m addresses row r0 + m/4, columns c0 + 4 (m%4) .. + 3, and lane
+// i receives column c0 + i of rows r0 .. r0 + 3.  Two such loads fill slots
+// 0..3 (rows k0 + 4g + 0..3) and 4..7 (rows k0 + 8 + 4g + 0..3).
+__device__ __forceinline__ Frag<bf16> tr_frag(const bf16 *base, int pitch, int k0, int col0, int lane) {
+    const int row = k0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const bf16 *q = base + row * pitch + col;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)q);
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(q + 8 * pitch));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
     const u32x4_t u = {a.x, a.y, b.x, b.y};
     Frag<bf16> f;
     f.v = __builtin_bit_cast(bf16x8_t, u);
@@ -126,39 +173,25 @@ __device__ __forceinline__ void store_piece(bf16 *dst, const u32x4_t &v) {
     reinterpret_cast<uint2 *>(dst)[0] = make_uint2(v[0], v[1]);
     reinterpret_cast<uint2 *>(dst)[1] = make_uint2(v[2], v[3]);
 }
-// The elements of a piece written down one LDS column (row stride `ld`
-// elements), each component named explicitly.
-__device__ __forceinline__ void store_column(bf16 *dst, int ld, const u32x4_t &v) {
-    const unsigned w[4] = {v.x, v.y, v.z, v.w};
-    unsigned short *d = reinterpret_cast<unsigned short *>(dst);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        d[(2 * k) * ld] = (unsigned short)(w[k] & 0xffffu);
-        d[(2 * k + 1) * ld] = (unsigned short)(w[k] >> 16);
-    }
-}
-
-// Per-head step scalars on the transcendental unit (relative error near 1e-7).
-__device__ __forceinline__ float ssd_exp(float z) { return fast_exp2(z * kLog2e); }
+// exp(z) - 1 on the transcendental unit (relative error near 1e-7).
 __device__ __forceinline__ float ssd_expm1(float z) {
     float e;
     return expm1_and_exp(z, e);
 }
 
-// LDS of one block.  The aggregate pass needs only the transposed B and x.
-// Rows are padded by 4 elements against bank conflicts.
+// LDS of one block: the chunk's B, C and x rows as stored (row = step), at
+// the pitches above.  The aggregate pass needs no C.
 template <typename T, int N>
 struct alignas(16) SsdSmemOut {
-    T c[kSsdQ][N + kSsdPad];               // C rows of the chunk
-    T b[kSsdQ][N + kSsdPad];               // B rows
-    T bt[N][kSsdQ + kSsdPad];              // B transposed
-    T xt[kSsdHeads][kSsdP][kSsdQ + kSsdPad];  // x transposed, per head
-    alignas(16) float sc[kSsdHeads][4][kSsdQ];  // per head: c_t, k_t, w_t, exp(c_t)
+    T c[kSsdQ][ssd_pitch(N)];
+    T b[kSsdQ][ssd_pitch(N)];
+    T x[kSsdQ][ssd_pitch(kSsdHeads * kSsdP)];      // the block's 128 channels
+    alignas(16) float sc[kSsdHeads][4][kSsdQ];      // per head: c_t log2(e), k_t, w_t, exp(c_t)
 };
 template <typename T, int N>
 struct alignas(16) SsdSmemAgg {
-    T bt[N][kSsdQ + kSsdPad];
-    T xt[kSsdHeads][kSsdP][kSsdQ + kSsdPad];
+    T b[kSsdQ][ssd_pitch(N)];
+    T x[kSsdQ][ssd_pitch(kSsdHeads * kSsdP)];
     alignas(16) float sc[kSsdHeads][4][kSsdQ];
 };
 
@@ -186,7 +219,7 @@ __device__ __forceinline__ void state_store(const f32x16_t (&hs)[N / 32], float 
 }
 
 template <typename T, int N, bool kOut>
-__global__ __launch_bounds__(kSsdBlock) void ssd_chunk_kernel(SsdParams p) {
+__global__ __launch_bounds__(kSsdBlock, 2) void ssd_chunk_kernel(SsdParams p) {
     constexpr int kNT = N / 32;  // 32-row state tiles
     constexpr int kNS = N / 16;  // K = 16 steps over the state
     constexpr int kPE = Piece<T>::kElems;
@@ -241,23 +274,21 @@ __global__ __launch_bounds__(kSsdBlock) void ssd_chunk_kernel(SsdParams p) {
         const int nc = (int)(p.L - t0 < kSsdQ ? p.L - t0 : kSsdQ);
         __syncthreads();  // the previous chunk is done with LDS
 
-        // ---- stage the chunk: B (rows and transposed), C rows, x transposed
+        // ---- stage the chunk's B, C and x rows (16-byte pieces, coalesced)
         {
+            constexpr int kRowPieces = N / kPE;
+            constexpr int kBPieces = kSsdQ * kRowPieces;
             const T *Bp = static_cast<const T *>(p.B) + (b * p.L + t0) * N;
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp, nc * N * (int)sizeof(T));
-            constexpr int kBPieces = kSsdQ * N / kPE;
 #pragma unroll
             for (int i = 0; i < kBPieces / kSsdBlock; ++i) {
                 const int pid = tid + kSsdBlock * i;
-                const int s = pid % kSsdQ, n0 = kPE * (pid / kSsdQ);
-                const u32x4_t v = load_piece(rb, (s * N + n0) * (int)sizeof(T));
-                if constexpr (kOut) store_piece(&sm.b[s][n0], v);
-                store_column(&sm.bt[n0][s], kSsdQ + kSsdPad, v);
+                const int s = pid / kRowPieces, n0 = kPE * (pid % kRowPieces);
+                store_piece(&sm.b[s][n0], load_piece(rb, (s * N + n0) * (int)sizeof(T)));
             }
             if constexpr (kOut) {
                 const T *Cp = static_cast<const T *>(p.C) + (b * p.L + t0) * N;
                 const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cp, nc * N * (int)sizeof(T));
-                constexpr int kRowPieces = N / kPE;
 #pragma unroll
                 for (int i = 0; i < kBPieces / kSsdBlock; ++i) {
                     const int pid = tid + kSsdBlock * i;
@@ -268,20 +299,20 @@ __global__ __launch_bounds__(kSsdBlock) void ssd_chunk_kernel(SsdParams p) {
             const T *Xp = static_cast<const T *>(p.x) + (b * p.L + t0) * p.Dm + col0;
             const int32_t xbytes = (int32_t)(((int64_t)(nc - 1) * p.Dm + ncols) * (int64_t)sizeof(T));
             const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xp, xbytes);
-            constexpr int kXPieces = kSsdQ * kSsdHeads * kSsdP / kPE;
+            constexpr int kXRow = kSsdHeads * kSsdP / kPE;
 #pragma unroll
-            for (int i = 0; i < kXPieces / kSsdBlock; ++i) {
+            for (int i = 0; i < kSsdQ * kXRow / kSsdBlock; ++i) {
                 const int pid = tid + kSsdBlock * i;
-                const int s = pid % kSsdQ, c0 = kPE * (pid / kSsdQ);
-                const int hx = c0 / kSsdP, dl = c0 % kSsdP;
+                const int s = pid / kXRow, c0 = kPE * (pid % kXRow);
                 u32x4_t v = {0u, 0u, 0u, 0u};
-                if (hx < heads_here) v = load_piece(rx, (int32_t)(((int64_t)s * p.Dm + c0) * (int64_t)sizeof(T)));
-                store_column(&sm.xt[hx][dl][s], kSsdQ + kSsdPad, v);
+                if (c0 < ncols) v = load_piece(rx, (int32_t)(((int64_t)s * p.Dm + c0) * (int64_t)sizeof(T)));
+                store_piece(&sm.x[s][c0], v);
             }
         }
 
-        // ---- step scalars of this wave's head (lane = step)
-        float cum, cend;
+        // ---- step scalars of this wave's head (lane = step); log decays are
+        // kept in base-2 units (c2 = c log2 e) for the exp2 unit
+        float cend;
         {
             float dt = 0.f;
             if (lane < nc) {
@@ -291,45 +322,61 @@ __global__ __launch_bounds__(kSsdBlock) void ssd_chunk_kernel(SsdParams p) {
                 dt = v;
             }
             const float la = dt * a;
-            cum = la;
+            float c2 = la * kLog2e;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
-                const float o = __shfl_up(cum, off);
-                if (lane >= off) cum += o;
+                const float o = __shfl_up(c2, off);
+                if (lane >= off) c2 += o;
             }
-            cend = __shfl(cum, kWave - 1);
+            const float cend2 = __shfl(c2, kWave - 1);
+            cend = cend2 * 0.6931471805599453f;
             // |a| below 1e-20 (zero included) takes the exact a -> 0 limit dt
             const float k = (p.euler_b || __builtin_fabsf(a) < 1e-20f) ? dt : ssd_expm1(la) / a;
             if (dh == 0) {
-                sm.sc[hh][0][lane] = cum;
+                sm.sc[hh][0][lane] = c2;
                 sm.sc[hh][1][lane] = k;
-                sm.sc[hh][2][lane] = ssd_exp(cend - cum) * k;
-                sm.sc[hh][3][lane] = ssd_exp(cum);
+                sm.sc[hh][2][lane] = fast_exp2(cend2 - c2) * k;
+                sm.sc[hh][3][lane] = fast_exp2(c2);
             }
         }
         dec_total += cend;
         __syncthreads();
         if (!head_ok) continue;
 
-        // x of this wave's channels, as the B operand over the chunk's steps
-        Frag<T> xf[kSsdQ / 16];
-#pragma unroll
-        for (int j = 0; j < kSsdQ / 16; ++j) xf[j] = lds_frag(&sm.xt[hh][32 * dh + li][0], 16 * j, g);
+        // x of this wave's 32 channels: the B operand over the chunk's steps
+        const int xcol = kSsdP * hh + 32 * dh;
+        constexpr int kPX = ssd_pitch(kSsdHeads * kSsdP);
+        constexpr int kPN = ssd_pitch(N);
 
         if constexpr (kOut) {
-            // ---- y = exp(c_t) C H + (G o mask) x + D x, two 32-step row tiles
-            f32x16_t yacc[2];
+            // ---- y = exp(c_t) (C H) + (G o mask) x + D x over two 32-step row
+            // tiles.  One sweep over the state dimension accumulates C H for
+            // both row tiles and the three causal tiles of G^T = B C^T (rows
+            // s, columns t: (0,0), (0,1), (1,1)), which share the C fragments;
+            // hi and lo halves of the split state go in separate passes so
+            // that consecutive matrix instructions feed different
+            // accumulators.
+            f32x16_t yacc[2], g00, g01, g11;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) yacc[tt][r] = 0.f;
+            for (int r = 0; r < 16; ++r) yacc[0][r] = yacc[1][r] = g00[r] = g01[r] = g11[r] = 0.f;
 #pragma unroll
             for (int j = 0; j < kNS; ++j) {
+                const Frag<T> c0 = lds_frag(&sm.c[li][0], 16 * j, g);
+                const Frag<T> c1 = lds_frag(&sm.c[32 + li][0], 16 * j, g);
+                const Frag<T> b0 = lds_frag(&sm.b[li][0], 16 * j, g);
+                const Frag<T> b1 = lds_frag(&sm.b[32 + li][0], 16 * j, g);
                 float hv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) hv[e] = hs[j / 2][8 * (j % 2) + e];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) mma_fb(yacc[tt], lds_frag(&sm.c[32 * tt + li][0], 16 * j, g), hv);
+                Frag<T> hhi, hlo;
+                split(hv, hhi, hlo);
+                mma(yacc[0], c0, hhi);
+                mma(yacc[1], c1, hhi);
+                mma(g00, b0, c0);
+                mma(g01, b0, c1);
+                mma(g11, b1, c1);
+                mma(yacc[0], c0, hlo);
+                mma(yacc[1], c1, hlo);
             }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
@@ -339,58 +386,64 @@ __global__ __launch_bounds__(kSsdBlock) void ssd_chunk_kernel(SsdParams p) {
                     yacc[tt][4 * m] *= e4.x, yacc[tt][4 * m + 1] *= e4.y;
                     yacc[tt][4 * m + 2] *= e4.z, yacc[tt][4 * m + 3] *= e4.w;
                 }
+            // mask and weight the G^T tiles -- M[t][s] = G[s][t] exp(c_t - c_s) k_s
+            // for s <= t (lane = t, registers = s) -- split them, and add M x,
+            // one 16-step half of each 32-step column tile at a time,
+            // alternating the two row tiles
+            const float ct0 = sm.sc[hh][0][li], ct1 = sm.sc[hh][0][32 + li];
+            auto masked = [&](const f32x16_t &gt, int st, int tt, float ct, int hf, Frag<T> &mh, Frag<T> &ml) {
+                const int t = 32 * tt + li;
+                float mv[8];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int t = 32 * tt + li;  // this lane's step in G^T tiles
-                const float ct = sm.sc[hh][0][t];
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    const int m = 2 * hf + m2;
+                    const int s0 = 32 * st + 8 * m + 4 * g;
+                    const float4 c4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][0][s0]);
+                    const float4 k4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][1][s0]);
+                    const float cs[4] = {c4.x, c4.y, c4.z, c4.w};
+                    const float ks[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-                for (int st = 0; st <= tt; ++st) {
-                    // G^T tile: rows s = 32 st + .., columns t
-                    f32x16_t gacc;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) gacc[r] = 0.f;
-#pragma unroll
-                    for (int j = 0; j < kNS; ++j)
-                        mma(gacc, lds_frag(&sm.b[32 * st + li][0], 16 * j, g), lds_frag(&sm.c[t][0], 16 * j, g));
-                    float mv[16];
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int s0 = 32 * st + 8 * m + 4 * g;
-                        const float4 c4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][0][s0]);
-                        const float4 k4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][1][s0]);
-                        const float cs[4] = {c4.x, c4.y, c4.z, c4.w};
-                        const float ks[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float w = ssd_exp(ct - cs[q]) * ks[q];
-                            mv[4 * m + q] = (s0 + q <= t) ? gacc[4 * m + q] * w : 0.f;
-                        }
-                    }
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        float av[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) av[e] = mv[8 * hf + e];
-                        mma_fa(yacc[tt], av, xf[2 * st + hf]);
+                    for (int q = 0; q < 4; ++q) {
+                        const float w = fast_exp2(ct - cs[q]) * ks[q];
+                        mv[4 * m2 + q] = (s0 + q <= t) ? gt[4 * m + q] * w : 0.f;
                     }
                 }
+                split(mv, mh, ml);
+            };
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const Frag<T> x0 = tr_frag(&sm.x[0][0], kPX, 16 * hf, xcol, lane);       // steps 0..31
+                const Frag<T> x1 = tr_frag(&sm.x[0][0], kPX, 32 + 16 * hf, xcol, lane);  // steps 32..63
+                Frag<T> h00, l00, h01, l01, h11, l11;
+                masked(g00, 0, 0, ct0, hf, h00, l00);
+                masked(g01, 0, 1, ct1, hf, h01, l01);
+                masked(g11, 1, 1, ct1, hf, h11, l11);
+                mma(yacc[0], h00, x0);
+                mma(yacc[1], h01, x0);
+                mma(yacc[0], l00, x0);
+                mma(yacc[1], h11, x1);
+                mma(yacc[1], l01, x0);
+                mma(yacc[1], l11, x1);
             }
-            // + D x, then y rows t < nc
+            // + D x, then y rows t < nc (the row offset goes in the scalar
+            // offset of the store)
             T *Yp = static_cast<T *>(p.y) + (b * p.L + t0) * p.Dm;
             const __amdgpu_buffer_rsrc_t ry = make_rsrc(Yp, (int32_t)((int64_t)nc * p.Dm * (int64_t)sizeof(T)));
-            const T *xrow = &sm.xt[hh][32 * dh + li][0];
+            const int32_t vrow = (int32_t)(((int64_t)(4 * g) * p.Dm + d) * (int64_t)sizeof(T));
+            const int32_t rowb = (int32_t)(p.Dm * (int64_t)sizeof(T));
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int t = 32 * tt + 8 * (r / 4) + 4 * g + (r % 4);
-                    const float v = fma_(Dd, to_f32(xrow[t]), yacc[tt][r]);
-                    buf_store(from_acc<T>(v), ry, (int32_t)(((int64_t)t * p.Dm + d) * (int64_t)sizeof(T)), 0);
+                    const int tq = 32 * tt + 8 * (r / 4) + (r % 4);  // t minus 4g
+                    const float v = fma_(Dd, to_f32(sm.x[tq + 4 * g][xcol + li]), yacc[tt][r]);
+                    buf_store(from_acc<T>(v), ry, vrow, tq * rowb);
                 }
         }
 
-        // ---- H = exp(c_end) H + B^T (w x)
-        const float decay = ssd_exp(cend);
+        // ---- H = exp(c_end) H + B^T (w x): the hi and lo halves of the
+        // weighted x in separate passes over the state tiles
+        const float decay = fast_exp2(cend * kLog2e);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
@@ -399,10 +452,18 @@ __global__ __launch_bounds__(kSsdBlock) void ssd_chunk_kernel(SsdParams p) {
         for (int j = 0; j < kSsdQ / 16; ++j) {
             float wv[8];
             lds_slots(&sm.sc[hh][2][0], 16 * j, g, wv);
+            const Frag<T> xj = tr_frag(&sm.x[0][0], kPX, 16 * j, xcol, lane);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wv[e] *= frag_elem(xf[j], e);
+            for (int e = 0; e < 8; ++e) wv[e] *= frag_elem(xj, e);
+            Frag<T> whi, wlo;
+            split(wv, whi, wlo);
+            Frag<T> bt[kNT];
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) mma_fb(hs[nt], lds_frag(&sm.bt[32 * nt + li][0], 16 * j, g), wv);
+            for (int nt = 0; nt < kNT; ++nt) bt[nt] = tr_frag(&sm.b[0][0], kPN, 16 * j, 32 * nt, lane);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) mma(hs[nt], bt[nt], whi);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) mma(hs[nt], bt[nt], wlo);
         }
     }
 
