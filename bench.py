@@ -39,6 +39,15 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # Algorithmic fp32 flops per state element of the scan: z = delta*A, exp(z)-1,
 # divide by A, times B, times x, Abar*h + Bbar*x (FMA, 2), C*h + y (FMA, 2).
 SCAN_FLOPS_PER_ELEM = 9
+# Backward, per state element: the adjoint step mu = C dy + nu, (1 + E) mu and
+# the six gradient terms (dx, dDelta, two for dA, dB, dC lane values: 20), the
+# channel sums of dB and dC (2), and one forward recurrence for the states
+# (exp-chain, input and update FMAs: 6).
+BWD_FLOPS_PER_ELEM = 28
+# Complex A, per state element of the output pass: delta*a, delta*w (2); exp,
+# sin, cos (3, one each); Abar (2); Abar - 1 (3); (Abar - 1)/A (complex
+# multiply, 6); B x and its product with it (3); Abar h + k u (8); C Re(h) + y (2).
+CPLX_FLOPS_PER_ELEM = 29
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_18_amd", "csrc")
 
@@ -259,7 +268,12 @@ def bench_backward(torch, ss, generate, cfg, steps, warmup):
     torch.cuda.empty_cache()
     elems = cfg.elems()
     main_ms = kern["bwd_main"]["avg_ms"]
+    achieved = elems * BWD_FLOPS_PER_ELEM / (main_ms * 1e-3) / 1e12
     return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": elems / (ms * 1e-3), "unit": "elems/s",
+            "roofline": {"kernel": "bwd_main_kernel", "bound": "alu", "achieved": round(achieved, 3),
+                         "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+                         "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
+                         "avg_ms": round(main_ms, 5), "algorithmic_flops_per_launch": elems * BWD_FLOPS_PER_ELEM},
             "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
             "main_kernel_elems_per_s": elems / (main_ms * 1e-3)}
 
@@ -281,8 +295,16 @@ def bench_complex(torch, ss, generate, cfg, steps, warmup):
     ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
     del inp, A, y, hf
     torch.cuda.empty_cache()
+    out_ms = kern["scan_output"]["avg_ms"]
+    achieved = cfg.elems() * CPLX_FLOPS_PER_ELEM / (out_ms * 1e-3) / 1e12
     return {"workload": cfg.name + "_complex_A", "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
-            "unit": "elems/s", "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()}}
+            "unit": "elems/s",
+            "roofline": {"kernel": "cplx_segment_kernel (output pass)", "bound": "alu", "achieved": round(achieved, 3),
+                         "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+                         "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
+                         "avg_ms": round(out_ms, 5), "algorithmic_flops_per_launch": cfg.elems() * CPLX_FLOPS_PER_ELEM,
+                         "note": "exp, sin and cos count one flop each and issue at a quarter of the VALU rate"},
+            "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()}}
 
 
 def bench_packed(torch, ss, generate, cfg, steps, warmup):
