@@ -114,3 +114,67 @@ def test_packed_scan_replays_match_eager(ss):
         y2, _ = ss.scan_varlen_fwd(*args, h_init=h0)
         torch.cuda.synchronize()
         assert torch.equal(y2, y_eager)
+
+
+def _replay_check(ss_call, outs, eager, reps=3):
+    """Capture ss_call (writing into outs) on a side stream and compare every
+    replay with the eager tensors, with eager work between replays."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ss_call()  # scratch memory is per (device, stream): size it before capturing
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ss_call()
+    for k in range(reps):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), f"replay {k}: output {i} differs"
+        ss_call()  # eager work between replays (on the current stream)
+        torch.cuda.synchronize()
+
+
+def test_ssd_replays_match_eager(ss):
+    print("case: scalar-decay layer graph replay", flush=True)
+    cfg = configs.SSD_LAYER.with_shape(name="graph_ssd", Bsz=2, L=500, Dm=192, N=64, h0_std=0.5, seed=51)
+    inp = generate.ssd_inputs(cfg, DEV)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], 64)
+    ss.set_option(ss.SSM_OPT_SEGMENT_LEN, 128)
+    try:
+        y_e, h_e = ss.scan_ssd_fwd(*args, h_init=inp["h_init"])
+        torch.cuda.synchronize()
+        y, hf = torch.empty_like(y_e), torch.empty_like(h_e)
+        _replay_check(lambda: ss.scan_ssd_fwd(*args, h_init=inp["h_init"], y=y, h_final=hf), (y, hf), (y_e, h_e))
+    finally:
+        ss.set_option(ss.SSM_OPT_SEGMENT_LEN, 0)
+
+
+def test_complex_scan_replays_match_eager(ss):
+    print("case: complex scan graph replay", flush=True)
+    cfg = configs.ScanConfig("graph_cplx", 2, 400, 130, 16, "bf16", "s4d_real", "per_token", 1.0, 52)
+    inp = generate.scan_inputs(cfg, DEV)
+    A = generate.complex_A(130, 16, 53, DEV)
+    args = (inp["x"], inp["delta"], A, inp["B"], inp["C"], inp["D"])
+    y_e, h_e = ss.scan_complex_fwd(*args)
+    torch.cuda.synchronize()
+    y, hf = torch.empty_like(y_e), torch.empty_like(h_e)
+    _replay_check(lambda: ss.scan_complex_fwd(*args, y=y, h_final=hf), (y, hf), (y_e, h_e))
+
+
+def test_backward_replays_match_eager(ss):
+    print("case: backward graph replay", flush=True)
+    cfg = configs.ScanConfig("graph_bwd", 2, 300, 130, 16, "bf16", "lognormal", "per_token", 1.0, 54)
+    inp = generate.scan_inputs(cfg, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(55)
+    dy = torch.randn(inp["x"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], dy)
+    eager = ss.scan_bwd(*args)
+    torch.cuda.synchronize()
+    names = sorted(k for k, v in eager.items() if v is not None)
+    out = {k: torch.empty_like(eager[k]) for k in names}
+    _replay_check(lambda: ss.scan_bwd(*args, out=out), [out[k] for k in names], [eager[k] for k in names])

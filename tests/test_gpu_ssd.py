@@ -195,3 +195,22 @@ def test_ssd_layer_sampled(ss):
     P.compare(y.index_select(2, cidx), yr, "bf16", "y (two heads)")
     P.compare(hf.index_select(1, cidx), hr, "bf16", "h_final (two heads)")
     tight(y.index_select(2, cidx), yr, hf.index_select(1, cidx), hr)
+
+
+def test_ssd_no_write_outside_outputs(ss):
+    """Guard bands around y and h_final stay untouched (ragged last chunk, a
+    half-empty block of an odd head count, several segments)."""
+    P.say("case: ssd canaries")
+    inp = make("bf16", 2, 130, 3, 64, seed=95)
+    Bsz, L, Dm, N = 2, 130, 192, 64
+    pad = 4096
+    ybuf = torch.full((pad + Bsz * L * Dm + pad,), 7.0, dtype=torch.bfloat16, device=DEV)
+    hbuf = torch.full((pad + Bsz * Dm * N + pad,), 7.0, dtype=torch.float32, device=DEV)
+    y = ybuf[pad:pad + Bsz * L * Dm].view(Bsz, L, Dm)
+    hf = hbuf[pad:pad + Bsz * Dm * N].view(Bsz, Dm, N)
+    run(ss, inp, {}, seg=64, y=y, h_final=hf)
+    for buf, n in ((ybuf, Bsz * L * Dm), (hbuf, Bsz * Dm * N)):
+        assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + n:] == 7.0)
+    yr, hr = oracle_run(inp, {})
+    P.compare(y, yr, "bf16", "y")
+    P.compare(hf, hr, "bf16", "h_final")
