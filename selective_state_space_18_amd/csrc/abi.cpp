@@ -564,27 +564,48 @@ int cplx_step_impl(const void *x, const void *delta, const float *delta_bias, co
 constexpr int64_t kSsdHeadDim = 64;
 constexpr int64_t kSsdChunk = 64;
 constexpr int64_t kSsdHeadsPerBlock = 2;
-// Blocks per CU the planner aims for: two 4-wave blocks fit on a CU at once,
-// and a few rounds of them smooth out the last round.
-constexpr int64_t kSsdBlocksPerCu = 4;
+// Blocks one CU holds at once: the output pass keeps two 4-wave blocks
+// (registers), the aggregate pass about three.
+constexpr int64_t kSsdOutSlotsPerCu = 2;
+constexpr int64_t kSsdAggSlotsPerCu = 3;
 
 bool ssd_supported_n(int64_t N) { return N == 32 || N == 64 || N == 128; }
 
-// Segments of whole 64-step chunks; SSM_OPT_SEGMENT_LEN (rounded up to a
-// chunk) overrides the automatic choice.
-void ssd_plan(int64_t Bsz, int64_t L, int64_t H, int cus, int *S, int64_t *seg_len) {
+// Segments of whole 64-step chunks.  A segment's chunks run one after another
+// in one block, so a pass takes about (rounds of resident blocks) x (chunks
+// per segment) chunk-times: the plan minimises that for the output pass plus
+// the aggregate pass (which does about a third of a chunk's work, over all
+// segments but the last), plus the segment states every extra segment moves
+// through HBM (written by the aggregate pass, read and written by the carry,
+// read by the output pass: 16 bytes per state element, counted at about
+// 4 TB/s against a chunk-time of about 11 us).  SSM_OPT_SEGMENT_LEN (rounded
+// up to a chunk) overrides it.
+void ssd_plan(int64_t Bsz, int64_t L, int64_t H, int64_t N, int cus, int *S, int64_t *seg_len) {
     const int64_t nchunks = (L + kSsdChunk - 1) / kSsdChunk;
     const int64_t rows = Bsz * ((H + kSsdHeadsPerBlock - 1) / kSsdHeadsPerBlock);
-    int64_t cps;
+    const int64_t c = cus > 0 ? cus : 256;
+    int64_t cps = 1;
     const int64_t forced = g_opt_segment_len.load();
     if (nchunks <= 0 || rows <= 0) {
         cps = 1;
     } else if (forced > 0) {
         cps = (forced + kSsdChunk - 1) / kSsdChunk;
     } else {
-        const int64_t want = (kSsdBlocksPerCu * (cus > 0 ? cus : 256) + rows - 1) / rows;
-        const int64_t segs = want < nchunks ? (want > 0 ? want : 1) : nchunks;
-        cps = (nchunks + segs - 1) / segs;
+        double best = -1.0;
+        const int64_t smax = nchunks < 256 ? nchunks : 256;
+        for (int64_t segs = 1; segs <= smax; ++segs) {
+            const int64_t per = (nchunks + segs - 1) / segs;
+            const int64_t sg = (nchunks + per - 1) / per;  // segments actually used
+            const double out = (double)((rows * sg + kSsdOutSlotsPerCu * c - 1) / (kSsdOutSlotsPerCu * c)) * per;
+            const double agg = sg > 1 ? 0.3 * (double)((rows * (sg - 1) + kSsdAggSlotsPerCu * c - 1) /
+                                                        (kSsdAggSlotsPerCu * c)) * per
+                                      : 0.0;
+            const double states = (double)(sg - 1) * (double)(Bsz * H * kSsdHeadDim * N) / 2.75e6;
+            if (best < 0 || out + agg + states < best - 1e-9) {
+                best = out + agg + states;
+                cps = per;
+            }
+        }
     }
     if (cps < 1) cps = 1;
     *seg_len = cps * kSsdChunk;
@@ -667,7 +688,7 @@ int ssd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     p.H = H;
     p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
     p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
-    ssd_plan(Bsz, L, H, cus, &p.S, &p.seg_len);
+    ssd_plan(Bsz, L, H, N, cus, &p.S, &p.seg_len);
     if (dtype == SSM_F32) {  // the fp64 recurrence runs over all of time at once
         p.S = 1;
         p.seg_len = L;
