@@ -826,12 +826,26 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     q.dD = dD;
     q.dh_init = dh_init;
     q.blocks_per_row = (p.tiles_per_b + kWavesPerBlock - 1) / kWavesPerBlock;
-    // segments per wave: as many as still leave about 8 blocks per CU
+    // Segments per wave.  A group's segments run one after another in one
+    // block and a CU holds two main-kernel blocks at once, so the kernel takes
+    // about (rounds of resident blocks) x (segments per group): pick the G
+    // that minimises it (ties: the larger G, fewer partial sums), with at
+    // most 256 groups.
     const int64_t rows = Bsz * q.blocks_per_row;
-    const int64_t want = 8 * (int64_t)(cus > 0 ? cus : 256);
-    int64_t G = (int64_t)p.S * rows / want;
-    if (G < 1) G = 1;
-    if (G > p.S) G = p.S;
+    const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+    int64_t G = p.S;
+    {
+        int64_t best = -1;
+        for (int64_t g = p.S; g >= 1; --g) {
+            const int64_t groups = (p.S + g - 1) / g;
+            if (groups > 256) break;
+            const int64_t cost = (groups * rows + slots - 1) / slots * g;
+            if (best < 0 || cost < best) {
+                best = cost;
+                G = g;
+            }
+        }
+    }
     q.seg_per_group = (int)G;
     q.n_groups = (int)((p.S + G - 1) / G);
     if ((int64_t)q.n_groups * rows >= ((int64_t)1 << 31) ||
