@@ -186,7 +186,8 @@ struct alignas(16) SsdSmemOut {
     T c[kSsdQ][ssd_pitch(N)];
     T b[kSsdQ][ssd_pitch(N)];
     T x[kSsdQ][ssd_pitch(kSsdHeads * kSsdP)];      // the block's 128 channels
-    alignas(16) float sc[kSsdHeads][4][kSsdQ];      // per head: c_t log2(e), k_t, w_t, exp(c_t)
+    // per head: c_t log2(e), k_t, w_t, exp(c_t), exp(-c_t) k_t
+    alignas(16) float sc[kSsdHeads][5][kSsdQ];
 };
 template <typename T, int N>
 struct alignas(16) SsdSmemAgg {
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(kSsdBlock, 2) void ssd_chunk_kernel(SsdParams p) {
         // ---- step scalars of this wave's head (lane = step); log decays are
         // kept in base-2 units (c2 = c log2 e) for the exp2 unit
         float cend;
+        bool split_decay;  // the mask factors as exp(c_t) exp(-c_s) (see below)
         {
             float dt = 0.f;
             if (lane < nc) {
@@ -332,11 +334,17 @@ __global__ __launch_bounds__(kSsdBlock, 2) void ssd_chunk_kernel(SsdParams p) {
             cend = cend2 * 0.6931471805599453f;
             // |a| below 1e-20 (zero included) takes the exact a -> 0 limit dt
             const float k = (p.euler_b || __builtin_fabsf(a) < 1e-20f) ? dt : ssd_expm1(la) / a;
+            // A chunk whose whole decay stays above 2^-64 keeps exp(-c_s) k_s
+            // below 2^64 k_s: far inside fp32 range, so the mask factors into
+            // a row scale and a column weight.  (cend2 is the same on every
+            // lane; the readfirstlane makes the branch scalar.)
+            split_decay = __builtin_amdgcn_readfirstlane((int)(cend2 >= -64.f)) != 0;
             if (dh == 0) {
                 sm.sc[hh][0][lane] = c2;
                 sm.sc[hh][1][lane] = k;
                 sm.sc[hh][2][lane] = fast_exp2(cend2 - c2) * k;
                 sm.sc[hh][3][lane] = fast_exp2(c2);
+                if constexpr (kOut) sm.sc[hh][4][lane] = split_decay ? fast_exp2(-c2) * k : 0.f;
             }
         }
         dec_total += cend;
@@ -378,52 +386,74 @@ __global__ __launch_bounds__(kSsdBlock, 2) void ssd_chunk_kernel(SsdParams p) {
                 mma(yacc[0], c0, hlo);
                 mma(yacc[1], c1, hlo);
             }
+            // y rows times exp(c_t)
+            auto row_scale = [&]() {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float4 e4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][3][32 * tt + 8 * m + 4 * g]);
-                    yacc[tt][4 * m] *= e4.x, yacc[tt][4 * m + 1] *= e4.y;
-                    yacc[tt][4 * m + 2] *= e4.z, yacc[tt][4 * m + 3] *= e4.w;
-                }
+                    for (int m = 0; m < 4; ++m) {
+                        const float4 e4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][3][32 * tt + 8 * m + 4 * g]);
+                        yacc[tt][4 * m] *= e4.x, yacc[tt][4 * m + 1] *= e4.y;
+                        yacc[tt][4 * m + 2] *= e4.z, yacc[tt][4 * m + 3] *= e4.w;
+                    }
+            };
             // mask and weight the G^T tiles -- M[t][s] = G[s][t] exp(c_t - c_s) k_s
             // for s <= t (lane = t, registers = s) -- split them, and add M x,
             // one 16-step half of each 32-step column tile at a time,
-            // alternating the two row tiles
-            const float ct0 = sm.sc[hh][0][li], ct1 = sm.sc[hh][0][32 + li];
-            auto masked = [&](const f32x16_t &gt, int st, int tt, float ct, int hf, Frag<T> &mh, Frag<T> &ml) {
-                const int t = 32 * tt + li;
-                float mv[8];
+            // alternating the two row tiles.  With the factored decay the
+            // tiles carry only exp(-c_s) k_s and the row scale exp(c_t) is
+            // applied once to C H + M x; otherwise each weight takes its own
+            // exponential and the row scale goes on C H alone.
+            auto mask_mx = [&](auto factored) {
+                constexpr bool kF = decltype(factored)::value;
+                const float ct0 = kF ? 0.f : sm.sc[hh][0][li], ct1 = kF ? 0.f : sm.sc[hh][0][32 + li];
+                auto masked = [&](const f32x16_t &gt, int st, int tt, float ct, int hf, Frag<T> &mh, Frag<T> &ml) {
+                    const int t = 32 * tt + li;
+                    float mv[8];
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2) {
-                    const int m = 2 * hf + m2;
-                    const int s0 = 32 * st + 8 * m + 4 * g;
-                    const float4 c4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][0][s0]);
-                    const float4 k4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][1][s0]);
-                    const float cs[4] = {c4.x, c4.y, c4.z, c4.w};
-                    const float ks[4] = {k4.x, k4.y, k4.z, k4.w};
+                    for (int m2 = 0; m2 < 2; ++m2) {
+                        const int m = 2 * hf + m2;
+                        const int s0 = 32 * st + 8 * m + 4 * g;
+                        float ws[4];
+                        if constexpr (kF) {
+                            const float4 w4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][4][s0]);
+                            ws[0] = w4.x, ws[1] = w4.y, ws[2] = w4.z, ws[3] = w4.w;
+                        } else {
+                            const float4 c4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][0][s0]);
+                            const float4 k4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][1][s0]);
+                            ws[0] = fast_exp2(ct - c4.x) * k4.x, ws[1] = fast_exp2(ct - c4.y) * k4.y;
+                            ws[2] = fast_exp2(ct - c4.z) * k4.z, ws[3] = fast_exp2(ct - c4.w) * k4.w;
+                        }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float w = fast_exp2(ct - cs[q]) * ks[q];
-                        mv[4 * m2 + q] = (s0 + q <= t) ? gt[4 * m + q] * w : 0.f;
+                        for (int q = 0; q < 4; ++q) {
+                            const float v = gt[4 * m + q] * ws[q];
+                            mv[4 * m2 + q] = (st < tt || s0 + q <= t) ? v : 0.f;  // below the diagonal tile: all kept
+                        }
                     }
-                }
-                split(mv, mh, ml);
-            };
+                    split(mv, mh, ml);
+                };
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const Frag<T> x0 = tr_frag(&sm.x[0][0], kPX, 16 * hf, xcol, lane);       // steps 0..31
-                const Frag<T> x1 = tr_frag(&sm.x[0][0], kPX, 32 + 16 * hf, xcol, lane);  // steps 32..63
-                Frag<T> h00, l00, h01, l01, h11, l11;
-                masked(g00, 0, 0, ct0, hf, h00, l00);
-                masked(g01, 0, 1, ct1, hf, h01, l01);
-                masked(g11, 1, 1, ct1, hf, h11, l11);
-                mma(yacc[0], h00, x0);
-                mma(yacc[1], h01, x0);
-                mma(yacc[0], l00, x0);
-                mma(yacc[1], h11, x1);
-                mma(yacc[1], l01, x0);
-                mma(yacc[1], l11, x1);
+                for (int hf = 0; hf < 2; ++hf) {
+                    const Frag<T> x0 = tr_frag(&sm.x[0][0], kPX, 16 * hf, xcol, lane);       // steps 0..31
+                    const Frag<T> x1 = tr_frag(&sm.x[0][0], kPX, 32 + 16 * hf, xcol, lane);  // steps 32..63
+                    Frag<T> h00, l00, h01, l01, h11, l11;
+                    masked(g00, 0, 0, ct0, hf, h00, l00);
+                    masked(g01, 0, 1, ct1, hf, h01, l01);
+                    masked(g11, 1, 1, ct1, hf, h11, l11);
+                    mma(yacc[0], h00, x0);
+                    mma(yacc[1], h01, x0);
+                    mma(yacc[0], l00, x0);
+                    mma(yacc[1], h11, x1);
+                    mma(yacc[1], l01, x0);
+                    mma(yacc[1], l11, x1);
+                }
+            };
+            if (split_decay) {
+                mask_mx(std::true_type{});
+                row_scale();
+            } else {
+                row_scale();
+                mask_mx(std::false_type{});
             }
             // + D x, then y rows t < nc (the row offset goes in the scalar
             // offset of the store)
