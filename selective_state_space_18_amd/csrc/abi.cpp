@@ -567,7 +567,7 @@ constexpr int64_t kSsdHeadsPerBlock = 2;
 // Blocks one CU holds at once: the output pass keeps two 4-wave blocks
 // (registers), the aggregate pass about three.
 constexpr int64_t kSsdOutSlotsPerCu = 2;
-constexpr int64_t kSsdAggSlotsPerCu = 3;
+constexpr int64_t kSsdAggSlotsPerCu = 4;
 
 bool ssd_supported_n(int64_t N) { return N == 32 || N == 64 || N == 128; }
 

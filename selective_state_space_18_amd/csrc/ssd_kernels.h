@@ -179,22 +179,41 @@ __device__ __forceinline__ float ssd_expm1(float z) {
     return expm1_and_exp(z, e);
 }
 
-// LDS of one block: the chunk's B, C and x rows as stored (row = step), at
-// the pitches above.  The aggregate pass needs no C.
-template <typename T, int N>
-struct alignas(16) SsdSmemOut {
-    T c[kSsdQ][ssd_pitch(N)];
-    T b[kSsdQ][ssd_pitch(N)];
-    T x[kSsdQ][ssd_pitch(kSsdHeads * kSsdP)];      // the block's 128 channels
-    // per head: c_t log2(e), k_t, w_t, exp(c_t), exp(-c_t) k_t
-    alignas(16) float sc[kSsdHeads][5][kSsdQ];
-};
-template <typename T, int N>
-struct alignas(16) SsdSmemAgg {
-    T b[kSsdQ][ssd_pitch(N)];
-    T x[kSsdQ][ssd_pitch(kSsdHeads * kSsdP)];
-    alignas(16) float sc[kSsdHeads][4][kSsdQ];
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Rows 0..63 of a chunk operand (row r at byte r * row_bytes of the
+// descriptor, kRowDw dwords each) into LDS rows `pitch` elements apart: one
+// dword load per row that writes straight into LDS (lane l moves dword l to
+// the row start + 4 l), rows dealt out to the 4 waves.  The row offset goes in
+// the scalar offset, which the descriptor's range check includes: bytes
+// outside the range arrive as zeros.  Nothing waits here: the caller waits
+// for the vector-memory counter before the rows are read.
+template <int kRowDw>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, bf16 *dst, int pitch, int32_t row_bytes, int wave,
+                                         int lane) {
+    static_assert(kRowDw == 16 || kRowDw == 32 || kRowDw == 64, "rows of 16, 32 or 64 dwords");
+#pragma unroll
+    for (int i = 0; i < kSsdQ / 4; ++i) {
+        const int row = wave + 4 * i;
+        if (kRowDw == 64 || lane < kRowDw)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + row * pitch), 4, lane * 4,
+                                                     row * row_bytes, 0, 0);
+    }
+}
+// Wait until every vector-memory operation of this wave (the row loads above
+// among them) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// A barrier for handing LDS buffers between waves: this wave's LDS accesses
+// are complete and every wave has arrived.  Unlike __syncthreads it does not
+// wait for the wave's vector-memory operations (row loads into LDS still in
+// flight, stores), which its release fence would.  The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
 
 // The state tiles of one wave (N x 32, fp32) to or from [Bsz][Dm][N]
 // memory: lane (channel, g) holds n = 32 nt + 8 m + 4 g + (0..3) in
@@ -219,17 +238,48 @@ __device__ __forceinline__ void state_store(const f32x16_t (&hs)[N / 32], float 
                 make_float4(hs[nt][4 * m], hs[nt][4 * m + 1], hs[nt][4 * m + 2], hs[nt][4 * m + 3]);
 }
 
+// LDS of one block, chunk rows as stored (row = step) at the pitches above,
+// one __shared__ array per buffer so that the compiler can tell them apart
+// (it then inserts no wait for a row load in flight into one buffer before
+// reading another).
+//
+// Output pass (two blocks per compute unit): x (the block's 128 channels)
+// and the step scalars are double-buffered -- the next chunk's rows arrive
+// while the current chunk is in use, the chunk loop unrolled by two so that
+// each buffer's role is fixed in each half -- and the single B and C buffers
+// are refilled as soon as every wave is done with them.  sc holds, per head:
+// c_t log2(e), k_t, w_t, exp(c_t), exp(-c_t) k_t.
+//
+// Aggregate pass (four blocks per compute unit, no C): one buffer each, rows
+// loaded and then used; the other resident blocks cover the wait.  Each wave
+// keeps its w_t in a row of its own.
 template <typename T, int N, bool kOut>
-__global__ __launch_bounds__(kSsdBlock, 2) void ssd_chunk_kernel(SsdParams p) {
+__global__ __launch_bounds__(kSsdBlock, kOut ? 2 : 4) void ssd_chunk_kernel(SsdParams p) {
+    static_assert(std::is_same<T, bf16>::value, "the matrix-core path stores bf16");
     constexpr int kNT = N / 32;  // 32-row state tiles
     constexpr int kNS = N / 16;  // K = 16 steps over the state
-    constexpr int kPE = Piece<T>::kElems;
-    typedef typename std::conditional<kOut, SsdSmemOut<T, N>, SsdSmemAgg<T, N>>::type Smem;
-    __shared__ Smem sm;
+    constexpr int kPX = ssd_pitch(kSsdHeads * kSsdP);
+    constexpr int kPN = ssd_pitch(N);
+    constexpr int kScH = kOut ? kSsdHeads : 1, kScR = kOut ? 5 : 1, kScQ = kOut ? kSsdQ : 1;
+    typedef float Scalars[kScH][kScR][kScQ];
+    __shared__ __attribute__((aligned(16))) bf16 lx0[kSsdQ * kPX];
+    __shared__ __attribute__((aligned(16))) bf16 lx1[(kOut ? kSsdQ : 1) * kPX];
+    __shared__ __attribute__((aligned(16))) bf16 lb0[kSsdQ * kPN];
+    __shared__ __attribute__((aligned(16))) bf16 lc[(kOut ? kSsdQ : 1) * kPN];
+    __shared__ __attribute__((aligned(16))) Scalars lsc0;
+    __shared__ __attribute__((aligned(16))) Scalars lsc1;
+    __shared__ __attribute__((aligned(16))) float lw[kOut ? 1 : kSsdBlock / kWave][kSsdQ];
+    static_assert(kOut ? 2 * kSsdQ * kPX * 2 + 2 * kSsdQ * kPN * 2 + 2 * (int)sizeof(Scalars) + 4 * 64 <= 81920
+                       : kSsdQ * kPX * 2 + kSsdQ * kPN * 2 + 4 * kSsdQ * 4 + 64 <= 40960,
+                  "the blocks resident on one compute unit must fit its 160 KB of LDS");
+    // The row buffers are written only by the row loads, which the compiler
+    // does not count as stores to them: let their addresses escape so that
+    // reads of them are not folded away.
+    __asm__ volatile("" ::"s"(lx0), "s"(lx1), "s"(lb0), "s"(lc) : "memory");
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int hh = wave >> 1;   // head of the block
     const int dh = wave & 1;    // channel half of the head
     const int g = lane >> 5;
@@ -248,6 +298,7 @@ __global__ __launch_bounds__(kSsdBlock, 2) void ssd_chunk_kernel(SsdParams p) {
     const int64_t d = h * kSsdP + 32 * dh + li;                // this lane's channel
     const int ncols = heads_here * kSsdP;
     const int64_t BD = p.Bsz * p.Dm;
+    const int xcol = kSsdP * hh + 32 * dh;                     // this wave's first column of x rows
 
     const float a = p.A[h];
     const float bias = p.delta_bias ? p.delta_bias[h] : 0.f;
@@ -268,211 +319,96 @@ __global__ __launch_bounds__(kSsdBlock, 2) void ssd_chunk_kernel(SsdParams p) {
     const int64_t cps = p.seg_len / kSsdQ;
     const int64_t ch_begin = (int64_t)seg * cps;
     const int64_t ch_end = ch_begin + cps < nchunks ? ch_begin + cps : nchunks;
-    float dec_total = 0.f;
+    auto rows_of = [&](int64_t c) -> int { return (int)(p.L - c * kSsdQ < kSsdQ ? p.L - c * kSsdQ : kSsdQ); };
+    const T *xblk = static_cast<const T *>(p.x) + b * p.L * p.Dm + col0;
+    const T *bblk = static_cast<const T *>(p.B) + b * p.L * N;
+    const T *cblk = static_cast<const T *>(p.C) + b * p.L * N;
 
-    for (int64_t ch = ch_begin; ch < ch_end; ++ch) {
-        const int64_t t0 = ch * kSsdQ;
-        const int nc = (int)(p.L - t0 < kSsdQ ? p.L - t0 : kSsdQ);
-        __syncthreads();  // the previous chunk is done with LDS
+    // ---- operand rows of chunk c into LDS (no wait)
+    auto fetch_x = [&](bf16 *dst, int64_t c) {
+        const int32_t bytes = (int32_t)(((int64_t)(rows_of(c) - 1) * p.Dm + ncols) * (int64_t)sizeof(T));
+        dma_rows<kSsdHeads * kSsdP / 2>(make_rsrc(xblk + c * kSsdQ * p.Dm, bytes), dst, kPX,
+                                        (int32_t)(p.Dm * (int64_t)sizeof(T)), wave, lane);
+    };
+    auto fetch_bc = [&](const T *src, bf16 *dst, int64_t c) {
+        dma_rows<N / 2>(make_rsrc(src + c * kSsdQ * N, rows_of(c) * N * (int)sizeof(T)), dst, kPN,
+                        N * (int)sizeof(T), wave, lane);
+    };
 
-        // ---- stage the chunk's B, C and x rows (16-byte pieces, coalesced)
-        {
-            constexpr int kRowPieces = N / kPE;
-            constexpr int kBPieces = kSsdQ * kRowPieces;
-            const T *Bp = static_cast<const T *>(p.B) + (b * p.L + t0) * N;
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bp, nc * N * (int)sizeof(T));
-#pragma unroll
-            for (int i = 0; i < kBPieces / kSsdBlock; ++i) {
-                const int pid = tid + kSsdBlock * i;
-                const int s = pid / kRowPieces, n0 = kPE * (pid % kRowPieces);
-                store_piece(&sm.b[s][n0], load_piece(rb, (s * N + n0) * (int)sizeof(T)));
-            }
-            if constexpr (kOut) {
-                const T *Cp = static_cast<const T *>(p.C) + (b * p.L + t0) * N;
-                const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cp, nc * N * (int)sizeof(T));
-#pragma unroll
-                for (int i = 0; i < kBPieces / kSsdBlock; ++i) {
-                    const int pid = tid + kSsdBlock * i;
-                    const int s = pid / kRowPieces, n0 = kPE * (pid % kRowPieces);
-                    store_piece(&sm.c[s][n0], load_piece(rc, (s * N + n0) * (int)sizeof(T)));
-                }
-            }
-            const T *Xp = static_cast<const T *>(p.x) + (b * p.L + t0) * p.Dm + col0;
-            const int32_t xbytes = (int32_t)(((int64_t)(nc - 1) * p.Dm + ncols) * (int64_t)sizeof(T));
-            const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xp, xbytes);
-            constexpr int kXRow = kSsdHeads * kSsdP / kPE;
-#pragma unroll
-            for (int i = 0; i < kSsdQ * kXRow / kSsdBlock; ++i) {
-                const int pid = tid + kSsdBlock * i;
-                const int s = pid / kXRow, c0 = kPE * (pid % kXRow);
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (c0 < ncols) v = load_piece(rx, (int32_t)(((int64_t)s * p.Dm + c0) * (int64_t)sizeof(T)));
-                store_piece(&sm.x[s][c0], v);
-            }
+    // ---- delta of step `lane` of chunk c as stored (0 past the sequence or
+    // the segment).  It stays in the stored type until used, so that the
+    // compiler's wait for it sits at the use, not at the load.
+    auto load_delta = [&](int64_t c) -> T {
+        const int64_t n = c < ch_end ? rows_of(c) : 0;
+        const T *dp = static_cast<const T *>(p.delta) + (b * p.L + c * kSsdQ) * p.H;
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dp, (int32_t)(n * p.H * (int64_t)sizeof(T)));
+        return buf_load<T>(rd, (int32_t)(((int64_t)lane * p.H + h) * (int64_t)sizeof(T)), 0);
+    };
+
+    // ---- step scalars of chunk c for this wave's head (lane = step); log
+    // decays in base-2 units (c2 = c log2 e) for the exp2 unit.  The output
+    // pass keeps all five per head in scw (written by one wave of the head);
+    // the aggregate pass needs only w_t, which every wave writes to its own
+    // row wrow.  Returns the chunk's total log decay; `split` tells whether
+    // the causal mask may be factored (below).
+    auto scalars = [&](Scalars &scw, float *wrow, int64_t c, T dstored, bool &split) -> float {
+        float dt = 0.f;
+        if (lane < rows_of(c)) {
+            float v = to_f32(dstored) + bias;
+            if (p.delta_softplus) v = softplus_(v);
+            dt = v;
         }
-
-        // ---- step scalars of this wave's head (lane = step); log decays are
-        // kept in base-2 units (c2 = c log2 e) for the exp2 unit
-        float cend;
-        bool split_decay;  // the mask factors as exp(c_t) exp(-c_s) (see below)
-        {
-            float dt = 0.f;
-            if (lane < nc) {
-                const T *dp = static_cast<const T *>(p.delta) + (b * p.L + t0 + lane) * p.H + h;
-                float v = to_f32(*dp) + bias;
-                if (p.delta_softplus) v = softplus_(v);
-                dt = v;
-            }
-            const float la = dt * a;
-            float c2 = la * kLog2e;
+        const float la = dt * a;
+        float c2 = la * kLog2e;
 #pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const float o = __shfl_up(c2, off);
-                if (lane >= off) c2 += o;
-            }
-            const float cend2 = __shfl(c2, kWave - 1);
-            cend = cend2 * 0.6931471805599453f;
-            // |a| below 1e-20 (zero included) takes the exact a -> 0 limit dt
-            const float k = (p.euler_b || __builtin_fabsf(a) < 1e-20f) ? dt : ssd_expm1(la) / a;
-            // A chunk whose whole decay stays above 2^-64 keeps exp(-c_s) k_s
-            // below 2^64 k_s: far inside fp32 range, so the mask factors into
-            // a row scale and a column weight.  (cend2 is the same on every
-            // lane; the readfirstlane makes the branch scalar.)
-            split_decay = __builtin_amdgcn_readfirstlane((int)(cend2 >= -64.f)) != 0;
-            if (dh == 0) {
-                sm.sc[hh][0][lane] = c2;
-                sm.sc[hh][1][lane] = k;
-                sm.sc[hh][2][lane] = fast_exp2(cend2 - c2) * k;
-                sm.sc[hh][3][lane] = fast_exp2(c2);
-                if constexpr (kOut) sm.sc[hh][4][lane] = split_decay ? fast_exp2(-c2) * k : 0.f;
-            }
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float o = __shfl_up(c2, off);
+            if (lane >= off) c2 += o;
         }
-        dec_total += cend;
-        __syncthreads();
-        if (!head_ok) continue;
-
-        // x of this wave's 32 channels: the B operand over the chunk's steps
-        const int xcol = kSsdP * hh + 32 * dh;
-        constexpr int kPX = ssd_pitch(kSsdHeads * kSsdP);
-        constexpr int kPN = ssd_pitch(N);
-
-        if constexpr (kOut) {
-            // ---- y = exp(c_t) (C H) + (G o mask) x + D x over two 32-step row
-            // tiles.  One sweep over the state dimension accumulates C H for
-            // both row tiles and the three causal tiles of G^T = B C^T (rows
-            // s, columns t: (0,0), (0,1), (1,1)), which share the C fragments;
-            // hi and lo halves of the split state go in separate passes so
-            // that consecutive matrix instructions feed different
-            // accumulators.
-            f32x16_t yacc[2], g00, g01, g11;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) yacc[0][r] = yacc[1][r] = g00[r] = g01[r] = g11[r] = 0.f;
-#pragma unroll
-            for (int j = 0; j < kNS; ++j) {
-                const Frag<T> c0 = lds_frag(&sm.c[li][0], 16 * j, g);
-                const Frag<T> c1 = lds_frag(&sm.c[32 + li][0], 16 * j, g);
-                const Frag<T> b0 = lds_frag(&sm.b[li][0], 16 * j, g);
-                const Frag<T> b1 = lds_frag(&sm.b[32 + li][0], 16 * j, g);
-                float hv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) hv[e] = hs[j / 2][8 * (j % 2) + e];
-                Frag<T> hhi, hlo;
-                split(hv, hhi, hlo);
-                mma(yacc[0], c0, hhi);
-                mma(yacc[1], c1, hhi);
-                mma(g00, b0, c0);
-                mma(g01, b0, c1);
-                mma(g11, b1, c1);
-                mma(yacc[0], c0, hlo);
-                mma(yacc[1], c1, hlo);
-            }
-            // y rows times exp(c_t)
-            auto row_scale = [&]() {
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const float4 e4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][3][32 * tt + 8 * m + 4 * g]);
-                        yacc[tt][4 * m] *= e4.x, yacc[tt][4 * m + 1] *= e4.y;
-                        yacc[tt][4 * m + 2] *= e4.z, yacc[tt][4 * m + 3] *= e4.w;
-                    }
-            };
-            // mask and weight the G^T tiles -- M[t][s] = G[s][t] exp(c_t - c_s) k_s
-            // for s <= t (lane = t, registers = s) -- split them, and add M x,
-            // one 16-step half of each 32-step column tile at a time,
-            // alternating the two row tiles.  With the factored decay the
-            // tiles carry only exp(-c_s) k_s and the row scale exp(c_t) is
-            // applied once to C H + M x; otherwise each weight takes its own
-            // exponential and the row scale goes on C H alone.
-            auto mask_mx = [&](auto factored) {
-                constexpr bool kF = decltype(factored)::value;
-                const float ct0 = kF ? 0.f : sm.sc[hh][0][li], ct1 = kF ? 0.f : sm.sc[hh][0][32 + li];
-                auto masked = [&](const f32x16_t &gt, int st, int tt, float ct, int hf, Frag<T> &mh, Frag<T> &ml) {
-                    const int t = 32 * tt + li;
-                    float mv[8];
-#pragma unroll
-                    for (int m2 = 0; m2 < 2; ++m2) {
-                        const int m = 2 * hf + m2;
-                        const int s0 = 32 * st + 8 * m + 4 * g;
-                        float ws[4];
-                        if constexpr (kF) {
-                            const float4 w4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][4][s0]);
-                            ws[0] = w4.x, ws[1] = w4.y, ws[2] = w4.z, ws[3] = w4.w;
-                        } else {
-                            const float4 c4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][0][s0]);
-                            const float4 k4 = *reinterpret_cast<const float4 *>(&sm.sc[hh][1][s0]);
-                            ws[0] = fast_exp2(ct - c4.x) * k4.x, ws[1] = fast_exp2(ct - c4.y) * k4.y;
-                            ws[2] = fast_exp2(ct - c4.z) * k4.z, ws[3] = fast_exp2(ct - c4.w) * k4.w;
-                        }
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float v = gt[4 * m + q] * ws[q];
-                            mv[4 * m2 + q] = (st < tt || s0 + q <= t) ? v : 0.f;  // below the diagonal tile: all kept
-                        }
-                    }
-                    split(mv, mh, ml);
-                };
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const Frag<T> x0 = tr_frag(&sm.x[0][0], kPX, 16 * hf, xcol, lane);       // steps 0..31
-                    const Frag<T> x1 = tr_frag(&sm.x[0][0], kPX, 32 + 16 * hf, xcol, lane);  // steps 32..63
-                    Frag<T> h00, l00, h01, l01, h11, l11;
-                    masked(g00, 0, 0, ct0, hf, h00, l00);
-                    masked(g01, 0, 1, ct1, hf, h01, l01);
-                    masked(g11, 1, 1, ct1, hf, h11, l11);
-                    mma(yacc[0], h00, x0);
-                    mma(yacc[1], h01, x0);
-                    mma(yacc[0], l00, x0);
-                    mma(yacc[1], h11, x1);
-                    mma(yacc[1], l01, x0);
-                    mma(yacc[1], l11, x1);
-                }
-            };
-            if (split_decay) {
-                mask_mx(std::true_type{});
-                row_scale();
-            } else {
-                row_scale();
-                mask_mx(std::false_type{});
-            }
-            // + D x, then y rows t < nc (the row offset goes in the scalar
-            // offset of the store)
-            T *Yp = static_cast<T *>(p.y) + (b * p.L + t0) * p.Dm;
-            const __amdgpu_buffer_rsrc_t ry = make_rsrc(Yp, (int32_t)((int64_t)nc * p.Dm * (int64_t)sizeof(T)));
-            const int32_t vrow = (int32_t)(((int64_t)(4 * g) * p.Dm + d) * (int64_t)sizeof(T));
-            const int32_t rowb = (int32_t)(p.Dm * (int64_t)sizeof(T));
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int tq = 32 * tt + 8 * (r / 4) + (r % 4);  // t minus 4g
-                    const float v = fma_(Dd, to_f32(sm.x[tq + 4 * g][xcol + li]), yacc[tt][r]);
-                    buf_store(from_acc<T>(v), ry, vrow, tq * rowb);
-                }
+        const float cend2 = __shfl(c2, kWave - 1);
+        // |a| below 1e-20 (zero included) takes the exact a -> 0 limit dt
+        const float k = (p.euler_b || __builtin_fabsf(a) < 1e-20f) ? dt : ssd_expm1(la) / a;
+        // A chunk whose whole decay stays above 2^-64 keeps exp(-c_s) k_s
+        // below 2^64 k_s: far inside fp32 range, so the mask factors into a
+        // row scale and a column weight.  (cend2 is the same on every lane;
+        // the readfirstlane makes the branch scalar.)
+        split = __builtin_amdgcn_readfirstlane((int)(cend2 >= -64.f)) != 0;
+        if constexpr (!kOut) {
+            wrow[lane] = fast_exp2(cend2 - c2) * k;
+        } else if (dh == 0) {
+            scw[hh][0][lane] = c2;
+            scw[hh][1][lane] = k;
+            scw[hh][2][lane] = fast_exp2(cend2 - c2) * k;
+            scw[hh][3][lane] = fast_exp2(c2);
+            scw[hh][4][lane] = split ? fast_exp2(-c2) * k : 0.f;
         }
+        return cend2 * 0.6931471805599453f;
+    };
 
-        // ---- H = exp(c_end) H + B^T (w x): the hi and lo halves of the
-        // weighted x in separate passes over the state tiles
+    // y of the previous chunk, held until the next chunk's rows are in (so
+    // that waiting for those does not wait for these stores): rows t of
+    // 32 tt + 8 (r / 4) + 4 g + r % 4 in pair r / 2 of tile tt
+    bf16x2_t ypend[2][8];
+    int64_t ypend_t0 = -1;
+    auto store_y = [&]() {
+        T *Yp = static_cast<T *>(p.y) + (b * p.L + ypend_t0) * p.Dm;
+        const int nrows = rows_of(ypend_t0 / kSsdQ);
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(Yp, (int32_t)((int64_t)nrows * p.Dm * (int64_t)sizeof(T)));
+        const int32_t vrow = (int32_t)(((int64_t)(4 * g) * p.Dm + d) * (int64_t)sizeof(T));
+        const int32_t rowb = (int32_t)(p.Dm * (int64_t)sizeof(T));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tq = 32 * tt + 8 * (r / 4) + (r % 4);  // t minus 4g
+                buf_store(ypend[tt][r / 2][r % 2], ry, vrow, tq * rowb);
+            }
+    };
+
+    // ---- H = exp(c_end) H + B^T (w x) over the chunk's rows in xr / br:
+    // the hi and lo halves of the weighted x in separate passes over the
+    // state tiles
+    auto state_update = [&](const bf16 *xr, const bf16 *br, const float *w, float cend) {
         const float decay = fast_exp2(cend * kLog2e);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
@@ -481,24 +417,211 @@ __global__ __launch_bounds__(kSsdBlock, 2) void ssd_chunk_kernel(SsdParams p) {
 #pragma unroll
         for (int j = 0; j < kSsdQ / 16; ++j) {
             float wv[8];
-            lds_slots(&sm.sc[hh][2][0], 16 * j, g, wv);
-            const Frag<T> xj = tr_frag(&sm.x[0][0], kPX, 16 * j, xcol, lane);
+            lds_slots(w, 16 * j, g, wv);
+            const Frag<T> xj = tr_frag(xr, kPX, 16 * j, xcol, lane);
 #pragma unroll
             for (int e = 0; e < 8; ++e) wv[e] *= frag_elem(xj, e);
             Frag<T> whi, wlo;
             split(wv, whi, wlo);
             Frag<T> bt[kNT];
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) bt[nt] = tr_frag(&sm.b[0][0], kPN, 16 * j, 32 * nt, lane);
+            for (int nt = 0; nt < kNT; ++nt) bt[nt] = tr_frag(br, kPN, 16 * j, 32 * nt, lane);
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) mma(hs[nt], bt[nt], whi);
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) mma(hs[nt], bt[nt], wlo);
         }
+    };
+
+    float dec_total = 0.f;
+    float cend_cur = 0.f, cend_next = 0.f;
+    bool split_cur = true, split_next = true;
+
+    if constexpr (kOut) {
+        // ---- one chunk of the output pass: its rows are in xr / br and lc, its
+        // scalars in scr; the next chunk's go to xw / bw / scw
+        auto chunk = [&](int64_t ch, const bf16 *xr, bf16 *xw, const bf16 *br, bf16 *bw, const Scalars &scr,
+                         Scalars &scw) {
+            const bool more = ch + 1 < ch_end;
+            wait_vmem();      // this wave's row loads of the chunk have landed
+            __syncthreads();  // ... and every wave's; the step scalars are written
+            dec_total += cend_cur;
+            if (kOut && ypend_t0 >= 0 && head_ok) store_y();
+            const T delta_next = load_delta(ch + 1);
+            if (more) fetch_x(xw, ch + 1);
+            const float(*sc)[kSsdQ] = scr[hh];
+
+            if constexpr (kOut) {
+                // ---- y = exp(c_t) (C H) + (G o mask) x + D x over two 32-step row
+                // tiles.  One sweep over the state dimension accumulates C H for
+                // both row tiles and the three causal tiles of G^T = B C^T (rows
+                // s, columns t: (0,0), (0,1), (1,1)), which share the C fragments;
+                // hi and lo halves of the split state go in separate passes so
+                // that consecutive matrix instructions feed different
+                // accumulators.
+                f32x16_t yacc[2], g00, g01, g11;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) yacc[0][r] = yacc[1][r] = g00[r] = g01[r] = g11[r] = 0.f;
+                if (head_ok) {
+#pragma unroll
+                    for (int j = 0; j < kNS; ++j) {
+                        const Frag<T> c0 = lds_frag(lc + li * kPN, 16 * j, g);
+                        const Frag<T> c1 = lds_frag(lc + (32 + li) * kPN, 16 * j, g);
+                        const Frag<T> b0 = lds_frag(br + li * kPN, 16 * j, g);
+                        const Frag<T> b1 = lds_frag(br + (32 + li) * kPN, 16 * j, g);
+                        float hv[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) hv[e] = hs[j / 2][8 * (j % 2) + e];
+                        Frag<T> hhi, hlo;
+                        split(hv, hhi, hlo);
+                        mma(yacc[0], c0, hhi);
+                        mma(yacc[1], c1, hhi);
+                        mma(g00, b0, c0);
+                        mma(g01, b0, c1);
+                        mma(g11, b1, c1);
+                        mma(yacc[0], c0, hlo);
+                        mma(yacc[1], c1, hlo);
+                    }
+                }
+                // the next chunk's step scalars, here where the wait for its delta
+                // only covers what was issued at the top of this chunk
+                if (more) cend_next = scalars(scw, nullptr, ch + 1, delta_next, split_next);
+                // Let the y stores, the x rows and the delta issued at the top
+                // complete now, a sweep after their issue: otherwise the first
+                // reuse of a stored register would wait on the vector-memory
+                // counter after the row loads below and so for them too.
+                wait_vmem();
+                lds_barrier();  // every wave is done with C
+                if (more) fetch_bc(cblk, lc, ch + 1);
+                if (head_ok) state_update(xr, br, sc[2], cend_cur);
+                lds_barrier();  // every wave is done with B
+                if (more) fetch_bc(bblk, bw, ch + 1);
+
+                if (head_ok) {
+                    // y rows times exp(c_t)
+                    auto row_scale = [&]() {
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                            for (int m = 0; m < 4; ++m) {
+                                const float4 e4 = *reinterpret_cast<const float4 *>(&sc[3][32 * tt + 8 * m + 4 * g]);
+                                yacc[tt][4 * m] *= e4.x, yacc[tt][4 * m + 1] *= e4.y;
+                                yacc[tt][4 * m + 2] *= e4.z, yacc[tt][4 * m + 3] *= e4.w;
+                            }
+                    };
+                    // mask and weight the G^T tiles -- M[t][s] = G[s][t] exp(c_t - c_s)
+                    // k_s for s <= t (lane = t, registers = s) -- split them, and add
+                    // M x, one 16-step half of each 32-step column tile at a time,
+                    // alternating the two row tiles.  With the factored decay the
+                    // tiles carry only exp(-c_s) k_s and the row scale exp(c_t) is
+                    // applied once to C H + M x; otherwise each weight takes its own
+                    // exponential and the row scale goes on C H alone.
+                    auto mask_mx = [&](auto factored) {
+                        constexpr bool kF = decltype(factored)::value;
+                        const float ct0 = kF ? 0.f : sc[0][li], ct1 = kF ? 0.f : sc[0][32 + li];
+                        auto masked = [&](const f32x16_t &gt, int st, int tt, float ct, int hf, Frag<T> &mh,
+                                          Frag<T> &ml) {
+                            const int t = 32 * tt + li;
+                            float mv[8];
+#pragma unroll
+                            for (int m2 = 0; m2 < 2; ++m2) {
+                                const int m = 2 * hf + m2;
+                                const int s0 = 32 * st + 8 * m + 4 * g;
+                                float ws[4];
+                                if constexpr (kF) {
+                                    const float4 w4 = *reinterpret_cast<const float4 *>(&sc[4][s0]);
+                                    ws[0] = w4.x, ws[1] = w4.y, ws[2] = w4.z, ws[3] = w4.w;
+                                } else {
+                                    const float4 c4 = *reinterpret_cast<const float4 *>(&sc[0][s0]);
+                                    const float4 k4 = *reinterpret_cast<const float4 *>(&sc[1][s0]);
+                                    ws[0] = fast_exp2(ct - c4.x) * k4.x, ws[1] = fast_exp2(ct - c4.y) * k4.y;
+                                    ws[2] = fast_exp2(ct - c4.z) * k4.z, ws[3] = fast_exp2(ct - c4.w) * k4.w;
+                                }
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const float v = gt[4 * m + q] * ws[q];
+                                    // below the diagonal tile every entry is kept
+                                    mv[4 * m2 + q] = (st < tt || s0 + q <= t) ? v : 0.f;
+                                }
+                            }
+                            split(mv, mh, ml);
+                        };
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const Frag<T> x0 = tr_frag(xr, kPX, 16 * hf, xcol, lane);       // steps 0..31
+                            const Frag<T> x1 = tr_frag(xr, kPX, 32 + 16 * hf, xcol, lane);  // steps 32..63
+                            Frag<T> h00, l00, h01, l01, h11, l11;
+                            masked(g00, 0, 0, ct0, hf, h00, l00);
+                            masked(g01, 0, 1, ct1, hf, h01, l01);
+                            masked(g11, 1, 1, ct1, hf, h11, l11);
+                            mma(yacc[0], h00, x0);
+                            mma(yacc[1], h01, x0);
+                            mma(yacc[0], l00, x0);
+                            mma(yacc[1], h11, x1);
+                            mma(yacc[1], l01, x0);
+                            mma(yacc[1], l11, x1);
+                        }
+                    };
+                    if (split_cur) {
+                        mask_mx(std::true_type{});
+                        row_scale();
+                    } else {
+                        row_scale();
+                        mask_mx(std::false_type{});
+                    }
+                    // + D x, rounded to the stored type and held for the store
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 16; r += 2) {
+                            const int tq = 32 * tt + 8 * (r / 4) + (r % 4) + 4 * g;
+                            const f32x2_t v = {fma_(Dd, to_f32(xr[tq * kPX + xcol + li]), yacc[tt][r]),
+                                               fma_(Dd, to_f32(xr[(tq + 1) * kPX + xcol + li]), yacc[tt][r + 1])};
+                            ypend[tt][r / 2] = __builtin_convertvector(v, bf16x2_t);
+                        }
+                    ypend_t0 = ch * kSsdQ;
+                }
+            }
+            cend_cur = cend_next;
+            split_cur = split_next;
+        };
+
+        if (ch_begin < ch_end) {
+            const T d0 = load_delta(ch_begin);
+            fetch_x(lx0, ch_begin);
+            fetch_bc(bblk, lb0, ch_begin);
+            fetch_bc(cblk, lc, ch_begin);
+            cend_cur = scalars(lsc0, nullptr, ch_begin, d0, split_cur);
+        }
+        for (int64_t ch = ch_begin; ch < ch_end; ch += 2) {
+            // even chunks of the segment read x and the scalars from buffers 0
+            // and fill buffers 1, odd ones the other way round
+            chunk(ch, lx0, lx1, lb0, lb0, lsc0, lsc1);
+            if (ch + 1 < ch_end) chunk(ch + 1, lx1, lx0, lb0, lb0, lsc1, lsc0);
+        }
+    } else {
+        // aggregate pass: rows of the chunk in, then its state update; the
+        // delta is fetched one chunk ahead
+        float *wrow = lw[kOut ? 0 : wave];
+        T delta_next = load_delta(ch_begin);
+        for (int64_t ch = ch_begin; ch < ch_end; ++ch) {
+            fetch_x(lx0, ch);
+            fetch_bc(bblk, lb0, ch);
+            const T delta_cur = delta_next;
+            delta_next = load_delta(ch + 1);
+            wait_vmem();      // this wave's row loads have landed
+            __syncthreads();  // ... and every wave's
+            bool factored;    // (the aggregate pass has no mask)
+            const float cend = scalars(lsc0, wrow, ch, delta_cur, factored);
+            dec_total += cend;
+            if (head_ok) state_update(lx0, lb0, wrow, cend);
+            lds_barrier();    // every wave is done with the rows
+        }
     }
 
     if (!head_ok) return;
     if constexpr (kOut) {
+        if (ypend_t0 >= 0) store_y();
         if (seg == p.S - 1 && p.h_final != nullptr) state_store<N>(hs, p.h_final + (b * p.Dm + d) * N, g);
     } else {
         state_store<N>(hs, p.agg + ((int64_t)seg * BD + b * p.Dm + d) * N, g);
