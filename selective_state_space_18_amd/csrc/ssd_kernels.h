@@ -25,10 +25,11 @@
 //
 // Layout of work: a block of 4 waves serves two heads of one batch row over a
 // segment of chunks; wave w takes head w/2 and channels 32 (w%2) .. +32 of
-// it.  Chunk inputs are staged in LDS as stored (one row per step); operands
-// whose contraction runs over the steps (x, and B for the state update) are
-// read from those rows with gfx950's transposing LDS load, the others as two
-// 8-byte pieces per lane.
+// it.  Chunk inputs are staged in LDS as stored (one row per step), moved
+// there by buffer loads that write LDS directly, while the previous chunk is
+// computed; operands whose contraction runs over the steps (x, and B for the
+// state update) are read from those rows with gfx950's transposing LDS load,
+// the others as two 8-byte pieces per lane.
 // Time is cut into segments joined as in the diagonal scan: an aggregate pass
 // (end state of each segment from zero, and its total log decay), a carry
 // pass, and an output pass that reruns each segment from its entering state.
@@ -107,21 +108,6 @@ __device__ __forceinline__ void split(const float (&v)[8], Frag<bf16> &hi, Frag<
     lo.v = __builtin_bit_cast(bf16x8_t, l);
 }
 
-// acc += A B with A given as fp32 values (split in the bf16 path), B exact.
-__device__ __forceinline__ void mma_fa(f32x16_t &acc, const float (&a)[8], const Frag<bf16> &b) {
-    Frag<bf16> hi, lo;
-    split(a, hi, lo);
-    mma(acc, hi, b);
-    mma(acc, lo, b);
-}
-// acc += A B with A exact, B given as fp32 values.
-__device__ __forceinline__ void mma_fb(f32x16_t &acc, const Frag<bf16> &a, const float (&b)[8]) {
-    Frag<bf16> hi, lo;
-    split(b, hi, lo);
-    mma(acc, a, hi);
-    mma(acc, a, lo);
-}
-
 // The fragment of one LDS row (matrix row or column, k contiguous) for the
 // K = 16 step at k0.
 __device__ __forceinline__ Frag<bf16> lds_frag(const bf16 *row, int k0, int g) {
@@ -160,19 +146,6 @@ __device__ __forceinline__ void lds_slots(const float *v, int k0, int g, float (
     o[4] = b.x, o[5] = b.y, o[6] = b.z, o[7] = b.w;
 }
 
-// One 16-byte element group of a storage row and its 16/sizeof(T) values.
-template <typename T>
-struct Piece {
-    static constexpr int kElems = 16 / (int)sizeof(T);
-};
-__device__ __forceinline__ u32x4_t load_piece(__amdgpu_buffer_rsrc_t r, int32_t voff) {
-    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-// A piece stored into an LDS row (rows are 8-byte aligned: two 8-byte writes).
-__device__ __forceinline__ void store_piece(bf16 *dst, const u32x4_t &v) {
-    reinterpret_cast<uint2 *>(dst)[0] = make_uint2(v[0], v[1]);
-    reinterpret_cast<uint2 *>(dst)[1] = make_uint2(v[2], v[3]);
-}
 // exp(z) - 1 on the transcendental unit (relative error near 1e-7).
 __device__ __forceinline__ float ssd_expm1(float z) {
     float e;
@@ -569,15 +542,20 @@ __global__ __launch_bounds__(kSsdBlock, kOut ? 2 : 4) void ssd_chunk_kernel(SsdP
                         row_scale();
                         mask_mx(std::false_type{});
                     }
-                    // + D x, rounded to the stored type and held for the store
+                    // + D x, with x from transposing reads of this wave's columns
+                    // (slot e of the K = 16 step at 32 tt + 16 hf is the row of
+                    // register 8 hf + e of row tile tt), rounded to the stored type
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                        for (int r = 0; r < 16; r += 2) {
-                            const int tq = 32 * tt + 8 * (r / 4) + (r % 4) + 4 * g;
-                            const f32x2_t v = {fma_(Dd, to_f32(xr[tq * kPX + xcol + li]), yacc[tt][r]),
-                                               fma_(Dd, to_f32(xr[(tq + 1) * kPX + xcol + li]), yacc[tt][r + 1])};
-                            ypend[tt][r / 2] = __builtin_convertvector(v, bf16x2_t);
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const Frag<T> xf = tr_frag(xr, kPX, 32 * tt + 16 * hf, xcol, lane);
+#pragma unroll
+                            for (int e = 0; e < 8; e += 2) {
+                                const f32x2_t v = {fma_(Dd, frag_elem(xf, e), yacc[tt][8 * hf + e]),
+                                                   fma_(Dd, frag_elem(xf, e + 1), yacc[tt][8 * hf + e + 1])};
+                                ypend[tt][(8 * hf + e) / 2] = __builtin_convertvector(v, bf16x2_t);
+                            }
                         }
                     ypend_t0 = ch * kSsdQ;
                 }
