@@ -153,6 +153,7 @@ __device__ __forceinline__ float ssd_expm1(float z) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // Rows 0..63 of a chunk operand (row r at byte r * row_bytes of the
 // descriptor, kRowDw dwords each) into LDS rows `pitch` elements apart: one
@@ -165,12 +166,17 @@ template <int kRowDw>
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, bf16 *dst, int pitch, int32_t row_bytes, int wave,
                                          int lane) {
     static_assert(kRowDw == 16 || kRowDw == 32 || kRowDw == 64, "rows of 16, 32 or 64 dwords");
+    // The row addresses are the same in every chunk; hidden behind the empty
+    // asm they are formed here (a scalar add each) rather than hoisted out of
+    // the chunk loop, where they would not fit in scalar registers.
+    lds_char_t *base = (lds_char_t *)dst;
+    __asm__ volatile("" : "+s"(base), "+s"(row_bytes));
 #pragma unroll
     for (int i = 0; i < kSsdQ / 4; ++i) {
         const int row = wave + 4 * i;
         if (kRowDw == 64 || lane < kRowDw)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + row * pitch), 4, lane * 4,
-                                                     row * row_bytes, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(base + row * pitch * (int)sizeof(bf16)), 4,
+                                                     lane * 4, row * row_bytes, 0, 0);
     }
 }
 // Wait until every vector-memory operation of this wave (the row loads above
@@ -492,9 +498,15 @@ __global__ __launch_bounds__(kSsdBlock, kOut ? 2 : 4) void ssd_chunk_kernel(SsdP
                     auto mask_mx = [&](auto factored) {
                         constexpr bool kF = decltype(factored)::value;
                         const float ct0 = kF ? 0.f : sc[0][li], ct1 = kF ? 0.f : sc[0][32 + li];
+                        // On a diagonal tile, register 4 m + q of this lane holds
+                        // s - t = 8 m + q - (li - 4 g): the lane masks of the
+                        // compares depend on the lane alone.  Formed here (one
+                        // compare each) instead of hoisted out of the chunk loop,
+                        // where they would not fit in scalar registers.
+                        int diag = li - 4 * g;
+                        __asm__ volatile("" : "+v"(diag));
                         auto masked = [&](const f32x16_t &gt, int st, int tt, float ct, int hf, Frag<T> &mh,
                                           Frag<T> &ml) {
-                            const int t = 32 * tt + li;
                             float mv[8];
 #pragma unroll
                             for (int m2 = 0; m2 < 2; ++m2) {
@@ -514,7 +526,7 @@ __global__ __launch_bounds__(kSsdBlock, kOut ? 2 : 4) void ssd_chunk_kernel(SsdP
                                 for (int q = 0; q < 4; ++q) {
                                     const float v = gt[4 * m + q] * ws[q];
                                     // below the diagonal tile every entry is kept
-                                    mv[4 * m2 + q] = (st < tt || s0 + q <= t) ? v : 0.f;
+                                    mv[4 * m2 + q] = (st < tt || 8 * m + q <= diag) ? v : 0.f;
                                 }
                             }
                             split(mv, mh, ml);
