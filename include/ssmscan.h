@@ -334,7 +334,7 @@ typedef enum {
     SSM_OPT_SEGMENT_LEN = 1,
     SSM_OPT_FORCE_GENERAL = 2,
     SSM_OPT_PROFILE = 3,      /* 1 = bracket every kernel launch with HIP events (see below) */
-    SSM_OPT_STEP_CHANNELS = 4 /* channels each decode-step thread updates: 1, 2 or 4 (default 1) */
+    SSM_OPT_STEP_CHANNELS = 4 /* (b, d) channels each decode-step thread updates, in consecutive batch rows: 1, 2 or 4 (default 1) */
 } ssm_option;
 
 int ssm_set_option(int option, int64_t value);

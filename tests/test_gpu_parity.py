@@ -252,6 +252,29 @@ def test_step_matches_oracle(ss, dtype, N, Bsz, Dm):
         P.compare(h, href, dtype, "h")
 
 
+@pytest.mark.parametrize("rows", [2, 4])
+@pytest.mark.parametrize("dtype,N,Bsz,Dm", [("bf16", 16, 7, 130), ("fp32", 8, 5, 33), ("bf16", 2, 3, 17)])
+def test_step_rows_per_thread_matches_oracle(ss, rows, dtype, N, Bsz, Dm):
+    """SSM_OPT_STEP_CHANNELS: 2 or 4 batch rows per thread (a row count that
+    is not a multiple of them leaves the last group part-empty)."""
+    cfg = configs.StepConfig("small_step", Bsz, Dm, N, dtype, 0.1, 3, seed=23)
+    P.say(f"case: step {dtype} N={N} {Bsz}x{Dm} rows/thread={rows}")
+    st = generate.step_state(cfg, DEV)
+    A = -torch.exp(torch.randn(Dm, N, device=DEV, generator=torch.Generator(DEV).manual_seed(5)))
+    h = st["h"].clone()
+    href = P.f64(h)
+    ss.set_option(ss.SSM_OPT_STEP_CHANNELS, rows)
+    try:
+        for tok in generate.step_tokens(cfg, st, 3):
+            y = ss.step(tok["x"], tok["delta"], A, tok["B"], tok["C"], st["D"], h)
+            torch.cuda.synchronize()
+            yr, href = P.oracle_step(tok, A, st["D"], href)
+            P.compare(y, yr, dtype, "y")
+            P.compare(h, href, dtype, "h")
+    finally:
+        ss.set_option(ss.SSM_OPT_STEP_CHANNELS, 1)
+
+
 def test_step_delta_zero_keeps_state_bitwise(ss):
     P.say("case: step delta=0")
     h = torch.randn(4, 64, 16, device=DEV)
