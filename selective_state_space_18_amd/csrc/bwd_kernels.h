@@ -351,8 +351,13 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     constexpr int kK = BwdShape<Acc>::kK;
     constexpr int kNck = BwdShape<Acc>::kT / kK;
     constexpr int kWaves = kBlock / kWave;
+    constexpr int kT = BwdShape<Acc>::kT;
     __shared__ Acc ck[kWaves][kNck][N][kWave];  // state checkpoints, per wave
-    __shared__ Acc bacc[kWaves][kC][2][N];      // per-wave dB, dC sums of one sub-chunk
+    // per-wave dB, dC sums of every step of one segment, summed over the
+    // block's waves once per segment (before the first segment its first
+    // words hold the waves' on flags)
+    __shared__ Acc bacc[kWaves][kT][2][N];
+    static_assert(sizeof(ck) + sizeof(bacc) <= 81920, "two blocks per compute unit must fit its 160 KB of LDS");
     const ScanParams &p = q.f;
 
     const int wave = uniform((int)threadIdx.x / kWave);
@@ -382,6 +387,8 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     // in every barrier.
     const bool wave_on = tile_ok && ((bool)__all(st) == kStruct);
     const bool live = wave_on && in_range;
+    // every lane of the tile is a channel of the row (uniform over the wave)
+    const bool full_tile = __builtin_amdgcn_readfirstlane((int)__all(in_range)) != 0;
     const ChanConst<N, kStruct, kEuler, Acc> cc(Ar);
     const Acc a0n = (Acc)Ar[0];
     const Acc inva = kStruct ? (Acc)1 / (Acc)Ar[0] : (Acc)0;
@@ -418,13 +425,14 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     // Which waves of the block serve this launch.  A block with none writes
     // zero dB/dC partials for its rows and leaves; a wave that is not on only
     // keeps the block's barriers (its LDS slots stay zero).
-    __shared__ int on_flags[kWaves];
+    int *on_flags = reinterpret_cast<int *>(&bacc[0][0][0][0]);
     if (lane == 0) on_flags[wave] = wave_on ? 1 : 0;
-    for (int e = lane; e < kC * 2 * N; e += kWave) (&bacc[wave][0][0][0])[e] = 0;
     __syncthreads();
     int any_on = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) any_on |= on_flags[w];
+    __syncthreads();  // every wave has read the flags
+    for (int e = lane; e < kT * 2 * N; e += kWave) (&bacc[wave][0][0][0])[e] = 0;
     if (!any_on) {
         const int64_t s_begin = (int64_t)grp * q.seg_per_group;
         const int64_t s_end = s_begin + q.seg_per_group < p.S ? s_begin + q.seg_per_group : p.S;
@@ -457,35 +465,39 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
         }
     };
 
-    // the block's dB/dC sums of one sub-chunk, in wave order (deterministic)
-    auto write_block_sums = [&](int64_t ta, int nc) {
+    // The block's dB/dC sums of the steps t0 .. t0 + nseg - 1 of a segment,
+    // each summed over the waves in wave order (deterministic); the
+    // kT * 2 * N entries are shared out among the waves.  Between two
+    // barriers: all partials of the segment are in, and no wave writes the
+    // next segment's before every wave is done reading these.
+    auto write_segment_sums = [&](int64_t t0, int nseg) {
         Acc *dst = static_cast<Acc *>(q.part_bc) + ((int64_t)(path * q.blocks_per_row + br) * 2) * BLN +
-                   (b * p.L + ta) * N;
-        for (int e = lane; e < kC * 2 * N; e += kWave) {
+                   (b * p.L + t0) * N;
+        constexpr int kE = kT * 2 * N;
+        constexpr int kPerWave = (kE + kWaves - 1) / kWaves;
+        for (int k = lane; k < kPerWave; k += kWave) {
+            const int e = wave * kPerWave + k;
+            if (e >= kE) break;
             const int i = e / (2 * N);
             const int v = (e / N) & 1;
             const int n = e % N;
             Acc sum = 0;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) sum += bacc[w][i][v][n];
-            if (i < nc) dst[(int64_t)v * BLN + (int64_t)i * N + n] = sum;
+            if (i < nseg) dst[(int64_t)v * BLN + (int64_t)i * N + n] = sum;
         }
     };
 
     if (!wave_on) {
-        // same barriers as the working waves; wave 0 still writes the sums
+        // same barriers as the working waves, and their share of the sums
         for (int si = 0; si < q.seg_per_group; ++si) {
             const int s = grp * q.seg_per_group + si;
             if (s >= p.S) break;
             const int64_t t0 = (int64_t)s * p.seg_len;
             const int nseg = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
-            for (int u = (nseg + kC - 1) / kC - 1; u >= 0; --u) {
-                const int64_t ta = t0 + (int64_t)u * kC;
-                const int nc = nseg - u * kC < kC ? nseg - u * kC : kC;
-                __syncthreads();
-                if (wave == 0) write_block_sums(ta, nc);
-                __syncthreads();
-            }
+            __syncthreads();
+            write_segment_sums(t0, nseg);
+            __syncthreads();
         }
         return;
     }
@@ -666,26 +678,30 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                         buf_store(from_acc<T>(gx), rdx, voff, i * row);
                         buf_store(from_acc<T>(gdl), rdd, voff, i * row);
                     }
-                    // dB, dC: sum over the wave's channels, then over the block's waves
+                    // dB, dC: sum over the wave's channels, then over the block's
+                    // waves; lanes past the row shadow a valid channel and add
+                    // nothing
+                    if (!full_tile) {
 #pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        vB[n] = live ? vB[n] : (Acc)0;
-                        vC[n] = live ? vC[n] : (Acc)0;
+                        for (int n = 0; n < N; ++n) {
+                            vB[n] = live ? vB[n] : (Acc)0;
+                            vC[n] = live ? vC[n] : (Acc)0;
+                        }
                     }
                     const int idx = wave_reduce_scatter<N>(vB, lane);
                     (void)wave_reduce_scatter<N>(vC, lane);
                     // every wave fills its slot (zeros when it is not on)
                     if ((lane & (kWave / N - 1)) == 0) {
-                        bacc[wave][i][0][idx] = vB[0];
-                        bacc[wave][i][1][idx] = vC[0];
+                        bacc[wave][u * kC + i][0][idx] = vB[0];
+                        bacc[wave][u * kC + i][1][idx] = vC[0];
                     }
                 }
             }
-            __syncthreads();
-            if (wave == 0) write_block_sums(ta, nc);
-            __syncthreads();
             if (u > 0) cur = nxt;
         }
+        __syncthreads();  // every wave's partials of the segment are in
+        write_segment_sums(t0, nseg);
+        __syncthreads();  // ... and summed before the next segment's are written
         if (s == 0 && live && q.dh_init != nullptr) {
 #pragma unroll
             for (int n = 0; n < N; ++n) q.dh_init[ch * N + n] = (float)(nu[n] * (Acc)(n + 1));
