@@ -387,8 +387,6 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     // in every barrier.
     const bool wave_on = tile_ok && ((bool)__all(st) == kStruct);
     const bool live = wave_on && in_range;
-    // every lane of the tile is a channel of the row (uniform over the wave)
-    const bool full_tile = __builtin_amdgcn_readfirstlane((int)__all(in_range)) != 0;
     const ChanConst<N, kStruct, kEuler, Acc> cc(Ar);
     const Acc a0n = (Acc)Ar[0];
     const Acc inva = kStruct ? (Acc)1 / (Acc)Ar[0] : (Acc)0;
@@ -558,9 +556,11 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
             Acc xs[kC], ds[kC], gys[kC];
 #pragma unroll
             for (int i = 0; i < kC; ++i) {
-                xs[i] = (Acc)to_f32(cur.x[i]);
+                // lanes past the row (shadowing a valid channel) take x = dy = 0:
+                // every dB and dC share is a multiple of x or dy, so theirs vanish
+                xs[i] = live ? (Acc)to_f32(cur.x[i]) : (Acc)0;
                 ds[i] = (Acc)to_f32(cur.dl[i]);
-                gys[i] = (Acc)to_f32(cur.dy[i]);
+                gys[i] = live ? (Acc)to_f32(cur.dy[i]) : (Acc)0;
             }
             if constexpr (kPre) {
 #pragma unroll
@@ -674,20 +674,12 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                     }
                     dDacc = fma_(gy, xv, dDacc);
                     dbacc += gdl;
-                    if (wave_on) {
+                    if (live) {
                         buf_store(from_acc<T>(gx), rdx, voff, i * row);
                         buf_store(from_acc<T>(gdl), rdd, voff, i * row);
                     }
                     // dB, dC: sum over the wave's channels, then over the block's
-                    // waves; lanes past the row shadow a valid channel and add
-                    // nothing
-                    if (!full_tile) {
-#pragma unroll
-                        for (int n = 0; n < N; ++n) {
-                            vB[n] = live ? vB[n] : (Acc)0;
-                            vC[n] = live ? vC[n] : (Acc)0;
-                        }
-                    }
+                    // waves (lanes past the row hold zeros)
                     const int idx = wave_reduce_scatter<N>(vB, lane);
                     (void)wave_reduce_scatter<N>(vC, lane);
                     // every wave fills its slot (zeros when it is not on)
