@@ -283,69 +283,83 @@ __global__ __launch_bounds__(kBlock) void cplx_carry_kernel(ScanParams p) {
 
 // Decode step: Q lanes per channel, each owning 2 complex states (16 bytes)
 // of the state row, so a wave-wide access is 1 KiB contiguous; y is summed
-// across the Q lanes with shuffles.
+// across the Q lanes with shuffles.  Grid: x over (channel d, lane j) of one
+// batch row (d = i / Q, j = i % Q, Q a power of two: no division), y over
+// batch rows, strided by the grid's height; the per-(d, n) constants of A are
+// formed once per thread.
 template <typename T, int N, bool kPrecise>
 __global__ __launch_bounds__(kBlock) void cplx_step_kernel(StepParams p) {
     constexpr int SPL = N >= 2 ? 2 : 1;  // complex states per lane
     constexpr int Q = N / SPL;
+    static_assert((Q & (Q - 1)) == 0 && 64 % Q == 0, "Q lanes of a channel within one wave");
     typedef float Acc;
-    const int64_t BD = p.Bsz * p.Dm;
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t ch = i / Q;
-    const int j = (int)(i - ch * Q);
-    if (ch >= BD) return;
-    const int64_t b = ch / p.Dm, d = ch - b * p.Dm;
-    Acc dv = to_f32(static_cast<const T *>(p.delta)[ch]);
-    if (p.delta_bias != nullptr || p.delta_softplus) {
-        const float v = dv + (p.delta_bias != nullptr ? p.delta_bias[d] : 0.f);
-        dv = p.delta_softplus ? (kPrecise ? softplus_precise(v) : softplus_(v)) : v;
-    }
-    const Acc xv = to_f32(static_cast<const T *>(p.x)[ch]);
-    float *hp = p.h + (ch * N + j * SPL) * 2;
-    Acc yv = 0;
+    const int64_t d = i / Q;
+    const int j = (int)(i % Q);
+    if (d >= p.Dm) return;
+    float a[SPL], w[SPL], wr[SPL], wi[SPL];
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
         const int n = j * SPL + k;
-        float a = p.A[(d * N + n) * 2], w = p.A[(d * N + n) * 2 + 1];
-        if (__builtin_fabsf(a) < -kTinyA && __builtin_fabsf(w) < -kTinyA) {
-            a = kTinyA;
-            w = 0.f;
+        a[k] = p.A[(d * N + n) * 2];
+        w[k] = p.A[(d * N + n) * 2 + 1];
+        if (__builtin_fabsf(a[k]) < -kTinyA && __builtin_fabsf(w[k]) < -kTinyA) {
+            a[k] = kTinyA;
+            w[k] = 0.f;
         }
-        const float zr = dv * a, zi = dv * w;
-        float mag, c, s, em1;
-        if constexpr (kPrecise) {
-            c = cosf(zi);
-            s = sinf(zi);
-            em1 = expm1f(zr);
-            mag = em1 + 1.f;
-        } else {
-            cplx_exp(zr, zi, mag, c, s, em1);
-        }
-        const float abr = mag * c, abi = mag * s;
-        const float u = to_f32(static_cast<const T *>(p.B)[b * N + n]) * xv;
-        float br, bi;
-        if (p.euler_b) {
-            br = dv * u;
-            bi = 0.f;
-        } else {
-            const float hs = kPrecise ? sinf(0.5f * zi) : 0.f;
-            const float cm1 = kPrecise ? -2.f * hs * hs : c - 1.f;
-            const float er = __builtin_fmaf(em1, c, cm1), ei = abi;
-            const float den = a * a + w * w;
-            const float wr = a / den, wi = -w / den;
-            br = (er * wr - ei * wi) * u;
-            bi = (er * wi + ei * wr) * u;
-        }
-        const float r = hp[2 * k], m = hp[2 * k + 1];
-        const float nr = __builtin_fmaf(abr, r, __builtin_fmaf(-abi, m, br));
-        const float ni = __builtin_fmaf(abr, m, __builtin_fmaf(abi, r, bi));
-        hp[2 * k] = nr;
-        hp[2 * k + 1] = ni;
-        yv = __builtin_fmaf(to_f32(static_cast<const T *>(p.C)[b * N + n]), nr, yv);
+        const float den = a[k] * a[k] + w[k] * w[k];
+        wr[k] = a[k] / den;
+        wi[k] = -w[k] / den;
     }
+    const float bias = p.delta_bias != nullptr ? p.delta_bias[d] : 0.f;
+    const float Dd = p.D[d];
+    for (int64_t b = blockIdx.y; b < p.Bsz; b += gridDim.y) {
+        const int64_t ch = b * p.Dm + d;
+        Acc dv = to_f32(static_cast<const T *>(p.delta)[ch]);
+        if (p.delta_bias != nullptr || p.delta_softplus) {
+            const float v = dv + bias;
+            dv = p.delta_softplus ? (kPrecise ? softplus_precise(v) : softplus_(v)) : v;
+        }
+        const Acc xv = to_f32(static_cast<const T *>(p.x)[ch]);
+        float *hp = p.h + (ch * N + j * SPL) * 2;
+        Acc yv = 0;
 #pragma unroll
-    for (int off = 1; off < Q; off <<= 1) yv += __shfl_xor(yv, off, Q);
-    if (j == 0) static_cast<T *>(p.y)[ch] = from_acc<T>(__builtin_fmaf(p.D[d], xv, yv));
+        for (int k = 0; k < SPL; ++k) {
+            const int n = j * SPL + k;
+            const float zr = dv * a[k], zi = dv * w[k];
+            float mag, c, s, em1;
+            if constexpr (kPrecise) {
+                c = cosf(zi);
+                s = sinf(zi);
+                em1 = expm1f(zr);
+                mag = em1 + 1.f;
+            } else {
+                cplx_exp(zr, zi, mag, c, s, em1);
+            }
+            const float abr = mag * c, abi = mag * s;
+            const float u = to_f32(static_cast<const T *>(p.B)[b * N + n]) * xv;
+            float br, bi;
+            if (p.euler_b) {
+                br = dv * u;
+                bi = 0.f;
+            } else {
+                const float hs = kPrecise ? sinf(0.5f * zi) : 0.f;
+                const float cm1 = kPrecise ? -2.f * hs * hs : c - 1.f;
+                const float er = __builtin_fmaf(em1, c, cm1), ei = abi;
+                br = (er * wr[k] - ei * wi[k]) * u;
+                bi = (er * wi[k] + ei * wr[k]) * u;
+            }
+            const float r = hp[2 * k], m = hp[2 * k + 1];
+            const float nr = __builtin_fmaf(abr, r, __builtin_fmaf(-abi, m, br));
+            const float ni = __builtin_fmaf(abr, m, __builtin_fmaf(abi, r, bi));
+            hp[2 * k] = nr;
+            hp[2 * k + 1] = ni;
+            yv = __builtin_fmaf(to_f32(static_cast<const T *>(p.C)[b * N + n]), nr, yv);
+        }
+#pragma unroll
+        for (int off = 1; off < Q; off <<= 1) yv += __shfl_xor(yv, off, Q);
+        if (j == 0) static_cast<T *>(p.y)[ch] = from_acc<T>(__builtin_fmaf(Dd, xv, yv));
+    }
 }
 
 template <typename T, int N, bool kOut>
@@ -414,10 +428,13 @@ hipError_t cplx_pass(ScanPass pass, const ScanParams &p, int N, hipStream_t s) {
 
 template <typename T, bool kPrecise>
 hipError_t cplx_step_launch(const StepParams &p, int N, hipStream_t s) {
-    const int64_t BD = p.Bsz * p.Dm;
-    if (BD == 0) return hipSuccess;
+    if (p.Bsz * p.Dm == 0) return hipSuccess;
     const int Q = N >= 2 ? N / 2 : 1;
-    const unsigned grid = (unsigned)((BD * Q + kBlock - 1) / kBlock);
+    const unsigned gx = (unsigned)((p.Dm * Q + kBlock - 1) / kBlock);
+    // about 2048 blocks in all, at least one row each
+    int64_t want = (2048 + (int64_t)gx - 1) / (int64_t)gx;
+    if (want < 1) want = 1;
+    const dim3 grid(gx, (unsigned)(p.Bsz < want ? p.Bsz : want));
     switch (N) {
         case 1: hipLaunchKernelGGL((cplx_step_kernel<T, 1, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
         case 2: hipLaunchKernelGGL((cplx_step_kernel<T, 2, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;

@@ -144,6 +144,22 @@ def test_complex_step_matches_oracle(ss, dtype, kind, N):
     compare_complex(h, hr, dtype, "h")
 
 
+@pytest.mark.parametrize("Bsz,Dm,N", [(700, 130, 16), (900, 33, 4)])
+def test_complex_step_many_rows(ss, Bsz, Dm, N):
+    """More batch rows than the grid has rows of blocks: each block walks
+    several rows (and a remainder)."""
+    P.say(f"case: complex step {Bsz}x{Dm} N={N}")
+    inp = make("bf16", Bsz, 1, Dm, N, seed=13 + N, kind="plain")
+    h = inp["h_init"].clone()
+    h0 = c128(h)
+    x, dl, B, C = (inp[k][:, 0] for k in ("x", "delta", "B", "C"))
+    y = ss.step_complex(x, dl, inp["A"], B, C, inp["D"], h)
+    torch.cuda.synchronize()
+    yr, hr = oracle.step_complex(P.f64(x), P.f64(dl), c128(inp["A"]), P.f64(B), P.f64(C), P.f64(inp["D"]), h0)
+    P.compare(y, yr, "bf16", "y")
+    compare_complex(h, hr, "bf16", "h")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_complex_step_chain_equals_scan(ss, dtype):
     P.say(f"case: complex step chain {dtype}")
