@@ -288,6 +288,8 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias,
  *   y        : [Bsz][Dm]     bf16   (out)     y = sum_n C[n]*h_new[n] + D*x
  *
  * y must not overlap any input or h; h must not overlap any input.
+ * Dm*N may be at most 2^24 (64 MiB of state per batch row), else
+ * SSM_ERR_BAD_DIM.
  */
 int ssm_step(const void *x, const void *delta, const float *A,
              const void *B, const void *C, const float *D,
@@ -334,7 +336,7 @@ typedef enum {
     SSM_OPT_SEGMENT_LEN = 1,
     SSM_OPT_FORCE_GENERAL = 2,
     SSM_OPT_PROFILE = 3,      /* 1 = bracket every kernel launch with HIP events (see below) */
-    SSM_OPT_STEP_CHANNELS = 4 /* (b, d) channels each decode-step thread updates, in consecutive batch rows: 1, 2 or 4 (default 1) */
+    SSM_OPT_STEP_CHANNELS = 4 /* (b, d) channels each decode-step thread updates, in consecutive batch rows: 1, 2 or 4 (default 4) */
 } ssm_option;
 
 int ssm_set_option(int option, int64_t value);

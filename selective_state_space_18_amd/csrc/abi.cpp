@@ -50,7 +50,7 @@ int hip_fail(hipError_t e, const char *what) {
 std::atomic<int64_t> g_opt_segment_len{0};
 std::atomic<int64_t> g_opt_force_general{0};
 std::atomic<int64_t> g_opt_profile{0};
-std::atomic<int64_t> g_opt_step_channels{1};
+std::atomic<int64_t> g_opt_step_channels{4};
 
 // ---------------------------------------------------------------------------
 // Optional per-kernel event timing (SSM_OPT_PROFILE).
@@ -367,6 +367,10 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     return ok();
 }
 
+// Largest state of one batch row the decode step takes (2^24 fp32 values,
+// 64 MiB): its kernel addresses a slice of rows through 32-bit buffer offsets.
+constexpr int64_t kStepMaxRowStates = int64_t(1) << 24;
+
 int step_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
               const float *D, float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,
               void *stream, const float *delta_bias = nullptr, unsigned flags = 0) {
@@ -380,6 +384,9 @@ int step_impl(const void *x, const void *delta, const float *A, const void *B, c
         BDN > INT64_MAX / 64)
         return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, Dm=%lld, N=%lld)", (long long)Bsz, (long long)Dm,
                     (long long)N);
+    if (DN > kStepMaxRowStates)
+        return fail(SSM_ERR_BAD_DIM, "decode step: Dm*N = %lld states per batch row exceeds %lld", (long long)DN,
+                    (long long)kStepMaxRowStates);
     const int64_t es = dtype_size(dtype);
     const Arg in[] = {{x, BD, es, "x"}, {delta, BD, es, "delta"}, {A, DN, 4, "A"},
                       {B, BN, es, "B"}, {C, BN, es, "C"}, {D, Dm, 4, "D"},

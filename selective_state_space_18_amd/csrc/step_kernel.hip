@@ -12,7 +12,7 @@
 // bandwidth.  Q = N/4 lanes share one (b, d) channel and each owns 4
 // consecutive states (16 bytes), so one wave-wide 16-byte load or store moves
 // 1 KiB of contiguous state.  The partial sums of y are combined across the Q
-// lanes with cross-lane shuffles.
+// lanes of a channel with DPP quad permutations.
 #include "ssm_device.h"
 #include "ssm_launch.h"
 
@@ -29,31 +29,78 @@ struct StepShape {
     static constexpr int SPL = N / Q;               // states per lane
 };
 
-// kVec: h and A rows are read/written as 16-byte vectors (needs 16-byte
-// aligned base pointers, checked on the host).
+// Sum over the Q <= 4 lanes of one channel (aligned groups within a quad) by
+// DPP quad permutations: no LDS round trip.
+template <int Q>
+__device__ __forceinline__ float quad_sum(float v) {
+    if constexpr (Q >= 2)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // lanes 1,0,3,2
+    if constexpr (Q >= 4)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // lanes 2,3,0,1
+    return v;
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kNt = 2;  // buffer cache policy: nontemporal
+
+// SPL consecutive values of T at byte offset voff + soff of a buffer: one
+// vector load where kVec guarantees the alignment, else one per value.
+template <typename T, int SPL, bool kVec, int kAux>
+__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff, T (&v)[SPL]) {
+    constexpr int bytes = SPL * (int)sizeof(T);
+    if constexpr (kVec && bytes == 16) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAux);
+        __builtin_memcpy(v, &w, 16);
+    } else if constexpr (kVec && bytes == 8) {
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kAux);
+        __builtin_memcpy(v, &w, 8);
+    } else if constexpr (kVec && bytes == 4 && sizeof(T) == 4) {
+        v[0] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kAux));
+    } else {
+#pragma unroll
+        for (int k = 0; k < SPL; ++k) {
+            if constexpr (sizeof(T) == 4)
+                v[k] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * k, soff, kAux));
+            else
+                v[k] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2 * k, soff, kAux));
+        }
+    }
+}
+
 // Grid: x runs over (channel d, lane j) of one batch row -- d = i / Q and
-// j = i % Q with Q a power of two, no division -- and y over groups of kU
-// batch rows.  The grid is kept to a few blocks per compute unit and each
-// thread walks the row groups y, y + gridDim.y, ... with the next group's
-// loads issued before the current group is computed: the state stream keeps
-// loads in flight instead of paying a block launch and a full memory latency
-// per row group.  A thread handles lane j of channel d; A's row, the bias and
-// D are loaded once.  The state moves with non-temporal loads and stores: it
-// is streamed once per step and should not displace the rows every channel
-// shares.
-template <typename T, int N, bool kPrecise, bool kVec, int kU>
+// j = i % Q with Q a power of two -- and y over groups of kU consecutive batch
+// rows.  About one block runs per compute unit, and each thread walks the row
+// groups y, y + gridDim.y, ... with the next group's loads issued before the
+// current group is computed (two register sets used in turn, no copies).
+// Measured on the 256 x 8192 x 16 state, one wave per SIMD with four rows in
+// flight per thread moved the state faster than more waves with fewer rows.
+// A's row, the bias and D are loaded once per thread.
+//
+// Rows are addressed through buffer descriptors whose range ends at the last
+// batch row: a load of a row past the end returns zeros without a memory
+// access and a store there is dropped.  So the next row group is fetched
+// unconditionally (a branch around the loads would make the compiler wait for
+// them before the current group is computed) and stores need no row test.
+// The state moves with non-temporal accesses: it is streamed once per step
+// and should not displace the rows every channel shares.
+//
+// kVec: h, A, B and C are read/written as 8- or 16-byte vectors (needs
+// 16-byte aligned base pointers, checked on the host).  kPre: delta goes
+// through the bias / softplus of the fused options.
+template <typename T, int N, bool kPrecise, bool kVec, int kU, bool kPre>
 __global__ __launch_bounds__(kBlock) void step_kernel(StepParams p) {
     constexpr int Q = StepShape<N>::Q;
     constexpr int SPL = StepShape<N>::SPL;
-    static_assert((Q & (Q - 1)) == 0 && 64 % Q == 0, "Q lanes of a channel within one wave");
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t d = i / Q;
-    const int j = (int)(i % Q);
+    static_assert((Q & (Q - 1)) == 0 && Q <= 4, "Q lanes of a channel within one quad");
+    const int i = blockIdx.x * kBlock + threadIdx.x;
+    const int d = i / Q;
+    const int j = i % Q;
     // Q divides the wave size, so the Q lanes of a channel leave together.
     if (d >= p.Dm) return;
     float a[SPL], a2[SPL];  // A and A log2(e) (exponent in base-2 units)
     {
-        const float *Ap = p.A + d * N + j * SPL;
+        const float *Ap = p.A + (int64_t)d * N + j * SPL;
         if constexpr (kVec && SPL == 4) {
             const float4 av = *reinterpret_cast<const float4 *>(Ap);
             a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
@@ -64,45 +111,58 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepParams p) {
 #pragma unroll
         for (int k = 0; k < SPL; ++k) a2[k] = a[k] * kLog2e;
     }
+    // The input coefficient is delta (Euler term, or the limit at A = 0) or
+    // (exp(delta A) - 1)/A: a per-lane choice fixed for the whole call.
+    bool lin[SPL];
+    float ainv[SPL];
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+        lin[k] = p.euler_b || a[k] == 0.f;
+        ainv[k] = __builtin_amdgcn_rcpf(a[k]);
+    }
     const float bias = p.delta_bias != nullptr ? p.delta_bias[d] : 0.f;
     const float Dd = p.D[d];
 
-    // one row group's inputs: state, x and delta of kU rows
+    const int Dm = (int)p.Dm;
+    const int Bsz = (int)p.Bsz;
+    const auto rh = make_rsrc(p.h, (int32_t)((int64_t)Bsz * Dm * N * 4));
+    const auto rx = make_rsrc(p.x, (int32_t)((int64_t)Bsz * Dm * sizeof(T)));
+    const auto rd = make_rsrc(p.delta, (int32_t)((int64_t)Bsz * Dm * sizeof(T)));
+    const auto rb = make_rsrc(p.B, (int32_t)(Bsz * N * (int)sizeof(T)));
+    const auto rc = make_rsrc(p.C, (int32_t)(Bsz * N * (int)sizeof(T)));
+    const auto ry = make_rsrc(p.y, (int32_t)((int64_t)Bsz * Dm * sizeof(T)));
+    // per-lane byte offsets within a row; the row goes into the scalar offset
+    const int vh = (d * N + j * SPL) * 4;
+    const int vx = d * (int)sizeof(T);
+    const int vbc = j * SPL * (int)sizeof(T);
+    const int rowh = Dm * N * 4, rowx = Dm * (int)sizeof(T), rowbc = N * (int)sizeof(T);
+
+    // One row group's inputs, as stored; converted at use.
     struct In {
-        float h[kU][SPL], xv[kU], dv[kU];
+        float h[kU][SPL];
+        T xv[kU], dv[kU], bv[kU][SPL], cv[kU][SPL];
     };
-    auto load = [&](int64_t b0, In &in) {
+    auto load = [&](int b0, In &in) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t b = b0 + u < p.Bsz ? b0 + u : b0;  // rows past the end redo b0 and store nothing
-            const int64_t ch = b * p.Dm + d;
-            const float *hp = p.h + ch * N + j * SPL;
-            if constexpr (kVec && SPL == 4) {
-                const f32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(hp));
-                in.h[u][0] = hv.x; in.h[u][1] = hv.y; in.h[u][2] = hv.z; in.h[u][3] = hv.w;
-            } else {
-#pragma unroll
-                for (int k = 0; k < SPL; ++k) in.h[u][k] = __builtin_nontemporal_load(hp + k);
-            }
-            in.xv[u] = to_f32(static_cast<const T *>(p.x)[ch]);
-            in.dv[u] = to_f32(static_cast<const T *>(p.delta)[ch]);
+            const int b = b0 + u;  // rows past the end read zeros
+            load_run<float, SPL, kVec, kNt>(rh, vh, b * rowh, in.h[u]);
+            T tmp[1];
+            load_run<T, 1, false, 0>(rx, vx, b * rowx, tmp);
+            in.xv[u] = tmp[0];
+            load_run<T, 1, false, 0>(rd, vx, b * rowx, tmp);
+            in.dv[u] = tmp[0];
+            load_run<T, SPL, kVec, 0>(rb, vbc, b * rowbc, in.bv[u]);
+            load_run<T, SPL, kVec, 0>(rc, vbc, b * rowbc, in.cv[u]);
         }
     };
-    const int64_t gstep = (int64_t)gridDim.y * kU;
-    int64_t b0 = (int64_t)blockIdx.y * kU;
-    In cur;
-    if (b0 < p.Bsz) load(b0, cur);
-    for (; b0 < p.Bsz; b0 += gstep) {
-        In nxt;
-        if (b0 + gstep < p.Bsz) load(b0 + gstep, nxt);
+    auto compute = [&](int b0, const In &cur) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t b = b0 + u < p.Bsz ? b0 + u : b0;
-            const int64_t ch = b * p.Dm + d;
-            const T *Bp = static_cast<const T *>(p.B) + b * N + j * SPL;
-            const T *Cp = static_cast<const T *>(p.C) + b * N + j * SPL;
-            float dv = cur.dv[u];
-            if (p.delta_bias != nullptr || p.delta_softplus) {  // uniform over the launch
+            const int b = b0 + u;  // rows past the end compute on zeros and store nothing
+            const float xv = to_f32(cur.xv[u]);
+            float dv = to_f32(cur.dv[u]);
+            if constexpr (kPre) {
                 const float v = dv + bias;
                 dv = p.delta_softplus ? (kPrecise ? softplus_precise(v) : softplus_(v)) : v;
             }
@@ -112,55 +172,94 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepParams p) {
             for (int k = 0; k < SPL; ++k) {
                 float abar;
                 const float E = kPrecise ? expm1_and_exp_precise(dv * a[k], abar) : expm1_and_exp2(dv * a2[k], abar);
-                float coef;
-                if (p.euler_b)
-                    coef = dv;
-                else if constexpr (kPrecise)
-                    coef = (a[k] != 0.f) ? E / a[k] : dv;
-                else
-                    coef = (a[k] != 0.f) ? E * __builtin_amdgcn_rcpf(a[k]) : dv;
-                const float bx = to_f32(Bp[k]) * cur.xv[u];
+                const float coef = lin[k] ? dv : (kPrecise ? E / a[k] : E * ainv[k]);
+                const float bx = to_f32(cur.bv[u][k]) * xv;
                 h[k] = __builtin_fmaf(abar, cur.h[u][k], coef * bx);
-                yv = __builtin_fmaf(to_f32(Cp[k]), h[k], yv);
+                yv = __builtin_fmaf(to_f32(cur.cv[u][k]), h[k], yv);
             }
-            const bool live = b0 + u < p.Bsz;
-            float *hp = p.h + ch * N + j * SPL;
-            if (live) {
-                if constexpr (kVec && SPL == 4) {
-                    const f32x4 hv = {h[0], h[1], h[2], h[3]};
-                    __builtin_nontemporal_store(hv, reinterpret_cast<f32x4 *>(hp));
-                } else {
+            if constexpr (kVec && SPL == 4) {
+                u32x4 w;
+                __builtin_memcpy(&w, h, 16);
+                __builtin_amdgcn_raw_buffer_store_b128(w, rh, vh, b * rowh, kNt);
+            } else {
 #pragma unroll
-                    for (int k = 0; k < SPL; ++k) __builtin_nontemporal_store(h[k], hp + k);
-                }
+                for (int k = 0; k < SPL; ++k)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, h[k]), rh, vh + 4 * k, b * rowh, kNt);
             }
-#pragma unroll
-            for (int off = 1; off < Q; off <<= 1) yv += __shfl_xor(yv, off, Q);
-            if (live && j == 0) static_cast<T *>(p.y)[ch] = from_acc<T>(__builtin_fmaf(Dd, cur.xv[u], yv));
+            yv = quad_sum<Q>(yv);
+            if (j == 0) buf_store(from_acc<T>(__builtin_fmaf(Dd, xv, yv)), ry, vx, b * rowx);
         }
-        cur = nxt;
+    };
+    const int gstep = gridDim.y * kU;
+    int b0 = blockIdx.y * kU;
+    In ra, rb2;
+    load(b0, ra);
+    // two copies of the body with the buffers' roles swapped: no register copies
+    for (;;) {
+        load(b0 + gstep, rb2);
+        compute(b0, ra);
+        b0 += gstep;
+        if (b0 >= Bsz) break;
+        load(b0 + gstep, ra);
+        compute(b0, rb2);
+        b0 += gstep;
+        if (b0 >= Bsz) break;
     }
 }
 
-int g_step_unroll = 1;  // batch rows per thread (1, 2 or 4)
+int g_step_unroll = 4;  // batch rows per thread and row group (1, 2 or 4)
+
+// Every buffer offset of one launch, including the row group fetched past the
+// last row, stays below 2^31: the batch is stepped in slices of at most
+// kSliceBytes of state and the row stride of a thread is capped so that the
+// overrun is at most another kSliceBytes.  A batch row of state is at most
+// kMaxRowBytes (the host rejects larger Dm * N).
+constexpr int64_t kSliceBytes = int64_t(1) << 30;
+constexpr int64_t kMaxRowBytes = int64_t(1) << 26;
+constexpr int64_t kTargetBlocks = 256;  // blocks per launch at four rows per group
+
+template <typename T, bool kPrecise, int N, bool kVec, int kU, bool kPre>
+hipError_t launch_p(const StepParams &p, hipStream_t s) {
+    const int64_t row_bytes = p.Dm * N * 4;
+    const int64_t rows = kSliceBytes / row_bytes;  // >= 16
+    const int64_t lanes = p.Dm * StepShape<N>::Q;
+    const unsigned gx = (unsigned)((lanes + kBlock - 1) / kBlock);
+    // about one block per compute unit at four rows per group (more blocks
+    // for fewer rows), at least one row group each
+    const int64_t target = kTargetBlocks * 4 / kU;
+    int64_t want = (target + (int64_t)gx - 1) / (int64_t)gx;
+    if (want > rows / kU - 1) want = rows / kU - 1;
+    if (want < 1) want = 1;
+    for (int64_t r0 = 0; r0 < p.Bsz; r0 += rows) {
+        StepParams q = p;
+        q.Bsz = p.Bsz - r0 < rows ? p.Bsz - r0 : rows;
+        q.x = static_cast<const T *>(p.x) + r0 * p.Dm;
+        q.delta = static_cast<const T *>(p.delta) + r0 * p.Dm;
+        q.y = static_cast<T *>(p.y) + r0 * p.Dm;
+        q.B = static_cast<const T *>(p.B) + r0 * N;
+        q.C = static_cast<const T *>(p.C) + r0 * N;
+        q.h = p.h + r0 * p.Dm * N;
+        const int64_t groups = (q.Bsz + kU - 1) / kU;
+        const unsigned gy = (unsigned)(groups < want ? groups : want);
+        hipLaunchKernelGGL((step_kernel<T, N, kPrecise, kVec, kU, kPre>), dim3(gx, gy), dim3(kBlock), 0, s, q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 template <typename T, bool kPrecise, int N, bool kVec, int kU>
 hipError_t launch_u(const StepParams &p, hipStream_t s) {
-    const int64_t lanes = p.Dm * StepShape<N>::Q;
-    const unsigned gx = (unsigned)((lanes + kBlock - 1) / kBlock);
-    // about 2048 blocks in all (8 per compute unit), at least one row group each
-    const int64_t groups = (p.Bsz + kU - 1) / kU;
-    int64_t want = (2048 + (int64_t)gx - 1) / (int64_t)gx;
-    if (want < 1) want = 1;
-    const unsigned gy = (unsigned)(groups < want ? groups : want);
-    hipLaunchKernelGGL((step_kernel<T, N, kPrecise, kVec, kU>), dim3(gx, gy), dim3(kBlock), 0, s, p);
-    return hipGetLastError();
+    if (p.Dm * N * 4 > kMaxRowBytes) return hipErrorInvalidValue;
+    if (p.delta_bias != nullptr || p.delta_softplus) return launch_p<T, kPrecise, N, kVec, kU, true>(p, s);
+    return launch_p<T, kPrecise, N, kVec, kU, false>(p, s);
 }
 
 template <typename T, bool kPrecise, int N>
 hipError_t launch_n(const StepParams &p, hipStream_t s) {
     if (p.Bsz * p.Dm == 0) return hipSuccess;
-    const bool vec = ((reinterpret_cast<uintptr_t>(p.h) | reinterpret_cast<uintptr_t>(p.A)) & 15) == 0;
+    const bool vec = ((reinterpret_cast<uintptr_t>(p.h) | reinterpret_cast<uintptr_t>(p.A) |
+                       reinterpret_cast<uintptr_t>(p.B) | reinterpret_cast<uintptr_t>(p.C)) & 15) == 0;
     const int u = g_step_unroll;
     if (vec) {
         if (u >= 4) return launch_u<T, kPrecise, N, true, 4>(p, s);

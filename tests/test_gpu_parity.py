@@ -252,11 +252,12 @@ def test_step_matches_oracle(ss, dtype, N, Bsz, Dm):
         P.compare(h, href, dtype, "h")
 
 
-@pytest.mark.parametrize("rows", [2, 4])
+@pytest.mark.parametrize("rows", [1, 2])
 @pytest.mark.parametrize("dtype,N,Bsz,Dm", [("bf16", 16, 7, 130), ("fp32", 8, 5, 33), ("bf16", 2, 3, 17)])
 def test_step_rows_per_thread_matches_oracle(ss, rows, dtype, N, Bsz, Dm):
-    """SSM_OPT_STEP_CHANNELS: 2 or 4 batch rows per thread (a row count that
-    is not a multiple of them leaves the last group part-empty)."""
+    """SSM_OPT_STEP_CHANNELS: 1 or 2 batch rows per thread instead of the
+    default 4 (a row count that is not a multiple of them leaves the last
+    group part-empty)."""
     cfg = configs.StepConfig("small_step", Bsz, Dm, N, dtype, 0.1, 3, seed=23)
     P.say(f"case: step {dtype} N={N} {Bsz}x{Dm} rows/thread={rows}")
     st = generate.step_state(cfg, DEV)
@@ -272,7 +273,34 @@ def test_step_rows_per_thread_matches_oracle(ss, rows, dtype, N, Bsz, Dm):
             P.compare(y, yr, dtype, "y")
             P.compare(h, href, dtype, "h")
     finally:
-        ss.set_option(ss.SSM_OPT_STEP_CHANNELS, 1)
+        ss.set_option(ss.SSM_OPT_STEP_CHANNELS, 4)
+
+
+@pytest.mark.parametrize("dtype,N,Bsz,Dm", [("bf16", 16, 6, 130), ("fp32", 4, 5, 40)])
+def test_step_unaligned_matches_oracle(ss, dtype, N, Bsz, Dm):
+    """State, A, B and C one element past a 16-byte boundary: the decode step
+    takes its element-wise (non-vector) path."""
+    cfg = configs.StepConfig("small_step", Bsz, Dm, N, dtype, 0.1, 3, seed=29)
+    P.say(f"case: step unaligned {dtype} N={N} {Bsz}x{Dm}")
+    st = generate.step_state(cfg, DEV)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    A = shifted(-torch.exp(torch.randn(Dm, N, device=DEV, generator=torch.Generator(DEV).manual_seed(6))))
+    h = shifted(st["h"])
+    href = P.f64(h)
+    for tok in generate.step_tokens(cfg, st, 3):
+        Bm, Cm = shifted(tok["B"]), shifted(tok["C"])
+        assert (h.data_ptr() | Bm.data_ptr()) % 16 != 0
+        y = ss.step(tok["x"], tok["delta"], A, Bm, Cm, st["D"], h)
+        torch.cuda.synchronize()
+        yr, href = P.oracle_step(tok, A, st["D"], href)
+        P.compare(y, yr, dtype, "y")
+        P.compare(h, href, dtype, "h")
 
 
 def test_step_delta_zero_keeps_state_bitwise(ss):
