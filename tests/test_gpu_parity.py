@@ -411,3 +411,48 @@ def test_decode_full_batch(ss):
     torch.cuda.synchronize()
     P.compare(h[bi2], href2, "bf16", "h after 1000 steps")
     assert np.isfinite(P.f64(h)).all()
+
+
+def test_step_largest_row(ss):
+    """The largest batch row of state the decode step takes (Dm N = 2^24,
+    64 MiB), three rows: one row group with its fourth row past the end."""
+    Bsz, Dm, N = 3, 1 << 20, 16
+    cfg = configs.StepConfig("step_largest_row", Bsz, Dm, N, "bf16", 0.1, 1, seed=37)
+    P.say(f"case: {cfg.name} {Bsz}x{Dm}x{N}")
+    st = generate.step_state(cfg, DEV)
+    h = st["h"]
+    href = P.f64(h)
+    tok = generate.step_tokens(cfg, st, 1)[0]
+    y = ss.step(tok["x"], tok["delta"], st["A"], tok["B"], tok["C"], st["D"], h)
+    torch.cuda.synchronize()
+    yr, href = P.oracle_step(tok, st["A"], st["D"], href)
+    P.compare(y, yr, "bf16", "y")
+    P.compare(h, href, "bf16", "h")
+
+
+@pytest.mark.slow
+def test_decode_batch_in_slices(ss):
+    """A state of more than 1 GiB is stepped in slices of whole batch rows
+    (2048 rows of 8192 x 16 states per slice): rows on both sides of the cut
+    and the last row match the oracle, and nothing is written past the state
+    or past y."""
+    Bsz, Dm, N = 2100, 8192, 16
+    cfg = configs.StepConfig("decode_sliced", Bsz, Dm, N, "bf16", 0.1, 2, seed=31)
+    P.say(f"case: {cfg.name} {Bsz}x{Dm}x{N}")
+    st = generate.step_state(cfg, DEV)
+    guard = 64
+    hbuf = torch.full((Bsz * Dm * N + guard,), 7.0, device=DEV)
+    h = hbuf[:Bsz * Dm * N].view(Bsz, Dm, N)
+    h.copy_(st["h"])
+    del st["h"]
+    ybuf = torch.full((Bsz * Dm + guard,), 7.0, device=DEV, dtype=torch.bfloat16)
+    y = ybuf[:Bsz * Dm].view(Bsz, Dm)
+    bi = [0, 1000, 2047, 2048, 2099]
+    href = P.f64(h[bi])
+    for k, tok in enumerate(generate.step_tokens(cfg, st, 2)):
+        ss.step(tok["x"], tok["delta"], st["A"], tok["B"], tok["C"], st["D"], h, y=y)
+        torch.cuda.synchronize()
+        yr, href = P.oracle_step(tok, st["A"], st["D"], href, b_idx=bi)
+        P.compare(y[bi], yr, "bf16", f"y step {k}")
+        P.compare(h[bi], href, "bf16", f"h step {k}")
+    assert bool((hbuf[Bsz * Dm * N:] == 7.0).all()) and bool((ybuf[Bsz * Dm:] == 7.0).all())
