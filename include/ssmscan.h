@@ -25,7 +25,9 @@
  *     passed as void*, NULL = the default stream) and the call returns.  The
  *     caller synchronises.  Buffers must stay valid until the work completes.
  *   - `dtype` (ssm_dtype) selects the storage type of x, delta, B, C and y.
- *     A, D and the state (h_final, h) are always fp32.  Arithmetic is fp32.
+ *     A, D and the state (h_final, h) are always fp32.  Arithmetic: fp32 for
+ *     bf16 storage; for fp32 storage the scans compute in fp64 and the decode
+ *     steps in fp32 with libm-accurate exp, expm1, sin and cos.
  *   - Return value: SSM_OK (0) or a positive ssm_status.  On an argument error
  *     nothing is enqueued and no device call is made; ssm_last_error() gives
  *     a thread-local description of the most recent failure.
@@ -61,7 +63,8 @@ typedef enum {
 typedef enum {
     SSM_OK = 0,
     SSM_ERR_NULLPTR = 1,        /* a non-empty tensor has a NULL pointer */
-    SSM_ERR_BAD_DIM = 2,        /* a negative size, or a size whose byte count overflows */
+    SSM_ERR_BAD_DIM = 2,        /* a negative size, a size whose byte count overflows, or a size
+                                   above an entry point's stated limit */
     SSM_ERR_BAD_DTYPE = 3,      /* dtype is not an ssm_dtype */
     SSM_ERR_UNSUPPORTED_N = 4,  /* N not in {1, 2, 4, 8, 16} */
     SSM_ERR_ALIGN = 5,          /* a pointer is not aligned to its element size */
