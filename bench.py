@@ -147,18 +147,19 @@ def bench_unfused_softplus(torch, ss, generate, cfg, steps, warmup):
 
 
 def profiled_loop(torch, ss, fn, steps, warmup):
-    """timed_loop with the library's per-kernel event timers on: returns the
-    wall time per step and each kernel kind's average launch duration."""
-    fn(0)
-    torch.cuda.synchronize()
+    """Wall time per step of `steps` calls, then each kernel kind's average
+    launch duration over the same number of calls with the library's
+    per-kernel HIP-event timers on.  The event records add gaps between
+    launches, so the wall time is taken with the timers off."""
+    ms = timed_loop(torch, fn, steps, warmup)
     ss.set_option(ss.SSM_OPT_PROFILE, 1)
     ss.profile_read()
     try:
-        ms = timed_loop(torch, fn, steps, warmup)
+        timed_loop(torch, fn, steps, 0)
         prof = ss.profile_read()
     finally:
         ss.set_option(ss.SSM_OPT_PROFILE, 0)
-    kern = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / (steps + warmup)}
+    kern = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / steps}
             for k, v in prof.items() if v[1] > 0}
     return ms, kern
 
@@ -387,17 +388,9 @@ def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
         t = toks[i % 16]
         ss.step(t["x"], t["delta"], st["A"], t["B"], t["C"], st["D"], st["h"], y=y)
 
-    fn(0)
-    torch.cuda.synchronize()
-    ss.set_option(ss.SSM_OPT_PROFILE, 1)
-    ss.profile_read()
-    try:
-        log(f"[bench] timing {cfg.name}: {n_tokens} steps")
-        ms = timed_loop(torch, fn, n_tokens, 16)
-        prof = ss.profile_read()
-    finally:
-        ss.set_option(ss.SSM_OPT_PROFILE, 0)
-    k_ms = prof["step"][0] / prof["step"][1]
+    log(f"[bench] timing {cfg.name}: {n_tokens} steps")
+    ms, kern = profiled_loop(torch, ss, fn, n_tokens, 16)
+    k_ms = kern["step"]["avg_ms"]
     alg = generate.alg_bytes_step(cfg)
     # The same steps replayed from a captured HIP graph (a decode loop of a
     # serving engine): removes the host launch gap between steps.
