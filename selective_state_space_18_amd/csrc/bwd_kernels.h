@@ -398,19 +398,26 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     const int32_t voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
 
     // state from step t_from over `count` steps (the forward's aggregate loop)
+    // (the aggregate loop carries g / agg_to_g)
+    Acc to_g[N], from_g[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        to_g[n] = agg_to_g<N, kStruct, kEuler, Acc>(Ar, n);
+        from_g[n] = (Acc)1 / to_g[n];
+    }
     auto advance = [&](Acc(&g)[N], int64_t t_from, int count) {
         if (count <= 0) return;
-        if constexpr (kStruct && !kEuler) {
+        if constexpr (!kEuler) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) g[n] *= a0n;
+            for (int n = 0; n < N; ++n) g[n] *= kStruct ? a0n : from_g[n];
         }
         const_row_ptr<Acc> bcp;
         const SegIO<T> io = seg_io<T, Acc, N, false>(p, b, t_from, count, d0, d, bcp);
         Acc lam_unused = 0;
         run_segment<T, N, kStruct, false, kEuler, kPre>(io, bcp, count, Ar, Dd, dp, g, lam_unused);
-        if constexpr (kStruct && !kEuler) {
+        if constexpr (!kEuler) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) g[n] *= inva;
+            for (int n = 0; n < N; ++n) g[n] *= kStruct ? inva : to_g[n];
         }
     };
 
