@@ -437,6 +437,39 @@ def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
     }
 
 
+def bench_complex_decode(torch, ss, generate, cfg, n_tokens, layers=4):
+    """The decode workload with complex A and a complex state (2 x 134 MB per
+    layer), cycling over `layers` layer states as bench_decode does."""
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name} with complex A ({layers} layer states)")
+    states = [generate.step_state_complex(cfg, dev, seed=cfg.seed + 17 * k) for k in range(layers)]
+    toks = generate.step_tokens(cfg, states[0], 16)
+    y = torch.empty(cfg.Bsz, cfg.Dm, dtype=toks[0]["x"].dtype, device=dev)
+
+    def fn(i):
+        st = states[i % layers]
+        t = toks[i % 16]
+        ss.step_complex(t["x"], t["delta"], st["A"], t["B"], t["C"], st["D"], st["h"], y=y)
+
+    log(f"[bench] timing {cfg.name} (complex A): {n_tokens} steps")
+    ms, kern = profiled_loop(torch, ss, fn, n_tokens, 16)
+    k_ms = kern["step"]["avg_ms"]
+    alg = generate.alg_bytes_step_complex(cfg)
+    del states, toks, y
+    torch.cuda.empty_cache()
+    return {
+        "workload": cfg.name + "_complex_A", "steps": n_tokens, "ms_per_step": round(ms, 5),
+        "value": cfg.elems_per_step() / (ms * 1e-3), "unit": "elems/s",
+        "hbm": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
+        "roofline": {"kernel": "cplx_step_kernel", "bound": "hbm",
+                     "achieved": round(alg / (k_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_ms": round(k_ms, 5)},
+        "state_layers_cycled": layers,
+    }
+
+
 def cpu_baseline(torch, generate, cfg, target_s=10.0):
     """The fp64 oracle on a channel subset of the same workload (channels are
     independent, so a subset is the same work per element)."""
@@ -507,7 +540,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
-                                       "complex", "general", "ssd"],
+                                       "complex", "cdecode", "general", "ssd"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
@@ -535,6 +568,10 @@ def main():
 
     if a.only == "decode":
         rec = bench_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "cdecode":
+        rec = bench_complex_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "complex":
@@ -621,6 +658,8 @@ def main():
         sec["ssd_layer"] = bench_ssd(torch, ss, generate, configs.SSD_LAYER, max(5, a.steps // 5), 2)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
                                      configs.DECODE_256x8192.n_tokens)
+        sec["complex_decode"] = bench_complex_decode(torch, ss, generate, configs.DECODE_256x8192,
+                                                     configs.DECODE_256x8192.n_tokens)
         cp = copy_peak(torch)
         out["copy_peak"] = cp
         out["hbm"]["frac_of_copy_peak"] = round(out["hbm"]["achieved"] / cp["achieved"], 4)

@@ -200,7 +200,8 @@ int ssm_scan_complex_fwd(const void *x, const void *delta, const float *delta_bi
                          unsigned flags, void *stream);
 
 /* One decode step with complex A; h [Bsz][Dm][N][2] fp32 updated in place.
- * Arguments otherwise as ssm_step_fused. */
+ * Dm*N may be at most 2^23 (64 MiB of state per batch row), else
+ * SSM_ERR_BAD_DIM.  Arguments otherwise as ssm_step_fused. */
 int ssm_step_complex(const void *x, const void *delta, const float *delta_bias,
                      const float *A, const void *B, const void *C, const float *D,
                      float *h, void *y, int64_t Bsz, int64_t Dm, int64_t N, int dtype,

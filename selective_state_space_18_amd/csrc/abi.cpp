@@ -530,6 +530,9 @@ int cplx_step_impl(const void *x, const void *delta, const float *delta_bias, co
         BDN > INT64_MAX / 64)
         return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, Dm=%lld, N=%lld)", (long long)Bsz, (long long)Dm,
                     (long long)N);
+    if (DN > kStepMaxRowStates / 2)
+        return fail(SSM_ERR_BAD_DIM, "complex decode step: Dm*N = %lld states per batch row exceeds %lld",
+                    (long long)DN, (long long)(kStepMaxRowStates / 2));
     const int64_t es = dtype_size(dtype);
     const Arg in[] = {{x, BD, es, "x"}, {delta, BD, es, "delta"}, {A, 2 * DN, 4, "A"},
                       {B, BN, es, "B"}, {C, BN, es, "C"},         {D, Dm, 4, "D"},

@@ -283,26 +283,33 @@ __global__ __launch_bounds__(kBlock) void cplx_carry_kernel(ScanParams p) {
 
 // Decode step: Q lanes per channel, each owning 2 complex states (16 bytes)
 // of the state row, so a wave-wide access is 1 KiB contiguous; y is summed
-// across the Q lanes with shuffles.  Grid: x over (channel d, lane j) of one
-// batch row (d = i / Q, j = i % Q, Q a power of two: no division), y over
-// batch rows, strided by the grid's height; the per-(d, n) constants of A are
-// formed once per thread.
-template <typename T, int N, bool kPrecise>
+// across the Q lanes with DPP.  Grid: x over (channel d, lane j) of one batch
+// row (d = i / Q, j = i % Q, Q a power of two), y over groups of kStepRows
+// consecutive batch rows; each thread walks its row groups with the next
+// group's loads issued before the current group is computed (two register
+// sets used in turn).  The rows go through buffer descriptors whose range
+// ends at the last batch row, so the fetch past the end reads zeros without a
+// memory access and stores there are dropped: no branch around the loads.
+// The per-(d, n) constants of A are formed once per thread.  kVec: state and
+// B/C rows as vectors (16-byte aligned pointers, checked on the host); kPre:
+// delta goes through the bias / softplus of the fused options.
+constexpr int kStepRows = 4;
+template <typename T, int N, bool kPrecise, bool kVec, bool kPre>
 __global__ __launch_bounds__(kBlock) void cplx_step_kernel(StepParams p) {
     constexpr int SPL = N >= 2 ? 2 : 1;  // complex states per lane
     constexpr int Q = N / SPL;
-    static_assert((Q & (Q - 1)) == 0 && 64 % Q == 0, "Q lanes of a channel within one wave");
-    typedef float Acc;
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t d = i / Q;
-    const int j = (int)(i % Q);
-    if (d >= p.Dm) return;
+    constexpr int kU = kStepRows;
+    static_assert((Q & (Q - 1)) == 0 && Q <= 8, "Q lanes of a channel within one half-row");
+    const int i = blockIdx.x * kBlock + threadIdx.x;
+    const int d = i / Q;
+    const int j = i % Q;
+    if (d >= p.Dm) return;  // the Q lanes of a channel leave together
     float a[SPL], w[SPL], wr[SPL], wi[SPL];
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
         const int n = j * SPL + k;
-        a[k] = p.A[(d * N + n) * 2];
-        w[k] = p.A[(d * N + n) * 2 + 1];
+        a[k] = p.A[((int64_t)d * N + n) * 2];
+        w[k] = p.A[((int64_t)d * N + n) * 2 + 1];
         if (__builtin_fabsf(a[k]) < -kTinyA && __builtin_fabsf(w[k]) < -kTinyA) {
             a[k] = kTinyA;
             w[k] = 0.f;
@@ -313,52 +320,98 @@ __global__ __launch_bounds__(kBlock) void cplx_step_kernel(StepParams p) {
     }
     const float bias = p.delta_bias != nullptr ? p.delta_bias[d] : 0.f;
     const float Dd = p.D[d];
-    for (int64_t b = blockIdx.y; b < p.Bsz; b += gridDim.y) {
-        const int64_t ch = b * p.Dm + d;
-        Acc dv = to_f32(static_cast<const T *>(p.delta)[ch]);
-        if (p.delta_bias != nullptr || p.delta_softplus) {
-            const float v = dv + bias;
-            dv = p.delta_softplus ? (kPrecise ? softplus_precise(v) : softplus_(v)) : v;
-        }
-        const Acc xv = to_f32(static_cast<const T *>(p.x)[ch]);
-        float *hp = p.h + (ch * N + j * SPL) * 2;
-        Acc yv = 0;
+
+    const int Dm = (int)p.Dm;
+    const int Bsz = (int)p.Bsz;
+    const auto rh = make_rsrc(p.h, (int32_t)((int64_t)Bsz * Dm * N * 8));
+    const auto rx = make_rsrc(p.x, (int32_t)((int64_t)Bsz * Dm * sizeof(T)));
+    const auto rd = make_rsrc(p.delta, (int32_t)((int64_t)Bsz * Dm * sizeof(T)));
+    const auto rb = make_rsrc(p.B, (int32_t)(Bsz * N * (int)sizeof(T)));
+    const auto rc = make_rsrc(p.C, (int32_t)(Bsz * N * (int)sizeof(T)));
+    const auto ry = make_rsrc(p.y, (int32_t)((int64_t)Bsz * Dm * sizeof(T)));
+    const int vh = (d * N + j * SPL) * 8;
+    const int vx = d * (int)sizeof(T);
+    const int vbc = j * SPL * (int)sizeof(T);
+    const int rowh = Dm * N * 8, rowx = Dm * (int)sizeof(T), rowbc = N * (int)sizeof(T);
+
+    struct In {
+        float h[kU][2 * SPL];  // (re, im) pairs
+        T xv[kU], dv[kU], bv[kU][SPL], cv[kU][SPL];
+    };
+    auto load = [&](int b0, In &in) {
 #pragma unroll
-        for (int k = 0; k < SPL; ++k) {
-            const int n = j * SPL + k;
-            const float zr = dv * a[k], zi = dv * w[k];
-            float mag, c, s, em1;
-            if constexpr (kPrecise) {
-                c = cosf(zi);
-                s = sinf(zi);
-                em1 = expm1f(zr);
-                mag = em1 + 1.f;
-            } else {
-                cplx_exp(zr, zi, mag, c, s, em1);
-            }
-            const float abr = mag * c, abi = mag * s;
-            const float u = to_f32(static_cast<const T *>(p.B)[b * N + n]) * xv;
-            float br, bi;
-            if (p.euler_b) {
-                br = dv * u;
-                bi = 0.f;
-            } else {
-                const float hs = kPrecise ? sinf(0.5f * zi) : 0.f;
-                const float cm1 = kPrecise ? -2.f * hs * hs : c - 1.f;
-                const float er = __builtin_fmaf(em1, c, cm1), ei = abi;
-                br = (er * wr[k] - ei * wi[k]) * u;
-                bi = (er * wi[k] + ei * wr[k]) * u;
-            }
-            const float r = hp[2 * k], m = hp[2 * k + 1];
-            const float nr = __builtin_fmaf(abr, r, __builtin_fmaf(-abi, m, br));
-            const float ni = __builtin_fmaf(abr, m, __builtin_fmaf(abi, r, bi));
-            hp[2 * k] = nr;
-            hp[2 * k + 1] = ni;
-            yv = __builtin_fmaf(to_f32(static_cast<const T *>(p.C)[b * N + n]), nr, yv);
+        for (int u = 0; u < kU; ++u) {
+            const int b = b0 + u;  // rows past the end read zeros
+            load_run<float, 2 * SPL, kVec, kBufNt>(rh, vh, b * rowh, in.h[u]);
+            T tmp[1];
+            load_run<T, 1, false, 0>(rx, vx, b * rowx, tmp);
+            in.xv[u] = tmp[0];
+            load_run<T, 1, false, 0>(rd, vx, b * rowx, tmp);
+            in.dv[u] = tmp[0];
+            load_run<T, SPL, kVec, 0>(rb, vbc, b * rowbc, in.bv[u]);
+            load_run<T, SPL, kVec, 0>(rc, vbc, b * rowbc, in.cv[u]);
         }
+    };
+    auto compute = [&](int b0, const In &cur) {
 #pragma unroll
-        for (int off = 1; off < Q; off <<= 1) yv += __shfl_xor(yv, off, Q);
-        if (j == 0) static_cast<T *>(p.y)[ch] = from_acc<T>(__builtin_fmaf(Dd, xv, yv));
+        for (int u = 0; u < kU; ++u) {
+            const int b = b0 + u;  // rows past the end compute on zeros and store nothing
+            const float xv = to_f32(cur.xv[u]);
+            float dv = to_f32(cur.dv[u]);
+            if constexpr (kPre) {
+                const float v = dv + bias;
+                dv = p.delta_softplus ? (kPrecise ? softplus_precise(v) : softplus_(v)) : v;
+            }
+            float hn[2 * SPL];
+            float yv = 0.f;
+#pragma unroll
+            for (int k = 0; k < SPL; ++k) {
+                const float zr = dv * a[k], zi = dv * w[k];
+                float mag, c, s, em1;
+                if constexpr (kPrecise) {
+                    c = cosf(zi);
+                    s = sinf(zi);
+                    em1 = expm1f(zr);
+                    mag = em1 + 1.f;
+                } else {
+                    cplx_exp(zr, zi, mag, c, s, em1);
+                }
+                const float abr = mag * c, abi = mag * s;
+                const float uu = to_f32(cur.bv[u][k]) * xv;
+                float br, bi;
+                if (p.euler_b) {
+                    br = dv * uu;
+                    bi = 0.f;
+                } else {
+                    const float hs = kPrecise ? sinf(0.5f * zi) : 0.f;
+                    const float cm1 = kPrecise ? -2.f * hs * hs : c - 1.f;
+                    const float er = __builtin_fmaf(em1, c, cm1), ei = abi;
+                    br = (er * wr[k] - ei * wi[k]) * uu;
+                    bi = (er * wi[k] + ei * wr[k]) * uu;
+                }
+                const float r = cur.h[u][2 * k], m = cur.h[u][2 * k + 1];
+                hn[2 * k] = __builtin_fmaf(abr, r, __builtin_fmaf(-abi, m, br));
+                hn[2 * k + 1] = __builtin_fmaf(abr, m, __builtin_fmaf(abi, r, bi));
+                yv = __builtin_fmaf(to_f32(cur.cv[u][k]), hn[2 * k], yv);
+            }
+            store_run<2 * SPL, kVec, kBufNt>(hn, rh, vh, b * rowh);
+            yv = lane_group_sum<Q>(yv);
+            if (j == 0) buf_store(from_acc<T>(__builtin_fmaf(Dd, xv, yv)), ry, vx, b * rowx);
+        }
+    };
+    const int gstep = gridDim.y * kU;
+    int b0 = blockIdx.y * kU;
+    In ra, rb2;
+    load(b0, ra);
+    for (;;) {
+        load(b0 + gstep, rb2);
+        compute(b0, ra);
+        b0 += gstep;
+        if (b0 >= Bsz) break;
+        load(b0 + gstep, ra);
+        compute(b0, rb2);
+        b0 += gstep;
+        if (b0 >= Bsz) break;
     }
 }
 
@@ -426,24 +479,64 @@ hipError_t cplx_pass(ScanPass pass, const ScanParams &p, int N, hipStream_t s) {
     }
 }
 
+// Offsets of one launch, the fetch past the last row included, stay below
+// 2^31: the batch is stepped in slices of at most kCplxSliceBytes of state,
+// the row stride of a thread is capped so that the overrun is at most as much
+// again, and a batch row holds at most kCplxMaxRowBytes (the host rejects
+// larger Dm * N).
+constexpr int64_t kCplxSliceBytes = int64_t(1) << 30;
+constexpr int64_t kCplxMaxRowBytes = int64_t(1) << 26;
+constexpr int64_t kCplxTargetBlocks = 256;  // blocks per launch: about one per compute unit
+
+template <typename T, bool kPrecise, int N, bool kVec, bool kPre>
+hipError_t cplx_step_n(const StepParams &p, hipStream_t s) {
+    constexpr int Q = N >= 2 ? N / 2 : 1;
+    constexpr int kU = kStepRows;
+    const int64_t row_bytes = p.Dm * N * 8;
+    const int64_t rows = kCplxSliceBytes / row_bytes;  // >= 16
+    const unsigned gx = (unsigned)((p.Dm * Q + kBlock - 1) / kBlock);
+    int64_t want = (kCplxTargetBlocks + (int64_t)gx - 1) / (int64_t)gx;
+    if (want > rows / kU - 1) want = rows / kU - 1;
+    if (want < 1) want = 1;
+    for (int64_t r0 = 0; r0 < p.Bsz; r0 += rows) {
+        StepParams q = p;
+        q.Bsz = p.Bsz - r0 < rows ? p.Bsz - r0 : rows;
+        q.x = static_cast<const T *>(p.x) + r0 * p.Dm;
+        q.delta = static_cast<const T *>(p.delta) + r0 * p.Dm;
+        q.y = static_cast<T *>(p.y) + r0 * p.Dm;
+        q.B = static_cast<const T *>(p.B) + r0 * N;
+        q.C = static_cast<const T *>(p.C) + r0 * N;
+        q.h = p.h + r0 * p.Dm * N * 2;
+        const int64_t groups = (q.Bsz + kU - 1) / kU;
+        const dim3 grid(gx, (unsigned)(groups < want ? groups : want));
+        hipLaunchKernelGGL((cplx_step_kernel<T, N, kPrecise, kVec, kPre>), grid, dim3(kBlock), 0, s, q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <typename T, bool kPrecise, int N>
+hipError_t cplx_step_v(const StepParams &p, hipStream_t s) {
+    if (p.Dm * N * 8 > kCplxMaxRowBytes) return hipErrorInvalidValue;
+    const bool vec = ((reinterpret_cast<uintptr_t>(p.h) | reinterpret_cast<uintptr_t>(p.B) |
+                       reinterpret_cast<uintptr_t>(p.C)) & 15) == 0;
+    const bool pre = p.delta_bias != nullptr || p.delta_softplus;
+    if (vec) return pre ? cplx_step_n<T, kPrecise, N, true, true>(p, s) : cplx_step_n<T, kPrecise, N, true, false>(p, s);
+    return pre ? cplx_step_n<T, kPrecise, N, false, true>(p, s) : cplx_step_n<T, kPrecise, N, false, false>(p, s);
+}
+
 template <typename T, bool kPrecise>
 hipError_t cplx_step_launch(const StepParams &p, int N, hipStream_t s) {
     if (p.Bsz * p.Dm == 0) return hipSuccess;
-    const int Q = N >= 2 ? N / 2 : 1;
-    const unsigned gx = (unsigned)((p.Dm * Q + kBlock - 1) / kBlock);
-    // about 2048 blocks in all, at least one row each
-    int64_t want = (2048 + (int64_t)gx - 1) / (int64_t)gx;
-    if (want < 1) want = 1;
-    const dim3 grid(gx, (unsigned)(p.Bsz < want ? p.Bsz : want));
     switch (N) {
-        case 1: hipLaunchKernelGGL((cplx_step_kernel<T, 1, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((cplx_step_kernel<T, 2, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
-        case 4: hipLaunchKernelGGL((cplx_step_kernel<T, 4, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
-        case 8: hipLaunchKernelGGL((cplx_step_kernel<T, 8, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
-        case 16: hipLaunchKernelGGL((cplx_step_kernel<T, 16, kPrecise>), dim3(grid), dim3(kBlock), 0, s, p); break;
+        case 1: return cplx_step_v<T, kPrecise, 1>(p, s);
+        case 2: return cplx_step_v<T, kPrecise, 2>(p, s);
+        case 4: return cplx_step_v<T, kPrecise, 4>(p, s);
+        case 8: return cplx_step_v<T, kPrecise, 8>(p, s);
+        case 16: return cplx_step_v<T, kPrecise, 16>(p, s);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

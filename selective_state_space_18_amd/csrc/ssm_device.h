@@ -148,6 +148,69 @@ __device__ __forceinline__ float softplus_precise(float v) {
 __device__ __forceinline__ double exp_units(double z) { return exp(z); }
 __device__ __forceinline__ float exp_units(float z2) { return fast_exp2(z2); }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufNt = 2;  // buffer cache-policy bit: nontemporal
+
+// K consecutive values of T at byte offset voff + soff of a buffer: one
+// vector load where kVec guarantees the alignment, else one per value.
+template <typename T, int K, bool kVec, int kAux>
+__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff, T (&v)[K]) {
+    constexpr int bytes = K * (int)sizeof(T);
+    if constexpr (kVec && bytes == 16) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAux);
+        __builtin_memcpy(v, &w, 16);
+    } else if constexpr (kVec && bytes == 8) {
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kAux);
+        __builtin_memcpy(v, &w, 8);
+    } else if constexpr (kVec && bytes == 4) {
+        const unsigned w = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kAux);
+        __builtin_memcpy(v, &w, 4);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if constexpr (sizeof(T) == 4)
+                v[k] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * k, soff, kAux));
+            else
+                v[k] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2 * k, soff, kAux));
+        }
+    }
+}
+
+// K consecutive fp32 values stored at byte offset voff + soff of a buffer,
+// as one vector store where kVec guarantees the alignment.
+template <int K, bool kVec, int kAux>
+__device__ __forceinline__ void store_run(const float (&v)[K], __amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    if constexpr (kVec && K == 4) {
+        u32x4 w;
+        __builtin_memcpy(&w, v, 16);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kAux);
+    } else if constexpr (kVec && K == 2) {
+        u32x2 w;
+        __builtin_memcpy(&w, v, 8);
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, kAux);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[k]), r, voff + 4 * k, soff, kAux);
+    }
+}
+
+// Sum over aligned groups of Q <= 8 lanes by DPP (every lane of a group gets
+// the group's sum): quad permutations, then the mirror within 8 lanes, which
+// pairs each quad with the other quad of its half-row.
+template <int Q>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    static_assert(Q == 1 || Q == 2 || Q == 4 || Q == 8, "groups of 1, 2, 4 or 8 lanes");
+    if constexpr (Q >= 2)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // lanes 1,0,3,2
+    if constexpr (Q >= 4)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // lanes 2,3,0,1
+    if constexpr (Q >= 8)
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // lane i <- 7-i
+    return v;
+}
+
 // Wave-uniform value (the compiler then keeps it in an SGPR).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -29,45 +29,6 @@ struct StepShape {
     static constexpr int SPL = N / Q;               // states per lane
 };
 
-// Sum over the Q <= 4 lanes of one channel (aligned groups within a quad) by
-// DPP quad permutations: no LDS round trip.
-template <int Q>
-__device__ __forceinline__ float quad_sum(float v) {
-    if constexpr (Q >= 2)
-        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // lanes 1,0,3,2
-    if constexpr (Q >= 4)
-        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // lanes 2,3,0,1
-    return v;
-}
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-constexpr int kNt = 2;  // buffer cache policy: nontemporal
-
-// SPL consecutive values of T at byte offset voff + soff of a buffer: one
-// vector load where kVec guarantees the alignment, else one per value.
-template <typename T, int SPL, bool kVec, int kAux>
-__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff, T (&v)[SPL]) {
-    constexpr int bytes = SPL * (int)sizeof(T);
-    if constexpr (kVec && bytes == 16) {
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAux);
-        __builtin_memcpy(v, &w, 16);
-    } else if constexpr (kVec && bytes == 8) {
-        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kAux);
-        __builtin_memcpy(v, &w, 8);
-    } else if constexpr (kVec && bytes == 4 && sizeof(T) == 4) {
-        v[0] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kAux));
-    } else {
-#pragma unroll
-        for (int k = 0; k < SPL; ++k) {
-            if constexpr (sizeof(T) == 4)
-                v[k] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * k, soff, kAux));
-            else
-                v[k] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2 * k, soff, kAux));
-        }
-    }
-}
-
 // Grid: x runs over (channel d, lane j) of one batch row -- d = i / Q and
 // j = i % Q with Q a power of two -- and y over groups of kU consecutive batch
 // rows.  About one block runs per compute unit, and each thread walks the row
@@ -146,7 +107,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepParams p) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int b = b0 + u;  // rows past the end read zeros
-            load_run<float, SPL, kVec, kNt>(rh, vh, b * rowh, in.h[u]);
+            load_run<float, SPL, kVec, kBufNt>(rh, vh, b * rowh, in.h[u]);
             T tmp[1];
             load_run<T, 1, false, 0>(rx, vx, b * rowx, tmp);
             in.xv[u] = tmp[0];
@@ -177,16 +138,8 @@ __global__ __launch_bounds__(kBlock) void step_kernel(StepParams p) {
                 h[k] = __builtin_fmaf(abar, cur.h[u][k], coef * bx);
                 yv = __builtin_fmaf(to_f32(cur.cv[u][k]), h[k], yv);
             }
-            if constexpr (kVec && SPL == 4) {
-                u32x4 w;
-                __builtin_memcpy(&w, h, 16);
-                __builtin_amdgcn_raw_buffer_store_b128(w, rh, vh, b * rowh, kNt);
-            } else {
-#pragma unroll
-                for (int k = 0; k < SPL; ++k)
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, h[k]), rh, vh + 4 * k, b * rowh, kNt);
-            }
-            yv = quad_sum<Q>(yv);
+            store_run<SPL, kVec && SPL == 4, kBufNt>(h, rh, vh, b * rowh);
+            yv = lane_group_sum<Q>(yv);
             if (j == 0) buf_store(from_acc<T>(__builtin_fmaf(Dd, xv, yv)), ry, vx, b * rowx);
         }
     };

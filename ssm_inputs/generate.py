@@ -123,6 +123,17 @@ def step_tokens(cfg: StepConfig, state: Dict[str, torch.Tensor], n_tokens: int) 
     return out
 
 
+def step_state_complex(cfg: StepConfig, device="cpu", seed=None) -> Dict[str, torch.Tensor]:
+    """step_state with complex A (the complex_A recipe, seed + 100) and a
+    complex resident state: the real part as step_state draws it, then the
+    imaginary part ~ N(0, h0_std) from the same generator."""
+    st = step_state(cfg, device, seed)
+    im = _normal((cfg.Bsz, cfg.Dm, cfg.N), st["_gen"], torch.device(device), cfg.h0_std)
+    st["h"] = torch.complex(st["h"], im)
+    st["A"] = complex_A(cfg.Dm, cfg.N, (cfg.seed if seed is None else seed) + 100, device)
+    return st
+
+
 def complex_A(Dm: int, N: int, seed: int, device="cpu") -> torch.Tensor:
     """Complex diagonal A [Dm, N] (complex64): real part -exp(N(0, 0.5)),
     imaginary part pi * n * (1 + 0.1 N(0, 1)) -- decaying oscillators whose
@@ -248,4 +259,12 @@ def alg_bytes_step(cfg: StepConfig) -> int:
     BD, BN = cfg.Bsz * cfg.Dm, cfg.Bsz * cfg.N
     return (8 * BD * cfg.N + 2 * s * BD + 2 * s * BN + s * BD
             + 4 * cfg.Dm * cfg.N + 4 * cfg.Dm)
+
+
+def alg_bytes_step_complex(cfg: StepConfig) -> int:
+    """As alg_bytes_step with a complex state and A (8 bytes per value)."""
+    s = 4 if cfg.dtype == "fp32" else 2
+    BD, BN = cfg.Bsz * cfg.Dm, cfg.Bsz * cfg.N
+    return (16 * BD * cfg.N + 2 * s * BD + 2 * s * BN + s * BD
+            + 8 * cfg.Dm * cfg.N + 4 * cfg.Dm)
 

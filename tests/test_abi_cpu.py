@@ -215,6 +215,20 @@ def test_step_argument_errors(L):
                       2, 64, 16, None) == 1
 
 
+def test_complex_step_argument_errors(L):
+    v = ctypes.c_void_p
+
+    def cstep(Bsz=2, Dm=64, N=16, dtype=1, flags=0, h=P[6]):
+        return L.ssm_step_complex(v(P[0]), v(P[1]), v(None), v(P[2]), v(P[3]), v(P[4]), v(P[5]), v(h), v(P[7]),
+                                  Bsz, Dm, N, dtype, flags, None)
+
+    assert cstep(dtype=2) == 3
+    assert cstep(N=3) == 4
+    assert cstep(flags=8) == 9
+    assert cstep(Dm=1 << 20) == 2          # 2^24 complex states per batch row
+    assert cstep(h=P[6] + 2) == 5
+
+
 def test_options(L):
     from selective_state_space_18_amd import ssmscan
     assert L.ssm_get_option(1) == 0 and L.ssm_get_option(2) == 0 and L.ssm_get_option(4) == 4

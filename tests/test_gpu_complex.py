@@ -160,6 +160,63 @@ def test_complex_step_many_rows(ss, Bsz, Dm, N):
     compare_complex(h, hr, "bf16", "h")
 
 
+@pytest.mark.parametrize("dtype,N", [("bf16", 16), ("fp32", 2)])
+def test_complex_step_unaligned(ss, dtype, N):
+    """State (as (re, im) fp32 pairs), B and C one element past a 16-byte
+    boundary: the element-wise (non-vector) path of the decode step."""
+    P.say(f"case: complex step unaligned {dtype} N={N}")
+    Bsz, Dm = 6, 70
+    inp = make(dtype, Bsz, 1, Dm, N, seed=17 + N, kind="plain")
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    h = shifted(torch.view_as_real(inp["h_init"]).contiguous())
+    h0 = c128(torch.view_as_complex(h.clone()))
+    x, dl = (inp[k][:, 0].contiguous() for k in ("x", "delta"))
+    B, C = (shifted(inp[k][:, 0].contiguous()) for k in ("B", "C"))
+    assert (h.data_ptr() | B.data_ptr()) % 16 != 0
+    y = ss.step_complex(x, dl, inp["A"], B, C, inp["D"], h)
+    torch.cuda.synchronize()
+    yr, hr = oracle.step_complex(P.f64(x), P.f64(dl), c128(inp["A"]), P.f64(B), P.f64(C), P.f64(inp["D"]), h0)
+    P.compare(y, yr, dtype, "y")
+    compare_complex(torch.view_as_complex(h.clone()), hr, dtype, "h")
+
+
+@pytest.mark.slow
+def test_complex_decode_batch_in_slices(ss):
+    """The decode workload's shape with complex A and 1100 batch rows: 1.15 GB
+    of complex state, stepped in slices of 1024 rows.  Rows on both sides of
+    the cut and the last row match the oracle; nothing is written past the
+    state or past y."""
+    Bsz, Dm, N = 1100, 8192, 16
+    cfg = configs.DECODE_256x8192.with_shape(Bsz=Bsz, Dm=Dm)
+    P.say(f"case: complex decode {Bsz}x{Dm}x{N}")
+    st = generate.step_state_complex(cfg, DEV)
+    guard = 64
+    hbuf = torch.full((Bsz * Dm * N * 2 + guard,), 7.0, device=DEV)
+    h = hbuf[:Bsz * Dm * N * 2].view(Bsz, Dm, N, 2)
+    h.copy_(torch.view_as_real(st["h"]))
+    del st["h"]
+    ybuf = torch.full((Bsz * Dm + guard,), 7.0, device=DEV, dtype=torch.bfloat16)
+    y = ybuf[:Bsz * Dm].view(Bsz, Dm)
+    bi = [0, 700, 1023, 1024, 1099]
+    idx = torch.tensor(bi, device=DEV)
+    href = c128(torch.view_as_complex(h.index_select(0, idx).contiguous()))
+    for k, tok in enumerate(generate.step_tokens(cfg, st, 2)):
+        ss.step_complex(tok["x"], tok["delta"], st["A"], tok["B"], tok["C"], st["D"], h, y=y)
+        torch.cuda.synchronize()
+        sel = lambda t: P.f64(t.index_select(0, idx))
+        yr, href = oracle.step_complex(sel(tok["x"]), sel(tok["delta"]), c128(st["A"]), sel(tok["B"]), sel(tok["C"]),
+                                       P.f64(st["D"]), href)
+        P.compare(y.index_select(0, idx), yr, "bf16", f"y step {k}")
+        compare_complex(torch.view_as_complex(h.index_select(0, idx).contiguous()), href, "bf16", f"h step {k}")
+    assert bool((hbuf[Bsz * Dm * N * 2:] == 7.0).all()) and bool((ybuf[Bsz * Dm:] == 7.0).all())
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_complex_step_chain_equals_scan(ss, dtype):
     P.say(f"case: complex step chain {dtype}")

@@ -73,6 +73,20 @@ def test_decode_tokens():
     assert not torch.equal(toks[0]["x"], toks[1]["x"])
 
 
+def test_decode_state_complex():
+    cfg = configs.DECODE_256x8192.with_shape(Bsz=4, Dm=128)
+    st = generate.step_state_complex(cfg)
+    real = generate.step_state(cfg)
+    assert st["h"].dtype == torch.complex64 and st["h"].shape == (4, 128, 16)
+    assert torch.equal(st["h"].real, real["h"])  # the real part is step_state's draw
+    assert abs(st["h"].imag.std().item() - 0.1) < 0.01
+    assert st["A"].dtype == torch.complex64 and bool((st["A"].real < 0).all())
+    # complex state and A take 8 bytes per value: 2 x 134 MB of state per step at full size
+    full = configs.DECODE_256x8192
+    extra = 8 * full.Bsz * full.Dm * full.N + 4 * full.Dm * full.N
+    assert generate.alg_bytes_step_complex(full) - generate.alg_bytes_step(full) == extra
+
+
 def test_algorithmic_bytes_match_published_table():
     # inputs read once + outputs written once; the [B,L,D,N] state never counts
     assert abs(generate.alg_bytes_scan(configs.MAMBA2P8B_LAYER) / 1e6 - 2019.1) < 0.5
