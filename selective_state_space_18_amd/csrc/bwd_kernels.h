@@ -452,9 +452,10 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
         return;
     }
 
-    // inputs of one sub-chunk (steps clamped into it), loaded one sub-chunk ahead
+    // inputs of one sub-chunk (steps clamped into it), loaded one sub-chunk
+    // ahead as raw bits, one value per register (buf_load_raw)
     struct SubIn {
-        T x[kC], dl[kC], dy[kC];
+        uint32_t x[kC], dl[kC], dy[kC];
     };
     auto load_sub = [&](int64_t ta, int nc, SubIn &in) {
         const int64_t off = (b * p.L + ta) * p.Dm + d0;
@@ -464,9 +465,9 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
 #pragma unroll
         for (int i = 0; i < kC; ++i) {
             const int so = (i < nc ? i : nc - 1) * row;
-            in.x[i] = buf_load<T>(rx, voff, so);
-            in.dl[i] = buf_load<T>(rdl, voff, so);
-            in.dy[i] = buf_load<T>(rdy, voff, so);
+            in.x[i] = buf_load_raw<T>(rx, voff, so);
+            in.dl[i] = buf_load_raw<T>(rdl, voff, so);
+            in.dy[i] = buf_load_raw<T>(rdy, voff, so);
         }
     };
 
@@ -565,9 +566,9 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
             for (int i = 0; i < kC; ++i) {
                 // lanes past the row (shadowing a valid channel) take x = dy = 0:
                 // every dB and dC share is a multiple of x or dy, so theirs vanish
-                xs[i] = live ? (Acc)to_f32(cur.x[i]) : (Acc)0;
-                ds[i] = (Acc)to_f32(cur.dl[i]);
-                gys[i] = live ? (Acc)to_f32(cur.dy[i]) : (Acc)0;
+                xs[i] = live ? (Acc)raw_to_f32<T>(cur.x[i]) : (Acc)0;
+                ds[i] = (Acc)raw_to_f32<T>(cur.dl[i]);
+                gys[i] = live ? (Acc)raw_to_f32<T>(cur.dy[i]) : (Acc)0;
             }
             if constexpr (kPre) {
 #pragma unroll

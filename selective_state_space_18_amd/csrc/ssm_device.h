@@ -103,6 +103,27 @@ template <>
 __device__ __forceinline__ float buf_load<float>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
+// The raw bits of one stored value, one per 32-bit register (a bf16 load
+// zero-extends).  Keeping prefetched bf16 values apart like this matters: two
+// bf16 packed into one register make the compiler wait for both loads at once.
+template <typename T>
+__device__ __forceinline__ uint32_t buf_load_raw(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff);
+template <>
+__device__ __forceinline__ uint32_t buf_load_raw<bf16>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+template <>
+__device__ __forceinline__ uint32_t buf_load_raw<float>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+template <typename T>
+__device__ __forceinline__ float raw_to_f32(uint32_t u) {
+    if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(float, u << 16);  // bf16 -> fp32 is exact
+    else
+        return __builtin_bit_cast(float, u);
+}
+
 __device__ __forceinline__ void buf_store(bf16 v, __amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, voff, soff, 0);
 }
