@@ -190,14 +190,14 @@ __global__ __launch_bounds__(kBlock) void cplx_segment_kernel(ScanParams p) {
     const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
 
     constexpr int G = kPrefetch;
-    T xc[G], dc[G], xn[G], dn[G];
-    auto load = [&](int tb, T(&xs)[G], T(&ds)[G]) {
+    uint32_t xc[G], dc[G], xn[G], dn[G];  // raw bits, one value per register (buf_load_raw)
+    auto load = [&](int tb, uint32_t(&xs)[G], uint32_t(&ds)[G]) {
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             const int t = tb + k;
             const int so = (t < nsteps - 1 ? t : nsteps - 1) * row;
-            xs[k] = buf_load<T>(rx, voff, so);
-            ds[k] = buf_load<T>(rdl, voff, so);
+            xs[k] = buf_load_raw<T>(rx, voff, so);
+            ds[k] = buf_load_raw<T>(rdl, voff, so);
         }
     };
     Acc lam = 0;
@@ -210,8 +210,8 @@ __global__ __launch_bounds__(kBlock) void cplx_segment_kernel(ScanParams p) {
             if (t < nsteps) {
                 Acc rw[2 * N];
                 load_row<N>(rw, bcp + (int64_t)t * (2 * N));
-                const Acc xv = (Acc)to_f32(xc[k]);
-                Acc dv = (Acc)to_f32(dc[k]);
+                const Acc xv = (Acc)raw_to_f32<T>(xc[k]);
+                Acc dv = (Acc)raw_to_f32<T>(dc[k]);
                 if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
                 const Acc yv = cplx_step<N, kOut, kEuler>(cc, rw, xv, dv, hr, hi);
                 if constexpr (kOut)
