@@ -116,14 +116,14 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
     for (int n = 0; n < N; ++n) nu[n] = 0;
     Acc lam = 0;
     constexpr int G = kPrefetch;
-    T dl_c[G], dy_c[G], dl_n[G], dy_n[G];
-    auto load = [&](int tb, T(&dl)[G], T(&dyv)[G]) {
+    uint32_t dl_c[G], dy_c[G], dl_n[G], dy_n[G];  // raw bits, one value per register (buf_load_raw)
+    auto load = [&](int tb, uint32_t(&dl)[G], uint32_t(&dyv)[G]) {
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             const int t = tb - k;
             const int so = (t > 0 ? t : 0) * row;
-            dl[k] = buf_load<T>(rdl, voff, so);
-            dyv[k] = buf_load<T>(rdy, voff, so);
+            dl[k] = buf_load_raw<T>(rdl, voff, so);
+            dyv[k] = buf_load_raw<T>(rdy, voff, so);
         }
     };
     load(nsteps - 1, dl_c, dy_c);
@@ -136,9 +136,9 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
                 Acc crow[N];
 #pragma unroll
                 for (int n = 0; n < N; ++n) crow[n] = bcp[(int64_t)t * (2 * N) + N + n];
-                Acc dv = (Acc)to_f32(dl_c[k]);
+                Acc dv = (Acc)raw_to_f32<T>(dl_c[k]);
                 if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
-                const Acc g = (Acc)to_f32(dy_c[k]);
+                const Acc g = (Acc)raw_to_f32<T>(dy_c[k]);
                 lam += dv;
                 if constexpr (kStruct) {
                     Acc r;
