@@ -470,14 +470,14 @@ def bench_complex_decode(torch, ss, generate, cfg, n_tokens, layers=4):
     }
 
 
-def cpu_baseline(torch, generate, cfg, target_s=10.0):
+def cpu_baseline(torch, generate, cfg, target_s=10.0, dev="cuda:0"):
     """The fp64 oracle on a channel subset of the same workload (channels are
-    independent, so a subset is the same work per element)."""
+    independent, so a subset is the same work per element).  The inputs are
+    drawn on `dev` as for the GPU run and copied to the host."""
     import numpy as np
     import oracle
 
     threads = len(os.sched_getaffinity(0))
-    dev = "cuda:0"
     inp = generate.scan_inputs(cfg, dev)
 
     def run(nch, nthreads=threads):
