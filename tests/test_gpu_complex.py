@@ -144,7 +144,7 @@ def test_complex_step_matches_oracle(ss, dtype, kind, N):
     compare_complex(h, hr, dtype, "h")
 
 
-@pytest.mark.parametrize("Bsz,Dm,N", [(700, 130, 16), (900, 33, 4)])
+@pytest.mark.parametrize("Bsz,Dm,N", [(700, 130, 16), (900, 33, 4), (1, 1, 16), (3, 1, 1)])
 def test_complex_step_many_rows(ss, Bsz, Dm, N):
     """More batch rows than the grid has rows of blocks: each block walks
     several rows (and a remainder)."""

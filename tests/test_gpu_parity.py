@@ -235,7 +235,8 @@ def test_no_write_outside_outputs(ss):
 
 
 @pytest.mark.parametrize("dtype,N,Bsz,Dm", [("fp32", 16, 3, 70), ("bf16", 16, 5, 130), ("fp32", 4, 2, 33),
-                                            ("bf16", 8, 4, 64), ("bf16", 2, 3, 17), ("fp32", 1, 2, 9)])
+                                            ("bf16", 8, 4, 64), ("bf16", 2, 3, 17), ("fp32", 1, 2, 9),
+                                            ("bf16", 16, 1, 1), ("fp32", 1, 1, 1)])
 def test_step_matches_oracle(ss, dtype, N, Bsz, Dm):
     cfg = configs.StepConfig("small_step", Bsz, Dm, N, dtype, 0.1, 4, seed=21)
     P.say(f"case: step {dtype} N={N} {Bsz}x{Dm}")
