@@ -869,7 +869,7 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     const size_t sz_agg = align256((S > 1 ? S - 1 : 0) * (N + 1) * BD * acc);
     const size_t sz_gin = align256(S * N * BD * acc);
     const size_t sz_ragg = align256(S * (N + 1) * BD * acc);
-    const size_t sz_gout = align256(S * N * BD * acc);
+    const size_t sz_gout = align256((size_t)q.n_groups * N * BD * acc);
     const size_t sz_pbc = align256((size_t)2 * q.blocks_per_row * 2 * BLN * acc);
     const size_t sz_pa = align256((size_t)q.n_groups * BD * N * acc);
     const size_t sz_pd = align256((size_t)q.n_groups * BD * 2 * acc);

@@ -197,7 +197,10 @@ __global__ __launch_bounds__(kBlock) void bwd_carry_kernel(BwdParams q) {
     const Acc *__restrict__ ragg = static_cast<const Acc *>(q.ragg);
     Acc *__restrict__ out = static_cast<Acc *>(q.gout) + (int64_t)n * BD + ch;
     const int64_t sa = (int64_t)(N + 1) * BD, sg = (int64_t)N * BD;
-    out[(int64_t)(p.S - 1) * sg] = nu;
+    const int spg = q.seg_per_group;
+    // only the last segment of each group needs it: the main pass carries the
+    // adjoint from segment to segment inside a group
+    out[(int64_t)((p.S - 1) / spg) * sg] = nu;
     constexpr int kBatch = 16;
     for (int s1 = p.S - 1; s1 >= 1; s1 -= kBatch) {
         Acc lc[kBatch], gc[kBatch];
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(kBlock) void bwd_carry_kernel(BwdParams q) {
             const int s = s1 - k;
             if (s >= 1) {
                 nu = fma_(lc[k], nu, gc[k]);
-                out[(int64_t)(s - 1) * sg] = nu;
+                if ((s - 1) % spg == spg - 1) out[(int64_t)((s - 1) / spg) * sg] = nu;
             }
         }
     }
@@ -495,10 +498,11 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     };
 
     if (!wave_on) {
-        // same barriers as the working waves, and their share of the sums
-        for (int si = 0; si < q.seg_per_group; ++si) {
+        // same barriers as the working waves (same segment order), and their
+        // share of the sums
+        for (int si = q.seg_per_group - 1; si >= 0; --si) {
             const int s = grp * q.seg_per_group + si;
-            if (s >= p.S) break;
+            if (s >= p.S) continue;
             const int64_t t0 = (int64_t)s * p.seg_len;
             const int nseg = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
             __syncthreads();
@@ -508,9 +512,19 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
         return;
     }
 
-    for (int si = 0; si < q.seg_per_group; ++si) {
+    // The group's segments from the last to the first: the adjoint that
+    // leaves a segment at its start is the one entering the segment before it
+    // from the right, so only the group's last segment reads it from the
+    // reverse carry.
+    Acc nu[N];
+    {
+        const Acc *gout = static_cast<const Acc *>(q.gout);
+#pragma unroll
+        for (int n = 0; n < N; ++n) nu[n] = gout[((int64_t)grp * N + n) * BD + ch];
+    }
+    for (int si = q.seg_per_group - 1; si >= 0; --si) {
         const int s = grp * q.seg_per_group + si;
-        if (s >= p.S) break;
+        if (s >= p.S) continue;
         const int64_t t0 = (int64_t)s * p.seg_len;
         const int nseg = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
         const int nck = (nseg + kK - 1) / kK;
@@ -532,12 +546,6 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
         }
         __builtin_amdgcn_wave_barrier();
 
-        Acc nu[N];
-        {
-            const Acc *gout = static_cast<const Acc *>(q.gout);
-#pragma unroll
-            for (int n = 0; n < N; ++n) nu[n] = gout[((int64_t)s * N + n) * BD + ch];
-        }
 
         // sub-chunks from the last to the first
         const int nsub = (nseg + kC - 1) / kC;

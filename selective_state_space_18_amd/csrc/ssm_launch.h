@@ -59,7 +59,9 @@ enum class ScanPass { kPrep, kAggregate, kCarry, kOutput };
 //   ragg  : [S][N+1][B*D] Acc -- per segment s >= 1: the adjoint a zero
 //           incoming adjoint leaves at the segment start (times Abar there,
 //           scaled-state units) and the sum of delta
-//   gout  : [S][N][B*D] Acc -- adjoint entering segment s from the right
+//   gout  : [groups][N][B*D] Acc -- adjoint entering the last segment of
+//           each group of segments from the right (the main pass carries it
+//           through the group)
 //           (scaled-state units: dL/dg = dL/dh / (n+1))
 //   part_bc : [2 paths][blocks per row][2 (dB, dC)][B*L*N] Acc -- per block
 //           sums over its channels
