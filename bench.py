@@ -508,6 +508,45 @@ def cpu_baseline(torch, generate, cfg, target_s=10.0, dev="cuda:0"):
                            "sample": f"{n1} channels, all rows and steps, {dt1:.1f} s wall"}}
 
 
+def bench_probe(torch, ss, iters=2048):
+    """Measured issue rates of the VALU and the transcendental unit, from the
+    library's probe kernels (known per-lane instruction mix, 16 independent
+    chains per lane), each launch timed with HIP events on the stream it runs
+    on.  Rates are lane-instructions per second; the derived peak is one
+    wave64 VALU instruction per 4 cycles per SIMD: 256 CUs x 4 SIMDs x 16
+    lanes x 2.4 GHz = 3.93e13 lane-instructions/s (78.6 TFLOP/s counting an
+    FMA as two flops, packed FP32 not used)."""
+    derived = 256 * 4 * 16 * 2.4e9
+    out = {"derived_peak_lane_instr_per_s": derived}
+    st = torch.cuda.current_stream()
+    for kind, blocks in (("fma_f32", 256), ("fma_f32", 1024), ("fma_f32", 4096), ("exp_f32", 4096),
+                         ("fma_exp_f32", 4096), ("fma_f64", 4096)):
+        sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda:0")
+        ss.probe_issue(kind, blocks, 16, sink)  # warm-up
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        ms = []
+        for _ in range(5):
+            a.record(st)
+            valu, trans = ss.probe_issue(kind, blocks, iters, sink)
+            b.record(st)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms.sort()
+        t = ms[len(ms) // 2] * 1e-3
+        lanes = blocks * 256 * iters
+        rec = {"blocks": blocks, "waves_per_simd": blocks * 4 / 1024, "ms": round(t * 1e3, 4),
+               "valu_per_iter": valu, "trans_per_iter": trans,
+               "valu_lane_instr_per_s": lanes * valu / t,
+               "frac_of_derived_peak": round(lanes * valu / t / derived, 4)}
+        if trans:
+            rec["trans_lane_instr_per_s"] = lanes * trans / t
+        out[f"{kind}_b{blocks}"] = rec
+        log(f"[bench] probe {kind} blocks={blocks}: {rec['ms']} ms, {rec['frac_of_derived_peak']} of derived peak")
+        del sink
+    return out
+
+
 def copy_peak(torch, nbytes=1 << 30, reps=10):
     """Device-to-device copy rate (bytes read + bytes written per second) of
     a plain torch copy: the practical HBM ceiling on this GPU, reported beside
@@ -540,7 +579,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
-                                       "complex", "cdecode", "general", "ssd"],
+                                       "complex", "cdecode", "general", "ssd", "probe"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
@@ -566,6 +605,9 @@ def main():
         copy_calibration(torch)
         return
 
+    if a.only == "probe":
+        print(json.dumps(bench_probe(torch, ss)), flush=True)
+        return
     if a.only == "decode":
         rec = bench_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
         print(json.dumps(rec), flush=True)

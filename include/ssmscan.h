@@ -38,13 +38,30 @@
  *   - A pointer may be NULL only when its tensor has no elements.
  *   - Every pointer must be aligned to its element size.
  *   - Supported state sizes: N in {1, 2, 4, 8, 16} (ssm_scan_ssd_fwd: 32, 64, 128).
+ *   - Scans: one time step of x (Dm * element size) must be below 1 GiB, else
+ *     SSM_ERR_BAD_DIM (kernels address a time segment with 32-bit offsets).
  *   - Thread safety: calls may come from several host threads.  Two calls that
  *     run concurrently on different streams of one device use separate
  *     library scratch memory (kept per device and stream).
  *   - Library scratch memory (time-chunk summaries, converted B/C rows) is
  *     allocated on first use per (device, stream), grows on demand, and is
  *     kept until ssm_release_workspaces() or process exit.  Allocation
- *     failure returns SSM_ERR_NOMEM.
+ *     failure returns SSM_ERR_NOMEM.  Calls on one stream share its scratch,
+ *     so they must not run concurrently with each other (stream order
+ *     guarantees that for eager calls).
+ *   - HIP graph capture.  A call made while `stream` is being captured
+ *     records kernels that use the stream's scratch buffer; the graph keeps
+ *     that buffer's address.  Such a call never allocates or synchronises: if
+ *     the stream's scratch is smaller than the call needs it returns
+ *     SSM_ERR_CAPTURE and records nothing (make the same call once, eagerly,
+ *     on the same stream before capturing).  A buffer that was used during a
+ *     capture is never freed when a later eager call grows the stream's
+ *     scratch; it is kept until ssm_release_workspaces(), which therefore
+ *     invalidates every captured graph that calls into the library.  A graph
+ *     replay uses the scratch of the stream it was captured on: do not replay
+ *     it concurrently with other library calls on that stream, or with
+ *     another replay of a graph captured on it.  ssm_step, ssm_step_ex,
+ *     ssm_step_fused and ssm_step_complex use no scratch.
  */
 #ifndef SSMSCAN_H
 #define SSMSCAN_H
@@ -71,7 +88,9 @@ typedef enum {
     SSM_ERR_ALIAS = 6,          /* an output overlaps an input or another output */
     SSM_ERR_NOMEM = 7,          /* library scratch memory could not be allocated */
     SSM_ERR_HIP = 8,            /* the HIP runtime reported an error (see ssm_last_error) */
-    SSM_ERR_BAD_OPTION = 9      /* unknown option id or value, or unknown flag bits */
+    SSM_ERR_BAD_OPTION = 9,     /* unknown option id or value, or unknown flag bits */
+    SSM_ERR_CAPTURE = 10        /* the stream is being captured into a HIP graph and the call
+                                   needs more library scratch than the stream already holds */
 } ssm_status;
 
 /*
@@ -267,9 +286,17 @@ int ssm_scan_ssd_fwd(const void *x, const void *delta, const float *delta_bias,
  *   dB, dC      : [Bsz][L][N] fp32   (sums over channels)
  *   dh_init     : [Bsz][Dm][N] fp32 or NULL
  * No output may overlap an input or another output.  The forward states are
- * recomputed (nothing is saved from the forward call).  Library scratch:
- * about 4 state-sized arrays per 64 steps (for fp32 storage: per 32 steps),
- * plus dB/dC partial sums.
+ * recomputed (nothing is saved from the forward call).  Library scratch
+ * (Acc = 4 bytes for bf16 storage, 8 for fp32; S = ceil(L / segment length),
+ * segments of 32 steps for bf16 and 16 for fp32, G groups and R =
+ * ceil(Dm / 256) blocks per batch row as ssm_scan_bwd_plan reports):
+ *   (3N + 2) * S * Bsz * Dm * Acc      segment summaries and entering states
+ * + 2 * N * G * Bsz * Dm * Acc         adjoint entering each group, dA partials
+ * + 4 * R * Bsz * L * N * Acc          per-block partial sums of dB and dC
+ * + 2 * Bsz * L * N * Acc              converted B/C rows
+ * (smaller terms omitted): about 2.5 GB for Bsz=4, L=16384, Dm=5120, N=16.
+ * A 32-step (fp32: 16-step) segment of x must span less than 1 GiB
+ * (segment length * Dm * element size), else SSM_ERR_BAD_DIM.
  */
 int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias,
                  const float *A, const void *B, const void *C, const float *D,
@@ -382,8 +409,50 @@ int ssm_profile_read(double *total_ms, int64_t *launches, int n);
 int ssm_scan_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
                   int compute_units, int64_t *segments, int64_t *segment_len);
 
-/* Free all library scratch memory (all devices and streams).  The caller must
- * make sure no library work is still running. */
+/*
+ * How ssm_scan_bwd would cut a problem: the number of fixed-length time
+ * segments and their length (32 steps for bf16 storage, 16 for fp32), and how
+ * the main backward pass groups them: each group of `seg_per_group`
+ * consecutive segments is walked by one block, from the last segment to the
+ * first, carrying the adjoint between them in registers; `groups` =
+ * ceil(segments / seg_per_group).  For a device with `compute_units` CUs
+ * (0 = ask the current device).  Returns SSM_OK or an argument error; makes
+ * no device call unless compute_units == 0.
+ */
+int ssm_scan_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
+                      int compute_units, int64_t *segments, int64_t *segment_len,
+                      int64_t *seg_per_group, int64_t *groups);
+
+/*
+ * Issue-rate probes, for calibrating the arithmetic roofline the scan kernels
+ * are measured against (they compute nothing of the scan).  Launches `blocks`
+ * blocks of 256 threads on `stream`; every thread runs `iters` iterations of
+ * a fixed instruction mix in 16 independent dependency chains:
+ *   SSM_PROBE_FMA_F32     : 64 v_fma_f32
+ *   SSM_PROBE_EXP_F32     : 16 v_exp_f32
+ *   SSM_PROBE_FMA_EXP_F32 : 64 v_fma_f32 and 16 v_exp_f32 (independent)
+ *   SSM_PROBE_FMA_F64     : 32 v_fma_f64
+ * *valu_per_iter and *trans_per_iter (either may be NULL) receive the VALU
+ * instructions per iteration (transcendentals included) and the
+ * transcendental ones.  `sink` is a device buffer of blocks * 256 floats that
+ * the kernel may write (it keeps the chains live).  The caller times the
+ * launch.  Returns SSM_OK, SSM_ERR_BAD_DIM (blocks or iters outside [1, 2^24]),
+ * SSM_ERR_NULLPTR, SSM_ERR_BAD_OPTION (unknown kind) or SSM_ERR_HIP.
+ */
+typedef enum {
+    SSM_PROBE_FMA_F32 = 0,
+    SSM_PROBE_EXP_F32 = 1,
+    SSM_PROBE_FMA_EXP_F32 = 2,
+    SSM_PROBE_FMA_F64 = 3
+} ssm_probe_kind;
+
+int ssm_probe_issue(int kind, int64_t blocks, int64_t iters, float *sink, void *stream,
+                    int64_t *valu_per_iter, int64_t *trans_per_iter);
+
+/* Free all library scratch memory (all devices and streams), including
+ * buffers kept for captured HIP graphs: graphs captured with library calls
+ * must not be replayed afterwards.  The caller must make sure no library work
+ * is still running. */
 int ssm_release_workspaces(void);
 
 #ifdef __cplusplus

@@ -206,28 +206,71 @@ int device_cus(int dev, int *cus) {
 // Scratch memory, one growable buffer per (device, stream).  The lock is held
 // for the whole enqueue so that a concurrent growth on the same stream cannot
 // free a buffer that is about to be handed to a kernel.
+//
+// HIP graphs.  A call made while its stream is being captured records kernels
+// that hold the scratch pointer for as long as the graph lives.  So:
+//   * a capturing call never grows the buffer (no synchronise, no allocation):
+//     if the buffer is too small it fails with SSM_ERR_CAPTURE;
+//   * a buffer that was handed out during a capture is never freed when a
+//     later eager call on the stream needs a larger one: it is retired and
+//     kept until ssm_release_workspaces(), so replays keep valid memory.
 
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
+    bool captured = false;  // handed to kernels recorded into a graph
 };
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+std::vector<std::pair<int, void *>> g_ws_retired;  // (device, buffer) a graph may still use
+
+// Whether `s` is being captured.  An implicit capture (the legacy default
+// stream while another stream captures in global mode) counts as capturing.
+int stream_capturing(hipStream_t s, bool *capturing) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e == hipErrorStreamCaptureImplicit) {
+        (void)hipGetLastError();
+        *capturing = true;
+        return SSM_OK;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    *capturing = cs != hipStreamCaptureStatusNone;
+    return SSM_OK;
+}
 
 int workspace(int dev, hipStream_t s, size_t need, void **out) {
+    bool capturing = false;
+    int rc = stream_capturing(s, &capturing);
+    if (rc) return rc;
     Workspace &w = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
     if (w.bytes >= need) {
+        if (capturing) w.captured = true;
         *out = w.ptr;
         return SSM_OK;
     }
+    if (capturing)
+        return fail(SSM_ERR_CAPTURE,
+                    "the stream is being captured and its library scratch (%zu bytes) is smaller than this "
+                    "call needs (%zu bytes); make the same call once on this stream before capturing",
+                    w.bytes, need);
     if (w.ptr != nullptr) {
-        hipError_t e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize before growing scratch");
-        e = hipFree(w.ptr);
+        if (w.captured) {
+            g_ws_retired.push_back({dev, w.ptr});
+        } else {
+            hipError_t e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize before growing scratch");
+            e = hipFree(w.ptr);
+            if (e != hipSuccess) {
+                w.ptr = nullptr;
+                w.bytes = 0;
+                return hip_fail(e, "hipFree(scratch)");
+            }
+        }
         w.ptr = nullptr;
         w.bytes = 0;
-        if (e != hipSuccess) return hip_fail(e, "hipFree(scratch)");
+        w.captured = false;
     }
     const size_t gran = (size_t)2 << 20;
     const size_t bytes = (need + gran - 1) / gran * gran;
@@ -247,12 +290,41 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // ---------------------------------------------------------------------------
 
+// One time step of x, delta or y (Dm * element size) must stay below 1 GiB:
+// the scan kernels address a segment through 32-bit buffer offsets, and the
+// planner needs at least one whole step inside a segment's 1 GiB span.
+constexpr int64_t kMaxStepBytes = int64_t(1) << 30;
+
+int check_step_bytes(int64_t Dm, int64_t es) {
+    if (Dm * es >= kMaxStepBytes)
+        return fail(SSM_ERR_BAD_DIM, "one time step of x (Dm = %lld values) is %lld bytes; the limit is 1 GiB",
+                    (long long)Dm, (long long)(Dm * es));
+    return SSM_OK;
+}
+
 constexpr unsigned kKnownFlags = SSM_DELTA_SOFTPLUS | SSM_EULER_B;
+
+// Scratch of fixed capacity that needs no allocation (the no-allocation entry
+// point): `resolve` gives its address on the current device.
+struct FixedScratch {
+    size_t cap;
+    int (*resolve)(int dev, void **ptr);
+};
+
+// Bytes of scan scratch for S segments: converted B/C rows, segment
+// summaries, entering states, and (packed sequences) restart flags.
+size_t scan_scratch_bytes(int64_t S, int64_t BL, int64_t BD, int64_t N, size_t acc, bool varlen) {
+    const size_t bc = align256((size_t)BL * 2 * N * acc);
+    if (S <= 1) return bc;
+    return bc + align256((size_t)(S - 1) * (N + 1) * BD * acc) + align256((size_t)S * N * BD * acc) +
+           (varlen ? align256((size_t)S * sizeof(int)) : 0);
+}
 
 int scan_impl(const void *x, const void *delta, const float *A, const void *B, const void *C,
               const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
               int64_t Dm, int64_t N, int dtype, void *stream, const int64_t *cu = nullptr,
-              int64_t nseq = 0, const float *delta_bias = nullptr, unsigned flags = 0) {
+              int64_t nseq = 0, const float *delta_bias = nullptr, unsigned flags = 0,
+              const FixedScratch *fixed = nullptr) {
     const bool varlen = cu != nullptr;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
     if (flags & ~kKnownFlags) return fail(SSM_ERR_BAD_OPTION, "unknown flag bits 0x%x", flags & ~kKnownFlags);
@@ -266,6 +338,8 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
         return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
                     (long long)L, (long long)Dm, (long long)N);
     const int64_t es = dtype_size(dtype);
+    int rc;
+    if ((rc = check_step_bytes(Dm, es))) return rc;
     int64_t SDN = BDN;  // elements of h_init / h_final
     if (varlen && !mul_ok(nseq, DN, &SDN)) return fail(SSM_ERR_BAD_DIM, "nseq * Dm * N overflows");
     const Arg in[] = {{x, BLD, es, "x"}, {delta, BLD, es, "delta"}, {A, DN, 4, "A"}, {B, BLN, es, "B"},
@@ -275,7 +349,6 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     const Arg hi = {h_init, h_init ? SDN : 0, 4, "h_init"};
     const Arg ya = {y, BLD, es, "y"};
     const Arg hf = {h_final, h_final ? SDN : 0, 4, "h_final"};
-    int rc;
     if ((rc = check_args(in, nin)) || (rc = check_args(&hi, 1)) || (rc = check_args(&ya, 1)) ||
         (rc = check_args(&hf, 1)))
         return rc;
@@ -288,7 +361,15 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
                                           : "h_init partially overlaps h_final");
 
     if (BD == 0 || (varlen && nseq == 0)) return ok();
+    const size_t acc = ssm::scan_acc_bytes(dtype);
+    if (fixed != nullptr && L > 0 && scan_scratch_bytes(1, BL, BD, N, acc, varlen) > fixed->cap)
+        return fail(SSM_ERR_BAD_DIM,
+                    "the call needs at least %zu bytes of scratch (Bsz * L * 2N converted B/C values); the "
+                    "no-allocation entry point holds %zu",
+                    scan_scratch_bytes(1, BL, BD, N, acc, varlen), fixed->cap);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // Kernel timing events are not created for the no-allocation entry point.
+    auto launch = [&](int kind, auto f) -> hipError_t { return fixed ? f() : timed(kind, s, f); };
 
     ssm::ScanParams p;
     std::memset(&p, 0, sizeof p);
@@ -315,14 +396,14 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     hipError_t e;
     if (varlen) {
         // empty sequences are never visited by the scan kernels
-        e = timed(SSM_K_STATE_INIT, s, [&] { return ssm::launch_varlen_empty(p, (int)N, s); });
+        e = launch(SSM_K_STATE_INIT, [&] { return ssm::launch_varlen_empty(p, (int)N, s); });
         if (e != hipSuccess) return hip_fail(e, "empty-sequence state launch");
         if (L == 0) return ok();
     }
     if (L == 0) {
         p.S = 1;
         if (h_final == nullptr) return ok();
-        e = timed(SSM_K_STATE_INIT, s, [&] { return ssm::launch_state_init(p, (int)N, s); });
+        e = launch(SSM_K_STATE_INIT, [&] { return ssm::launch_state_init(p, (int)N, s); });
         return e == hipSuccess ? ok() : hip_fail(e, "state init launch");
     }
 
@@ -331,21 +412,37 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     int cus = 0;
     if ((rc = device_cus(dev, &cus))) return rc;
-    const Plan pl = make_plan(Bsz, L, Dm, es, cus);
+    Plan pl = make_plan(Bsz, L, Dm, es, cus);
+    if (fixed != nullptr && scan_scratch_bytes(pl.S, BL, BD, N, acc, varlen) > fixed->cap) {
+        // Fewer, longer segments until the summaries fit the fixed scratch
+        // (the scratch grows with S, so the first S that fits is the largest).
+        int64_t S = pl.S;
+        while (S > 1 && scan_scratch_bytes(S, BL, BD, N, acc, varlen) > fixed->cap) --S;
+        pl.seg_len = (L + S - 1) / S;
+        pl.S = (int)((L + pl.seg_len - 1) / pl.seg_len);
+        if (pl.seg_len * Dm * es >= kMaxStepBytes)
+            return fail(SSM_ERR_BAD_DIM,
+                        "with %zu bytes of scratch the scan needs segments of %lld steps, which span 1 GiB of x "
+                        "or more", fixed->cap, (long long)pl.seg_len);
+    }
     p.S = pl.S;
     p.seg_len = pl.seg_len;
     p.tiles_per_b = pl.tiles_per_b;
     p.n_tiles = pl.n_tiles;
 
-    const size_t acc = ssm::scan_acc_bytes(dtype);
     const size_t bc_bytes = align256((size_t)BL * 2 * N * acc);
     const size_t agg_bytes = pl.S > 1 ? align256((size_t)(pl.S - 1) * (N + 1) * BD * acc) : 0;
     const size_t gin_bytes = pl.S > 1 ? align256((size_t)pl.S * N * BD * acc) : 0;
     const size_t flag_bytes = (varlen && pl.S > 1) ? align256((size_t)pl.S * sizeof(int)) : 0;
 
-    std::lock_guard<std::mutex> lk(g_ws_mu);
+    std::unique_lock<std::mutex> lk(g_ws_mu, std::defer_lock);
     void *ws = nullptr;
-    if ((rc = workspace(dev, s, bc_bytes + agg_bytes + gin_bytes + flag_bytes, &ws))) return rc;
+    if (fixed != nullptr) {
+        if ((rc = fixed->resolve(dev, &ws))) return rc;
+    } else {
+        lk.lock();
+        if ((rc = workspace(dev, s, bc_bytes + agg_bytes + gin_bytes + flag_bytes, &ws))) return rc;
+    }
     char *base = static_cast<char *>(ws);
     p.bc = base;
     p.agg = agg_bytes ? base + bc_bytes : nullptr;
@@ -353,16 +450,16 @@ int scan_impl(const void *x, const void *delta, const float *A, const void *B, c
     p.seg_reset = flag_bytes ? reinterpret_cast<int *>(base + bc_bytes + agg_bytes + gin_bytes) : nullptr;
 
     const int n = (int)N;
-    if ((e = timed(SSM_K_BC_PREP, s, [&] { return ssm::launch_bc_prep(p, n, dtype, s); })) != hipSuccess)
+    if ((e = launch(SSM_K_BC_PREP, [&] { return ssm::launch_bc_prep(p, n, dtype, s); })) != hipSuccess)
         return hip_fail(e, "B/C prep launch");
     if (pl.S > 1) {
-        if ((e = timed(SSM_K_SCAN_AGGREGATE, s, [&] { return ssm::launch_scan_aggregate(p, n, dtype, s); })) !=
+        if ((e = launch(SSM_K_SCAN_AGGREGATE, [&] { return ssm::launch_scan_aggregate(p, n, dtype, s); })) !=
             hipSuccess)
             return hip_fail(e, "segment aggregate launch");
-        if ((e = timed(SSM_K_SCAN_CARRY, s, [&] { return ssm::launch_scan_carry(p, n, dtype, s); })) != hipSuccess)
+        if ((e = launch(SSM_K_SCAN_CARRY, [&] { return ssm::launch_scan_carry(p, n, dtype, s); })) != hipSuccess)
             return hip_fail(e, "segment carry launch");
     }
-    if ((e = timed(SSM_K_SCAN_OUTPUT, s, [&] { return ssm::launch_scan_output(p, n, dtype, s); })) != hipSuccess)
+    if ((e = launch(SSM_K_SCAN_OUTPUT, [&] { return ssm::launch_scan_output(p, n, dtype, s); })) != hipSuccess)
         return hip_fail(e, "segment output launch");
     return ok();
 }
@@ -436,13 +533,14 @@ int cplx_impl(const void *x, const void *delta, const float *delta_bias, const f
         return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
                     (long long)L, (long long)Dm, (long long)N);
     const int64_t es = dtype_size(dtype);
+    int rc;
+    if ((rc = check_step_bytes(Dm, es))) return rc;
     const Arg in[] = {{x, BLD, es, "x"},        {delta, BLD, es, "delta"}, {A, 2 * DN, 4, "A"},
                       {B, BLN, es, "B"},        {C, BLN, es, "C"},         {D, Dm, 4, "D"},
                       {delta_bias, delta_bias ? Dm : 0, 4, "delta_bias"}};
     const Arg hi = {h_init, h_init ? 2 * BDN : 0, 4, "h_init"};
     const Arg ya = {y, BLD, es, "y"};
     const Arg hf = {h_final, h_final ? 2 * BDN : 0, 4, "h_final"};
-    int rc;
     if ((rc = check_args(in, 7)) || (rc = check_args(&hi, 1)) || (rc = check_args(&ya, 1)) || (rc = check_args(&hf, 1)))
         return rc;
     if ((rc = check_output(ya, in, 7)) || (rc = check_output(ya, &hi, 1)) || (rc = check_output(hf, in, 7)) ||
@@ -733,6 +831,44 @@ int ssd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     return ok();
 }
 
+// Backward plan.  Segments have a fixed length (bwd_segment_len: 32 steps
+// for bf16 storage, 16 for fp32).  A group's segments run one after another
+// in one block and a CU holds two main-kernel blocks at once, so the main
+// kernel takes about (rounds of resident blocks) x (segments per group): the
+// plan picks the group size G that minimises it (ties: the larger G, fewer
+// partial sums), with at most 256 groups.
+struct BwdPlan {
+    int S;
+    int64_t seg_len;
+    int seg_per_group;
+    int groups;
+    int blocks_per_row;
+};
+
+BwdPlan make_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int dtype, int cus) {
+    BwdPlan bp;
+    bp.seg_len = ssm::bwd_segment_len(dtype);
+    bp.S = L > 0 ? (int)((L + bp.seg_len - 1) / bp.seg_len) : 1;
+    const int64_t tiles_per_b = (Dm + 63) / 64;
+    bp.blocks_per_row = (int)((tiles_per_b + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int64_t rows = Bsz * bp.blocks_per_row;
+    const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+    int64_t G = bp.S;
+    int64_t best = -1;
+    for (int64_t g = bp.S; g >= 1; --g) {
+        const int64_t groups = (bp.S + g - 1) / g;
+        if (groups > 256) break;
+        const int64_t cost = (groups * rows + slots - 1) / slots * g;
+        if (best < 0 || cost < best) {
+            best = cost;
+            G = g;
+        }
+    }
+    bp.seg_per_group = (int)G;
+    bp.groups = (int)((bp.S + G - 1) / G);
+    return bp;
+}
+
 int bwd_impl(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
              const void *C, const float *D, const float *h_init, const void *dy, const float *dh_final, void *dx,
              void *ddelta, float *ddelta_bias, float *dA, float *dB, float *dC, float *dD, float *dh_init,
@@ -749,6 +885,12 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
         return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
                     (long long)L, (long long)Dm, (long long)N);
     const int64_t es = dtype_size(dtype);
+    // The backward addresses a whole fixed-length segment through 32-bit
+    // buffer offsets: its span must stay below 1 GiB.
+    if (ssm::bwd_segment_len(dtype) * Dm * es >= kMaxStepBytes)
+        return fail(SSM_ERR_BAD_DIM, "backward: a %d-step segment of x (Dm = %lld) spans %lld bytes; the limit is 1 GiB",
+                    ssm::bwd_segment_len(dtype), (long long)Dm,
+                    (long long)(ssm::bwd_segment_len(dtype) * Dm * es));
     const Arg in[] = {{x, BLD, es, "x"},
                       {delta, BLD, es, "delta"},
                       {A, DN, 4, "A"},
@@ -835,30 +977,11 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     q.dC = dC;
     q.dD = dD;
     q.dh_init = dh_init;
-    q.blocks_per_row = (p.tiles_per_b + kWavesPerBlock - 1) / kWavesPerBlock;
-    // Segments per wave.  A group's segments run one after another in one
-    // block and a CU holds two main-kernel blocks at once, so the kernel takes
-    // about (rounds of resident blocks) x (segments per group): pick the G
-    // that minimises it (ties: the larger G, fewer partial sums), with at
-    // most 256 groups.
-    const int64_t rows = Bsz * q.blocks_per_row;
-    const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
-    int64_t G = p.S;
-    {
-        int64_t best = -1;
-        for (int64_t g = p.S; g >= 1; --g) {
-            const int64_t groups = (p.S + g - 1) / g;
-            if (groups > 256) break;
-            const int64_t cost = (groups * rows + slots - 1) / slots * g;
-            if (best < 0 || cost < best) {
-                best = cost;
-                G = g;
-            }
-        }
-    }
-    q.seg_per_group = (int)G;
-    q.n_groups = (int)((p.S + G - 1) / G);
-    if ((int64_t)q.n_groups * rows >= ((int64_t)1 << 31) ||
+    const BwdPlan bp = make_bwd_plan(Bsz, L, Dm, dtype, cus);
+    q.blocks_per_row = bp.blocks_per_row;
+    q.seg_per_group = bp.seg_per_group;
+    q.n_groups = bp.groups;
+    if ((int64_t)q.n_groups * Bsz * q.blocks_per_row >= ((int64_t)1 << 31) ||
         (int64_t)((p.n_tiles + kWavesPerBlock - 1) / kWavesPerBlock) * p.S >= ((int64_t)1 << 31))
         return fail(SSM_ERR_BAD_DIM, "backward grid too large (Bsz=%lld, L=%lld, Dm=%lld)", (long long)Bsz,
                     (long long)L, (long long)Dm);
@@ -920,6 +1043,21 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
 }
 
 }  // namespace
+
+namespace ssm {
+
+int scan_fwd_fixed_scratch(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                           const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
+                           int64_t Dm, int64_t N, int dtype, void *stream, size_t cap,
+                           int (*resolve)(int dev, void **ptr)) {
+    const FixedScratch fs = {cap, resolve};
+    return scan_impl(x, delta, A, B, C, D, h_init, y, h_final, Bsz, L, Dm, N, dtype, stream, nullptr, 0, nullptr,
+                     0, &fs);
+}
+
+int set_error(int code, const char *msg) { return fail(code, "%s", msg); }
+
+}  // namespace ssm
 
 extern "C" {
 
@@ -1014,6 +1152,7 @@ const char *ssm_strerror(int code) {
         case SSM_ERR_NOMEM: return "scratch allocation failed";
         case SSM_ERR_HIP: return "HIP runtime error";
         case SSM_ERR_BAD_OPTION: return "unknown option or invalid option value";
+        case SSM_ERR_CAPTURE: return "scratch too small for a call on a capturing stream";
         default: return "unknown status code";
     }
 }
@@ -1077,6 +1216,29 @@ int ssm_scan_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, int 
     return ok();
 }
 
+int ssm_scan_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, int compute_units,
+                      int64_t *segments, int64_t *segment_len, int64_t *seg_per_group, int64_t *groups) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d", dtype);
+    if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld", (long long)N);
+    if (Bsz < 0 || L < 0 || Dm < 0) return fail(SSM_ERR_BAD_DIM, "negative size");
+    if (segments == nullptr || segment_len == nullptr || seg_per_group == nullptr || groups == nullptr)
+        return fail(SSM_ERR_NULLPTR, "output pointer is NULL");
+    int cus = compute_units;
+    if (cus <= 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        int rc = device_cus(dev, &cus);
+        if (rc) return rc;
+    }
+    const BwdPlan bp = make_bwd_plan(Bsz, L, Dm, dtype, cus);
+    *segments = bp.S;
+    *segment_len = bp.seg_len;
+    *seg_per_group = bp.seg_per_group;
+    *groups = bp.groups;
+    return ok();
+}
+
 int ssm_profile_read(double *total_ms, int64_t *launches, int n) {
     std::vector<ProfRec> recs;
     {
@@ -1106,18 +1268,19 @@ int ssm_profile_read(double *total_ms, int64_t *launches, int n) {
 int ssm_release_workspaces(void) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     int rc = SSM_OK;
-    for (auto &kv : g_ws) {
-        if (kv.second.ptr == nullptr) continue;
+    auto release = [&](int dev, void *ptr) {
         int cur = 0;
-        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first.first) == hipSuccess) {
-            hipError_t e = hipFree(kv.second.ptr);
-            if (e != hipSuccess) rc = hip_fail(e, "hipFree(scratch)");
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(dev) == hipSuccess) {
+            hipError_t e = hipFree(ptr);
+            if (e != hipSuccess && rc == SSM_OK) rc = hip_fail(e, "hipFree(scratch)");
             (void)hipSetDevice(cur);
         }
-        kv.second.ptr = nullptr;
-        kv.second.bytes = 0;
-    }
+    };
+    for (auto &kv : g_ws)
+        if (kv.second.ptr != nullptr) release(kv.first.first, kv.second.ptr);
+    for (auto &r : g_ws_retired) release(r.first, r.second);
     g_ws.clear();
+    g_ws_retired.clear();
     return rc == SSM_OK ? ok() : rc;
 }
 

@@ -142,4 +142,17 @@ hipError_t launch_fill(float *dst, int64_t count, float v, hipStream_t s);
 // Channels per thread of the decode-step kernel (1, 2 or 4).
 void set_step_unroll(int u);
 
+// The dense scan with initial state (ssm_scan_fwd_ex's arguments) on scratch
+// of fixed capacity `cap` bytes instead of the per-stream buffer: resolve(dev,
+// &ptr) gives its address on device dev after the arguments are validated.
+// The segment plan is shortened until its scratch fits; calls that do not fit
+// with one segment fail with SSM_ERR_BAD_DIM.  Allocates nothing and creates
+// no timing events.  Returns an ssm_status (abi.cpp).
+int scan_fwd_fixed_scratch(const void *x, const void *delta, const float *A, const void *B, const void *C,
+                           const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz, int64_t L,
+                           int64_t Dm, int64_t N, int dtype, void *stream, size_t cap,
+                           int (*resolve)(int dev, void **ptr));
+// Records `msg` as the calling thread's last error and returns `code`.
+int set_error(int code, const char *msg);
+
 }  // namespace ssm

@@ -28,14 +28,14 @@ KERNEL_KINDS = ("bc_prep", "scan_aggregate", "scan_carry", "scan_output", "step"
                 "ssd_output")
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULLPTR", 2: "SSM_ERR_BAD_DIM", 3: "SSM_ERR_BAD_DTYPE",
           4: "SSM_ERR_UNSUPPORTED_N", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_NOMEM",
-          8: "SSM_ERR_HIP", 9: "SSM_ERR_BAD_OPTION"}
+          8: "SSM_ERR_HIP", 9: "SSM_ERR_BAD_OPTION", 10: "SSM_ERR_CAPTURE"}
 
 # Every symbol include/ssmscan.h declares.
 EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_strerror",
            "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
            "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
            "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd", "ssm_scan_complex_fwd",
-           "ssm_step_complex", "ssm_scan_ssd_fwd")
+           "ssm_step_complex", "ssm_scan_ssd_fwd", "ssm_scan_bwd_plan", "ssm_probe_issue")
 
 
 class SSMError(RuntimeError):
@@ -91,6 +91,10 @@ def lib():
     L.ssm_scan_plan.argtypes = [_i64] * 4 + [ctypes.c_int, ctypes.c_int,
                                              ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
     L.ssm_scan_plan.restype = ctypes.c_int
+    L.ssm_scan_bwd_plan.argtypes = [_i64] * 4 + [ctypes.c_int, ctypes.c_int] + [ctypes.POINTER(_i64)] * 4
+    L.ssm_scan_bwd_plan.restype = ctypes.c_int
+    L.ssm_probe_issue.argtypes = [ctypes.c_int, _i64, _i64, _vp, _vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+    L.ssm_probe_issue.restype = ctypes.c_int
     L.ssm_release_workspaces.argtypes = []
     L.ssm_release_workspaces.restype = ctypes.c_int
     L.ssm_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), ctypes.c_int]
@@ -127,6 +131,28 @@ def plan(Bsz, L, Dm, N, dtype=SSM_BF16, compute_units=0):
     _check(lib().ssm_scan_plan(Bsz, L, Dm, N, dtype, compute_units, ctypes.byref(s), ctypes.byref(sl)),
            "ssm_scan_plan")
     return s.value, sl.value
+
+
+def bwd_plan(Bsz, L, Dm, N, dtype=SSM_BF16, compute_units=0):
+    """(segments, segment_len, seg_per_group, groups) the backward would use."""
+    out = [_i64() for _ in range(4)]
+    _check(lib().ssm_scan_bwd_plan(Bsz, L, Dm, N, dtype, compute_units, *(ctypes.byref(v) for v in out)),
+           "ssm_scan_bwd_plan")
+    return tuple(v.value for v in out)
+
+
+PROBE_KINDS = ("fma_f32", "exp_f32", "fma_exp_f32", "fma_f64")
+
+
+def probe_issue(kind: str, blocks: int, iters: int, sink: torch.Tensor):
+    """Launch an issue-rate probe on the current stream (the caller times it).
+    Returns (VALU instructions per iteration, transcendental ones) per lane."""
+    if sink.device.type != "cuda" or sink.dtype != torch.float32 or sink.numel() < blocks * 256:
+        raise ValueError("sink must be a CUDA float32 tensor of at least blocks * 256 elements")
+    v, t = _i64(), _i64()
+    _check(lib().ssm_probe_issue(PROBE_KINDS.index(kind), blocks, iters, _ptr(sink), _stream(sink.device),
+                                 ctypes.byref(v), ctypes.byref(t)), "ssm_probe_issue")
+    return v.value, t.value
 
 
 def profile_read():

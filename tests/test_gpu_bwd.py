@@ -180,3 +180,62 @@ def test_bwd_blocks_with_both_A_paths(ss, kind):
     got = gpu_bwd(ss, inp, opts)
     torch.cuda.synchronize()
     check(got, oracle_bwd(inp, opts), "bf16")
+
+
+# Plans with more than one segment per group: the main pass carries the
+# adjoint from segment to segment inside a group, and the reverse carry writes
+# only the adjoint entering each group's last segment.  Expected plans on 256
+# CUs: (segments, segments per group).
+MULTI_GROUP = [
+    # dtype, A kind, Bsz, L, Dm, N, options, h_init, dh_final, (S, G)
+    ("bf16", "s4d_real", 4, 16384, 512, 16, "plain", True, True, (512, 8)),
+    ("bf16", "s4d_real", 1, 130000, 72, 16, "softplus_bias", True, True, (4063, 16)),  # last group: 15
+    ("fp32", "s4d_real", 1, 4900, 64, 16, "plain", True, True, (307, 2)),               # last group: 1
+    ("bf16", "lognormal", 1, 33000, 100, 16, "plain", True, True, (1032, 5)),          # general A; last: 2
+    ("bf16", "s4d_real", 1, 33000, 100, 16, "euler", False, True, (1032, 5)),
+]
+
+
+@pytest.mark.parametrize("case", MULTI_GROUP,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}x{c[3]}x{c[4]}-{c[6]}-S{c[9][0]}G{c[9][1]}" for c in MULTI_GROUP])
+def test_bwd_multi_segment_groups(ss, case):
+    dtype, a_kind, Bsz, L, Dm, N, kind, with_h, with_dhf, expect = case
+    S, seg_len, G, groups = ss.bwd_plan(Bsz, L, Dm, N, ss.SSM_F32 if dtype == "fp32" else ss.SSM_BF16)
+    P.say(f"case: bwd multi-group {case[:9]} plan S={S} seg_len={seg_len} G={G} groups={groups}")
+    assert G > 1, "this case must exercise the in-group adjoint carry"
+    assert (S, G) == expect
+    inp = make(dtype, a_kind, Bsz, L, Dm, N, kind, with_h, with_dhf, seed=L + Dm + 7)
+    opts = opts_of(kind, inp)
+    got = gpu_bwd(ss, inp, opts)
+    torch.cuda.synchronize()
+    check(got, oracle_bwd(inp, opts), dtype)
+
+
+def test_bwd_2p8b_layer_plan_sampled_channels(ss):
+    """The Mamba-2.8B-shaped layer in the plan the benchmark times (512
+    segments of 32 steps, 16 per group), with an initial state and dh_final:
+    the per-channel gradients of every 64th channel (and the last) against
+    the oracle run on those channels alone (channels are independent; dB and
+    dC sum over all channels and are covered by the cases above)."""
+    cfg = configs.MAMBA2P8B_LAYER
+    S, seg_len, G, groups = ss.bwd_plan(cfg.Bsz, cfg.L, cfg.Dm, cfg.N)
+    P.say(f"case: bwd {cfg.name} sampled channels, plan S={S} G={G} groups={groups}")
+    assert (S, G) == (512, 16)
+    inp = generate.scan_inputs(cfg, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(cfg.seed + 77)
+    inp["dy"] = torch.randn((cfg.Bsz, cfg.L, cfg.Dm), generator=g, device=DEV).to(torch.bfloat16)
+    inp["h_init"] = torch.randn((cfg.Bsz, cfg.Dm, cfg.N), generator=g, device=DEV) * 0.5
+    inp["dh_final"] = torch.randn((cfg.Bsz, cfg.Dm, cfg.N), generator=g, device=DEV)
+    got = gpu_bwd(ss, inp, {})
+    torch.cuda.synchronize()
+    idx = torch.tensor(list(range(0, cfg.Dm, 64)) + [cfg.Dm - 1], device=DEV)
+    sub = {k: inp[k].index_select(2, idx) for k in ("x", "delta", "dy")}
+    sub.update(A=inp["A"].index_select(0, idx), D=inp["D"].index_select(0, idx), B=inp["B"], C=inp["C"],
+               h_init=inp["h_init"].index_select(1, idx), dh_final=inp["dh_final"].index_select(1, idx))
+    ref = oracle_bwd(sub, {}, want_dBC=False)
+    P.compare(got["dx"].index_select(2, idx), ref["dx"], "bf16", "dx")
+    P.compare(got["ddelta"].index_select(2, idx), ref["ddelta"], "bf16", "ddelta")
+    P.compare(got["dA"].index_select(0, idx), ref["dA"], "bf16", "dA")
+    P.compare(got["dD"].index_select(0, idx), ref["dD"], "bf16", "dD")
+    P.compare(got["dh_init"].index_select(1, idx), ref["dh0"], "bf16", "dh_init")

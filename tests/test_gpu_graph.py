@@ -178,3 +178,69 @@ def test_backward_replays_match_eager(ss):
     names = sorted(k for k, v in eager.items() if v is not None)
     out = {k: torch.empty_like(eager[k]) for k in names}
     _replay_check(lambda: ss.scan_bwd(*args, out=out), [out[k] for k in names], [eager[k] for k in names])
+
+
+def test_captured_scratch_survives_a_larger_eager_call(ss):
+    """A graph keeps the address of the stream's scratch buffer.  A later,
+    larger eager call on the same stream must not free that buffer (it is
+    kept until ssm_release_workspaces), so replays stay correct."""
+    print("case: capture, larger eager call on the capture stream, replay", flush=True)
+    small = configs.ScanConfig("graph_small", 2, 700, 192, 16, "bf16", "s4d_real", "per_token", 1.0, 61)
+    large = configs.ScanConfig("graph_large", 4, 6000, 640, 16, "bf16", "lognormal", "per_token", 1.0, 62)
+    si = generate.scan_inputs(small, DEV)
+    li = generate.scan_inputs(large, DEV)
+    sargs = (si["x"], si["delta"], si["A"], si["B"], si["C"], si["D"])
+    largs = (li["x"], li["delta"], li["A"], li["B"], li["C"], li["D"])
+    y_e, h_e = ss.scan_fwd(*sargs)
+    yl_e, hl_e = ss.scan_fwd(*largs)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    y, hf = torch.empty_like(y_e), torch.empty_like(h_e)
+    yl, hl = torch.empty_like(yl_e), torch.empty_like(hl_e)
+    with torch.cuda.stream(s):
+        ss.scan_fwd(*sargs, y=y, h_final=hf)  # sizes the stream's scratch for the small call only
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ss.scan_fwd(*sargs, y=y, h_final=hf)
+    for k in range(3):
+        with torch.cuda.stream(s):
+            ss.scan_fwd(*largs, y=yl, h_final=hl)  # grows the scratch of stream s (first time)
+            filler = torch.full((16 << 20,), float(k + 1), device=DEV)  # reuses freed memory if any
+        s.synchronize()
+        assert torch.equal(yl, yl_e) and torch.equal(hl, hl_e)
+        y.zero_()
+        hf.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_e), f"replay {k}: y differs"
+        assert torch.equal(hf, h_e), f"replay {k}: h_final differs"
+        del filler
+    del g
+    torch.cuda.synchronize()
+    ss.release_workspaces()
+
+
+def test_capture_with_too_little_scratch_is_refused(ss):
+    """A capturing call never allocates or synchronises: with no scratch yet
+    on the stream it fails with SSM_ERR_CAPTURE and records nothing."""
+    print("case: capture without sized scratch", flush=True)
+    cfg = configs.ScanConfig("graph_unsized", 2, 500, 128, 16, "bf16", "s4d_real", "per_token", 1.0, 63)
+    inp = generate.scan_inputs(cfg, DEV)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"])
+    y_e, h_e = ss.scan_fwd(*args)
+    torch.cuda.synchronize()
+    y, hf = torch.empty_like(y_e), torch.empty_like(h_e)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(ss.SSMError) as err:
+        with torch.cuda.graph(g, stream=s):
+            ss.scan_fwd(*args, y=y, h_final=hf)
+    assert err.value.code == 10  # SSM_ERR_CAPTURE
+    torch.cuda.synchronize()
+    # the stream works normally afterwards
+    with torch.cuda.stream(s):
+        ss.scan_fwd(*args, y=y, h_final=hf)
+    s.synchronize()
+    assert torch.equal(y, y_e) and torch.equal(hf, h_e)
