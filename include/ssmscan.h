@@ -152,6 +152,28 @@ int ssm_scan_fwd_ex(const void *x, const void *delta, const float *A,
                     int dtype, void *stream);
 
 /*
+ * ssm_scan_fwd_ex without allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid it).  Arguments, layouts and results as ssm_scan_fwd_ex.
+ * Instead of the per-stream scratch it uses a fixed 64 MiB device array that
+ * the library holds on every GPU it runs on until the process ends; it calls
+ * no allocator and creates no timing events.  The segment plan is shortened
+ * when the default one needs more than 64 MiB (results then differ from
+ * ssm_scan_fwd_ex by fp32 rounding only).  A call that needs more than
+ * 64 MiB with a single segment -- Bsz * L * 2N converted B/C values (4 bytes
+ * each for bf16 storage, 8 for fp32) -- returns SSM_ERR_BAD_DIM and enqueues
+ * nothing.  Every call on a GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (on different streams, from several host threads, or
+ * graphs replayed concurrently) race and give wrong results.
+ * Nothing in the array needs to start at zero; it keeps the last call's data.
+ */
+int ssm_scan_fwd_noalloc(const void *x, const void *delta, const float *A,
+                         const void *B, const void *C, const float *D,
+                         const float *h_init, void *y, float *h_final,
+                         int64_t Bsz, int64_t L, int64_t Dm, int64_t N,
+                         int dtype, void *stream);
+
+/*
  * Packed variable-length scan (resumable prefill of several sequences at once,
  * without padding).  nseq sequences are concatenated along time in one row:
  * sequence k covers steps cu_seqlens[k] .. cu_seqlens[k+1]-1.

@@ -35,7 +35,8 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_st
            "ssm_last_error", "ssm_version", "ssm_set_option", "ssm_get_option",
            "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
            "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd", "ssm_scan_complex_fwd",
-           "ssm_step_complex", "ssm_scan_ssd_fwd", "ssm_scan_bwd_plan", "ssm_probe_issue")
+           "ssm_step_complex", "ssm_scan_ssd_fwd", "ssm_scan_bwd_plan", "ssm_probe_issue",
+           "ssm_scan_fwd_noalloc")
 
 
 class SSMError(RuntimeError):
@@ -60,6 +61,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     L.ssm_scan_fwd.argtypes = [_vp] * 8 + [_i64] * 4 + [ctypes.c_int, _vp]
     L.ssm_scan_fwd_ex.argtypes = [_vp] * 9 + [_i64] * 4 + [ctypes.c_int, _vp]
+    L.ssm_scan_fwd_noalloc.argtypes = [_vp] * 9 + [_i64] * 4 + [ctypes.c_int, _vp]
     L.ssm_scan_varlen_fwd.argtypes = [_vp] * 7 + [_i64] + [_vp] * 3 + [_i64] * 3 + [ctypes.c_int, _vp]
     L.ssm_scan_varlen_fwd.restype = ctypes.c_int
     L.ssm_scan_fused_fwd.argtypes = [_vp] * 8 + [_i64] + [_vp] * 3 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
@@ -76,7 +78,7 @@ def lib():
     L.ssm_step_fused.restype = ctypes.c_int
     L.ssm_step.argtypes = [_vp] * 8 + [_i64] * 3 + [_vp]
     L.ssm_step_ex.argtypes = [_vp] * 8 + [_i64] * 3 + [ctypes.c_int, _vp]
-    for f in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex"):
+    for f in ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_scan_fwd_noalloc", "ssm_step", "ssm_step_ex"):
         getattr(L, f).restype = ctypes.c_int
     L.ssm_strerror.argtypes = [ctypes.c_int]
     L.ssm_strerror.restype = ctypes.c_char_p
@@ -253,6 +255,39 @@ def scan_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, want_state
                                        _ptr(h_init), _ptr(y), _ptr(h_final), Bsz, L, Dm, N, code,
                                        _stream(dev))
     _check(rc, "ssm_scan_fwd")
+    return y, h_final
+
+
+def scan_fwd_noalloc(x, delta, A, B, C, D, h_init=None, y=None, h_final=None):
+    """ssm_scan_fwd_noalloc: the scan of scan_fwd (no options) on the library's
+    fixed 64 MiB device array instead of allocated scratch.  The C call
+    allocates nothing; pass y and h_final to keep this wrapper from
+    allocating them.  Returns (y, h_final)."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    _need(x, "x", (Bsz, L, Dm), dt, dev)
+    _need(delta, "delta", (Bsz, L, Dm), dt, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(B, "B", (Bsz, L, N), dt, dev)
+    _need(C, "C", (Bsz, L, N), dt, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    if h_init is not None:
+        _need(h_init, "h_init", (Bsz, Dm, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty((Bsz, L, Dm), dtype=dt, device=dev)
+    _need(y, "y", (Bsz, L, Dm), dt, dev)
+    if h_final is None:
+        h_final = torch.empty((Bsz, Dm, N), dtype=torch.float32, device=dev)
+    _need(h_final, "h_final", (Bsz, Dm, N), torch.float32, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_fwd_noalloc(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h_init),
+                                        _ptr(y), _ptr(h_final), Bsz, L, Dm, N, code, _stream(dev))
+    _check(rc, "ssm_scan_fwd_noalloc")
     return y, h_final
 
 

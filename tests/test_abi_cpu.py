@@ -325,3 +325,22 @@ def test_time_step_span_limits(L):
     assert bwd(1 << 24, 1) == 2                                  # 32 steps x 2 B x 2^24 = 1 GiB
     assert "segment" in L.ssm_last_error().decode()
     assert bwd(1 << 24, 0) == 2                                  # 16 steps x 4 B x 2^24 = 1 GiB
+
+
+def test_noalloc_rejects_oversized_calls_without_a_device(L):
+    """ssm_scan_fwd_noalloc's fixed 64 MiB array: a call whose converted B/C
+    rows alone (Bsz * L * 2N fp32 values) exceed it is refused before any
+    device call; argument errors behave as in ssm_scan_fwd_ex."""
+    v = ctypes.c_void_p
+    far = [0x10000000000 * (i + 1) for i in range(9)]  # 1 TiB apart: no overlap
+
+    def call(Bsz, Ls, Dm, N=16, dtype=1, x=far[0]):
+        return L.ssm_scan_fwd_noalloc(v(x), v(far[1]), v(far[2]), v(far[3]), v(far[4]), v(far[5]), v(None),
+                                      v(far[7]), v(far[8]), Bsz, Ls, Dm, N, dtype, None)
+
+    assert call(1, 600000, 64) == 2          # 600000 x 32 x 4 B = 73 MiB of B/C rows
+    assert "no-allocation" in L.ssm_last_error().decode()
+    assert call(1, 300000, 64, dtype=0) == 2  # fp32 storage: 8-byte rows
+    assert call(1, 8, 64, N=3) == 4
+    assert call(1, 8, 64, x=0) == 1
+    assert call(0, 8, 64) == 0                # nothing to do: no device call
