@@ -4,20 +4,27 @@
 A step is one selective-scan forward (B/C prep, segment aggregate, carry and
 output kernels) over the Mamba-2.8B-shaped layer: Bsz=4, L=16384, D=5120,
 N=16, bf16 storage, fp32 arithmetic, synthetic seeded inputs resident in HBM.
-The JSON line reports elements/s (B*L*D*N per second), the achieved
-algorithmic HBM bandwidth, the roofline of the dominant kernel, the fp64 CPU
-oracle timed on a bounded sample of the same workload, and -- under
-"secondary" -- the long-context scan, the scan options (fused delta
-activation, Euler input term), a packed variable-length prefill, the scan
-with complex A, the backward, the general-A path forced on the same layer,
-the scalar-decay (state-space duality) layer and the decode step.  A measured device-copy rate is reported beside the
-8 TB/s specification.
+`value` is elements/s (B*L*D*N per second) over exactly --steps back-to-back
+steps.  The JSON line also reports the achieved algorithmic HBM bandwidth;
+the roofline of the dominant kernel (VALU-issue bound, with the HBM fractions
+of the kernel and of the step, and counter-measured HBM traffic of the kernel
+and of the whole call); the timing protocol (the median of individually
+timed calls after a 512 MiB last-level-cache flush, and of cache-warm
+calls); calibration probes (VALU and transcendental issue rates, streaming
+read / read-modify-write / write HBM rates, empty-launch overhead, a torch
+copy); the fp64 CPU oracle timed on a bounded sample of the same workload;
+and -- under "secondary" -- the long-context scan, the Mamba-130M-shaped
+layer, the scan options (fused delta activation, Euler input term), a packed
+variable-length prefill, the scan with complex A, the backward (structured
+and general A), the general-A path forced on the 2.8B-shaped layer, the
+scalar-decay (state-space duality) layer, and the decode step.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
                     [--no-cpu-baseline] [--no-secondary]
-    python bench.py --only decode      # one workload, for profiler runs
+    python bench.py --only scan        # one workload, for profiler runs
                                        # (scan, long, small, packed, options, backward,
-                                       #  complex, general, ssd, decode)
+                                       #  backward_general, complex, cdecode, general,
+                                       #  ssd, decode, probe, hbmprobe)
     python bench.py --copy-calibration # plain copy of known size (for counters)
 """
 import argparse
@@ -74,16 +81,25 @@ def source_sha(kind):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, kind):
-    """HBM bytes per launch measured with counters, if the kernel is unchanged."""
+def traffic_for(workload, kind):
+    """HBM bytes measured with counters for one call of `workload`, if the
+    kernel sources are unchanged since: (dominant kernel's bytes per launch,
+    bytes of the whole call), else (None, None)."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
-        rec = json.load(f).get(kernel)
+        rec = json.load(f).get(workload)
     if not rec or rec.get("source_sha") != source_sha(kind):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return None, None
+    ks = rec["kernels"]
+    return ks[rec["dominant"]]["hbm_bytes_per_launch"], sum(k["hbm_bytes_per_launch"] for k in ks.values())
+
+
+def traffic_fields(workload, kind, alg):
+    dom, call = traffic_for(workload, kind)
+    return {"traffic": dom, "traffic_call": call,
+            "traffic_call_over_algorithmic": None if call is None else round(call / alg, 3)}
 
 
 def timed_loop(torch, fn, steps, warmup):
@@ -101,27 +117,85 @@ def timed_loop(torch, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
-def bench_scan(torch, ss, generate, cfg, steps, warmup, **opts):
+# Last-level cache (MALL) of MI355X: 256 MB.  Before each individually timed
+# call a 512 MiB buffer is written so that nothing of the previous call stays
+# cached; inputs are rotated over enough copies that back-to-back steps never
+# find the previous step's inputs in that cache either.
+MALL_BYTES = 256 << 20
+FLUSH_BYTES = 512 << 20
+
+
+class Flusher:
+    def __init__(self, torch):
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+
+    def __call__(self, k):
+        self.buf.fill_(float(k & 7))
+
+
+def rotation_count(working_set_bytes):
+    """Input copies so that the rotated working set is at least 4x the MALL."""
+    return max(1, -(-4 * MALL_BYTES // max(1, working_set_bytes)))
+
+
+def event_timed_calls(torch, fn, n, flush=None, start=0):
+    """Median and all times (ms) of n calls, each bracketed by its own HIP
+    events on the current stream (the stream the library launches on);
+    flush(k) runs before call k, outside its events."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for k in range(n):
+        if flush is not None:
+            flush(k)
+        evs[k][0].record(st)
+        fn(start + k)
+        evs[k][1].record(st)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    return t[n // 2], t
+
+
+def protocol_record(torch, fn, fn_fixed, steps, flusher, rotation):
+    """The per-call figures beside the back-to-back rate: the median of
+    individually timed calls after a MALL flush, and the median of calls
+    repeated on one input set without a flush (cache-warm)."""
+    n = max(5, min(steps, 20))
+    fm, _ = event_timed_calls(torch, fn, n, flush=flusher)
+    um, _ = event_timed_calls(torch, fn_fixed, n)
+    return {"input_copies_rotated": rotation, "calls": n, "mall_flush_bytes": FLUSH_BYTES,
+            "flushed_median_ms": round(fm, 5), "unflushed_same_input_median_ms": round(um, 5)}
+
+
+def bench_scan(torch, ss, generate, cfg, steps, warmup, flusher=None, **opts):
     """opts: scan options (delta_bias is taken from the inputs when the
-    workload's delta is the raw projection output)."""
+    workload's delta is the raw projection output).  Returns (ms per
+    back-to-back step over rotated inputs, kernel times, S, segment length,
+    protocol record)."""
     dev = "cuda:0"
     log(f"[bench] generating {cfg.name}")
     inp = generate.scan_inputs(cfg, dev)
     if "delta_bias" in inp:
         opts = dict(opts, delta_bias=inp["delta_bias"], delta_softplus=True)
+    R = rotation_count(generate.alg_bytes_scan(cfg))
+    sets = [inp] + [{k: (v.clone() if k in ("x", "delta", "B", "C") else v) for k, v in inp.items()}
+                    for _ in range(R - 1)]
     y = torch.empty_like(inp["x"])
     hf = torch.empty(cfg.Bsz, cfg.Dm, cfg.N, device=dev, dtype=torch.float32)
 
-    def fn(_i):
-        ss.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], y=y, h_final=hf, **opts)
+    def call(z):
+        ss.scan_fwd(z["x"], z["delta"], z["A"], z["B"], z["C"], z["D"], y=y, h_final=hf, **opts)
+
+    def fn(i):
+        call(sets[i % R])
 
     log(f"[bench] timing {cfg.name} {sorted(k for k, v in opts.items() if v is not None and v is not False)}: "
-        f"{warmup} warmup + {steps} steps")
+        f"{warmup} warmup + {steps} steps over {R} input copies")
     ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    proto = protocol_record(torch, fn, lambda _i: call(inp), steps, flusher, R) if flusher else None
     S, seg = ss.plan(cfg.Bsz, cfg.L, cfg.Dm, cfg.N)
-    del inp, y, hf
+    del inp, sets, y, hf
     torch.cuda.empty_cache()
-    return ms, kern, S, seg
+    return ms, kern, S, seg, proto
 
 
 def bench_unfused_softplus(torch, ss, generate, cfg, steps, warmup):
@@ -164,52 +238,57 @@ def profiled_loop(torch, ss, fn, steps, warmup):
     return ms, kern
 
 
-def bench_options(torch, ss, generate, configs, steps):
+def scan_line(cfg, res, generate, **cfg_extra):
+    ms, kern, S, seg, proto = res
+    roof, hbm, cfgd, kms, proto = scan_record(cfg, ms, kern, S, seg, generate, proto=proto)
+    rec = {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
+           "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms, "config": dict(cfgd, **cfg_extra)}
+    if proto is not None:
+        rec["protocol"] = proto
+    return rec
+
+
+def bench_options(torch, ss, generate, configs, steps, flusher=None):
     """The Mamba-2.8B-shaped layer with the scan options: delta's activation
     fused (softplus(delta + bias) inside the kernels), and the Euler input
     term, against the separate-activation route."""
     out = {}
     fc = configs.FUSED_2P8B_LAYER
-    ms, kern, S, seg = bench_scan(torch, ss, generate, fc, steps, 2)
-    roof, hbm, cfgd, kms = scan_record(fc, ms, kern, S, seg, generate)
-    out["fused_softplus"] = {"workload": fc.name, "ms_per_step": round(ms, 5), "value": fc.elems() / (ms * 1e-3),
-                             "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
-                             "config": dict(cfgd, delta="softplus(raw + bias) in the kernels")}
+    out["fused_softplus"] = scan_line(fc, bench_scan(torch, ss, generate, fc, steps, 2, flusher),
+                                      generate, delta="softplus(raw + bias) in the kernels")
     ums = bench_unfused_softplus(torch, ss, generate, fc, steps, 2)
     out["separate_softplus_pass"] = {"ms_per_step": round(ums, 5), "value": fc.elems() / (ums * 1e-3),
                                      "note": "torch softplus pass over delta, then the plain scan"}
     ec = configs.MAMBA2P8B_LAYER
-    ms, kern, S, seg = bench_scan(torch, ss, generate, ec, steps, 2, euler_b=True)
-    roof, hbm, cfgd, kms = scan_record(ec, ms, kern, S, seg, generate)
-    out["euler_b"] = {"workload": ec.name, "ms_per_step": round(ms, 5), "value": ec.elems() / (ms * 1e-3),
-                      "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
-                      "config": dict(cfgd, input_term="Euler: delta * B")}
+    out["euler_b"] = scan_line(ec, bench_scan(torch, ss, generate, ec, steps, 2, flusher, euler_b=True),
+                               generate, input_term="Euler: delta * B")
     return out
 
 
-def bench_general_path(torch, ss, generate, cfg, steps):
+def bench_general_path(torch, ss, generate, cfg, steps, flusher=None):
     """The same layer with the structured-A fast path switched off, so every
     state element takes its own exponential (the path a layer with arbitrary
     real A runs)."""
     ss.set_option(ss.SSM_OPT_FORCE_GENERAL, 1)
     try:
-        ms, kern, S, seg = bench_scan(torch, ss, generate, cfg, steps, 2)
+        res = bench_scan(torch, ss, generate, cfg, steps, 2, flusher)
     finally:
         ss.set_option(ss.SSM_OPT_FORCE_GENERAL, 0)
-    roof, hbm, cfgd, kms = scan_record(cfg, ms, kern, S, seg, generate)
-    roof["kernel"] = "scan_segment_kernel (output pass, general A)"
-    roof["traffic"] = None  # the counter figures are the structured kernel's
-    return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
-            "unit": "elems/s", "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms,
-            "config": dict(cfgd, A="general path forced (one exp per state element)")}
+    rec = scan_line(cfg, res, generate, A="general path forced (one exp per state element)")
+    rec["roofline"]["kernel"] = "scan_segment_kernel (output pass, general A)"
+    # the counter figures are the structured kernels'
+    rec["roofline"].update(traffic=None, traffic_call=None, traffic_call_over_algorithmic=None)
+    return rec
 
 
-def bench_ssd(torch, ss, generate, cfg, steps, warmup):
+def bench_ssd(torch, ss, generate, cfg, steps, warmup, flusher=None):
     """The scalar-decay layer (heads of 64 channels sharing A and delta, N =
-    128) in its chunked matrix form.  Algorithmic flops of the output pass per
-    (b, t, d): 2N for C H, 2N for the state update B^T (w x), Q + 1 for the
-    causal intra-chunk product (Q = 64 steps; the lower triangle of a Q x Q
-    matrix times x), plus (Q + 1) N / Dm for the shared G = C B^T."""
+    128) in its chunked matrix form.  Its binding roof is HBM: the layer's
+    algorithmic bytes take longer at 8 TB/s than its algorithmic flops at the
+    bf16 matrix-core peak.  Algorithmic flops of the output pass per (b, t, d):
+    2N for C H, 2N for the state update B^T (w x), Q + 1 for the causal
+    intra-chunk product (Q = 64 steps; the lower triangle of a Q x Q matrix
+    times x), plus (Q + 1) N / Dm for the shared G = C B^T."""
     dev = "cuda:0"
     log(f"[bench] generating {cfg.name}")
     inp = generate.ssd_inputs(cfg, dev)
@@ -221,6 +300,7 @@ def bench_ssd(torch, ss, generate, cfg, steps, warmup):
 
     log(f"[bench] timing {cfg.name}: {warmup} warmup + {steps} steps")
     ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    proto = protocol_record(torch, fn, fn, steps, flusher, 1) if flusher else None
     del inp, y, hf
     torch.cuda.empty_cache()
     Q = 64
@@ -229,24 +309,42 @@ def bench_ssd(torch, ss, generate, cfg, steps, warmup):
     out_ms = kern["ssd_output"]["avg_ms"]
     alg = generate.alg_bytes_ssd(cfg)
     mfma = flops_out / (out_ms * 1e-3) / 1e12
-    return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
-            "unit": "elems/s",
-            "hbm": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
-            "roofline": {"kernel": "ssd_chunk_kernel (output pass)", "bound": "mfma",
-                         "achieved": round(mfma, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(mfma / BF16_MFMA_PEAK_TFLOPS, 4), "avg_ms": round(out_ms, 5),
-                         "traffic": traffic_for("ssd_output_" + cfg.name, "ssd"),
-                         "algorithmic_flops_per_launch": flops_out,
-                         "hbm_frac_at_algorithmic_bytes": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-            "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
-            "config": {"workload": cfg.name, "Bsz": cfg.Bsz, "L": cfg.L, "Dm": cfg.Dm, "N": cfg.N,
-                       "head_dim": cfg.head_dim, "storage": cfg.dtype,
-                       "A": "one real scalar per head, -exp(N(0, 0.5))", "delta": "per head, " + cfg.delta_kind,
-                       "input_term": "ZOH"}}
+    gbs = alg / (out_ms * 1e-3) / 1e9
+    roof = {"kernel": "ssd_chunk_kernel (output pass)", "bound": "hbm",
+            "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBPS, 4), "avg_ms": round(out_ms, 5),
+            "algorithmic_bytes_per_call": alg,
+            "hbm_frac_step": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "floor_ms_hbm": round(alg / HBM_PEAK_GBPS / 1e9 * 1e3, 4),
+            "floor_ms_mfma": round(flops_out / BF16_MFMA_PEAK_TFLOPS / 1e12 * 1e3, 4),
+            "mfma_tflops": round(mfma, 2), "mfma_frac": round(mfma / BF16_MFMA_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_launch": flops_out}
+    roof.update(traffic_fields(cfg.name, "ssd", alg))
+    rec = {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
+           "unit": "elems/s",
+           "hbm": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                   "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
+           "roofline": roof,
+           "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
+           "config": {"workload": cfg.name, "Bsz": cfg.Bsz, "L": cfg.L, "Dm": cfg.Dm, "N": cfg.N,
+                      "head_dim": cfg.head_dim, "storage": cfg.dtype,
+                      "A": "one real scalar per head, -exp(N(0, 0.5))", "delta": "per head, " + cfg.delta_kind,
+                      "input_term": "ZOH"}}
+    if proto is not None:
+        rec["protocol"] = proto
+    return rec
 
 
-def bench_backward(torch, ss, generate, cfg, steps, warmup):
+def alg_bytes_bwd(cfg):
+    """Backward, inputs read once and outputs written once: x, delta, dy, B,
+    C, A, D, dh_final read; dx, ddelta (storage type), dB, dC (fp32), dA, dD,
+    dh_init written."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    BLD, BLN, DN, BDN = cfg.Bsz * cfg.L * cfg.Dm, cfg.Bsz * cfg.L * cfg.N, cfg.Dm * cfg.N, cfg.Bsz * cfg.Dm * cfg.N
+    return 5 * BLD * s + 2 * BLN * s + 2 * BLN * 4 + 2 * DN * 4 + 2 * cfg.Dm * 4 + 2 * BDN * 4
+
+
+def bench_backward(torch, ss, generate, cfg, steps, warmup, flusher=None):
     """Backward of the scan over the layer: every input gradient for a random
     dy (and dh_final), forward states recomputed inside the call."""
     dev = "cuda:0"
@@ -265,21 +363,33 @@ def bench_backward(torch, ss, generate, cfg, steps, warmup):
 
     log(f"[bench] timing {cfg.name} backward: {warmup} warmup + {steps} steps")
     ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    proto = protocol_record(torch, fn, fn, steps, flusher, 1) if flusher else None
+    plan = ss.bwd_plan(cfg.Bsz, cfg.L, cfg.Dm, cfg.N)
     del inp, dy, dhf, out
     torch.cuda.empty_cache()
     elems = cfg.elems()
     main_ms = kern["bwd_main"]["avg_ms"]
+    alg = alg_bytes_bwd(cfg)
     achieved = elems * BWD_FLOPS_PER_ELEM / (main_ms * 1e-3) / 1e12
-    return {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": elems / (ms * 1e-3), "unit": "elems/s",
-            "roofline": {"kernel": "bwd_main_kernel", "bound": "alu", "achieved": round(achieved, 3),
-                         "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
-                         "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
-                         "avg_ms": round(main_ms, 5), "algorithmic_flops_per_launch": elems * BWD_FLOPS_PER_ELEM},
-            "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
-            "main_kernel_elems_per_s": elems / (main_ms * 1e-3)}
+    roof = {"kernel": "bwd_main_kernel", "bound": "alu", "achieved": round(achieved, 3),
+            "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+            "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
+            "avg_ms": round(main_ms, 5), "algorithmic_flops_per_launch": elems * BWD_FLOPS_PER_ELEM,
+            "algorithmic_bytes_per_call": alg,
+            "hbm_frac_kernel": round(alg / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "hbm_frac_step": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    roof.update(traffic_fields("backward_" + cfg.name, "bwd", alg))
+    rec = {"workload": cfg.name, "ms_per_step": round(ms, 5), "value": elems / (ms * 1e-3), "unit": "elems/s",
+           "roofline": roof, "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
+           "main_kernel_elems_per_s": elems / (main_ms * 1e-3),
+           "config": {"workload": cfg.name, "A": cfg.a_kind, "segments": plan[0], "segment_len": plan[1],
+                      "segments_per_group": plan[2], "groups": plan[3]}}
+    if proto is not None:
+        rec["protocol"] = proto
+    return rec
 
 
-def bench_complex(torch, ss, generate, cfg, steps, warmup):
+def bench_complex(torch, ss, generate, cfg, steps, warmup, flusher=None):
     """The layer with complex diagonal A (decaying oscillators): one exp and
     one sin/cos pair per state element; no structured fast path."""
     dev = "cuda:0"
@@ -294,21 +404,29 @@ def bench_complex(torch, ss, generate, cfg, steps, warmup):
 
     log(f"[bench] timing {cfg.name} complex: {warmup} warmup + {steps} steps")
     ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    proto = protocol_record(torch, fn, fn, steps, flusher, 1) if flusher else None
     del inp, A, y, hf
     torch.cuda.empty_cache()
     out_ms = kern["scan_output"]["avg_ms"]
     achieved = cfg.elems() * CPLX_FLOPS_PER_ELEM / (out_ms * 1e-3) / 1e12
-    return {"workload": cfg.name + "_complex_A", "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
-            "unit": "elems/s",
-            "roofline": {"kernel": "cplx_segment_kernel (output pass)", "bound": "alu", "achieved": round(achieved, 3),
-                         "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
-                         "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
-                         "avg_ms": round(out_ms, 5), "algorithmic_flops_per_launch": cfg.elems() * CPLX_FLOPS_PER_ELEM,
-                         "note": "exp, sin and cos count one flop each and issue at a quarter of the VALU rate"},
-            "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()}}
+    alg = generate.alg_bytes_scan(cfg) + cfg.Dm * cfg.N * 4 + cfg.Bsz * cfg.Dm * cfg.N * 4  # complex A, h_final
+    rec = {"workload": cfg.name + "_complex_A", "ms_per_step": round(ms, 5), "value": cfg.elems() / (ms * 1e-3),
+           "unit": "elems/s",
+           "roofline": {"kernel": "cplx_segment_kernel (output pass)", "bound": "alu",
+                        "achieved": round(achieved, 3), "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+                        "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
+                        "avg_ms": round(out_ms, 5),
+                        "algorithmic_flops_per_launch": cfg.elems() * CPLX_FLOPS_PER_ELEM,
+                        "hbm_frac_kernel": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "hbm_frac_step": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "note": "exp, sin and cos count one flop each; each takes two VALU issue slots"},
+           "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()}}
+    if proto is not None:
+        rec["protocol"] = proto
+    return rec
 
 
-def bench_packed(torch, ss, generate, cfg, steps, warmup):
+def bench_packed(torch, ss, generate, cfg, steps, warmup, flusher=None):
     """Packed variable-length prefill: one row of cfg.L steps holding a few
     dozen sequences, each restarting from its own initial state."""
     dev = "cuda:0"
@@ -324,6 +442,7 @@ def bench_packed(torch, ss, generate, cfg, steps, warmup):
 
     log(f"[bench] timing {cfg.name}: {warmup} warmup + {steps} steps")
     ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    proto = protocol_record(torch, fn, fn, steps, flusher, 1) if flusher else None
     S, seg = ss.plan(1, cfg.L, cfg.Dm, cfg.N)
     lens = (inp["cu"][1:] - inp["cu"][:-1]).tolist()
     del inp, y, hf
@@ -332,23 +451,34 @@ def bench_packed(torch, ss, generate, cfg, steps, warmup):
     alg = generate.alg_bytes_varlen(cfg.L, cfg.Dm, cfg.N, nseq, cfg.dtype, cfg.h0_std > 0)
     out_ms = kern["scan_output"]["avg_ms"]
     achieved = elems * SCAN_FLOPS_PER_ELEM / (out_ms * 1e-3) / 1e12
-    return {
+    roof = {"kernel": "scan_segment_kernel (output pass, packed)", "bound": "alu",
+            "achieved": round(achieved, 3), "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+            "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "avg_ms": round(out_ms, 5),
+            "hbm_frac_kernel": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "hbm_frac_step": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    roof.update(traffic_fields(cfg.name, "scan", alg))
+    rec = {
         "workload": cfg.name, "ms_per_step": round(ms, 5), "value": elems / (ms * 1e-3), "unit": "elems/s",
         "config": {"workload": cfg.name, "L": cfg.L, "Dm": cfg.Dm, "N": cfg.N, "storage": cfg.dtype,
                    "A": cfg.a_kind, "sequences": nseq, "empty_sequences": lens.count(0),
                    "longest": max(lens), "segments": S, "segment_len": seg, "h_init": cfg.h0_std > 0},
         "hbm": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
-        "roofline": {"kernel": "scan_segment_kernel (output pass, packed)", "bound": "alu",
-                     "achieved": round(achieved, 3), "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
-                     "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
-                     "traffic": traffic_for("scan_output_" + cfg.name, "scan"),
-                     "avg_ms": round(out_ms, 5)},
+        "roofline": roof,
         "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
     }
+    if proto is not None:
+        rec["protocol"] = proto
+    return rec
 
 
-def scan_record(cfg, ms, kern, S, seg, generate):
+def scan_record(cfg, ms, kern, S, seg, generate, kind="scan", proto=None):
+    """Roofline of the dominant kernel (the output pass) and the step.  The
+    binding roof is VALU issue: 'achieved' counts SCAN_FLOPS_PER_ELEM
+    algorithmic flops per state element against the derived non-packed fp32
+    peak (calibrated by the probe kernels).  The HBM fractions are the
+    algorithmic bytes of the whole call over the output pass's time and over
+    the whole step's time, against 8 TB/s."""
     elems = cfg.elems()
     alg = generate.alg_bytes_scan(cfg)
     out_ms = kern["scan_output"]["avg_ms"]
@@ -360,20 +490,25 @@ def scan_record(cfg, ms, kern, S, seg, generate):
         "peak": round(VALU_FP32_PEAK_TFLOPS, 2),
         "unit": "TFLOP/s",
         "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
-        "traffic": traffic_for("scan_output_" + cfg.name, "scan"),
         "avg_ms": round(out_ms, 5),
         "algorithmic_flops_per_launch": elems * SCAN_FLOPS_PER_ELEM,
-        "hbm_frac_at_algorithmic_bytes": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_call": alg,
+        "hbm_frac_kernel": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "hbm_frac_step": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
     }
+    roof.update(traffic_fields(cfg.name, kind, alg))
     hbm = {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
            "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg}
     cfgd = {"workload": cfg.name, "Bsz": cfg.Bsz, "L": cfg.L, "Dm": cfg.Dm, "N": cfg.N,
             "storage": cfg.dtype, "A": cfg.a_kind, "delta": cfg.delta_kind,
             "segments": S, "segment_len": seg}
-    return roof, hbm, cfgd, {k: round(v["avg_ms"], 5) for k, v in kern.items()}
+    kms = {k: round(v["avg_ms"], 5) for k, v in kern.items()}
+    if proto is not None:
+        proto = dict(proto, flushed_median_elems_per_s=elems / (proto["flushed_median_ms"] * 1e-3))
+    return roof, hbm, cfgd, kms, proto
 
 
-def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
+def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4, flusher=None, launch_us=None):
     """n_tokens consecutive steps; the resident state cycles over `layers`
     independent layer states so the working set (layers x 134 MB) exceeds the
     256 MB last-level cache, as in a multi-layer model."""
@@ -392,6 +527,13 @@ def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
     ms, kern = profiled_loop(torch, ss, fn, n_tokens, 16)
     k_ms = kern["step"]["avg_ms"]
     alg = generate.alg_bytes_step(cfg)
+    proto = None
+    if flusher is not None:
+        fm, _ = event_timed_calls(torch, fn, 50, flush=flusher)
+        um, _ = event_timed_calls(torch, lambda _i: fn(0), 50)
+        proto = {"layer_states_cycled": layers, "calls": 50, "mall_flush_bytes": FLUSH_BYTES,
+                 "flushed_median_ms": round(fm, 5), "unflushed_same_state_median_ms": round(um, 5),
+                 "flushed_median_hbm_frac": round(alg / (fm * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     # The same steps replayed from a captured HIP graph (a decode loop of a
     # serving engine): removes the host launch gap between steps.
     graph_ms = None
@@ -426,14 +568,16 @@ def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4):
         "value": cfg.elems_per_step() / (ms * 1e-3), "unit": "elems/s",
         "hbm": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
-        "roofline": {"kernel": "step_kernel", "bound": "hbm",
-                     "achieved": round(alg / (k_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic_for("step_" + cfg.name, "step"),
-                     "avg_ms": round(k_ms, 5)},
+        "roofline": dict({"kernel": "step_kernel", "bound": "hbm",
+                          "achieved": round(alg / (k_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                          "avg_ms": round(k_ms, 5), "algorithmic_bytes_per_launch": alg},
+                         **traffic_fields(cfg.name, "step", alg)),
         "state_layers_cycled": layers,
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "graph_value": None if graph_ms is None else cfg.elems_per_step() / (graph_ms * 1e-3),
+        "protocol": proto,
+        "launch_overhead_us": launch_us,
     }
 
 
@@ -547,6 +691,32 @@ def bench_probe(torch, ss, iters=2048):
     return out
 
 
+def hbm_probes(torch, ss, nbytes=2 << 30, reps=5):
+    """Streaming read, in-place read-modify-write and write rates over a
+    2 GiB buffer (8x the last-level cache), median of `reps` event-timed
+    calls: the practical HBM ceiling beside the 8 TB/s specification."""
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    out = {}
+    for kind in ("read", "rmw", "write"):
+        moved = ss.probe_hbm(kind, buf)  # warm-up
+        med, _ = event_timed_calls(torch, lambda _i: ss.probe_hbm(kind, buf), reps)
+        out[kind] = {"GB/s": round(moved / (med * 1e-3) / 1e9, 1), "bytes": moved, "ms": round(med, 4)}
+        log(f"[bench] hbm probe {kind}: {out[kind]['GB/s']} GB/s")
+    del buf
+    torch.cuda.empty_cache()
+    out["practical_peak_gbps"] = max(v["GB/s"] for v in out.values() if isinstance(v, dict))
+    return out
+
+
+def launch_overhead_us(torch, ss, n=200):
+    """Time per launch of an empty one-block kernel, back to back on one
+    stream (what a step pays before any work)."""
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda:0")
+    ss.probe_issue("empty", 1, 1, sink)
+    ms = timed_loop(torch, lambda _i: ss.probe_issue("empty", 1, 1, sink), n, 10)
+    return round(ms * 1e3, 3)
+
+
 def copy_peak(torch, nbytes=1 << 30, reps=10):
     """Device-to-device copy rate (bytes read + bytes written per second) of
     a plain torch copy: the practical HBM ceiling on this GPU, reported beside
@@ -579,7 +749,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
-                                       "complex", "cdecode", "general", "ssd", "probe"],
+                                       "backward_general", "complex", "cdecode", "general", "ssd", "probe",
+                                       "hbmprobe"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
@@ -608,6 +779,9 @@ def main():
     if a.only == "probe":
         print(json.dumps(bench_probe(torch, ss)), flush=True)
         return
+    if a.only == "hbmprobe":
+        print(json.dumps(hbm_probes(torch, ss)), flush=True)
+        return
     if a.only == "decode":
         rec = bench_decode(torch, ss, generate, configs.DECODE_256x8192, a.steps)
         print(json.dumps(rec), flush=True)
@@ -632,6 +806,10 @@ def main():
         rec = bench_backward(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps, a.warmup)
         print(json.dumps(rec), flush=True)
         return
+    if a.only == "backward_general":
+        rec = bench_backward(torch, ss, generate, configs.MAMBA130M_LAYER, a.steps, a.warmup)
+        print(json.dumps(rec), flush=True)
+        return
     if a.only == "options":
         print(json.dumps(bench_options(torch, ss, generate, configs, a.steps)), flush=True)
         return
@@ -639,24 +817,17 @@ def main():
         rec = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER, a.steps, a.warmup)
         print(json.dumps(rec), flush=True)
         return
-    if a.only == "long":
-        cfg = configs.LONG_CONTEXT_1M
-        ms, kern, S, seg = bench_scan(torch, ss, generate, cfg, a.steps, a.warmup)
-        roof, hbm, cfgd, kms = scan_record(cfg, ms, kern, S, seg, generate)
-        print(json.dumps({"workload": cfg.name, "ms_per_step": ms, "value": cfg.elems() / (ms * 1e-3),
-                          "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms}), flush=True)
-        return
-    if a.only == "small":
-        cfg = configs.MAMBA130M_LAYER
-        ms, kern, S, seg = bench_scan(torch, ss, generate, cfg, a.steps, a.warmup)
-        roof, hbm, cfgd, kms = scan_record(cfg, ms, kern, S, seg, generate)
-        print(json.dumps({"workload": cfg.name, "ms_per_step": ms, "value": cfg.elems() / (ms * 1e-3),
-                          "hbm": hbm, "roofline": roof, "kernels_avg_ms": kms}), flush=True)
+    if a.only in ("long", "small", "scan"):
+        cfg = {"long": configs.LONG_CONTEXT_1M, "small": configs.MAMBA130M_LAYER,
+               "scan": configs.MAMBA2P8B_LAYER}[a.only]
+        print(json.dumps(scan_line(cfg, bench_scan(torch, ss, generate, cfg, a.steps, a.warmup), generate)),
+              flush=True)
         return
 
+    flusher = Flusher(torch)
     cfg = configs.MAMBA2P8B_LAYER
-    ms, kern, S, seg = bench_scan(torch, ss, generate, cfg, a.steps, a.warmup)
-    roof, hbm, cfgd, kms = scan_record(cfg, ms, kern, S, seg, generate)
+    ms, kern, S, seg, proto = bench_scan(torch, ss, generate, cfg, a.steps, a.warmup, flusher)
+    roof, hbm, cfgd, kms, proto = scan_record(cfg, ms, kern, S, seg, generate, proto=proto)
     out = {
         "metric": METRIC,
         "value": cfg.elems() / (ms * 1e-3),
@@ -674,39 +845,45 @@ def main():
         "hbm": hbm,
         "roofline": roof,
         "kernels_avg_ms": kms,
+        "protocol": proto,
     }
     if a.only is None and not a.no_secondary:
+        cal = {"valu": bench_probe(torch, ss), "hbm": hbm_probes(torch, ss),
+               "launch_overhead_us": launch_overhead_us(torch, ss), "copy": copy_peak(torch)}
+        out["calibration"] = cal
+        fma = cal["valu"]["fma_f32_b4096"]["frac_of_derived_peak"]
+        out["roofline"]["peak_measured_frac"] = fma
+        out["roofline"]["frac_of_measured_peak"] = round(out["roofline"]["frac"] / fma, 4)
+        practical = cal["hbm"]["practical_peak_gbps"]
+        out["hbm"]["practical_peak_gbps"] = practical
+        out["hbm"]["frac_of_practical_peak"] = round(out["hbm"]["achieved"] / practical, 4)
+        steps5 = max(5, a.steps // 5)
         sec = {}
         lc = configs.LONG_CONTEXT_1M
-        lms, lk, lS, lseg = bench_scan(torch, ss, generate, lc, max(3, a.steps // 5), 2)
-        lroof, lhbm, lcfg, lkms = scan_record(lc, lms, lk, lS, lseg, generate)
-        sec["long_context"] = {"workload": lc.name, "ms_per_step": round(lms, 5),
-                               "value": lc.elems() / (lms * 1e-3), "unit": "elems/s", "hbm": lhbm,
-                               "roofline": lroof, "config": lcfg, "kernels_avg_ms": lkms}
+        sec["long_context"] = scan_line(lc, bench_scan(torch, ss, generate, lc, max(3, a.steps // 5), 2, flusher),
+                                        generate)
         sm = configs.MAMBA130M_LAYER
-        sms, sk, sS, sseg = bench_scan(torch, ss, generate, sm, a.steps, a.warmup)
-        sroof, shbm, scfg, skms = scan_record(sm, sms, sk, sS, sseg, generate)
-        sec["mamba130m_layer"] = {
-            "workload": sm.name, "ms_per_step": round(sms, 5), "value": sm.elems() / (sms * 1e-3),
-            "unit": "elems/s", "hbm": shbm, "roofline": sroof, "config": scfg, "kernels_avg_ms": skms,
-            "note": "random A: every state element takes its own exp (general path); the 153 MB working "
-                    "set stays in the 256 MB last-level cache between calls"}
-        sec["fused_softplus"] = bench_options(torch, ss, generate, configs, max(5, a.steps // 5))
-        sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER,
-                                             max(5, a.steps // 5), 2)
-        sec["complex_A"] = bench_complex(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
-        sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), 1)
-        sec["general_A_path"] = bench_general_path(torch, ss, generate, cfg, max(5, a.steps // 5))
-        sec["ssd_layer"] = bench_ssd(torch, ss, generate, configs.SSD_LAYER, max(5, a.steps // 5), 2)
+        sec["mamba130m_layer"] = scan_line(sm, bench_scan(torch, ss, generate, sm, a.steps, a.warmup, flusher),
+                                           generate)
+        sec["mamba130m_layer"]["note"] = (
+            "random A: every state element takes its own exp (general path); ms_per_step rotates over input "
+            "copies whose total exceeds the 256 MB last-level cache, protocol gives the flushed and the "
+            "cache-warm (same input, no flush) per-call medians")
+        sec["fused_softplus"] = bench_options(torch, ss, generate, configs, steps5, flusher)
+        sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER, steps5, 2, flusher)
+        sec["complex_A"] = bench_complex(torch, ss, generate, cfg, max(3, a.steps // 10), 1, flusher)
+        sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), 1, flusher)
+        sec["backward_general_A"] = bench_backward(torch, ss, generate, configs.MAMBA130M_LAYER, steps5, 2,
+                                                   flusher)
+        sec["general_A_path"] = bench_general_path(torch, ss, generate, cfg, steps5, flusher)
+        sec["ssd_layer"] = bench_ssd(torch, ss, generate, configs.SSD_LAYER, steps5, 2, flusher)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
-                                     configs.DECODE_256x8192.n_tokens)
+                                     configs.DECODE_256x8192.n_tokens, flusher=flusher,
+                                     launch_us=cal["launch_overhead_us"])
         sec["complex_decode"] = bench_complex_decode(torch, ss, generate, configs.DECODE_256x8192,
                                                      configs.DECODE_256x8192.n_tokens)
-        cp = copy_peak(torch)
-        out["copy_peak"] = cp
-        out["hbm"]["frac_of_copy_peak"] = round(out["hbm"]["achieved"] / cp["achieved"], 4)
-        dec = sec["decode"]
-        dec["roofline"]["frac_of_copy_peak"] = round(dec["roofline"]["achieved"] / cp["achieved"], 4)
+        for rec in (sec["decode"], sec["complex_decode"], sec["ssd_layer"]):
+            rec["roofline"]["frac_of_practical_peak"] = round(rec["roofline"]["achieved"] / practical, 4)
         out["secondary"] = sec
     if a.only is None and not a.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample")

@@ -454,6 +454,7 @@ int ssm_scan_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
  *   SSM_PROBE_EXP_F32     : 16 v_exp_f32
  *   SSM_PROBE_FMA_EXP_F32 : 64 v_fma_f32 and 16 v_exp_f32 (independent)
  *   SSM_PROBE_FMA_F64     : 32 v_fma_f64
+ *   SSM_PROBE_EMPTY       : nothing (launch overhead)
  * *valu_per_iter and *trans_per_iter (either may be NULL) receive the VALU
  * instructions per iteration (transcendentals included) and the
  * transcendental ones.  `sink` is a device buffer of blocks * 256 floats that
@@ -465,11 +466,26 @@ typedef enum {
     SSM_PROBE_FMA_F32 = 0,
     SSM_PROBE_EXP_F32 = 1,
     SSM_PROBE_FMA_EXP_F32 = 2,
-    SSM_PROBE_FMA_F64 = 3
+    SSM_PROBE_FMA_F64 = 3,
+    SSM_PROBE_EMPTY = 4,
+    SSM_PROBE_HBM_READ = 16,   /* ssm_probe_hbm: read `bytes` */
+    SSM_PROBE_HBM_RMW = 17,    /* ssm_probe_hbm: read and write back `bytes` in place */
+    SSM_PROBE_HBM_WRITE = 18   /* ssm_probe_hbm: write `bytes` */
 } ssm_probe_kind;
 
 int ssm_probe_issue(int kind, int64_t blocks, int64_t iters, float *sink, void *stream,
                     int64_t *valu_per_iter, int64_t *trans_per_iter);
+
+/*
+ * Streaming memory probes, for the practical HBM ceiling beside the 8 TB/s
+ * specification: 16-byte nontemporal buffer loads and/or stores over the
+ * device buffer [buf, buf + bytes) (16-byte aligned, bytes a positive multiple
+ * of 16), enqueued on `stream` as one launch per 512 MiB.  READ moves `bytes`,
+ * RMW (every 32-bit value incremented in place) 2 * bytes, WRITE `bytes`;
+ * RMW and WRITE change the buffer.  The caller times the calls.  Returns
+ * SSM_OK, SSM_ERR_BAD_OPTION, SSM_ERR_NULLPTR, SSM_ERR_ALIGN or SSM_ERR_HIP.
+ */
+int ssm_probe_hbm(int kind, void *buf, int64_t bytes, void *stream);
 
 /* Free all library scratch memory (all devices and streams), including
  * buffers kept for captured HIP graphs: graphs captured with library calls

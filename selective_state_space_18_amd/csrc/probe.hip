@@ -53,17 +53,75 @@ __global__ __launch_bounds__(kProbeBlock) void probe_kernel(float *sink, int ite
     if (s == sentinel) sink[tid] = s;
 }
 
+__global__ __launch_bounds__(kProbeBlock) void empty_kernel() {}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kNt = 2;  // buffer cache-policy bit: nontemporal
+
+// Streaming probes over `words` 16-byte words, grid-stride, every access a
+// range-checked buffer access (a chunk is below 1 GiB, so offsets fit 32 bits).
+//   kMode 0 (read) : sum the words; the sum is stored only if it matches the sentinel
+//   kMode 1 (rmw)  : add 1 to every 32-bit value in place
+//   kMode 2 (write): store a constant
+template <int kMode>
+__global__ __launch_bounds__(kProbeBlock) void stream_kernel(unsigned *buf, int32_t words, unsigned sentinel) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(buf, (short)0, words * 16, 0x00020000);
+    const int32_t stride = (int32_t)(gridDim.x * kProbeBlock);
+    unsigned acc = 0;
+    for (int32_t w = (int32_t)(blockIdx.x * kProbeBlock + threadIdx.x); w < words; w += stride) {
+        if constexpr (kMode == 2) {
+            const u32x4 v = {(unsigned)w, 1u, 2u, 3u};
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, w * 16, 0, kNt);
+        } else {
+            u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, w * 16, 0, kNt);
+            if constexpr (kMode == 0) {
+                acc += v.x ^ v.y ^ v.z ^ v.w;
+            } else {
+                v += 1u;
+                __builtin_amdgcn_raw_buffer_store_b128(v, r, w * 16, 0, kNt);
+            }
+        }
+    }
+    if constexpr (kMode == 0)
+        if (acc == sentinel) __builtin_amdgcn_raw_buffer_store_b32(acc, r, 0, 0, 0);
+}
+
 }  // namespace
+
+extern "C" int ssm_probe_hbm(int kind, void *buf, int64_t bytes, void *stream) {
+    if (kind < SSM_PROBE_HBM_READ || kind > SSM_PROBE_HBM_WRITE)
+        return ssm::set_error(SSM_ERR_BAD_OPTION, "probe: unknown memory probe kind");
+    if (buf == nullptr) return ssm::set_error(SSM_ERR_NULLPTR, "probe: buf is NULL");
+    if (bytes < 16 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+        return ssm::set_error(SSM_ERR_ALIGN, "probe: buf must be 16-byte aligned and bytes a positive multiple of 16");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // chunks below 1 GiB, each its own launch of 256 x 8 blocks (8 per CU)
+    const int64_t chunk = int64_t(1) << 29;
+    for (int64_t off = 0; off < bytes; off += chunk) {
+        const int64_t n = bytes - off < chunk ? bytes - off : chunk;
+        unsigned *p = reinterpret_cast<unsigned *>(static_cast<char *>(buf) + off);
+        const int32_t words = (int32_t)(n / 16);
+        const dim3 grid(2048), block(kProbeBlock);
+        switch (kind) {
+            case SSM_PROBE_HBM_READ: hipLaunchKernelGGL((stream_kernel<0>), grid, block, 0, s, p, words, 0x9e3779b9u); break;
+            case SSM_PROBE_HBM_RMW: hipLaunchKernelGGL((stream_kernel<1>), grid, block, 0, s, p, words, 0u); break;
+            case SSM_PROBE_HBM_WRITE: hipLaunchKernelGGL((stream_kernel<2>), grid, block, 0, s, p, words, 0u); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return ssm::set_error(SSM_ERR_HIP, hipGetErrorString(e));
+    }
+    return SSM_OK;
+}
 
 extern "C" int ssm_probe_issue(int kind, int64_t blocks, int64_t iters, float *sink, void *stream,
                                int64_t *valu_per_iter, int64_t *trans_per_iter) {
     if (blocks <= 0 || blocks > (int64_t(1) << 24) || iters <= 0 || iters > (int64_t(1) << 24))
         return ssm::set_error(SSM_ERR_BAD_DIM, "probe: blocks and iterations must be in [1, 2^24]");
     if (sink == nullptr) return ssm::set_error(SSM_ERR_NULLPTR, "probe: sink is NULL");
-    if (kind < SSM_PROBE_FMA_F32 || kind > SSM_PROBE_FMA_F64)
+    if (kind < SSM_PROBE_FMA_F32 || kind > SSM_PROBE_EMPTY)
         return ssm::set_error(SSM_ERR_BAD_OPTION, "probe: unknown kind");
-    static const int64_t valu[] = {4 * kChains, kChains, 4 * kChains + kChains, 2 * kChains};
-    static const int64_t trans[] = {0, kChains, kChains, 0};
+    static const int64_t valu[] = {4 * kChains, kChains, 4 * kChains + kChains, 2 * kChains, 0};
+    static const int64_t trans[] = {0, kChains, kChains, 0, 0};
     if (valu_per_iter) *valu_per_iter = valu[kind];
     if (trans_per_iter) *trans_per_iter = trans[kind];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -82,6 +140,9 @@ extern "C" int ssm_probe_issue(int kind, int64_t blocks, int64_t iters, float *s
             break;
         case SSM_PROBE_FMA_F64:
             hipLaunchKernelGGL((probe_kernel<0, false, true>), grid, block, 0, s, sink, it, a, b, sentinel);
+            break;
+        case SSM_PROBE_EMPTY:
+            hipLaunchKernelGGL(empty_kernel, grid, block, 0, s);
             break;
     }
     const hipError_t e = hipGetLastError();

@@ -36,7 +36,7 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_st
            "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
            "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd", "ssm_scan_complex_fwd",
            "ssm_step_complex", "ssm_scan_ssd_fwd", "ssm_scan_bwd_plan", "ssm_probe_issue",
-           "ssm_scan_fwd_noalloc")
+           "ssm_scan_fwd_noalloc", "ssm_probe_hbm")
 
 
 class SSMError(RuntimeError):
@@ -97,6 +97,8 @@ def lib():
     L.ssm_scan_bwd_plan.restype = ctypes.c_int
     L.ssm_probe_issue.argtypes = [ctypes.c_int, _i64, _i64, _vp, _vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
     L.ssm_probe_issue.restype = ctypes.c_int
+    L.ssm_probe_hbm.argtypes = [ctypes.c_int, _vp, _i64, _vp]
+    L.ssm_probe_hbm.restype = ctypes.c_int
     L.ssm_release_workspaces.argtypes = []
     L.ssm_release_workspaces.restype = ctypes.c_int
     L.ssm_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), ctypes.c_int]
@@ -143,7 +145,8 @@ def bwd_plan(Bsz, L, Dm, N, dtype=SSM_BF16, compute_units=0):
     return tuple(v.value for v in out)
 
 
-PROBE_KINDS = ("fma_f32", "exp_f32", "fma_exp_f32", "fma_f64")
+PROBE_KINDS = ("fma_f32", "exp_f32", "fma_exp_f32", "fma_f64", "empty")
+HBM_PROBES = {"read": 16, "rmw": 17, "write": 18}
 
 
 def probe_issue(kind: str, blocks: int, iters: int, sink: torch.Tensor):
@@ -155,6 +158,16 @@ def probe_issue(kind: str, blocks: int, iters: int, sink: torch.Tensor):
     _check(lib().ssm_probe_issue(PROBE_KINDS.index(kind), blocks, iters, _ptr(sink), _stream(sink.device),
                                  ctypes.byref(v), ctypes.byref(t)), "ssm_probe_issue")
     return v.value, t.value
+
+
+def probe_hbm(kind: str, buf: torch.Tensor) -> int:
+    """Launch a streaming memory probe over buf on the current stream (the
+    caller times it); returns the bytes it moves."""
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous CUDA tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().ssm_probe_hbm(HBM_PROBES[kind], _ptr(buf), nbytes, _stream(buf.device)), "ssm_probe_hbm")
+    return 2 * nbytes if kind == "rmw" else nbytes
 
 
 def profile_read():

@@ -27,3 +27,35 @@ def test_cpu_baseline_record():
     assert rec["value"] > 0 and rec["cores"] >= 1
     assert rec["sample"].startswith(cfg.name)
     assert rec["one_thread"]["value"] > 0
+
+
+def test_scan_record_fields():
+    """The headline roofline carries the VALU-issue figure and the HBM
+    fractions of the dominant kernel and of the whole step (algorithmic bytes
+    over time against 8 TB/s)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from ssm_inputs import configs, generate
+
+    cfg = configs.MAMBA2P8B_LAYER
+    kern = {"scan_output": {"avg_ms": 0.5}, "scan_aggregate": {"avg_ms": 0.4}}
+    roof, hbm, cfgd, kms, proto = bench.scan_record(cfg, 1.0, kern, 64, 256, generate,
+                                                    proto={"flushed_median_ms": 1.1})
+    alg = generate.alg_bytes_scan(cfg)
+    assert roof["bound"] == "alu" and roof["unit"] == "TFLOP/s"
+    assert abs(roof["hbm_frac_kernel"] - alg / 0.5e-3 / 8e12) < 1e-4
+    assert abs(roof["hbm_frac_step"] - alg / 1.0e-3 / 8e12) < 1e-4
+    assert abs(roof["achieved"] - cfg.elems() * bench.SCAN_FLOPS_PER_ELEM / 0.5e-3 / 1e12) < 1e-2
+    assert hbm["algorithmic_bytes"] == alg and cfgd["segments"] == 64
+    assert proto["flushed_median_elems_per_s"] > 0
+
+
+def test_rotation_and_backward_bytes():
+    sys.path.insert(0, ROOT)
+    import bench
+    from ssm_inputs import configs
+
+    assert bench.rotation_count(2_000_000_000) == 1
+    assert bench.rotation_count(150_000_000) == 8       # >= 4 x the 256 MiB cache
+    b = bench.alg_bytes_bwd(configs.MAMBA2P8B_LAYER)
+    assert 3.3e9 < b < 3.5e9                            # x, delta, dy read; dx, ddelta written; dB, dC
