@@ -9,7 +9,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+# SSM_ORACLE_LIB selects another build of the same source (the sanitizer build).
+DEFAULT_LIB = os.environ.get("SSM_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _dp = ctypes.POINTER(ctypes.c_double)
 _i64 = ctypes.c_int64

@@ -72,9 +72,36 @@ def build(verbose: bool = False, isa_dir: str = None) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libssmscan.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The library with its host-side argument validation, planning and
+    dispatch (abi.cpp) built by g++ with AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the device objects of the normal
+    build (which runs first if they are missing).  For CPU runs with gcc's
+    libasan preloaded, the library selected through SSMSCAN_LIB."""
+    objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "abi.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose=verbose)
+    os.makedirs(SAN_DIR, exist_ok=True)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    abi = os.path.join(SAN_DIR, "abi.o")
+    _run(["g++", "-std=c++17", "-O1", "-fPIC", *SAN_FLAGS, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+          "-I", CSRC, "-I", INCLUDE, "-c", os.path.join(CSRC, "abi.cpp"), "-o", abi], verbose)
+    tmp = SAN_LIB + ".tmp"
+    _run(["g++", "-shared", *SAN_FLAGS, abi, *objs, "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+          f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", tmp], verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-v", action="store_true")
     ap.add_argument("--isa", default=None)
+    ap.add_argument("--sanitize", action="store_true", help="build the ASan/UBSan host variant instead")
     a = ap.parse_args()
-    print(build(verbose=a.v, isa_dir=a.isa))
+    print(build_sanitized(verbose=a.v) if a.sanitize else build(verbose=a.v, isa_dir=a.isa))

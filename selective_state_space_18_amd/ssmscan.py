@@ -18,7 +18,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+# SSMSCAN_LIB selects another build of the same library (the sanitizer build
+# of the host code, for example); by default the in-tree one.
+LIB_PATH = os.environ.get("SSMSCAN_LIB") or os.path.join(_HERE, "libssmscan.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 SSM_OPT_SEGMENT_LEN, SSM_OPT_FORCE_GENERAL, SSM_OPT_PROFILE, SSM_OPT_STEP_CHANNELS = 1, 2, 3, 4
