@@ -664,7 +664,8 @@ def bench_probe(torch, ss, iters=2048):
     out = {"derived_peak_lane_instr_per_s": derived}
     st = torch.cuda.current_stream()
     for kind, blocks in (("fma_f32", 256), ("fma_f32", 1024), ("fma_f32", 4096), ("exp_f32", 4096),
-                         ("fma_exp_f32", 4096), ("fma_f64", 4096)):
+                         ("fma_exp_f32", 4096), ("fma_f64", 4096), ("fmac_f32", 4096), ("mul_f32", 4096),
+                         ("add_f32", 4096), ("fma_f32_vgpr", 4096), ("fmac_f32", 1024), ("fma_f32_vgpr", 1024)):
         sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda:0")
         ss.probe_issue(kind, blocks, 16, sink)  # warm-up
         a = torch.cuda.Event(enable_timing=True)

@@ -455,6 +455,10 @@ int ssm_scan_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
  *   SSM_PROBE_FMA_EXP_F32 : 64 v_fma_f32 and 16 v_exp_f32 (independent)
  *   SSM_PROBE_FMA_F64     : 32 v_fma_f64
  *   SSM_PROBE_EMPTY       : nothing (launch overhead)
+ *   SSM_PROBE_FMAC_F32    : 64 v_fmac_f32 (two-operand accumulate form, VGPRs)
+ *   SSM_PROBE_MUL_F32     : 64 v_mul_f32
+ *   SSM_PROBE_ADD_F32     : 64 v_add_f32
+ *   SSM_PROBE_FMA_F32_VGPR: 64 v_fma_f32 with VGPR operands only
  * *valu_per_iter and *trans_per_iter (either may be NULL) receive the VALU
  * instructions per iteration (transcendentals included) and the
  * transcendental ones.  `sink` is a device buffer of blocks * 256 floats that
@@ -468,6 +472,10 @@ typedef enum {
     SSM_PROBE_FMA_EXP_F32 = 2,
     SSM_PROBE_FMA_F64 = 3,
     SSM_PROBE_EMPTY = 4,
+    SSM_PROBE_FMAC_F32 = 5,
+    SSM_PROBE_MUL_F32 = 6,
+    SSM_PROBE_ADD_F32 = 7,
+    SSM_PROBE_FMA_F32_VGPR = 8,
     SSM_PROBE_HBM_READ = 16,   /* ssm_probe_hbm: read `bytes` */
     SSM_PROBE_HBM_RMW = 17,    /* ssm_probe_hbm: read and write back `bytes` in place */
     SSM_PROBE_HBM_WRITE = 18   /* ssm_probe_hbm: write `bytes` */

@@ -196,11 +196,14 @@ __global__ __launch_bounds__(kBlock) void cplx_segment_kernel(ScanParams p) {
         for (int k = 0; k < G; ++k) {
             const int t = tb + k;
             const int so = (t < nsteps - 1 ? t : nsteps - 1) * row;
-            xs[k] = buf_load_raw<T>(rx, voff, so);
-            ds[k] = buf_load_raw<T>(rdl, voff, so);
+            xs[k] = buf_load_raw<T, kBufNt>(rx, voff, so);
+            ds[k] = buf_load_raw<T, kBufNt>(rdl, voff, so);
         }
     };
+    static_assert(G % 2 == 0, "the B/C row buffers alternate within a group");
     Acc lam = 0;
+    Acc rowa[2 * N], rowb[2 * N];  // this step's B/C row and the next one's
+    load_row<N>(rowa, bcp);
     load(0, xc, dc);
     for (int tb = 0; tb < nsteps; tb += G) {
         load(tb + G, xn, dn);
@@ -208,14 +211,18 @@ __global__ __launch_bounds__(kBlock) void cplx_segment_kernel(ScanParams p) {
         for (int k = 0; k < G; ++k) {
             const int t = tb + k;
             if (t < nsteps) {
-                Acc rw[2 * N];
-                load_row<N>(rw, bcp + (int64_t)t * (2 * N));
+                // as in the real-A scan: wait for this row, then fetch the next
+                Acc(&rw)[2 * N] = (k & 1) ? rowb : rowa;
+                Acc(&nxt)[2 * N] = (k & 1) ? rowa : rowb;
+                row_ready<N>(rw);
+                load_row<N>(nxt, bcp + (int64_t)(t + 1 < nsteps ? t + 1 : t) * (2 * N));
+                __builtin_amdgcn_sched_barrier(0);
                 const Acc xv = (Acc)raw_to_f32<T>(xc[k]);
                 Acc dv = (Acc)raw_to_f32<T>(dc[k]);
                 if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
                 const Acc yv = cplx_step<N, kOut, kEuler>(cc, rw, xv, dv, hr, hi);
                 if constexpr (kOut)
-                    buf_store(from_acc<T>(fma_(Dd, xv, yv)), ry, voff, t * row);
+                    buf_store<kBufNt>(from_acc<T>(fma_(Dd, xv, yv)), ry, voff, t * row);
                 else
                     lam += dv;
             }

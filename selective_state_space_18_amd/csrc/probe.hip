@@ -53,6 +53,37 @@ __global__ __launch_bounds__(kProbeBlock) void probe_kernel(float *sink, int ite
     if (s == sentinel) sink[tid] = s;
 }
 
+// One instruction form per probe, 16 independent chains, kRep x 16 per iteration:
+//   kOp 0: v_fmac_f32 (VOP2: v += w * u, all VGPRs)
+//   kOp 1: v_mul_f32  (VOP2: v = v * w)
+//   kOp 2: v_add_f32  (VOP2: v = v + w)
+//   kOp 3: v_fma_f32 with two VGPR sources and the VGPR addend (VOP3: v = v * w + u)
+template <int kOp>
+__global__ __launch_bounds__(kProbeBlock) void form_kernel(float *sink, int iters, float a, float b, float sentinel) {
+    const int tid = blockIdx.x * kProbeBlock + threadIdx.x;
+    float v[kChains];
+    float w = a + 1e-7f * (float)threadIdx.x, u = b;
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) v[k] = 0.001f * (float)(threadIdx.x + k);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int k = 0; k < kChains; ++k) {
+                if constexpr (kOp == 0) v[k] = __builtin_fmaf(w, u, v[k]);
+                else if constexpr (kOp == 1) v[k] = v[k] * w;
+                else if constexpr (kOp == 2) v[k] = v[k] + w;
+                else v[k] = __builtin_fmaf(v[k], w, u);
+            }
+        }
+        __asm__ volatile("" : "+v"(w), "+v"(u));  // keep w, u in VGPRs, opaque per iteration
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) s += v[k];
+    if (s == sentinel) sink[tid] = s;
+}
+
 __global__ __launch_bounds__(kProbeBlock) void empty_kernel() {}
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -118,10 +149,11 @@ extern "C" int ssm_probe_issue(int kind, int64_t blocks, int64_t iters, float *s
     if (blocks <= 0 || blocks > (int64_t(1) << 24) || iters <= 0 || iters > (int64_t(1) << 24))
         return ssm::set_error(SSM_ERR_BAD_DIM, "probe: blocks and iterations must be in [1, 2^24]");
     if (sink == nullptr) return ssm::set_error(SSM_ERR_NULLPTR, "probe: sink is NULL");
-    if (kind < SSM_PROBE_FMA_F32 || kind > SSM_PROBE_EMPTY)
+    if (kind < SSM_PROBE_FMA_F32 || kind > SSM_PROBE_FMA_F32_VGPR)
         return ssm::set_error(SSM_ERR_BAD_OPTION, "probe: unknown kind");
-    static const int64_t valu[] = {4 * kChains, kChains, 4 * kChains + kChains, 2 * kChains, 0};
-    static const int64_t trans[] = {0, kChains, kChains, 0, 0};
+    static const int64_t valu[] = {4 * kChains, kChains, 4 * kChains + kChains, 2 * kChains, 0,
+                                   4 * kChains, 4 * kChains, 4 * kChains, 4 * kChains};
+    static const int64_t trans[] = {0, kChains, kChains, 0, 0, 0, 0, 0, 0};
     if (valu_per_iter) *valu_per_iter = valu[kind];
     if (trans_per_iter) *trans_per_iter = trans[kind];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -143,6 +175,18 @@ extern "C" int ssm_probe_issue(int kind, int64_t blocks, int64_t iters, float *s
             break;
         case SSM_PROBE_EMPTY:
             hipLaunchKernelGGL(empty_kernel, grid, block, 0, s);
+            break;
+        case SSM_PROBE_FMAC_F32:
+            hipLaunchKernelGGL((form_kernel<0>), grid, block, 0, s, sink, it, a, b, sentinel);
+            break;
+        case SSM_PROBE_MUL_F32:
+            hipLaunchKernelGGL((form_kernel<1>), grid, block, 0, s, sink, it, a, b, sentinel);
+            break;
+        case SSM_PROBE_ADD_F32:
+            hipLaunchKernelGGL((form_kernel<2>), grid, block, 0, s, sink, it, a, b, sentinel);
+            break;
+        case SSM_PROBE_FMA_F32_VGPR:
+            hipLaunchKernelGGL((form_kernel<3>), grid, block, 0, s, sink, it, a, b, sentinel);
             break;
     }
     const hipError_t e = hipGetLastError();

@@ -86,6 +86,17 @@ __device__ __forceinline__ float expm1_and_exp2(float z2, float& e) {
 }
 __device__ __forceinline__ double expm1_and_exp2(double z, double& e) { return expm1_and_exp(z, e); }
 
+// exp2(z2) - 1 as a plain difference, for fp32 callers that know |z| >= 2^-13
+// (|z2| >= kExpm1DirectZ2) on every lane.  exp2 is accurate to about an ulp
+// (2^-24 near 1), so the difference carries a relative error of at most about
+// 2 * 2^-24 / 2^-13 = 2^-10 at the threshold, falling as 1/|z| above it: half
+// an ulp of the bf16 outputs of the kernels that use it, at worst.
+constexpr float kExpm1DirectZ2 = 1.4426950408889634f / 8192.0f;
+__device__ __forceinline__ float expm1_direct_exp2(float z2, float& e) {
+    e = fast_exp2(z2);
+    return e - 1.0f;
+}
+
 // Raw buffer descriptor over [base, base + bytes): loads outside read 0 and
 // stores outside are dropped by the hardware range check.  Word 3 is the
 // gfx9-family raw-buffer format.
@@ -93,28 +104,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-template <typename T>
-__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff);
-template <>
-__device__ __forceinline__ bf16 buf_load<bf16>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
-    return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
-}
-template <>
-__device__ __forceinline__ float buf_load<float>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+constexpr int kBufNt = 2;  // buffer cache-policy bit: nontemporal
+
+// kAux: cache-policy bits of the access (0, or kBufNt for data streamed once).
+template <typename T, int kAux = 0>
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    static_assert(sizeof(T) == 2 || sizeof(T) == 4, "bf16 or fp32");
+    if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kAux));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kAux));
 }
 // The raw bits of one stored value, one per 32-bit register (a bf16 load
 // zero-extends).  Keeping prefetched bf16 values apart like this matters: two
 // bf16 packed into one register make the compiler wait for both loads at once.
-template <typename T>
-__device__ __forceinline__ uint32_t buf_load_raw(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff);
-template <>
-__device__ __forceinline__ uint32_t buf_load_raw<bf16>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
-template <>
-__device__ __forceinline__ uint32_t buf_load_raw<float>(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+template <typename T, int kAux = 0>
+__device__ __forceinline__ uint32_t buf_load_raw(__amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
+    static_assert(sizeof(T) == 2 || sizeof(T) == 4, "bf16 or fp32");
+    if constexpr (sizeof(T) == 2)
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kAux);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kAux);
 }
 template <typename T>
 __device__ __forceinline__ float raw_to_f32(uint32_t u) {
@@ -124,11 +134,13 @@ __device__ __forceinline__ float raw_to_f32(uint32_t u) {
         return __builtin_bit_cast(float, u);
 }
 
+template <int kAux = 0>
 __device__ __forceinline__ void buf_store(bf16 v, __amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, voff, soff, kAux);
 }
+template <int kAux = 0>
 __device__ __forceinline__ void buf_store(float v, __amdgpu_buffer_rsrc_t r, int32_t voff, int32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, kAux);
 }
 
 // Accurate fp32 variant (ocml expm1f), for the fp32-storage decode step.
@@ -171,7 +183,6 @@ __device__ __forceinline__ float exp_units(float z2) { return fast_exp2(z2); }
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-constexpr int kBufNt = 2;  // buffer cache-policy bit: nontemporal
 
 // K consecutive values of T at byte offset voff + soff of a buffer: one
 // vector load where kVec guarantees the alignment, else one per value.

@@ -180,6 +180,51 @@ def test_zero_and_tiny_A_and_zero_delta(ss, dtype):
         P.compare(hf, hr, dtype, f"h_final (general={general})")
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["dense", "packed"])
+def test_general_path_small_argument_threshold(ss, packed):
+    """General-path exp(delta A) - 1: a wave whose every |delta A| stays at or
+    just above 2^-13 takes the plain difference (its worst relative error, about
+    2^-10, is at the threshold); a wave with one channel below it keeps the
+    small-argument form.  Both against the oracle, dense and packed."""
+    P.say(f"case: general path exp threshold packed={packed}")
+    Bsz, L, Dm, N = 1, 700, 192, 16
+    cfg = small_cfg("bf16", "lognormal", Bsz, L, Dm, N, seed=29)
+    inp = generate.scan_inputs(cfg, DEV)
+    amin = inp["A"].abs().min(dim=1).values                       # [Dm]
+    thr = 2.0 ** -13
+    # waves 0 and 2 (channels 0..63, 128..191): |delta A_min| in [1, 1.5] x 2^-13
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    scale = 1.0 + 0.5 * torch.rand((Bsz, L, Dm), generator=g, device=DEV)
+    near = (thr * scale / amin).to(torch.bfloat16)
+    near = torch.where(near.float() * amin < thr, (near.float() * 1.02).to(torch.bfloat16), near)
+    dl = inp["delta"].clone()
+    dl[:, :, 0:64] = near[:, :, 0:64]
+    dl[:, :, 128:192] = near[:, :, 128:192]
+    # wave 2 also gets one channel far below the threshold (small-argument form)
+    dl[:, 100:400, 150] = (thr * 0.01 / amin[150]).to(torch.bfloat16)
+    inp["delta"] = dl
+    assert float((dl[:, :, 0:64].float() * amin[0:64]).min()) >= thr
+    if not packed:
+        y, hf = run_scan(ss, inp)
+        yr, hr = P.oracle_scan(inp)
+        P.compare(y, yr, "bf16", "y")
+        P.compare(hf, hr, "bf16", "h_final")
+    else:
+        lengths = [250, 0, 450]
+        cu = generate.cu_seqlens(lengths, DEV)
+        y, hf = ss.scan_varlen_fwd(inp["x"][0], dl[0], inp["A"], inp["B"][0], inp["C"][0], inp["D"], cu)
+        torch.cuda.synchronize()
+        t0 = 0
+        for k, n in enumerate(lengths):
+            sub = {"x": inp["x"][:, t0:t0 + n], "delta": dl[:, t0:t0 + n], "A": inp["A"], "B": inp["B"][:, t0:t0 + n],
+                   "C": inp["C"][:, t0:t0 + n], "D": inp["D"]}
+            yr, hr = P.oracle_scan(sub)
+            P.compare(y[t0:t0 + n], yr[0], "bf16", f"y of sequence {k}")
+            P.compare(hf[k], hr[0], "bf16", f"h_final of sequence {k}")
+            t0 += n
+
+
 def test_structured_A_with_other_scale(ss):
     """A[d, n] = (n+1) * a_d with a per-channel a_d takes the structured path."""
     cfg = small_cfg("bf16", "s4d_real", 2, 400, 128, 16, seed=9)
