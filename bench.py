@@ -39,8 +39,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selective-scan elems/s (B·L·D·N) + achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBPS = 8000.0
-# Non-packed fp32 FMA issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 2 flops.
-VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2.4e9 * 2 / 1e12
+# Published fp32 vector peak of MI355X: 256 CUs x 128 fp32 FMA lanes per cycle x
+# 2 flops x 2.4 GHz = 157.3 TFLOP/s.  The probe kernels measure how much of it
+# each instruction form reaches without packed FP32 (VGPR-only forms issue at
+# up to twice the rate of a form with a scalar operand).
+VALU_FP32_PEAK_TFLOPS = 256 * 128 * 2.4e9 * 2 / 1e12
+# Wave64 VALU instructions per second at one instruction per 4 cycles per SIMD
+# (the rate of an FMA with a scalar operand): 256 x 4 x 16 lanes x 2.4 GHz.
+SINGLE_RATE_LANE_INSTR_PER_S = 256 * 4 * 16 * 2.4e9
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
 # Dense bf16 matrix-core peak of MI355X (no sparsity).
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 # Algorithmic fp32 flops per state element of the scan: z = delta*A, exp(z)-1,
@@ -475,10 +483,11 @@ def bench_packed(torch, ss, generate, cfg, steps, warmup, flusher=None):
 def scan_record(cfg, ms, kern, S, seg, generate, kind="scan", proto=None):
     """Roofline of the dominant kernel (the output pass) and the step.  The
     binding roof is VALU issue: 'achieved' counts SCAN_FLOPS_PER_ELEM
-    algorithmic flops per state element against the derived non-packed fp32
-    peak (calibrated by the probe kernels).  The HBM fractions are the
-    algorithmic bytes of the whole call over the output pass's time and over
-    the whole step's time, against 8 TB/s."""
+    algorithmic flops per state element against the published fp32 vector
+    peak; cycles_per_wave_step_per_simd is the pass's issue cost per time step
+    of a 64-channel tile, to set beside the step-mix probe's.  The HBM
+    fractions are the algorithmic bytes of the whole call over the output
+    pass's time and over the whole step's time, against 8 TB/s."""
     elems = cfg.elems()
     alg = generate.alg_bytes_scan(cfg)
     out_ms = kern["scan_output"]["avg_ms"]
@@ -496,6 +505,10 @@ def scan_record(cfg, ms, kern, S, seg, generate, kind="scan", proto=None):
         "hbm_frac_kernel": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "hbm_frac_step": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
     }
+    # one wave-step = one time step of one 64-channel tile; the output pass
+    # runs Bsz * ceil(Dm/64) * L of them
+    wave_steps = cfg.Bsz * ((cfg.Dm + 63) // 64) * cfg.L
+    roof["cycles_per_wave_step_per_simd"] = round(out_ms * 1e-3 * CLOCK_HZ * SIMDS / wave_steps, 1)
     roof.update(traffic_fields(cfg.name, kind, alg))
     hbm = {"achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
            "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg}
@@ -656,16 +669,19 @@ def bench_probe(torch, ss, iters=2048):
     """Measured issue rates of the VALU and the transcendental unit, from the
     library's probe kernels (known per-lane instruction mix, 16 independent
     chains per lane), each launch timed with HIP events on the stream it runs
-    on.  Rates are lane-instructions per second; the derived peak is one
-    wave64 VALU instruction per 4 cycles per SIMD: 256 CUs x 4 SIMDs x 16
-    lanes x 2.4 GHz = 3.93e13 lane-instructions/s (78.6 TFLOP/s counting an
-    FMA as two flops, packed FP32 not used)."""
-    derived = 256 * 4 * 16 * 2.4e9
-    out = {"derived_peak_lane_instr_per_s": derived}
+    on.  Rates are lane-instructions per second, given as fractions of the
+    single rate (one wave64 instruction per 4 cycles per SIMD, 3.93e13
+    lane-instructions/s) and of the published peak (twice that: 157.3 TFLOP/s
+    counting an FMA as two flops).  scan_step_mix is one structured output
+    step of the scan (N = 16) without memory traffic; its cycles per
+    wave-step are the issue ceiling of the scan's own instruction mix."""
+    derived = SINGLE_RATE_LANE_INSTR_PER_S
+    out = {"single_rate_lane_instr_per_s": derived, "published_peak_lane_instr_per_s": 2 * derived}
     st = torch.cuda.current_stream()
     for kind, blocks in (("fma_f32", 256), ("fma_f32", 1024), ("fma_f32", 4096), ("exp_f32", 4096),
                          ("fma_exp_f32", 4096), ("fma_f64", 4096), ("fmac_f32", 4096), ("mul_f32", 4096),
-                         ("add_f32", 4096), ("fma_f32_vgpr", 4096), ("fmac_f32", 1024), ("fma_f32_vgpr", 1024)):
+                         ("add_f32", 4096), ("fma_f32_vgpr", 4096), ("fmac_f32", 1024), ("fma_f32_vgpr", 1024),
+                         ("scan_step_mix", 2048), ("scan_step_mix", 8192)):
         sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda:0")
         ss.probe_issue(kind, blocks, 16, sink)  # warm-up
         a = torch.cuda.Event(enable_timing=True)
@@ -683,11 +699,13 @@ def bench_probe(torch, ss, iters=2048):
         rec = {"blocks": blocks, "waves_per_simd": blocks * 4 / 1024, "ms": round(t * 1e3, 4),
                "valu_per_iter": valu, "trans_per_iter": trans,
                "valu_lane_instr_per_s": lanes * valu / t,
-               "frac_of_derived_peak": round(lanes * valu / t / derived, 4)}
+               "frac_of_single_rate": round(lanes * valu / t / derived, 4),
+               "frac_of_published_peak": round(lanes * valu / t / (2 * derived), 4),
+               "cycles_per_wave_step_per_simd": round(t * CLOCK_HZ * SIMDS / (blocks * 4 * iters), 1)}
         if trans:
             rec["trans_lane_instr_per_s"] = lanes * trans / t
         out[f"{kind}_b{blocks}"] = rec
-        log(f"[bench] probe {kind} blocks={blocks}: {rec['ms']} ms, {rec['frac_of_derived_peak']} of derived peak")
+        log(f"[bench] probe {kind} blocks={blocks}: {rec['ms']} ms, {rec['frac_of_single_rate']} of the single rate")
         del sink
     return out
 
@@ -852,9 +870,9 @@ def main():
         cal = {"valu": bench_probe(torch, ss), "hbm": hbm_probes(torch, ss),
                "launch_overhead_us": launch_overhead_us(torch, ss), "copy": copy_peak(torch)}
         out["calibration"] = cal
-        fma = cal["valu"]["fma_f32_b4096"]["frac_of_derived_peak"]
-        out["roofline"]["peak_measured_frac"] = fma
-        out["roofline"]["frac_of_measured_peak"] = round(out["roofline"]["frac"] / fma, 4)
+        mix = cal["valu"]["scan_step_mix_b8192"]["cycles_per_wave_step_per_simd"]
+        out["roofline"]["step_mix_cycles_per_wave_step_per_simd"] = mix
+        out["roofline"]["frac_of_step_mix_rate"] = round(mix / out["roofline"]["cycles_per_wave_step_per_simd"], 4)
         practical = cal["hbm"]["practical_peak_gbps"]
         out["hbm"]["practical_peak_gbps"] = practical
         out["hbm"]["frac_of_practical_peak"] = round(out["hbm"]["achieved"] / practical, 4)

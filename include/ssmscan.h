@@ -459,6 +459,10 @@ int ssm_scan_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
  *   SSM_PROBE_MUL_F32     : 64 v_mul_f32
  *   SSM_PROBE_ADD_F32     : 64 v_add_f32
  *   SSM_PROBE_FMA_F32_VGPR: 64 v_fma_f32 with VGPR operands only
+ *   SSM_PROBE_SCAN_STEP_MIX: one structured-A output step of the scan for
+ *                           N = 16 without memory traffic: 63 FMAs and
+ *                           1 v_exp_f32 (64 reported), the B/C row as scalar
+ *                           operands; one iteration is one wave-step
  * *valu_per_iter and *trans_per_iter (either may be NULL) receive the VALU
  * instructions per iteration (transcendentals included) and the
  * transcendental ones.  `sink` is a device buffer of blocks * 256 floats that
@@ -476,6 +480,7 @@ typedef enum {
     SSM_PROBE_MUL_F32 = 6,
     SSM_PROBE_ADD_F32 = 7,
     SSM_PROBE_FMA_F32_VGPR = 8,
+    SSM_PROBE_SCAN_STEP_MIX = 9,
     SSM_PROBE_HBM_READ = 16,   /* ssm_probe_hbm: read `bytes` */
     SSM_PROBE_HBM_RMW = 17,    /* ssm_probe_hbm: read and write back `bytes` in place */
     SSM_PROBE_HBM_WRITE = 18   /* ssm_probe_hbm: write `bytes` */

@@ -126,6 +126,15 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
             dyv[k] = buf_load_raw<T>(rdy, voff, so);
         }
     };
+    // C rows alternate between two register sets: each step waits for its
+    // own row, then fetches the previous step's (as in the forward scan)
+    static_assert(G % 2 == 0, "the C row buffers alternate within a group");
+    Acc ca[N], cb[N];
+    auto load_c = [&](Acc(&dst)[N], int t) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) dst[n] = bcp[(int64_t)t * (2 * N) + N + n];
+    };
+    load_c(ca, nsteps - 1);
     load(nsteps - 1, dl_c, dy_c);
     for (int tb = nsteps - 1; tb >= 0; tb -= G) {
         load(tb - G, dl_n, dy_n);
@@ -133,9 +142,10 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
         for (int k = 0; k < G; ++k) {
             const int t = tb - k;
             if (t >= 0) {
-                Acc crow[N];
-#pragma unroll
-                for (int n = 0; n < N; ++n) crow[n] = bcp[(int64_t)t * (2 * N) + N + n];
+                Acc(&crow)[N] = (k & 1) ? cb : ca;
+                row_ready(crow);
+                load_c((k & 1) ? ca : cb, t > 0 ? t - 1 : 0);
+                __builtin_amdgcn_sched_barrier(0);
                 Acc dv = (Acc)raw_to_f32<T>(dl_c[k]);
                 if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
                 const Acc g = (Acc)raw_to_f32<T>(dy_c[k]);

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kBlock) void cplx_segment_kernel(ScanParams p) {
                 // as in the real-A scan: wait for this row, then fetch the next
                 Acc(&rw)[2 * N] = (k & 1) ? rowb : rowa;
                 Acc(&nxt)[2 * N] = (k & 1) ? rowa : rowb;
-                row_ready<N>(rw);
+                row_ready(rw);
                 load_row<N>(nxt, bcp + (int64_t)(t + 1 < nsteps ? t + 1 : t) * (2 * N));
                 __builtin_amdgcn_sched_barrier(0);
                 const Acc xv = (Acc)raw_to_f32<T>(xc[k]);

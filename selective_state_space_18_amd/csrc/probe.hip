@@ -84,6 +84,47 @@ __global__ __launch_bounds__(kProbeBlock) void form_kernel(float *sink, int iter
     if (s == sentinel) sink[tid] = s;
 }
 
+// The arithmetic of one structured-A output step for N = 16 states, with no
+// memory traffic: per step an exp, the E chain, and per state element the
+// input, update and output FMAs, the B/C row entering as wave-uniform scalar
+// operands (kernel arguments) as in the scan.  x and delta follow cheap
+// per-lane recurrences, so nothing is loop-invariant.  One iteration is one
+// wave-step of the scan's output pass without its loads and stores.
+constexpr int kMixN = 16;
+struct MixRow {
+    float v[2 * kMixN];
+};
+
+__global__ __launch_bounds__(kProbeBlock) void step_mix_kernel(float *sink, int iters, MixRow row, float sentinel) {
+    const int tid = blockIdx.x * kProbeBlock + threadIdx.x;
+    float g[kMixN];
+#pragma unroll
+    for (int n = 0; n < kMixN; ++n) g[n] = 0.01f * (float)(threadIdx.x & 7) + 0.001f * (float)n;
+    const float a0 = -0.5f - 1e-4f * (float)(threadIdx.x & 15), inva = 1.0f / a0;
+    float xv = 0.3f + 1e-3f * (float)(threadIdx.x & 31), dv = 0.01f + 1e-5f * (float)(threadIdx.x & 63);
+    float ysum = 0.f;
+    for (int i = 0; i < iters; ++i) {
+        const float r = __builtin_amdgcn_exp2f(dv * a0);
+        const float E1 = r - 1.0f;
+        const float xa = xv * inva;
+        float E = E1, y = 0.f;
+#pragma unroll
+        for (int n = 0; n < kMixN; ++n) {
+            const float tt = __builtin_fmaf(row.v[n], xa, g[n]);
+            g[n] = __builtin_fmaf(E, tt, g[n]);
+            y = __builtin_fmaf(row.v[kMixN + n], g[n], y);
+            if (n + 1 < kMixN) E = __builtin_fmaf(E, r, E1);
+        }
+        ysum += y;
+        xv = __builtin_fmaf(xv, 0.999f, 1e-4f);
+        dv = __builtin_fmaf(dv, 1.0001f, 1e-7f);
+    }
+    float s = ysum;
+#pragma unroll
+    for (int n = 0; n < kMixN; ++n) s += g[n];
+    if (s == sentinel) sink[tid] = s;
+}
+
 __global__ __launch_bounds__(kProbeBlock) void empty_kernel() {}
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -149,11 +190,13 @@ extern "C" int ssm_probe_issue(int kind, int64_t blocks, int64_t iters, float *s
     if (blocks <= 0 || blocks > (int64_t(1) << 24) || iters <= 0 || iters > (int64_t(1) << 24))
         return ssm::set_error(SSM_ERR_BAD_DIM, "probe: blocks and iterations must be in [1, 2^24]");
     if (sink == nullptr) return ssm::set_error(SSM_ERR_NULLPTR, "probe: sink is NULL");
-    if (kind < SSM_PROBE_FMA_F32 || kind > SSM_PROBE_FMA_F32_VGPR)
+    if (kind < SSM_PROBE_FMA_F32 || kind > SSM_PROBE_SCAN_STEP_MIX)
         return ssm::set_error(SSM_ERR_BAD_OPTION, "probe: unknown kind");
+    // VALU instructions per iteration counted from the source (the step mix:
+    // its 63 FMAs and the exp; the compiled loop adds a few more)
     static const int64_t valu[] = {4 * kChains, kChains, 4 * kChains + kChains, 2 * kChains, 0,
-                                   4 * kChains, 4 * kChains, 4 * kChains, 4 * kChains};
-    static const int64_t trans[] = {0, kChains, kChains, 0, 0, 0, 0, 0, 0};
+                                   4 * kChains, 4 * kChains, 4 * kChains, 4 * kChains, 4 * kMixN};
+    static const int64_t trans[] = {0, kChains, kChains, 0, 0, 0, 0, 0, 0, 1};
     if (valu_per_iter) *valu_per_iter = valu[kind];
     if (trans_per_iter) *trans_per_iter = trans[kind];
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -188,6 +231,12 @@ extern "C" int ssm_probe_issue(int kind, int64_t blocks, int64_t iters, float *s
         case SSM_PROBE_FMA_F32_VGPR:
             hipLaunchKernelGGL((form_kernel<3>), grid, block, 0, s, sink, it, a, b, sentinel);
             break;
+        case SSM_PROBE_SCAN_STEP_MIX: {
+            MixRow row;
+            for (int k = 0; k < 2 * kMixN; ++k) row.v[k] = 0.1f + 0.01f * (float)k;
+            hipLaunchKernelGGL(step_mix_kernel, grid, block, 0, s, sink, it, row, sentinel);
+            break;
+        }
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return ssm::set_error(SSM_ERR_HIP, hipGetErrorString(e));

@@ -207,8 +207,8 @@ __device__ __forceinline__ void load_row(Acc (&dst)[2 * N], const_row_ptr<Acc> s
 // Makes the row's scalar registers readable at this point (the wait for
 // its load goes here).  One element suffices: the wait covers every
 // outstanding scalar load.
-template <int N, typename Acc>
-__device__ __forceinline__ void row_ready(const Acc (&row)[2 * N]) {
+template <typename Acc, int M>
+__device__ __forceinline__ void row_ready(const Acc (&row)[M]) {
     __asm__ volatile("" ::"s"(row[0]));
 }
 
@@ -267,7 +267,7 @@ __device__ __forceinline__ void run_group(const SegIO<T> &io, const_row_ptr<Acc>
             // one, which then has the whole step to arrive.  (Left alone the
             // scheduler puts the load at the end of the step, just before the
             // wait.)
-            row_ready<N>(cur);
+            row_ready(cur);
             load_row<N>(nxt, bcp + (int64_t)(tn < last ? tn : last) * (2 * N));
             __builtin_amdgcn_sched_barrier(0);
             const Acc xv = (Acc)to_f32(xs[k]);

@@ -148,7 +148,7 @@ def bwd_plan(Bsz, L, Dm, N, dtype=SSM_BF16, compute_units=0):
 
 
 PROBE_KINDS = ("fma_f32", "exp_f32", "fma_exp_f32", "fma_f64", "empty", "fmac_f32", "mul_f32", "add_f32",
-               "fma_f32_vgpr")
+               "fma_f32_vgpr", "scan_step_mix")
 HBM_PROBES = {"read": 16, "rmw": 17, "write": 18}
 
 
