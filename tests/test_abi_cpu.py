@@ -344,3 +344,17 @@ def test_noalloc_rejects_oversized_calls_without_a_device(L):
     assert call(1, 8, 64, N=3) == 4
     assert call(1, 8, 64, x=0) == 1
     assert call(0, 8, 64) == 0                # nothing to do: no device call
+
+
+def test_probe_argument_errors(L):
+    """The calibration probes validate before launching: unknown kinds, bad
+    sizes and NULL buffers are refused without a device call."""
+    v = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    sink = v(P[0])
+    assert L.ssm_probe_issue(10, i64(1), i64(1), sink, None, None, None) == 9  # past the step-mix kind
+    assert L.ssm_probe_issue(-1, i64(1), i64(1), sink, None, None, None) == 9
+    assert L.ssm_probe_issue(9, i64(0), i64(1), sink, None, None, None) == 2
+    assert L.ssm_probe_issue(9, i64(1), i64(1), v(None), None, None, None) == 1
+    assert L.ssm_probe_hbm(15, sink, i64(1 << 20), None) == 9
+    assert L.ssm_probe_hbm(16, sink, i64(24), None) != 0  # not a multiple of 16

@@ -46,6 +46,11 @@ def test_scan_record_fields():
     assert abs(roof["hbm_frac_kernel"] - alg / 0.5e-3 / 8e12) < 1e-4
     assert abs(roof["hbm_frac_step"] - alg / 1.0e-3 / 8e12) < 1e-4
     assert abs(roof["achieved"] - cfg.elems() * bench.SCAN_FLOPS_PER_ELEM / 0.5e-3 / 1e12) < 1e-2
+    # the published fp32 vector peak of MI355X, not the single-issue rate
+    assert abs(roof["peak"] - 157.29) < 0.01
+    assert abs(roof["frac"] - roof["achieved"] / 157.286) < 1e-3
+    # one wave-step = one step of one 64-channel tile: 4 x 80 x 16384 of them
+    assert abs(roof["cycles_per_wave_step_per_simd"] - 0.5e-3 * 2.4e9 * 1024 / (4 * 80 * 16384)) < 0.1
     assert hbm["algorithmic_bytes"] == alg and cfgd["segments"] == 64
     assert proto["flushed_median_elems_per_s"] > 0
 
