@@ -996,10 +996,11 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     const size_t sz_pbc = align256((size_t)2 * q.blocks_per_row * 2 * BLN * acc);
     const size_t sz_pa = align256((size_t)q.n_groups * BD * N * acc);
     const size_t sz_pd = align256((size_t)q.n_groups * BD * 2 * acc);
+    const size_t sz_pon = align256((size_t)2 * q.blocks_per_row * Bsz * q.n_groups * sizeof(int));
 
     std::lock_guard<std::mutex> lk(g_ws_mu);
     void *ws = nullptr;
-    if ((rc = workspace(dev, s, sz_bc + sz_agg + sz_gin + sz_ragg + sz_gout + sz_pbc + sz_pa + sz_pd, &ws)))
+    if ((rc = workspace(dev, s, sz_bc + sz_agg + sz_gin + sz_ragg + sz_gout + sz_pbc + sz_pa + sz_pd + sz_pon, &ws)))
         return rc;
     char *base = static_cast<char *>(ws);
     p.bc = base;
@@ -1017,6 +1018,8 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     q.part_a = base;
     base += sz_pa;
     q.part_d = base;
+    base += sz_pd;
+    q.part_on = reinterpret_cast<int *>(base);
 
     const int n = (int)N;
     auto bwd = [&](ssm::BwdPass pass) {

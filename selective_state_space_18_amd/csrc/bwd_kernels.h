@@ -440,9 +440,9 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     Acc dDacc = 0, dbacc = 0;
     const int path = kStruct ? 0 : 1;
 
-    // Which waves of the block serve this launch.  A block with none writes
-    // zero dB/dC partials for its rows and leaves; a wave that is not on only
-    // keeps the block's barriers (its LDS slots stay zero).
+    // Which waves of the block serve this launch.  A block with none records
+    // that its dB/dC partial rows are absent and leaves; a wave that is not on
+    // only keeps the block's barriers (its LDS slots stay zero).
     int *on_flags = reinterpret_cast<int *>(&bacc[0][0][0][0]);
     if (lane == 0) on_flags[wave] = wave_on ? 1 : 0;
     __syncthreads();
@@ -450,20 +450,10 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) any_on |= on_flags[w];
     __syncthreads();  // every wave has read the flags
+    if (threadIdx.x == 0)
+        q.part_on[((int64_t)(path * q.blocks_per_row + br) * p.Bsz + b) * q.n_groups + grp] = any_on ? 1 : 0;
+    if (!any_on) return;
     for (int e = lane; e < kT * 2 * N; e += kWave) (&bacc[wave][0][0][0])[e] = 0;
-    if (!any_on) {
-        const int64_t s_begin = (int64_t)grp * q.seg_per_group;
-        const int64_t s_end = s_begin + q.seg_per_group < p.S ? s_begin + q.seg_per_group : p.S;
-        const int64_t t_lo = s_begin * p.seg_len;
-        const int64_t t_hi = s_end * p.seg_len < p.L ? s_end * p.seg_len : p.L;
-        Acc *dst = static_cast<Acc *>(q.part_bc) + ((int64_t)(path * q.blocks_per_row + br) * 2) * BLN;
-        const int64_t cnt = (t_hi - t_lo) * N;
-        for (int64_t e = threadIdx.x; e < 2 * cnt; e += kBlock) {
-            const int64_t v = e / cnt, k = e - v * cnt;
-            dst[v * BLN + (b * p.L + t_lo) * N + k] = 0;
-        }
-        return;
-    }
 
     // inputs of one sub-chunk (steps clamped into it), loaded one sub-chunk
     // ahead as raw bits, one value per register (buf_load_raw)
@@ -753,10 +743,16 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_bc_kernel(BwdParams q) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i >= BLN) return;
     const int n = (int)(i % N);
+    const int64_t bt = i / N;
+    const int64_t b = bt / p.L, t = bt - b * p.L;
+    const int grp = (int)(t / ((int64_t)q.seg_per_group * p.seg_len));
     const Acc *src = static_cast<const Acc *>(q.part_bc);
     const int parts = 2 * q.blocks_per_row;
     Acc sb = 0, sc = 0;
     for (int k = 0; k < parts; ++k) {
+        // part k = (path, block of the row); absent where that block had no
+        // wave of its path
+        if (q.part_on[((int64_t)k * p.Bsz + b) * q.n_groups + grp] == 0) continue;
         sb += src[((int64_t)k * 2) * BLN + i];
         sc += src[((int64_t)k * 2 + 1) * BLN + i];
     }

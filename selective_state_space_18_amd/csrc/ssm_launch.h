@@ -67,6 +67,9 @@ enum class ScanPass { kPrep, kAggregate, kCarry, kOutput };
 //           sums over its channels
 //   part_a  : [groups][B*D][N] Acc -- dA per group of segments (final form)
 //   part_d  : [groups][B*D][2] Acc -- dD and d(delta_bias)
+//   part_on : [2 paths][blocks per row][B][groups] int -- 1 where the block
+//           wrote its part_bc rows, 0 where it had no wave of its path (its
+//           rows are then not written and not read)
 struct BwdParams {
     ScanParams f;
     const void *dy;          // [B,L,D] storage dtype
@@ -74,6 +77,7 @@ struct BwdParams {
     void *dx, *ddelta;       // [B,L,D] storage dtype
     float *dA, *dB, *dC, *dD, *ddelta_bias, *dh_init;
     void *ragg, *gout, *part_bc, *part_a, *part_d;
+    int *part_on;
     int seg_per_group;       // segments one wave processes in turn
     int n_groups;            // ceil(S / seg_per_group)
     int blocks_per_row;      // ceil(tiles_per_b / 4)
