@@ -358,3 +358,29 @@ def test_probe_argument_errors(L):
     assert L.ssm_probe_issue(9, i64(1), i64(1), v(None), None, None, None) == 1
     assert L.ssm_probe_hbm(15, sink, i64(1 << 20), None) == 9
     assert L.ssm_probe_hbm(16, sink, i64(24), None) != 0  # not a multiple of 16
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With no built library the binding raises; there is no fallback path."""
+    code = ("import torch\n"
+            "from selective_state_space_18_amd import ssmscan as ss\n"
+            "try:\n"
+            "    ss.lib()\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n"
+            "else:\n"
+            "    print('loaded')\n"
+            "x = torch.zeros(1, 4, 64, dtype=torch.bfloat16)\n"
+            "try:\n"
+            "    ss.scan_fwd(x, x, torch.zeros(64, 16), torch.zeros(1, 4, 16, dtype=torch.bfloat16),\n"
+            "                torch.zeros(1, 4, 16, dtype=torch.bfloat16), torch.zeros(64))\n"
+            "except Exception as e:\n"
+            "    print('scan raised', type(e).__name__)\n"
+            "else:\n"
+            "    print('scan ran')\n")
+    env = dict(os.environ, SSMSCAN_LIB=str(tmp_path / "absent" / "libssmscan.so"))
+    r = subprocess.run([__import__("sys").executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "raised" in r.stdout and "loaded" not in r.stdout, r.stdout
+    assert "scan raised" in r.stdout and "scan ran" not in r.stdout, r.stdout
