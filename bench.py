@@ -19,7 +19,7 @@ variable-length prefill, the scan with complex A, the backward (structured
 and general A), the general-A path forced on the 2.8B-shaped layer, the
 scalar-decay (state-space duality) layer, and the decode step.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 20]
                     [--no-cpu-baseline] [--no-secondary]
     python bench.py --only scan        # one workload, for profiler runs
                                        # (scan, long, small, packed, options, backward,
@@ -256,30 +256,30 @@ def scan_line(cfg, res, generate, **cfg_extra):
     return rec
 
 
-def bench_options(torch, ss, generate, configs, steps, flusher=None):
+def bench_options(torch, ss, generate, configs, steps, flusher=None, warmup=20):
     """The Mamba-2.8B-shaped layer with the scan options: delta's activation
     fused (softplus(delta + bias) inside the kernels), and the Euler input
     term, against the separate-activation route."""
     out = {}
     fc = configs.FUSED_2P8B_LAYER
-    out["fused_softplus"] = scan_line(fc, bench_scan(torch, ss, generate, fc, steps, 2, flusher),
+    out["fused_softplus"] = scan_line(fc, bench_scan(torch, ss, generate, fc, steps, warmup, flusher),
                                       generate, delta="softplus(raw + bias) in the kernels")
-    ums = bench_unfused_softplus(torch, ss, generate, fc, steps, 2)
+    ums = bench_unfused_softplus(torch, ss, generate, fc, steps, warmup)
     out["separate_softplus_pass"] = {"ms_per_step": round(ums, 5), "value": fc.elems() / (ums * 1e-3),
                                      "note": "torch softplus pass over delta, then the plain scan"}
     ec = configs.MAMBA2P8B_LAYER
-    out["euler_b"] = scan_line(ec, bench_scan(torch, ss, generate, ec, steps, 2, flusher, euler_b=True),
+    out["euler_b"] = scan_line(ec, bench_scan(torch, ss, generate, ec, steps, warmup, flusher, euler_b=True),
                                generate, input_term="Euler: delta * B")
     return out
 
 
-def bench_general_path(torch, ss, generate, cfg, steps, flusher=None):
+def bench_general_path(torch, ss, generate, cfg, steps, flusher=None, warmup=20):
     """The same layer with the structured-A fast path switched off, so every
     state element takes its own exponential (the path a layer with arbitrary
     real A runs)."""
     ss.set_option(ss.SSM_OPT_FORCE_GENERAL, 1)
     try:
-        res = bench_scan(torch, ss, generate, cfg, steps, 2, flusher)
+        res = bench_scan(torch, ss, generate, cfg, steps, warmup, flusher)
     finally:
         ss.set_option(ss.SSM_OPT_FORCE_GENERAL, 0)
     rec = scan_line(cfg, res, generate, A="general path forced (one exp per state element)")
@@ -537,7 +537,7 @@ def bench_decode(torch, ss, generate, cfg, n_tokens, layers=4, flusher=None, lau
         ss.step(t["x"], t["delta"], st["A"], t["B"], t["C"], st["D"], st["h"], y=y)
 
     log(f"[bench] timing {cfg.name}: {n_tokens} steps")
-    ms, kern = profiled_loop(torch, ss, fn, n_tokens, 16)
+    ms, kern = profiled_loop(torch, ss, fn, n_tokens, 400)  # about 20 ms of warmup: the clocks come up
     k_ms = kern["step"]["avg_ms"]
     alg = generate.alg_bytes_step(cfg)
     proto = None
@@ -609,7 +609,7 @@ def bench_complex_decode(torch, ss, generate, cfg, n_tokens, layers=4):
         ss.step_complex(t["x"], t["delta"], st["A"], t["B"], t["C"], st["D"], st["h"], y=y)
 
     log(f"[bench] timing {cfg.name} (complex A): {n_tokens} steps")
-    ms, kern = profiled_loop(torch, ss, fn, n_tokens, 16)
+    ms, kern = profiled_loop(torch, ss, fn, n_tokens, 400)  # about 20 ms of warmup: the clocks come up
     k_ms = kern["step"]["avg_ms"]
     alg = generate.alg_bytes_step_complex(cfg)
     del states, toks, y
@@ -764,7 +764,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
@@ -818,7 +818,7 @@ def main():
         print(json.dumps(rec), flush=True)
         return
     if a.only == "general":
-        rec = bench_general_path(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps)
+        rec = bench_general_path(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps, warmup=a.warmup)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "backward":
@@ -830,7 +830,7 @@ def main():
         print(json.dumps(rec), flush=True)
         return
     if a.only == "options":
-        print(json.dumps(bench_options(torch, ss, generate, configs, a.steps)), flush=True)
+        print(json.dumps(bench_options(torch, ss, generate, configs, a.steps, warmup=a.warmup)), flush=True)
         return
     if a.only == "packed":
         rec = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER, a.steps, a.warmup)
@@ -877,9 +877,12 @@ def main():
         out["hbm"]["practical_peak_gbps"] = practical
         out["hbm"]["frac_of_practical_peak"] = round(out["hbm"]["achieved"] / practical, 4)
         steps5 = max(5, a.steps // 5)
+        # every workload starts right after its input generation, when the
+        # clocks are still coming up: the same warmup as the headline
+        wu = a.warmup
         sec = {}
         lc = configs.LONG_CONTEXT_1M
-        sec["long_context"] = scan_line(lc, bench_scan(torch, ss, generate, lc, max(3, a.steps // 5), 2, flusher),
+        sec["long_context"] = scan_line(lc, bench_scan(torch, ss, generate, lc, max(3, a.steps // 5), wu, flusher),
                                         generate)
         sm = configs.MAMBA130M_LAYER
         sec["mamba130m_layer"] = scan_line(sm, bench_scan(torch, ss, generate, sm, a.steps, a.warmup, flusher),
@@ -888,14 +891,14 @@ def main():
             "random A: every state element takes its own exp (general path); ms_per_step rotates over input "
             "copies whose total exceeds the 256 MB last-level cache, protocol gives the flushed and the "
             "cache-warm (same input, no flush) per-call medians")
-        sec["fused_softplus"] = bench_options(torch, ss, generate, configs, steps5, flusher)
-        sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER, steps5, 2, flusher)
-        sec["complex_A"] = bench_complex(torch, ss, generate, cfg, max(3, a.steps // 10), 1, flusher)
-        sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), 1, flusher)
-        sec["backward_general_A"] = bench_backward(torch, ss, generate, configs.MAMBA130M_LAYER, steps5, 2,
+        sec["fused_softplus"] = bench_options(torch, ss, generate, configs, steps5, flusher, wu)
+        sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER, steps5, wu, flusher)
+        sec["complex_A"] = bench_complex(torch, ss, generate, cfg, max(3, a.steps // 10), wu, flusher)
+        sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), wu, flusher)
+        sec["backward_general_A"] = bench_backward(torch, ss, generate, configs.MAMBA130M_LAYER, steps5, wu,
                                                    flusher)
-        sec["general_A_path"] = bench_general_path(torch, ss, generate, cfg, steps5, flusher)
-        sec["ssd_layer"] = bench_ssd(torch, ss, generate, configs.SSD_LAYER, steps5, 2, flusher)
+        sec["general_A_path"] = bench_general_path(torch, ss, generate, cfg, steps5, flusher, wu)
+        sec["ssd_layer"] = bench_ssd(torch, ss, generate, configs.SSD_LAYER, steps5, wu, flusher)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,
                                      configs.DECODE_256x8192.n_tokens, flusher=flusher,
                                      launch_us=cal["launch_overhead_us"])
