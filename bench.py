@@ -78,6 +78,7 @@ KERNEL_SOURCES = {
     "step": ("step_kernel.hip", "ssm_device.h", "ssm_launch.h"),
     "bwd": ("bwd_kernels.h", "scan_kernels.h", "ssm_device.h", "ssm_launch.h"),
     "ssd": ("ssd_kernels.h", "ssm_device.h", "ssm_launch.h"),
+    "cplx": ("cplx_kernels.h", "scan_kernels.h", "ssm_device.h", "ssm_launch.h"),
 }
 
 
@@ -422,7 +423,8 @@ def bench_complex(torch, ss, generate, cfg, steps, warmup, flusher=None):
            "unit": "elems/s",
            "roofline": {"kernel": "cplx_segment_kernel (output pass)", "bound": "alu",
                         "achieved": round(achieved, 3), "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
-                        "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
+                        "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
+                        **traffic_fields("complex_A_" + cfg.name, "cplx", alg),
                         "avg_ms": round(out_ms, 5),
                         "algorithmic_flops_per_launch": cfg.elems() * CPLX_FLOPS_PER_ELEM,
                         "hbm_frac_kernel": round(alg / (out_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -621,7 +623,8 @@ def bench_complex_decode(torch, ss, generate, cfg, n_tokens, layers=4):
                 "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": alg},
         "roofline": {"kernel": "cplx_step_kernel", "bound": "hbm",
                      "achieved": round(alg / (k_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     **traffic_fields("complex_" + cfg.name, "cplx", alg),
                      "avg_ms": round(k_ms, 5)},
         "state_layers_cycled": layers,
     }
