@@ -329,6 +329,41 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias,
                  unsigned flags, void *stream);
 
 /*
+ * Backward of the packed variable-length scan (ssm_scan_varlen_fwd, or
+ * ssm_scan_fused_fwd with cu_seqlens): sequences concatenated along time,
+ * each with its own initial state, as in training on packed batches.  The
+ * chain rule on the recurrence ("Mamba SSM Nedir?", section "Ayrik Zamana
+ * Gecis") applied to every sequence alone: the gradients are those of
+ * ssm_scan_bwd with Bsz = 1 on that sequence's steps and state rows, with dA,
+ * dD and ddelta_bias summed over the sequences.  At a sequence start the
+ * adjoint leaving the step is that sequence's dh_init, and the previous
+ * sequence's last state receives only its own outputs' and dh_final's share.
+ *
+ *   x, delta, dy, dx, ddelta : [L][Dm]   dtype
+ *   B, C                     : [L][N]    dtype
+ *   dB, dC                   : [L][N]    fp32
+ *   cu_seqlens               : [nseq+1] int64, device memory, rules as in
+ *                              ssm_scan_varlen_fwd (read on the device, not
+ *                              validated; values that break the rules give
+ *                              unspecified results but every access stays
+ *                              inside the buffers)
+ *   h_init, dh_final, dh_init: [nseq][Dm][N] fp32 or NULL (h_init, dh_final:
+ *                              zero).  An empty sequence gets dh_init =
+ *                              dh_final (its final state is its initial one).
+ *   A, D, delta_bias, dA, dD, ddelta_bias, dtype, flags: as in ssm_scan_bwd.
+ * nseq = 0 is allowed only with L = 0.  Overlap rules, scratch (with Bsz = 1,
+ * plus 2 S ints) and the segment size limit as in ssm_scan_bwd.
+ */
+int ssm_scan_varlen_bwd(const void *x, const void *delta, const float *delta_bias,
+                        const float *A, const void *B, const void *C, const float *D,
+                        const int64_t *cu_seqlens, int64_t nseq, const float *h_init,
+                        const void *dy, const float *dh_final,
+                        void *dx, void *ddelta, float *ddelta_bias, float *dA,
+                        float *dB, float *dC, float *dD, float *dh_init,
+                        int64_t L, int64_t Dm, int64_t N, int dtype,
+                        unsigned flags, void *stream);
+
+/*
  * One recurrent decode step on a resident state, updated in place
  * ("Mamba SSM Nedir?", section "Karmasiklik Karsilastirmasi": inference
  * updates a fixed-size state per token).  bf16 I/O:

@@ -872,7 +872,9 @@ BwdPlan make_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int dtype, int cus) {
 int bwd_impl(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
              const void *C, const float *D, const float *h_init, const void *dy, const float *dh_final, void *dx,
              void *ddelta, float *ddelta_bias, float *dA, float *dB, float *dC, float *dD, float *dh_init,
-             int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, unsigned flags, void *stream) {
+             int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, unsigned flags, void *stream,
+             const int64_t *cu = nullptr, int64_t nseq = 0) {
+    const bool varlen = cu != nullptr;
     if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
     if (flags & ~kKnownFlags) return fail(SSM_ERR_BAD_OPTION, "unknown flag bits 0x%x", flags & ~kKnownFlags);
     if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
@@ -884,6 +886,9 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
         !mul_ok(Bsz, Dm, &BD) || !mul_ok(BD, N, &BDN) || BD > INT32_MAX / 2 || Bsz * ((Dm + 63) / 64) > INT32_MAX / 8)
         return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
                     (long long)L, (long long)Dm, (long long)N);
+    // state rows: one per batch row, or one per packed sequence
+    int64_t RDN = BDN;
+    if (varlen && !mul_ok(nseq, DN, &RDN)) return fail(SSM_ERR_BAD_DIM, "nseq * Dm * N overflows");
     const int64_t es = dtype_size(dtype);
     // The backward addresses a whole fixed-length segment through 32-bit
     // buffer offsets: its span must stay below 1 GiB.
@@ -898,9 +903,10 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
                       {C, BLN, es, "C"},
                       {D, Dm, 4, "D"},
                       {delta_bias, delta_bias ? Dm : 0, 4, "delta_bias"},
-                      {h_init, h_init ? BDN : 0, 4, "h_init"},
+                      {h_init, h_init ? RDN : 0, 4, "h_init"},
                       {dy, BLD, es, "dy"},
-                      {dh_final, dh_final ? BDN : 0, 4, "dh_final"}};
+                      {dh_final, dh_final ? RDN : 0, 4, "dh_final"},
+                      {cu, varlen ? nseq + 1 : 0, 8, "cu_seqlens"}};
     const Arg out[] = {{dx, BLD, es, "dx"},
                        {ddelta, BLD, es, "ddelta"},
                        {ddelta_bias, ddelta_bias ? Dm : 0, 4, "ddelta_bias"},
@@ -908,8 +914,9 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
                        {dB, BLN, 4, "dB"},
                        {dC, BLN, 4, "dC"},
                        {dD, Dm, 4, "dD"},
-                       {dh_init, dh_init ? BDN : 0, 4, "dh_init"}};
-    constexpr int nin = 10, nout = 8;
+                       {dh_init, dh_init ? RDN : 0, 4, "dh_init"}};
+    const int nin = varlen ? 11 : 10;
+    constexpr int nout = 8;
     int rc;
     if ((rc = check_args(in, nin)) || (rc = check_args(out, nout))) return rc;
     for (int i = 0; i < nout; ++i) {
@@ -926,9 +933,10 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
             if (r == hipSuccess) r = ssm::launch_fill(dD, Dm, 0.f, s);
             if (r == hipSuccess) r = ssm::launch_fill(ddelta_bias, ddelta_bias ? Dm : 0, 0.f, s);
             if (r == hipSuccess && dh_init != nullptr) {
+                // (packed: every sequence is empty, or Dm is 0)
                 ssm::ScanParams z;
                 std::memset(&z, 0, sizeof z);
-                z.Bsz = Bsz;
+                z.Bsz = varlen ? nseq : Bsz;
                 z.Dm = Dm;
                 z.h_init = dh_final;
                 z.h_final = dh_init;
@@ -960,6 +968,8 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     p.Dm = Dm;
     p.waves_per_block = kWavesPerBlock;
     p.force_general = g_opt_force_general.load() ? 1 : 0;
+    p.cu = cu;
+    p.nseq = nseq;
     p.delta_bias = delta_bias;
     p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
     p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
@@ -997,10 +1007,13 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     const size_t sz_pa = align256((size_t)q.n_groups * BD * N * acc);
     const size_t sz_pd = align256((size_t)q.n_groups * BD * 2 * acc);
     const size_t sz_pon = align256((size_t)2 * q.blocks_per_row * Bsz * q.n_groups * sizeof(int));
+    const size_t sz_res = varlen ? align256(S * sizeof(int)) : 0;  // each of the two reset flag arrays
 
     std::lock_guard<std::mutex> lk(g_ws_mu);
     void *ws = nullptr;
-    if ((rc = workspace(dev, s, sz_bc + sz_agg + sz_gin + sz_ragg + sz_gout + sz_pbc + sz_pa + sz_pd + sz_pon, &ws)))
+    if ((rc = workspace(dev, s,
+                        sz_bc + sz_agg + sz_gin + sz_ragg + sz_gout + sz_pbc + sz_pa + sz_pd + sz_pon + 2 * sz_res,
+                        &ws)))
         return rc;
     char *base = static_cast<char *>(ws);
     p.bc = base;
@@ -1020,10 +1033,16 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     q.part_d = base;
     base += sz_pd;
     q.part_on = reinterpret_cast<int *>(base);
+    base += sz_pon;
+    p.seg_reset = varlen ? reinterpret_cast<int *>(base) : nullptr;
+    base += sz_res;
+    q.rseg_reset = varlen ? reinterpret_cast<int *>(base) : nullptr;
 
     const int n = (int)N;
     auto bwd = [&](ssm::BwdPass pass) {
-        return dtype == SSM_F32 ? ssm::bwd_pass_f32(pass, q, n, s) : ssm::bwd_pass_bf16(pass, q, n, s);
+        if (dtype == SSM_F32)
+            return varlen ? ssm::bwd_pass_f32_packed(pass, q, n, s) : ssm::bwd_pass_f32(pass, q, n, s);
+        return varlen ? ssm::bwd_pass_bf16_packed(pass, q, n, s) : ssm::bwd_pass_bf16(pass, q, n, s);
     };
     if ((e = timed(SSM_K_BC_PREP, s, [&] { return ssm::launch_bc_prep(p, n, dtype, s); })) != hipSuccess)
         return hip_fail(e, "B/C conversion launch");
@@ -1042,6 +1061,18 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
         return hip_fail(e, "backward main launch");
     if ((e = timed(SSM_K_BWD_REDUCE, s, [&] { return bwd(ssm::BwdPass::kReduce); })) != hipSuccess)
         return hip_fail(e, "backward reduction launch");
+    if (varlen && dh_init != nullptr) {
+        // empty sequences: dh_init = dh_final (their final state is their initial one)
+        ssm::ScanParams z;
+        std::memset(&z, 0, sizeof z);
+        z.Dm = Dm;
+        z.cu = cu;
+        z.nseq = nseq;
+        z.h_init = dh_final;
+        z.h_final = dh_init;
+        if ((e = timed(SSM_K_STATE_INIT, s, [&] { return ssm::launch_varlen_empty(z, n, s); })) != hipSuccess)
+            return hip_fail(e, "empty-sequence launch");
+    }
     return ok();
 }
 
@@ -1111,6 +1142,18 @@ int ssm_scan_bwd(const void *x, const void *delta, const float *delta_bias, cons
                  void *stream) {
     return bwd_impl(x, delta, delta_bias, A, B, C, D, h_init, dy, dh_final, dx, ddelta, ddelta_bias, dA, dB, dC,
                     dD, dh_init, Bsz, L, Dm, N, dtype, flags, stream);
+}
+
+int ssm_scan_varlen_bwd(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+                        const void *C, const float *D, const int64_t *cu_seqlens, int64_t nseq, const float *h_init,
+                        const void *dy, const float *dh_final, void *dx, void *ddelta, float *ddelta_bias,
+                        float *dA, float *dB, float *dC, float *dD, float *dh_init, int64_t L, int64_t Dm,
+                        int64_t N, int dtype, unsigned flags, void *stream) {
+    if (nseq < 0) return fail(SSM_ERR_BAD_DIM, "nseq = %lld < 0", (long long)nseq);
+    if (nseq == 0 && L > 0) return fail(SSM_ERR_BAD_DIM, "nseq = 0 but L = %lld", (long long)L);
+    if (cu_seqlens == nullptr) return fail(SSM_ERR_NULLPTR, "cu_seqlens is NULL");
+    return bwd_impl(x, delta, delta_bias, A, B, C, D, h_init, dy, dh_final, dx, ddelta, ddelta_bias, dA, dB, dC,
+                    dD, dh_init, 1, L, Dm, N, dtype, flags, stream, cu_seqlens, nseq);
 }
 
 int ssm_scan_complex_fwd(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,

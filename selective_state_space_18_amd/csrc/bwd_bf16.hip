@@ -4,7 +4,7 @@
 namespace ssm {
 
 hipError_t bwd_pass_bf16(BwdPass pass, const BwdParams &q, int N, hipStream_t s) {
-    return bwd_pass<bf16>(pass, q, N, s);
+    return bwd_pass<bf16, false>(pass, q, N, s);
 }
 
 }  // namespace ssm

@@ -4,7 +4,7 @@
 namespace ssm {
 
 hipError_t bwd_pass_f32(BwdPass pass, const BwdParams &q, int N, hipStream_t s) {
-    return bwd_pass<float>(pass, q, N, s);
+    return bwd_pass<float, false>(pass, q, N, s);
 }
 
 }  // namespace ssm

@@ -1,5 +1,5 @@
 // Backward of the selective scan for gfx950: templates shared by the per-dtype
-// translation units (bwd_bf16.hip, bwd_f32.hip).
+// translation units (bwd_bf16.hip, bwd_f32.hip and their _packed variants).
 //
 // Reverse-mode derivative of the recurrence the forward computes ("Mamba SSM
 // Nedir?" page, section "Ayrik Zamana Gecis"; training runs the same scan,
@@ -71,9 +71,67 @@ __device__ __forceinline__ Acc zoh_dphi(Acc z, Acc E) {
 }
 
 // ---------------------------------------------------------------------------
-// Reverse aggregate: segments 1..S-1, adjoint from zero at the segment end.
+// Packed sequences (kVarlen: ScanParams::cu set, one batch row).  Step t
+// starts a sequence when t == cu[k] for some k < nseq.  There the forward
+// state restarts from h_init[k]; in reverse, the adjoint leaving that step is
+// dL/dh_init[k], and the last state of the sequence before it is reached only
+// through its own outputs and its dh_final row.
 
-template <typename T, int N, bool kStruct, bool kEuler, bool kPre>
+// Bit i set when step t0 + i (i < n <= 32) starts a sequence.  Wave-uniform.
+__device__ __forceinline__ uint32_t seq_start_mask(const_row_ptr<int64_t> cu, int64_t nseq, int64_t t0, int n) {
+    const int64_t k = find_seq(cu, nseq, t0);
+    uint32_t m = cu[k] == t0 ? 1u : 0u;
+    for (int64_t j = k + 1; j < nseq; ++j) {
+        const int64_t c = cu[j];
+        if (c >= t0 + n) break;
+        if (c > t0) m |= 1u << (int)(c - t0);
+    }
+    return m;
+}
+
+// The sequence holding step t - 1, for a start t > 0 of sequence k_t
+// (find_seq(t)): the last one before k_t that is not empty.
+__device__ __forceinline__ int64_t seq_before(const_row_ptr<int64_t> cu, int64_t k_t, int64_t t) {
+    int64_t k = k_t - 1;
+    while (k > 0 && cu[k] >= t) --k;
+    return k < 0 ? 0 : k;
+}
+
+// Scaled state g_n = (n+1) h_n of row k of a [rows][Dm][N] fp32 array, zero
+// when the array is absent.
+template <typename Acc, int N>
+__device__ __forceinline__ void load_scaled_state(const float *h, int64_t k, int64_t Dm, int64_t d, Acc (&g)[N]) {
+    if (h != nullptr) {
+        const float *r = h + (k * Dm + d) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) g[n] = (Acc)r[n] * (Acc)(n + 1);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) g[n] = 0;
+    }
+}
+
+// Scaled adjoint dL/dg_n = dL/dh_n / (n+1) of row k, zero when absent.
+template <typename Acc, int N>
+__device__ __forceinline__ void load_scaled_adjoint(const float *dh, int64_t k, int64_t Dm, int64_t d,
+                                                    Acc (&nu)[N]) {
+    if (dh != nullptr) {
+        const float *r = dh + (k * Dm + d) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) nu[n] = (Acc)r[n] / (Acc)(n + 1);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) nu[n] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse aggregate: segments 1..S-1, adjoint from zero at the segment end.
+// Packed sequences: past a sequence start the adjoint restarts from the
+// previous sequence's dh_final row, and the segment is flagged so that the
+// reverse carry drops what enters it from the right.
+
+template <typename T, int N, bool kStruct, bool kEuler, bool kPre, bool kVarlen>
 __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
     typedef typename AccOf<T>::type Acc;
     const ScanParams &p = q.f;
@@ -115,6 +173,11 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
 #pragma unroll
     for (int n = 0; n < N; ++n) nu[n] = 0;
     Acc lam = 0;
+    uint32_t smask = 0;
+    if constexpr (kVarlen) {
+        smask = seq_start_mask((const_row_ptr<int64_t>)p.cu, p.nseq, t0, nsteps);
+        if (tile == 0 && lane == 0) q.rseg_reset[s] = smask != 0 ? 1 : 0;
+    }
     constexpr int G = kPrefetch;
     uint32_t dl_c[G], dy_c[G], dl_n[G], dy_n[G];  // raw bits, one value per register (buf_load_raw)
     auto load = [&](int tb, uint32_t(&dl)[G], uint32_t(&dyv)[G]) {
@@ -174,6 +237,14 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
                         nu[n] = fma_(E, mu, mu);
                     }
                 }
+                if constexpr (kVarlen) {
+                    if ((smask >> t) & 1u) {
+                        const const_row_ptr<int64_t> cu = (const_row_ptr<int64_t>)p.cu;
+                        const int64_t ts = t0 + t;  // >= seg_len: a sequence ends at ts - 1
+                        const int64_t kp = seq_before(cu, find_seq(cu, p.nseq, ts), ts);
+                        load_scaled_adjoint(q.dh_final, kp, p.Dm, d, nu);
+                    }
+                }
             }
         }
 #pragma unroll
@@ -190,9 +261,11 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
 }
 
 // Reverse carry: one thread per (state n, channel).  The adjoint entering the
-// last segment from the right is dL/dh_final (scaled units); segment s-1
-// receives exp(A_n * sum(delta over s)) times what enters s, plus s's summary.
-template <typename Acc, int N>
+// last segment from the right is dL/dh_final (scaled units; packed sequences:
+// the row of the sequence holding the last step); segment s-1 receives
+// exp(A_n * sum(delta over s)) times what enters s, plus s's summary -- only
+// the summary where a sequence starts inside s.
+template <typename Acc, int N, bool kVarlen>
 __global__ __launch_bounds__(kBlock) void bwd_carry_kernel(BwdParams q) {
     const ScanParams &p = q.f;
     const int64_t BD = p.Bsz * p.Dm;
@@ -203,7 +276,13 @@ __global__ __launch_bounds__(kBlock) void bwd_carry_kernel(BwdParams q) {
     const int64_t d = ch % p.Dm;
     constexpr Acc unit = sizeof(Acc) == 4 ? (Acc)kLog2e : (Acc)1;
     const Acc a = (Acc)p.A[d * N + n] * unit;
-    Acc nu = q.dh_final ? (Acc)q.dh_final[ch * N + n] / (Acc)(n + 1) : (Acc)0;
+    Acc nu;
+    if constexpr (kVarlen) {
+        const int64_t k = find_seq((const_row_ptr<int64_t>)p.cu, p.nseq, p.L - 1);
+        nu = q.dh_final ? (Acc)q.dh_final[(k * p.Dm + d) * N + n] / (Acc)(n + 1) : (Acc)0;
+    } else {
+        nu = q.dh_final ? (Acc)q.dh_final[ch * N + n] / (Acc)(n + 1) : (Acc)0;
+    }
     const Acc *__restrict__ ragg = static_cast<const Acc *>(q.ragg);
     Acc *__restrict__ out = static_cast<Acc *>(q.gout) + (int64_t)n * BD + ch;
     const int64_t sa = (int64_t)(N + 1) * BD, sg = (int64_t)N * BD;
@@ -222,11 +301,22 @@ __global__ __launch_bounds__(kBlock) void bwd_carry_kernel(BwdParams q) {
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) lc[k] = exp_units(a * lc[k]);
+        // a sequence start inside s cuts off what enters s from the right
+        // (selected, not multiplied by 0: an inf or NaN adjoint of a later
+        // sequence cannot reach an earlier one)
+        bool cut[kBatch];
+        if constexpr (kVarlen) {
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) cut[k] = s1 - k >= 1 && q.rseg_reset[s1 - k] != 0;
+        }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int s = s1 - k;
             if (s >= 1) {
-                nu = fma_(lc[k], nu, gc[k]);
+                if constexpr (kVarlen)
+                    nu = cut[k] ? gc[k] : fma_(lc[k], nu, gc[k]);
+                else
+                    nu = fma_(lc[k], nu, gc[k]);
                 if ((s - 1) % spg == spg - 1) out[(int64_t)((s - 1) / spg) * sg] = nu;
             }
         }
@@ -357,7 +447,10 @@ __device__ __forceinline__ int wave_reduce_scatter(double (&v)[N], int lane) {
     return idx;
 }
 
-template <typename T, int N, bool kStruct, bool kEuler, bool kPre>
+// Packed sequences (kVarlen): the recomputed state restarts from h_init[k] at
+// the start of sequence k; in reverse, the adjoint leaving that step is stored
+// as dh_init[k] and restarts from the previous sequence's dh_final row.
+template <typename T, int N, bool kStruct, bool kEuler, bool kPre, bool kVarlen>
 __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
     typedef typename AccOf<T>::type Acc;
     constexpr int kC = BwdShape<Acc>::kC;
@@ -431,6 +524,27 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
         if constexpr (!kEuler) {
 #pragma unroll
             for (int n = 0; n < N; ++n) g[n] *= kStruct ? inva : to_g[n];
+        }
+    };
+    // Packed sequences: the state restarts before every step that starts a
+    // sequence, except step t_from (g is already the state before it).
+    // smask: the sequence starts of the segment that begins at step t0.
+    const const_row_ptr<int64_t> cu = (const_row_ptr<int64_t>)p.cu;
+    auto restart = [&](Acc(&g)[N], int64_t t) { load_scaled_state(p.h_init, find_seq(cu, p.nseq, t), p.Dm, d, g); };
+    auto advance_v = [&](Acc(&g)[N], int64_t t0, uint32_t smask, int64_t t_from, int count) {
+        if constexpr (!kVarlen) {
+            advance(g, t_from, count);
+        } else {
+            int o = (int)(t_from - t0);
+            const int end = o + count;
+            while (o < end) {
+                const uint32_t later = smask & ~((2u << o) - 1u);  // starts after offset o
+                int nx = later != 0 ? (int)__builtin_ctz(later) : end;
+                if (nx > end) nx = end;
+                advance(g, t0 + o, nx - o);
+                if (nx < end) restart(g, t0 + nx);
+                o = nx;
+            }
         }
     };
 
@@ -528,10 +642,15 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
         const int64_t t0 = (int64_t)s * p.seg_len;
         const int nseg = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
         const int nck = (nseg + kK - 1) / kK;
+        const uint32_t smask = kVarlen ? seq_start_mask(cu, p.nseq, t0, nseg) : 0u;
 
-        // checkpoints: the state before steps t0, t0 + kK, ...
+        // checkpoints: the state before steps t0, t0 + kK, ... (restarted
+        // where a sequence starts there)
         Acc g[N];
-        if (s == 0) {
+        if (kVarlen && s == 0) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) g[n] = 0;
+        } else if (s == 0) {
 #pragma unroll
             for (int n = 0; n < N; ++n) g[n] = p.h_init ? (Acc)p.h_init[ch * N + n] * (Acc)(n + 1) : (Acc)0;
         } else {
@@ -540,9 +659,12 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
             for (int n = 0; n < N; ++n) g[n] = gin[((int64_t)s * N + n) * BD + ch];
         }
         for (int j = 0; j < nck; ++j) {
+            if constexpr (kVarlen) {
+                if ((smask >> (j * kK)) & 1u) restart(g, t0 + (int64_t)j * kK);
+            }
 #pragma unroll
             for (int n = 0; n < N; ++n) ck[wave][j][n][lane] = g[n];
-            if (j + 1 < nck) advance(g, t0 + (int64_t)j * kK, kK);
+            if (j + 1 < nck) advance_v(g, t0, smask, t0 + (int64_t)j * kK, kK);
         }
         __builtin_amdgcn_wave_barrier();
 
@@ -563,7 +685,7 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
             Acc gp[N];
 #pragma unroll
             for (int n = 0; n < N; ++n) gp[n] = ck[wave][j][n][lane];
-            advance(gp, t0 + (int64_t)j * kK, u * kC - j * kK);
+            advance_v(gp, t0, smask, t0 + (int64_t)j * kK, u * kC - j * kK);
 
             const int64_t off = (b * p.L + ta) * p.Dm + d0;
             const __amdgpu_buffer_rsrc_t rdx = make_rsrc(static_cast<const T *>(q.dx) + off, nc * row);
@@ -591,6 +713,9 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
 #pragma unroll
                 for (int i = 0; i < kC; ++i) {
                     if (i < nc) {
+                        if constexpr (kVarlen) {
+                            if ((smask >> (u * kC + i)) & 1u) restart(gc, ta + i);
+                        }
                         Acc rw[2 * N];
                         load_row<N>(rw, bcp + (int64_t)i * (2 * N));
                         (void)scan_step<N, kStruct, true, kEuler>(cc, rw, xs[i], ds[i], gc);
@@ -609,6 +734,16 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                     const Acc xv = xs[i], dv = ds[i], gy = gys[i];
                     Acc vB[N], vC[N];
                     Acc acc_x = 0, acc_d = 0;
+                    // a sequence starts here: the state before the step is its h_init
+                    const bool rs = kVarlen && ((smask >> (u * kC + i)) & 1u) != 0;
+                    int64_t ks = 0;
+                    Acc hs[N];
+                    if constexpr (kVarlen) {
+                        if (rs) {
+                            ks = find_seq(cu, p.nseq, ta + i);
+                            load_scaled_state(p.h_init, ks, p.Dm, d, hs);
+                        }
+                    }
                     if constexpr (kStruct) {
                         Acc r;
                         const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
@@ -618,6 +753,7 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                         for (int n = 0; n < N; ++n) {
                             Acc gprev = gp[n];
                             if (i > 0) gprev = gs[i > 0 ? i - 1 : 0][n];
+                            if constexpr (kVarlen) gprev = rs ? hs[n] : gprev;
                             const Acc mu = fma_(rw[N + n], gy, nu[n]);
                             const Acc pp = E * mu;
                             const Acc nup = mu + pp;
@@ -651,6 +787,7 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                         for (int n = 0; n < N; ++n) {
                             Acc gprev = gp[n];
                             if (i > 0) gprev = gs[i > 0 ? i - 1 : 0][n];
+                            if constexpr (kVarlen) gprev = rs ? hs[n] : gprev;
                             Acc e;
                             const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
                             const Acc mu = fma_(rw[N + n], gy, nu[n]);
@@ -703,6 +840,19 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                         bacc[wave][u * kC + i][0][idx] = vB[0];
                         bacc[wave][u * kC + i][1][idx] = vC[0];
                     }
+                    if constexpr (kVarlen) {
+                        if (rs) {
+                            // nu is now dL/dg before the sequence's first step
+                            if (live && q.dh_init != nullptr) {
+                                float *dh = q.dh_init + (ks * p.Dm + d) * N;
+#pragma unroll
+                                for (int n = 0; n < N; ++n) dh[n] = (float)(nu[n] * (Acc)(n + 1));
+                            }
+                            const int64_t ts = ta + i;
+                            if (ts > 0)
+                                load_scaled_adjoint(q.dh_final, seq_before(cu, ks, ts), p.Dm, d, nu);
+                        }
+                    }
                 }
             }
             if (u > 0) cur = nxt;
@@ -710,7 +860,7 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
         __syncthreads();  // every wave's partials of the segment are in
         write_segment_sums(t0, nseg);
         __syncthreads();  // ... and summed before the next segment's are written
-        if (s == 0 && live && q.dh_init != nullptr) {
+        if (!kVarlen && s == 0 && live && q.dh_init != nullptr) {
 #pragma unroll
             for (int n = 0; n < N; ++n) q.dh_init[ch * N + n] = (float)(nu[n] * (Acc)(n + 1));
         }
@@ -790,39 +940,39 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_ad_kernel(BwdParams q) {
     dst[d] = (float)sacc;
 }
 
-template <typename T, int N, bool kStruct, bool kEuler, bool kPre>
+template <typename T, int N, bool kStruct, bool kEuler, bool kPre, bool kVarlen>
 void bwd_launch_variant(BwdPass pass, const BwdParams &q, hipStream_t s) {
     const ScanParams &p = q.f;
     if (pass == BwdPass::kAggregate) {
         const int bps = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
         if (p.S <= 1 || bps == 0) return;
-        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, kStruct, kEuler, kPre>), dim3((unsigned)bps * (p.S - 1)),
+        hipLaunchKernelGGL((bwd_aggregate_kernel<T, N, kStruct, kEuler, kPre, kVarlen>), dim3((unsigned)bps * (p.S - 1)),
                            dim3(kBlock), 0, s, q);
     } else {
         const unsigned grid = (unsigned)(q.n_groups * p.Bsz * q.blocks_per_row);
         if (grid == 0) return;
-        hipLaunchKernelGGL((bwd_main_kernel<T, N, kStruct, kEuler, kPre>), dim3(grid), dim3(kBlock), 0, s, q);
+        hipLaunchKernelGGL((bwd_main_kernel<T, N, kStruct, kEuler, kPre, kVarlen>), dim3(grid), dim3(kBlock), 0, s, q);
     }
 }
 
-template <typename T, int N, bool kStruct>
+template <typename T, int N, bool kStruct, bool kVarlen>
 void bwd_launch_path(BwdPass pass, const BwdParams &q, hipStream_t s) {
     const ScanParams &p = q.f;
     const bool pre = p.delta_bias != nullptr || p.delta_softplus != 0;
     if (p.euler_b) {
         if (pre)
-            bwd_launch_variant<T, N, kStruct, true, true>(pass, q, s);
+            bwd_launch_variant<T, N, kStruct, true, true, kVarlen>(pass, q, s);
         else
-            bwd_launch_variant<T, N, kStruct, true, false>(pass, q, s);
+            bwd_launch_variant<T, N, kStruct, true, false, kVarlen>(pass, q, s);
     } else {
         if (pre)
-            bwd_launch_variant<T, N, kStruct, false, true>(pass, q, s);
+            bwd_launch_variant<T, N, kStruct, false, true, kVarlen>(pass, q, s);
         else
-            bwd_launch_variant<T, N, kStruct, false, false>(pass, q, s);
+            bwd_launch_variant<T, N, kStruct, false, false, kVarlen>(pass, q, s);
     }
 }
 
-template <typename T, int N>
+template <typename T, int N, bool kVarlen>
 hipError_t bwd_pass_n(BwdPass pass, const BwdParams &q, hipStream_t s) {
     typedef typename AccOf<T>::type Acc;
     const ScanParams &p = q.f;
@@ -830,13 +980,13 @@ hipError_t bwd_pass_n(BwdPass pass, const BwdParams &q, hipStream_t s) {
         case BwdPass::kAggregate:
         case BwdPass::kMain:
             // both A paths; each wave works in exactly one of them
-            bwd_launch_path<T, N, true>(pass, q, s);
-            bwd_launch_path<T, N, false>(pass, q, s);
+            bwd_launch_path<T, N, true, kVarlen>(pass, q, s);
+            bwd_launch_path<T, N, false, kVarlen>(pass, q, s);
             break;
         case BwdPass::kCarry: {
             const int64_t work = p.Bsz * p.Dm * N;
             if (work == 0) return hipSuccess;
-            hipLaunchKernelGGL((bwd_carry_kernel<Acc, N>), dim3((unsigned)((work + kBlock - 1) / kBlock)),
+            hipLaunchKernelGGL((bwd_carry_kernel<Acc, N, kVarlen>), dim3((unsigned)((work + kBlock - 1) / kBlock)),
                                dim3(kBlock), 0, s, q);
             break;
         }
@@ -855,14 +1005,15 @@ hipError_t bwd_pass_n(BwdPass pass, const BwdParams &q, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T>
+// kVarlen must match q.f.cu != nullptr.
+template <typename T, bool kVarlen>
 hipError_t bwd_pass(BwdPass pass, const BwdParams &q, int N, hipStream_t s) {
     switch (N) {
-        case 1: return bwd_pass_n<T, 1>(pass, q, s);
-        case 2: return bwd_pass_n<T, 2>(pass, q, s);
-        case 4: return bwd_pass_n<T, 4>(pass, q, s);
-        case 8: return bwd_pass_n<T, 8>(pass, q, s);
-        case 16: return bwd_pass_n<T, 16>(pass, q, s);
+        case 1: return bwd_pass_n<T, 1, kVarlen>(pass, q, s);
+        case 2: return bwd_pass_n<T, 2, kVarlen>(pass, q, s);
+        case 4: return bwd_pass_n<T, 4, kVarlen>(pass, q, s);
+        case 8: return bwd_pass_n<T, 8, kVarlen>(pass, q, s);
+        case 16: return bwd_pass_n<T, 16, kVarlen>(pass, q, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -70,6 +70,10 @@ enum class ScanPass { kPrep, kAggregate, kCarry, kOutput };
 //   part_on : [2 paths][blocks per row][B][groups] int -- 1 where the block
 //           wrote its part_bc rows, 0 where it had no wave of its path (its
 //           rows are then not written and not read)
+// Packed sequences (f.cu set, B = 1): f.h_init, dh_final and dh_init are
+// [nseq][D][N]; f.seg_reset serves the forward carry and
+//   rseg_reset : [S] int -- 1 where a sequence starts inside segment s >= 1
+//           (the reverse carry takes that segment's summary alone)
 struct BwdParams {
     ScanParams f;
     const void *dy;          // [B,L,D] storage dtype
@@ -78,6 +82,7 @@ struct BwdParams {
     float *dA, *dB, *dC, *dD, *ddelta_bias, *dh_init;
     void *ragg, *gout, *part_bc, *part_a, *part_d;
     int *part_on;
+    int *rseg_reset;
     int seg_per_group;       // segments one wave processes in turn
     int n_groups;            // ceil(S / seg_per_group)
     int blocks_per_row;      // ceil(tiles_per_b / 4)
@@ -117,8 +122,12 @@ hipError_t ssd_pass_bf16(SsdPass pass, const SsdParams &p, int N, hipStream_t s)
 
 // Segment length the backward kernels are built for (the plan must use it).
 int bwd_segment_len(int dtype);
+// Per storage type and layout, one translation unit each: bwd_f32.hip,
+// bwd_f32_packed.hip, bwd_bf16.hip, bwd_bf16_packed.hip.
 hipError_t bwd_pass_f32(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
+hipError_t bwd_pass_f32_packed(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
 hipError_t bwd_pass_bf16(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
+hipError_t bwd_pass_bf16_packed(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
 
 // Bytes per element of the scan's arithmetic type for a storage dtype.
 size_t scan_acc_bytes(int dtype);

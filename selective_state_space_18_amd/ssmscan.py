@@ -38,7 +38,7 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_st
            "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
            "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd", "ssm_scan_complex_fwd",
            "ssm_step_complex", "ssm_scan_ssd_fwd", "ssm_scan_bwd_plan", "ssm_probe_issue",
-           "ssm_scan_fwd_noalloc", "ssm_probe_hbm")
+           "ssm_scan_fwd_noalloc", "ssm_probe_hbm", "ssm_scan_varlen_bwd")
 
 
 class SSMError(RuntimeError):
@@ -76,6 +76,9 @@ def lib():
     L.ssm_step_complex.restype = ctypes.c_int
     L.ssm_scan_bwd.argtypes = [_vp] * 18 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_scan_bwd.restype = ctypes.c_int
+    L.ssm_scan_varlen_bwd.argtypes = [_vp] * 8 + [_i64] + [_vp] * 11 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint,
+                                                                                    _vp]
+    L.ssm_scan_varlen_bwd.restype = ctypes.c_int
     L.ssm_step_fused.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_step_fused.restype = ctypes.c_int
     L.ssm_step.argtypes = [_vp] * 8 + [_i64] * 3 + [_vp]
@@ -444,6 +447,56 @@ def scan_bwd(x, delta, A, B, C, D, dy, h_init=None, dh_final=None, delta_bias=No
                                 _ptr(o["dD"]), _ptr(o.get("dh_init")), Bsz, L, Dm, N, code,
                                 _flags(delta_softplus, euler_b), _stream(dev))
     _check(rc, "ssm_scan_bwd")
+    return o
+
+
+def scan_varlen_bwd(x, delta, A, B, C, D, cu_seqlens, dy, h_init=None, dh_final=None, delta_bias=None,
+                    delta_softplus=False, euler_b=False, want_dh_init=True, out=None):
+    """ssm_scan_varlen_bwd: gradients of the packed variable-length scan.
+
+    Forward inputs as in scan_varlen_fwd (x, delta [L, Dm]; B, C [L, N];
+    cu_seqlens [nseq+1] int64; h_init [nseq, Dm, N] or None; same options),
+    dy [L, Dm] in x's dtype and optional dh_final [nseq, Dm, N] fp32.  Returns
+    a dict with dx, ddelta [L, Dm] (x's dtype), dA [Dm, N], dB, dC [L, N], dD
+    [Dm] (fp32), dh_init [nseq, Dm, N] (if want_dh_init) and ddelta_bias [Dm]
+    (if delta_bias is given).  `out` may supply any of these tensors.
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    L, Dm = x.shape
+    N = A.shape[1]
+    nseq = cu_seqlens.shape[0] - 1
+    dt = x.dtype
+    code = _dtype_code(x)
+    for t, name, shape, tdt in ((x, "x", (L, Dm), dt), (delta, "delta", (L, Dm), dt),
+                                (A, "A", (Dm, N), torch.float32), (B, "B", (L, N), dt), (C, "C", (L, N), dt),
+                                (D, "D", (Dm,), torch.float32), (cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int64),
+                                (dy, "dy", (L, Dm), dt)):
+        _need(t, name, shape, tdt, dev)
+    _bias(delta_bias, Dm, dev)
+    if h_init is not None:
+        _need(h_init, "h_init", (nseq, Dm, N), torch.float32, dev)
+    if dh_final is not None:
+        _need(dh_final, "dh_final", (nseq, Dm, N), torch.float32, dev)
+    o = dict(out or {})
+    shapes = {"dx": ((L, Dm), dt), "ddelta": ((L, Dm), dt), "dA": ((Dm, N), torch.float32),
+              "dB": ((L, N), torch.float32), "dC": ((L, N), torch.float32), "dD": ((Dm,), torch.float32)}
+    if want_dh_init:
+        shapes["dh_init"] = ((nseq, Dm, N), torch.float32)
+    if delta_bias is not None:
+        shapes["ddelta_bias"] = ((Dm,), torch.float32)
+    for k, (shape, tdt) in shapes.items():
+        if o.get(k) is None:
+            o[k] = torch.empty(shape, dtype=tdt, device=dev)
+        _need(o[k], k, shape, tdt, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_varlen_bwd(_ptr(x), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(cu_seqlens), nseq, _ptr(h_init), _ptr(dy), _ptr(dh_final),
+                                       _ptr(o["dx"]), _ptr(o["ddelta"]), _ptr(o.get("ddelta_bias")), _ptr(o["dA"]),
+                                       _ptr(o["dB"]), _ptr(o["dC"]), _ptr(o["dD"]), _ptr(o.get("dh_init")), L, Dm,
+                                       N, code, _flags(delta_softplus, euler_b), _stream(dev))
+    _check(rc, "ssm_scan_varlen_bwd")
     return o
 
 

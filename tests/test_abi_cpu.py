@@ -171,6 +171,34 @@ def test_bwd_argument_errors(L):
     assert bwd(Bsz=1 << 40, Ls=1 << 40) == 2
 
 
+def test_varlen_bwd_argument_errors(L):
+    v = ctypes.c_void_p
+    Q = [0x10000000 * (i + 1) for i in range(20)]  # fake, aligned, far apart
+
+    def bwd(**k):
+        a = dict(x=Q[0], dl=Q[1], bias=None, A=Q[2], B=Q[3], C=Q[4], D=Q[5], cu=Q[14], nseq=3, hi=None, dy=Q[6],
+                 dhf=None, dx=Q[7], ddl=Q[8], dbias=None, dA=Q[9], dB=Q[10], dC=Q[11], dD=Q[12], dhi=None,
+                 Ls=8, Dm=64, N=16, dtype=1, flags=0)
+        a.update(k)
+        return L.ssm_scan_varlen_bwd(v(a["x"]), v(a["dl"]), v(a["bias"]), v(a["A"]), v(a["B"]), v(a["C"]),
+                                     v(a["D"]), v(a["cu"]), a["nseq"], v(a["hi"]), v(a["dy"]), v(a["dhf"]),
+                                     v(a["dx"]), v(a["ddl"]), v(a["dbias"]), v(a["dA"]), v(a["dB"]), v(a["dC"]),
+                                     v(a["dD"]), v(a["dhi"]), a["Ls"], a["Dm"], a["N"], a["dtype"], a["flags"],
+                                     None)
+    assert bwd(cu=0) == 1
+    assert b"cu_seqlens" in L.ssm_last_error()
+    assert bwd(nseq=-1) == 2
+    assert bwd(nseq=0) == 2                    # L > 0 needs at least one sequence
+    assert bwd(cu=Q[14] + 4) == 5              # int64 offsets need 8-byte alignment
+    assert bwd(dtype=3) == 3 and bwd(N=7) == 4 and bwd(flags=4) == 9 and bwd(Ls=-1) == 2
+    assert bwd(dy=0) == 1 and bwd(dx=0) == 1
+    assert bwd(dx=Q[14]) == 6                  # dx overlaps cu_seqlens
+    assert bwd(dhi=Q[14] + 8) == 6             # dh_init overlaps cu_seqlens
+    assert bwd(dhi=Q[13], dhf=Q[13] + 64) == 6  # dh_init overlaps dh_final ([nseq][Dm][N] rows)
+    assert b"overlaps" in L.ssm_last_error()
+    assert bwd(nseq=1 << 60) == 2              # nseq * Dm * N overflows
+
+
 def test_ssd_argument_errors(L):
     v = ctypes.c_void_p
     Q = [0x10000000 * (i + 1) for i in range(12)]  # fake, 16-byte aligned, far apart
