@@ -16,14 +16,16 @@ copy); the fp64 CPU oracle timed on a bounded sample of the same workload;
 and -- under "secondary" -- the long-context scan, the Mamba-130M-shaped
 layer, the scan options (fused delta activation, Euler input term), a packed
 variable-length prefill, the scan with complex A, the backward (structured
-and general A), the general-A path forced on the 2.8B-shaped layer, the
+and general A, and of the packed prefill), the general-A path forced on the
+2.8B-shaped layer, the
 scalar-decay (state-space duality) layer, and the decode step.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 20]
                     [--no-cpu-baseline] [--no-secondary]
     python bench.py --only scan        # one workload, for profiler runs
                                        # (scan, long, small, packed, options, backward,
-                                       #  backward_general, complex, cdecode, general,
+                                       #  backward_general, packed_backward, complex,
+                                       #  cdecode, general,
                                        #  ssd, decode, probe, hbmprobe)
     python bench.py --copy-calibration # plain copy of known size (for counters)
 """
@@ -393,6 +395,65 @@ def bench_backward(torch, ss, generate, cfg, steps, warmup, flusher=None):
            "main_kernel_elems_per_s": elems / (main_ms * 1e-3),
            "config": {"workload": cfg.name, "A": cfg.a_kind, "segments": plan[0], "segment_len": plan[1],
                       "segments_per_group": plan[2], "groups": plan[3]}}
+    if proto is not None:
+        rec["protocol"] = proto
+    return rec
+
+
+def alg_bytes_bwd_packed(cfg, nseq):
+    """Packed backward, inputs read once and outputs written once: as the
+    dense backward for one row of cfg.L steps, with h_init, dh_final read and
+    dh_init written per sequence and the sequence offsets read."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    LD, LN, DN, SDN = cfg.L * cfg.Dm, cfg.L * cfg.N, cfg.Dm * cfg.N, nseq * cfg.Dm * cfg.N
+    return 5 * LD * s + 2 * LN * s + 2 * LN * 4 + 2 * DN * 4 + 2 * cfg.Dm * 4 + 3 * SDN * 4 + 8 * (nseq + 1)
+
+
+def bench_packed_backward(torch, ss, generate, cfg, steps, warmup, flusher=None):
+    """Backward of the packed prefill: every input gradient of the packed scan
+    for a random dy and dh_final, each sequence restarting from its own
+    initial state; forward states recomputed inside the call."""
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name} (packed backward)")
+    inp = generate.packed_inputs(cfg, dev)
+    nseq = inp["cu"].numel() - 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 1)
+    dy = torch.randn(inp["x"].shape, generator=g, device=dev).to(inp["x"].dtype)
+    dhf = torch.randn((nseq, cfg.Dm, cfg.N), generator=g, device=dev)
+    out = {}
+
+    def fn(_i):
+        nonlocal out
+        out = ss.scan_varlen_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["cu"], dy,
+                                 h_init=inp["h_init"], dh_final=dhf, out=out or None)
+
+    log(f"[bench] timing {cfg.name} packed backward: {warmup} warmup + {steps} steps")
+    ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    proto = protocol_record(torch, fn, fn, steps, flusher, 1) if flusher else None
+    plan = ss.bwd_plan(1, cfg.L, cfg.Dm, cfg.N)
+    lens = (inp["cu"][1:] - inp["cu"][:-1]).tolist()
+    del inp, dy, dhf, out
+    torch.cuda.empty_cache()
+    elems = cfg.elems()
+    main_ms = kern["bwd_main"]["avg_ms"]
+    alg = alg_bytes_bwd_packed(cfg, nseq)
+    achieved = elems * BWD_FLOPS_PER_ELEM / (main_ms * 1e-3) / 1e12
+    roof = {"kernel": "bwd_main_kernel (packed)", "bound": "alu", "achieved": round(achieved, 3),
+            "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+            "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
+            "avg_ms": round(main_ms, 5), "algorithmic_flops_per_launch": elems * BWD_FLOPS_PER_ELEM,
+            "algorithmic_bytes_per_call": alg,
+            "hbm_frac_kernel": round(alg / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "hbm_frac_step": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    roof.update(traffic_fields("packed_backward_" + cfg.name, "bwd", alg))
+    rec = {"workload": cfg.name + "_backward", "ms_per_step": round(ms, 5), "value": elems / (ms * 1e-3),
+           "unit": "elems/s", "roofline": roof,
+           "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
+           "main_kernel_elems_per_s": elems / (main_ms * 1e-3),
+           "config": {"workload": cfg.name, "A": cfg.a_kind, "sequences": nseq, "empty_sequences": lens.count(0),
+                      "longest": max(lens), "segments": plan[0], "segment_len": plan[1],
+                      "segments_per_group": plan[2], "groups": plan[3], "h_init": cfg.h0_std > 0}}
     if proto is not None:
         rec["protocol"] = proto
     return rec
@@ -771,8 +832,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
-                                       "backward_general", "complex", "cdecode", "general", "ssd", "probe",
-                                       "hbmprobe"],
+                                       "backward_general", "packed_backward", "complex", "cdecode", "general",
+                                       "ssd", "probe", "hbmprobe"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     a = ap.parse_args()
@@ -830,6 +891,10 @@ def main():
         return
     if a.only == "backward_general":
         rec = bench_backward(torch, ss, generate, configs.MAMBA130M_LAYER, a.steps, a.warmup)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "packed_backward":
+        rec = bench_packed_backward(torch, ss, generate, configs.PACKED_2P8B_LAYER, a.steps, a.warmup)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "options":
@@ -900,6 +965,8 @@ def main():
         sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), wu, flusher)
         sec["backward_general_A"] = bench_backward(torch, ss, generate, configs.MAMBA130M_LAYER, steps5, wu,
                                                    flusher)
+        sec["packed_backward"] = bench_packed_backward(torch, ss, generate, configs.PACKED_2P8B_LAYER,
+                                                       max(3, a.steps // 10), wu, flusher)
         sec["general_A_path"] = bench_general_path(torch, ss, generate, cfg, steps5, flusher, wu)
         sec["ssd_layer"] = bench_ssd(torch, ss, generate, configs.SSD_LAYER, steps5, wu, flusher)
         sec["decode"] = bench_decode(torch, ss, generate, configs.DECODE_256x8192,

@@ -64,3 +64,9 @@ def test_rotation_and_backward_bytes():
     assert bench.rotation_count(150_000_000) == 8       # >= 4 x the 256 MiB cache
     b = bench.alg_bytes_bwd(configs.MAMBA2P8B_LAYER)
     assert 3.3e9 < b < 3.5e9                            # x, delta, dy read; dx, ddelta written; dB, dC
+    # packed: the same per-step arrays for one row of 65536 steps, plus three
+    # [nseq][Dm][N] fp32 state rows (h_init, dh_final, dh_init) and the offsets
+    pc = configs.PACKED_2P8B_LAYER
+    bp = bench.alg_bytes_bwd_packed(pc, 40)
+    assert bp == (5 * 65536 * 5120 * 2 + 2 * 65536 * 16 * 2 + 2 * 65536 * 16 * 4 + 2 * 5120 * 16 * 4 + 2 * 5120 * 4
+                  + 3 * 40 * 5120 * 16 * 4 + 8 * 41)
