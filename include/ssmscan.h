@@ -444,7 +444,8 @@ typedef enum {
     SSM_K_SCAN_CARRY = 2,       /* states entering each segment */
     SSM_K_SCAN_OUTPUT = 3,      /* y (and h_final) from the entering states */
     SSM_K_STEP = 4,             /* decode step */
-    SSM_K_STATE_INIT = 5,       /* h_final of an empty sequence; zero fills */
+    SSM_K_STATE_INIT = 5,       /* h_final (or dh_init) of empty sequences; zero fills;
+                                   sequence-start masks of a packed backward */
     SSM_K_BWD_AGGREGATE = 6,    /* backward: per-segment adjoint summaries */
     SSM_K_BWD_CARRY = 7,        /* backward: adjoint entering each segment */
     SSM_K_BWD_MAIN = 8,         /* backward: gradients per segment */

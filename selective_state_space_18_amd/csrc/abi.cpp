@@ -1007,7 +1007,7 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     const size_t sz_pa = align256((size_t)q.n_groups * BD * N * acc);
     const size_t sz_pd = align256((size_t)q.n_groups * BD * 2 * acc);
     const size_t sz_pon = align256((size_t)2 * q.blocks_per_row * Bsz * q.n_groups * sizeof(int));
-    const size_t sz_res = varlen ? align256(S * sizeof(int)) : 0;  // each of the two reset flag arrays
+    const size_t sz_res = varlen ? align256(S * sizeof(int)) : 0;  // forward reset flags; start masks
 
     std::lock_guard<std::mutex> lk(g_ws_mu);
     void *ws = nullptr;
@@ -1036,7 +1036,7 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     base += sz_pon;
     p.seg_reset = varlen ? reinterpret_cast<int *>(base) : nullptr;
     base += sz_res;
-    q.rseg_reset = varlen ? reinterpret_cast<int *>(base) : nullptr;
+    q.seg_starts = varlen ? reinterpret_cast<uint32_t *>(base) : nullptr;
 
     const int n = (int)N;
     auto bwd = [&](ssm::BwdPass pass) {
@@ -1046,6 +1046,8 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     };
     if ((e = timed(SSM_K_BC_PREP, s, [&] { return ssm::launch_bc_prep(p, n, dtype, s); })) != hipSuccess)
         return hip_fail(e, "B/C conversion launch");
+    if (varlen && (e = timed(SSM_K_STATE_INIT, s, [&] { return bwd(ssm::BwdPass::kStarts); })) != hipSuccess)
+        return hip_fail(e, "sequence-start launch");
     if (p.S > 1) {
         if ((e = timed(SSM_K_SCAN_AGGREGATE, s, [&] { return ssm::launch_scan_aggregate(p, n, dtype, s); })) !=
             hipSuccess)

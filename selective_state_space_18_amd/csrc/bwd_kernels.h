@@ -30,6 +30,8 @@
 // ({B or (n+1)B for Euler, C/(n+1)}).
 #pragma once
 
+#include <type_traits>
+
 #include "scan_kernels.h"
 
 namespace ssm {
@@ -125,11 +127,24 @@ __device__ __forceinline__ void load_scaled_adjoint(const float *dh, int64_t k, 
     }
 }
 
+// Start masks of every segment (packed sequences), one thread per segment:
+// the aggregate and main passes read their segment's with one scalar load.
+// (a template only so that it is emitted where the packed passes use it)
+template <int kUnused>
+__global__ __launch_bounds__(kBlock) void seg_starts_kernel(BwdParams q) {
+    const ScanParams &p = q.f;
+    const int s = (int)(blockIdx.x * kBlock + threadIdx.x);
+    if (s >= p.S) return;
+    const int64_t t0 = (int64_t)s * p.seg_len;
+    const int n = (int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0);
+    q.seg_starts[s] = seq_start_mask((const_row_ptr<int64_t>)p.cu, p.nseq, t0, n);
+}
+
 // ---------------------------------------------------------------------------
 // Reverse aggregate: segments 1..S-1, adjoint from zero at the segment end.
 // Packed sequences: past a sequence start the adjoint restarts from the
-// previous sequence's dh_final row, and the segment is flagged so that the
-// reverse carry drops what enters it from the right.
+// previous sequence's dh_final row (the reverse carry then drops what enters
+// the segment from the right).
 
 template <typename T, int N, bool kStruct, bool kEuler, bool kPre, bool kVarlen>
 __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
@@ -173,11 +188,7 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
 #pragma unroll
     for (int n = 0; n < N; ++n) nu[n] = 0;
     Acc lam = 0;
-    uint32_t smask = 0;
-    if constexpr (kVarlen) {
-        smask = seq_start_mask((const_row_ptr<int64_t>)p.cu, p.nseq, t0, nsteps);
-        if (tile == 0 && lane == 0) q.rseg_reset[s] = smask != 0 ? 1 : 0;
-    }
+    const uint32_t smask = kVarlen ? ((const_row_ptr<uint32_t>)q.seg_starts)[s] : 0u;
     constexpr int G = kPrefetch;
     uint32_t dl_c[G], dy_c[G], dl_n[G], dy_n[G];  // raw bits, one value per register (buf_load_raw)
     auto load = [&](int tb, uint32_t(&dl)[G], uint32_t(&dyv)[G]) {
@@ -197,62 +208,71 @@ __global__ __launch_bounds__(kBlock) void bwd_aggregate_kernel(BwdParams q) {
 #pragma unroll
         for (int n = 0; n < N; ++n) dst[n] = bcp[(int64_t)t * (2 * N) + N + n];
     };
-    load_c(ca, nsteps - 1);
-    load(nsteps - 1, dl_c, dy_c);
-    for (int tb = nsteps - 1; tb >= 0; tb -= G) {
-        load(tb - G, dl_n, dy_n);
+    // A segment without a sequence start runs the dense loop (no per-step
+    // test in it).
+    auto run = [&](auto has_starts) __attribute__((always_inline)) {
+        constexpr bool kR = decltype(has_starts)::value;
+        load_c(ca, nsteps - 1);
+        load(nsteps - 1, dl_c, dy_c);
+        for (int tb = nsteps - 1; tb >= 0; tb -= G) {
+            load(tb - G, dl_n, dy_n);
 #pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const int t = tb - k;
-            if (t >= 0) {
-                Acc(&crow)[N] = (k & 1) ? cb : ca;
-                row_ready(crow);
-                load_c((k & 1) ? ca : cb, t > 0 ? t - 1 : 0);
-                __builtin_amdgcn_sched_barrier(0);
-                Acc dv = (Acc)raw_to_f32<T>(dl_c[k]);
-                if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
-                const Acc g = (Acc)raw_to_f32<T>(dy_c[k]);
-                lam += dv;
-                if constexpr (kStruct) {
-                    Acc r;
-                    const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
-                    Acc E = E1;
+            for (int k = 0; k < G; ++k) {
+                const int t = tb - k;
+                if (t >= 0) {
+                    Acc(&crow)[N] = (k & 1) ? cb : ca;
+                    row_ready(crow);
+                    load_c((k & 1) ? ca : cb, t > 0 ? t - 1 : 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    Acc dv = (Acc)raw_to_f32<T>(dl_c[k]);
+                    if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
+                    const Acc g = (Acc)raw_to_f32<T>(dy_c[k]);
+                    lam += dv;
+                    if constexpr (kStruct) {
+                        Acc r;
+                        const Acc E1 = expm1_and_exp2(dv * cc.a0, r);
+                        Acc E = E1;
 #pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        const Acc mu = fma_(crow[n], g, nu[n]);
-                        nu[n] = fma_(E, mu, mu);
-                        if (n + 1 < N) {
-                            if constexpr (sizeof(Acc) == 8)
-                                E = fma_(E, E1, E + E1);
-                            else
-                                E = fma_(E, r, E1);
+                        for (int n = 0; n < N; ++n) {
+                            const Acc mu = fma_(crow[n], g, nu[n]);
+                            nu[n] = fma_(E, mu, mu);
+                            if (n + 1 < N) {
+                                if constexpr (sizeof(Acc) == 8)
+                                    E = fma_(E, E1, E + E1);
+                                else
+                                    E = fma_(E, r, E1);
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int n = 0; n < N; ++n) {
+                            Acc e;
+                            const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
+                            const Acc mu = fma_(crow[n], g, nu[n]);
+                            nu[n] = fma_(E, mu, mu);
                         }
                     }
-                } else {
-#pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        Acc e;
-                        const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
-                        const Acc mu = fma_(crow[n], g, nu[n]);
-                        nu[n] = fma_(E, mu, mu);
-                    }
-                }
-                if constexpr (kVarlen) {
-                    if ((smask >> t) & 1u) {
-                        const const_row_ptr<int64_t> cu = (const_row_ptr<int64_t>)p.cu;
-                        const int64_t ts = t0 + t;  // >= seg_len: a sequence ends at ts - 1
-                        const int64_t kp = seq_before(cu, find_seq(cu, p.nseq, ts), ts);
-                        load_scaled_adjoint(q.dh_final, kp, p.Dm, d, nu);
+                    if constexpr (kR) {
+                        if ((smask >> t) & 1u) {
+                            const const_row_ptr<int64_t> cu = (const_row_ptr<int64_t>)p.cu;
+                            const int64_t ts = t0 + t;  // >= seg_len: a sequence ends at ts - 1
+                            const int64_t kp = seq_before(cu, find_seq(cu, p.nseq, ts), ts);
+                            load_scaled_adjoint(q.dh_final, kp, p.Dm, d, nu);
+                        }
                     }
                 }
             }
-        }
 #pragma unroll
-        for (int k = 0; k < G; ++k) {
-            dl_c[k] = dl_n[k];
-            dy_c[k] = dy_n[k];
+            for (int k = 0; k < G; ++k) {
+                dl_c[k] = dl_n[k];
+                dy_c[k] = dy_n[k];
+            }
         }
-    }
+    };
+    if (kVarlen && smask != 0)
+        run(std::integral_constant<bool, kVarlen>());
+    else
+        run(std::integral_constant<bool, false>());
     if (!active) return;
     Acc *a = static_cast<Acc *>(q.ragg) + (int64_t)s * (N + 1) * BD + ch;
 #pragma unroll
@@ -307,7 +327,7 @@ __global__ __launch_bounds__(kBlock) void bwd_carry_kernel(BwdParams q) {
         bool cut[kBatch];
         if constexpr (kVarlen) {
 #pragma unroll
-            for (int k = 0; k < kBatch; ++k) cut[k] = s1 - k >= 1 && q.rseg_reset[s1 - k] != 0;
+            for (int k = 0; k < kBatch; ++k) cut[k] = s1 - k >= 1 && q.seg_starts[s1 - k] != 0;
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
@@ -642,7 +662,7 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
         const int64_t t0 = (int64_t)s * p.seg_len;
         const int nseg = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
         const int nck = (nseg + kK - 1) / kK;
-        const uint32_t smask = kVarlen ? seq_start_mask(cu, p.nseq, t0, nseg) : 0u;
+        const uint32_t smask = kVarlen ? ((const_row_ptr<uint32_t>)q.seg_starts)[s] : 0u;
 
         // checkpoints: the state before steps t0, t0 + kK, ... (restarted
         // where a sequence starts there)
@@ -977,6 +997,13 @@ hipError_t bwd_pass_n(BwdPass pass, const BwdParams &q, hipStream_t s) {
     typedef typename AccOf<T>::type Acc;
     const ScanParams &p = q.f;
     switch (pass) {
+        case BwdPass::kStarts:
+            if constexpr (kVarlen) {
+                if (p.S > 0)
+                    hipLaunchKernelGGL(seg_starts_kernel<0>, dim3((unsigned)((p.S + kBlock - 1) / kBlock)), dim3(kBlock),
+                                       0, s, q);
+            }
+            break;
         case BwdPass::kAggregate:
         case BwdPass::kMain:
             // both A paths; each wave works in exactly one of them

@@ -72,8 +72,10 @@ enum class ScanPass { kPrep, kAggregate, kCarry, kOutput };
 //           rows are then not written and not read)
 // Packed sequences (f.cu set, B = 1): f.h_init, dh_final and dh_init are
 // [nseq][D][N]; f.seg_reset serves the forward carry and
-//   rseg_reset : [S] int -- 1 where a sequence starts inside segment s >= 1
-//           (the reverse carry takes that segment's summary alone)
+//   seg_starts : [S] uint32 -- bit i set where a sequence starts at step
+//           s * seg_len + i (the reverse carry takes the summary alone of a
+//           segment with a start; the aggregate and main passes restart the
+//           adjoint, and the state, there)
 struct BwdParams {
     ScanParams f;
     const void *dy;          // [B,L,D] storage dtype
@@ -82,13 +84,14 @@ struct BwdParams {
     float *dA, *dB, *dC, *dD, *ddelta_bias, *dh_init;
     void *ragg, *gout, *part_bc, *part_a, *part_d;
     int *part_on;
-    int *rseg_reset;
+    uint32_t *seg_starts;
     int seg_per_group;       // segments one wave processes in turn
     int n_groups;            // ceil(S / seg_per_group)
     int blocks_per_row;      // ceil(tiles_per_b / 4)
 };
 
-enum class BwdPass { kAggregate, kCarry, kMain, kReduce };
+// kStarts: the per-segment sequence-start masks (packed sequences only).
+enum class BwdPass { kStarts, kAggregate, kCarry, kMain, kReduce };
 
 // Complex diagonal A (cplx_kernels.h).  ScanParams as for the real scan, with
 // A [Dm][N][2], h_init/h_final [Bsz][Dm][N][2] as (re, im) pairs and scratch
