@@ -62,13 +62,19 @@ __device__ __forceinline__ double softplus_grad_from_value(double sp) { return -
 
 // phi'(z) = (z e^z - (e^z - 1)) / z^2 with E = e^z - 1; a Taylor polynomial
 // for |z| < 1/8 (truncation below z^5/840, relative 1e-7), where the closed
-// form cancels.
+// form cancels.  In fp32 the closed form takes the hardware reciprocal (about
+// 1 ulp) instead of a correctly rounded division, whose expansion was a large
+// share of the general path's per-element instructions and registers.
 template <typename Acc>
 __device__ __forceinline__ Acc zoh_dphi(Acc z, Acc E) {
     const Acc poly =
         fma_(z, fma_(z, fma_(z, fma_(z, (Acc)(1.0 / 144.0), (Acc)(1.0 / 30.0)), (Acc)(1.0 / 8.0)), (Acc)(1.0 / 3.0)),
              (Acc)0.5);
-    const Acc closed = fma_(z, (Acc)1 + E, -E) / (z * z);
+    Acc closed;
+    if constexpr (sizeof(Acc) == 4)
+        closed = fma_(z, (Acc)1 + E, -E) * __builtin_amdgcn_rcpf(z * z);
+    else
+        closed = fma_(z, (Acc)1 + E, -E) / (z * z);
     return abs_(z) < (Acc)0.125 ? poly : closed;
 }
 
@@ -803,13 +809,19 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                         }
                     } else {
                         const Acc dxv = dv * xv;
+                        // (ZOH: the exponent argument from delta in the exp
+                        // unit's base times A, not from the per-channel array
+                        // of A in that base: 16 fewer live registers)
+                        constexpr Acc unit = sizeof(Acc) == 4 ? (Acc)kLog2e : (Acc)1;
+                        const Acc dvu = dv * unit;
 #pragma unroll
                         for (int n = 0; n < N; ++n) {
                             Acc gprev = gp[n];
                             if (i > 0) gprev = gs[i > 0 ? i - 1 : 0][n];
                             if constexpr (kVarlen) gprev = rs ? hs[n] : gprev;
                             Acc e;
-                            const Acc E = expm1_and_exp2(dv * cc.Aeff[n], e);
+                            const Acc E = kEuler ? expm1_and_exp2(dv * cc.Aeff[n], e)
+                                                 : expm1_and_exp2(dvu * zoh_a<Acc>(Ar[n]), e);
                             const Acc mu = fma_(rw[N + n], gy, nu[n]);
                             const Acc pp = E * mu;
                             const Acc nup = mu + pp;
