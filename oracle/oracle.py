@@ -67,6 +67,8 @@ class Oracle:
         lib.ssm_oracle_scan_complex.restype = ctypes.c_int
         lib.ssm_oracle_step_complex.argtypes = [_dp] * 9 + [_i64] * 3 + [ctypes.c_int]
         lib.ssm_oracle_step_complex.restype = ctypes.c_int
+        lib.ssm_oracle_scan_complex_bwd.argtypes = [_dp] * 18 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int]
+        lib.ssm_oracle_scan_complex_bwd.restype = ctypes.c_int
         lib.ssm_oracle_max_threads.argtypes = []
         lib.ssm_oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -157,6 +159,45 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"ssm_oracle_scan_complex failed with code {rc}")
         return y, hf[..., 0] + 1j * hf[..., 1]
+
+    def scan_complex_bwd(self, x, delta, A, B, C, D, dy, h0=None, dh_final=None, delta_bias=None,
+                         delta_softplus: bool = False, euler_b: bool = False, want_dBC: bool = True,
+                         threads: int = 0):
+        """Gradients of the complex-A scan for output gradients dy [Bsz,L,Dm] and,
+        if given, dh_final complex [Bsz,Dm,N] (the loss pairs it with h_final as
+        Re(conj(dh_final) h_final)).  A, h0 as scan_complex.  Returns a dict with
+        dx, ddelta, dD, dbias (if delta_bias is given), dB, dC (if want_dBC), and
+        dA [Dm,N], dh0 [Bsz,Dm,N] complex: the gradients of the real and the
+        imaginary parts as one complex number."""
+        x = np.asarray(x)
+        Bsz, L, Dm = x.shape
+        Ac = _as_complex(A)
+        N = Ac.shape[1]
+        x = _f64(x, (Bsz, L, Dm), "x")
+        delta = _f64(delta, (Bsz, L, Dm), "delta")
+        A2 = _pairs(Ac, (Dm, N), "A")
+        B = _f64(B, (Bsz, L, N), "B")
+        C = _f64(C, (Bsz, L, N), "C")
+        D = _f64(D, (Dm,), "D")
+        dy = _f64(dy, (Bsz, L, Dm), "dy")
+        h2 = None if h0 is None else _pairs(_as_complex(h0), (Bsz, Dm, N), "h0")
+        g2 = None if dh_final is None else _pairs(_as_complex(dh_final), (Bsz, Dm, N), "dh_final")
+        bias = None if delta_bias is None else _f64(delta_bias, (Dm,), "delta_bias")
+        out = {"dx": np.empty((Bsz, L, Dm)), "ddelta": np.empty((Bsz, L, Dm)), "dD": np.empty(Dm)}
+        dA = np.empty((Dm, N, 2))
+        dh0 = np.empty((Bsz, Dm, N, 2))
+        out["dbias"] = np.empty(Dm) if bias is not None else None
+        out["dB"] = np.empty((Bsz, L, N)) if want_dBC else None
+        out["dC"] = np.empty((Bsz, L, N)) if want_dBC else None
+        rc = self.lib.ssm_oracle_scan_complex_bwd(
+            _ptr(x), _ptr(delta), _ptr(bias), _ptr(A2), _ptr(B), _ptr(C), _ptr(D), _ptr(h2), _ptr(dy), _ptr(g2),
+            _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dbias"]), _ptr(dA), _ptr(out["dB"]), _ptr(out["dC"]),
+            _ptr(out["dD"]), _ptr(dh0), Bsz, L, Dm, N, _flags(delta_softplus, euler_b), int(threads or self.threads))
+        if rc != 0:
+            raise RuntimeError(f"ssm_oracle_scan_complex_bwd failed with code {rc}")
+        out["dA"] = dA[..., 0] + 1j * dA[..., 1]
+        out["dh0"] = dh0[..., 0] + 1j * dh0[..., 1]
+        return out
 
     def step_complex(self, x, delta, A, B, C, D, h, delta_bias=None, delta_softplus: bool = False,
                      euler_b: bool = False):
@@ -272,6 +313,10 @@ def scan_complex(x, delta, A, B, C, D, **opts):
 
 def step_complex(x, delta, A, B, C, D, h, **opts):
     return load().step_complex(x, delta, A, B, C, D, h, **opts)
+
+
+def scan_complex_bwd(x, delta, A, B, C, D, dy, **opts):
+    return load().scan_complex_bwd(x, delta, A, B, C, D, dy, **opts)
 
 
 def scan_ssd(x, delta, A, B, C, D, head_dim, **opts):

@@ -51,6 +51,7 @@
  * All arithmetic is IEEE double with libm exp/expm1; build without
  * -ffast-math.
  */
+#include <complex.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -462,6 +463,196 @@ int ssm_oracle_step_complex(const double *x, const double *delta, const double *
                                         C + b * N, D[d], N, euler);
         }
     return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Backward of the complex-A scan: the chain rule on the recurrence above, with
+ * every complex quantity taken as its (re, im) pair of reals.  For a real loss
+ * L and a product w = p q of complex numbers, the pair (dL/dRe p, dL/dIm p) is
+ * G_w conj(q) as a complex number, G_w = dL/dRe w + i dL/dIm w; for w = f(p)
+ * holomorphic it is G_w conj(f'(p)).  With lambda = G_{h_t}:
+ *   lambda_t  += C_t[n] dy_t              (y reads Re h_t)
+ *   G_Abar     = lambda conj(h_{t-1}),    G_k = lambda u,   u = B_t[n] x_t
+ *   dL/du      = Re(lambda conj(k))       (dx, dB through u)
+ *   dL/ddelta += Re(G_Abar conj(A Abar)) + Re(G_k conj(dk/ddelta))
+ *   dL/dA     += G_Abar conj(delta Abar)  + G_k conj(dk/dA)
+ *   lambda_{t-1} = lambda conj(Abar)
+ * where k = delta phi(delta A) = (Abar - 1)/A (ZOH: dk/ddelta = Abar,
+ * dk/dA = delta^2 phi'(delta A)) or k = delta (Euler: dk/ddelta = 1).
+ * Layouts as ssm_oracle_scan_bwd, with A, dA [Dm][N][2] and h0, dh_final, dh0
+ * [Bsz][Dm][N][2] as (re, im) pairs.
+ * ---------------------------------------------------------------------- */
+
+/* phi(z) = (exp(z) - 1) / z for complex z, 1 at z = 0 */
+static double complex cphi(double complex z)
+{
+    if (creal(z) == 0.0 && cimag(z) == 0.0)
+        return 1.0;
+    double er, ei;
+    cexpm1(creal(z), cimag(z), &er, &ei);
+    return (er + I * ei) / z;
+}
+
+/* phi'(z) = (z e^z - (e^z - 1)) / z^2 for complex z; for |z| < 1 its series
+ * sum_{m>=1} m z^(m-1) / (m+1)!, which has no cancellation */
+static double complex cdphi(double complex z)
+{
+    if (cabs(z) < 1.0) {
+        double complex term = 0.5, sum = 0.0;
+        for (int m = 1; m < 40; ++m) {
+            sum += term;
+            term *= z * (double)(m + 1) / ((double)m * (double)(m + 2));
+        }
+        return sum;
+    }
+    double er, ei;
+    cexpm1(creal(z), cimag(z), &er, &ei);
+    return (z * cexp(z) - (er + I * ei)) / (z * z);
+}
+
+int ssm_oracle_scan_complex_bwd(const double *x, const double *delta, const double *bias,
+                                const double *A, const double *B, const double *C,
+                                const double *D, const double *h0, const double *dy,
+                                const double *dh_final, double *dx, double *ddelta,
+                                double *dbias, double *dA, double *dB, double *dC,
+                                double *dD, double *dh0, int64_t Bsz, int64_t L,
+                                int64_t Dm, int64_t N, int flags, int nthreads)
+{
+    if (Bsz < 0 || L < 0 || Dm < 0 || N <= 0)
+        return 1;
+    const int euler = (flags & ORACLE_EULER_B) != 0;
+    const int soft = (flags & ORACLE_DELTA_SOFTPLUS) != 0;
+    const int64_t BLN = Bsz * L * N;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+    const int nth = omp_get_max_threads();
+#else
+    (void)nthreads;
+    const int nth = 1;
+#endif
+    double *priv = NULL;
+    if (dB || dC) {
+        priv = (double *)calloc((size_t)nth * 2 * (size_t)BLN + 1, sizeof(double));
+        if (!priv)
+            return 2;
+    }
+    int err = 0;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+        const int tid = omp_get_thread_num();
+#else
+        const int tid = 0;
+#endif
+        /* hs[(t+1) N + n] = h_t as (re, im) pairs, hs[n] = h0 */
+        double *hs = (double *)malloc((size_t)(L + 1) * (size_t)(2 * N) * sizeof(double));
+        double complex *lam = (double complex *)malloc((size_t)N * sizeof(double complex));
+        double complex *dAd = (double complex *)malloc((size_t)N * sizeof(double complex));
+        double *myB = priv ? priv + (size_t)tid * 2 * (size_t)BLN : NULL;
+        double *myC = priv ? myB + BLN : NULL;
+        if (!hs || !lam || !dAd) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t d = 0; d < Dm; ++d) {
+                const double *a = A + d * 2 * N;
+                const double bias_d = bias ? bias[d] : 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    dAd[n] = 0.0;
+                double dD_d = 0.0, dbias_d = 0.0;
+                for (int64_t b = 0; b < Bsz; ++b) {
+                    /* forward with the forward oracle's own step, keeping every state */
+                    for (int64_t k = 0; k < 2 * N; ++k)
+                        hs[k] = h0 ? h0[(b * Dm + d) * 2 * N + k] : 0.0;
+                    for (int64_t t = 0; t < L; ++t) {
+                        const int64_t i = (b * L + t) * Dm + d;
+                        const int64_t r = (b * L + t) * N;
+                        const double dt = step_size(delta[i], bias_d, flags);
+                        for (int64_t k = 0; k < 2 * N; ++k)
+                            hs[(t + 1) * 2 * N + k] = hs[t * 2 * N + k];
+                        (void)channel_step_complex(hs + (t + 1) * 2 * N, x[i], dt, a, B + r, C + r, D[d], N, euler);
+                    }
+                    /* backward */
+                    for (int64_t n = 0; n < N; ++n) {
+                        const int64_t j = ((b * Dm + d) * N + n) * 2;
+                        lam[n] = dh_final ? dh_final[j] + I * dh_final[j + 1] : 0.0;
+                    }
+                    for (int64_t t = L - 1; t >= 0; --t) {
+                        const int64_t i = (b * L + t) * Dm + d;
+                        const int64_t r = (b * L + t) * N;
+                        const double dt = step_size(delta[i], bias_d, flags);
+                        const double g = dy[i];
+                        double gx = D[d] * g, gdt = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double complex An = a[2 * n] + I * a[2 * n + 1];
+                            const double complex z = dt * An;
+                            const double complex abar = cexp(z);
+                            const double complex k = euler ? (double complex)dt : dt * cphi(z);
+                            const double complex hprev = hs[t * 2 * N + 2 * n] + I * hs[t * 2 * N + 2 * n + 1];
+                            const double u = B[r + n] * x[i];
+                            lam[n] += C[r + n] * g;
+                            const double complex gabar = lam[n] * conj(hprev);
+                            const double complex gk = lam[n] * u;
+                            const double gu = creal(lam[n] * conj(k));
+                            gx += gu * B[r + n];
+                            if (myB)
+                                myB[r + n] += gu * x[i];
+                            if (myC)
+                                myC[r + n] += g * hs[(t + 1) * 2 * N + 2 * n];
+                            gdt += creal(gabar * conj(An * abar));
+                            if (euler) {
+                                gdt += creal(gk);
+                                dAd[n] += gabar * conj(dt * abar);
+                            } else {
+                                gdt += creal(gk * conj(abar));
+                                dAd[n] += gabar * conj(dt * abar) + gk * conj(dt * dt * cdphi(z));
+                            }
+                            lam[n] *= conj(abar);
+                        }
+                        dD_d += g * x[i];
+                        dx[i] = gx;
+                        if (soft)
+                            gdt *= sigmoid(delta[i] + bias_d);
+                        ddelta[i] = gdt;
+                        dbias_d += gdt;
+                    }
+                    if (dh0)
+                        for (int64_t n = 0; n < N; ++n) {
+                            const int64_t j = ((b * Dm + d) * N + n) * 2;
+                            dh0[j] = creal(lam[n]);
+                            dh0[j + 1] = cimag(lam[n]);
+                        }
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    dA[(d * N + n) * 2] = creal(dAd[n]);
+                    dA[(d * N + n) * 2 + 1] = cimag(dAd[n]);
+                }
+                dD[d] = dD_d;
+                if (dbias)
+                    dbias[d] = dbias_d;
+            }
+        }
+        free(hs);
+        free(lam);
+        free(dAd);
+    }
+    if (priv) {
+        for (int64_t j = 0; j < BLN; ++j) {
+            double sb = 0.0, sc = 0.0;
+            for (int th = 0; th < nth; ++th) {
+                sb += priv[(size_t)th * 2 * (size_t)BLN + (size_t)j];
+                sc += priv[(size_t)th * 2 * (size_t)BLN + (size_t)BLN + (size_t)j];
+            }
+            if (dB)
+                dB[j] = sb;
+            if (dC)
+                dC[j] = sc;
+        }
+        free(priv);
+    }
+    return err;
 }
 
 int ssm_oracle_max_threads(void)

@@ -550,6 +550,90 @@ def check_complex_reduces_to_real(orc, seed=20):
         assert np.all(hc.imag == 0.0)
 
 
+def _cbwd_case(rng, opts, Bsz=2, L=7, Dm=3, N=4):
+    x, delta, A, B, C, D = random_case(rng, Bsz, L, Dm, N)
+    w = rng.normal(0.0, 2.0, A.shape)
+    A = A + 1j * w
+    A[0, 1] = 0.0          # exact A = 0 (limit of the ZOH input term and of its derivative)
+    A[1, 2] = -1e-7 + 3e-8j  # tiny A, inside the series branch of phi'
+    A[2, 3] = 0.7j         # pure rotation
+    h0 = rng.standard_normal((Bsz, Dm, N)) + 1j * rng.standard_normal((Bsz, Dm, N))
+    dy = rng.standard_normal((Bsz, L, Dm))
+    dhf = rng.standard_normal((Bsz, Dm, N)) + 1j * rng.standard_normal((Bsz, Dm, N))
+    bias = None
+    if opts.get("delta_softplus"):
+        delta = rng.normal(-2.0, 1.0, delta.shape)
+        bias = rng.normal(0.0, 0.5, Dm)
+    return dict(x=x, delta=delta, A=A, B=B, C=C, D=D, h0=h0), dy, dhf, bias
+
+
+def _closs(orc, p, dy, dhf, bias, opts):
+    """<dy, y> + Re<dh_final, h_final> (each complex entry as its (re, im) pair)."""
+    y, hf = orc.scan_complex(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], h0=p["h0"], delta_bias=bias,
+                             **opts)
+    return float(np.sum(dy * y) + np.sum(dhf.real * hf.real + dhf.imag * hf.imag))
+
+
+def check_complex_bwd_finite_differences(orc, seed=30):
+    """Every gradient of the complex-A scan, real and imaginary parts of A and
+    h0 separately, against central differences of the complex forward oracle,
+    for ZOH, softplus(delta + bias), and the Euler input term."""
+    for k, opts in enumerate(({}, {"delta_softplus": True}, {"delta_softplus": True, "euler_b": True},
+                              {"euler_b": True})):
+        rng = np.random.default_rng(seed + k)
+        p, dy, dhf, bias = _cbwd_case(rng, opts)
+        g = orc.scan_complex_bwd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], dy, h0=p["h0"],
+                                 dh_final=dhf, delta_bias=bias, **opts)
+        grads = {"x": g["dx"], "delta": g["ddelta"], "B": g["dB"], "C": g["dC"], "D": g["dD"],
+                 "A.re": g["dA"].real, "A.im": g["dA"].imag, "h0.re": g["dh0"].real, "h0.im": g["dh0"].imag}
+        if bias is not None:
+            grads["bias"] = g["dbias"]
+        scale = max(1.0, max(float(np.max(np.abs(v))) for v in grads.values()))
+        for name, got in grads.items():
+            base, part = (name.split(".") + [None])[:2]
+            shape = (bias if base == "bias" else p[base]).shape
+            for idx in np.ndindex(shape):
+                def loss_at(delta_v):
+                    q = dict(p)
+                    bb = bias
+                    if base == "bias":
+                        bb = bias.copy()
+                        bb[idx] += delta_v
+                    else:
+                        arr = q[base].copy()
+                        arr[idx] += delta_v * (1j if part == "im" else 1.0)
+                        q[base] = arr
+                    return _closs(orc, q, dy, dhf, bb, opts)
+                ref = (bias if base == "bias" else p[base])[idx]
+                eps = 1e-6 * max(1.0, abs(ref))
+                fd = (loss_at(eps) - loss_at(-eps)) / (2 * eps)
+                assert abs(fd - got[idx]) <= 2e-7 * scale + 1e-6 * abs(fd), (opts, name, idx, fd, got[idx])
+
+
+def check_complex_bwd_identities(orc, seed=34):
+    """Exact identities: with delta and A fixed the outputs are linear in
+    (x, h0), so <dy, y> + Re<dhf, h_final> = <dx, x> + Re<dh0, h0>; and with
+    every imaginary part zero the gradients are the real scan's (the real
+    backward is pinned on its own) and the adjoint of h0 stays real."""
+    rng = np.random.default_rng(seed)
+    for opts in ({}, {"euler_b": True}):
+        p, dy, dhf, _ = _cbwd_case(rng, opts, Bsz=2, L=11, Dm=4, N=5)
+        x, delta, A, B, C, D, h0 = (p[k] for k in ("x", "delta", "A", "B", "C", "D", "h0"))
+        g = orc.scan_complex_bwd(x, delta, A, B, C, D, dy, h0=h0, dh_final=dhf, **opts)
+        y, hf = orc.scan_complex(x, delta, A, B, C, D, h0=h0, **opts)
+        lhs = np.sum(dy * y) + np.sum(dhf.real * hf.real + dhf.imag * hf.imag)
+        rhs = np.sum(g["dx"] * x) + np.sum(g["dh0"].real * h0.real + g["dh0"].imag * h0.imag)
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), (opts, lhs, rhs)
+        Ar, h0r, dhfr = A.real.copy(), h0.real.copy(), dhf.real.copy()
+        gc = orc.scan_complex_bwd(x, delta, Ar.astype(complex), B, C, D, dy, h0=h0r.astype(complex),
+                                  dh_final=dhfr.astype(complex), **opts)
+        gr = orc.scan_bwd(x, delta, Ar, B, C, D, dy, h0=h0r, dh_final=dhfr, **opts)
+        for k in ("dx", "ddelta", "dB", "dC", "dD"):
+            assert rel_err(gc[k], gr[k]) < 1e-12, (opts, k)
+        assert rel_err(gc["dA"].real, gr["dA"]) < 1e-11 and rel_err(gc["dh0"].real, gr["dh0"]) < 1e-12
+        assert np.all(gc["dh0"].imag == 0.0)
+
+
 def check_complex_rotation(orc, seed=21):
     """a = 0, x = 0: the state turns by w * sum(delta) at constant modulus."""
     rng = np.random.default_rng(seed)
@@ -709,5 +793,7 @@ ALL_CHECKS = [
     check_complex_exact_for_constant_input,
     check_complex_lfilter,
     check_complex_step_chain,
+    check_complex_bwd_finite_differences,
+    check_complex_bwd_identities,
     check_ssd_duality,
 ]

@@ -54,26 +54,26 @@ MUTANTS = [
     ("euler_ignored_in_scan", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    const int64_t nchan",
      "const int euler = 0;\n    const int64_t nchan", 0),
     # backward
-    ("bwd_dx_drops_D", "double gx = D[d] * g, gdt = 0.0;", "double gx = 0.0, gdt = 0.0;"),
-    ("bwd_lambda_uses_C_of_state_0", "lam[n] += C[r + n] * g;", "lam[n] += C[r] * g;"),
+    ("bwd_dx_drops_D", "double gx = D[d] * g, gdt = 0.0;", "double gx = 0.0, gdt = 0.0;", 0),
+    ("bwd_lambda_uses_C_of_state_0", "lam[n] += C[r + n] * g;", "lam[n] += C[r] * g;", 0),
     ("bwd_zoh_dk_ddelta_missing_abar", "const double dk_ddt = euler ? 1.0 : abar;",
      "const double dk_ddt = euler ? 1.0 : 1.0;"),
     ("bwd_euler_dk_ddelta_is_abar", "const double dk_ddt = euler ? 1.0 : abar;",
      "const double dk_ddt = euler ? abar : abar;"),
     ("bwd_dk_dA_constant", "dt * dt * zoh_dphi(z);", "dt * dt * 0.5;"),
     ("bwd_dphi_series_wrong", "term *= z * (double)(m + 1) / ((double)m * (double)(m + 2));",
-     "term *= z / (double)(m + 2);"),
+     "term *= z / (double)(m + 2);", 0),
     ("bwd_uses_h_t_for_h_prev", "const double hprev = hs[t * N + n];", "const double hprev = hs[(t + 1) * N + n];"),
     ("bwd_dC_uses_h_prev", "myC[r + n] += g * hs[(t + 1) * N + n];", "myC[r + n] += g * hs[t * N + n];"),
     ("bwd_lambda_not_decayed", "                            lam[n] *= abar;\n", ""),
     ("bwd_softplus_chain_missing", "                            gdt *= sigmoid(delta[i] + bias_d);\n",
-     "                            gdt *= 1.0;\n"),
-    ("bwd_sigmoid_without_bias", "gdt *= sigmoid(delta[i] + bias_d);", "gdt *= sigmoid(delta[i]);"),
+     "                            gdt *= 1.0;\n", 0),
+    ("bwd_sigmoid_without_bias", "gdt *= sigmoid(delta[i] + bias_d);", "gdt *= sigmoid(delta[i]);", 0),
     ("bwd_dB_missing_x", "myB[r + n] += lam[n] * k * x[i];", "myB[r + n] += lam[n] * k;"),
     ("bwd_dA_missing_abar", "dAd[n] += lam[n] * (dt * abar * hprev", "dAd[n] += lam[n] * (dt * hprev"),
     ("bwd_ddelta_missing_A", "gdt += lam[n] * (a[n] * abar * hprev", "gdt += lam[n] * (abar * hprev"),
     ("bwd_dh_final_ignored", "lam[n] = dh_final ? dh_final[(b * Dm + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
-    ("bwd_dbias_overwritten", "dbias_d += gdt;", "dbias_d = gdt;"),
+    ("bwd_dbias_overwritten", "dbias_d += gdt;", "dbias_d = gdt;", 0),
     ("bwd_forward_ignores_euler", "const double k = euler ? dt : dt * zoh_phi(z);\n                            hs[",
      "const double k = dt * zoh_phi(z);\n                            hs["),
     # complex A
@@ -91,6 +91,25 @@ MUTANTS = [
     ("cplx_D_of_channel_0", "C + r, D[d], N, euler);", "C + r, D[0], N, euler);", 1),
     ("cplx_euler_ignored_in_scan", "const int euler = (flags & ORACLE_EULER_B) != 0;\n    const int64_t nchan",
      "const int euler = 0;\n    const int64_t nchan", 1),
+    # backward of the complex-A scan
+    ("cbwd_adjoint_not_conjugated", "lam[n] *= conj(abar);", "lam[n] *= abar;"),
+    ("cbwd_G_abar_without_conj", "lam[n] * conj(hprev);", "lam[n] * hprev;"),
+    ("cbwd_du_without_conj", "creal(lam[n] * conj(k));", "creal(lam[n] * k);"),
+    ("cbwd_dk_dA_not_conjugated", "gk * conj(dt * dt * cdphi(z));", "gk * dt * dt * cdphi(z);"),
+    ("cbwd_ddelta_missing_A", "creal(gabar * conj(An * abar));", "creal(gabar * conj(abar));"),
+    ("cbwd_dA_missing_abar", "dAd[n] += gabar * conj(dt * abar) + gk", "dAd[n] += gabar * conj(dt) + gk"),
+    ("cbwd_euler_dk_ddelta_is_abar", "                                gdt += creal(gk);\n",
+     "                                gdt += creal(gk * conj(abar));\n"),
+    ("cbwd_dphi_series_wrong", "term *= z * (double)(m + 1) / ((double)m * (double)(m + 2));",
+     "term *= z * (double)(m + 1) / ((double)m * (double)(m + 3));", 1),
+    ("cbwd_dphi_closed_form_sign", "return (z * cexp(z) - (er + I * ei)) / (z * z);",
+     "return (z * cexp(z) + (er + I * ei)) / (z * z);"),
+    ("cbwd_C_into_imag_part", "lam[n] += C[r + n] * g;", "lam[n] += I * C[r + n] * g;", 1),
+    ("cbwd_dh_final_imag_ignored", "dh_final[j] + I * dh_final[j + 1]", "dh_final[j]"),
+    ("cbwd_dh0_imag_dropped", "dh0[j + 1] = cimag(lam[n]);", "dh0[j + 1] = 0.0;"),
+    ("cbwd_dC_uses_h_prev", "myC[r + n] += g * hs[(t + 1) * 2 * N + 2 * n];", "myC[r + n] += g * hs[t * 2 * N + 2 * n];"),
+    ("cbwd_h0_imag_dropped_in_forward", "hs[k] = h0 ? h0[(b * Dm + d) * 2 * N + k] : 0.0;",
+     "hs[k] = h0 && k % 2 == 0 ? h0[(b * Dm + d) * 2 * N + k] : 0.0;"),
     ("h_final_not_last_state",
      "h_final[(b * Dm + d) * N + n] = h[n];",
      "h_final[(b * Dm + d) * N + n] = h[n] * 0.5 + 0.5 * h[n] * (n == 0 ? 1.0 : 0.999);"),
