@@ -364,6 +364,43 @@ int ssm_scan_varlen_bwd(const void *x, const void *delta, const float *delta_bia
                         unsigned flags, void *stream);
 
 /*
+ * Backward of the complex-A scan (ssm_scan_complex_fwd): the chain rule on
+ * its recurrence (the bitig.info page on Mamba-3, section "Karmasik Degerli
+ * Durum Guncellemesi"; training as in "Mamba SSM Nedir?", section "Paralel
+ * Tarama Algoritmasi").  For the real loss L, the gradient of a complex
+ * quantity z is the pair (dL/dRe z, dL/dIm z).  With lambda_t = dL/dh_t,
+ *   lambda_t = C_t dy_t + conj(Abar_{t+1}) lambda_{t+1}   (lambda_{L-1} adds dh_final)
+ * (the output reads Re h_t, so C_t dy_t enters the real part only).
+ *
+ * Inputs: the forward's x, delta, delta_bias, A, B, C, D, h_init (shapes,
+ *   dtype and flags exactly as in ssm_scan_complex_fwd) and
+ *   dy       : [Bsz][L][Dm] dtype
+ *   dh_final : [Bsz][Dm][N][2] fp32 or NULL (zero)
+ * Outputs (overwritten, never accumulated):
+ *   dx, ddelta  : [Bsz][L][Dm] dtype  (ddelta for delta as passed)
+ *   ddelta_bias : [Dm] fp32 or NULL
+ *   dA          : [Dm][N][2] fp32     dD : [Dm] fp32
+ *   dB, dC      : [Bsz][L][N] fp32    (sums over channels)
+ *   dh_init     : [Bsz][Dm][N][2] fp32 or NULL
+ * No output may overlap an input or another output.  The forward states are
+ * recomputed.  Segments of 16 steps; library scratch (Acc = 4 bytes for bf16
+ * storage, 8 for fp32; S = ceil(L / 16), G groups, R = ceil(Dm / 256) blocks
+ * per batch row for bf16 and ceil(Dm / 128) for fp32):
+ *   (6N + 2) * S * Bsz * Dm * Acc      segment summaries and entering states
+ * + (4N + 2) * G * Bsz * Dm * Acc      adjoint entering each group, partials
+ * + 2 * (R + 1) * Bsz * L * N * Acc    partial sums of dB, dC; B/C rows
+ * A 16-step segment of x must span less than 1 GiB, else SSM_ERR_BAD_DIM.
+ * Dense batch only.
+ */
+int ssm_scan_complex_bwd(const void *x, const void *delta, const float *delta_bias,
+                         const float *A, const void *B, const void *C, const float *D,
+                         const float *h_init, const void *dy, const float *dh_final,
+                         void *dx, void *ddelta, float *ddelta_bias, float *dA,
+                         float *dB, float *dC, float *dD, float *dh_init,
+                         int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype,
+                         unsigned flags, void *stream);
+
+/*
  * One recurrent decode step on a resident state, updated in place
  * ("Mamba SSM Nedir?", section "Karmasiklik Karsilastirmasi": inference
  * updates a fixed-size state per token).  bf16 I/O:

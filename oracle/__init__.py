@@ -9,5 +9,5 @@ the matrix-exponential ZOH identity, the LTI convolution mode, limits and
 invariants; for the backward, finite differences of the forward and exact
 adjoint dot-product identities); no function is "parity unpinned".
 """
-from .oracle import (Oracle, scan, scan_bwd, scan_complex, scan_ssd, step, step_complex,  # noqa: F401
-                     max_threads, load)
+from .oracle import (Oracle, scan, scan_bwd, scan_complex, scan_complex_bwd, scan_ssd, step,  # noqa: F401
+                     step_complex, max_threads, load)

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libssmscan.so")
 ARCH = "gfx950"
 SOURCES = ["abi.cpp", "scan_f32.hip", "scan_f32_packed.hip", "scan_bf16.hip", "scan_bf16_packed.hip",
            "scan_launch.hip", "step_kernel.hip", "bwd_f32.hip", "bwd_f32_packed.hip", "bwd_bf16.hip",
-           "bwd_bf16_packed.hip", "cplx_f32.hip", "cplx_bf16.hip",
+           "bwd_bf16_packed.hip", "cplx_f32.hip", "cplx_bf16.hip", "cbwd_f32.hip", "cbwd_bf16.hip",
            "ssd_f32.hip", "ssd_bf16.hip", "probe.hip", "noalloc.hip"]
 
 # Packed-FP32 instructions are switched off for every device pass.

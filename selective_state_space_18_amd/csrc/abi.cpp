@@ -845,14 +845,8 @@ struct BwdPlan {
     int blocks_per_row;
 };
 
-BwdPlan make_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int dtype, int cus) {
-    BwdPlan bp;
-    bp.seg_len = ssm::bwd_segment_len(dtype);
-    bp.S = L > 0 ? (int)((L + bp.seg_len - 1) / bp.seg_len) : 1;
-    const int64_t tiles_per_b = (Dm + 63) / 64;
-    bp.blocks_per_row = (int)((tiles_per_b + kWavesPerBlock - 1) / kWavesPerBlock);
-    const int64_t rows = Bsz * bp.blocks_per_row;
-    const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+// Segments per group for `rows` blocks per group and `slots` resident blocks.
+void pick_groups(BwdPlan &bp, int64_t rows, int64_t slots) {
     int64_t G = bp.S;
     int64_t best = -1;
     for (int64_t g = bp.S; g >= 1; --g) {
@@ -866,6 +860,29 @@ BwdPlan make_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int dtype, int cus) {
     }
     bp.seg_per_group = (int)G;
     bp.groups = (int)((bp.S + G - 1) / G);
+}
+
+BwdPlan make_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int dtype, int cus) {
+    BwdPlan bp;
+    bp.seg_len = ssm::bwd_segment_len(dtype);
+    bp.S = L > 0 ? (int)((L + bp.seg_len - 1) / bp.seg_len) : 1;
+    const int64_t tiles_per_b = (Dm + 63) / 64;
+    bp.blocks_per_row = (int)((tiles_per_b + kWavesPerBlock - 1) / kWavesPerBlock);
+    pick_groups(bp, Bsz * bp.blocks_per_row, 2 * (int64_t)(cus > 0 ? cus : 256));
+    return bp;
+}
+
+// Complex-A backward: cbwd_segment_len() steps per segment, cbwd_waves()
+// waves per main-kernel block and one such block per CU (its state
+// checkpoints take most of the LDS).
+BwdPlan make_cbwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int dtype, int cus) {
+    BwdPlan bp;
+    bp.seg_len = ssm::cbwd_segment_len();
+    bp.S = L > 0 ? (int)((L + bp.seg_len - 1) / bp.seg_len) : 1;
+    const int64_t tiles_per_b = (Dm + 63) / 64;
+    const int w = ssm::cbwd_waves(dtype);
+    bp.blocks_per_row = (int)((tiles_per_b + w - 1) / w);
+    pick_groups(bp, Bsz * bp.blocks_per_row, (int64_t)(cus > 0 ? cus : 256));
     return bp;
 }
 
@@ -932,6 +949,9 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
             hipError_t r = ssm::launch_fill(dA, DN, 0.f, s);
             if (r == hipSuccess) r = ssm::launch_fill(dD, Dm, 0.f, s);
             if (r == hipSuccess) r = ssm::launch_fill(ddelta_bias, ddelta_bias ? Dm : 0, 0.f, s);
+            // dB, dC are sums over channels: zero when there are none
+            if (r == hipSuccess) r = ssm::launch_fill(dB, BLN, 0.f, s);
+            if (r == hipSuccess) r = ssm::launch_fill(dC, BLN, 0.f, s);
             if (r == hipSuccess && dh_init != nullptr) {
                 // (packed: every sequence is empty, or Dm is 0)
                 ssm::ScanParams z;
@@ -1078,6 +1098,184 @@ int bwd_impl(const void *x, const void *delta, const float *delta_bias, const fl
     return ok();
 }
 
+// Complex diagonal A: A, dA [Dm][N][2]; h_init, dh_final, dh_init
+// [Bsz][Dm][N][2] (re, im pairs).  The forward's aggregate and carry passes
+// (cplx_pass) give the state entering every backward segment.
+int cbwd_impl(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+              const void *C, const float *D, const float *h_init, const void *dy, const float *dh_final, void *dx,
+              void *ddelta, float *ddelta_bias, float *dA, float *dB, float *dC, float *dD, float *dh_init,
+              int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, unsigned flags, void *stream) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return fail(SSM_ERR_BAD_DTYPE, "dtype %d is not SSM_F32 or SSM_BF16", dtype);
+    if (flags & ~kKnownFlags) return fail(SSM_ERR_BAD_OPTION, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    if (!supported_n(N)) return fail(SSM_ERR_UNSUPPORTED_N, "N = %lld; supported: 1, 2, 4, 8, 16", (long long)N);
+    if (Bsz < 0 || L < 0 || Dm < 0)
+        return fail(SSM_ERR_BAD_DIM, "negative size (Bsz=%lld, L=%lld, Dm=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm);
+    int64_t BL, BLD, BLN, DN, BD, BDN;
+    if (!mul_ok(Bsz, L, &BL) || !mul_ok(BL, Dm, &BLD) || !mul_ok(BL, N, &BLN) || !mul_ok(Dm, N, &DN) ||
+        !mul_ok(Bsz, Dm, &BD) || !mul_ok(BD, N, &BDN) || BD > INT32_MAX / 2 || Bsz * ((Dm + 63) / 64) > INT32_MAX / 8 ||
+        DN > INT64_MAX / 4 || BDN > INT64_MAX / 4)
+        return fail(SSM_ERR_BAD_DIM, "sizes overflow (Bsz=%lld, L=%lld, Dm=%lld, N=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm, (long long)N);
+    const int64_t es = dtype_size(dtype);
+    const int seg = ssm::cbwd_segment_len();
+    if (seg * Dm * es >= kMaxStepBytes)
+        return fail(SSM_ERR_BAD_DIM, "backward: a %d-step segment of x (Dm = %lld) spans %lld bytes; the limit is 1 GiB",
+                    seg, (long long)Dm, (long long)(seg * Dm * es));
+    const Arg in[] = {{x, BLD, es, "x"},
+                      {delta, BLD, es, "delta"},
+                      {A, 2 * DN, 4, "A"},
+                      {B, BLN, es, "B"},
+                      {C, BLN, es, "C"},
+                      {D, Dm, 4, "D"},
+                      {delta_bias, delta_bias ? Dm : 0, 4, "delta_bias"},
+                      {h_init, h_init ? 2 * BDN : 0, 4, "h_init"},
+                      {dy, BLD, es, "dy"},
+                      {dh_final, dh_final ? 2 * BDN : 0, 4, "dh_final"}};
+    const Arg out[] = {{dx, BLD, es, "dx"},
+                       {ddelta, BLD, es, "ddelta"},
+                       {ddelta_bias, ddelta_bias ? Dm : 0, 4, "ddelta_bias"},
+                       {dA, 2 * DN, 4, "dA"},
+                       {dB, BLN, 4, "dB"},
+                       {dC, BLN, 4, "dC"},
+                       {dD, Dm, 4, "dD"},
+                       {dh_init, dh_init ? 2 * BDN : 0, 4, "dh_init"}};
+    constexpr int nin = 10, nout = 8;
+    int rc;
+    if ((rc = check_args(in, nin)) || (rc = check_args(out, nout))) return rc;
+    for (int i = 0; i < nout; ++i) {
+        if ((rc = check_output(out[i], in, nin))) return rc;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(out[i], out[j])) return fail(SSM_ERR_ALIAS, "%s overlaps %s", out[i].name, out[j].name);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (BD == 0 || L == 0) {
+        e = timed(SSM_K_STATE_INIT, s, [&] {
+            hipError_t r = ssm::launch_fill(dA, 2 * DN, 0.f, s);
+            if (r == hipSuccess) r = ssm::launch_fill(dD, Dm, 0.f, s);
+            if (r == hipSuccess) r = ssm::launch_fill(ddelta_bias, ddelta_bias ? Dm : 0, 0.f, s);
+            if (r == hipSuccess) r = ssm::launch_fill(dB, BLN, 0.f, s);
+            if (r == hipSuccess) r = ssm::launch_fill(dC, BLN, 0.f, s);
+            if (r == hipSuccess && dh_init != nullptr) {
+                // dh_init = dh_final (or zero), 2N floats per channel
+                ssm::ScanParams z;
+                std::memset(&z, 0, sizeof z);
+                z.Bsz = Bsz;
+                z.Dm = Dm * 2;
+                z.h_init = dh_final;
+                z.h_final = dh_init;
+                r = ssm::launch_state_init(z, (int)N, s);
+            }
+            return r;
+        });
+        return e == hipSuccess ? ok() : hip_fail(e, "zero-size backward");
+    }
+
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int cus = 0;
+    if ((rc = device_cus(dev, &cus))) return rc;
+
+    ssm::BwdParams q;
+    std::memset(&q, 0, sizeof q);
+    ssm::ScanParams &p = q.f;
+    p.x = x;
+    p.delta = delta;
+    p.B = B;
+    p.C = C;
+    p.A = A;
+    p.D = D;
+    p.h_init = h_init;
+    p.Bsz = Bsz;
+    p.L = L;
+    p.Dm = Dm;
+    p.waves_per_block = kWavesPerBlock;
+    p.delta_bias = delta_bias;
+    p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+    p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
+    const BwdPlan bp = make_cbwd_plan(Bsz, L, Dm, dtype, cus);
+    p.seg_len = bp.seg_len;
+    p.S = bp.S;
+    p.tiles_per_b = (int)((Dm + 63) / 64);
+    p.n_tiles = (int)(Bsz * p.tiles_per_b);
+    q.dy = dy;
+    q.dh_final = dh_final;
+    q.dx = dx;
+    q.ddelta = ddelta;
+    q.ddelta_bias = ddelta_bias;
+    q.dA = dA;
+    q.dB = dB;
+    q.dC = dC;
+    q.dD = dD;
+    q.dh_init = dh_init;
+    q.blocks_per_row = bp.blocks_per_row;
+    q.seg_per_group = bp.seg_per_group;
+    q.n_groups = bp.groups;
+    if ((int64_t)q.n_groups * Bsz * q.blocks_per_row >= ((int64_t)1 << 31) ||
+        (int64_t)((p.n_tiles + kWavesPerBlock - 1) / kWavesPerBlock) * p.S >= ((int64_t)1 << 31))
+        return fail(SSM_ERR_BAD_DIM, "backward grid too large (Bsz=%lld, L=%lld, Dm=%lld)", (long long)Bsz,
+                    (long long)L, (long long)Dm);
+
+    const size_t acc = ssm::scan_acc_bytes(dtype);
+    const size_t S = (size_t)p.S;
+    const size_t sz_bc = align256((size_t)BL * 2 * N * acc);
+    const size_t sz_agg = align256((S > 1 ? S - 1 : 0) * (2 * N + 1) * BD * acc);
+    const size_t sz_gin = align256(S * 2 * N * BD * acc);
+    const size_t sz_ragg = align256(S * (2 * N + 1) * BD * acc);
+    const size_t sz_gout = align256((size_t)q.n_groups * 2 * N * BD * acc);
+    const size_t sz_pbc = align256((size_t)q.blocks_per_row * 2 * BLN * acc);
+    const size_t sz_pa = align256((size_t)q.n_groups * BD * 2 * N * acc);
+    const size_t sz_pd = align256((size_t)q.n_groups * BD * 2 * acc);
+
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    void *ws = nullptr;
+    if ((rc = workspace(dev, s, sz_bc + sz_agg + sz_gin + sz_ragg + sz_gout + sz_pbc + sz_pa + sz_pd, &ws)))
+        return rc;
+    char *base = static_cast<char *>(ws);
+    p.bc = base;
+    base += sz_bc;
+    p.agg = sz_agg ? base : nullptr;
+    base += sz_agg;
+    p.gin = base;
+    base += sz_gin;
+    q.ragg = base;
+    base += sz_ragg;
+    q.gout = base;
+    base += sz_gout;
+    q.part_bc = base;
+    base += sz_pbc;
+    q.part_a = base;
+    base += sz_pa;
+    q.part_d = base;
+
+    const int n = (int)N;
+    auto fwd = [&](ssm::ScanPass ps) {
+        return dtype == SSM_F32 ? ssm::cplx_pass_f32(ps, p, n, s) : ssm::cplx_pass_bf16(ps, p, n, s);
+    };
+    auto bwd = [&](ssm::BwdPass pass) {
+        return dtype == SSM_F32 ? ssm::cbwd_pass_f32(pass, q, n, s) : ssm::cbwd_pass_bf16(pass, q, n, s);
+    };
+    if ((e = timed(SSM_K_BC_PREP, s, [&] { return fwd(ssm::ScanPass::kPrep); })) != hipSuccess)
+        return hip_fail(e, "B/C conversion launch");
+    if (p.S > 1) {
+        if ((e = timed(SSM_K_SCAN_AGGREGATE, s, [&] { return fwd(ssm::ScanPass::kAggregate); })) != hipSuccess)
+            return hip_fail(e, "forward aggregate launch");
+        if ((e = timed(SSM_K_SCAN_CARRY, s, [&] { return fwd(ssm::ScanPass::kCarry); })) != hipSuccess)
+            return hip_fail(e, "forward carry launch");
+        if ((e = timed(SSM_K_BWD_AGGREGATE, s, [&] { return bwd(ssm::BwdPass::kAggregate); })) != hipSuccess)
+            return hip_fail(e, "backward aggregate launch");
+    }
+    if ((e = timed(SSM_K_BWD_CARRY, s, [&] { return bwd(ssm::BwdPass::kCarry); })) != hipSuccess)
+        return hip_fail(e, "backward carry launch");
+    if ((e = timed(SSM_K_BWD_MAIN, s, [&] { return bwd(ssm::BwdPass::kMain); })) != hipSuccess)
+        return hip_fail(e, "backward main launch");
+    if ((e = timed(SSM_K_BWD_REDUCE, s, [&] { return bwd(ssm::BwdPass::kReduce); })) != hipSuccess)
+        return hip_fail(e, "backward reduction launch");
+    return ok();
+}
+
 }  // namespace
 
 namespace ssm {
@@ -1162,6 +1360,15 @@ int ssm_scan_complex_fwd(const void *x, const void *delta, const float *delta_bi
                          const void *C, const float *D, const float *h_init, void *y, float *h_final, int64_t Bsz,
                          int64_t L, int64_t Dm, int64_t N, int dtype, unsigned flags, void *stream) {
     return cplx_impl(x, delta, delta_bias, A, B, C, D, h_init, y, h_final, Bsz, L, Dm, N, dtype, flags, stream);
+}
+
+int ssm_scan_complex_bwd(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,
+                         const void *C, const float *D, const float *h_init, const void *dy, const float *dh_final,
+                         void *dx, void *ddelta, float *ddelta_bias, float *dA, float *dB, float *dC, float *dD,
+                         float *dh_init, int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, unsigned flags,
+                         void *stream) {
+    return cbwd_impl(x, delta, delta_bias, A, B, C, D, h_init, dy, dh_final, dx, ddelta, ddelta_bias, dA, dB, dC, dD,
+                     dh_init, Bsz, L, Dm, N, dtype, flags, stream);
 }
 
 int ssm_scan_ssd_fwd(const void *x, const void *delta, const float *delta_bias, const float *A, const void *B,

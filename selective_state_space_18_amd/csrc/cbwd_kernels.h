@@ -1,0 +1,656 @@
+// Backward of the selective scan with complex diagonal A for gfx950:
+// templates shared by cbwd_bf16.hip and cbwd_f32.hip.
+//
+// The recurrence is the complex-A forward's (cplx_kernels.h; the bitig.info
+// page on Mamba-3, section "Karmasik Degerli Durum Guncellemesi"), and the
+// gradients its chain rule ("Mamba SSM Nedir?", section "Paralel Tarama
+// Algoritmasi": training runs the same scan).  Every complex quantity is a
+// pair of reals; for a real loss and w = p q the gradient pair of p is G_w
+// conj(q) as a complex number.  With lambda = dL/dh_t (complex), u = B_t[n] x_t
+// and k the input coefficient ((Abar - 1)/A, or delta for the Euler rule):
+//   lambda   += C_t[n] dy_t                (y reads Re h)
+//   dL/du     = Re(lambda conj(k))         -> dx, dB
+//   ddelta   += Re(lambda conj(h_{t-1}) conj(A Abar)) + Re(lambda u conj(dk/ddelta))
+//   dA       += lambda conj(h_{t-1}) conj(delta Abar)  + lambda u conj(dk/dA)
+//   lambda    = lambda conj(Abar)          (into step t-1)
+// with dk/ddelta = Abar, dk/dA = (delta A Abar - (Abar - 1)) / A^2 (ZOH), and
+// dk/ddelta = 1, dk/dA = 0 (Euler).
+//
+// Work layout, as the real backward (bwd_kernels.h) with one lane per channel:
+//   1. the complex forward's aggregate and carry passes give the state
+//      entering every 16-step segment;
+//   2. cbwd_aggregate_kernel runs the adjoint back from zero over each segment
+//      but the first; cbwd_carry_kernel composes these summaries from the
+//      right and keeps the adjoint entering the last segment of each group;
+//   3. cbwd_main_kernel: one wave per 64-channel tile and group of segments,
+//      last segment first.  A segment's x, delta and dy are loaded once; its
+//      state every 4 steps goes to LDS; each 4-step sub-chunk's states are
+//      recomputed from its checkpoint with the forward's own step, then the
+//      adjoint runs back over them.  dB and dC (sums over channels) go through
+//      the real backward's reduce-scatter and per-block LDS sums, then
+//      cbwd_reduce_kernel.
+// The 2N-value states make the checkpoints 32 KB per wave (fp32 arithmetic),
+// so a block holds all of a compute unit's waves: one wave per SIMD.
+#pragma once
+
+#include "bwd_kernels.h"
+#include "cplx_kernels.h"
+
+namespace ssm {
+
+namespace {
+
+template <typename Acc>
+struct CbwdShape;
+template <>
+struct CbwdShape<float> {
+    static constexpr int kWaves = 4;  // waves per block (checkpoints: 32 KB each)
+};
+template <>
+struct CbwdShape<double> {
+    static constexpr int kWaves = 2;  // (64 KB each)
+};
+constexpr int kCbwdT = 16;  // segment length
+constexpr int kCbwdK = 4;   // checkpoint interval = sub-chunk length
+
+// A and 1/A of one channel.  The exponent is formed as (delta * unit) * A with
+// the unit taken per step (log2 e and 1/(2 pi) in fp32 arithmetic, where the
+// transcendental unit takes base-2 exponents and angles in revolutions), so
+// no scaled copy of A is kept.
+template <int N, typename Acc>
+struct CbwdConst {
+    Acc ar[N], ai[N];  // A (the forward's tiny real stand-in for |A| ~ 0)
+    Acc wr[N], wi[N];  // 1 / A
+    __device__ __forceinline__ explicit CbwdConst(const float *A2) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            Acc a = (Acc)A2[2 * n], w = (Acc)A2[2 * n + 1];
+            if (abs_(a) < (Acc)(-kTinyA) && abs_(w) < (Acc)(-kTinyA)) {
+                a = (Acc)kTinyA;
+                w = 0;
+            }
+            ar[n] = a;
+            ai[n] = w;
+            const Acc den = a * a + w * w;
+            wr[n] = a / den;
+            wi[n] = -w / den;
+        }
+    }
+};
+
+// delta in the exponent units of cplx_exp_units: (real part, angle).
+template <typename Acc>
+__device__ __forceinline__ void delta_units(Acc dv, Acc &ur, Acc &ui) {
+    ur = sizeof(Acc) == 4 ? dv * (Acc)kLog2e : dv;
+    ui = sizeof(Acc) == 4 ? dv * (Acc)0.15915494309189535 : dv;
+}
+
+// Abar = exp(delta A) of state n, Re(Abar - 1) (er; Im(Abar - 1) = abi) and
+// the input coefficient k ((Abar - 1)/A, or delta for the Euler rule).
+template <int N, bool kEuler, typename Acc>
+__device__ __forceinline__ void cplx_coef(const CbwdConst<N, Acc> &cc, int n, Acc dv, Acc ur, Acc ui, Acc &abr,
+                                          Acc &abi, Acc &kr, Acc &ki, Acc &er) {
+    const Acc zi = ui * cc.ai[n];
+    Acc mag, c, s, em1;
+    cplx_exp_units(ur * cc.ar[n], zi, mag, c, s, em1);
+    abr = mag * c;
+    abi = mag * s;
+    er = fma_(em1, c, cplx_cos_m1(zi, c));
+    if constexpr (kEuler) {
+        kr = dv;
+        ki = 0;
+    } else {
+        kr = er * cc.wr[n] - abi * cc.wi[n];
+        ki = er * cc.wi[n] + abi * cc.wr[n];
+    }
+}
+
+// One forward step of one channel (states advanced in place).
+template <int N, bool kEuler, typename Acc>
+__device__ __forceinline__ void cbwd_fwd_step(const CbwdConst<N, Acc> &cc, const Acc (&row)[2 * N], Acc xv, Acc dv,
+                                              Acc (&hr)[N], Acc (&hi)[N]) {
+    Acc ur, ui;
+    delta_units(dv, ur, ui);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        Acc abr, abi, kr, ki, er;
+        cplx_coef<N, kEuler>(cc, n, dv, ur, ui, abr, abi, kr, ki, er);
+        const Acc u = row[n] * xv;
+        const Acc r = hr[n], m = hi[n];
+        hr[n] = fma_(abr, r, fma_(-abi, m, kr * u));
+        hi[n] = fma_(abr, m, fma_(abi, r, ki * u));
+    }
+}
+
+// dk/dA of state n for ZOH: (delta A Abar - (Abar - 1)) / A^2 = delta^2 phi'(delta A),
+// phi'(z) = (z e^z - (e^z - 1)) / z^2.  Near z = 0 the closed form cancels (it
+// loses about log2(2/|z|) bits): there the Taylor polynomial to z^4 is used,
+// whose truncation is below |z|^5 / 840 -- for |z| < 1/8 in fp32 arithmetic,
+// |z| < 1/1000 in fp64.
+template <int N, typename Acc>
+__device__ __forceinline__ void cplx_dk_da(const CbwdConst<N, Acc> &cc, int n, Acc dv, Acc abr, Acc abi, Acc er,
+                                           Acc &gr, Acc &gi) {
+    const Acc zr = dv * cc.ar[n], zi = dv * cc.ai[n];
+    constexpr Acc kSmall2 = sizeof(Acc) == 4 ? (Acc)(1.0 / 64.0) : (Acc)1e-6;
+    if (zr * zr + zi * zi < kSmall2) {
+        // 1/2 + z/3 + z^2/8 + z^3/30 + z^4/144 (Horner, complex)
+        Acc pr = (Acc)(1.0 / 144.0), pi = 0;
+        const Acc cs[4] = {(Acc)(1.0 / 30.0), (Acc)(1.0 / 8.0), (Acc)(1.0 / 3.0), (Acc)0.5};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const Acc r = fma_(pr, zr, fma_(-pi, zi, cs[k]));
+            const Acc m = fma_(pr, zi, pi * zr);
+            pr = r;
+            pi = m;
+        }
+        const Acc d2 = dv * dv;
+        gr = pr * d2;
+        gi = pi * d2;
+    } else {
+        // (z Abar - E) W^2, W = 1/A
+        const Acc nr = (zr * abr - zi * abi) - er;
+        const Acc ni = (zr * abi + zi * abr) - abi;
+        const Acc w2r = cc.wr[n] * cc.wr[n] - cc.wi[n] * cc.wi[n];
+        const Acc w2i = 2 * cc.wr[n] * cc.wi[n];
+        gr = nr * w2r - ni * w2i;
+        gi = nr * w2i + ni * w2r;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse aggregate: segments 1..S-1, adjoint from zero at the segment end;
+// stores what reaches the segment start (after its first step's decay) and
+// the segment's sum of delta.  ragg [S][2N+1][B*D].
+
+template <typename T, int N, bool kEuler, bool kPre>
+__global__ __launch_bounds__(kBlock) void cbwd_aggregate_kernel(BwdParams q) {
+    typedef typename AccOf<T>::type Acc;
+    const ScanParams &p = q.f;
+    const int blocks_per_seg = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int s = lb / blocks_per_seg + 1;
+    const int wave = uniform((int)threadIdx.x / kWave);
+    const int tile = (lb - (s - 1) * blocks_per_seg) * p.waves_per_block + wave;
+    if (wave >= p.waves_per_block || tile >= p.n_tiles) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t b = tile / p.tiles_per_b;
+    const int64_t d0 = (int64_t)(tile - b * p.tiles_per_b) * kWave;
+    const bool active = d0 + lane < p.Dm;
+    const int64_t d = active ? d0 + lane : d0;
+    const int64_t ch = b * p.Dm + d;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t t0 = (int64_t)s * p.seg_len;
+    const int nsteps = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
+
+    const CbwdConst<N, Acc> cc(p.A + d * 2 * N);
+    const Acc bias = (kPre && p.delta_bias != nullptr) ? (Acc)p.delta_bias[d] : (Acc)0;
+    const bool soft = p.delta_softplus != 0;
+    const int64_t off = (b * p.L + t0) * p.Dm + d0;
+    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rdl = make_rsrc(static_cast<const T *>(p.delta) + off, nsteps * row);
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const T *>(q.dy) + off, nsteps * row);
+    const int32_t voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
+    const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
+
+    Acc lr[N], li[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) lr[n] = li[n] = 0;
+    Acc lam = 0;
+    // the step's delta and dy, and the previous step's fetched meanwhile
+    uint32_t dlc = buf_load_raw<T>(rdl, voff, (nsteps - 1) * row);
+    uint32_t dyc = buf_load_raw<T>(rdy, voff, (nsteps - 1) * row);
+    for (int i = nsteps - 1; i >= 0; --i) {
+        const int j = i > 0 ? i - 1 : 0;
+        const uint32_t dln = buf_load_raw<T>(rdl, voff, j * row);
+        const uint32_t dyn = buf_load_raw<T>(rdy, voff, j * row);
+        Acc rw[2 * N];
+        load_row<N>(rw, bcp + (int64_t)i * (2 * N));
+        Acc dv = (Acc)raw_to_f32<T>(dlc);
+        if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
+        const Acc gy = (Acc)raw_to_f32<T>(dyc);
+        lam += dv;
+        Acc ur, ui;
+        delta_units(dv, ur, ui);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            Acc mag, c, sn, em1;
+            cplx_exp_units(ur * cc.ar[n], ui * cc.ai[n], mag, c, sn, em1);
+            const Acc abr = mag * c, abi = mag * sn;
+            const Acc r = fma_(rw[N + n], gy, lr[n]), m = li[n];
+            lr[n] = fma_(r, abr, m * abi);
+            li[n] = fma_(m, abr, -r * abi);
+        }
+        dlc = dln;
+        dyc = dyn;
+    }
+    if (!active) return;
+    Acc *a = static_cast<Acc *>(q.ragg) + (int64_t)s * (2 * N + 1) * BD + ch;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        a[(int64_t)(2 * n) * BD] = lr[n];
+        a[(int64_t)(2 * n + 1) * BD] = li[n];
+    }
+    a[(int64_t)(2 * N) * BD] = lam;
+}
+
+// Reverse carry: one thread per (state n, channel).  The adjoint entering the
+// last segment is dL/dh_final; segment s-1 receives conj(exp(A sum(delta over
+// s))) times what enters s, plus s's summary.  Only the adjoint entering each
+// group's last segment is kept (gout [groups][2N][B*D]).
+template <typename Acc, int N>
+__global__ __launch_bounds__(kBlock) void cbwd_carry_kernel(BwdParams q) {
+    const ScanParams &p = q.f;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= BD * N) return;
+    const int n = (int)(i / BD);
+    const int64_t ch = i - (int64_t)n * BD;
+    const int64_t d = ch % p.Dm;
+    const Acc a = (Acc)p.A[(d * N + n) * 2], w = (Acc)p.A[(d * N + n) * 2 + 1];
+    Acc lr = 0, li = 0;
+    if (q.dh_final) {
+        lr = (Acc)q.dh_final[(ch * N + n) * 2];
+        li = (Acc)q.dh_final[(ch * N + n) * 2 + 1];
+    }
+    const Acc *ragg = static_cast<const Acc *>(q.ragg);
+    Acc *out = static_cast<Acc *>(q.gout);
+    const int64_t sa = (int64_t)(2 * N + 1) * BD, sg = (int64_t)(2 * N) * BD;
+    const int spg = q.seg_per_group;
+    auto put = [&](int grp) {
+        out[(int64_t)grp * sg + (int64_t)(2 * n) * BD + ch] = lr;
+        out[(int64_t)grp * sg + (int64_t)(2 * n + 1) * BD + ch] = li;
+    };
+    put((p.S - 1) / spg);
+    for (int s = p.S - 1; s >= 1; --s) {
+        const Acc lam = ragg[(int64_t)s * sa + (int64_t)(2 * N) * BD + ch];
+        const Acc gr = ragg[(int64_t)s * sa + (int64_t)(2 * n) * BD + ch];
+        const Acc gi = ragg[(int64_t)s * sa + (int64_t)(2 * n + 1) * BD + ch];
+        Acc mag, c, sn, em1;
+        cplx_exp(a * lam, w * lam, mag, c, sn, em1);
+        const Acc er = mag * c, ei = mag * sn;  // exp(A sum); the adjoint takes its conjugate
+        const Acc nr = fma_(er, lr, fma_(ei, li, gr));
+        const Acc ni = fma_(er, li, fma_(-ei, lr, gi));
+        lr = nr;
+        li = ni;
+        if ((s - 1) % spg == spg - 1) put((s - 1) / spg);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Main pass.  part_bc [blocks per row][2][B*L*N] (block sums of the dB and dC
+// lane values), part_a [groups][B*D][2N] (dA), part_d [groups][B*D][2] (dD,
+// d(delta_bias)).
+template <typename T, int N, bool kEuler, bool kPre>
+__global__ __launch_bounds__(CbwdShape<typename AccOf<T>::type>::kWaves *kWave) void cbwd_main_kernel(BwdParams q) {
+    typedef typename AccOf<T>::type Acc;
+    constexpr int kWaves = CbwdShape<Acc>::kWaves;
+    constexpr int kT = kCbwdT, kK = kCbwdK, kNck = kT / kK;
+    __shared__ Acc ck[kWaves][kNck][2 * N][kWave];  // state checkpoints, per wave
+    __shared__ Acc bacc[kWaves][kT][2][N];          // per-wave dB, dC sums of one segment
+    static_assert(sizeof(ck) + sizeof(bacc) <= 163840, "one block per compute unit must fit its 160 KB of LDS");
+    const ScanParams &p = q.f;
+
+    const int wave = uniform((int)threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_grp = (int)p.Bsz * q.blocks_per_row;
+    const int grp = lb / per_grp;
+    const int rem = lb - grp * per_grp;
+    const int64_t b = rem / q.blocks_per_row;
+    const int br = rem - (int)b * q.blocks_per_row;
+    const int tir = br * kWaves + wave;
+    const bool tile_ok = tir < p.tiles_per_b;
+    const int64_t d0 = (int64_t)(tile_ok ? tir : p.tiles_per_b - 1) * kWave;
+    const bool in_range = d0 + lane < p.Dm;
+    const int64_t d = in_range ? d0 + lane : d0;  // idle lanes shadow a valid channel
+    const int64_t ch = b * p.Dm + d;
+    const int64_t BD = p.Bsz * p.Dm;
+    const int64_t BLN = p.Bsz * p.L * N;
+    // waves past the row and lanes past it run on x = dy = 0: every dB, dC,
+    // dx and d(delta) share is a multiple of x or dy, and they store nothing
+    const bool live = tile_ok && in_range;
+
+    const CbwdConst<N, Acc> cc(p.A + d * 2 * N);
+    const Acc Dd = (Acc)p.D[d];
+    const Acc bias = (kPre && p.delta_bias != nullptr) ? (Acc)p.delta_bias[d] : (Acc)0;
+    const bool soft = p.delta_softplus != 0;
+    const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
+    const int32_t voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
+
+    Acc dAr[N], dAi[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) dAr[n] = dAi[n] = 0;
+    Acc dDacc = 0, dbacc = 0;
+    for (int e = lane; e < kT * 2 * N; e += kWave) (&bacc[wave][0][0][0])[e] = 0;
+
+    // the block's dB/dC sums of the segment's steps, each over the waves in
+    // wave order (between two barriers)
+    auto write_segment_sums = [&](int64_t t0, int nseg) {
+        Acc *dst = static_cast<Acc *>(q.part_bc) + ((int64_t)br * 2) * BLN + (b * p.L + t0) * N;
+        constexpr int kE = kT * 2 * N;
+        constexpr int kPerWave = (kE + kWaves - 1) / kWaves;
+        for (int k = lane; k < kPerWave; k += kWave) {
+            const int e = wave * kPerWave + k;
+            if (e >= kE) break;
+            const int i = e / (2 * N);
+            const int v = (e / N) & 1;
+            const int n = e % N;
+            Acc sum = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) sum += bacc[w][i][v][n];
+            if (i < nseg) dst[(int64_t)v * BLN + (int64_t)i * N + n] = sum;
+        }
+    };
+
+    // the adjoint entering the group's last segment from the right
+    Acc lr[N], li[N];
+    {
+        const Acc *gout = static_cast<const Acc *>(q.gout);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            lr[n] = gout[((int64_t)grp * 2 * N + 2 * n) * BD + ch];
+            li[n] = gout[((int64_t)grp * 2 * N + 2 * n + 1) * BD + ch];
+        }
+    }
+    for (int si = q.seg_per_group - 1; si >= 0; --si) {
+        const int s = grp * q.seg_per_group + si;
+        if (s >= p.S) continue;
+        const int64_t t0 = (int64_t)s * kT;
+        const int nseg = uniform((int)((t0 + kT < p.L ? t0 + kT : p.L) - t0));
+        const int64_t off = (b * p.L + t0) * p.Dm + d0;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const T *>(p.x) + off, nseg * row);
+        const __amdgpu_buffer_rsrc_t rdl = make_rsrc(static_cast<const T *>(p.delta) + off, nseg * row);
+        const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const T *>(q.dy) + off, nseg * row);
+        const __amdgpu_buffer_rsrc_t rdx = make_rsrc(static_cast<const T *>(q.dx) + off, nseg * row);
+        const __amdgpu_buffer_rsrc_t rdd = make_rsrc(static_cast<const T *>(q.ddelta) + off, nseg * row);
+        const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
+        // the segment's inputs, once
+        uint32_t xr[kT], dr[kT], yr[kT];
+#pragma unroll
+        for (int i = 0; i < kT; ++i) {
+            const int so = (i < nseg ? i : nseg - 1) * row;
+            xr[i] = buf_load_raw<T>(rx, voff, so);
+            dr[i] = buf_load_raw<T>(rdl, voff, so);
+            yr[i] = buf_load_raw<T>(rdy, voff, so);
+        }
+        auto xval = [&](int i) { return live ? (Acc)raw_to_f32<T>(xr[i]) : (Acc)0; };
+        auto gval = [&](int i) { return live ? (Acc)raw_to_f32<T>(yr[i]) : (Acc)0; };
+        auto dval = [&](int i) {
+            Acc v = (Acc)raw_to_f32<T>(dr[i]);
+            if constexpr (kPre) v = soft ? softplus_(v + bias) : v + bias;
+            return v;
+        };
+
+        // checkpoints: the state before steps 0, 4, 8, 12 of the segment
+        Acc hr[N], hi[N];
+        if (s == 0) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                hr[n] = p.h_init ? (Acc)p.h_init[(ch * N + n) * 2] : (Acc)0;
+                hi[n] = p.h_init ? (Acc)p.h_init[(ch * N + n) * 2 + 1] : (Acc)0;
+            }
+        } else {
+            const Acc *gin = static_cast<const Acc *>(p.gin);
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                hr[n] = gin[((int64_t)s * 2 * N + 2 * n) * BD + ch];
+                hi[n] = gin[((int64_t)s * 2 * N + 2 * n + 1) * BD + ch];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kNck; ++j) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                ck[wave][j][2 * n][lane] = hr[n];
+                ck[wave][j][2 * n + 1][lane] = hi[n];
+            }
+            if (j + 1 < kNck) {
+#pragma unroll
+                for (int i = 0; i < kK; ++i) {
+                    const int t = j * kK + i;
+                    if (t < nseg) {
+                        Acc rw[2 * N];
+                        load_row<N>(rw, bcp + (int64_t)t * (2 * N));
+                        cbwd_fwd_step<N, kEuler>(cc, rw, (Acc)raw_to_f32<T>(xr[t]), dval(t), hr, hi);
+                    }
+                }
+            }
+        }
+
+        // sub-chunks from the last to the first
+#pragma unroll
+        for (int u = kNck - 1; u >= 0; --u) {
+            if (u * kK >= nseg) continue;
+            // the sub-chunk's states after each step: complex but for the
+            // last step's (its real part only); the entering state stays in
+            // its checkpoint (each lane reads back only what it wrote)
+            Acc gsr[kK][N], gsi[kK - 1][N];
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                hr[n] = ck[wave][u][2 * n][lane];
+                hi[n] = ck[wave][u][2 * n + 1][lane];
+            }
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                const int t = u * kK + i;
+                if (t < nseg) {
+                    Acc rw[2 * N];
+                    load_row<N>(rw, bcp + (int64_t)t * (2 * N));
+                    cbwd_fwd_step<N, kEuler>(cc, rw, (Acc)raw_to_f32<T>(xr[t]), dval(t), hr, hi);
+                }
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    gsr[i][n] = hr[n];
+                    if (i + 1 < kK) gsi[i < kK - 1 ? i : 0][n] = hi[n];
+                }
+            }
+            // back over the sub-chunk
+#pragma unroll
+            for (int i = kK - 1; i >= 0; --i) {
+                const int t = u * kK + i;
+                if (t < nseg) {
+                    Acc rw[2 * N];
+                    load_row<N>(rw, bcp + (int64_t)t * (2 * N));
+                    const Acc xv = xval(t), gy = gval(t), dv = dval(t);
+                    Acc ur, ui;
+                    delta_units(dv, ur, ui);
+                    Acc vB[N], vC[N];
+                    Acc acc_x = 0, gdt = 0;
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        const Acc hpr = i > 0 ? gsr[i > 0 ? i - 1 : 0][n] : ck[wave][u][2 * n][lane];
+                        const Acc hpi = i > 0 ? gsi[i > 0 ? i - 1 : 0][n] : ck[wave][u][2 * n + 1][lane];
+                        Acc abr, abi, kr, ki, er;
+                        cplx_coef<N, kEuler>(cc, n, dv, ur, ui, abr, abi, kr, ki, er);
+                        // lambda: the adjoint of h_t (y reads its real part)
+                        const Acc mr = fma_(rw[N + n], gy, lr[n]), mi = li[n];
+                        const Acc u_ = rw[n] * xv;
+                        // G_Abar = lambda conj(h_{t-1}),  G_k = lambda u
+                        const Acc gar = fma_(mr, hpr, mi * hpi), gai = fma_(mi, hpr, -mr * hpi);
+                        const Acc gkr = mr * u_, gki = mi * u_;
+                        // dL/du = Re(lambda conj(k))
+                        const Acc gu = fma_(mr, kr, mi * ki);
+                        acc_x = fma_(gu, rw[n], acc_x);
+                        vB[n] = gu * xv;
+                        vC[n] = gy * gsr[i][n];
+                        // d(delta): Re(G_Abar conj(A Abar)) + Re(G_k conj(dk/ddelta))
+                        const Acc par = cc.ar[n] * abr - cc.ai[n] * abi, pai = cc.ar[n] * abi + cc.ai[n] * abr;
+                        gdt = fma_(gar, par, fma_(gai, pai, gdt));
+                        if constexpr (kEuler)
+                            gdt += gkr;
+                        else
+                            gdt = fma_(gkr, abr, fma_(gki, abi, gdt));
+                        // dA: G_Abar conj(delta Abar) + G_k conj(dk/dA)
+                        const Acc dar = dv * abr, dai = dv * abi;
+                        dAr[n] = fma_(gar, dar, fma_(gai, dai, dAr[n]));
+                        dAi[n] = fma_(gai, dar, fma_(-gar, dai, dAi[n]));
+                        if constexpr (!kEuler) {
+                            Acc qr, qi;
+                            cplx_dk_da<N>(cc, n, dv, abr, abi, er, qr, qi);
+                            dAr[n] = fma_(gkr, qr, fma_(gki, qi, dAr[n]));
+                            dAi[n] = fma_(gki, qr, fma_(-gkr, qi, dAi[n]));
+                        }
+                        // into step t-1: lambda conj(Abar)
+                        lr[n] = fma_(mr, abr, mi * abi);
+                        li[n] = fma_(mi, abr, -mr * abi);
+                    }
+                    const Acc gx = fma_(Dd, gy, acc_x);
+                    Acc gdl = gdt;
+                    if constexpr (kPre) {
+                        if (soft) gdl *= softplus_grad_from_value(dv);
+                    }
+                    dDacc = fma_(gy, xv, dDacc);
+                    dbacc += gdl;
+                    if (live) {
+                        buf_store(from_acc<T>(gx), rdx, voff, t * row);
+                        buf_store(from_acc<T>(gdl), rdd, voff, t * row);
+                    }
+                    const int idx = wave_reduce_scatter<N>(vB, lane);
+                    (void)wave_reduce_scatter<N>(vC, lane);
+                    if ((lane & (kWave / N - 1)) == 0) {
+                        bacc[wave][t][0][idx] = vB[0];
+                        bacc[wave][t][1][idx] = vC[0];
+                    }
+                }
+            }
+        }
+        __syncthreads();  // every wave's partials of the segment are in
+        write_segment_sums(t0, nseg);
+        __syncthreads();  // ... and summed before the next segment's are written
+        if (s == 0 && live && q.dh_init != nullptr) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                q.dh_init[(ch * N + n) * 2] = (float)lr[n];
+                q.dh_init[(ch * N + n) * 2 + 1] = (float)li[n];
+            }
+        }
+    }
+
+    if (!live) return;
+    Acc *pa = static_cast<Acc *>(q.part_a) + ((int64_t)grp * BD + ch) * 2 * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        pa[2 * n] = dAr[n];
+        pa[2 * n + 1] = dAi[n];
+    }
+    Acc *pd = static_cast<Acc *>(q.part_d) + ((int64_t)grp * BD + ch) * 2;
+    pd[0] = dDacc;
+    pd[1] = dbacc;
+}
+
+// dB, dC: the block partials summed (one thread per (b, t, n)); dA, dD,
+// d(delta_bias): sums over batch rows and groups (one thread per value).
+template <typename Acc, int N>
+__global__ __launch_bounds__(kBlock) void cbwd_reduce_kernel(BwdParams q) {
+    const ScanParams &p = q.f;
+    const int64_t BLN = p.Bsz * p.L * N;
+    const int64_t DN2 = p.Dm * N * 2;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < BLN) {
+        const Acc *src = static_cast<const Acc *>(q.part_bc);
+        Acc sb = 0, sc = 0;
+        for (int k = 0; k < q.blocks_per_row; ++k) {
+            sb += src[((int64_t)k * 2) * BLN + i];
+            sc += src[((int64_t)k * 2 + 1) * BLN + i];
+        }
+        q.dB[i] = (float)sb;
+        q.dC[i] = (float)sc;
+        return;
+    }
+    const int64_t j = i - BLN;
+    const int64_t BD = p.Bsz * p.Dm;
+    if (j < DN2) {
+        const int64_t d = j / (2 * N);
+        const int64_t e = j - d * 2 * N;
+        const Acc *src = static_cast<const Acc *>(q.part_a);
+        Acc sacc = 0;
+        for (int g = 0; g < q.n_groups; ++g)
+            for (int64_t b = 0; b < p.Bsz; ++b) sacc += src[((int64_t)g * BD + b * p.Dm + d) * 2 * N + e];
+        q.dA[j] = (float)sacc;
+        return;
+    }
+    const int64_t k = j - DN2;
+    if (k >= 2 * p.Dm) return;
+    const int64_t d = k % p.Dm;
+    const int which = (int)(k / p.Dm);  // 0: dD, 1: d(delta_bias)
+    float *dst = which == 0 ? q.dD : q.ddelta_bias;
+    if (dst == nullptr) return;
+    const Acc *src = static_cast<const Acc *>(q.part_d);
+    Acc sacc = 0;
+    for (int g = 0; g < q.n_groups; ++g)
+        for (int64_t b = 0; b < p.Bsz; ++b) sacc += src[((int64_t)g * BD + b * p.Dm + d) * 2 + which];
+    dst[d] = (float)sacc;
+}
+
+template <typename T, int N, bool kEuler, bool kPre>
+void cbwd_launch_variant(BwdPass pass, const BwdParams &q, hipStream_t s) {
+    typedef typename AccOf<T>::type Acc;
+    const ScanParams &p = q.f;
+    if (pass == BwdPass::kAggregate) {
+        const int bps = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
+        if (p.S <= 1 || bps == 0) return;
+        hipLaunchKernelGGL((cbwd_aggregate_kernel<T, N, kEuler, kPre>), dim3((unsigned)bps * (p.S - 1)),
+                           dim3(kBlock), 0, s, q);
+    } else {
+        const unsigned grid = (unsigned)(q.n_groups * p.Bsz * q.blocks_per_row);
+        if (grid == 0) return;
+        hipLaunchKernelGGL((cbwd_main_kernel<T, N, kEuler, kPre>), dim3(grid), dim3(CbwdShape<Acc>::kWaves * kWave),
+                           0, s, q);
+    }
+}
+
+template <typename T, int N>
+hipError_t cbwd_pass_n(BwdPass pass, const BwdParams &q, hipStream_t s) {
+    typedef typename AccOf<T>::type Acc;
+    const ScanParams &p = q.f;
+    const bool pre = p.delta_bias != nullptr || p.delta_softplus != 0;
+    switch (pass) {
+        case BwdPass::kStarts:
+            break;
+        case BwdPass::kAggregate:
+        case BwdPass::kMain:
+            if (p.euler_b) {
+                if (pre)
+                    cbwd_launch_variant<T, N, true, true>(pass, q, s);
+                else
+                    cbwd_launch_variant<T, N, true, false>(pass, q, s);
+            } else {
+                if (pre)
+                    cbwd_launch_variant<T, N, false, true>(pass, q, s);
+                else
+                    cbwd_launch_variant<T, N, false, false>(pass, q, s);
+            }
+            break;
+        case BwdPass::kCarry: {
+            const int64_t work = p.Bsz * p.Dm * N;
+            if (work == 0) return hipSuccess;
+            hipLaunchKernelGGL((cbwd_carry_kernel<Acc, N>), dim3((unsigned)((work + kBlock - 1) / kBlock)),
+                               dim3(kBlock), 0, s, q);
+            break;
+        }
+        case BwdPass::kReduce: {
+            const int64_t work = p.Bsz * p.L * N + p.Dm * N * 2 + 2 * p.Dm;
+            if (work == 0) return hipSuccess;
+            hipLaunchKernelGGL((cbwd_reduce_kernel<Acc, N>), dim3((unsigned)((work + kBlock - 1) / kBlock)),
+                               dim3(kBlock), 0, s, q);
+            break;
+        }
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t cbwd_pass(BwdPass pass, const BwdParams &q, int N, hipStream_t s) {
+    switch (N) {
+        case 1: return cbwd_pass_n<T, 1>(pass, q, s);
+        case 2: return cbwd_pass_n<T, 2>(pass, q, s);
+        case 4: return cbwd_pass_n<T, 4>(pass, q, s);
+        case 8: return cbwd_pass_n<T, 8>(pass, q, s);
+        case 16: return cbwd_pass_n<T, 16>(pass, q, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+}  // namespace ssm

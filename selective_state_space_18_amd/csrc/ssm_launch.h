@@ -101,6 +101,18 @@ hipError_t cplx_pass_f32(ScanPass pass, const ScanParams &p, int N, hipStream_t 
 hipError_t cplx_pass_bf16(ScanPass pass, const ScanParams &p, int N, hipStream_t s);
 hipError_t cplx_step_f32(const StepParams &p, int N, hipStream_t s);
 hipError_t cplx_step_bf16(const StepParams &p, int N, hipStream_t s);
+// Backward of the complex-A scan (cbwd_kernels.h), segments of
+// cbwd_segment_len() steps.  BwdParams as for the real backward, with A,
+// dA [Dm][N][2], h_init, dh_final, dh_init [Bsz][Dm][N][2] and scratch
+//   ragg    : [S][2N+1][B*D] Acc (adjoint summaries, re/im at 2n, 2n+1)
+//   gout    : [groups][2N][B*D] Acc
+//   part_bc : [blocks per row][2][B*L*N] Acc, written by every block
+//   part_a  : [groups][B*D][2N] Acc
+// blocks_per_row = ceil(tiles_per_b / cbwd_waves(dtype)); kStarts is not used.
+int cbwd_segment_len();
+int cbwd_waves(int dtype);
+hipError_t cbwd_pass_f32(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
+hipError_t cbwd_pass_bf16(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
 
 // Scalar decay per head, chunked matrix form (ssd_kernels.h).  x, y
 // [Bsz][L][Dm]; delta [Bsz][L][H]; A, delta_bias [H]; D [Dm]; B, C

@@ -38,7 +38,8 @@ EXPORTS = ("ssm_scan_fwd", "ssm_scan_fwd_ex", "ssm_step", "ssm_step_ex", "ssm_st
            "ssm_scan_plan", "ssm_release_workspaces", "ssm_profile_read", "ssm_scan_varlen_fwd",
            "ssm_scan_fused_fwd", "ssm_step_fused", "ssm_scan_bwd", "ssm_scan_complex_fwd",
            "ssm_step_complex", "ssm_scan_ssd_fwd", "ssm_scan_bwd_plan", "ssm_probe_issue",
-           "ssm_scan_fwd_noalloc", "ssm_probe_hbm", "ssm_scan_varlen_bwd")
+           "ssm_scan_fwd_noalloc", "ssm_probe_hbm", "ssm_scan_varlen_bwd",
+           "ssm_scan_complex_bwd")
 
 
 class SSMError(RuntimeError):
@@ -79,6 +80,8 @@ def lib():
     L.ssm_scan_varlen_bwd.argtypes = [_vp] * 8 + [_i64] + [_vp] * 11 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint,
                                                                                     _vp]
     L.ssm_scan_varlen_bwd.restype = ctypes.c_int
+    L.ssm_scan_complex_bwd.argtypes = [_vp] * 18 + [_i64] * 4 + [ctypes.c_int, ctypes.c_uint, _vp]
+    L.ssm_scan_complex_bwd.restype = ctypes.c_int
     L.ssm_step_fused.argtypes = [_vp] * 9 + [_i64] * 3 + [ctypes.c_int, ctypes.c_uint, _vp]
     L.ssm_step_fused.restype = ctypes.c_int
     L.ssm_step.argtypes = [_vp] * 8 + [_i64] * 3 + [_vp]
@@ -545,6 +548,61 @@ def scan_complex_fwd(x, delta, A, B, C, D, h_init=None, y=None, h_final=None, wa
                                         _flags(delta_softplus, euler_b), _stream(dev))
     _check(rc, "ssm_scan_complex_fwd")
     return y, h_final
+
+
+def scan_complex_bwd(x, delta, A, B, C, D, dy, h_init=None, dh_final=None, delta_bias=None, delta_softplus=False,
+                     euler_b=False, want_dh_init=True, out=None):
+    """ssm_scan_complex_bwd: gradients of the complex-A scan.
+
+    Forward inputs as in scan_complex_fwd (A complex64 [Dm, N] or float32
+    [Dm, N, 2]; h_init complex64 [Bsz, Dm, N] or None), dy [Bsz, L, Dm] in x's
+    dtype and optional dh_final complex64 [Bsz, Dm, N].  Returns a dict with
+    dx, ddelta (x's dtype), dA complex64 [Dm, N] (dL/dRe A + i dL/dIm A), dB,
+    dC [Bsz, L, N], dD [Dm] (fp32), dh_init complex64 [Bsz, Dm, N] (if
+    want_dh_init) and ddelta_bias [Dm] (if delta_bias is given).  `out` may
+    supply any of these tensors (the complex ones as complex64 or as float32
+    with a trailing (re, im) axis).
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssmscan runs on the GPU: x must be a device tensor")
+    Bsz, L, Dm = x.shape
+    N = A.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    for t, name, shape, tdt in ((x, "x", (Bsz, L, Dm), dt), (delta, "delta", (Bsz, L, Dm), dt),
+                                (B, "B", (Bsz, L, N), dt), (C, "C", (Bsz, L, N), dt),
+                                (D, "D", (Dm,), torch.float32), (dy, "dy", (Bsz, L, Dm), dt)):
+        _need(t, name, shape, tdt, dev)
+    A2 = _pairs(A, "A", (Dm, N), dev)
+    _bias(delta_bias, Dm, dev)
+    hi2 = None if h_init is None else _pairs(h_init, "h_init", (Bsz, Dm, N), dev)
+    dhf2 = None if dh_final is None else _pairs(dh_final, "dh_final", (Bsz, Dm, N), dev)
+    o = dict(out or {})
+    shapes = {"dx": ((Bsz, L, Dm), dt), "ddelta": ((Bsz, L, Dm), dt), "dB": ((Bsz, L, N), torch.float32),
+              "dC": ((Bsz, L, N), torch.float32), "dD": ((Dm,), torch.float32)}
+    if delta_bias is not None:
+        shapes["ddelta_bias"] = ((Dm,), torch.float32)
+    for k, (shape, tdt) in shapes.items():
+        if o.get(k) is None:
+            o[k] = torch.empty(shape, dtype=tdt, device=dev)
+        _need(o[k], k, shape, tdt, dev)
+    cplx = {"dA": (Dm, N)}
+    if want_dh_init:
+        cplx["dh_init"] = (Bsz, Dm, N)
+    pairs = {}
+    for k, shape in cplx.items():
+        if o.get(k) is None:
+            o[k] = torch.empty(shape, dtype=torch.complex64, device=dev)
+        pairs[k] = _pairs(o[k], k, shape, dev)
+    with torch.cuda.device(dev):
+        rc = lib().ssm_scan_complex_bwd(_ptr(x), _ptr(delta), _ptr(delta_bias), _ptr(A2), _ptr(B), _ptr(C),
+                                        _ptr(D), _ptr(hi2), _ptr(dy), _ptr(dhf2), _ptr(o["dx"]), _ptr(o["ddelta"]),
+                                        _ptr(o.get("ddelta_bias")), _ptr(pairs["dA"]), _ptr(o["dB"]),
+                                        _ptr(o["dC"]), _ptr(o["dD"]), _ptr(pairs.get("dh_init")), Bsz, L, Dm, N,
+                                        code, _flags(delta_softplus, euler_b), _stream(dev))
+    _check(rc, "ssm_scan_complex_bwd")
+    return o
 
 
 def scan_ssd_fwd(x, delta, A, B, C, D, head_dim=64, h_init=None, y=None, h_final=None, want_state=True,

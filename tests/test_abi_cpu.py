@@ -199,6 +199,32 @@ def test_varlen_bwd_argument_errors(L):
     assert bwd(nseq=1 << 60) == 2              # nseq * Dm * N overflows
 
 
+def test_complex_bwd_argument_errors(L):
+    v = ctypes.c_void_p
+    Q = [0x10000000 * (i + 1) for i in range(20)]  # fake, aligned, far apart
+
+    def bwd(**k):
+        a = dict(x=Q[0], dl=Q[1], bias=None, A=Q[2], B=Q[3], C=Q[4], D=Q[5], hi=None, dy=Q[6], dhf=None, dx=Q[7],
+                 ddl=Q[8], dbias=None, dA=Q[9], dB=Q[10], dC=Q[11], dD=Q[12], dhi=None, Bsz=2, Ls=8, Dm=64, N=16,
+                 dtype=1, flags=0)
+        a.update(k)
+        return L.ssm_scan_complex_bwd(v(a["x"]), v(a["dl"]), v(a["bias"]), v(a["A"]), v(a["B"]), v(a["C"]),
+                                      v(a["D"]), v(a["hi"]), v(a["dy"]), v(a["dhf"]), v(a["dx"]), v(a["ddl"]),
+                                      v(a["dbias"]), v(a["dA"]), v(a["dB"]), v(a["dC"]), v(a["dD"]), v(a["dhi"]),
+                                      a["Bsz"], a["Ls"], a["Dm"], a["N"], a["dtype"], a["flags"], None)
+    assert bwd(dtype=3) == 3 and bwd(N=7) == 4 and bwd(flags=4) == 9 and bwd(Ls=-1) == 2
+    assert bwd(x=0) == 1 and bwd(dy=0) == 1 and bwd(dA=0) == 1 and bwd(dx=0) == 1
+    assert bwd(A=Q[2] + 2) == 5                # fp32 pairs need 4-byte alignment
+    # A and dA hold (re, im) pairs: 2 * Dm * N floats (8 KiB here)
+    assert bwd(dA=Q[2] + 4096) == 6
+    assert b"dA" in L.ssm_last_error()
+    # dh_init and dh_final hold Bsz * Dm * N pairs (16 KiB here)
+    assert bwd(dhi=Q[13], dhf=Q[13] + 8192) == 6
+    assert bwd(dx=Q[0]) == 6 and bwd(dB=Q[10] + 0, dC=Q[10] + 64) == 6
+    assert bwd(Dm=1 << 40) == 2                # sizes overflow
+    assert bwd(Dm=(1 << 30) // 32) == 2        # a 16-step bf16 segment spans 1 GiB
+
+
 def test_ssd_argument_errors(L):
     v = ctypes.c_void_p
     Q = [0x10000000 * (i + 1) for i in range(12)]  # fake, 16-byte aligned, far apart

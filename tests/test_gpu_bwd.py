@@ -123,6 +123,12 @@ def test_bwd_empty_and_deterministic(ss):
     torch.cuda.synchronize()
     assert torch.all(got["dA"] == 0) and torch.all(got["dD"] == 0)
     assert torch.equal(got["dh_init"], inp["dh_final"])
+    # no channels: dB, dC are empty sums, written as zeros
+    inp = make("fp32", "s4d_real", 2, 30, 0, 4, "plain", False, False, seed=2)
+    out = {k: torch.full((2, 30, 4), 7.0, device=DEV) for k in ("dB", "dC")}
+    got = ss.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["dy"], out=out)
+    torch.cuda.synchronize()
+    assert torch.all(got["dB"] == 0) and torch.all(got["dC"] == 0)
     inp = make("bf16", "lognormal", 2, 300, 200, 16, "plain", True, True, seed=2)
     a = gpu_bwd(ss, inp, {})
     b = gpu_bwd(ss, inp, {})
