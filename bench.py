@@ -65,6 +65,15 @@ BWD_FLOPS_PER_ELEM = 28
 # sin, cos (3, one each); Abar (2); Abar - 1 (3); (Abar - 1)/A (complex
 # multiply, 6); B x and its product with it (3); Abar h + k u (8); C Re(h) + y (2).
 CPLX_FLOPS_PER_ELEM = 29
+# Complex-A backward, per state element: the forward recurrence once (27: the
+# forward's count without the output term) and the adjoint with the gradient
+# terms (71): lambda = C dy + nu (2); G_Abar = lambda conj(h_{t-1}) (6); G_k =
+# lambda u (2); dL/du = Re(lambda conj(k)) (3) into dx (2), dB (1); dC (1);
+# d(delta): A Abar (6) and two real parts (4 + 4); dA: delta Abar (2), its
+# product (6) and sum (2), dk/dA = (z Abar - (Abar - 1)) / A^2 with 1/A^2
+# per channel (14), its product (6) and sum (2); lambda conj(Abar) (6); the
+# channel sums of dB and dC (2).
+CBWD_FLOPS_PER_ELEM = 98
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_18_amd", "csrc")
 
@@ -81,6 +90,8 @@ KERNEL_SOURCES = {
     "bwd": ("bwd_kernels.h", "scan_kernels.h", "ssm_device.h", "ssm_launch.h"),
     "ssd": ("ssd_kernels.h", "ssm_device.h", "ssm_launch.h"),
     "cplx": ("cplx_kernels.h", "scan_kernels.h", "ssm_device.h", "ssm_launch.h"),
+    "cbwd": ("cbwd_kernels.h", "bwd_kernels.h", "cplx_kernels.h", "scan_kernels.h", "ssm_device.h",
+             "ssm_launch.h"),
 }
 
 
@@ -497,6 +508,61 @@ def bench_complex(torch, ss, generate, cfg, steps, warmup, flusher=None):
     return rec
 
 
+def alg_bytes_bwd_complex(cfg):
+    """Complex-A backward, inputs read once and outputs written once: as the
+    real backward, with A, dA and the state pairs (dh_final, dh_init) twice
+    as large."""
+    return alg_bytes_bwd(cfg) + 2 * cfg.Dm * cfg.N * 4 + 2 * cfg.Bsz * cfg.Dm * cfg.N * 4
+
+
+def bench_complex_backward(torch, ss, generate, cfg, steps, warmup, flusher=None):
+    """Backward of the complex-A layer: every input gradient for a random dy
+    and dh_final, forward states recomputed inside the call."""
+    dev = "cuda:0"
+    log(f"[bench] generating {cfg.name} (complex A, backward)")
+    inp = generate.scan_inputs(cfg, dev)
+    A = generate.complex_A(cfg.Dm, cfg.N, cfg.seed + 100, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 1)
+    dy = torch.randn(inp["x"].shape, generator=g, device=dev).to(inp["x"].dtype)
+    dhf = torch.complex(torch.randn((cfg.Bsz, cfg.Dm, cfg.N), generator=g, device=dev),
+                        torch.randn((cfg.Bsz, cfg.Dm, cfg.N), generator=g, device=dev))
+    out = {}
+
+    def fn(_i):
+        nonlocal out
+        out = ss.scan_complex_bwd(inp["x"], inp["delta"], A, inp["B"], inp["C"], inp["D"], dy, dh_final=dhf,
+                                  out=out or None)
+
+    log(f"[bench] timing {cfg.name} complex backward: {warmup} warmup + {steps} steps")
+    ms, kern = profiled_loop(torch, ss, fn, steps, warmup)
+    proto = protocol_record(torch, fn, fn, steps, flusher, 1) if flusher else None
+    del inp, A, dy, dhf, out
+    torch.cuda.empty_cache()
+    elems = cfg.elems()
+    main_ms = kern["bwd_main"]["avg_ms"]
+    alg = alg_bytes_bwd_complex(cfg)
+    achieved = elems * CBWD_FLOPS_PER_ELEM / (main_ms * 1e-3) / 1e12
+    roof = {"kernel": "cbwd_main_kernel", "bound": "alu", "achieved": round(achieved, 3),
+            "peak": round(VALU_FP32_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+            "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
+            "avg_ms": round(main_ms, 5), "algorithmic_flops_per_launch": elems * CBWD_FLOPS_PER_ELEM,
+            "algorithmic_bytes_per_call": alg,
+            "hbm_frac_kernel": round(alg / (main_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "hbm_frac_step": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "exp, sin and cos count one flop each; each takes two VALU issue slots"}
+    roof.update(traffic_fields("complex_backward_" + cfg.name, "cbwd", alg))
+    rec = {"workload": cfg.name + "_complex_A_backward", "ms_per_step": round(ms, 5),
+           "value": elems / (ms * 1e-3), "unit": "elems/s", "roofline": roof,
+           "kernels_avg_ms": {k: round(v["avg_ms"], 5) for k, v in kern.items()},
+           "main_kernel_elems_per_s": elems / (main_ms * 1e-3),
+           "config": {"workload": cfg.name, "A": "complex: a = -exp(N(0, 0.5)), w = pi n (1 + 0.1 N(0, 1))",
+                      "segment_len": 16}}
+    if proto is not None:
+        rec["protocol"] = proto
+    return rec
+
+
 def bench_packed(torch, ss, generate, cfg, steps, warmup, flusher=None):
     """Packed variable-length prefill: one row of cfg.L steps holding a few
     dozen sequences, each restarting from its own initial state."""
@@ -832,7 +898,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["scan", "long", "decode", "small", "packed", "options", "backward",
-                                       "backward_general", "packed_backward", "complex", "cdecode", "general",
+                                       "backward_general", "packed_backward", "complex", "complex_backward", "cdecode",
+                                       "general",
                                        "ssd", "probe", "hbmprobe"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -875,6 +942,10 @@ def main():
         return
     if a.only == "complex":
         rec = bench_complex(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps, a.warmup)
+        print(json.dumps(rec), flush=True)
+        return
+    if a.only == "complex_backward":
+        rec = bench_complex_backward(torch, ss, generate, configs.MAMBA2P8B_LAYER, a.steps, a.warmup)
         print(json.dumps(rec), flush=True)
         return
     if a.only == "ssd":
@@ -962,6 +1033,7 @@ def main():
         sec["fused_softplus"] = bench_options(torch, ss, generate, configs, steps5, flusher, wu)
         sec["packed_prefill"] = bench_packed(torch, ss, generate, configs.PACKED_2P8B_LAYER, steps5, wu, flusher)
         sec["complex_A"] = bench_complex(torch, ss, generate, cfg, max(3, a.steps // 10), wu, flusher)
+        sec["complex_A_backward"] = bench_complex_backward(torch, ss, generate, cfg, 3, wu, flusher)
         sec["backward"] = bench_backward(torch, ss, generate, cfg, max(3, a.steps // 10), wu, flusher)
         sec["backward_general_A"] = bench_backward(torch, ss, generate, configs.MAMBA130M_LAYER, steps5, wu,
                                                    flusher)
