@@ -872,17 +872,17 @@ BwdPlan make_bwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int dtype, int cus) {
     return bp;
 }
 
-// Complex-A backward: cbwd_segment_len() steps per segment, cbwd_waves()
-// waves per main-kernel block and one such block per CU (its state
-// checkpoints take most of the LDS).
-BwdPlan make_cbwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int dtype, int cus) {
+// Complex-A backward: cbwd_segment_len() steps per segment, the main
+// kernel's channel tiles per block and blocks per CU (bounded by the LDS its
+// state checkpoints take) from the kernels.
+BwdPlan make_cbwd_plan(int64_t Bsz, int64_t L, int64_t Dm, int64_t N, int dtype, int cus) {
     BwdPlan bp;
     bp.seg_len = ssm::cbwd_segment_len();
     bp.S = L > 0 ? (int)((L + bp.seg_len - 1) / bp.seg_len) : 1;
     const int64_t tiles_per_b = (Dm + 63) / 64;
-    const int w = ssm::cbwd_waves(dtype);
+    const int w = ssm::cbwd_tiles_per_block(dtype, (int)N);
     bp.blocks_per_row = (int)((tiles_per_b + w - 1) / w);
-    pick_groups(bp, Bsz * bp.blocks_per_row, (int64_t)(cus > 0 ? cus : 256));
+    pick_groups(bp, Bsz * bp.blocks_per_row, (int64_t)ssm::cbwd_blocks_per_cu(dtype) * (cus > 0 ? cus : 256));
     return bp;
 }
 
@@ -1195,7 +1195,7 @@ int cbwd_impl(const void *x, const void *delta, const float *delta_bias, const f
     p.delta_bias = delta_bias;
     p.delta_softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
     p.euler_b = (flags & SSM_EULER_B) ? 1 : 0;
-    const BwdPlan bp = make_cbwd_plan(Bsz, L, Dm, dtype, cus);
+    const BwdPlan bp = make_cbwd_plan(Bsz, L, Dm, N, dtype, cus);
     p.seg_len = bp.seg_len;
     p.S = bp.S;
     p.tiles_per_b = (int)((Dm + 63) / 64);

@@ -40,18 +40,28 @@ namespace ssm {
 
 namespace {
 
+// Main-kernel blocks: kWaves waves; kBlocksPerCU of them share a compute
+// unit (their LDS fits), one wave per SIMD each.
 template <typename Acc>
 struct CbwdShape;
 template <>
 struct CbwdShape<float> {
-    static constexpr int kWaves = 4;  // waves per block (checkpoints: 32 KB each)
+    static constexpr int kWaves = 4;
+    static constexpr int kBlocksPerCU = 2;
 };
 template <>
 struct CbwdShape<double> {
-    static constexpr int kWaves = 2;  // (64 KB each)
+    static constexpr int kWaves = 4;
+    static constexpr int kBlocksPerCU = 1;
 };
 constexpr int kCbwdT = 16;  // segment length
 constexpr int kCbwdK = 4;   // checkpoint interval = sub-chunk length
+// Waves that share one 64-channel tile in the main kernel, each holding
+// N / split of its states.
+template <int N>
+constexpr int cbwd_split() {
+    return N >= 2 ? 2 : 1;
+}
 
 // A and 1/A of one channel.  The exponent is formed as (delta * unit) * A with
 // the unit taken per step (log2 e and 1/(2 pi) in fp32 arithmetic, where the
@@ -122,17 +132,34 @@ __device__ __forceinline__ void cbwd_fwd_step(const CbwdConst<N, Acc> &cc, const
     }
 }
 
-// dk/dA of state n for ZOH: (delta A Abar - (Abar - 1)) / A^2 = delta^2 phi'(delta A),
-// phi'(z) = (z e^z - (e^z - 1)) / z^2.  Near z = 0 the closed form cancels (it
-// loses about log2(2/|z|) bits): there the Taylor polynomial to z^4 is used,
-// whose truncation is below |z|^5 / 840 -- for |z| < 1/8 in fp32 arithmetic,
-// |z| < 1/1000 in fp64.
+// dk/dA of state n for ZOH: (delta A Abar - (Abar - 1)) / A^2 = (delta Abar -
+// k) / A = delta^2 phi'(delta A), phi'(z) = (z e^z - (e^z - 1)) / z^2.  Near
+// z = 0 the closed forms cancel: they lose about log2(2/|z|) bits.
+//  fp64: the Taylor polynomial to z^4 where |z| < 1/1000 (truncation below
+//        |z|^5 / 840), the closed form elsewhere.
+//  fp32: (delta Abar - k) / A, with no branch (a per-lane branch here costs
+//        the registers that keep the kernel at two waves per SIMD).  Its
+//        absolute error is about 6 eps |delta| / |A| against a value near
+//        delta^2 / 2: a few eps of the dA sum for |A| above about 1e-3.  The
+//        tiny real stand-in that replaces A = 0 takes the limit delta^2 / 2
+//        instead (exact in fp32 at that |z|).
 template <int N, typename Acc>
 __device__ __forceinline__ void cplx_dk_da(const CbwdConst<N, Acc> &cc, int n, Acc dv, Acc abr, Acc abi, Acc er,
-                                           Acc &gr, Acc &gi) {
+                                           Acc kr, Acc ki, Acc &gr, Acc &gi) {
+    if constexpr (sizeof(Acc) == 4) {
+        (void)er;
+        const Acc nr = fma_(dv, abr, -kr), ni = fma_(dv, abi, -ki);
+        const Acc cr = nr * cc.wr[n] - ni * cc.wi[n];
+        const Acc ci = nr * cc.wi[n] + ni * cc.wr[n];
+        const bool zero = cc.ar[n] == (Acc)kTinyA && cc.ai[n] == (Acc)0;
+        gr = zero ? (Acc)0.5 * dv * dv : cr;
+        gi = zero ? (Acc)0 : ci;
+        return;
+    }
+    (void)kr;
+    (void)ki;
     const Acc zr = dv * cc.ar[n], zi = dv * cc.ai[n];
-    constexpr Acc kSmall2 = sizeof(Acc) == 4 ? (Acc)(1.0 / 64.0) : (Acc)1e-6;
-    if (zr * zr + zi * zi < kSmall2) {
+    if (zr * zr + zi * zi < (Acc)1e-6) {
         // 1/2 + z/3 + z^2/8 + z^3/30 + z^4/144 (Horner, complex)
         Acc pr = (Acc)(1.0 / 144.0), pi = 0;
         const Acc cs[4] = {(Acc)(1.0 / 30.0), (Acc)(1.0 / 8.0), (Acc)(1.0 / 3.0), (Acc)0.5};
@@ -277,28 +304,52 @@ __global__ __launch_bounds__(kBlock) void cbwd_carry_kernel(BwdParams q) {
 }
 
 // ---------------------------------------------------------------------------
-// Main pass.  part_bc [blocks per row][2][B*L*N] (block sums of the dB and dC
-// lane values), part_a [groups][B*D][2N] (dA), part_d [groups][B*D][2] (dD,
+// Main pass.  A 64-channel tile is shared by cbwd_split<N>() waves, wave h
+// holding states n0 = h NH .. n0 + NH - 1 (NH = N / split): their registers
+// and checkpoints are halved, so two blocks fit on a compute unit.  The
+// waves of a tile add their shares of dx and d(delta) through LDS once per
+// sub-chunk (the first wave stores them).
+// part_bc [blocks per row][2][B*L*N] (block sums of the dB and dC lane
+// values), part_a [groups][B*D][2N] (dA), part_d [groups][B*D][2] (dD,
 // d(delta_bias)).
+template <int NH, int N, typename Acc>
+__device__ __forceinline__ void load_half_row(Acc (&dst)[2 * NH], const_row_ptr<Acc> row, int n0) {
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+        dst[i] = row[n0 + i];
+        dst[NH + i] = row[N + n0 + i];
+    }
+}
+
 template <typename T, int N, bool kEuler, bool kPre>
-__global__ __launch_bounds__(CbwdShape<typename AccOf<T>::type>::kWaves *kWave) void cbwd_main_kernel(BwdParams q) {
+__global__ __launch_bounds__(CbwdShape<typename AccOf<T>::type>::kWaves *kWave,
+                             CbwdShape<typename AccOf<T>::type>::kBlocksPerCU) void cbwd_main_kernel(BwdParams q) {
     typedef typename AccOf<T>::type Acc;
     constexpr int kWaves = CbwdShape<Acc>::kWaves;
+    constexpr int P = cbwd_split<N>();
+    constexpr int NH = N / P;
+    constexpr int kTiles = kWaves / P;
     constexpr int kT = kCbwdT, kK = kCbwdK, kNck = kT / kK;
-    __shared__ Acc ck[kWaves][kNck][2 * N][kWave];  // state checkpoints, per wave
-    __shared__ Acc bacc[kWaves][kT][2][N];          // per-wave dB, dC sums of one segment
-    static_assert(sizeof(ck) + sizeof(bacc) <= 163840, "one block per compute unit must fit its 160 KB of LDS");
+    __shared__ Acc ck[kWaves][kNck - 1][2 * NH][kWave];  // state before steps 4, 8, 12, per wave
+    __shared__ Acc bacc[kTiles][kT][2][N];               // per-tile dB, dC sums of one segment
+    __shared__ Acc xb[2][kTiles][kK][2][kWave];          // shares of dx, d(delta) from waves h > 0
+    static_assert(sizeof(ck) + sizeof(bacc) + (P > 1 ? sizeof(xb) : 0) <= 163840 / CbwdShape<Acc>::kBlocksPerCU,
+                  "the blocks of one compute unit must fit its 160 KB of LDS");
+    static_assert(P <= 2 && kWaves % P == 0, "xb holds the share of one other wave per tile");
     const ScanParams &p = q.f;
 
     const int wave = uniform((int)threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
+    const int tb = wave / P;  // tile within the block
+    const int half = wave - tb * P;
+    const int n0 = uniform(half * NH);
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int per_grp = (int)p.Bsz * q.blocks_per_row;
     const int grp = lb / per_grp;
     const int rem = lb - grp * per_grp;
     const int64_t b = rem / q.blocks_per_row;
     const int br = rem - (int)b * q.blocks_per_row;
-    const int tir = br * kWaves + wave;
+    const int tir = br * kTiles + tb;
     const bool tile_ok = tir < p.tiles_per_b;
     const int64_t d0 = (int64_t)(tile_ok ? tir : p.tiles_per_b - 1) * kWave;
     const bool in_range = d0 + lane < p.Dm;
@@ -306,50 +357,63 @@ __global__ __launch_bounds__(CbwdShape<typename AccOf<T>::type>::kWaves *kWave) 
     const int64_t ch = b * p.Dm + d;
     const int64_t BD = p.Bsz * p.Dm;
     const int64_t BLN = p.Bsz * p.L * N;
-    // waves past the row and lanes past it run on x = dy = 0: every dB, dC,
+    // tiles past the row and lanes past it run on x = dy = 0: every dB, dC,
     // dx and d(delta) share is a multiple of x or dy, and they store nothing
     const bool live = tile_ok && in_range;
 
-    const CbwdConst<N, Acc> cc(p.A + d * 2 * N);
+    const CbwdConst<NH, Acc> cc(p.A + (d * N + n0) * 2);
     const Acc Dd = (Acc)p.D[d];
     const Acc bias = (kPre && p.delta_bias != nullptr) ? (Acc)p.delta_bias[d] : (Acc)0;
     const bool soft = p.delta_softplus != 0;
     const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
     const int32_t voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
 
-    Acc dAr[N], dAi[N];
+    Acc dAr[NH], dAi[NH];
 #pragma unroll
-    for (int n = 0; n < N; ++n) dAr[n] = dAi[n] = 0;
+    for (int k = 0; k < NH; ++k) dAr[k] = dAi[k] = 0;
     Acc dDacc = 0, dbacc = 0;
-    for (int e = lane; e < kT * 2 * N; e += kWave) (&bacc[wave][0][0][0])[e] = 0;
 
-    // the block's dB/dC sums of the segment's steps, each over the waves in
-    // wave order (between two barriers)
+    // the block's dB/dC sums of the segment's steps, each over the tiles in
+    // order (between two barriers)
     auto write_segment_sums = [&](int64_t t0, int nseg) {
         Acc *dst = static_cast<Acc *>(q.part_bc) + ((int64_t)br * 2) * BLN + (b * p.L + t0) * N;
         constexpr int kE = kT * 2 * N;
-        constexpr int kPerWave = (kE + kWaves - 1) / kWaves;
-        for (int k = lane; k < kPerWave; k += kWave) {
-            const int e = wave * kPerWave + k;
-            if (e >= kE) break;
+        for (int e = threadIdx.x; e < kE; e += kWaves * kWave) {
             const int i = e / (2 * N);
             const int v = (e / N) & 1;
             const int n = e % N;
             Acc sum = 0;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) sum += bacc[w][i][v][n];
+            for (int w = 0; w < kTiles; ++w) sum += bacc[w][i][v][n];
             if (i < nseg) dst[(int64_t)v * BLN + (int64_t)i * N + n] = sum;
+        }
+    };
+    // the state entering segment s (this wave's states)
+    auto load_entry = [&](int s, Acc(&er)[NH], Acc(&ei)[NH]) {
+        if (s == 0) {
+#pragma unroll
+            for (int k = 0; k < NH; ++k) {
+                er[k] = p.h_init ? (Acc)p.h_init[(ch * N + n0 + k) * 2] : (Acc)0;
+                ei[k] = p.h_init ? (Acc)p.h_init[(ch * N + n0 + k) * 2 + 1] : (Acc)0;
+            }
+        } else {
+            const Acc *gin = static_cast<const Acc *>(p.gin);
+#pragma unroll
+            for (int k = 0; k < NH; ++k) {
+                er[k] = gin[((int64_t)s * 2 * N + 2 * (n0 + k)) * BD + ch];
+                ei[k] = gin[((int64_t)s * 2 * N + 2 * (n0 + k) + 1) * BD + ch];
+            }
         }
     };
 
     // the adjoint entering the group's last segment from the right
-    Acc lr[N], li[N];
+    Acc lr[NH], li[NH];
     {
         const Acc *gout = static_cast<const Acc *>(q.gout);
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            lr[n] = gout[((int64_t)grp * 2 * N + 2 * n) * BD + ch];
-            li[n] = gout[((int64_t)grp * 2 * N + 2 * n + 1) * BD + ch];
+        for (int k = 0; k < NH; ++k) {
+            lr[k] = gout[((int64_t)grp * 2 * N + 2 * (n0 + k)) * BD + ch];
+            li[k] = gout[((int64_t)grp * 2 * N + 2 * (n0 + k) + 1) * BD + ch];
         }
     }
     for (int si = q.seg_per_group - 1; si >= 0; --si) {
@@ -364,56 +428,54 @@ __global__ __launch_bounds__(CbwdShape<typename AccOf<T>::type>::kWaves *kWave) 
         const __amdgpu_buffer_rsrc_t rdx = make_rsrc(static_cast<const T *>(q.dx) + off, nseg * row);
         const __amdgpu_buffer_rsrc_t rdd = make_rsrc(static_cast<const T *>(q.ddelta) + off, nseg * row);
         const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
-        // the segment's inputs, once
-        uint32_t xr[kT], dr[kT], yr[kT];
-#pragma unroll
-        for (int i = 0; i < kT; ++i) {
+        // raw x and delta of steps t0 + i, clamped into the segment
+        auto load_xd = [&](int i, uint32_t &xv, uint32_t &dv) {
             const int so = (i < nseg ? i : nseg - 1) * row;
-            xr[i] = buf_load_raw<T>(rx, voff, so);
-            dr[i] = buf_load_raw<T>(rdl, voff, so);
-            yr[i] = buf_load_raw<T>(rdy, voff, so);
-        }
-        auto xval = [&](int i) { return live ? (Acc)raw_to_f32<T>(xr[i]) : (Acc)0; };
-        auto gval = [&](int i) { return live ? (Acc)raw_to_f32<T>(yr[i]) : (Acc)0; };
-        auto dval = [&](int i) {
-            Acc v = (Acc)raw_to_f32<T>(dr[i]);
+            xv = buf_load_raw<T>(rx, voff, so);
+            dv = buf_load_raw<T>(rdl, voff, so);
+        };
+        auto dval = [&](uint32_t raw) {
+            Acc v = (Acc)raw_to_f32<T>(raw);
             if constexpr (kPre) v = soft ? softplus_(v + bias) : v + bias;
             return v;
         };
+        // d(delta) as passed from d(delta) as used, and the running sums
+        auto finish_step = [&](int t, Acc gy, Acc xv, Acc dv, Acc gx, Acc gdt) {
+            Acc gdl = gdt;
+            if constexpr (kPre) {
+                if (soft) gdl *= softplus_grad_from_value(dv);
+            }
+            dDacc = fma_(gy, xv, dDacc);
+            dbacc += gdl;
+            if (live) {
+                buf_store(from_acc<T>(gx), rdx, voff, t * row);
+                buf_store(from_acc<T>(gdl), rdd, voff, t * row);
+            }
+        };
 
-        // checkpoints: the state before steps 0, 4, 8, 12 of the segment
-        Acc hr[N], hi[N];
-        if (s == 0) {
+        // checkpoints: the state before steps 4, 8, 12 of the segment (x and
+        // delta of steps 0..11 are loaded for this pass only; each sub-chunk
+        // loads its own again, from the cache)
+        Acc hr[NH], hi[NH];
+        uint32_t xr[kT - kK], dr[kT - kK];
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                hr[n] = p.h_init ? (Acc)p.h_init[(ch * N + n) * 2] : (Acc)0;
-                hi[n] = p.h_init ? (Acc)p.h_init[(ch * N + n) * 2 + 1] : (Acc)0;
-            }
-        } else {
-            const Acc *gin = static_cast<const Acc *>(p.gin);
+        for (int i = 0; i < kT - kK; ++i) load_xd(i, xr[i], dr[i]);
+        load_entry(s, hr, hi);
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                hr[n] = gin[((int64_t)s * 2 * N + 2 * n) * BD + ch];
-                hi[n] = gin[((int64_t)s * 2 * N + 2 * n + 1) * BD + ch];
-            }
-        }
+        for (int j = 1; j < kNck; ++j) {
 #pragma unroll
-        for (int j = 0; j < kNck; ++j) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) {
-                ck[wave][j][2 * n][lane] = hr[n];
-                ck[wave][j][2 * n + 1][lane] = hi[n];
-            }
-            if (j + 1 < kNck) {
-#pragma unroll
-                for (int i = 0; i < kK; ++i) {
-                    const int t = j * kK + i;
-                    if (t < nseg) {
-                        Acc rw[2 * N];
-                        load_row<N>(rw, bcp + (int64_t)t * (2 * N));
-                        cbwd_fwd_step<N, kEuler>(cc, rw, (Acc)raw_to_f32<T>(xr[t]), dval(t), hr, hi);
-                    }
+            for (int i = 0; i < kK; ++i) {
+                const int t = (j - 1) * kK + i;
+                if (t < nseg) {
+                    Acc rw[2 * NH];
+                    load_half_row<NH, N>(rw, bcp + (int64_t)t * (2 * N), n0);
+                    cbwd_fwd_step<NH, kEuler>(cc, rw, (Acc)raw_to_f32<T>(xr[t]), dval(dr[t]), hr, hi);
                 }
+            }
+#pragma unroll
+            for (int k = 0; k < NH; ++k) {
+                ck[wave][j - 1][2 * k][lane] = hr[k];
+                ck[wave][j - 1][2 * k + 1][lane] = hi[k];
             }
         }
 
@@ -421,49 +483,77 @@ __global__ __launch_bounds__(CbwdShape<typename AccOf<T>::type>::kWaves *kWave) 
 #pragma unroll
         for (int u = kNck - 1; u >= 0; --u) {
             if (u * kK >= nseg) continue;
-            // the sub-chunk's states after each step: complex but for the
-            // last step's (its real part only); the entering state stays in
-            // its checkpoint (each lane reads back only what it wrote)
-            Acc gsr[kK][N], gsi[kK - 1][N];
+            // the sub-chunk's x, delta and dy
+            uint32_t xs[kK], ds[kK], ys[kK];
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                hr[n] = ck[wave][u][2 * n][lane];
-                hi[n] = ck[wave][u][2 * n + 1][lane];
+            for (int i = 0; i < kK; ++i) {
+                const int t = u * kK + i;
+                load_xd(t, xs[i], ds[i]);
+                ys[i] = buf_load_raw<T>(rdy, voff, (t < nseg ? t : nseg - 1) * row);
             }
+            auto xval = [&](int i) { return live ? (Acc)raw_to_f32<T>(xs[i]) : (Acc)0; };
+            auto gval = [&](int i) { return live ? (Acc)raw_to_f32<T>(ys[i]) : (Acc)0; };
+            // the entering state: its checkpoint, or for the first sub-chunk
+            // the segment's entry state, read again and kept in the slot of
+            // the state before step 4 (whose sub-chunk is done); each lane
+            // reads back only what it wrote.  Then the states after each
+            // step: complex but for the last step's (its real part only).
+            const int ks = u > 0 ? u - 1 : 0;
+            if (u > 0) {
+#pragma unroll
+                for (int k = 0; k < NH; ++k) {
+                    hr[k] = ck[wave][ks][2 * k][lane];
+                    hi[k] = ck[wave][ks][2 * k + 1][lane];
+                }
+            } else {
+                load_entry(s, hr, hi);
+#pragma unroll
+                for (int k = 0; k < NH; ++k) {
+                    ck[wave][ks][2 * k][lane] = hr[k];
+                    ck[wave][ks][2 * k + 1][lane] = hi[k];
+                }
+            }
+            Acc gsr[kK][NH], gsi[kK - 1][NH];
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
                 const int t = u * kK + i;
                 if (t < nseg) {
-                    Acc rw[2 * N];
-                    load_row<N>(rw, bcp + (int64_t)t * (2 * N));
-                    cbwd_fwd_step<N, kEuler>(cc, rw, (Acc)raw_to_f32<T>(xr[t]), dval(t), hr, hi);
+                    Acc rw[2 * NH];
+                    load_half_row<NH, N>(rw, bcp + (int64_t)t * (2 * N), n0);
+                    cbwd_fwd_step<NH, kEuler>(cc, rw, (Acc)raw_to_f32<T>(xs[i]), dval(ds[i]), hr, hi);
                 }
 #pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    gsr[i][n] = hr[n];
-                    if (i + 1 < kK) gsi[i < kK - 1 ? i : 0][n] = hi[n];
+                for (int k = 0; k < NH; ++k) {
+                    gsr[i][k] = hr[k];
+                    if (i + 1 < kK) gsi[i < kK - 1 ? i : 0][k] = hi[k];
                 }
             }
-            // back over the sub-chunk
+            // back over the sub-chunk; this wave's shares of dx and d(delta)
+            Acc px[kK], pg[kK];
 #pragma unroll
             for (int i = kK - 1; i >= 0; --i) {
+                px[i] = pg[i] = 0;
                 const int t = u * kK + i;
                 if (t < nseg) {
-                    Acc rw[2 * N];
-                    load_row<N>(rw, bcp + (int64_t)t * (2 * N));
-                    const Acc xv = xval(t), gy = gval(t), dv = dval(t);
+                    Acc rw[2 * NH];
+                    load_half_row<NH, N>(rw, bcp + (int64_t)t * (2 * N), n0);
+                    const Acc xv = xval(i), gy = gval(i);
+                    // delta through an empty asm: the coefficients are formed
+                    // again rather than kept in registers from the recompute
+                    Acc dv = dval(ds[i]);
+                    __asm__ volatile("" : "+v"(dv));
                     Acc ur, ui;
                     delta_units(dv, ur, ui);
-                    Acc vB[N], vC[N];
+                    Acc vB[NH], vC[NH];
                     Acc acc_x = 0, gdt = 0;
 #pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        const Acc hpr = i > 0 ? gsr[i > 0 ? i - 1 : 0][n] : ck[wave][u][2 * n][lane];
-                        const Acc hpi = i > 0 ? gsi[i > 0 ? i - 1 : 0][n] : ck[wave][u][2 * n + 1][lane];
+                    for (int n = 0; n < NH; ++n) {
+                        const Acc hpr = i > 0 ? gsr[i > 0 ? i - 1 : 0][n] : ck[wave][ks][2 * n][lane];
+                        const Acc hpi = i > 0 ? gsi[i > 0 ? i - 1 : 0][n] : ck[wave][ks][2 * n + 1][lane];
                         Acc abr, abi, kr, ki, er;
-                        cplx_coef<N, kEuler>(cc, n, dv, ur, ui, abr, abi, kr, ki, er);
+                        cplx_coef<NH, kEuler>(cc, n, dv, ur, ui, abr, abi, kr, ki, er);
                         // lambda: the adjoint of h_t (y reads its real part)
-                        const Acc mr = fma_(rw[N + n], gy, lr[n]), mi = li[n];
+                        const Acc mr = fma_(rw[NH + n], gy, lr[n]), mi = li[n];
                         const Acc u_ = rw[n] * xv;
                         // G_Abar = lambda conj(h_{t-1}),  G_k = lambda u
                         const Acc gar = fma_(mr, hpr, mi * hpi), gai = fma_(mi, hpr, -mr * hpi);
@@ -486,7 +576,7 @@ __global__ __launch_bounds__(CbwdShape<typename AccOf<T>::type>::kWaves *kWave) 
                         dAi[n] = fma_(gai, dar, fma_(-gar, dai, dAi[n]));
                         if constexpr (!kEuler) {
                             Acc qr, qi;
-                            cplx_dk_da<N>(cc, n, dv, abr, abi, er, qr, qi);
+                            cplx_dk_da<NH>(cc, n, dv, abr, abi, er, kr, ki, qr, qi);
                             dAr[n] = fma_(gkr, qr, fma_(gki, qi, dAr[n]));
                             dAi[n] = fma_(gki, qr, fma_(-gkr, qi, dAi[n]));
                         }
@@ -494,48 +584,65 @@ __global__ __launch_bounds__(CbwdShape<typename AccOf<T>::type>::kWaves *kWave) 
                         lr[n] = fma_(mr, abr, mi * abi);
                         li[n] = fma_(mi, abr, -mr * abi);
                     }
-                    const Acc gx = fma_(Dd, gy, acc_x);
-                    Acc gdl = gdt;
-                    if constexpr (kPre) {
-                        if (soft) gdl *= softplus_grad_from_value(dv);
+                    if constexpr (P == 1) {
+                        finish_step(t, gy, xv, dv, fma_(Dd, gy, acc_x), gdt);
+                    } else {
+                        px[i] = acc_x;
+                        pg[i] = gdt;
+                        if (half != 0) {
+                            xb[u & 1][tb][i][0][lane] = acc_x;
+                            xb[u & 1][tb][i][1][lane] = gdt;
+                        }
                     }
-                    dDacc = fma_(gy, xv, dDacc);
-                    dbacc += gdl;
-                    if (live) {
-                        buf_store(from_acc<T>(gx), rdx, voff, t * row);
-                        buf_store(from_acc<T>(gdl), rdd, voff, t * row);
+                    const int idx = wave_reduce_scatter<NH>(vB, lane);
+                    (void)wave_reduce_scatter<NH>(vC, lane);
+                    if ((lane & (kWave / NH - 1)) == 0) {
+                        bacc[tb][t][0][n0 + idx] = vB[0];
+                        bacc[tb][t][1][n0 + idx] = vC[0];
                     }
-                    const int idx = wave_reduce_scatter<N>(vB, lane);
-                    (void)wave_reduce_scatter<N>(vC, lane);
-                    if ((lane & (kWave / N - 1)) == 0) {
-                        bacc[wave][t][0][idx] = vB[0];
-                        bacc[wave][t][1][idx] = vC[0];
+                }
+            }
+            if constexpr (P > 1) {
+                // the other waves' shares of the sub-chunk are in (the buffer
+                // alternates, so it is not written again before the next barrier)
+                __syncthreads();
+                if (half == 0) {
+#pragma unroll
+                    for (int i = 0; i < kK; ++i) {
+                        const int t = u * kK + i;
+                        if (t < nseg) {
+                            const Acc gy = gval(i);
+                            const Acc gx = fma_(Dd, gy, px[i]) + xb[u & 1][tb][i][0][lane];
+                            finish_step(t, gy, xval(i), dval(ds[i]), gx, pg[i] + xb[u & 1][tb][i][1][lane]);
+                        }
                     }
                 }
             }
         }
-        __syncthreads();  // every wave's partials of the segment are in
+        __syncthreads();  // every tile's partials of the segment are in
         write_segment_sums(t0, nseg);
         __syncthreads();  // ... and summed before the next segment's are written
         if (s == 0 && live && q.dh_init != nullptr) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                q.dh_init[(ch * N + n) * 2] = (float)lr[n];
-                q.dh_init[(ch * N + n) * 2 + 1] = (float)li[n];
+            for (int k = 0; k < NH; ++k) {
+                q.dh_init[(ch * N + n0 + k) * 2] = (float)lr[k];
+                q.dh_init[(ch * N + n0 + k) * 2 + 1] = (float)li[k];
             }
         }
     }
 
     if (!live) return;
-    Acc *pa = static_cast<Acc *>(q.part_a) + ((int64_t)grp * BD + ch) * 2 * N;
+    Acc *pa = static_cast<Acc *>(q.part_a) + ((int64_t)grp * BD + ch) * 2 * N + 2 * n0;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        pa[2 * n] = dAr[n];
-        pa[2 * n + 1] = dAi[n];
+    for (int k = 0; k < NH; ++k) {
+        pa[2 * k] = dAr[k];
+        pa[2 * k + 1] = dAi[k];
     }
-    Acc *pd = static_cast<Acc *>(q.part_d) + ((int64_t)grp * BD + ch) * 2;
-    pd[0] = dDacc;
-    pd[1] = dbacc;
+    if (half == 0) {
+        Acc *pd = static_cast<Acc *>(q.part_d) + ((int64_t)grp * BD + ch) * 2;
+        pd[0] = dDacc;
+        pd[1] = dbacc;
+    }
 }
 
 // dB, dC: the block partials summed (one thread per (b, t, n)); dA, dD,

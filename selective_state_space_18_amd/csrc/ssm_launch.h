@@ -108,9 +108,12 @@ hipError_t cplx_step_bf16(const StepParams &p, int N, hipStream_t s);
 //   gout    : [groups][2N][B*D] Acc
 //   part_bc : [blocks per row][2][B*L*N] Acc, written by every block
 //   part_a  : [groups][B*D][2N] Acc
-// blocks_per_row = ceil(tiles_per_b / cbwd_waves(dtype)); kStarts is not used.
+// blocks_per_row = ceil(tiles_per_b / cbwd_tiles_per_block(dtype, N)); the
+// main kernel's blocks fit cbwd_blocks_per_cu(dtype) to a compute unit.
+// kStarts is not used.
 int cbwd_segment_len();
-int cbwd_waves(int dtype);
+int cbwd_tiles_per_block(int dtype, int N);
+int cbwd_blocks_per_cu(int dtype);
 hipError_t cbwd_pass_f32(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
 hipError_t cbwd_pass_bf16(BwdPass pass, const BwdParams &q, int N, hipStream_t s);
 
