@@ -234,9 +234,10 @@ def test_complex_bwd_2p8b_layer_sampled_channels(ss):
     frequencies w up to about 50 here: a channel's d(delta) reaches tens while
     the fp32 arithmetic leaves about 1e-5 relative error in lambda and h, so
     elements where the terms cancel carry an error that scales with the
-    channel, not with the element.  Its absolute floor is therefore 5e-4 of
-    the channel's largest |d(delta)| over time (about 1e-4 is measured); the
-    other gradients meet the plain bar."""
+    channel, not with the element.  Its absolute floor is therefore 1e-4 of
+    the channel's largest |d(delta)| over time (1.2e-5 is the least that
+    passes every element on this input); the other gradients meet the plain
+    bar."""
     cfg = configs.MAMBA2P8B_LAYER
     P.say(f"case: complex bwd {cfg.name} sampled channels")
     inp = generate.scan_inputs(cfg, DEV)
@@ -258,7 +259,7 @@ def test_complex_bwd_2p8b_layer_sampled_channels(ss):
                                   dh_final=cz(sub["dh_final"]), want_dBC=False)
     P.compare(got["dx"].index_select(2, idx), ref["dx"], "bf16", "dx")
     g, r = P.f64(got["ddelta"].index_select(2, idx)), ref["ddelta"]
-    floor = np.maximum(5e-4 * np.abs(r).max(axis=1, keepdims=True), P.BF16_ATOL)
+    floor = np.maximum(1e-4 * np.abs(r).max(axis=1, keepdims=True), P.BF16_ATOL)
     ratio = np.abs(g - r) / np.maximum(P.BF16_RTOL * np.abs(r), floor)
     assert ratio.max() <= 1.0, f"ddelta: exceeds its bound by {ratio.max():.3f}x"
     P.compare(got["dD"].index_select(0, idx), ref["dD"], "bf16", "dD")
