@@ -1260,12 +1260,11 @@ int cbwd_impl(const void *x, const void *delta, const float *delta_bias, const f
     if ((e = timed(SSM_K_BC_PREP, s, [&] { return fwd(ssm::ScanPass::kPrep); })) != hipSuccess)
         return hip_fail(e, "B/C conversion launch");
     if (p.S > 1) {
-        if ((e = timed(SSM_K_SCAN_AGGREGATE, s, [&] { return fwd(ssm::ScanPass::kAggregate); })) != hipSuccess)
-            return hip_fail(e, "forward aggregate launch");
+        // one pass gives the segment summaries of both directions
+        if ((e = timed(SSM_K_BWD_AGGREGATE, s, [&] { return bwd(ssm::BwdPass::kAggregate); })) != hipSuccess)
+            return hip_fail(e, "segment summary launch");
         if ((e = timed(SSM_K_SCAN_CARRY, s, [&] { return fwd(ssm::ScanPass::kCarry); })) != hipSuccess)
             return hip_fail(e, "forward carry launch");
-        if ((e = timed(SSM_K_BWD_AGGREGATE, s, [&] { return bwd(ssm::BwdPass::kAggregate); })) != hipSuccess)
-            return hip_fail(e, "backward aggregate launch");
     }
     if ((e = timed(SSM_K_BWD_CARRY, s, [&] { return bwd(ssm::BwdPass::kCarry); })) != hipSuccess)
         return hip_fail(e, "backward carry launch");

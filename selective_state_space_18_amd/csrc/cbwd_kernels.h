@@ -185,19 +185,26 @@ __device__ __forceinline__ void cplx_dk_da(const CbwdConst<N, Acc> &cc, int n, A
 }
 
 // ---------------------------------------------------------------------------
-// Reverse aggregate: segments 1..S-1, adjoint from zero at the segment end;
-// stores what reaches the segment start (after its first step's decay) and
-// the segment's sum of delta.  ragg [S][2N+1][B*D].
-
+// Segment summaries of both directions in one pass over each segment, which
+// forms every Abar once for both:
+//  * forward (segments 0..S-2, for the complex forward's carry): the end
+//    state from a zero start, agg [S-1][2N+1][B*D];
+//  * reverse (segments 1..S-1): the adjoint that a zero adjoint at the
+//    segment end leaves at its start, after the first step's decay,
+//    ragg [S][2N+1][B*D].  Run back step by step it is
+//    sum_i c_i conj(P_i) with c_i = C_i[n] dy_i and P_i = Abar_0 ... Abar_i,
+//    so forward in time it takes the running product P and one complex
+//    multiply-add per step.
+// Both store the segment's sum of delta in slot 2N.
 template <typename T, int N, bool kEuler, bool kPre>
 __global__ __launch_bounds__(kBlock) void cbwd_aggregate_kernel(BwdParams q) {
     typedef typename AccOf<T>::type Acc;
     const ScanParams &p = q.f;
     const int blocks_per_seg = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
-    const int s = lb / blocks_per_seg + 1;
+    const int s = lb / blocks_per_seg;
     const int wave = uniform((int)threadIdx.x / kWave);
-    const int tile = (lb - (s - 1) * blocks_per_seg) * p.waves_per_block + wave;
+    const int tile = (lb - s * blocks_per_seg) * p.waves_per_block + wave;
     if (wave >= p.waves_per_block || tile >= p.n_tiles) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t b = tile / p.tiles_per_b;
@@ -208,56 +215,84 @@ __global__ __launch_bounds__(kBlock) void cbwd_aggregate_kernel(BwdParams q) {
     const int64_t BD = p.Bsz * p.Dm;
     const int64_t t0 = (int64_t)s * p.seg_len;
     const int nsteps = uniform((int)((t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L) - t0));
+    const bool fwd = s + 1 < p.S, rev = s > 0;
 
     const CbwdConst<N, Acc> cc(p.A + d * 2 * N);
     const Acc bias = (kPre && p.delta_bias != nullptr) ? (Acc)p.delta_bias[d] : (Acc)0;
     const bool soft = p.delta_softplus != 0;
     const int64_t off = (b * p.L + t0) * p.Dm + d0;
     const int32_t row = (int32_t)(p.Dm * (int64_t)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const T *>(p.x) + off, nsteps * row);
     const __amdgpu_buffer_rsrc_t rdl = make_rsrc(static_cast<const T *>(p.delta) + off, nsteps * row);
     const __amdgpu_buffer_rsrc_t rdy = make_rsrc(static_cast<const T *>(q.dy) + off, nsteps * row);
     const int32_t voff = (int32_t)((d - d0) * (int64_t)sizeof(T));
     const_row_ptr<Acc> bcp = (const_row_ptr<Acc>)(static_cast<const Acc *>(p.bc) + (b * p.L + t0) * (2 * N));
 
-    Acc lr[N], li[N];
+    Acc hr[N], hi[N], pr[N], pi[N], rr[N], ri[N];
 #pragma unroll
-    for (int n = 0; n < N; ++n) lr[n] = li[n] = 0;
+    for (int n = 0; n < N; ++n) {
+        hr[n] = hi[n] = rr[n] = ri[n] = pi[n] = 0;
+        pr[n] = 1;
+    }
     Acc lam = 0;
-    // the step's delta and dy, and the previous step's fetched meanwhile
-    uint32_t dlc = buf_load_raw<T>(rdl, voff, (nsteps - 1) * row);
-    uint32_t dyc = buf_load_raw<T>(rdy, voff, (nsteps - 1) * row);
-    for (int i = nsteps - 1; i >= 0; --i) {
-        const int j = i > 0 ? i - 1 : 0;
-        const uint32_t dln = buf_load_raw<T>(rdl, voff, j * row);
+    // the step's inputs, and the next step's fetched meanwhile
+    uint32_t xc = buf_load_raw<T>(rx, voff, 0), dlc = buf_load_raw<T>(rdl, voff, 0);
+    uint32_t dyc = buf_load_raw<T>(rdy, voff, 0);
+    for (int i = 0; i < nsteps; ++i) {
+        const int j = i + 1 < nsteps ? i + 1 : i;
+        const uint32_t xn = buf_load_raw<T>(rx, voff, j * row), dln = buf_load_raw<T>(rdl, voff, j * row);
         const uint32_t dyn = buf_load_raw<T>(rdy, voff, j * row);
         Acc rw[2 * N];
         load_row<N>(rw, bcp + (int64_t)i * (2 * N));
         Acc dv = (Acc)raw_to_f32<T>(dlc);
         if constexpr (kPre) dv = soft ? softplus_(dv + bias) : dv + bias;
-        const Acc gy = (Acc)raw_to_f32<T>(dyc);
+        const Acc xv = (Acc)raw_to_f32<T>(xc), gy = (Acc)raw_to_f32<T>(dyc);
         lam += dv;
         Acc ur, ui;
         delta_units(dv, ur, ui);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            Acc mag, c, sn, em1;
-            cplx_exp_units(ur * cc.ar[n], ui * cc.ai[n], mag, c, sn, em1);
-            const Acc abr = mag * c, abi = mag * sn;
-            const Acc r = fma_(rw[N + n], gy, lr[n]), m = li[n];
-            lr[n] = fma_(r, abr, m * abi);
-            li[n] = fma_(m, abr, -r * abi);
+            Acc abr, abi, kr, ki, er;
+            cplx_coef<N, kEuler>(cc, n, dv, ur, ui, abr, abi, kr, ki, er);
+            if (fwd) {
+                const Acc u = rw[n] * xv;
+                const Acc r = hr[n], m = hi[n];
+                hr[n] = fma_(abr, r, fma_(-abi, m, kr * u));
+                hi[n] = fma_(abr, m, fma_(abi, r, ki * u));
+            }
+            if (rev) {
+                // P = P Abar;  R += c conj(P)
+                const Acc r = pr[n], m = pi[n];
+                pr[n] = fma_(r, abr, -m * abi);
+                pi[n] = fma_(r, abi, m * abr);
+                const Acc c = rw[N + n] * gy;
+                rr[n] = fma_(c, pr[n], rr[n]);
+                ri[n] = fma_(-c, pi[n], ri[n]);
+            }
         }
+        xc = xn;
         dlc = dln;
         dyc = dyn;
     }
     if (!active) return;
-    Acc *a = static_cast<Acc *>(q.ragg) + (int64_t)s * (2 * N + 1) * BD + ch;
+    if (fwd) {
+        Acc *a = static_cast<Acc *>(p.agg) + (int64_t)s * (2 * N + 1) * BD + ch;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        a[(int64_t)(2 * n) * BD] = lr[n];
-        a[(int64_t)(2 * n + 1) * BD] = li[n];
+        for (int n = 0; n < N; ++n) {
+            a[(int64_t)(2 * n) * BD] = hr[n];
+            a[(int64_t)(2 * n + 1) * BD] = hi[n];
+        }
+        a[(int64_t)(2 * N) * BD] = lam;
     }
-    a[(int64_t)(2 * N) * BD] = lam;
+    if (rev) {
+        Acc *a = static_cast<Acc *>(q.ragg) + (int64_t)s * (2 * N + 1) * BD + ch;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            a[(int64_t)(2 * n) * BD] = rr[n];
+            a[(int64_t)(2 * n + 1) * BD] = ri[n];
+        }
+        a[(int64_t)(2 * N) * BD] = lam;
+    }
 }
 
 // Reverse carry: one thread per (state n, channel).  The adjoint entering the
@@ -696,8 +731,8 @@ void cbwd_launch_variant(BwdPass pass, const BwdParams &q, hipStream_t s) {
     if (pass == BwdPass::kAggregate) {
         const int bps = (p.n_tiles + p.waves_per_block - 1) / p.waves_per_block;
         if (p.S <= 1 || bps == 0) return;
-        hipLaunchKernelGGL((cbwd_aggregate_kernel<T, N, kEuler, kPre>), dim3((unsigned)bps * (p.S - 1)),
-                           dim3(kBlock), 0, s, q);
+        hipLaunchKernelGGL((cbwd_aggregate_kernel<T, N, kEuler, kPre>), dim3((unsigned)bps * p.S), dim3(kBlock), 0,
+                           s, q);
     } else {
         const unsigned grid = (unsigned)(q.n_groups * p.Bsz * q.blocks_per_row);
         if (grid == 0) return;
