@@ -809,18 +809,24 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                         }
                     } else {
                         const Acc dxv = dv * xv;
+                        // Euler: delta through an empty asm, so that E is
+                        // formed again here rather than kept in registers from
+                        // the recompute (two waves per SIMD instead of one;
+                        // ZOH's per-channel constants keep it at one either way)
+                        Acc dvo = dv;
+                        if constexpr (kEuler) __asm__ volatile("" : "+v"(dvo));
                         // (ZOH: the exponent argument from delta in the exp
                         // unit's base times A, not from the per-channel array
                         // of A in that base: 16 fewer live registers)
                         constexpr Acc unit = sizeof(Acc) == 4 ? (Acc)kLog2e : (Acc)1;
-                        const Acc dvu = dv * unit;
+                        const Acc dvu = dvo * unit;
 #pragma unroll
                         for (int n = 0; n < N; ++n) {
                             Acc gprev = gp[n];
                             if (i > 0) gprev = gs[i > 0 ? i - 1 : 0][n];
                             if constexpr (kVarlen) gprev = rs ? hs[n] : gprev;
                             Acc e;
-                            const Acc E = kEuler ? expm1_and_exp2(dv * cc.Aeff[n], e)
+                            const Acc E = kEuler ? expm1_and_exp2(dvo * cc.Aeff[n], e)
                                                  : expm1_and_exp2(dvu * zoh_a<Acc>(Ar[n]), e);
                             const Acc mu = fma_(rw[N + n], gy, nu[n]);
                             const Acc pp = E * mu;
@@ -833,9 +839,22 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdParams q) {
                                 const Acc bx = rw[n] * xv;
                                 const Acc w = fma_(bx, (Acc)(n + 1), (Acc)Ar[n] * gprev);
                                 acc_d = fma_(nup, w, acc_d);
-                                const Acc z = dv * (Acc)Ar[n];
                                 dA1[n] = fma_(dv, nup * gprev, dA1[n]);
-                                dA2[n] = fma_(dv * dv * zoh_dphi(z, E), mu * bx, dA2[n]);
+                                Acc dphi;  // delta^2 phi'(delta A)
+                                if constexpr (sizeof(Acc) == 4) {
+                                    // (delta (1 + E) - E / A) / A with 1/A = W / (n+1):
+                                    // no branch and no reciprocal.  Its absolute
+                                    // error, about 6 eps |delta| / |A| against a
+                                    // value near delta^2 / 2, stays a few eps of the
+                                    // dA sum for nonzero A; the stand-in of A = 0
+                                    // takes the exact limit delta^2 / 2.
+                                    const Acc w0 = cc.W[n] * (Acc)(1.0 / (n + 1));
+                                    const Acc q = fma_(dv, (Acc)1 + E, -E * w0) * w0;
+                                    dphi = __builtin_fabsf(Ar[n]) < -kTinyA ? (Acc)0.5 * dv * dv : q;
+                                } else {
+                                    dphi = dv * dv * zoh_dphi(dv * (Acc)Ar[n], E);
+                                }
+                                dA2[n] = fma_(dphi, mu * bx, dA2[n]);
                             } else {
                                 acc_x = fma_(mu, rw[n], acc_x);
                                 vB[n] = mu * dxv;
