@@ -180,6 +180,46 @@ def test_backward_replays_match_eager(ss):
     _replay_check(lambda: ss.scan_bwd(*args, out=out), [out[k] for k in names], [eager[k] for k in names])
 
 
+def test_complex_backward_replays_match_eager(ss):
+    print("case: complex backward graph replay", flush=True)
+    cfg = configs.ScanConfig("graph_cbwd", 2, 300, 130, 16, "bf16", "s4d_real", "per_token", 1.0, 56)
+    inp = generate.scan_inputs(cfg, DEV)
+    A = generate.complex_A(130, 16, 57, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(58)
+    dy = torch.randn(inp["x"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    h0 = torch.complex(torch.randn((2, 130, 16), generator=gen, device=DEV),
+                       torch.randn((2, 130, 16), generator=gen, device=DEV))
+    dhf = torch.complex(torch.randn((2, 130, 16), generator=gen, device=DEV),
+                        torch.randn((2, 130, 16), generator=gen, device=DEV))
+    args = (inp["x"], inp["delta"], A, inp["B"], inp["C"], inp["D"], dy)
+    eager = ss.scan_complex_bwd(*args, h_init=h0, dh_final=dhf)
+    torch.cuda.synchronize()
+    names = sorted(k for k, v in eager.items() if v is not None)
+    out = {k: torch.empty_like(eager[k]) for k in names}
+    _replay_check(lambda: ss.scan_complex_bwd(*args, h_init=h0, dh_final=dhf, out=out), [out[k] for k in names],
+                  [eager[k] for k in names])
+
+
+def test_packed_backward_replays_match_eager(ss):
+    print("case: packed backward graph replay", flush=True)
+    cfg = configs.PackedConfig("graph_pbwd", 1500, 130, 16, "bf16", "s4d_real", "per_token", 1.0, mean_len=200,
+                               max_len=600, p_empty=0.1, h0_std=0.5, seed=59)
+    inp = generate.packed_inputs(cfg, DEV)
+    nseq = inp["cu"].numel() - 1
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(60)
+    dy = torch.randn(inp["x"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    dhf = torch.randn((nseq, 130, 16), generator=gen, device=DEV)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["cu"], dy)
+    eager = ss.scan_varlen_bwd(*args, h_init=inp["h_init"], dh_final=dhf)
+    torch.cuda.synchronize()
+    names = sorted(k for k, v in eager.items() if v is not None)
+    out = {k: torch.empty_like(eager[k]) for k in names}
+    _replay_check(lambda: ss.scan_varlen_bwd(*args, h_init=inp["h_init"], dh_final=dhf, out=out),
+                  [out[k] for k in names], [eager[k] for k in names])
+
+
 def test_captured_scratch_survives_a_larger_eager_call(ss):
     """A graph keeps the address of the stream's scratch buffer.  A later,
     larger eager call on the same stream must not free that buffer (it is
