@@ -16,21 +16,22 @@
 // with dk/ddelta = Abar, dk/dA = (delta A Abar - (Abar - 1)) / A^2 (ZOH), and
 // dk/ddelta = 1, dk/dA = 0 (Euler).
 //
-// Work layout, as the real backward (bwd_kernels.h) with one lane per channel:
-//   1. the complex forward's aggregate and carry passes give the state
-//      entering every 16-step segment;
-//   2. cbwd_aggregate_kernel runs the adjoint back from zero over each segment
-//      but the first; cbwd_carry_kernel composes these summaries from the
-//      right and keeps the adjoint entering the last segment of each group;
-//   3. cbwd_main_kernel: one wave per 64-channel tile and group of segments,
-//      last segment first.  A segment's x, delta and dy are loaded once; its
-//      state every 4 steps goes to LDS; each 4-step sub-chunk's states are
-//      recomputed from its checkpoint with the forward's own step, then the
-//      adjoint runs back over them.  dB and dC (sums over channels) go through
-//      the real backward's reduce-scatter and per-block LDS sums, then
-//      cbwd_reduce_kernel.
-// The 2N-value states make the checkpoints 32 KB per wave (fp32 arithmetic),
-// so a block holds all of a compute unit's waves: one wave per SIMD.
+// Work layout, as the real backward (bwd_kernels.h), one lane per channel:
+//   1. cbwd_aggregate_kernel: per 16-step segment, in one pass forward in
+//      time, the end state from a zero start (the complex forward's carry,
+//      cplx_carry_kernel, then gives the state entering every segment) and
+//      the adjoint a zero adjoint at the segment end leaves at its start;
+//   2. cbwd_carry_kernel composes the adjoint summaries from the right and
+//      keeps the adjoint entering the last segment of each group;
+//   3. cbwd_main_kernel: a block per group of segments and two 64-channel
+//      tiles, last segment first.  A tile is shared by two waves, each holding
+//      half of its N complex states, so that two blocks fit on a compute unit
+//      (two waves per SIMD).  Per segment, the states before steps 4, 8 and 12
+//      go to LDS; each 4-step sub-chunk's states are recomputed from its
+//      checkpoint, then the adjoint runs back over them, and the two waves of
+//      a tile add their dx and d(delta) shares through LDS.  dB and dC (sums
+//      over channels) go through the real backward's reduce-scatter and
+//      per-block LDS sums, then cbwd_reduce_kernel.
 #pragma once
 
 #include "bwd_kernels.h"
@@ -41,7 +42,8 @@ namespace ssm {
 namespace {
 
 // Main-kernel blocks: kWaves waves; kBlocksPerCU of them share a compute
-// unit (their LDS fits), one wave per SIMD each.
+// unit (their LDS fits), one wave per SIMD each.  fp64 arithmetic doubles the
+// checkpoints, so that block takes a compute unit alone.
 template <typename Acc>
 struct CbwdShape;
 template <>
