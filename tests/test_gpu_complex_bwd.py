@@ -267,3 +267,16 @@ def test_complex_bwd_2p8b_layer_sampled_channels(ss):
         v = c128(got[k].index_select(0 if k == "dA" else 1, idx))
         P.compare(v.real, r.real, "bf16", k + " (re)")
         P.compare(v.imag, r.imag, "bf16", k + " (im)")
+
+
+def test_complex_bwd_without_dh_init(ss):
+    """dh_init not asked for (NULL): the other gradients are unchanged."""
+    P.say("case: complex bwd without dh_init")
+    inp = make("bf16", 2, 150, 70, 8, "softplus_bias", True, True, seed=9)
+    opts = opts_of("softplus_bias", inp)
+    full = gpu_bwd(ss, inp, opts)
+    part = gpu_bwd(ss, inp, opts, want_dh_init=False)
+    torch.cuda.synchronize()
+    assert part.get("dh_init") is None
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias"):
+        assert torch.equal(part[k], full[k]), k
