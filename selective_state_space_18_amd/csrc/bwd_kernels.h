@@ -968,15 +968,25 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_ad_kernel(BwdParams q) {
     const int64_t DN = p.Dm * N;
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i >= DN + 2 * p.Dm) return;
-    const int64_t BD = p.Bsz * p.Dm;
-    if (i < DN) {
-        const int64_t d = i / N;
-        const int n = (int)(i % N);
-        const Acc *src = static_cast<const Acc *>(q.part_a);
+    // The partial rows are (group, batch row) pairs, row r = g * Bsz + b, summed
+    // in that order; kBatch loads are in flight before their adds (one at a
+    // time, the sum waited on every load).
+    constexpr int kBatch = 16;
+    const int64_t rows = (int64_t)q.n_groups * p.Bsz;
+    auto sum_rows = [&](const Acc *src, int64_t stride, int64_t off) -> Acc {
         Acc sacc = 0;
-        for (int g = 0; g < q.n_groups; ++g)
-            for (int64_t b = 0; b < p.Bsz; ++b) sacc += src[((int64_t)g * BD + b * p.Dm + d) * N + n];
-        q.dA[i] = (float)sacc;
+        for (int64_t r0 = 0; r0 < rows; r0 += kBatch) {
+            Acc v[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) v[k] = r0 + k < rows ? src[(r0 + k) * stride + off] : (Acc)0;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) sacc += v[k];
+        }
+        return sacc;
+    };
+    if (i < DN) {
+        // part_a: [groups][Bsz * Dm][N]
+        q.dA[i] = (float)sum_rows(static_cast<const Acc *>(q.part_a), p.Dm * N, i);
         return;
     }
     const int64_t j = i - DN;
@@ -984,11 +994,8 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_ad_kernel(BwdParams q) {
     const int which = (int)(j / p.Dm);  // 0: dD, 1: d(delta_bias)
     float *dst = which == 0 ? q.dD : q.ddelta_bias;
     if (dst == nullptr) return;
-    const Acc *src = static_cast<const Acc *>(q.part_d);
-    Acc sacc = 0;
-    for (int g = 0; g < q.n_groups; ++g)
-        for (int64_t b = 0; b < p.Bsz; ++b) sacc += src[((int64_t)g * BD + b * p.Dm + d) * 2 + which];
-    dst[d] = (float)sacc;
+    // part_d: [groups][Bsz * Dm][2]
+    dst[d] = (float)sum_rows(static_cast<const Acc *>(q.part_d), p.Dm * 2, d * 2 + which);
 }
 
 template <typename T, int N, bool kStruct, bool kEuler, bool kPre, bool kVarlen>

@@ -702,15 +702,24 @@ __global__ __launch_bounds__(kBlock) void cbwd_reduce_kernel(BwdParams q) {
         return;
     }
     const int64_t j = i - BLN;
-    const int64_t BD = p.Bsz * p.Dm;
-    if (j < DN2) {
-        const int64_t d = j / (2 * N);
-        const int64_t e = j - d * 2 * N;
-        const Acc *src = static_cast<const Acc *>(q.part_a);
+    // The partial rows are (group, batch row) pairs, row r = g * Bsz + b, summed
+    // in that order with kBatch loads in flight before their adds.
+    constexpr int kBatch = 16;
+    const int64_t rows = (int64_t)q.n_groups * p.Bsz;
+    auto sum_rows = [&](const Acc *src, int64_t stride, int64_t off) -> Acc {
         Acc sacc = 0;
-        for (int g = 0; g < q.n_groups; ++g)
-            for (int64_t b = 0; b < p.Bsz; ++b) sacc += src[((int64_t)g * BD + b * p.Dm + d) * 2 * N + e];
-        q.dA[j] = (float)sacc;
+        for (int64_t r0 = 0; r0 < rows; r0 += kBatch) {
+            Acc v[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) v[k] = r0 + k < rows ? src[(r0 + k) * stride + off] : (Acc)0;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) sacc += v[k];
+        }
+        return sacc;
+    };
+    if (j < DN2) {
+        // part_a: [groups][Bsz * Dm][2N]
+        q.dA[j] = (float)sum_rows(static_cast<const Acc *>(q.part_a), p.Dm * 2 * N, j);
         return;
     }
     const int64_t k = j - DN2;
@@ -719,11 +728,8 @@ __global__ __launch_bounds__(kBlock) void cbwd_reduce_kernel(BwdParams q) {
     const int which = (int)(k / p.Dm);  // 0: dD, 1: d(delta_bias)
     float *dst = which == 0 ? q.dD : q.ddelta_bias;
     if (dst == nullptr) return;
-    const Acc *src = static_cast<const Acc *>(q.part_d);
-    Acc sacc = 0;
-    for (int g = 0; g < q.n_groups; ++g)
-        for (int64_t b = 0; b < p.Bsz; ++b) sacc += src[((int64_t)g * BD + b * p.Dm + d) * 2 + which];
-    dst[d] = (float)sacc;
+    // part_d: [groups][Bsz * Dm][2]
+    dst[d] = (float)sum_rows(static_cast<const Acc *>(q.part_d), p.Dm * 2, d * 2 + which);
 }
 
 template <typename T, int N, bool kEuler, bool kPre>
