@@ -949,13 +949,25 @@ __global__ __launch_bounds__(kBlock) void bwd_reduce_bc_kernel(BwdParams q) {
     const int grp = (int)(t / ((int64_t)q.seg_per_group * p.seg_len));
     const Acc *src = static_cast<const Acc *>(q.part_bc);
     const int parts = 2 * q.blocks_per_row;
+    // part k = (path, block of the row); absent where that block had no wave
+    // of its path (never read then).  kBatch parts are loaded before their
+    // adds, which keep the order of k.
+    constexpr int kBatch = 8;
     Acc sb = 0, sc = 0;
-    for (int k = 0; k < parts; ++k) {
-        // part k = (path, block of the row); absent where that block had no
-        // wave of its path
-        if (q.part_on[((int64_t)k * p.Bsz + b) * q.n_groups + grp] == 0) continue;
-        sb += src[((int64_t)k * 2) * BLN + i];
-        sc += src[((int64_t)k * 2 + 1) * BLN + i];
+    for (int k0 = 0; k0 < parts; k0 += kBatch) {
+        Acc vb[kBatch], vc[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int64_t kk = k0 + k;
+            const bool on = kk < parts && q.part_on[(kk * p.Bsz + b) * q.n_groups + grp] != 0;
+            vb[k] = on ? src[(kk * 2) * BLN + i] : (Acc)0;
+            vc[k] = on ? src[(kk * 2 + 1) * BLN + i] : (Acc)0;
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            sb += vb[k];
+            sc += vc[k];
+        }
     }
     q.dB[i] = (float)(p.euler_b ? sb * (Acc)(n + 1) : sb);
     q.dC[i] = (float)(sc / (Acc)(n + 1));
