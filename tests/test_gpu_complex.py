@@ -217,6 +217,45 @@ def test_complex_decode_batch_in_slices(ss):
     assert bool((hbuf[Bsz * Dm * N * 2:] == 7.0).all()) and bool((ybuf[Bsz * Dm:] == 7.0).all())
 
 
+@pytest.mark.slow
+def test_complex_decode_full_batch(ss):
+    """The complex-A decode workload at its full size (256 x 8192 x 16, one
+    launch per token as bench.py times it): 16 steps checked on sampled
+    sequences, then 100 more with the state of two sequences checked at the
+    end."""
+    cfg = configs.DECODE_256x8192
+    P.say(f"case: {cfg.name} with complex A")
+    st = generate.step_state_complex(cfg, DEV)
+    h = torch.view_as_real(st["h"]).contiguous()
+    y = torch.empty(cfg.Bsz, cfg.Dm, dtype=torch.bfloat16, device=DEV)
+    toks = generate.step_tokens(cfg, st, 116)
+    bi = [0, 1, 128, 255]
+    idx = torch.tensor(bi, device=DEV)
+    sel = lambda t: P.f64(t.index_select(0, idx))
+    href = c128(torch.view_as_complex(h.index_select(0, idx).contiguous()))
+    for k in range(16):
+        tok = toks[k]
+        ss.step_complex(tok["x"], tok["delta"], st["A"], tok["B"], tok["C"], st["D"], h, y=y)
+        torch.cuda.synchronize()
+        yr, href = oracle.step_complex(sel(tok["x"]), sel(tok["delta"]), c128(st["A"]), sel(tok["B"]),
+                                       sel(tok["C"]), P.f64(st["D"]), href)
+        P.compare(y.index_select(0, idx), yr, "bf16", f"y step {k}")
+        compare_complex(torch.view_as_complex(h.index_select(0, idx).contiguous()), href, "bf16", f"h step {k}")
+    bi2 = [7, 200]
+    idx2 = torch.tensor(bi2, device=DEV)
+    sel2 = lambda t: P.f64(t.index_select(0, idx2))
+    href2 = c128(torch.view_as_complex(h.index_select(0, idx2).contiguous()))
+    for k in range(16, len(toks)):
+        tok = toks[k]
+        ss.step_complex(tok["x"], tok["delta"], st["A"], tok["B"], tok["C"], st["D"], h, y=y)
+        yr, href2 = oracle.step_complex(sel2(tok["x"]), sel2(tok["delta"]), c128(st["A"]), sel2(tok["B"]),
+                                        sel2(tok["C"]), P.f64(st["D"]), href2)
+    torch.cuda.synchronize()
+    P.compare(y.index_select(0, idx2), yr, "bf16", "y, last step")
+    compare_complex(torch.view_as_complex(h.index_select(0, idx2).contiguous()), href2, "bf16", "h after 116 steps")
+    assert np.isfinite(P.f64(h)).all()
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_complex_step_chain_equals_scan(ss, dtype):
     P.say(f"case: complex step chain {dtype}")

@@ -222,3 +222,18 @@ def test_fused_2p8b_layer_sampled(ss):
     yr, hr = oracle_run(inp, opts, d_idx=idx)
     P.compare(y[:, :, idx], yr, "bf16", "y (sampled channels)")
     P.compare(hf[:, idx], hr, "bf16", "h_final (sampled channels)")
+
+
+@pytest.mark.slow
+def test_euler_2p8b_layer_sampled(ss):
+    """The Euler input term on the Mamba-2.8B-shaped layer at full size in the
+    planner's launch configuration; every 64th channel compared."""
+    cfg = configs.MAMBA2P8B_LAYER
+    P.say(f"case: {cfg.name}, Euler input term")
+    inp = generate.scan_inputs(cfg, DEV)
+    opts = dict(euler_b=True)
+    y, hf = run(ss, inp, opts)
+    idx = np.arange(0, cfg.Dm, 64) + 41
+    yr, hr = oracle_run(inp, opts, d_idx=idx)
+    P.compare(y[:, :, idx], yr, "bf16", "y (sampled channels)")
+    P.compare(hf[:, idx], hr, "bf16", "h_final (sampled channels)")

@@ -416,6 +416,22 @@ def test_mamba2p8b_layer_sampled(ss):
 
 
 @pytest.mark.slow
+def test_mamba2p8b_layer_general_path_sampled(ss):
+    """The 2.8B-shaped layer with the structured-A path switched off (one
+    exponential per state element), at full size in the planner's launch
+    configuration: every 64th channel against the oracle."""
+    cfg = configs.MAMBA2P8B_LAYER
+    P.say(f"case: {cfg.name}, general path forced (every 64th channel)")
+    inp = generate.scan_inputs(cfg, DEV)
+    y, hf = run_scan(ss, inp, general=True)
+    idx = list(range(17, cfg.Dm, 64)) + [cfg.Dm - 1]
+    yr, hr = P.oracle_scan(inp, d_idx=idx)
+    ii = torch.tensor(idx, device=DEV)
+    P.compare(y.index_select(2, ii), yr, "bf16", "y (sampled channels, general path)")
+    P.compare(hf.index_select(1, ii), hr, "bf16", "h_final (sampled channels, general path)")
+
+
+@pytest.mark.slow
 def test_long_context_sampled(ss):
     cfg = configs.LONG_CONTEXT_1M
     P.say(f"case: {cfg.name} (every 64th channel)")
