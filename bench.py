@@ -5,7 +5,9 @@ A step is one selective-scan forward (B/C prep, segment aggregate, carry and
 output kernels) over the Mamba-2.8B-shaped layer: Bsz=4, L=16384, D=5120,
 N=16, bf16 storage, fp32 arithmetic, synthetic seeded inputs resident in HBM.
 `value` is elements/s (B*L*D*N per second) over exactly --steps back-to-back
-steps.  The JSON line also reports the achieved algorithmic HBM bandwidth;
+steps, taken after --warmup untimed steps; before those, every timed workload
+runs itself untimed for SETTLE_MS (60 ms), which the clocks need to reach
+their loaded state after the input generation.  The JSON line also reports the achieved algorithmic HBM bandwidth;
 the roofline of the dominant kernel (VALU-issue bound, with the HBM fractions
 of the kernel and of the step, and counter-measured HBM traffic of the kernel
 and of the whole call); the timing protocol (the median of individually
@@ -124,6 +126,29 @@ def traffic_fields(workload, kind, alg):
             "traffic_call_over_algorithmic": None if call is None else round(call / alg, 3)}
 
 
+# Sustained load the clocks need before a timed loop.  After input generation
+# or any idle gap the GPU takes tens of milliseconds of load to settle: on the
+# 2.8B-shaped scan a call after a 2 s pause ran 1.09 ms, the next ones 1.47,
+# easing to 1.07 ms over about 30 calls.  Every timed workload first runs
+# itself untimed for this long, then its W warmup steps, then the timed steps.
+SETTLE_MS = 60.0
+
+
+def settle(torch, fn, ms=SETTLE_MS):
+    """Untimed calls of `fn` until about `ms` of wall time has passed
+    (synchronising every 4 calls).  Returns the number of calls."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(4):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return n
+
+
 def timed_loop(torch, fn, steps, warmup):
     for i in range(warmup):
         fn(i)
@@ -185,6 +210,7 @@ def protocol_record(torch, fn, fn_fixed, steps, flusher, rotation):
     fm, _ = event_timed_calls(torch, fn, n, flush=flusher)
     um, _ = event_timed_calls(torch, fn_fixed, n)
     return {"input_copies_rotated": rotation, "calls": n, "mall_flush_bytes": FLUSH_BYTES,
+            "untimed_settle_ms_before_warmup": SETTLE_MS,
             "flushed_median_ms": round(fm, 5), "unflushed_same_input_median_ms": round(um, 5)}
 
 
@@ -236,6 +262,7 @@ def bench_unfused_softplus(torch, ss, generate, cfg, steps, warmup):
         ss.scan_fwd(inp["x"], act, inp["A"], inp["B"], inp["C"], inp["D"], y=y, h_final=hf)
 
     log(f"[bench] timing {cfg.name} with a separate softplus pass: {warmup} warmup + {steps} steps")
+    settle(torch, fn)
     ms = timed_loop(torch, fn, steps, warmup)
     del inp, y, hf, act
     torch.cuda.empty_cache()
@@ -247,6 +274,7 @@ def profiled_loop(torch, ss, fn, steps, warmup):
     launch duration over the same number of calls with the library's
     per-kernel HIP-event timers on.  The event records add gaps between
     launches, so the wall time is taken with the timers off."""
+    settle(torch, fn)
     ms = timed_loop(torch, fn, steps, warmup)
     ss.set_option(ss.SSM_OPT_PROFILE, 1)
     ss.profile_read()
